@@ -1,0 +1,469 @@
+"""fp64 CPU oracle for one-pass block-sparse masked attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module.  The library's product path never
+calls it; it shares no code, table or helper with the HIP kernels.
+
+What it computes follows the pages on One-Pass to Reason (Goru, Mehta, Jain,
+arXiv 2504.18246):
+
+* wiki summary "One-Pass to Reason: 多轮推理的高效单遍微调", sections
+  "Token 复制" (token duplication), "分块稀疏注意力掩码" (block-sparse attention
+  mask: the four visibility rules), "位置 ID 策略" (strategic position ids),
+  "理论保证" (Theorem 2.1, one pass equals N passes) and "实现细节"
+  (implementation notes: packing with the custom mask);
+* raw note "One-Pass to Reason: Token Duplication and Block-Sparse Mask ...",
+  sections "Core Problem" and "Method".
+
+Plain definition used here: every token attends, with ordinary softmax
+attention, to exactly the keys that the four rules allow, and RoPE is applied
+at the strategic position ids.  The mask is built by set membership from the
+rules (never from a simplified predicate); the N-pass brute force runs the N
+separate causal sequences with positions 0..n-1.  Everything is float64 numpy.
+
+Readings where the pages are silent (each listed in the design notes):
+segment order within a turn is h, t, r_in, r_out; H_<i is the human messages
+and context response copies of earlier turns of the same conversation; each
+segment is causal inside itself; each packed conversation starts at position 0
+and never sees another; an empty segment x "ends" at s_x + 0 - 1, so the next
+start is s_x + len_x; PAD rows see nothing (O = 0, LSE = -inf, zero gradients);
+RoPE is the rotate-half form with inv_freq_j = theta^(-2j/D); the softmax scale
+is 1/sqrt(D); q head h reads kv head h // (Hq/Hkv).
+
+Parity status: every function here is pinned by the CPU tests (hand-derived
+worked example, invariants, library attention, finite differences and the
+N-pass brute force); the tile schedule is pinned by brute-force counting.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+# token types
+H, T, RIN, ROUT, PAD = 0, 1, 2, 3, 4
+TYPE_NAMES = {H: "h", T: "t", RIN: "r_in", ROUT: "r_out", PAD: "pad"}
+
+
+# ----------------------------------------------------------------------------
+# layout: tokens and strategic position ids
+# ----------------------------------------------------------------------------
+def layout(rows: Sequence, L: int) -> Dict[str, np.ndarray]:
+    """Per-token conversation, turn, type and position id for packed rows.
+
+    Token duplication (wiki summary, "Token 复制"): each turn contributes the
+    human message h_i, the reasoning t_i, the context copy r_in_i and the
+    generation copy r_out_i, in that order; conversations follow each other in
+    a row (packing, "实现细节"), the rest of the row is PAD.
+
+    Position ids (wiki summary, "位置 ID 策略"):
+      t_i and r_in_i both start right after h_i ends;
+      r_out_i starts right after t_i ends;
+      h_{i+1} starts right after r_in_i ends;
+    the first human message of each conversation starts at 0.
+    """
+    B = len(rows)
+    conv = np.full((B, L), -1, dtype=np.int64)
+    turn = np.full((B, L), -1, dtype=np.int64)
+    typ = np.full((B, L), PAD, dtype=np.int64)
+    pos = np.zeros((B, L), dtype=np.int64)
+    for b, convs in enumerate(rows):
+        idx = 0
+        for c, turns in enumerate(convs):
+            s_h = 0
+            for i, (h, t, r_in, r_out) in enumerate(turns):
+                e_h = s_h + h - 1          # last position of h_i
+                s_t = e_h + 1              # t_i starts right after h_i
+                s_rin = e_h + 1            # so does r_in_i
+                e_t = s_t + t - 1
+                s_rout = e_t + 1           # r_out_i starts right after t_i
+                e_rin = s_rin + r_in - 1
+                for y, n, s in ((H, h, s_h), (T, t, s_t), (RIN, r_in, s_rin), (ROUT, r_out, s_rout)):
+                    if idx + n > L:
+                        raise ValueError(f"row {b}: conversations exceed L={L}")
+                    sl = slice(idx, idx + n)
+                    conv[b, sl] = c
+                    turn[b, sl] = i
+                    typ[b, sl] = y
+                    pos[b, sl] = s + np.arange(n)
+                    idx += n
+                s_h = e_rin + 1            # h_{i+1} starts right after r_in_i
+    return {"conv": conv, "turn": turn, "type": typ, "pos": pos}
+
+
+def conv_range(lay, b: int, c: int) -> Tuple[int, int]:
+    """Packed index range [a, a + n) of conversation c in row b (contiguous)."""
+    idx = np.nonzero(lay["conv"][b] == c)[0]
+    if len(idx) == 0:
+        return 0, 0
+    return int(idx[0]), int(idx[-1]) + 1
+
+
+def n_convs(lay, b: int) -> int:
+    return int(lay["conv"][b].max()) + 1
+
+
+def _segments(lay, b: int, a: int, e: int):
+    """Contiguous runs of equal (turn, type) inside [a, e): (turn, type, start, stop)."""
+    tu = lay["turn"][b, a:e]
+    ty = lay["type"][b, a:e]
+    segs = []
+    s = 0
+    n = e - a
+    while s < n:
+        f = s
+        while f < n and tu[f] == tu[s] and ty[f] == ty[s]:
+            f += 1
+        segs.append((int(tu[s]), int(ty[s]), a + s, a + f))
+        s = f
+    return segs
+
+
+# ----------------------------------------------------------------------------
+# the block-sparse mask, from the four rules
+# ----------------------------------------------------------------------------
+# Within its own turn a query of type y sees these whole segments
+# (wiki summary, "分块稀疏注意力掩码"):
+#   h_i    -> (nothing else of turn i)
+#   t_i    -> h_i
+#   r_in_i -> h_i
+#   r_out_i-> h_i, t_i
+# and its own segment causally.  Every query also sees H_<i.
+_SAME_TURN_WHOLE = {H: (), T: (H,), RIN: (H,), ROUT: (H, T)}
+# H_<i: the human messages and the context copies of earlier turns.
+_HISTORY_TYPES = (H, RIN)
+
+
+def conv_mask(lay, b: int, c: int, q0: int = 0, q1: int = None) -> np.ndarray:
+    """Rows [q0, q1) (local to conversation c) of its dense bool mask [nq, n].
+
+    Built by set membership: for each (query segment, key segment) pair the
+    rules say "all", "causal" (same segment) or "none".  Conversations are
+    separate blocks of the packed mask; PAD sees nothing and is never seen.
+    """
+    a, e = conv_range(lay, b, c)
+    n = e - a
+    if q1 is None:
+        q1 = n
+    M = np.zeros((q1 - q0, n), dtype=bool)
+    segs = _segments(lay, b, a, e)
+    for (i, y, qs, qe) in segs:
+        qs_l, qe_l = max(qs - a, q0), min(qe - a, q1)
+        if qs_l >= qe_l:
+            continue
+        rows = slice(qs_l - q0, qe_l - q0)
+        for (j, x, ks, ke) in segs:
+            cols = slice(ks - a, ke - a)
+            if j < i and x in _HISTORY_TYPES:
+                M[rows, cols] = True
+            elif j == i and x in _SAME_TURN_WHOLE[y]:
+                M[rows, cols] = True
+            elif j == i and x == y:
+                # causal inside the segment: key index <= query index
+                qi = np.arange(qs_l, qe_l)[:, None]
+                ki = np.arange(ks - a, ke - a)[None, :]
+                M[rows, cols] = ki <= qi
+    return M
+
+
+def dense_mask(lay, b: int) -> np.ndarray:
+    """The whole [L, L] mask of row b (small L only)."""
+    L = lay["conv"].shape[1]
+    M = np.zeros((L, L), dtype=bool)
+    for c in range(n_convs(lay, b)):
+        a, e = conv_range(lay, b, c)
+        M[a:e, a:e] = conv_mask(lay, b, c)
+    return M
+
+
+# ----------------------------------------------------------------------------
+# tile schedule, counted from the mask
+# ----------------------------------------------------------------------------
+EMPTY, PARTIAL, FULL = 0, 1, 2
+SUB = 32
+
+
+def _group_sum(M: np.ndarray, start: int, axis: int, g: int):
+    """Sum M (non-empty along ``axis``) in groups of g aligned to the absolute
+    index ``start`` of its first entry; returns (first group index, sums)."""
+    n = M.shape[axis]
+    cuts = [0] + [k for k in range(1, n) if (start + k) % g == 0]
+    return start // g, np.add.reduceat(M.astype(np.int64), cuts, axis=axis)
+
+
+def schedule(lay, b: int, BQ: int, BK: int, row_chunk: int = 2048) -> Dict[str, np.ndarray]:
+    """Tile classes and lists of row b for BQ x BK tiles.
+
+    A tile is EMPTY if the mask allows none of its pairs, FULL if it allows all
+    BQ*BK of them (entries beyond L count as masked), PARTIAL otherwise; the
+    same rule at 32 x 32 gives the sub-block classes, packed two bits each
+    (sub-block (i, j) at bit 2*(i*BK/32 + j)).  q_list[m] lists the non-empty
+    k-tiles of q-tile m ascending, k_list[n] the non-empty q-tiles of k-tile n.
+    """
+    L = lay["conv"].shape[1]
+    MT, NT = -(-L // BQ), -(-L // BK)
+    gg = math.gcd(math.gcd(BQ, BK), SUB)   # counting granularity
+    G = np.zeros((MT * BQ // gg, NT * BK // gg), dtype=np.int64)
+    for c in range(n_convs(lay, b)):
+        a, e = conv_range(lay, b, c)
+        n = e - a
+        for r0 in range(0, n, row_chunk):
+            r1 = min(n, r0 + row_chunk)
+            M = conv_mask(lay, b, c, r0, r1)
+            c0, Mc = _group_sum(M, a, 1, gg)
+            r0g, Mrc = _group_sum(Mc, a + r0, 0, gg)
+            G[r0g:r0g + Mrc.shape[0], c0:c0 + Mrc.shape[1]] += Mrc
+    counts = G.reshape(MT, BQ // gg, NT, BK // gg).sum(axis=(1, 3))
+    tile_class = np.where(counts == 0, EMPTY, np.where(counts == BQ * BK, FULL, PARTIAL)).astype(np.uint8)
+    sub_class = np.zeros((MT, NT), dtype=np.uint64)
+    if BQ % SUB == 0 and BK % SUB == 0:
+        sq, sk, f = BQ // SUB, BK // SUB, SUB // gg
+        Gs = G.reshape(G.shape[0] // f, f, G.shape[1] // f, f).sum(axis=(1, 3))
+        sub_cls = np.where(Gs == 0, EMPTY, np.where(Gs == SUB * SUB, FULL, PARTIAL)).astype(np.uint64)
+        sub_cls = sub_cls.reshape(MT, sq, NT, sk).transpose(0, 2, 1, 3)  # [MT, NT, sq, sk]
+        for i in range(sq):
+            for j in range(sk):
+                sub_class |= sub_cls[:, :, i, j] << np.uint64(2 * (i * sk + j))
+    q_nnz = np.zeros(MT, dtype=np.int64)
+    q_list = np.full((MT, NT), -1, dtype=np.int64)
+    for m in range(MT):
+        nz = np.nonzero(counts[m] > 0)[0]
+        q_nnz[m] = len(nz)
+        q_list[m, :len(nz)] = nz
+    k_nnz = np.zeros(NT, dtype=np.int64)
+    k_list = np.full((NT, MT), -1, dtype=np.int64)
+    for nn in range(NT):
+        nz = np.nonzero(counts[:, nn] > 0)[0]
+        k_nnz[nn] = len(nz)
+        k_list[nn, :len(nz)] = nz
+    return {"counts": counts, "tile_class": tile_class, "sub_class": sub_class.astype(np.uint32),
+            "q_nnz": q_nnz, "q_list": q_list, "k_nnz": k_nnz, "k_list": k_list}
+
+
+def useful_pairs(lay) -> int:
+    """P: allowed (query, key) pairs summed over all rows, counted from the mask."""
+    P = 0
+    for b in range(lay["conv"].shape[0]):
+        for c in range(n_convs(lay, b)):
+            a, e = conv_range(lay, b, c)
+            n = e - a
+            for r0 in range(0, n, 2048):
+                P += int(conv_mask(lay, b, c, r0, min(n, r0 + 2048)).sum())
+    return P
+
+
+# ----------------------------------------------------------------------------
+# RoPE at the strategic positions
+# ----------------------------------------------------------------------------
+def rope_angles(pos: np.ndarray, D: int, theta: float) -> np.ndarray:
+    """angle[..., j] = pos * theta^(-2j/D), j < D/2."""
+    j = np.arange(D // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * j / D)
+    return np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+
+
+def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half RoPE of x [n, H, D] at positions pos [n]:
+    x' = [x1 cos - x2 sin, x2 cos + x1 sin] with x1 = x[:D/2], x2 = x[D/2:]."""
+    D = x.shape[-1]
+    ang = rope_angles(pos, D, theta)[:, None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., : D // 2], x[..., D // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def rope_transpose(g: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """R(pos)^T g: the rotation by the negated angle (gradient through RoPE)."""
+    D = g.shape[-1]
+    ang = rope_angles(pos, D, theta)[:, None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    g1, g2 = g[..., : D // 2], g[..., D // 2:]
+    return np.concatenate([g1 * c + g2 * s, g2 * c - g1 * s], axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# attention forward / backward
+# ----------------------------------------------------------------------------
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def attn_fwd(q, k, v, lay, theta: float, scale: float = None):
+    """Masked GQA attention of every row.  q [B, L, Hq, D], k/v [B, L, Hkv, D].
+
+    Returns O [B, L, Hq, D] and LSE [B, Hq, L] (natural log), float64.
+    Queries are grouped by conversation: the packed mask is block diagonal.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    O = np.zeros((B, L, Hq, D))
+    LSE = np.full((B, Hq, L), -np.inf)
+    for b in range(B):
+        for c in range(n_convs(lay, b)):
+            a, e = conv_range(lay, b, c)
+            M = conv_mask(lay, b, c)
+            pos = lay["pos"][b, a:e]
+            qr = rope(q[b, a:e], pos, theta)
+            kr = rope(k[b, a:e], pos, theta)
+            for h in range(Hq):
+                kv = h // g
+                S = scale * (qr[:, h] @ kr[:, kv].T)
+                S = np.where(M, S, -np.inf)
+                m = S.max(axis=1, keepdims=True)
+                P = np.exp(S - m)
+                l = P.sum(axis=1, keepdims=True)
+                P = P / l
+                O[b, a:e, h] = P @ v[b, a:e, kv]
+                LSE[b, h, a:e] = (m + np.log(l))[:, 0]
+    return O, LSE
+
+
+def attn_bwd(q, k, v, do, lay, theta: float, scale: float = None):
+    """Gradients of sum(O * dO) w.r.t. the pre-RoPE q, k and v, float64.
+
+    dV = sum_group P^T dO; dP = dO V^T; dS = P (dP - rowsum(P dP));
+    dQ' = scale dS K'; dK' = scale sum_group dS^T Q'; dQ = R^T dQ', dK = R^T dK'.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for c in range(n_convs(lay, b)):
+            a, e = conv_range(lay, b, c)
+            M = conv_mask(lay, b, c)
+            pos = lay["pos"][b, a:e]
+            qr = rope(q[b, a:e], pos, theta)
+            kr = rope(k[b, a:e], pos, theta)
+            dqr = np.zeros_like(qr)
+            dkr = np.zeros_like(kr)
+            for h in range(Hq):
+                kv = h // g
+                S = scale * (qr[:, h] @ kr[:, kv].T)
+                S = np.where(M, S, -np.inf)
+                P = np.exp(S - S.max(axis=1, keepdims=True))
+                P = P / P.sum(axis=1, keepdims=True)
+                dO = do[b, a:e, h]
+                dv[b, a:e, kv] += P.T @ dO
+                dP = dO @ v[b, a:e, kv].T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                dqr[:, h] = scale * (dS @ kr[:, kv])
+                dkr[:, kv] += scale * (dS.T @ qr[:, h])
+            dq[b, a:e] = rope_transpose(dqr, pos, theta)
+            dk[b, a:e] = rope_transpose(dkr, pos, theta)
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# N-pass brute force (Theorem 2.1)
+# ----------------------------------------------------------------------------
+def _seg_index(lay, b, c):
+    """{(turn, type): packed indices} for conversation c of row b."""
+    a, e = conv_range(lay, b, c)
+    out = {}
+    for (i, y, s, f) in _segments(lay, b, a, e):
+        out[(i, y)] = np.arange(s, f)
+    return out
+
+
+def npass_index(lay, b: int, c: int) -> List[Dict[str, np.ndarray]]:
+    """For each turn i, the packed rows that make up pass i of the N-pass.
+
+    Pass i is the ordinary sequence [h_1, r_1, ..., h_{i-1}, r_{i-1}, h_i, t_i, r_i]
+    in which earlier reasoning is dropped (wiki summary, "问题背景"); the context
+    copy r_in_j stands for r_j of an earlier turn, the generation copy r_out_i
+    for r_i of turn i.  Returns per pass: 'idx' (packed rows in sequence order)
+    and 'role' (the packed type each sequence position stands for).
+    """
+    seg = _seg_index(lay, b, c)
+    empty = np.zeros(0, dtype=np.int64)
+    N = max(i for (i, _y) in seg) + 1
+    passes = []
+    for i in range(N):
+        parts, roles = [], []
+        for j in range(i):
+            for y in (H, RIN):
+                ix = seg.get((j, y), empty)
+                parts.append(ix)
+                roles.append(np.full(len(ix), y))
+        for y in (H, T, ROUT):
+            ix = seg.get((i, y), empty)
+            parts.append(ix)
+            roles.append(np.full(len(ix), y))
+        passes.append({"idx": np.concatenate(parts).astype(np.int64),
+                       "role": np.concatenate(roles).astype(np.int64)})
+    return passes
+
+
+def causal_attn(q, k, v, theta: float, scale: float = None):
+    """Textbook causal attention of one sequence at positions 0..n-1.
+
+    q [n, Hq, D], k/v [n, Hkv, D]; returns O [n, Hq, D], LSE [Hq, n]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, Hq, D = q.shape
+    g = Hq // k.shape[1]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    pos = np.arange(n)
+    qr, kr = rope(q, pos, theta), rope(k, pos, theta)
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    O = np.zeros((n, Hq, D))
+    LSE = np.zeros((Hq, n))
+    for h in range(Hq):
+        S = np.where(causal, scale * (qr[:, h] @ kr[:, h // g].T), -np.inf)
+        m = S.max(axis=1, keepdims=True)
+        P = np.exp(S - m)
+        l = P.sum(axis=1, keepdims=True)
+        O[:, h] = (P / l) @ v[:, h // g]
+        LSE[h] = (m + np.log(l))[:, 0]
+    return O, LSE
+
+
+def causal_attn_bwd(q, k, v, do, theta: float, scale: float = None):
+    """Gradients of sum(O * dO) for causal_attn, w.r.t. pre-RoPE q, k, v."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    n, Hq, D = q.shape
+    g = Hq // k.shape[1]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    pos = np.arange(n)
+    qr, kr = rope(q, pos, theta), rope(k, pos, theta)
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    dqr, dkr, dv = np.zeros_like(qr), np.zeros_like(kr), np.zeros_like(v)
+    for h in range(Hq):
+        kv = h // g
+        S = np.where(causal, scale * (qr[:, h] @ kr[:, kv].T), -np.inf)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P = P / P.sum(axis=1, keepdims=True)
+        dv[:, kv] += P.T @ do[:, h]
+        dP = do[:, h] @ v[:, kv].T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dqr[:, h] = scale * (dS @ kr[:, kv])
+        dkr[:, kv] += scale * (dS.T @ qr[:, h])
+    return rope_transpose(dqr, pos, theta), rope_transpose(dkr, pos, theta), dv
+
+
+# ----------------------------------------------------------------------------
+# per-token loss (attention-only proxy for the SFT loss)
+# ----------------------------------------------------------------------------
+def token_ce(feats: np.ndarray, W: np.ndarray, labels: np.ndarray) -> np.ndarray:
+    """Cross entropy of softmax(feats @ W) at the given labels, one value per row."""
+    z = _f64(feats) @ _f64(W)
+    zmax = z.max(axis=1, keepdims=True)
+    lse = zmax[:, 0] + np.log(np.exp(z - zmax).sum(axis=1))
+    return lse - z[np.arange(len(labels)), labels]
+
+
+def loss_rows_1pass(lay, b: int) -> np.ndarray:
+    """Packed rows in the 1-pass loss: reasoning and generation copies (t_i, r_out_i).
+
+    The generation copy is the one in the loss (wiki summary, "Token 复制");
+    the reasoning is generated text too, so both are scored."""
+    typ = lay["type"][b]
+    return np.nonzero((typ == T) | (typ == ROUT))[0]
