@@ -1,0 +1,213 @@
+"""ctypes binding of libopr (include/opr.h), with the same entry-point names.
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every step of the computation runs in libopr's kernels.  Importing
+this module loads libopr.so and raises if it has not been built; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import inputs
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libopr.so")
+
+OPR_OK, OPR_E_INVALID, OPR_E_CAPACITY, OPR_E_UNSUPPORTED, OPR_E_HIP = 0, -1, -2, -3, -4
+OPR_ATTN_BLOCK = 128
+OPR_SUB_BLOCK = 32
+
+
+class OprError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {opr_status_string(status)} ({status})")
+        self.status = status
+
+
+class OprTurn(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_int32), ("t", ctypes.c_int32),
+                ("r_in", ctypes.c_int32), ("r_out", ctypes.c_int32)]
+
+
+class OprLayout(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "tok_conv", "tok_turn", "tok_pos", "tok_type", "tile_class", "sub_class",
+        "q_nnz", "q_list", "k_nnz", "k_list")]
+
+
+class OprAttnIn(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("L", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("rope_theta", ctypes.c_double),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("layout", OprLayout),
+                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libopr.so is not built ({_LIB_PATH}); run "
+                          "`python -m block_sparse_masked_opr_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, sz, vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    lib.opr_build_layout.restype = i32
+    lib.opr_build_layout.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, sz,
+                                     ctypes.POINTER(OprLayout), vp]
+    lib.opr_build_layout_workspace_size.restype = sz
+    lib.opr_build_layout_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.opr_attn_fwd.restype = i32
+    lib.opr_attn_fwd.argtypes = [ctypes.POINTER(OprAttnIn), vp, vp, vp, sz, vp]
+    lib.opr_attn_bwd.restype = i32
+    lib.opr_attn_bwd.argtypes = [ctypes.POINTER(OprAttnIn), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.opr_attn_workspace_size.restype = sz
+    lib.opr_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.opr_status_string.restype = ctypes.c_char_p
+    lib.opr_status_string.argtypes = [i32]
+    return lib
+
+
+LIB = _load()
+
+EXPORTED = ("opr_build_layout", "opr_build_layout_workspace_size", "opr_attn_fwd",
+            "opr_attn_bwd", "opr_attn_workspace_size", "opr_status_string")
+
+
+def opr_status_string(status: int) -> str:
+    return LIB.opr_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != OPR_OK:
+        raise OprError(status, what)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def opr_build_layout_workspace_size(B: int, L: int, n_convs: int, n_turns: int) -> int:
+    return int(LIB.opr_build_layout_workspace_size(B, L, n_convs, n_turns))
+
+
+def opr_attn_workspace_size(B: int, L: int, Hq: int, Hkv: int, D: int, is_bwd: bool) -> int:
+    return int(LIB.opr_attn_workspace_size(B, L, Hq, Hkv, D, 1 if is_bwd else 0))
+
+
+class Layout:
+    """Device tensors filled by opr_build_layout (int32 unless noted)."""
+
+    FIELDS = ("tok_conv", "tok_turn", "tok_pos", "tok_type", "tile_class", "sub_class",
+              "q_nnz", "q_list", "k_nnz", "k_list")
+
+    def __init__(self, B: int, L: int, block_q: int, block_k: int, device):
+        self.B, self.L, self.block_q, self.block_k = B, L, block_q, block_k
+        self.MT, self.NT = -(-L // block_q), -(-L // block_k)
+        e = dict(device=device)
+        self.tok_conv = torch.empty((B, L), dtype=torch.int32, **e)
+        self.tok_turn = torch.empty((B, L), dtype=torch.int32, **e)
+        self.tok_pos = torch.empty((B, L), dtype=torch.int32, **e)
+        self.tok_type = torch.empty((B, L), dtype=torch.uint8, **e)
+        self.tile_class = torch.empty((B, self.MT, self.NT), dtype=torch.uint8, **e)
+        # uint32 bit words, held as int32 (same bits)
+        self.sub_class = torch.empty((B, self.MT, self.NT), dtype=torch.int32, **e)
+        self.q_nnz = torch.empty((B, self.MT), dtype=torch.int32, **e)
+        self.q_list = torch.empty((B, self.MT, self.NT), dtype=torch.int32, **e)
+        self.k_nnz = torch.empty((B, self.NT), dtype=torch.int32, **e)
+        self.k_list = torch.empty((B, self.NT, self.MT), dtype=torch.int32, **e)
+
+    def c_struct(self) -> OprLayout:
+        return OprLayout(*[getattr(self, f).data_ptr() for f in self.FIELDS])
+
+    def numpy(self) -> Dict[str, np.ndarray]:
+        out = {f: getattr(self, f).cpu().numpy() for f in self.FIELDS}
+        out["sub_class"] = out["sub_class"].view(np.uint32)
+        return out
+
+
+def opr_build_layout(rows: Sequence, L: int, block_q: int = OPR_ATTN_BLOCK,
+                     block_k: int = OPR_ATTN_BLOCK, device="cuda",
+                     workspace: Optional[torch.Tensor] = None) -> Layout:
+    """rows: list of rows, each a list of conversations of (h, t, r_in, r_out) turns."""
+    device = torch.device(device)
+    B = len(rows)
+    cpr, tpc, turns = inputs.flatten_rows(rows)
+    C, T = len(tpc), len(turns)
+    lay = Layout(B, L, block_q, block_k, device)
+    need = opr_build_layout_workspace_size(B, L, C, T)
+    if need == 0:
+        raise OprError(OPR_E_INVALID, "opr_build_layout_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    cpr = np.ascontiguousarray(cpr, dtype=np.int32)
+    tpc = np.ascontiguousarray(tpc if C else np.zeros(1, np.int32), dtype=np.int32)
+    turns = np.ascontiguousarray(turns if T else np.zeros((1, 4), np.int32), dtype=np.int32)
+    out = lay.c_struct()
+    st = LIB.opr_build_layout(B, L, block_q, block_k, cpr.ctypes.data, tpc.ctypes.data,
+                              turns.ctypes.data, workspace.data_ptr(), workspace.numel(),
+                              ctypes.byref(out), _stream(device))
+    _check(st, "opr_build_layout")
+    return lay
+
+
+def _attn_in(q, k, v, lay: Layout, theta: float, scale: float) -> OprAttnIn:
+    B, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    for name, t, H in (("q", q, Hq), ("k", k, Hkv), ("v", v, Hkv)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != (B, L, H, D):
+            raise ValueError(f"{name} must be contiguous bfloat16 [B, L, H, D]")
+    if (lay.B, lay.L) != (B, L):
+        raise ValueError("layout built for a different B or L")
+    return OprAttnIn(B, L, Hq, Hkv, D, float(scale), float(theta), q.data_ptr(), k.data_ptr(),
+                     v.data_ptr(), lay.c_struct(), lay.block_q, lay.block_k)
+
+
+def opr_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lay: Layout,
+                 theta: float = 1.0e6, scale: float = 0.0,
+                 workspace: Optional[torch.Tensor] = None, out=None):
+    """Returns (o bf16 [B, L, Hq, D], lse fp32 [B, Hq, L])."""
+    a = _attn_in(q, k, v, lay, theta, scale)
+    B, L, Hq, D = q.shape
+    need = opr_attn_workspace_size(B, L, Hq, k.shape[2], D, False)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    st = LIB.opr_attn_fwd(ctypes.byref(a), o.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                          workspace.numel(), _stream(q.device))
+    _check(st, "opr_attn_fwd")
+    return o, lse
+
+
+def opr_attn_bwd(q, k, v, o, lse, dout, lay: Layout, theta: float = 1.0e6, scale: float = 0.0,
+                 workspace: Optional[torch.Tensor] = None, out=None):
+    """Returns (dq, dk, dv) fp32 with the shapes of q, k, v."""
+    a = _attn_in(q, k, v, lay, theta, scale)
+    B, L, Hq, D = q.shape
+    if dout.dtype != torch.bfloat16 or not dout.is_contiguous() or dout.shape != q.shape:
+        raise ValueError("dout must be contiguous bfloat16 shaped like q")
+    need = opr_attn_workspace_size(B, L, Hq, k.shape[2], D, True)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv = out
+    st = LIB.opr_attn_bwd(ctypes.byref(a), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                          workspace.numel(), _stream(q.device))
+    _check(st, "opr_attn_bwd")
+    return dq, dk, dv

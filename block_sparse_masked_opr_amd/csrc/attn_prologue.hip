@@ -1,0 +1,166 @@
+// Prologue kernels of the attention path: the RoPE table at the strategic
+// position ids, head-major (optionally rotated) copies of q / k / v / dout, and
+// their transposes, all padded to a whole number of 128-token tiles with
+// zeros; plus the backward preprocessing delta = rowsum(dout * o).
+//
+// RoPE (rotate-half): pair (j, j + D/2) of a head vector is rotated by
+// pos * theta^(-2j/D).  The angle and its cosine and sine are computed in
+// float64 (positions reach ~2.4e5, where a float32 angle would be off by
+// ~1e-2 rad); the rotation itself runs in float32.
+#include "attn_common.h"
+#include "opr_internal.h"
+
+namespace opr {
+namespace {
+
+// table[b][t][j] = (cos, sin) of pos(b, t) * theta^(-2j/D); PAD and t >= L use 0.
+__global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, int32_t Lp,
+                                                         int32_t half, double log2_theta,
+                                                         const int32_t *tok_pos, float2 *table) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)B * Lp * half;
+  if (gid >= total) return;
+  const int32_t j = (int32_t)(gid % half);
+  const int64_t bt = gid / half;
+  const int32_t t = (int32_t)(bt % Lp);
+  const int32_t b = (int32_t)(bt / Lp);
+  const int32_t pos = t < L ? tok_pos[(int64_t)b * L + t] : 0;
+  const double inv_freq = exp2(-(2.0 * j / (2.0 * half)) * log2_theta);
+  double s, c;
+  sincos((double)pos * inv_freq, &s, &c);
+  table[gid] = make_float2((float)c, (float)s);
+}
+
+// One workgroup per (64-token block, head, row).  x: [B][L][H][D] bf16.
+// rows (optional): [B][H][Lp][D]; trans (optional): [B][H][D][Lp].
+template <int D, bool ROPE>
+__global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H,
+                                                   const uint16_t *x, const float2 *table,
+                                                   uint16_t *rows, uint16_t *trans) {
+  constexpr int HALF = D / 2;
+  constexpr int PER = HALF / 4;           // pairs per thread (4 threads per token)
+  constexpr int TS = 64 + 8;              // LDS row stride of the transposed tile
+  __shared__ __attribute__((aligned(16))) uint16_t tile[D * TS];
+  const int t0 = blockIdx.x * 64;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int tt = tid >> 2, part = tid & 3;
+  const int t = t0 + tt;
+  const int j0 = part * PER;
+  uint16_t lo[PER], hi[PER];
+  if (t < L) {
+    const uint16_t *src = x + (((int64_t)b * L + t) * H + h) * D;
+#pragma unroll
+    for (int c = 0; c < PER; c += 8) {
+      *reinterpret_cast<uint4 *>(&lo[c]) = *reinterpret_cast<const uint4 *>(src + j0 + c);
+      *reinterpret_cast<uint4 *>(&hi[c]) = *reinterpret_cast<const uint4 *>(src + HALF + j0 + c);
+    }
+    if (ROPE) {
+      const float2 *cs = table + ((int64_t)b * Lp + t) * HALF + j0;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const float2 r = cs[e];
+        const float x1 = bf16_to_f32(lo[e]), x2 = bf16_to_f32(hi[e]);
+        lo[e] = f32_to_bf16(x1 * r.x - x2 * r.y);
+        hi[e] = f32_to_bf16(x2 * r.x + x1 * r.y);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) lo[e] = hi[e] = 0;
+  }
+  if (rows) {
+    uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
+#pragma unroll
+    for (int c = 0; c < PER; c += 8) {
+      *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lo[c]);
+      *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hi[c]);
+    }
+  }
+  if (trans) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      tile[(j0 + e) * TS + tt] = lo[e];
+      tile[(HALF + j0 + e) * TS + tt] = hi[e];
+    }
+    __syncthreads();
+    // D rows of 64 tokens (128 bytes = 8 chunks of 16 bytes)
+    for (int c = tid; c < D * 8; c += 256) {
+      const int d = c >> 3, ch = c & 7;
+      uint16_t *dst = trans + (((int64_t)b * H + h) * D + d) * Lp + t0 + ch * 8;
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&tile[d * TS + ch * 8]);
+    }
+  }
+}
+
+// delta[b][h][t] = sum_d dout * o (float32 over bf16 inputs);
+// lse2[b][h][t] = lse * log2(e), +inf where the row has no key (lse = -inf)
+// or t >= L, so that recomputed probabilities are exactly 0 there.
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_t Lp, int32_t Hq,
+                                                    const uint16_t *o, const uint16_t *dout,
+                                                    const float *lse, float *delta, float *lse2) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, t, h)
+  if (gid >= (int64_t)B * Lp * Hq) return;
+  const int32_t h = (int32_t)(gid % Hq);
+  const int64_t bt = gid / Hq;
+  const int32_t t = (int32_t)(bt % Lp);
+  const int32_t b = (int32_t)(bt / Lp);
+  float acc = 0.0f, l2 = INFINITY;
+  if (t < L) {
+    const int64_t base = (((int64_t)b * L + t) * Hq + h) * D;
+#pragma unroll
+    for (int c = 0; c < D; c += 8) {
+      uint16_t ov[8], dv[8];
+      *reinterpret_cast<uint4 *>(ov) = *reinterpret_cast<const uint4 *>(o + base + c);
+      *reinterpret_cast<uint4 *>(dv) = *reinterpret_cast<const uint4 *>(dout + base + c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += bf16_to_f32(ov[e]) * bf16_to_f32(dv[e]);
+    }
+    const float l = lse[((int64_t)b * Hq + h) * L + t];
+    l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  }
+  const int64_t out = ((int64_t)b * Hq + h) * Lp + t;
+  delta[out] = acc;
+  lse2[out] = l2;
+}
+
+template <int D>
+void launch_pack(bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x,
+                 const float2 *table, uint16_t *rows, uint16_t *trans, hipStream_t s) {
+  const dim3 grid(Lp / 64, H, B);
+  const uint16_t *src = static_cast<const uint16_t *>(x);
+  if (rope)
+    pack_kernel<D, true><<<grid, 256, 0, s>>>(L, Lp, H, src, table, rows, trans);
+  else
+    pack_kernel<D, false><<<grid, 256, 0, s>>>(L, Lp, H, src, table, rows, trans);
+}
+
+}  // namespace
+
+void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+  const int32_t half = in.D / 2;
+  const int64_t total = (int64_t)in.B * ws.Lp * half;
+  rope_table_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
+      in.B, in.L, ws.Lp, half, log2(in.rope_theta), in.layout.tok_pos, ws.rope);
+}
+
+void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x,
+                     const float2 *table, uint16_t *rows, uint16_t *trans, hipStream_t s) {
+  if (D == 64) launch_pack<64>(rope, B, L, Lp, H, x, table, rows, trans, s);
+  else launch_pack<128>(rope, B, L, Lp, H, x, table, rows, trans, s);
+}
+
+void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
+                  const AttnWs &ws, hipStream_t s) {
+  const int64_t total = (int64_t)in.B * ws.Lp * in.Hq;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const uint16_t *o16 = static_cast<const uint16_t *>(o);
+  const uint16_t *d16 = static_cast<const uint16_t *>(dout);
+  if (in.D == 64)
+    delta_kernel<64><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, ws.delta, ws.lse2);
+  else
+    delta_kernel<128><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, ws.delta, ws.lse2);
+}
+
+}  // namespace opr

@@ -1,0 +1,243 @@
+// Host entry points of libopr: argument validation (before any HIP call),
+// workspace carving and kernel launch order.  See include/opr.h.
+#include <math.h>
+#include <string.h>
+
+#include "attn_common.h"
+#include "opr_internal.h"
+
+namespace opr {
+
+// launchers defined in the .hip files
+void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
+void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x,
+                     const float2 *table, uint16_t *rows, uint16_t *trans, hipStream_t s);
+void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
+                  const AttnWs &ws, hipStream_t s);
+hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, float *lse,
+                                  const AttnWs &ws, hipStream_t s);
+hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq, float *dk,
+                                   float *dv, const AttnWs &ws, hipStream_t s);
+
+static bool valid_block(int32_t b) { return b == 32 || b == 64 || b == 128; }
+
+size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
+  Carver cv(p);
+  AttnWs w;
+  memset(&w, 0, sizeof(w));
+  const int64_t Lp = (int64_t)(in.L + OPR_ATTN_BLOCK - 1) / OPR_ATTN_BLOCK * OPR_ATTN_BLOCK;
+  const size_t qn = (size_t)in.B * in.Hq * Lp * in.D;
+  const size_t kn = (size_t)in.B * in.Hkv * Lp * in.D;
+  w.Lp = (int32_t)Lp;
+  w.rope = cv.take<float2>((size_t)in.B * Lp * (in.D / 2));
+  w.qr = cv.take<uint16_t>(qn);
+  w.kr = cv.take<uint16_t>(kn);
+  if (!is_bwd) {
+    w.vt = cv.take<uint16_t>(kn);
+  } else {
+    w.vr = cv.take<uint16_t>(kn);
+    w.qt = cv.take<uint16_t>(qn);
+    w.kt = cv.take<uint16_t>(kn);
+    w.dor = cv.take<uint16_t>(qn);
+    w.dot = cv.take<uint16_t>(qn);
+    w.delta = cv.take<float>((size_t)in.B * in.Hq * Lp);
+    w.lse2 = cv.take<float>((size_t)in.B * in.Hq * Lp);
+  }
+  if (o) *o = w;
+  return cv.off;
+}
+
+void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParams *p) {
+  p->B = in.B;
+  p->L = in.L;
+  p->Lp = ws.Lp;
+  p->Hq = in.Hq;
+  p->Hkv = in.Hkv;
+  p->group = in.Hq / in.Hkv;
+  p->MT = ws.Lp / OPR_ATTN_BLOCK;
+  p->NT = ws.Lp / OPR_ATTN_BLOCK;
+  p->scale = scale;
+  p->scale_log2 = scale * kLog2e;
+  p->tok_conv = in.layout.tok_conv;
+  p->tok_turn = in.layout.tok_turn;
+  p->tok_pos = in.layout.tok_pos;
+  p->tok_type = in.layout.tok_type;
+  p->tile_class = in.layout.tile_class;
+  p->sub_class = in.layout.sub_class;
+  p->q_nnz = in.layout.q_nnz;
+  p->q_list = in.layout.q_list;
+  p->k_nnz = in.layout.k_nnz;
+  p->k_list = in.layout.k_list;
+  p->rope = ws.rope;
+  p->qr = ws.qr;
+  p->kr = ws.kr;
+  p->vt = ws.vt;
+  p->vr = ws.vr;
+  p->qt = ws.qt;
+  p->kt = ws.kt;
+  p->dor = ws.dor;
+  p->dot = ws.dot;
+  p->delta = ws.delta;
+  p->lse2 = ws.lse2;
+}
+
+// Shape checks shared by the attention entry points and the size query.
+static opr_status check_attn_shape(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D) {
+  if (B < 1 || L < 1 || Hq < 1 || Hkv < 1 || D < 1) return OPR_E_INVALID;
+  if (Hq % Hkv != 0) return OPR_E_INVALID;
+  if (D != 64 && D != 128) return OPR_E_UNSUPPORTED;
+  if (B > 65535 || Hq > 65535) return OPR_E_UNSUPPORTED;  // grid dimensions
+  const int64_t Lp = ((int64_t)L + OPR_ATTN_BLOCK - 1) / OPR_ATTN_BLOCK * OPR_ATTN_BLOCK;
+  // every element index of the largest tensor must fit in int64 with room;
+  // row indices (b*L + t) are kept in int32 by the layout
+  if ((int64_t)B * Lp >= (int64_t)1 << 31) return OPR_E_UNSUPPORTED;
+  if (Lp / OPR_ATTN_BLOCK > 65535) return OPR_E_UNSUPPORTED;
+  return OPR_OK;
+}
+
+static opr_status check_attn_in(const opr_attn_in *in) {
+  if (!in) return OPR_E_INVALID;
+  const opr_status st = check_attn_shape(in->B, in->L, in->Hq, in->Hkv, in->D);
+  if (st != OPR_OK) return st;
+  if (!in->q || !in->k || !in->v) return OPR_E_INVALID;
+  const opr_layout &l = in->layout;
+  if (!l.tok_conv || !l.tok_turn || !l.tok_pos || !l.tok_type || !l.tile_class || !l.sub_class ||
+      !l.q_nnz || !l.q_list || !l.k_nnz || !l.k_list)
+    return OPR_E_INVALID;
+  if (!(in->rope_theta > 0.0) || !isfinite(in->rope_theta)) return OPR_E_INVALID;
+  if (!(in->softmax_scale >= 0.0f) || !isfinite(in->softmax_scale)) return OPR_E_INVALID;
+  if (in->block_q != OPR_ATTN_BLOCK || in->block_k != OPR_ATTN_BLOCK) return OPR_E_UNSUPPORTED;
+  return OPR_OK;
+}
+
+static float effective_scale(const opr_attn_in *in) {
+  return in->softmax_scale > 0.0f ? in->softmax_scale : 1.0f / sqrtf((float)in->D);
+}
+
+static opr_status hip_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? OPR_OK : OPR_E_HIP;
+}
+
+}  // namespace opr
+
+using namespace opr;
+
+extern "C" {
+
+size_t opr_build_layout_workspace_size(int32_t B, int32_t L, int32_t n_convs, int32_t n_turns) {
+  if (B < 1 || L < 1 || n_convs < 0 || n_turns < 0) return 0;
+  if ((int64_t)B * L >= (int64_t)1 << 31) return 0;
+  return carve_layout_ws(nullptr, B, L, n_convs, n_turns, nullptr);
+}
+
+opr_status opr_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
+                            const int32_t *convs_per_row, const int32_t *turns_per_conv,
+                            const opr_turn *turns, void *workspace, size_t ws_bytes,
+                            const opr_layout *out, hipStream_t stream) {
+  if (B < 1 || L < 1) return OPR_E_INVALID;
+  if ((int64_t)B * L >= (int64_t)1 << 31) return OPR_E_UNSUPPORTED;
+  if (!valid_block(block_q) || !valid_block(block_k)) return OPR_E_UNSUPPORTED;
+  if (!convs_per_row || !workspace || !out) return OPR_E_INVALID;
+  if (!out->tok_conv || !out->tok_turn || !out->tok_pos || !out->tok_type || !out->tile_class ||
+      !out->sub_class || !out->q_nnz || !out->q_list || !out->k_nnz || !out->k_list)
+    return OPR_E_INVALID;
+  const int64_t MT = ((int64_t)L + block_q - 1) / block_q, NT = ((int64_t)L + block_k - 1) / block_k;
+  if ((int64_t)B * MT * NT >= (int64_t)1 << 31) return OPR_E_UNSUPPORTED;
+  // count conversations and turns, check every length and each row's capacity
+  int64_t C = 0, T = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (convs_per_row[b] < 0) return OPR_E_INVALID;
+    C += convs_per_row[b];
+    if (C >= (int64_t)1 << 30) return OPR_E_INVALID;
+  }
+  if (C > 0 && !turns_per_conv) return OPR_E_INVALID;
+  int64_t c = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    int64_t row_tokens = 0;
+    for (int32_t i = 0; i < convs_per_row[b]; ++i, ++c) {
+      const int32_t nt = turns_per_conv[c];
+      if (nt < 0) return OPR_E_INVALID;
+      if (nt > 0 && !turns) return OPR_E_INVALID;
+      for (int32_t j = 0; j < nt; ++j) {
+        const opr_turn &u = turns[T + j];
+        if (u.h < 0 || u.t < 0 || u.r_in < 0 || u.r_out < 0) return OPR_E_INVALID;
+        row_tokens += (int64_t)u.h + u.t + u.r_in + u.r_out;
+        if (row_tokens > L) return OPR_E_CAPACITY;
+      }
+      T += nt;
+      if (T >= (int64_t)1 << 30) return OPR_E_INVALID;
+    }
+  }
+  const size_t need = carve_layout_ws(nullptr, B, L, (int32_t)C, (int32_t)T, nullptr);
+  if (ws_bytes < need) return OPR_E_CAPACITY;
+
+  LayoutWs ws;
+  carve_layout_ws(workspace, B, L, (int32_t)C, (int32_t)T, &ws);
+  if (hipMemcpyAsync(ws.cpr, convs_per_row, sizeof(int32_t) * B, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return OPR_E_HIP;
+  if (C > 0 && hipMemcpyAsync(ws.tpc, turns_per_conv, sizeof(int32_t) * C, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return OPR_E_HIP;
+  if (T > 0 && hipMemcpyAsync(ws.turns, turns, sizeof(opr_turn) * T, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return OPR_E_HIP;
+  if (launch_build_layout(B, L, block_q, block_k, (int32_t)C, (int32_t)T, ws, *out, stream) != hipSuccess)
+    return OPR_E_HIP;
+  return hip_status();
+}
+
+size_t opr_attn_workspace_size(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int is_bwd) {
+  if (check_attn_shape(B, L, Hq, Hkv, D) != OPR_OK) return 0;
+  opr_attn_in in;
+  memset(&in, 0, sizeof(in));
+  in.B = B; in.L = L; in.Hq = Hq; in.Hkv = Hkv; in.D = D;
+  return carve_attn_ws(nullptr, in, is_bwd ? 1 : 0, nullptr);
+}
+
+opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *workspace, size_t ws_bytes,
+                        hipStream_t stream) {
+  const opr_status st = check_attn_in(in);
+  if (st != OPR_OK) return st;
+  if (!o || !lse || !workspace) return OPR_E_INVALID;
+  if (ws_bytes < carve_attn_ws(nullptr, *in, 0, nullptr)) return OPR_E_CAPACITY;
+  AttnWs ws;
+  carve_attn_ws(workspace, *in, 0, &ws);
+  launch_rope_table(*in, ws, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, nullptr, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, nullptr, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, nullptr, ws.vt, stream);
+  if (launch_attn_fwd_kernel(*in, effective_scale(in), o, lse, ws, stream) != hipSuccess) return OPR_E_HIP;
+  return hip_status();
+}
+
+opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, const void *dout,
+                        float *dq, float *dk, float *dv, void *workspace, size_t ws_bytes,
+                        hipStream_t stream) {
+  const opr_status st = check_attn_in(in);
+  if (st != OPR_OK) return st;
+  if (!o || !lse || !dout || !dq || !dk || !dv || !workspace) return OPR_E_INVALID;
+  if (ws_bytes < carve_attn_ws(nullptr, *in, 1, nullptr)) return OPR_E_CAPACITY;
+  AttnWs ws;
+  carve_attn_ws(workspace, *in, 1, &ws);
+  launch_rope_table(*in, ws, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, ws.qt, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, ws.kt, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, ws.vr, nullptr, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, dout, nullptr, ws.dor, ws.dot, stream);
+  launch_delta(*in, o, dout, lse, ws, stream);
+  if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream) != hipSuccess)
+    return OPR_E_HIP;
+  return hip_status();
+}
+
+const char *opr_status_string(opr_status s) {
+  switch (s) {
+    case OPR_OK: return "OPR_OK";
+    case OPR_E_INVALID: return "OPR_E_INVALID: invalid argument";
+    case OPR_E_CAPACITY: return "OPR_E_CAPACITY: row longer than L or workspace too small";
+    case OPR_E_UNSUPPORTED: return "OPR_E_UNSUPPORTED: size or option not supported";
+    case OPR_E_HIP: return "OPR_E_HIP: HIP launch or call failed";
+  }
+  return "unknown opr_status";
+}
+
+}  // extern "C"

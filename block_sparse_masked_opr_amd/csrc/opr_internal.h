@@ -1,0 +1,77 @@
+// Internal declarations shared by the host entry points (opr_api.cpp) and the
+// kernel launchers (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "opr.h"
+
+namespace opr {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Carves consecutive, 256-byte aligned pieces out of a workspace.
+struct Carver {
+  char *base;
+  size_t off = 0;
+  explicit Carver(void *p) : base(static_cast<char *>(p)) {}
+  template <class T>
+  T *take(size_t count) {
+    T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+// ---------------------------------------------------------------- layout
+struct LayoutWs {
+  int32_t *cpr;         // [B]   convs per row (copied from the host)
+  int32_t *tpc;         // [C]   turns per conversation (copied)
+  int4 *turns;          // [T]   (h, t, r_in, r_out) (copied)
+  int32_t *row_conv0;   // [B+1] first conversation of each row
+  int32_t *conv_turn0;  // [C+1] first turn of each conversation
+  int32_t *tok_g;       // [T+1] tokens before each turn, counted over all rows
+  int32_t *pos_g;       // [T+1] sum of (h + r_in) before each turn, over all rows
+  int32_t *conv_row;    // [C]   row of each conversation
+  int32_t *turn_conv;   // [T]   conversation of each turn
+  int32_t *row_turn0;   // [B+1] first turn of each row
+  int32_t *gturn;       // [B][L] turn of each token (-1 for PAD)
+};
+
+// Carves the layout workspace; with ws == nullptr only the size is computed.
+size_t carve_layout_ws(void *ws, int32_t B, int32_t L, int32_t C, int32_t T, LayoutWs *out);
+
+hipError_t launch_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
+                               int32_t C, int32_t T, const LayoutWs &ws, const opr_layout &out,
+                               hipStream_t stream);
+
+// ---------------------------------------------------------------- attention
+struct AttnWs {
+  int32_t Lp;           // L rounded up to OPR_ATTN_BLOCK
+  float2 *rope;         // [B][Lp][D/2] (cos, sin) at each token's position id
+  uint16_t *qr;         // [B][Hq][Lp][D]  q after RoPE, head-major, zero past L
+  uint16_t *kr;         // [B][Hkv][Lp][D] k after RoPE
+  uint16_t *vt;         // [B][Hkv][D][Lp] v transposed                (fwd)
+  uint16_t *vr;         // [B][Hkv][Lp][D] v head-major                (bwd)
+  uint16_t *qt;         // [B][Hq][D][Lp]  q after RoPE, transposed    (bwd)
+  uint16_t *kt;         // [B][Hkv][D][Lp] k after RoPE, transposed    (bwd)
+  uint16_t *dor;        // [B][Hq][Lp][D]  dout head-major             (bwd)
+  uint16_t *dot;        // [B][Hq][D][Lp]  dout transposed             (bwd)
+  float *delta;         // [B][Hq][Lp] rowsum(dout * o)                (bwd)
+  float *lse2;          // [B][Hq][Lp] log2-domain lse, +inf where no key (bwd)
+};
+
+size_t carve_attn_ws(void *ws, const opr_attn_in &in, int is_bwd, AttnWs *out);
+
+hipError_t launch_attn_fwd(const opr_attn_in &in, float scale, void *o, float *lse,
+                           const AttnWs &ws, hipStream_t stream);
+
+hipError_t launch_attn_bwd(const opr_attn_in &in, float scale, const void *o, const float *lse,
+                           const void *dout, float *dq, float *dk, float *dv, const AttnWs &ws,
+                           hipStream_t stream);
+
+}  // namespace opr

@@ -1,0 +1,182 @@
+/*
+ * opr.h - C ABI of libopr: one-pass block-sparse masked attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is One-Pass to Reason (Goru, Mehta, Jain; arXiv 2504.18246).
+ * A multi-turn reasoning conversation is packed once: every turn i holds the
+ * human message h_i, the reasoning t_i, and the response stored twice, as a
+ * context copy r_in_i and a generation copy r_out_i (wiki summary of the
+ * paper, section "Token 复制" / token duplication).  A block-sparse mask
+ * (section "分块稀疏注意力掩码") lets
+ *     h_i     see H_<i,
+ *     t_i     see H_<i and h_i,
+ *     r_in_i  see H_<i and h_i,
+ *     r_out_i see H_<i, h_i and t_i,
+ * where H_<i is the human messages and context copies of the earlier turns,
+ * and every token sees its own segment causally.  Position ids (section
+ * "位置 ID 策略") start t_i and r_in_i right after h_i, r_out_i right after
+ * t_i, and h_{i+1} right after r_in_i, so that one pass gives the same
+ * per-token results as the N separate causal passes (section "理论保证",
+ * Theorem 2.1).  Packed conversations (section "实现细节") never see each
+ * other and each starts at position 0.
+ *
+ * Conventions for every entry point
+ *  - Pointers are device pointers unless the comment says "host".  The caller
+ *    allocates and owns every buffer, including the workspace; the library
+ *    never allocates or frees memory and never synchronises the stream.
+ *  - All arguments are validated on the host before any HIP call.  On a
+ *    validation failure the call returns an error status, writes nothing and
+ *    enqueues nothing.
+ *  - Work is enqueued on `stream` in order; outputs are ready when the stream
+ *    reaches that point.  A failed launch returns OPR_E_HIP (the HIP error is
+ *    read with hipGetLastError and cleared).
+ *  - Concurrent calls on different streams must use different workspaces.
+ *  - Row-major layouts are written [dim0][dim1]...; "bf16" is IEEE bfloat16.
+ */
+#ifndef OPR_H
+#define OPR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OPR_OK = 0,
+  OPR_E_INVALID = -1,     /* null pointer, negative length, inconsistent sizes */
+  OPR_E_CAPACITY = -2,    /* a row needs more than L tokens, or workspace too small */
+  OPR_E_UNSUPPORTED = -3, /* well-formed but not implemented (head dim, tile size) */
+  OPR_E_HIP = -4          /* a HIP call or kernel launch failed */
+} opr_status;
+
+/* Token types, in their order inside a turn. */
+enum { OPR_TOK_H = 0, OPR_TOK_T = 1, OPR_TOK_RIN = 2, OPR_TOK_ROUT = 3, OPR_TOK_PAD = 4 };
+
+/* Tile classes: no allowed pair / some / all (entries past L count as masked). */
+enum { OPR_TILE_EMPTY = 0, OPR_TILE_PARTIAL = 1, OPR_TILE_FULL = 2 };
+
+/* Sub-block edge of the sub-block classes, in tokens. */
+#define OPR_SUB_BLOCK 32
+
+/* Attention tile the kernels run on: opr_attn_* need a layout built with
+ * block_q == block_k == OPR_ATTN_BLOCK. */
+#define OPR_ATTN_BLOCK 128
+
+/* Segment lengths of one turn, each >= 0.  An ordinary turn has
+ * r_in == r_out (the response stored twice); a history-only turn of a K-pass
+ * chunk is (h, 0, r, 0) and the last turn of an N-pass sequence (h, t, 0, r). */
+typedef struct {
+  int32_t h, t, r_in, r_out;
+} opr_turn;
+
+/* Outputs of opr_build_layout for B rows of L tokens and block_q x block_k
+ * tiles; MT = ceil(L / block_q), NT = ceil(L / block_k). */
+typedef struct {
+  int32_t *tok_conv;   /* [B][L] conversation index within the row; -1 for PAD */
+  int32_t *tok_turn;   /* [B][L] turn index within the conversation; -1 for PAD */
+  int32_t *tok_pos;    /* [B][L] strategic position id; 0 for PAD */
+  uint8_t *tok_type;   /* [B][L] OPR_TOK_* */
+  uint8_t *tile_class; /* [B][MT][NT] OPR_TILE_* */
+  uint32_t *sub_class; /* [B][MT][NT] two bits per 32x32 sub-block (i, j) at bit
+                          2*(i*(block_k/32) + j), same codes as tile_class */
+  int32_t *q_nnz;      /* [B][MT] number of non-empty tiles in q-tile row m */
+  int32_t *q_list;     /* [B][MT][NT] their k-tile indices ascending, then -1 */
+  int32_t *k_nnz;      /* [B][NT] number of non-empty tiles in k-tile column n */
+  int32_t *k_list;     /* [B][NT][MT] their q-tile indices ascending, then -1 */
+} opr_layout;
+
+/*
+ * opr_build_layout - token layout, position ids and tile schedule.
+ *
+ * Packs each row's conversations back to back (segments of a turn in the
+ * order h, t, r_in, r_out; the rest of the row is PAD), assigns the strategic
+ * position ids above, and classifies every block_q x block_k tile of the
+ * block-sparse mask as empty / partial / full, with 32x32 sub-block classes
+ * and the per-row and per-column lists of non-empty tiles.  Everything is
+ * computed on the device from the segment lengths; no dense mask is formed.
+ *
+ *  B, L            rows and tokens per row; B >= 1, L >= 1, B*L < 2^31.
+ *  block_q/block_k tile edges, each 32, 64 or 128.
+ *  convs_per_row   host [B], >= 0.  turns_per_conv host [sum convs_per_row],
+ *                  >= 0.  turns host [sum turns_per_conv].  Conversations are
+ *                  listed row by row, turns conversation by conversation.
+ *  workspace       device, at least opr_build_layout_workspace_size(...) bytes.
+ *  out             host struct of device pointers, all non-NULL.
+ * Errors: OPR_E_INVALID (null pointer, negative count or length, bad B/L),
+ * OPR_E_UNSUPPORTED (block size), OPR_E_CAPACITY (a row longer than L, or
+ * ws_bytes too small), OPR_E_HIP.  The host arrays are copied to the
+ * workspace with hipMemcpyAsync before the call returns control.
+ */
+opr_status opr_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
+                            const int32_t *convs_per_row, const int32_t *turns_per_conv,
+                            const opr_turn *turns, void *workspace, size_t ws_bytes,
+                            const opr_layout *out, hipStream_t stream);
+
+/* Workspace bytes for opr_build_layout with n_convs conversations and n_turns
+ * turns in total (the sums of convs_per_row and turns_per_conv). */
+size_t opr_build_layout_workspace_size(int32_t B, int32_t L, int32_t n_convs, int32_t n_turns);
+
+/* Inputs shared by the forward and backward calls. */
+typedef struct {
+  int32_t B, L, Hq, Hkv, D; /* D in {64, 128}; Hq % Hkv == 0; q head h reads kv
+                               head h / (Hq / Hkv) (grouped-query attention) */
+  float softmax_scale;      /* 0 selects 1/sqrt(D) */
+  double rope_theta;        /* RoPE base; > 0 */
+  const void *q;            /* bf16 [B][L][Hq][D], before RoPE */
+  const void *k;            /* bf16 [B][L][Hkv][D], before RoPE */
+  const void *v;            /* bf16 [B][L][Hkv][D] */
+  opr_layout layout;        /* from opr_build_layout(B, L, block_q, block_k, ...) */
+  int32_t block_q, block_k; /* must both be OPR_ATTN_BLOCK */
+} opr_attn_in;
+
+/*
+ * opr_attn_fwd - masked attention forward.
+ *
+ * RoPE (rotate-half pairs (j, j + D/2), angle pos * theta^(-2j/D)) is applied
+ * to q and k at the layout's position ids; then for every query token and q
+ * head, softmax(scale * q k^T) over exactly the keys the mask allows, times v.
+ * Empty tiles are skipped, full tiles run without a mask, partial tiles test
+ * the mask per element from the per-token (conversation, turn, type).
+ *
+ *  o    bf16 [B][L][Hq][D]   attention output; PAD rows get 0.
+ *  lse  fp32 [B][Hq][L]      natural-log sum of exp of the scaled scores of
+ *                            the allowed keys; -inf for PAD rows.
+ *  workspace  >= opr_attn_workspace_size(B, L, Hq, Hkv, D, 0) bytes.
+ * Errors: OPR_E_INVALID, OPR_E_UNSUPPORTED (D, block sizes), OPR_E_CAPACITY
+ * (ws_bytes), OPR_E_HIP.
+ */
+opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *workspace,
+                        size_t ws_bytes, hipStream_t stream);
+
+/*
+ * opr_attn_bwd - gradients of sum(o * dout) with respect to q, k and v
+ * (before RoPE: the RoPE rotation is transposed back onto dq and dk).
+ *
+ *  o, lse  the outputs of opr_attn_fwd for the same inputs.
+ *  dout    bf16 [B][L][Hq][D].
+ *  dq      fp32 [B][L][Hq][D];  dk, dv  fp32 [B][L][Hkv][D].  Every element
+ *          is written (PAD rows get 0); nothing is accumulated into them.
+ *  workspace  >= opr_attn_workspace_size(B, L, Hq, Hkv, D, 1) bytes.
+ * Errors as for opr_attn_fwd.
+ */
+opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse,
+                        const void *dout, float *dq, float *dk, float *dv,
+                        void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for opr_attn_fwd (is_bwd = 0) or opr_attn_bwd (is_bwd = 1);
+ * 0 if the sizes are invalid. */
+size_t opr_attn_workspace_size(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D,
+                               int is_bwd);
+
+/* Static, human-readable name of a status code. */
+const char *opr_status_string(opr_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OPR_H */

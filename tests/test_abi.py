@@ -1,0 +1,125 @@
+"""The C ABI on a host without a GPU: libopr.so loads, exports every entry
+point that include/opr.h declares, and rejects bad arguments with the
+documented status before any HIP call (fake device pointers are never touched
+on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "opr.h")
+
+
+@pytest.fixture(scope="module")
+def Bd():
+    import torch
+    # fake device pointers must never meet a real device: these checks are for
+    # hosts without a GPU (a mistake in a case would otherwise reach the GPU)
+    if torch.cuda.device_count() > 0:
+        pytest.skip("host-only ABI checks run where no GPU is visible")
+    from block_sparse_masked_opr_amd import binding
+    return binding
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:opr_status|size_t|const char \*)\s*(opr_\w+)\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(Bd):
+    names = declared_entry_points()
+    assert len(names) == 6, names
+    lib = ctypes.CDLL(Bd._LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(Bd.EXPORTED) == names
+
+
+def test_status_strings(Bd):
+    for s in (0, -1, -2, -3, -4):
+        assert Bd.opr_status_string(s).startswith("OPR_")
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _layout_struct(Bd, null_field=None):
+    lay = Bd.OprLayout(*[FAKE] * 10)
+    if null_field:
+        setattr(lay, null_field, None)
+    return lay
+
+
+def _build(Bd, B=1, L=64, bq=128, bk=128, cpr=(1,), tpc=(1,), turns=((8, 12, 6, 6),),
+           ws_bytes=1 << 30, out=None, ws=FAKE):
+    cpr_a = (ctypes.c_int32 * max(1, len(cpr)))(*cpr)
+    tpc_a = (ctypes.c_int32 * max(1, len(tpc)))(*tpc)
+    turns_a = (Bd.OprTurn * max(1, len(turns)))(*[Bd.OprTurn(*t) for t in turns])
+    out = _layout_struct(Bd) if out is None else out
+    return Bd.LIB.opr_build_layout(B, L, bq, bk, ctypes.addressof(cpr_a), ctypes.addressof(tpc_a),
+                                   ctypes.addressof(turns_a), ws, ws_bytes, ctypes.byref(out), None)
+
+
+def test_build_layout_errors(Bd):
+    assert _build(Bd, B=0) == Bd.OPR_E_INVALID
+    assert _build(Bd, L=0) == Bd.OPR_E_INVALID
+    assert _build(Bd, bq=48) == Bd.OPR_E_UNSUPPORTED
+    assert _build(Bd, bk=256) == Bd.OPR_E_UNSUPPORTED
+    assert _build(Bd, cpr=(-1,)) == Bd.OPR_E_INVALID
+    assert _build(Bd, tpc=(-2,)) == Bd.OPR_E_INVALID
+    assert _build(Bd, turns=((8, -1, 6, 6),)) == Bd.OPR_E_INVALID
+    assert _build(Bd, L=31) == Bd.OPR_E_CAPACITY                      # 32 tokens > L
+    assert _build(Bd, L=60, cpr=(2,), tpc=(1, 2), turns=((8, 12, 6, 6), (8, 12, 6, 6), (1, 1, 1, 1))) \
+        == Bd.OPR_E_CAPACITY                                          # 32 + 36 tokens > 60
+    assert _build(Bd, ws_bytes=16) == Bd.OPR_E_CAPACITY
+    assert _build(Bd, ws=None) == Bd.OPR_E_INVALID
+    assert _build(Bd, out=_layout_struct(Bd, "q_list")) == Bd.OPR_E_INVALID
+    assert _build(Bd, B=1 << 16, L=1 << 15, cpr=(0,) * (1 << 16)) == Bd.OPR_E_UNSUPPORTED
+
+
+def test_layout_workspace_size(Bd):
+    assert Bd.opr_build_layout_workspace_size(1, 64, 1, 2) > 0
+    assert Bd.opr_build_layout_workspace_size(0, 64, 1, 2) == 0
+    assert Bd.opr_build_layout_workspace_size(1, 64, -1, 2) == 0
+
+
+def _attn_in(Bd, **kw):
+    a = dict(B=1, L=256, Hq=4, Hkv=2, D=128, softmax_scale=0.0, rope_theta=1e6,
+             q=FAKE, k=FAKE, v=FAKE, layout=_layout_struct(Bd), block_q=128, block_k=128)
+    a.update(kw)
+    return Bd.OprAttnIn(**a)
+
+
+def _fwd(Bd, ws_bytes=1 << 40, **kw):
+    a = _attn_in(Bd, **kw)
+    return Bd.LIB.opr_attn_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def _bwd(Bd, ws_bytes=1 << 40, dq=FAKE, **kw):
+    a = _attn_in(Bd, **kw)
+    return Bd.LIB.opr_attn_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, dq, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def test_attn_errors(Bd):
+    assert Bd.LIB.opr_attn_fwd(None, FAKE, FAKE, FAKE, 1 << 40, None) == Bd.OPR_E_INVALID
+    for f in (_fwd, _bwd):
+        assert f(Bd, D=96) == Bd.OPR_E_UNSUPPORTED
+        assert f(Bd, Hq=6, Hkv=4) == Bd.OPR_E_INVALID
+        assert f(Bd, block_q=64) == Bd.OPR_E_UNSUPPORTED
+        assert f(Bd, rope_theta=0.0) == Bd.OPR_E_INVALID
+        assert f(Bd, softmax_scale=-1.0) == Bd.OPR_E_INVALID
+        assert f(Bd, q=None) == Bd.OPR_E_INVALID
+        assert f(Bd, layout=_layout_struct(Bd, "sub_class")) == Bd.OPR_E_INVALID
+        assert f(Bd, ws_bytes=1024) == Bd.OPR_E_CAPACITY
+        assert f(Bd, B=0) == Bd.OPR_E_INVALID
+    assert _bwd(Bd, dq=None) == Bd.OPR_E_INVALID
+
+
+def test_attn_workspace_size(Bd):
+    f = Bd.opr_attn_workspace_size(2, 16384, 32, 8, 128, False)
+    b = Bd.opr_attn_workspace_size(2, 16384, 32, 8, 128, True)
+    assert 0 < f < b
+    assert Bd.opr_attn_workspace_size(1, 100, 3, 2, 128, False) == 0
+    assert Bd.opr_attn_workspace_size(1, 100, 4, 2, 80, True) == 0

@@ -1,0 +1,166 @@
+"""GPU parity of opr_attn_fwd / opr_attn_bwd against the fp64 oracle.
+
+Bar: max |x - ref| <= 2e-2 and sum|x - ref| / sum|ref| <= 5e-3 for O, LSE,
+dQ, dK, dV over non-PAD rows; PAD rows must be exactly O = 0, LSE = -inf and
+zero gradients.  Both sides consume the same bf16 inputs (the oracle upcasts).
+Full comparisons run at sizes the oracle finishes in seconds (several tiles,
+ragged L, GQA 1/2/4/8, D 64 and 128, empty segments, empty rows); the packed
+workloads are checked on whole sampled conversations (the mask is block
+diagonal by conversation, so their rows and keys depend on nothing else) and
+on complete kv-head groups.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from block_sparse_masked_opr_amd import inputs as I  # noqa: E402
+from oracle import opr_oracle as O  # noqa: E402
+from tests.helpers import assert_close, bf16_f64, from_device_bf16, to_device_bf16  # noqa: E402
+
+THETA = 1.0e6
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_sparse_masked_opr_amd import binding
+    return binding
+
+
+def run_gpu(Bd, rows, L, t, bwd=True):
+    dev = torch.device("cuda:0")
+    lay = Bd.opr_build_layout(rows, L, 128, 128, device=dev)
+    q, k, v = (to_device_bf16(t[n], dev) for n in ("q", "k", "v"))
+    o, lse = Bd.opr_attn_fwd(q, k, v, lay, THETA)
+    res = {"o": o, "lse": lse}
+    if bwd:
+        do = to_device_bf16(t["do"], dev)
+        res["dq"], res["dk"], res["dv"] = Bd.opr_attn_bwd(q, k, v, o, lse, do, lay, THETA)
+    torch.cuda.synchronize()
+    out = {"o": bf16_f64(from_device_bf16(res["o"])), "lse": res["lse"].cpu().numpy().astype(np.float64)}
+    if bwd:
+        for n in ("dq", "dk", "dv"):
+            out[n] = res[n].cpu().numpy().astype(np.float64)
+    return out
+
+
+def compare_full(label, rows, L, t, got, bwd=True):
+    lay = O.layout(rows, L)
+    q, k, v = (bf16_f64(t[n]) for n in ("q", "k", "v"))
+    o, lse = O.attn_fwd(q, k, v, lay, THETA)
+    pad = lay["type"] == O.PAD                      # [B, L]
+    live = ~pad
+    print(f"[attn] {label}", flush=True)
+    assert (got["o"][pad] == 0).all()
+    assert np.isneginf(got["lse"].transpose(0, 2, 1)[pad]).all()
+    assert_close("O", got["o"][live], o[live])
+    assert_close("LSE", got["lse"].transpose(0, 2, 1)[live], lse.transpose(0, 2, 1)[live])
+    if bwd:
+        dq, dk, dv = O.attn_bwd(q, k, v, bf16_f64(t["do"]), lay, THETA)
+        for n, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+            assert (got[n][pad] == 0).all(), n
+            assert_close(n, got[n][live], ref[live])
+
+
+def test_tiny(B):
+    rows = I.tiny_rows()
+    t = I.make_tensors(1, 64, 1, 1, 64, seed=I.SEEDS["tiny"][1])
+    compare_full("tiny", rows, 64, t, run_gpu(B, rows, 64, t))
+
+
+SMALL = [
+    # (label, seed, B, extra L, Hq, Hkv, D)
+    ("gqa2 d128 ragged", 1, 2, 37, 4, 2, 128),
+    ("mqa d64", 2, 1, 5, 8, 1, 64),
+    ("mha d128 one tile", 3, 3, 0, 2, 2, 128),
+    ("gqa8 d128", 4, 1, 200, 8, 1, 128),
+    ("gqa4 d64 long turns", 5, 2, 1, 4, 1, 64),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small(B, case):
+    label, seed, nb, extra, Hq, Hkv, D = case
+    rng = np.random.default_rng(seed)
+    rows = []
+    for _ in range(nb):
+        row = []
+        for _ in range(int(rng.integers(1, 4))):
+            turns = []
+            for _ in range(int(rng.integers(1, 4))):
+                lim = 180 if seed == 5 else 60
+                h, tt, r = (int(x) for x in rng.integers(0, lim, size=3))
+                turns.append((h, tt, r, r))
+            row.append(turns)
+        rows.append(row)
+    L = max(1, max(I.row_used(r) for r in rows)) + extra
+    t = I.make_tensors(nb, L, Hq, Hkv, D, seed=100 + seed)
+    compare_full(label, rows, L, t, run_gpu(B, rows, L, t))
+
+
+def test_empty_row_and_pad(B):
+    rows = [[], [[(40, 30, 20, 20), (10, 0, 5, 5)]]]
+    L = 260
+    t = I.make_tensors(2, L, 2, 1, 128, seed=77)
+    compare_full("empty row", rows, L, t, run_gpu(B, rows, L, t))
+
+
+def _group_subset(Hq, Hkv, groups):
+    g = Hq // Hkv
+    qh = [kv * g + j for kv in groups for j in range(g)]
+    return qh, list(groups)
+
+
+def compare_convs(label, rows, L, t, got, shape, convs_per_row=2, groups=(0, None), bwd=True):
+    """Whole sampled conversations, complete kv groups (first and last)."""
+    groups = tuple(shape.Hkv - 1 if gg is None else gg for gg in groups)
+    qh, kvh = _group_subset(shape.Hq, shape.Hkv, groups)
+    lay = O.layout(rows, L)
+    rng = np.random.default_rng(12345)
+    for b in range(len(rows)):
+        nc = O.n_convs(lay, b)
+        picks = sorted(set([0, nc - 1] + [int(x) for x in rng.integers(0, nc, size=convs_per_row)]))[:convs_per_row + 1]
+        for c in picks:
+            a, e = O.conv_range(lay, b, c)
+            sub = [[rows[b][c]]]
+            sl = {n: t[n][b:b + 1, a:e] for n in t}
+            q = bf16_f64(sl["q"][:, :, qh])
+            k = bf16_f64(sl["k"][:, :, kvh])
+            v = bf16_f64(sl["v"][:, :, kvh])
+            lay_c = O.layout(sub, e - a)
+            o, lse = O.attn_fwd(q, k, v, lay_c, THETA)
+            print(f"[attn] {label} row {b} conv {c} tokens {e - a}", flush=True)
+            assert_close("O", got["o"][b:b + 1, a:e][:, :, qh], o)
+            assert_close("LSE", got["lse"][b:b + 1][:, qh, a:e], lse)
+            if bwd:
+                dq, dk, dv = O.attn_bwd(q, k, v, bf16_f64(sl["do"][:, :, qh]), lay_c, THETA)
+                assert_close("dq", got["dq"][b:b + 1, a:e][:, :, qh], dq)
+                assert_close("dk", got["dk"][b:b + 1, a:e][:, :, kvh], dk)
+                assert_close("dv", got["dv"][b:b + 1, a:e][:, :, kvh], dv)
+
+
+def test_packed_fwd(B):
+    s = I.PACKED_FWD
+    seed_len, seed_t = I.SEEDS["packed_fwd"]
+    rows = I.packed_rows(s, seed_len)
+    t = I.make_tensors(s.B, s.L, s.Hq, s.Hkv, s.D, seed=seed_t, with_dout=False)
+    got = run_gpu(B, rows, s.L, t, bwd=False)
+    compare_convs("packed_fwd", rows, s.L, t, got, s, convs_per_row=3, bwd=False)
+
+
+def test_packed_fwd_bwd(B):
+    s = I.PACKED_FWD_BWD
+    seed_len, seed_t = I.SEEDS["packed_fwd_bwd"]
+    rows = I.packed_rows(s, seed_len)
+    t = I.make_tensors(s.B, s.L, s.Hq, s.Hkv, s.D, seed=seed_t)
+    got = run_gpu(B, rows, s.L, t)
+    # the PAD tail of each row
+    lay = O.layout(rows, s.L)
+    pad = lay["type"] == O.PAD
+    assert (got["o"][pad] == 0).all() and (got["dq"][pad] == 0).all()
+    assert (got["dk"][pad] == 0).all() and (got["dv"][pad] == 0).all()
+    compare_convs("packed_fwd_bwd", rows, s.L, t, got, s, convs_per_row=2)

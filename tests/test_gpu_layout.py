@@ -1,0 +1,107 @@
+"""GPU parity of opr_build_layout: bit-exact against the oracle.
+
+Tokens, turns, types, position ids, tile classes, 32x32 sub-block classes and
+both tile lists, on the worked example, random rows with empty segments,
+empty conversations and empty rows, ragged L, every supported tile shape, and
+the packed / depth / K-pass workloads.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from block_sparse_masked_opr_amd import inputs as I  # noqa: E402
+from oracle import opr_oracle as O  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_sparse_masked_opr_amd import binding
+    return binding
+
+
+def check_layout(B, rows, L, bq, bk, label):
+    print(f"[layout] {label} rows={len(rows)} L={L} tiles={bq}x{bk}", flush=True)
+    lay = B.opr_build_layout(rows, L, bq, bk)
+    torch.cuda.synchronize()
+    got = lay.numpy()
+    ref = O.layout(rows, L)
+    for f in ("conv", "turn", "type", "pos"):
+        np.testing.assert_array_equal(got["tok_" + f], ref[f], err_msg=f"tok_{f} {label}")
+    for b in range(len(rows)):
+        s = O.schedule(ref, b, bq, bk)
+        np.testing.assert_array_equal(got["tile_class"][b], s["tile_class"], err_msg=f"tile_class {label} b={b}")
+        np.testing.assert_array_equal(got["sub_class"][b], s["sub_class"], err_msg=f"sub_class {label} b={b}")
+        np.testing.assert_array_equal(got["q_nnz"][b], s["q_nnz"], err_msg=f"q_nnz {label}")
+        np.testing.assert_array_equal(got["q_list"][b], s["q_list"], err_msg=f"q_list {label}")
+        np.testing.assert_array_equal(got["k_nnz"][b], s["k_nnz"], err_msg=f"k_nnz {label}")
+        np.testing.assert_array_equal(got["k_list"][b], s["k_list"], err_msg=f"k_list {label}")
+    return got
+
+
+@pytest.mark.parametrize("bq,bk", [(32, 32), (64, 64), (128, 128), (32, 128), (128, 64), (64, 32)])
+def test_tiny(B, bq, bk):
+    check_layout(B, I.tiny_rows(), 64, bq, bk, "tiny")
+
+
+def _random_rows(seed, n_rows, max_convs, max_turns, max_len):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for _ in range(n_rows):
+        row = []
+        for _ in range(int(rng.integers(0, max_convs + 1))):
+            turns = []
+            for _ in range(int(rng.integers(0, max_turns + 1))):
+                h, t, r = (int(x) for x in rng.integers(0, max_len + 1, size=3))
+                if rng.random() < 0.2:
+                    turns.append((h, 0, r, 0))          # history-only turn
+                elif rng.random() < 0.2:
+                    turns.append((h, t, 0, r))          # last turn of an N-pass sequence
+                else:
+                    turns.append((h, t, r, r))
+            row.append(turns)
+        rows.append(row)
+    return rows
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_rows(B, seed):
+    rows = _random_rows(seed, n_rows=3, max_convs=4, max_turns=5, max_len=[3, 40, 90, 7, 150, 60][seed])
+    L = max(1, max(I.row_used(r) for r in rows)) + [0, 1, 17, 130, 5, 64][seed]
+    for bq, bk in [(128, 128), (32, 64), (64, 128)]:
+        check_layout(B, rows, L, bq, bk, f"random seed={seed}")
+
+
+def test_all_pad_row(B):
+    got = check_layout(B, [[], [[(5, 3, 2, 2)]]], 200, 128, 128, "empty row")
+    assert (got["tok_type"][0] == O.PAD).all() and (got["q_nnz"][0] == 0).all()
+
+
+def test_packed_fwd(B):
+    rows = I.packed_rows(I.PACKED_FWD, I.SEEDS["packed_fwd"][0])
+    check_layout(B, rows, I.PACKED_FWD.L, 128, 128, "packed_fwd")
+    check_layout(B, rows, I.PACKED_FWD.L, 64, 32, "packed_fwd")
+
+
+def test_packed_fwd_bwd(B):
+    rows = I.packed_rows(I.PACKED_FWD_BWD, I.SEEDS["packed_fwd_bwd"][0])
+    check_layout(B, rows, I.PACKED_FWD_BWD.L, 128, 128, "packed_fwd_bwd")
+
+
+@pytest.mark.parametrize("N", [2, 8, 32])
+def test_depth(B, N):
+    conv = I.depth_conversation(N)
+    check_layout(B, [[conv]], I.conv_len(conv), 128, 128, f"depth 1-pass N={N}")
+    if N <= 8:
+        np_convs = I.npass_conversations(conv)
+        L = sum(I.conv_len(c) for c in np_convs)
+        check_layout(B, [np_convs], L, 128, 128, f"depth N-pass N={N}")
+
+
+def test_kpass_rows(B):
+    rows = I.kpass_rows(2)
+    check_layout(B, rows, I.KPASS_ROW_LEN, 128, 128, "kpass K=2")
