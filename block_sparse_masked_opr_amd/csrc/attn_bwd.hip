@@ -15,6 +15,11 @@
 // attn_dq_kernel: one workgroup per (128-query tile, q head, row), like the
 //   forward kernel; S and dP^T are recomputed per non-empty sub-block and
 //   dQ^T += K'^T dS^T.
+// Operands are fp16 with per-64-token exponents (q, k, v, dout); P is stored
+// as fp16(P * 2^kPExp) and dS in the units of dP (2^(e_v + e_dout)) shifted
+// down by 2^kDsShift.  The accumulators carry power-of-two units that are
+// rescaled whenever a block with other exponents arrives, and removed in the
+// epilogue.
 #include "attn_common.h"
 #include "opr_internal.h"
 
@@ -41,15 +46,20 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
   const int key = n * 128 + 32 * w + li;
   const int64_t row_base = (int64_t)b * p.L;
 
-  bf16x8 kb_[NS], vb_[NS];
+  const int nblk = p.Lp / 64;
+  f16x8 kb_[NS], vb_[NS];
   {
     const int64_t off = (((int64_t)b * p.Hkv + kvh) * p.Lp + key) * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      kb_[s] = *reinterpret_cast<const bf16x8 *>(p.kr + off + 16 * s + 8 * g);
-      vb_[s] = *reinterpret_cast<const bf16x8 *>(p.vr + off + 16 * s + 8 * g);
+      kb_[s] = ld_f16x8(p.kr + off + 16 * s + 8 * g);
+      vb_[s] = ld_f16x8(p.vr + off + 16 * s + 8 * g);
     }
   }
+  const int ek = p.ek[((int64_t)b * p.Hkv + kvh) * nblk + (key >> 6)];
+  const int ev = p.ev[((int64_t)b * p.Hkv + kvh) * nblk + (key >> 6)];
+  // dV^T accumulator units 2^(kPExp + uv), dK^T units 2^(uk + ev - kDsShift)
+  int uv = 0, uk = 0;
   const TokMeta km = load_meta(p.tok_conv, p.tok_turn, p.tok_type, row_base, key, p.L);
 
   f32x16 dkacc[NDB], dvacc[NDB];
@@ -98,31 +108,49 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
         const uint32_t c1 = (sub >> (2 * (4 * (2 * qh + 1) + w))) & 3u;
         if ((c0 | c1) == 0) continue;
         const uint32_t cls[2] = {c0, c1};
+        const int eq = p.eq[((int64_t)b * p.Hq + h) * nblk + (q0 >> 6)];
+        const int edo = p.edo[((int64_t)b * p.Hq + h) * nblk + (q0 >> 6)];
+        const float fs = ldexpf(p.scale_log2, -(eq + ek));
+        const int udp = ev + edo;  // units of dP
 
-        bf16x8 pb[2][2], dsb[2][2];
+        f16x8 pb[2][2], dsb[2][2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           if (cls[qb] == 0) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) pb[qb][hh] = dsb[qb][hh] = zero_bf16x8();
+            for (int hh = 0; hh < 2; ++hh) pb[qb][hh] = dsb[qb][hh] = zero_f16x8();
             continue;
           }
           f32x16 s = zero_f32x16(), dp = zero_f32x16();
           const int arow = (32 * qb + kperm(li)) * RS + 8 * g;
 #pragma unroll
           for (int st = 0; st < NS; ++st) {
-            s = mfma32x32x16(lds_bf16x8(&Qs[arow + 16 * st]), kb_[st], s);
-            dp = mfma32x32x16(lds_bf16x8(&dOs[arow + 16 * st]), vb_[st], dp);
+            s = mfma32x32x16(ld_f16x8(&Qs[arow + 16 * st]), kb_[st], s);
+            dp = mfma32x32x16(ld_f16x8(&dOs[arow + 16 * st]), vb_[st], dp);
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ql = 32 * qb + acc_row(r, g);
-            float pv = __builtin_amdgcn_exp2f(s[r] * p.scale_log2 - lse2s[ql]);
-            if (cls[qb] == 1 && !mask_allows(q0 + ql, qmeta[ql], key, km)) pv = 0.0f;
-            const float ds = pv * (dp[r] - deltas[ql]);
-            pb[qb][r >> 3][r & 7] = (__bf16)pv;
-            dsb[qb][r >> 3][r & 7] = (__bf16)ds;
+            const float x = s[r] * fs - lse2s[ql];
+            float pv = __builtin_amdgcn_exp2f(x);
+            float ps = __builtin_amdgcn_exp2f(x + (float)kPExp);
+            if (cls[qb] == 1 && !mask_allows(q0 + ql, qmeta[ql], key, km)) pv = ps = 0.0f;
+            const float ds = ldexpf(pv * (dp[r] - ldexpf(deltas[ql], udp)), -kDsShift);
+            pb[qb][r >> 3][r & 7] = (_Float16)ps;
+            dsb[qb][r >> 3][r & 7] = (_Float16)ds;
           }
+        }
+        if (edo != uv) {
+          const float f = ldexpf(1.0f, edo - uv);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) dvacc[db] *= f;
+          uv = edo;
+        }
+        if (eq + edo != uk) {
+          const float f = ldexpf(1.0f, eq + edo - uk);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) dkacc[db] *= f;
+          uk = eq + edo;
         }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -132,8 +160,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
             const int arow = (32 * db + li) * TS + 32 * qb + 8 * g;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-              dvacc[db] = mfma32x32x16(lds_bf16x8(&dOts[arow + 16 * hh]), pb[qb][hh], dvacc[db]);
-              dkacc[db] = mfma32x32x16(lds_bf16x8(&Qts[arow + 16 * hh]), dsb[qb][hh], dkacc[db]);
+              dvacc[db] = mfma32x32x16(ld_f16x8(&dOts[arow + 16 * hh]), pb[qb][hh], dvacc[db]);
+              dkacc[db] = mfma32x32x16(ld_f16x8(&Qts[arow + 16 * hh]), dsb[qb][hh], dkacc[db]);
             }
           }
         }
@@ -144,6 +172,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
   if (key < p.L) {
     const int64_t out = ((row_base + key) * p.Hkv + kvh) * D;
     const float2 *cs = p.rope + ((int64_t)b * p.Lp + key) * (D / 2);
+    const float kscale = ldexpf(p.scale, kDsShift - uk - ev);
+    const float vscale = ldexpf(1.0f, -kPExp - uv);
 #pragma unroll
     for (int db = 0; db < HALF_DB; ++db) {
 #pragma unroll
@@ -153,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * a + c;
           const float2 rc = cs[acc_dim(db, r, g)];
-          const float g1 = p.scale * dkacc[db][r], g2 = p.scale * dkacc[db + HALF_DB][r];
+          const float g1 = kscale * dkacc[db][r], g2 = kscale * dkacc[db + HALF_DB][r];
           lo[c] = g1 * rc.x + g2 * rc.y;
           hi[c] = g2 * rc.x - g1 * rc.y;
         }
@@ -166,7 +196,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
 #pragma unroll
       for (int a = 0; a < 4; ++a)
         *reinterpret_cast<float4 *>(dv + out + acc_dim(db, 4 * a, g)) =
-            make_float4(dvacc[db][4 * a], dvacc[db][4 * a + 1], dvacc[db][4 * a + 2], dvacc[db][4 * a + 3]);
+            make_float4(vscale * dvacc[db][4 * a], vscale * dvacc[db][4 * a + 1],
+                        vscale * dvacc[db][4 * a + 2], vscale * dvacc[db][4 * a + 3]);
     }
   }
 }
@@ -190,12 +221,18 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnParams p, float *dq
   const int64_t row_base = (int64_t)b * p.L;
   const int64_t hq_row = ((int64_t)b * p.Hq + h) * p.Lp + q;
 
-  bf16x8 qb[NS], dob[NS];
+  const int nblk = p.Lp / 64;
+  f16x8 qb[NS], dob[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    qb[s] = *reinterpret_cast<const bf16x8 *>(p.qr + hq_row * D + 16 * s + 8 * g);
-    dob[s] = *reinterpret_cast<const bf16x8 *>(p.dor + hq_row * D + 16 * s + 8 * g);
+    qb[s] = ld_f16x8(p.qr + hq_row * D + 16 * s + 8 * g);
+    dob[s] = ld_f16x8(p.dor + hq_row * D + 16 * s + 8 * g);
   }
+  const int eq = p.eq[((int64_t)b * p.Hq + h) * nblk + (q >> 6)];
+  const int edo = p.edo[((int64_t)b * p.Hq + h) * nblk + (q >> 6)];
+  const int32_t *ekp = p.ek + ((int64_t)b * p.Hkv + kvh) * nblk;
+  const int32_t *evp = p.ev + ((int64_t)b * p.Hkv + kvh) * nblk;
+  int uq = 0;  // dQ^T accumulator units 2^(uq + edo - kDsShift), uq = e_k + e_v of the block
   const float lse2_q = p.lse2[hq_row];
   const float delta_q = p.delta[hq_row];
   const TokMeta qm = load_meta(p.tok_conv, p.tok_turn, p.tok_type, row_base, q, p.L);
@@ -235,28 +272,37 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnParams p, float *dq
       const uint32_t c1 = (sub >> (2 * (4 * w + 2 * kh + 1))) & 3u;
       if ((c0 | c1) == 0) continue;
       const uint32_t cls[2] = {c0, c1};
+      const int ek = ekp[k0 >> 6], ev = evp[k0 >> 6];
+      const float fs = ldexpf(p.scale_log2, -(eq + ek));
+      const float dd = ldexpf(delta_q, ev + edo);  // delta in the units of dP
 
-      bf16x8 dsb[2][2];
+      f16x8 dsb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (cls[kb] == 0) {
-          dsb[kb][0] = dsb[kb][1] = zero_bf16x8();
+          dsb[kb][0] = dsb[kb][1] = zero_f16x8();
           continue;
         }
         f32x16 s = zero_f32x16(), dpt = zero_f32x16();
         const int arow = (32 * kb + kperm(li)) * RS + 8 * g;
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          s = mfma32x32x16(lds_bf16x8(&Ks[arow + 16 * st]), qb[st], s);
-          dpt = mfma32x32x16(lds_bf16x8(&Vs[arow + 16 * st]), dob[st], dpt);
+          s = mfma32x32x16(ld_f16x8(&Ks[arow + 16 * st]), qb[st], s);
+          dpt = mfma32x32x16(ld_f16x8(&Vs[arow + 16 * st]), dob[st], dpt);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kl = 32 * kb + acc_row(r, g);
-          float pv = __builtin_amdgcn_exp2f(s[r] * p.scale_log2 - lse2_q);
+          float pv = __builtin_amdgcn_exp2f(s[r] * fs - lse2_q);
           if (cls[kb] == 1 && !mask_allows(q, qm, k0 + kl, kmeta[kl])) pv = 0.0f;
-          dsb[kb][r >> 3][r & 7] = (__bf16)(pv * (dpt[r] - delta_q));
+          dsb[kb][r >> 3][r & 7] = (_Float16)ldexpf(pv * (dpt[r] - dd), -kDsShift);
         }
+      }
+      if (ek + ev != uq) {
+        const float f = ldexpf(1.0f, ek + ev - uq);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dqacc[db] *= f;
+        uq = ek + ev;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -265,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnParams p, float *dq
         for (int db = 0; db < NDB; ++db) {
           const int arow = (32 * db + li) * TS + 32 * kb + 8 * g;
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) dqacc[db] = mfma32x32x16(lds_bf16x8(&Kts[arow + 16 * hh]), dsb[kb][hh], dqacc[db]);
+          for (int hh = 0; hh < 2; ++hh) dqacc[db] = mfma32x32x16(ld_f16x8(&Kts[arow + 16 * hh]), dsb[kb][hh], dqacc[db]);
         }
       }
     }
@@ -274,6 +320,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnParams p, float *dq
   if (q < p.L) {
     float *out = dq + ((row_base + q) * p.Hq + h) * D;
     const float2 *cs = p.rope + ((int64_t)b * p.Lp + q) * (D / 2);
+    const float qscale = ldexpf(p.scale, kDsShift - uq - edo);
 #pragma unroll
     for (int db = 0; db < HALF_DB; ++db) {
 #pragma unroll
@@ -283,7 +330,7 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnParams p, float *dq
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * a + c;
           const float2 rc = cs[acc_dim(db, r, g)];
-          const float g1 = p.scale * dqacc[db][r], g2 = p.scale * dqacc[db + HALF_DB][r];
+          const float g1 = qscale * dqacc[db][r], g2 = qscale * dqacc[db + HALF_DB][r];
           lo[c] = g1 * rc.x + g2 * rc.y;
           hi[c] = g2 * rc.x - g1 * rc.y;
         }

@@ -1,7 +1,20 @@
 // Device-side building blocks of the attention kernels (gfx950 / CDNA4).
 //
-// MFMA v_mfma_f32_32x32x16_bf16 computes C[32x32] += A[32x16] * B[16x32].
-// Lane l (g = l / 32, i = l % 32) supplies 8 bf16 of A row i and 8 bf16 of
+// Number format.  Every matrix product runs on v_mfma_f32_32x32x16_f16 (fp16
+// operands, fp32 accumulation; the same rate as bf16 on gfx950).  fp16 keeps
+// 11 significant bits where bf16 keeps 8, which is what lets the summed
+// gradients of a GQA group stay within 2e-2 of the exact result.  To keep
+// bf16's range, each 64-token block of every staged operand (q and k after
+// RoPE, v, dout) is stored as fp16(x * 2^e) with its own power-of-two exponent
+// e chosen so that the block's largest magnitude lands in [2^14, 2^15).  The
+// kernels fold the exponents back exactly: into the score scale (q, k), and
+// into the running units of the fp32 accumulators (v, dout), which are
+// rescaled by powers of two when a block with another exponent arrives.
+// Probabilities are stored as fp16(p * 2^15) so that small ones keep full
+// precision (p <= 1).
+//
+// MFMA v_mfma_f32_32x32x16_f16 computes C[32x32] += A[32x16] * B[16x32].
+// Lane l (g = l / 32, i = l % 32) supplies 8 fp16 of A row i and 8 fp16 of
 // B column i for k-group g; any assignment of the 16 k indices to (g, element)
 // works as long as A and B use the same one.  The accumulator holds, in lane
 // l and register r, C[8*(r/4) + 4*g + r%4][i].
@@ -21,12 +34,20 @@
 
 namespace opr {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma32x32x16(const f16x8 &a, const f16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+
+// Exponent range of the per-block scales; keeps every folded product of up to
+// three exponents inside fp32's normal range.
+constexpr int kExpMin = -32, kExpMax = 32;
+// Probabilities are stored scaled by 2^kPExp; dS by 2^-kDsShift on top of the
+// units of v and dout (|v|, |dout| < 2^15 after scaling, so |dP| < 2^37).
+constexpr int kPExp = 15;
+constexpr int kDsShift = 22;
 
 // A-operand row order of a 32-row block: swap bits 2 and 3.
 __device__ __forceinline__ int kperm(int i) {
@@ -45,15 +66,29 @@ __device__ __forceinline__ constexpr int acc_dim(int db, int r, int g) {
   return 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
 }
 
-__device__ __forceinline__ bf16x8 lds_bf16x8(const uint16_t *p) {
-  return *reinterpret_cast<const bf16x8 *>(p);
+__device__ __forceinline__ f16x8 ld_f16x8(const uint16_t *p) {
+  return *reinterpret_cast<const f16x8 *>(p);
 }
 
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-  bf16x8 z;
+__device__ __forceinline__ f16x8 zero_f16x8() {
+  f16x8 z;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
+  for (int e = 0; e < 8; ++e) z[e] = (_Float16)0.0f;
   return z;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;
+  return *reinterpret_cast<uint16_t *>(&h);
+}
+
+// Exponent e with max_abs * 2^e in [2^14, 2^15) (0 for an all-zero block),
+// clamped to [kExpMin, kExpMax].
+__device__ __forceinline__ int block_exponent(float max_abs) {
+  if (!(max_abs > 0.0f)) return 0;
+  int x;
+  frexpf(max_abs, &x);
+  return min(kExpMax, max(kExpMin, 15 - x));
 }
 
 __device__ __forceinline__ f32x16 zero_f32x16() {
@@ -120,7 +155,10 @@ struct AttnParams {
   const uint32_t *sub_class;
   const int32_t *q_nnz, *q_list, *k_nnz, *k_list;
   const float2 *rope;                    // [B][Lp][D/2]
+  // fp16 bits, scaled per 64-token block (see the number format above)
   const uint16_t *qr, *kr, *vt, *vr, *qt, *kt, *dor, *dot;
+  // block exponents [B][H][Lp/64] of q, k, v, dout
+  const int32_t *eq, *ek, *ev, *edo;
   const float *delta, *lse2;
 };
 

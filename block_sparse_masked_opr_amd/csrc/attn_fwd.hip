@@ -5,11 +5,13 @@
 // the ascending list of non-empty 128-key tiles of q-tile m, half a tile (64
 // keys) at a time, skipping halves whose 32x32 sub-blocks are all empty.  Per
 // half: K (after RoPE) and V^T are staged in LDS; each wave computes
-// S^T = K Q^T on its non-empty 32x32 sub-blocks with bf16 MFMA (fp32
+// S^T = K Q^T on its non-empty 32x32 sub-blocks with fp16 MFMA (fp32
 // accumulate), applies the mask predicate only on partial sub-blocks, updates
 // the online softmax (base-2 exponent with log2(e) folded into the scale) and
 // accumulates O^T += V^T P^T.  The epilogue normalises, writes O (bf16) and
-// the natural-log LSE.
+// the natural-log LSE.  Operands are fp16 with per-64-token exponents: the q
+// and k exponents are folded into the score scale, the v exponent into the
+// units of the O accumulator (rescaled together with the softmax correction).
 #include "attn_common.h"
 #include "opr_internal.h"
 
@@ -32,12 +34,17 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
   const int q = m * 128 + 32 * w + li;
   const int64_t row_base = (int64_t)b * p.L;
 
-  bf16x8 qb[NS];
+  const int nblk = p.Lp / 64;
+  f16x8 qb[NS];
   {
     const uint16_t *qrow = p.qr + (((int64_t)b * p.Hq + h) * p.Lp + q) * D;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qb[s] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * s + 8 * g);
+    for (int s = 0; s < NS; ++s) qb[s] = ld_f16x8(qrow + 16 * s + 8 * g);
   }
+  const int eq = p.eq[((int64_t)b * p.Hq + h) * nblk + (q >> 6)];
+  const int32_t *ekp = p.ek + ((int64_t)b * p.Hkv + kvh) * nblk;
+  const int32_t *evp = p.ev + ((int64_t)b * p.Hkv + kvh) * nblk;
+  int ev_ref = 0;  // O accumulator holds O * sum(p) * 2^(kPExp + ev_ref)
   const TokMeta qm = load_meta(p.tok_conv, p.tok_turn, p.tok_type, row_base, q, p.L);
 
   f32x16 oacc[NDB];
@@ -79,6 +86,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
       const uint32_t c1 = (sub >> (2 * (4 * w + 2 * kh + 1))) & 3u;
       if ((c0 | c1) == 0) continue;
       const uint32_t cls[2] = {c0, c1};
+      const int ek = ekp[k0 >> 6], ev = evp[k0 >> 6];
+      const float fs = ldexpf(p.scale_log2, -(eq + ek));
 
       f32x16 s[2];
 #pragma unroll
@@ -87,14 +96,14 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
         if (cls[kb] == 0) continue;
         const uint16_t *arow = &Ks[(32 * kb + kperm(li)) * KS + 8 * g];
 #pragma unroll
-        for (int st = 0; st < NS; ++st) s[kb] = mfma32x32x16(lds_bf16x8(arow + 16 * st), qb[st], s[kb]);
+        for (int st = 0; st < NS; ++st) s[kb] = mfma32x32x16(ld_f16x8(arow + 16 * st), qb[st], s[kb]);
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * p.scale_log2;
+          float x = s[kb][r] * fs;
           if (cls[kb] == 0) {
             x = -INFINITY;
           } else if (cls[kb] == 1) {
@@ -109,21 +118,24 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
       const float mnew = fmaxf(mrow, mx);
       const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
       const float alpha = __builtin_amdgcn_exp2f(mrow - msafe);
+      const float ofac = ldexpf(alpha, ev - ev_ref);  // softmax correction and new v units
       mrow = mnew;
+      ev_ref = ev;
       lrow *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= ofac;
       }
-      bf16x8 pb[2][2];
+      const float mshift = msafe - (float)kPExp;
+      f16x8 pb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(s[kb][r] - msafe);
+          const float pv = __builtin_amdgcn_exp2f(s[kb][r] - mshift);  // p * 2^kPExp
           lrow += pv;
-          pb[kb][r >> 3][r & 7] = (__bf16)pv;
+          pb[kb][r >> 3][r & 7] = (_Float16)pv;
         }
       }
 #pragma unroll
@@ -133,7 +145,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
         for (int db = 0; db < NDB; ++db) {
           const uint16_t *arow = &Vts[(32 * db + li) * VS + 32 * kb + 8 * g];
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) oacc[db] = mfma32x32x16(lds_bf16x8(arow + 16 * hh), pb[kb][hh], oacc[db]);
+          for (int hh = 0; hh < 2; ++hh) oacc[db] = mfma32x32x16(ld_f16x8(arow + 16 * hh), pb[kb][hh], oacc[db]);
         }
       }
     }
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
 
   const float lsum = lrow + __shfl_xor(lrow, 32);
   if (q < p.L) {
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    const float inv = lsum > 0.0f ? ldexpf(1.0f / lsum, -ev_ref) : 0.0f;
     uint16_t *orow = o + ((row_base + q) * p.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -154,7 +166,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
       }
     }
     if (g == 0)
-      lse[((int64_t)b * p.Hq + h) * p.L + q] = lsum > 0.0f ? (mrow + log2f(lsum)) * kLn2 : -INFINITY;
+      lse[((int64_t)b * p.Hq + h) * p.L + q] =
+          lsum > 0.0f ? (mrow + log2f(lsum) - (float)kPExp) * kLn2 : -INFINITY;
   }
 }
 

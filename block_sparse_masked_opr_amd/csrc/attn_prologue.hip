@@ -1,7 +1,8 @@
 // Prologue kernels of the attention path: the RoPE table at the strategic
-// position ids, head-major (optionally rotated) copies of q / k / v / dout, and
-// their transposes, all padded to a whole number of 128-token tiles with
-// zeros; plus the backward preprocessing delta = rowsum(dout * o).
+// position ids, head-major (optionally rotated) fp16 copies of q / k / v / dout
+// with one power-of-two scale per 64-token block, and their transposes, all
+// padded to a whole number of 128-token tiles with zeros; plus the backward
+// preprocessing delta = rowsum(dout * o).
 //
 // RoPE (rotate-half): pair (j, j + D/2) of a head vector is rotated by
 // pos * theta^(-2j/D).  The angle and its cosine and sine are computed in
@@ -32,56 +33,84 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, i
 }
 
 // One workgroup per (64-token block, head, row).  x: [B][L][H][D] bf16.
-// rows (optional): [B][H][Lp][D]; trans (optional): [B][H][D][Lp].
+// Writes the block as fp16(x' * 2^e), x' = RoPE(x) or x, with the block
+// exponent e (largest |x'| of the block scaled into [2^14, 2^15)) stored in
+// exps[b][h][block]; rows (optional): [B][H][Lp][D]; trans (optional):
+// [B][H][D][Lp].  Tokens t >= L are zero.
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H,
                                                    const uint16_t *x, const float2 *table,
-                                                   uint16_t *rows, uint16_t *trans) {
+                                                   uint16_t *rows, uint16_t *trans,
+                                                   int32_t *exps) {
   constexpr int HALF = D / 2;
   constexpr int PER = HALF / 4;           // pairs per thread (4 threads per token)
   constexpr int TS = 64 + 8;              // LDS row stride of the transposed tile
   __shared__ __attribute__((aligned(16))) uint16_t tile[D * TS];
+  __shared__ float wmax[4];
   const int t0 = blockIdx.x * 64;
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int tt = tid >> 2, part = tid & 3;
   const int t = t0 + tt;
   const int j0 = part * PER;
-  uint16_t lo[PER], hi[PER];
+  float lo[PER], hi[PER];
   if (t < L) {
     const uint16_t *src = x + (((int64_t)b * L + t) * H + h) * D;
+    uint16_t lb[PER], hb[PER];
 #pragma unroll
     for (int c = 0; c < PER; c += 8) {
-      *reinterpret_cast<uint4 *>(&lo[c]) = *reinterpret_cast<const uint4 *>(src + j0 + c);
-      *reinterpret_cast<uint4 *>(&hi[c]) = *reinterpret_cast<const uint4 *>(src + HALF + j0 + c);
+      *reinterpret_cast<uint4 *>(&lb[c]) = *reinterpret_cast<const uint4 *>(src + j0 + c);
+      *reinterpret_cast<uint4 *>(&hb[c]) = *reinterpret_cast<const uint4 *>(src + HALF + j0 + c);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      lo[e] = bf16_to_f32(lb[e]);
+      hi[e] = bf16_to_f32(hb[e]);
     }
     if (ROPE) {
       const float2 *cs = table + ((int64_t)b * Lp + t) * HALF + j0;
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
         const float2 r = cs[e];
-        const float x1 = bf16_to_f32(lo[e]), x2 = bf16_to_f32(hi[e]);
-        lo[e] = f32_to_bf16(x1 * r.x - x2 * r.y);
-        hi[e] = f32_to_bf16(x2 * r.x + x1 * r.y);
+        const float x1 = lo[e], x2 = hi[e];
+        lo[e] = x1 * r.x - x2 * r.y;
+        hi[e] = x2 * r.x + x1 * r.y;
       }
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) lo[e] = hi[e] = 0;
+    for (int e = 0; e < PER; ++e) lo[e] = hi[e] = 0.0f;
+  }
+  // block max |x'|: lanes, then the four waves
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) m = fmaxf(m, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int ex = block_exponent(m);
+  if (tid == 0) exps[((int64_t)b * H + h) * (Lp / 64) + blockIdx.x] = ex;
+  uint16_t lq[PER], hq[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    lq[e] = f32_to_f16_bits(ldexpf(lo[e], ex));
+    hq[e] = f32_to_f16_bits(ldexpf(hi[e], ex));
   }
   if (rows) {
     uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
 #pragma unroll
     for (int c = 0; c < PER; c += 8) {
-      *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lo[c]);
-      *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hi[c]);
+      *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
+      *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
     }
   }
   if (trans) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      tile[(j0 + e) * TS + tt] = lo[e];
-      tile[(HALF + j0 + e) * TS + tt] = hi[e];
+      tile[(j0 + e) * TS + tt] = lq[e];
+      tile[(HALF + j0 + e) * TS + tt] = hq[e];
     }
     __syncthreads();
     // D rows of 64 tokens (128 bytes = 8 chunks of 16 bytes)
@@ -127,13 +156,14 @@ __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_
 
 template <int D>
 void launch_pack(bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x,
-                 const float2 *table, uint16_t *rows, uint16_t *trans, hipStream_t s) {
+                 const float2 *table, uint16_t *rows, uint16_t *trans, int32_t *exps,
+                 hipStream_t s) {
   const dim3 grid(Lp / 64, H, B);
   const uint16_t *src = static_cast<const uint16_t *>(x);
   if (rope)
-    pack_kernel<D, true><<<grid, 256, 0, s>>>(L, Lp, H, src, table, rows, trans);
+    pack_kernel<D, true><<<grid, 256, 0, s>>>(L, Lp, H, src, table, rows, trans, exps);
   else
-    pack_kernel<D, false><<<grid, 256, 0, s>>>(L, Lp, H, src, table, rows, trans);
+    pack_kernel<D, false><<<grid, 256, 0, s>>>(L, Lp, H, src, table, rows, trans, exps);
 }
 
 }  // namespace
@@ -146,9 +176,10 @@ void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
 }
 
 void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x,
-                     const float2 *table, uint16_t *rows, uint16_t *trans, hipStream_t s) {
-  if (D == 64) launch_pack<64>(rope, B, L, Lp, H, x, table, rows, trans, s);
-  else launch_pack<128>(rope, B, L, Lp, H, x, table, rows, trans, s);
+                     const float2 *table, uint16_t *rows, uint16_t *trans, int32_t *exps,
+                     hipStream_t s) {
+  if (D == 64) launch_pack<64>(rope, B, L, Lp, H, x, table, rows, trans, exps, s);
+  else launch_pack<128>(rope, B, L, Lp, H, x, table, rows, trans, exps, s);
 }
 
 void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,

@@ -11,7 +11,8 @@ namespace opr {
 // launchers defined in the .hip files
 void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x,
-                     const float2 *table, uint16_t *rows, uint16_t *trans, hipStream_t s);
+                     const float2 *table, uint16_t *rows, uint16_t *trans, int32_t *exps,
+                     hipStream_t s);
 void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
                   const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, float *lse,
@@ -32,6 +33,10 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   w.rope = cv.take<float2>((size_t)in.B * Lp * (in.D / 2));
   w.qr = cv.take<uint16_t>(qn);
   w.kr = cv.take<uint16_t>(kn);
+  const size_t qb = (size_t)in.B * in.Hq * (Lp / 64), kb = (size_t)in.B * in.Hkv * (Lp / 64);
+  w.eq = cv.take<int32_t>(qb);
+  w.ek = cv.take<int32_t>(kb);
+  w.ev = cv.take<int32_t>(kb);
   if (!is_bwd) {
     w.vt = cv.take<uint16_t>(kn);
   } else {
@@ -40,6 +45,7 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
     w.kt = cv.take<uint16_t>(kn);
     w.dor = cv.take<uint16_t>(qn);
     w.dot = cv.take<uint16_t>(qn);
+    w.edo = cv.take<int32_t>(qb);
     w.delta = cv.take<float>((size_t)in.B * in.Hq * Lp);
     w.lse2 = cv.take<float>((size_t)in.B * in.Hq * Lp);
   }
@@ -77,6 +83,10 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->kt = ws.kt;
   p->dor = ws.dor;
   p->dot = ws.dot;
+  p->eq = ws.eq;
+  p->ek = ws.ek;
+  p->ev = ws.ev;
+  p->edo = ws.edo;
   p->delta = ws.delta;
   p->lse2 = ws.lse2;
 }
@@ -202,9 +212,9 @@ opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *worksp
   AttnWs ws;
   carve_attn_ws(workspace, *in, 0, &ws);
   launch_rope_table(*in, ws, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, nullptr, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, nullptr, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, nullptr, ws.vt, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, nullptr, ws.eq, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, nullptr, ws.ek, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, nullptr, ws.vt, ws.ev, stream);
   if (launch_attn_fwd_kernel(*in, effective_scale(in), o, lse, ws, stream) != hipSuccess) return OPR_E_HIP;
   return hip_status();
 }
@@ -219,10 +229,10 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   AttnWs ws;
   carve_attn_ws(workspace, *in, 1, &ws);
   launch_rope_table(*in, ws, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, ws.qt, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, ws.kt, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, ws.vr, nullptr, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, dout, nullptr, ws.dor, ws.dot, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, ws.qt, ws.eq, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, ws.kt, ws.ek, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, ws.vr, nullptr, ws.ev, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, dout, nullptr, ws.dor, ws.dot, ws.edo, stream);
   launch_delta(*in, o, dout, lse, ws, stream);
   if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream) != hipSuccess)
     return OPR_E_HIP;

@@ -53,6 +53,7 @@ hipError_t launch_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t bl
 struct AttnWs {
   int32_t Lp;           // L rounded up to OPR_ATTN_BLOCK
   float2 *rope;         // [B][Lp][D/2] (cos, sin) at each token's position id
+  // fp16 copies, one power-of-two scale per 64-token block (exponents below)
   uint16_t *qr;         // [B][Hq][Lp][D]  q after RoPE, head-major, zero past L
   uint16_t *kr;         // [B][Hkv][Lp][D] k after RoPE
   uint16_t *vt;         // [B][Hkv][D][Lp] v transposed                (fwd)
@@ -61,6 +62,7 @@ struct AttnWs {
   uint16_t *kt;         // [B][Hkv][D][Lp] k after RoPE, transposed    (bwd)
   uint16_t *dor;        // [B][Hq][Lp][D]  dout head-major             (bwd)
   uint16_t *dot;        // [B][Hq][D][Lp]  dout transposed             (bwd)
+  int32_t *eq, *ek, *ev, *edo;  // block exponents [B][H][Lp/64]   (edo: bwd)
   float *delta;         // [B][Hq][Lp] rowsum(dout * o)                (bwd)
   float *lse2;          // [B][Hq][Lp] log2-domain lse, +inf where no key (bwd)
 };

@@ -164,3 +164,57 @@ def test_packed_fwd_bwd(B):
     assert (got["o"][pad] == 0).all() and (got["dq"][pad] == 0).all()
     assert (got["dk"][pad] == 0).all() and (got["dv"][pad] == 0).all()
     compare_convs("packed_fwd_bwd", rows, s.L, t, got, s, convs_per_row=2)
+
+
+def test_depth_gqa8(B):
+    """Depth-sweep attention shape (64 q heads over 8 kv heads, D = 128), N = 4
+    turns of (128, 1024, 256): whole conversation, two complete kv groups."""
+    conv = I.depth_conversation(4)
+    rows = [[conv]]
+    L = I.conv_len(conv)
+    s = I.Shape("depth4", 1, L, **I.DEPTH_HEADS)
+    t = I.make_tensors(1, L, s.Hq, s.Hkv, s.D, seed=I.SEEDS["depth"][1])
+    got = run_gpu(B, rows, L, t)
+    compare_convs("depth N=4", rows, L, t, got, s, convs_per_row=0)
+
+
+def test_npass_rows_match_onepass(B):
+    """Theorem 2.1 on the GPU: the N-pass sequences, gathered from the one-pass
+    row's tokens and run through the same kernels, reproduce the one-pass rows."""
+    conv = [(40, 130, 70, 70), (20, 90, 50, 50), (60, 30, 80, 80)]
+    L1 = I.conv_len(conv)
+    t = I.make_tensors(1, L1, 4, 2, 128, seed=5150)
+    lay1 = O.layout([[conv]], L1)
+    passes = O.npass_index(lay1, 0, 0)
+    np_rows = [[I.npass_conversations(conv)[i] for i in range(len(conv))]]
+    Ln = sum(len(p["idx"]) for p in passes)
+    idx = np.concatenate([p["idx"] for p in passes])
+    tn = {n: np.ascontiguousarray(t[n][:, idx]) for n in t}
+    g1 = run_gpu(B, [[conv]], L1, t)
+    gn = run_gpu(B, np_rows, Ln, tn)
+    # same kernels, same inputs at the same relative positions
+    print("[attn] N-pass vs one-pass rows", flush=True)
+    assert_close("O", gn["o"][0], g1["o"][0, idx], max_abs=1e-2, mean_rel=2e-3)
+
+
+def test_scaled_inputs(B):
+    """Magnitudes far from 1 (q x4, k x1/4, v x1e3, dout x1e-5): the per-block
+    fp16 exponents must keep the relative error at the unscaled level."""
+    rows = [[[(50, 120, 40, 40), (30, 60, 70, 70)], [(100, 0, 30, 30)]]]
+    L = I.row_used(rows[0]) + 11
+    t = I.make_tensors(1, L, 4, 1, 128, seed=99)
+    f = {"q": 4.0, "k": 0.25, "v": 1.0e3, "do": 1.0e-5}
+    ts = {n: I.round_to_bf16_bits(I.bf16_bits_to_f32(t[n]) * np.float32(f[n])) for n in t}
+    got = run_gpu(B, rows, L, ts)
+    lay = O.layout(rows, L)
+    q, k, v, do = (bf16_f64(ts[n]) for n in ("q", "k", "v", "do"))
+    o, lse = O.attn_fwd(q, k, v, lay, THETA)
+    dq, dk, dv = O.attn_bwd(q, k, v, do, lay, THETA)
+    live = lay["type"] != O.PAD
+    print("[attn] scaled inputs", flush=True)
+    # relative to the largest magnitude; O is bf16, whose rounding alone is up
+    # to 2^-9 of it
+    for n, x, ref in (("O", got["o"], o), ("dq", got["dq"], dq), ("dk", got["dk"], dk), ("dv", got["dv"], dv)):
+        top = float(np.abs(ref[live]).max())
+        assert_close(n, x[live] / top, ref[live] / top, max_abs=5e-3)
+    assert_close("LSE", got["lse"].transpose(0, 2, 1)[live], lse.transpose(0, 2, 1)[live])
