@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of one-pass block-sparse masked attention on one MI355X.
+
+A step is one pass of the whole path over one batch: opr_build_layout (tokens,
+position ids, tile schedule) + opr_attn_fwd + opr_attn_bwd, on the packed
+fwd+bwd workload: 2 rows x 16384 tokens of packed multi-turn conversations
+(N~U[2,6] turns, h~U[16,128], t~U[64,512], r~U[32,256], responses duplicated),
+32 q heads over 8 kv heads, head dim 128, RoPE theta 1e6; seeded synthetic
+bf16 inputs already resident in HBM.
+
+Prints one JSON line: useful TFLOP/s (12 * D * Hq * P, P = allowed query-key
+pairs, recomputation not counted), conversation tokens/s, the roofline of the
+dominant kernel (timed with HIP events on its own stream), the fp64 CPU oracle
+timed on a bounded sample, and (unless --no-sweep) the one-pass vs N-pass
+speedup across conversation depth and the K-pass trade-off.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from block_sparse_masked_opr_amd import inputs as I  # noqa: E402  (no torch, no GPU)
+
+PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self, torch):
+        libdir = os.path.join(os.path.dirname(torch.__file__), "lib")
+        path = os.path.join(libdir, "libamdhip64.so")
+        self.hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def array(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = h
+        return arr
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def free(self, arr):
+        for h in arr:
+            self.hip.hipEventDestroy(h)
+
+
+def useful_pairs(torch, lay):
+    """P = sum over non-PAD tokens of (pos + 1): every query sees positions 0..pos."""
+    live = lay.tok_type != 4
+    return int(((lay.tok_pos.to(torch.int64) + 1) * live).sum().item())
+
+
+def device_inputs(torch, B, L, Hq, Hkv, D, seed, dev):
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    out = {}
+    for n, H in (("q", Hq), ("k", Hkv), ("v", Hkv), ("do", Hq)):
+        out[n] = torch.randn((B, L, H, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    return out
+
+
+class Runner:
+    """Buffers and calls for one workload; step() = layout + fwd + bwd."""
+
+    def __init__(self, torch, Bd, rows, L, Hq, Hkv, D, t, dev, theta=1.0e6):
+        self.torch, self.Bd, self.rows, self.L, self.theta = torch, Bd, rows, L, theta
+        B = len(rows)
+        self.t = t
+        self.lay = Bd.opr_build_layout(rows, L, 128, 128, device=dev)
+        cpr, tpc, turns = I.flatten_rows(rows)
+        self.lws = torch.empty(Bd.opr_build_layout_workspace_size(B, L, len(tpc), len(turns)), dtype=torch.uint8, device=dev)
+        self.fws = torch.empty(Bd.opr_attn_workspace_size(B, L, Hq, Hkv, D, False), dtype=torch.uint8, device=dev)
+        self.bws = torch.empty(Bd.opr_attn_workspace_size(B, L, Hq, Hkv, D, True), dtype=torch.uint8, device=dev)
+        self.o = torch.empty_like(t["q"])
+        self.lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+        self.dq = torch.empty(t["q"].shape, dtype=torch.float32, device=dev)
+        self.dk = torch.empty(t["k"].shape, dtype=torch.float32, device=dev)
+        self.dv = torch.empty(t["v"].shape, dtype=torch.float32, device=dev)
+
+    def step(self, ev_f=None, ev_b=None):
+        Bd, t = self.Bd, self.t
+        Bd.opr_build_layout(self.rows, self.L, 128, 128, device=self.o.device, workspace=self.lws, out=self.lay)
+        Bd.opr_attn_fwd(t["q"], t["k"], t["v"], self.lay, self.theta, workspace=self.fws,
+                        out=(self.o, self.lse), events=ev_f)
+        Bd.opr_attn_bwd(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], self.lay, self.theta,
+                        workspace=self.bws, out=(self.dq, self.dk, self.dv), events=ev_b)
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            self.step()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps
+
+
+def cpu_baseline(rows, L, shape, t_np):
+    """The fp64 oracle on a bounded sample: one conversation, one kv group."""
+    from oracle import opr_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    lay = O.layout(rows, L)
+    a, e = O.conv_range(lay, 0, 0)
+    g = shape.Hq // shape.Hkv
+    sub = {n: I.bf16_bits_to_f32(t_np[n][0:1, a:e]).astype(np.float64) for n in t_np}
+    q, k, v, do = sub["q"][:, :, :g], sub["k"][:, :, :1], sub["v"][:, :, :1], sub["do"][:, :, :g]
+    lay_c = O.layout([[rows[0][0]]], e - a)
+    P = O.useful_pairs(lay_c)
+    t0 = time.perf_counter()
+    O.attn_fwd(q, k, v, lay_c, shape.theta)
+    O.attn_bwd(q, k, v, do, lay_c, shape.theta)
+    dt = time.perf_counter() - t0
+    flops = 12.0 * shape.D * g * P
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"row 0 conversation 0 ({e - a} tokens, {P} pairs), q heads 0-{g - 1} over kv head 0, "
+                      f"fwd+bwd, {dt:.2f} s"}
+
+
+def depth_sweep(torch, Bd, dev, Ns, steps):
+    out = []
+    Hq, Hkv, D = I.DEPTH_HEADS["Hq"], I.DEPTH_HEADS["Hkv"], I.DEPTH_HEADS["D"]
+    for N in Ns:
+        conv = I.depth_conversation(N)
+        rec = {"N": N}
+        for kind, rows in (("one_pass", [[conv]]), ("n_pass", [I.npass_conversations(conv)])):
+            L = I.row_used(rows[0])
+            t = device_inputs(torch, 1, L, Hq, Hkv, D, I.SEEDS["depth"][1], dev)
+            r = Runner(torch, Bd, rows, L, Hq, Hkv, D, t, dev)
+            ms = r.time_steps(steps, 1)
+            P = useful_pairs(torch, r.lay)
+            rec[kind] = {"tokens": L, "ms": round(ms, 4), "useful_tflops": round(12.0 * D * Hq * P / (ms * 1e-3) / 1e12, 2)}
+            del r, t
+            torch.cuda.empty_cache()
+        rec["speedup"] = round(rec["n_pass"]["ms"] / rec["one_pass"]["ms"], 3)
+        log(f"depth N={N}: {rec}")
+        out.append(rec)
+    return out
+
+
+def kpass_sweep(torch, Bd, dev, steps):
+    out = []
+    Hq, Hkv, D = I.KPASS_HEADS["Hq"], I.KPASS_HEADS["Hkv"], I.KPASS_HEADS["D"]
+    L = I.KPASS_ROW_LEN
+    for K in (1, 2, 4, "N"):
+        rows = I.kpass_rows(K)
+        t = device_inputs(torch, len(rows), L, Hq, Hkv, D, I.SEEDS["kpass"][1], dev)
+        r = Runner(torch, Bd, rows, L, Hq, Hkv, D, t, dev)
+        ms = r.time_steps(steps, 1)
+        packed = sum(I.row_used(row) for row in rows)
+        longest = max(I.conv_len(c) for row in rows for c in row)
+        out.append({"K": K, "rows": len(rows), "packed_tokens": packed, "longest_sequence": longest,
+                    "ms": round(ms, 4)})
+        log(f"kpass K={K}: {out[-1]}")
+        del r, t
+        torch.cuda.empty_cache()
+    base = next(x for x in out if x["K"] == "N")["ms"]
+    for x in out:
+        x["speedup_vs_npass"] = round(base / x["ms"], 3)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the depth and K-pass sweeps")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--sweep-steps", type=int, default=3)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the one-pass attention path runs on a single MI355X; "
+              "multi-GPU sharding is a design note only (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_masked_opr_amd import binding as Bd
+
+    dev = torch.device("cuda:0")
+    shape = I.PACKED_FWD_BWD
+    seed_len, seed_t = I.SEEDS["packed_fwd_bwd"]
+    rows = I.packed_rows(shape, seed_len)
+    log("generating inputs ...")
+    t_np = I.make_tensors(shape.B, shape.L, shape.Hq, shape.Hkv, shape.D, seed=seed_t)
+    t = {n: torch.from_numpy(t_np[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in t_np}
+    r = Runner(torch, Bd, rows, shape.L, shape.Hq, shape.Hkv, shape.D, t, dev, shape.theta)
+    P = useful_pairs(torch, r.lay)
+    conv_tokens = sum(I.conv_logical_tokens(c) for row in rows for c in row)
+    packed_tokens = sum(I.row_used(row) for row in rows)
+
+    # timed region: exactly `steps` steps, HIP events per stage
+    ev = HipEvents(torch)
+    evs = [(ev.array(3), ev.array(4)) for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        r.step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        r.step(*evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    stages = {"fwd_prologue": 0.0, "attn_fwd": 0.0, "bwd_prologue": 0.0, "attn_dkdv": 0.0, "attn_dq": 0.0}
+    for f, b in evs:
+        stages["fwd_prologue"] += ev.ms(f[0], f[1])
+        stages["attn_fwd"] += ev.ms(f[1], f[2])
+        stages["bwd_prologue"] += ev.ms(b[0], b[1])
+        stages["attn_dkdv"] += ev.ms(b[1], b[2])
+        stages["attn_dq"] += ev.ms(b[2], b[3])
+    stages = {k: v / args.steps for k, v in stages.items()}
+    for f, b in evs:
+        ev.free(f)
+        ev.free(b)
+    flops = 12.0 * shape.D * shape.Hq * P
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"step {ms:.3f} ms, useful {tflops:.1f} TFLOP/s, stages (ms): "
+        + ", ".join(f"{k}={v:.4f}" for k, v in stages.items()))
+
+    # roofline of the dominant kernel: useful flops per launch / its time
+    per_pair = {"attn_fwd": 4.0, "attn_dkdv": 6.0, "attn_dq": 2.0}
+    dom = max(per_pair, key=lambda k: stages[k])
+    achieved = per_pair[dom] * shape.D * shape.Hq * P / (stages[dom] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                "avg_ms": round(stages[dom], 4)}
+
+    result = {
+        "metric": "masked-attn fwd+bwd useful TFLOP/s & tokens/s; 1-pass vs N-pass speedup",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "packed_fwd_bwd: 2 rows x 16384 tokens, 32 q / 8 kv heads, D=128, "
+                               "layout + fwd + bwd per step",
+                   "rows": shape.B, "row_tokens": shape.L, "Hq": shape.Hq, "Hkv": shape.Hkv, "D": shape.D,
+                   "useful_pairs": P, "conversation_tokens": conv_tokens, "packed_tokens": packed_tokens},
+        "tokens_per_s": round(conv_tokens / (ms * 1e-3), 1),
+        "packed_tokens_per_s": round(packed_tokens / (ms * 1e-3), 1),
+        "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "roofline": roofline,
+    }
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        result["depth_sweep"] = depth_sweep(torch, Bd, dev, [2, 4, 8, 16, 32], args.sweep_steps)
+        result["kpass"] = kpass_sweep(torch, Bd, dev, args.sweep_steps)
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample ...")
+        result["cpu_baseline"] = cpu_baseline(rows, shape.L, shape, t_np)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

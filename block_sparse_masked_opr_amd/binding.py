@@ -46,7 +46,8 @@ class OprAttnIn(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float), ("rope_theta", ctypes.c_double),
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("layout", OprLayout),
-                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32)]
+                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("timing_events", ctypes.c_void_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -90,10 +91,6 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    return None if t is None else t.data_ptr()
-
-
 def opr_build_layout_workspace_size(B: int, L: int, n_convs: int, n_turns: int) -> int:
     return int(LIB.opr_build_layout_workspace_size(B, L, n_convs, n_turns))
 
@@ -135,13 +132,17 @@ class Layout:
 
 def opr_build_layout(rows: Sequence, L: int, block_q: int = OPR_ATTN_BLOCK,
                      block_k: int = OPR_ATTN_BLOCK, device="cuda",
-                     workspace: Optional[torch.Tensor] = None) -> Layout:
-    """rows: list of rows, each a list of conversations of (h, t, r_in, r_out) turns."""
+                     workspace: Optional[torch.Tensor] = None, out: Optional[Layout] = None) -> Layout:
+    """rows: list of rows, each a list of conversations of (h, t, r_in, r_out)
+    turns.  ``out``: a Layout of the same (B, L, block_q, block_k) to refill."""
     device = torch.device(device)
     B = len(rows)
     cpr, tpc, turns = inputs.flatten_rows(rows)
     C, T = len(tpc), len(turns)
-    lay = Layout(B, L, block_q, block_k, device)
+    if out is not None and (out.B, out.L, out.block_q, out.block_k) == (B, L, block_q, block_k):
+        lay = out
+    else:
+        lay = Layout(B, L, block_q, block_k, device)
     need = opr_build_layout_workspace_size(B, L, C, T)
     if need == 0:
         raise OprError(OPR_E_INVALID, "opr_build_layout_workspace_size")
@@ -150,15 +151,15 @@ def opr_build_layout(rows: Sequence, L: int, block_q: int = OPR_ATTN_BLOCK,
     cpr = np.ascontiguousarray(cpr, dtype=np.int32)
     tpc = np.ascontiguousarray(tpc if C else np.zeros(1, np.int32), dtype=np.int32)
     turns = np.ascontiguousarray(turns if T else np.zeros((1, 4), np.int32), dtype=np.int32)
-    out = lay.c_struct()
+    cs = lay.c_struct()
     st = LIB.opr_build_layout(B, L, block_q, block_k, cpr.ctypes.data, tpc.ctypes.data,
                               turns.ctypes.data, workspace.data_ptr(), workspace.numel(),
-                              ctypes.byref(out), _stream(device))
+                              ctypes.byref(cs), _stream(device))
     _check(st, "opr_build_layout")
     return lay
 
 
-def _attn_in(q, k, v, lay: Layout, theta: float, scale: float) -> OprAttnIn:
+def _attn_in(q, k, v, lay: Layout, theta: float, scale: float, events=None) -> OprAttnIn:
     B, L, Hq, D = q.shape
     Hkv = k.shape[2]
     for name, t, H in (("q", q, Hq), ("k", k, Hkv), ("v", v, Hkv)):
@@ -167,14 +168,16 @@ def _attn_in(q, k, v, lay: Layout, theta: float, scale: float) -> OprAttnIn:
     if (lay.B, lay.L) != (B, L):
         raise ValueError("layout built for a different B or L")
     return OprAttnIn(B, L, Hq, Hkv, D, float(scale), float(theta), q.data_ptr(), k.data_ptr(),
-                     v.data_ptr(), lay.c_struct(), lay.block_q, lay.block_k)
+                     v.data_ptr(), lay.c_struct(), lay.block_q, lay.block_k,
+                     None if events is None else ctypes.addressof(events))
 
 
 def opr_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lay: Layout,
                  theta: float = 1.0e6, scale: float = 0.0,
-                 workspace: Optional[torch.Tensor] = None, out=None):
-    """Returns (o bf16 [B, L, Hq, D], lse fp32 [B, Hq, L])."""
-    a = _attn_in(q, k, v, lay, theta, scale)
+                 workspace: Optional[torch.Tensor] = None, out=None, events=None):
+    """Returns (o bf16 [B, L, Hq, D], lse fp32 [B, Hq, L]).  ``events``: optional
+    ctypes array of 3 hipEvent_t handles recorded around the stages."""
+    a = _attn_in(q, k, v, lay, theta, scale, events)
     B, L, Hq, D = q.shape
     need = opr_attn_workspace_size(B, L, Hq, k.shape[2], D, False)
     if workspace is None or workspace.numel() < need:
@@ -191,9 +194,10 @@ def opr_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lay: Layout,
 
 
 def opr_attn_bwd(q, k, v, o, lse, dout, lay: Layout, theta: float = 1.0e6, scale: float = 0.0,
-                 workspace: Optional[torch.Tensor] = None, out=None):
-    """Returns (dq, dk, dv) fp32 with the shapes of q, k, v."""
-    a = _attn_in(q, k, v, lay, theta, scale)
+                 workspace: Optional[torch.Tensor] = None, out=None, events=None):
+    """Returns (dq, dk, dv) fp32 with the shapes of q, k, v.  ``events``:
+    optional ctypes array of 4 hipEvent_t handles recorded around the stages."""
+    a = _attn_in(q, k, v, lay, theta, scale, events)
     B, L, Hq, D = q.shape
     if dout.dtype != torch.bfloat16 or not dout.is_contiguous() or dout.shape != q.shape:
         raise ValueError("dout must be contiguous bfloat16 shaped like q")

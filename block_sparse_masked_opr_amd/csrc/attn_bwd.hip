@@ -345,18 +345,19 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnParams p, float *dq
 
 void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParams *p);
 
+// ev (optional): events recorded before dK/dV, before dQ and after dQ.
 hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq, float *dk,
-                                   float *dv, const AttnWs &ws, hipStream_t s) {
+                                   float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev) {
   AttnParams p;
   fill_params(in, scale, ws, &p);
   const dim3 gk(p.NT, in.Hkv, in.B), gq(p.MT, in.Hq, in.B);
-  if (in.D == 64) {
-    attn_dkdv_kernel<64><<<gk, 256, 0, s>>>(p, dk, dv);
-    attn_dq_kernel<64><<<gq, 256, 0, s>>>(p, dq);
-  } else {
-    attn_dkdv_kernel<128><<<gk, 256, 0, s>>>(p, dk, dv);
-    attn_dq_kernel<128><<<gq, 256, 0, s>>>(p, dq);
-  }
+  if (ev) hipEventRecord(ev[0], s);
+  if (in.D == 64) attn_dkdv_kernel<64><<<gk, 256, 0, s>>>(p, dk, dv);
+  else attn_dkdv_kernel<128><<<gk, 256, 0, s>>>(p, dk, dv);
+  if (ev) hipEventRecord(ev[1], s);
+  if (in.D == 64) attn_dq_kernel<64><<<gq, 256, 0, s>>>(p, dq);
+  else attn_dq_kernel<128><<<gq, 256, 0, s>>>(p, dq);
+  if (ev) hipEventRecord(ev[2], s);
   return hipGetLastError();
 }
 

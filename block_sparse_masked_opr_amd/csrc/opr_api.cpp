@@ -18,7 +18,7 @@ void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const 
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, float *lse,
                                   const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq, float *dk,
-                                   float *dv, const AttnWs &ws, hipStream_t s);
+                                   float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev);
 
 static bool valid_block(int32_t b) { return b == 32 || b == 64 || b == 128; }
 
@@ -124,6 +124,10 @@ static float effective_scale(const opr_attn_in *in) {
   return in->softmax_scale > 0.0f ? in->softmax_scale : 1.0f / sqrtf((float)in->D);
 }
 
+static void mark(const opr_attn_in *in, int i, hipStream_t s) {
+  if (in->timing_events) hipEventRecord(in->timing_events[i], s);
+}
+
 static opr_status hip_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? OPR_OK : OPR_E_HIP;
@@ -211,11 +215,14 @@ opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *worksp
   if (ws_bytes < carve_attn_ws(nullptr, *in, 0, nullptr)) return OPR_E_CAPACITY;
   AttnWs ws;
   carve_attn_ws(workspace, *in, 0, &ws);
+  mark(in, 0, stream);
   launch_rope_table(*in, ws, stream);
   launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, nullptr, ws.eq, stream);
   launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, nullptr, ws.ek, stream);
   launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, nullptr, ws.vt, ws.ev, stream);
+  mark(in, 1, stream);
   if (launch_attn_fwd_kernel(*in, effective_scale(in), o, lse, ws, stream) != hipSuccess) return OPR_E_HIP;
+  mark(in, 2, stream);
   return hip_status();
 }
 
@@ -228,13 +235,15 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   if (ws_bytes < carve_attn_ws(nullptr, *in, 1, nullptr)) return OPR_E_CAPACITY;
   AttnWs ws;
   carve_attn_ws(workspace, *in, 1, &ws);
+  mark(in, 0, stream);
   launch_rope_table(*in, ws, stream);
   launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, ws.qt, ws.eq, stream);
   launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, ws.kt, ws.ek, stream);
   launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, ws.vr, nullptr, ws.ev, stream);
   launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, dout, nullptr, ws.dor, ws.dot, ws.edo, stream);
   launch_delta(*in, o, dout, lse, ws, stream);
-  if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream) != hipSuccess)
+  if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream,
+                              in->timing_events ? in->timing_events + 1 : nullptr) != hipSuccess)
     return OPR_E_HIP;
   return hip_status();
 }

@@ -131,6 +131,12 @@ typedef struct {
   const void *v;            /* bf16 [B][L][Hkv][D] */
   opr_layout layout;        /* from opr_build_layout(B, L, block_q, block_k, ...) */
   int32_t block_q, block_k; /* must both be OPR_ATTN_BLOCK */
+  /* Optional instrumentation, may be NULL: host array of events created by
+   * the caller (hipEventCreate).  opr_attn_fwd records [0] before its
+   * prologue, [1] before the attention kernel and [2] after it;
+   * opr_attn_bwd records [0] before its prologue, [1] before the dK/dV
+   * kernel, [2] before the dQ kernel and [3] after it. */
+  hipEvent_t *timing_events;
 } opr_attn_in;
 
 /*
