@@ -142,6 +142,93 @@ __device__ __forceinline__ TokMeta load_meta(const int32_t *conv, const int32_t 
   return m;
 }
 
+// ---------------------------------------------------------------------------
+// LDS tiles of 64 rows x D fp16.  A row is D/8 chunks of 16 bytes; chunk c of
+// row r is stored in slot c ^ swz(r), so that 16 lanes reading the same chunk
+// of 16 different rows (MFMA A operand) or 4 rows x 32 bytes (transposing
+// reads) hit distinct banks without padding, and a 1 KB run of LDS is filled
+// by one global_load_lds instruction (lane L writes bytes 16L..16L+15).
+#define OPR_LDS __attribute__((address_space(3)))
+typedef short __attribute__((ext_vector_type(4))) s16x4;
+
+template <int D>
+struct Tile {
+  static constexpr int NC = D / 8;       // chunks per row
+  static constexpr int RB = 2 * D;       // bytes per row
+  static constexpr int BYTES = 64 * RB;
+  __device__ static __forceinline__ int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static __forceinline__ int off(int r, int c) { return r * RB + ((c ^ swz(r)) << 4); }
+};
+
+// Asynchronous copy of 64 consecutive rows (row stride D elements) into a
+// swizzled LDS tile; the four waves of a workgroup share the D/8 instructions.
+template <int D>
+__device__ __forceinline__ void tile_load_async(const uint16_t *src, char *lds, int w, int lane) {
+  constexpr int NC = Tile<D>::NC, RPI = 1024 / Tile<D>::RB;
+#pragma unroll
+  for (int t = w; t < NC; t += 4) {
+    const int r = t * RPI + lane / NC;
+    const int c = (lane % NC) ^ Tile<D>::swz(r);
+    __builtin_amdgcn_global_load_lds(src + r * D + c * 8, (OPR_LDS void *)(lds + t * 1024), 16, 0, 0);
+  }
+}
+
+// Asynchronous copy of 64 consecutive 8-byte records (256 B per instruction).
+__device__ __forceinline__ void rec8_load_async(const void *src, char *lds, int lane) {
+  const char *g = static_cast<const char *>(src);
+  __builtin_amdgcn_global_load_lds(g + 4 * lane, (OPR_LDS void *)lds, 4, 0, 0);
+  __builtin_amdgcn_global_load_lds(g + 256 + 4 * lane, (OPR_LDS void *)(lds + 256), 4, 0, 0);
+}
+
+// Asynchronous copy of 64 consecutive floats.
+__device__ __forceinline__ void f32x64_load_async(const float *src, char *lds, int lane) {
+  __builtin_amdgcn_global_load_lds(src + lane, (OPR_LDS void *)lds, 4, 0, 0);
+}
+
+// Wait for this thread's outstanding memory operations (including the
+// asynchronous LDS fills), then for the whole workgroup.
+__device__ __forceinline__ void wait_all_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+template <int D>
+__device__ __forceinline__ f16x8 tile_row8(const char *lds, int r, int c) {
+  return *reinterpret_cast<const f16x8 *>(lds + Tile<D>::off(r, c));
+}
+
+__device__ __forceinline__ s16x4 ds_read_tr16(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((OPR_LDS s16x4 *)p);
+}
+
+// Transposed MFMA operand from a row-major tile X[row][col]: lane l receives
+// X[r0 + 0..7][col0 + l % 32] with r0 = rbase + 8 * (l / 32) and
+// col0 = cbase; i.e. 8 consecutive rows of its own column.  Built from two
+// ds_read_b64_tr_b16: inside each 16-lane group, the lane that points at
+// row r0 + j / 4, columns c + 4 * (j % 4) .. +3 supplies column entries so
+// that lane i receives rows r0 .. r0 + 3 of column c + i.
+template <int D>
+__device__ __forceinline__ f16x8 tile_col8(const char *lds, int rbase, int cbase, int lane) {
+  const int G = lane >> 4, j = lane & 15;
+  const int col = cbase + 16 * (G & 1) + 4 * (j & 3);
+  const int r = rbase + 8 * (G >> 1) + (j >> 2);
+  const int cb = (col & 7) * 2;
+  const s16x4 lo = ds_read_tr16(lds + Tile<D>::off(r, col >> 3) + cb);
+  const s16x4 hi = ds_read_tr16(lds + Tile<D>::off(r + 4, col >> 3) + cb);
+  typedef short __attribute__((ext_vector_type(8))) s16x8;
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Remap the linear block id so that each XCD walks a contiguous range
+// of work items: neighbouring items share K/V (or Q/dO) tiles in that L2.
+__device__ __forceinline__ int64_t xcd_work_item(int64_t nitems) {
+  const int64_t per = (nitems + 7) / 8;
+  const int64_t bid = blockIdx.x;
+  return (bid & 7) * per + (bid >> 3);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -156,9 +243,10 @@ struct AttnParams {
   const int32_t *q_nnz, *q_list, *k_nnz, *k_list;
   const float2 *rope;                    // [B][Lp][D/2]
   // fp16 bits, scaled per 64-token block (see the number format above)
-  const uint16_t *qr, *kr, *vt, *vr, *qt, *kt, *dor, *dot;
+  const uint16_t *qr, *kr, *vr, *qt, *kt, *dor, *dot;
   // block exponents [B][H][Lp/64] of q, k, v, dout
   const int32_t *eq, *ek, *ev, *edo;
+  const int2 *meta;                      // [B][Lp] (conv, turn * 8 + type); conv -1 for PAD / past L
   const float *delta, *lse2;
 };
 

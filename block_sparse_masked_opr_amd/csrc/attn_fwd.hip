@@ -1,40 +1,92 @@
 // Forward kernel of the one-pass masked attention (gfx950).
 //
 // One workgroup of 4 waves per (128-query tile m, q head h, row b); wave w
-// owns queries m*128 + 32w .. +31, one query per lane column.  The kernel walks
-// the ascending list of non-empty 128-key tiles of q-tile m, half a tile (64
-// keys) at a time, skipping halves whose 32x32 sub-blocks are all empty.  Per
-// half: K (after RoPE) and V^T are staged in LDS; each wave computes
-// S^T = K Q^T on its non-empty 32x32 sub-blocks with fp16 MFMA (fp32
-// accumulate), applies the mask predicate only on partial sub-blocks, updates
-// the online softmax (base-2 exponent with log2(e) folded into the scale) and
-// accumulates O^T += V^T P^T.  The epilogue normalises, writes O (bf16) and
-// the natural-log LSE.  Operands are fp16 with per-64-token exponents: the q
-// and k exponents are folded into the score scale, the v exponent into the
-// units of the O accumulator (rescaled together with the softmax correction).
+// owns queries m*128 + 32w .. +31, one query per lane column.  Work items are
+// remapped so each XCD walks a contiguous range of (row, kv head, q-tile,
+// head-in-group): the heads of one kv group and neighbouring q-tiles run side
+// by side and share K/V tiles in that XCD's L2.
+//
+// The non-empty 64-key halves of the q-tile's non-empty 128-key tiles are
+// first compacted into a stage list in LDS (a ballot over the tile list and
+// its 32x32 sub-block classes), so the main loop has no dependent global
+// loads.  Stages are double buffered: while stage i is computed, K and V of
+// stage i+1 stream from memory straight into LDS (global_load_lds); one
+// barrier per stage.  Per stage each wave computes S^T = K Q^T on its
+// non-empty 32x32 sub-blocks with fp16 MFMA (fp32 accumulate), applies the
+// mask predicate only on partial sub-blocks, updates the online softmax
+// (base-2 exponent, log2(e) folded into the scale) and accumulates
+// O^T += V^T P^T, reading V^T from the row-major V tile with transposing LDS
+// reads.  The epilogue normalises, writes O (bf16) and the natural-log LSE.
+// Operands are fp16 with per-64-token exponents: the q and k exponents are
+// folded into the score scale, the v exponent into the units of the O
+// accumulator (rescaled together with the softmax correction).
 #include "attn_common.h"
 #include "opr_internal.h"
 
 namespace opr {
 namespace {
 
+constexpr int kStageCap = 1024;  // stage descriptors per list chunk
+
+// Fills stages[] (wave 0 only) with the non-empty 64-key halves of the tiles
+// q_list[t ...]; returns the count and advances *t past the tiles consumed.
+// Descriptor: (first key, classes | exponents): the 2-bit class of sub-block
+// (wave w, 32-key block kb) at bits 4w + 2kb, the k and v block exponents
+// (+128) at bits 16..23 and 24..31.
+__device__ int build_q_stages(const int32_t *lst, const uint32_t *subs, const int32_t *ekp,
+                              const int32_t *evp, int nnz, int *t, uint2 *stages, int lane) {
+  int count = 0;
+  while (*t < nnz && count + 64 <= kStageCap) {
+    const int tile = *t + (lane >> 1), kh = lane & 1;
+    uint32_t cls = 0;
+    int k0 = 0;
+    if (tile < nnz) {
+      const int n = lst[tile];
+      const uint32_t sub = subs[n];
+      k0 = n * 128 + 64 * kh;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) cls |= ((sub >> (2 * (4 * w + 2 * kh + kb))) & 3u) << (4 * w + 2 * kb);
+    }
+    const uint64_t bal = __ballot(cls != 0);
+    if (cls != 0) {
+      const uint32_t ex = ((uint32_t)(ekp[k0 >> 6] + 128) << 16) | ((uint32_t)(evp[k0 >> 6] + 128) << 24);
+      stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint2((uint32_t)k0, cls | ex);
+    }
+    count += __popcll(bal);
+    *t += 32;
+  }
+  if (*t > nnz) *t = nnz;
+  return count;
+}
+
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t *o, float *lse) {
-  constexpr int KS = D + 8;    // LDS row stride (elements) of the K tile
-  constexpr int VS = 64 + 8;   // LDS row stride of the V^T tile
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t *o, float *lse) {
   constexpr int NS = D / 16;   // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;  // 32-wide blocks of the head dim
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vts[D * VS];
-  __shared__ TokMeta kmeta[64];
+  constexpr int TB = Tile<D>::BYTES;
+  // per buffer: K tile, V tile, 64 key records
+  constexpr int BUF = 2 * TB + 512;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  __shared__ uint2 stages[kStageCap];
+  __shared__ int sh_count, sh_next;
 
-  const int m = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t nitems = (int64_t)p.B * p.Hq * p.MT;
+  const int64_t u = xcd_work_item(nitems);
+  if (u >= nitems) return;
+  const int j = (int)(u % p.group);
+  int64_t rest = u / p.group;
+  const int m = (int)(rest % p.MT);
+  rest /= p.MT;
+  const int kvh = (int)(rest % p.Hkv);
+  const int b = (int)(rest / p.Hkv);
+  const int h = kvh * p.group + j;
+
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
-  const int kvh = h / p.group;
   const int q = m * 128 + 32 * w + li;
-  const int64_t row_base = (int64_t)b * p.L;
-
   const int nblk = p.Lp / 64;
+
   f16x8 qb[NS];
   {
     const uint16_t *qrow = p.qr + (((int64_t)b * p.Hq + h) * p.Lp + q) * D;
@@ -44,8 +96,9 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
   const int eq = p.eq[((int64_t)b * p.Hq + h) * nblk + (q >> 6)];
   const int32_t *ekp = p.ek + ((int64_t)b * p.Hkv + kvh) * nblk;
   const int32_t *evp = p.ev + ((int64_t)b * p.Hkv + kvh) * nblk;
-  int ev_ref = 0;  // O accumulator holds O * sum(p) * 2^(kPExp + ev_ref)
-  const TokMeta qm = load_meta(p.tok_conv, p.tok_turn, p.tok_type, row_base, q, p.L);
+  const int2 qmi = p.meta[(int64_t)b * p.Lp + q];
+  const TokMeta qm = {qmi.x, qmi.y};
+  int ev_ref = 0;  // the O accumulator holds O * sum(p) * 2^(kPExp + ev_ref)
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -54,49 +107,62 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
 
   const int64_t trow = (int64_t)b * p.MT + m;
   const int nnz = p.q_nnz[trow];
-  const uint16_t *kbase = p.kr + ((int64_t)b * p.Hkv + kvh) * p.Lp * D;
-  const uint16_t *vbase = p.vt + ((int64_t)b * p.Hkv + kvh) * D * p.Lp;
+  const int32_t *lst = p.q_list + trow * p.NT;
+  const uint32_t *subs = p.sub_class + trow * p.NT;
+  const int64_t kvoff = ((int64_t)b * p.Hkv + kvh) * p.Lp;
+  const uint16_t *kbase = p.kr + kvoff * D;
+  const uint16_t *vbase = p.vr + kvoff * D;
+  const int2 *mbase = p.meta + (int64_t)b * p.Lp;
 
-  for (int it = 0; it < nnz; ++it) {
-    const int n = p.q_list[trow * p.NT + it];
-    const uint32_t sub = p.sub_class[trow * p.NT + n];
-#pragma unroll 1
-    for (int kh = 0; kh < 2; ++kh) {
-      if ((sub & (kh ? 0xF0F0F0F0u : 0x0F0F0F0Fu)) == 0) continue;
-      const int k0 = n * 128 + 64 * kh;
-      __syncthreads();
-      // K tile: 64 rows x D, 16-byte chunks
-#pragma unroll
-      for (int c = tid; c < 64 * D / 8; c += 256) {
-        const int r = c / (D / 8), ch = c % (D / 8);
-        *reinterpret_cast<uint4 *>(&Ks[r * KS + ch * 8]) =
-            *reinterpret_cast<const uint4 *>(kbase + (int64_t)(k0 + r) * D + ch * 8);
+  int tnext = 0;
+  while (tnext < nnz) {
+    __syncthreads();  // previous chunk's stages and buffers are no longer read
+    if (w == 0) {
+      int t = tnext;
+      const int c = build_q_stages(lst, subs, ekp, evp, nnz, &t, stages, lane);
+      if (lane == 0) {
+        sh_count = c;
+        sh_next = t;
       }
-      // V^T tile: D rows x 64 keys
-#pragma unroll
-      for (int c = tid; c < D * 8; c += 256) {
-        const int r = c >> 3, ch = c & 7;
-        *reinterpret_cast<uint4 *>(&Vts[r * VS + ch * 8]) =
-            *reinterpret_cast<const uint4 *>(vbase + (int64_t)r * p.Lp + k0 + ch * 8);
+    }
+    __syncthreads();
+    const int ns = sh_count;
+    tnext = sh_next;
+    if (ns == 0) continue;
+    {
+      const int k0 = (int)stages[0].x;
+      tile_load_async<D>(kbase + (int64_t)k0 * D, smem, w, lane);
+      tile_load_async<D>(vbase + (int64_t)k0 * D, smem + TB, w, lane);
+      if (w == 0) rec8_load_async(mbase + k0, smem + 2 * TB, lane);
+    }
+    for (int i = 0; i < ns; ++i) {
+      wait_all_and_barrier();
+      const char *buf = smem + (i & 1) * BUF;
+      if (i + 1 < ns) {
+        char *nb = smem + ((i + 1) & 1) * BUF;
+        const int k1 = (int)stages[i + 1].x;
+        tile_load_async<D>(kbase + (int64_t)k1 * D, nb, w, lane);
+        tile_load_async<D>(vbase + (int64_t)k1 * D, nb + TB, w, lane);
+        if (w == 0) rec8_load_async(mbase + k1, nb + 2 * TB, lane);
       }
-      if (tid < 64) kmeta[tid] = load_meta(p.tok_conv, p.tok_turn, p.tok_type, row_base, k0 + tid, p.L);
-      __syncthreads();
-
-      const uint32_t c0 = (sub >> (2 * (4 * w + 2 * kh))) & 3u;
-      const uint32_t c1 = (sub >> (2 * (4 * w + 2 * kh + 1))) & 3u;
+      const uint2 desc = stages[i];
+      const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
       if ((c0 | c1) == 0) continue;
       const uint32_t cls[2] = {c0, c1};
-      const int ek = ekp[k0 >> 6], ev = evp[k0 >> 6];
+      const int k0 = (int)desc.x;
+      const int ek = (int)((desc.y >> 16) & 255u) - 128, ev = (int)(desc.y >> 24) - 128;
       const float fs = ldexpf(p.scale_log2, -(eq + ek));
+      const char *Kt = buf, *Vt = buf + TB;
+      const int2 *kmeta = reinterpret_cast<const int2 *>(buf + 2 * TB);
 
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = zero_f32x16();
         if (cls[kb] == 0) continue;
-        const uint16_t *arow = &Ks[(32 * kb + kperm(li)) * KS + 8 * g];
+        const int r = 32 * kb + kperm(li);
 #pragma unroll
-        for (int st = 0; st < NS; ++st) s[kb] = mfma32x32x16(ld_f16x8(arow + 16 * st), qb[st], s[kb]);
+        for (int st = 0; st < NS; ++st) s[kb] = mfma32x32x16(tile_row8<D>(Kt, r, 2 * st + g), qb[st], s[kb]);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -108,7 +174,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
             x = -INFINITY;
           } else if (cls[kb] == 1) {
             const int kl = 32 * kb + acc_row(r, g);
-            if (!mask_allows(q, qm, k0 + kl, kmeta[kl])) x = -INFINITY;
+            const int2 km = kmeta[kl];
+            if (!mask_allows(q, qm, k0 + kl, TokMeta{km.x, km.y})) x = -INFINITY;
           }
           s[kb][r] = x;
           mx = fmaxf(mx, x);
@@ -123,10 +190,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
       ev_ref = ev;
       lrow *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= ofac;
-      }
+      for (int db = 0; db < NDB; ++db) oacc[db] *= ofac;
       const float mshift = msafe - (float)kPExp;
       f16x8 pb[2][2];
 #pragma unroll
@@ -142,10 +206,10 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
       for (int kb = 0; kb < 2; ++kb) {
         if (cls[kb] == 0) continue;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const uint16_t *arow = &Vts[(32 * db + li) * VS + 32 * kb + 8 * g];
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) oacc[db] = mfma32x32x16(ld_f16x8(arow + 16 * hh), pb[kb][hh], oacc[db]);
+          for (int db = 0; db < NDB; ++db)
+            oacc[db] = mfma32x32x16(tile_col8<D>(Vt, 32 * kb + 16 * hh, 32 * db, lane), pb[kb][hh], oacc[db]);
         }
       }
     }
@@ -154,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(AttnParams p, uint16_t
   const float lsum = lrow + __shfl_xor(lrow, 32);
   if (q < p.L) {
     const float inv = lsum > 0.0f ? ldexpf(1.0f / lsum, -ev_ref) : 0.0f;
-    uint16_t *orow = o + ((row_base + q) * p.Hq + h) * D;
+    uint16_t *orow = o + (((int64_t)b * p.L + q) * p.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -179,7 +243,8 @@ hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, f
                                   const AttnWs &ws, hipStream_t s) {
   AttnParams p;
   fill_params(in, scale, ws, &p);
-  const dim3 grid(p.MT, in.Hq, in.B);
+  const int64_t nitems = (int64_t)in.B * in.Hq * p.MT;
+  const unsigned grid = (unsigned)(8 * ((nitems + 7) / 8));
   uint16_t *o16 = static_cast<uint16_t *>(o);
   if (in.D == 64) attn_fwd_kernel<64><<<grid, 256, 0, s>>>(p, o16, lse);
   else attn_fwd_kernel<128><<<grid, 256, 0, s>>>(p, o16, lse);

@@ -122,6 +122,21 @@ __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_
   }
 }
 
+// meta[b][t] = (conv, turn * 8 + type) for t < L, (-1, PAD) past L.
+__global__ __launch_bounds__(256) void meta_kernel(int32_t B, int32_t L, int32_t Lp, const int32_t *conv,
+                                                   const int32_t *turn, const uint8_t *type, int2 *meta) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)B * Lp) return;
+  const int32_t t = (int32_t)(gid % Lp);
+  const int64_t b = gid / Lp;
+  int2 m = make_int2(-1, 4);
+  if (t < L) {
+    const int64_t i = b * L + t;
+    m = make_int2(conv[i], (turn[i] << 3) | type[i]);
+  }
+  meta[gid] = m;
+}
+
 // delta[b][h][t] = sum_d dout * o (float32 over bf16 inputs);
 // lse2[b][h][t] = lse * log2(e), +inf where the row has no key (lse = -inf)
 // or t >= L, so that recomputed probabilities are exactly 0 there.
@@ -167,6 +182,12 @@ void launch_pack(bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const v
 }
 
 }  // namespace
+
+void launch_meta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+  const int64_t total = (int64_t)in.B * ws.Lp;
+  meta_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(in.B, in.L, ws.Lp, in.layout.tok_conv,
+                                                              in.layout.tok_turn, in.layout.tok_type, ws.meta);
+}
 
 void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int32_t half = in.D / 2;

@@ -10,6 +10,7 @@ namespace opr {
 
 // launchers defined in the .hip files
 void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
+void launch_meta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x,
                      const float2 *table, uint16_t *rows, uint16_t *trans, int32_t *exps,
                      hipStream_t s);
@@ -37,10 +38,9 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   w.eq = cv.take<int32_t>(qb);
   w.ek = cv.take<int32_t>(kb);
   w.ev = cv.take<int32_t>(kb);
-  if (!is_bwd) {
-    w.vt = cv.take<uint16_t>(kn);
-  } else {
-    w.vr = cv.take<uint16_t>(kn);
+  w.meta = cv.take<int2>((size_t)in.B * Lp);
+  w.vr = cv.take<uint16_t>(kn);
+  if (is_bwd) {
     w.qt = cv.take<uint16_t>(qn);
     w.kt = cv.take<uint16_t>(kn);
     w.dor = cv.take<uint16_t>(qn);
@@ -77,7 +77,6 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->rope = ws.rope;
   p->qr = ws.qr;
   p->kr = ws.kr;
-  p->vt = ws.vt;
   p->vr = ws.vr;
   p->qt = ws.qt;
   p->kt = ws.kt;
@@ -87,6 +86,7 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->ek = ws.ek;
   p->ev = ws.ev;
   p->edo = ws.edo;
+  p->meta = ws.meta;
   p->delta = ws.delta;
   p->lse2 = ws.lse2;
 }
@@ -219,7 +219,8 @@ opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *worksp
   launch_rope_table(*in, ws, stream);
   launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, nullptr, ws.eq, stream);
   launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, nullptr, ws.ek, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, nullptr, ws.vt, ws.ev, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, ws.vr, nullptr, ws.ev, stream);
+  launch_meta(*in, ws, stream);
   mark(in, 1, stream);
   if (launch_attn_fwd_kernel(*in, effective_scale(in), o, lse, ws, stream) != hipSuccess) return OPR_E_HIP;
   mark(in, 2, stream);
@@ -242,6 +243,7 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, ws.vr, nullptr, ws.ev, stream);
   launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, dout, nullptr, ws.dor, ws.dot, ws.edo, stream);
   launch_delta(*in, o, dout, lse, ws, stream);
+  launch_meta(*in, ws, stream);
   if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream,
                               in->timing_events ? in->timing_events + 1 : nullptr) != hipSuccess)
     return OPR_E_HIP;
