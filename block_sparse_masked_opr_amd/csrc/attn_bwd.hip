@@ -7,20 +7,26 @@
 // and dQ, dK are rotated back by the transposed RoPE rotation.
 //
 // attn_dkdv_kernel: one workgroup per (128-key tile n, kv head, row); wave w
-//   owns keys n*128 + 32w .. +31, one key per lane column, K' and V of its key
-//   in registers.  It walks the ascending list of non-empty q-tiles of k-tile
-//   n, for every q head of the group, 64 queries at a time (Q', dO and their
-//   transposes staged in LDS), and keeps dK^T, dV^T in accumulators.  Each key
-//   is owned by exactly one workgroup: no atomics.
-// attn_dq_kernel: one workgroup per (128-query tile, q head, row), like the
-//   forward kernel; S and dP^T are recomputed per non-empty sub-block and
-//   dQ^T += K'^T dS^T.
+//   owns keys n*128 + 32w .. +31, one key per lane column, K' and V of its
+//   key in registers.  Its stages are (q-tile of k_list, head of the group,
+//   64-query half) with a non-empty sub-block; each streams the Q' and dO rows
+//   of the stage into LDS (double buffered, global_load_lds) and reads Q'^T
+//   and dO^T from the same row-major tiles with transposing LDS reads.
+//   dK^T and dV^T stay in accumulators; each key is owned by exactly one
+//   workgroup: no atomics.
+// attn_dq_kernel: one workgroup per (128-query tile, q head, row), pipelined
+//   like the forward kernel over the K' / V tiles; S and dP^T are recomputed
+//   per non-empty sub-block and dQ^T += K'^T dS^T (K'^T from the K' tile).
+// Work items are remapped so each XCD walks a contiguous range (shared tiles
+// stay in that XCD's L2).
+//
 // Operands are fp16 with per-64-token exponents (q, k, v, dout); P is stored
 // as fp16(P * 2^kPExp) and dS in the units of dP (2^(e_v + e_dout)) shifted
 // down by 2^kDsShift.  The accumulators carry power-of-two units that are
 // rescaled whenever a block with other exponents arrives, and removed in the
 // epilogue.
 #include "attn_common.h"
+#include "attn_sched.h"
 #include "opr_internal.h"
 
 namespace opr {
@@ -28,25 +34,28 @@ namespace {
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *dk, float *dv) {
-  constexpr int RS = D + 8;    // LDS row stride of row-major tiles
-  constexpr int TS = 64 + 8;   // LDS row stride of transposed tiles
   constexpr int NS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int HALF_DB = NDB / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qts[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t dOts[D * TS];
-  __shared__ __attribute__((aligned(16))) float lse2s[64];
-  __shared__ __attribute__((aligned(16))) float deltas[64];
-  __shared__ TokMeta qmeta[64];
+  constexpr int TB = Tile<D>::BYTES;
+  // per buffer: Q' tile, dO tile, lse2[64], delta[64], 64 query records
+  constexpr int BUF = 2 * TB + 1024;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  __shared__ uint2 stages[kStageCap];
+  __shared__ int sh_count;
+  __shared__ int64_t sh_next;
 
-  const int n = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int64_t nitems = (int64_t)p.B * p.Hkv * p.NT;
+  const int64_t u = xcd_work_item(nitems);
+  if (u >= nitems) return;
+  const int n = (int)(u % p.NT);
+  const int kvh = (int)((u / p.NT) % p.Hkv);
+  const int b = (int)(u / ((int64_t)p.NT * p.Hkv));
+
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int key = n * 128 + 32 * w + li;
-  const int64_t row_base = (int64_t)b * p.L;
-
   const int nblk = p.Lp / 64;
+
   f16x8 kb_[NS], vb_[NS];
   {
     const int64_t off = (((int64_t)b * p.Hkv + kvh) * p.Lp + key) * D;
@@ -60,7 +69,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
   const int ev = p.ev[((int64_t)b * p.Hkv + kvh) * nblk + (key >> 6)];
   // dV^T accumulator units 2^(kPExp + uv), dK^T units 2^(uk + ev - kDsShift)
   int uv = 0, uk = 0;
-  const TokMeta km = load_meta(p.tok_conv, p.tok_turn, p.tok_type, row_base, key, p.L);
+  const int2 kmi = p.meta[(int64_t)b * p.Lp + key];
+  const TokMeta km = {kmi.x, kmi.y};
 
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -71,98 +81,112 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
 
   const int64_t tcol = (int64_t)b * p.NT + n;
   const int nnz = p.k_nnz[tcol];
-  for (int it = 0; it < nnz; ++it) {
-    const int m = p.k_list[tcol * p.MT + it];
-    const uint32_t sub = p.sub_class[((int64_t)b * p.MT + m) * p.NT + n];
-#pragma unroll 1
-    for (int hq = 0; hq < p.group; ++hq) {
-      const int h = kvh * p.group + hq;
-      const int64_t hrow = ((int64_t)b * p.Hq + h) * p.Lp;   // row index base in [B][Hq][Lp]
-#pragma unroll 1
-      for (int qh = 0; qh < 2; ++qh) {
-        if ((sub & (qh ? 0xFFFF0000u : 0x0000FFFFu)) == 0) continue;
-        const int q0 = m * 128 + 64 * qh;
-        __syncthreads();
-#pragma unroll
-        for (int c = tid; c < 64 * D / 8; c += 256) {
-          const int r = c / (D / 8), ch = c % (D / 8);
-          const int64_t src = (hrow + q0 + r) * D + ch * 8;
-          *reinterpret_cast<uint4 *>(&Qs[r * RS + ch * 8]) = *reinterpret_cast<const uint4 *>(p.qr + src);
-          *reinterpret_cast<uint4 *>(&dOs[r * RS + ch * 8]) = *reinterpret_cast<const uint4 *>(p.dor + src);
-        }
-#pragma unroll
-        for (int c = tid; c < D * 8; c += 256) {
-          const int r = c >> 3, ch = c & 7;
-          const int64_t src = (hrow * D) + (int64_t)r * p.Lp + q0 + ch * 8;  // [B][Hq][D][Lp]
-          *reinterpret_cast<uint4 *>(&Qts[r * TS + ch * 8]) = *reinterpret_cast<const uint4 *>(p.qt + src);
-          *reinterpret_cast<uint4 *>(&dOts[r * TS + ch * 8]) = *reinterpret_cast<const uint4 *>(p.dot + src);
-        }
-        if (tid < 64) {
-          lse2s[tid] = p.lse2[hrow + q0 + tid];
-          deltas[tid] = p.delta[hrow + q0 + tid];
-          qmeta[tid] = load_meta(p.tok_conv, p.tok_turn, p.tok_type, row_base, q0 + tid, p.L);
-        }
-        __syncthreads();
+  const int32_t *lst = p.k_list + tcol * p.MT;
+  const uint32_t *subs_b = p.sub_class + (int64_t)b * p.MT * p.NT;
+  const int64_t hbase = (int64_t)b * p.Hq + (int64_t)kvh * p.group;  // first head of the group
+  const int32_t *eqp = p.eq + hbase * nblk;
+  const int32_t *edop = p.edo + hbase * nblk;
+  const int2 *mbase = p.meta + (int64_t)b * p.Lp;
 
-        const uint32_t c0 = (sub >> (2 * (4 * (2 * qh) + w))) & 3u;
-        const uint32_t c1 = (sub >> (2 * (4 * (2 * qh + 1) + w))) & 3u;
-        if ((c0 | c1) == 0) continue;
-        const uint32_t cls[2] = {c0, c1};
-        const int eq = p.eq[((int64_t)b * p.Hq + h) * nblk + (q0 >> 6)];
-        const int edo = p.edo[((int64_t)b * p.Hq + h) * nblk + (q0 >> 6)];
-        const float fs = ldexpf(p.scale_log2, -(eq + ek));
-        const int udp = ev + edo;  // units of dP
+  auto issue = [&](uint32_t x, char *nb) {
+    const int q0 = (int)(x & 0xFFFFFFu), hj = (int)(x >> 24);
+    const int64_t row = (hbase + hj) * p.Lp + q0;
+    tile_load_async<D>(p.qr + row * D, nb, w, lane);
+    tile_load_async<D>(p.dor + row * D, nb + TB, w, lane);
+    if (w == 0) {
+      f32x64_load_async(p.lse2 + row, nb + 2 * TB, lane);
+    } else if (w == 1) {
+      f32x64_load_async(p.delta + row, nb + 2 * TB + 256, lane);
+    } else if (w == 2) {
+      rec8_load_async(mbase + q0, nb + 2 * TB + 512, lane);
+    }
+  };
 
-        f16x8 pb[2][2], dsb[2][2];
+  int64_t fnext = 0;
+  const int64_t ftotal = (int64_t)nnz * p.group * 2;
+  while (fnext < ftotal) {
+    __syncthreads();
+    if (w == 0) {
+      int64_t f = fnext;
+      const int c = build_k_stages(lst, subs_b, p.NT, n, p.group, eqp, edop, nblk, nnz, &f, stages, lane);
+      if (lane == 0) {
+        sh_count = c;
+        sh_next = f;
+      }
+    }
+    __syncthreads();
+    const int ns = sh_count;
+    fnext = sh_next;
+    if (ns == 0) continue;
+    issue(stages[0].x, smem);
+    for (int i = 0; i < ns; ++i) {
+      wait_all_and_barrier();
+      const char *buf = smem + (i & 1) * BUF;
+      if (i + 1 < ns) issue(stages[i + 1].x, smem + ((i + 1) & 1) * BUF);
+      const uint2 desc = stages[i];
+      const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
+      if ((c0 | c1) == 0) continue;
+      const uint32_t cls[2] = {c0, c1};
+      const int q0 = (int)(desc.x & 0xFFFFFFu);
+      const int eq = (int)((desc.y >> 16) & 255u) - 128, edo = (int)(desc.y >> 24) - 128;
+      const float fs = ldexpf(p.scale_log2, -(eq + ek));
+      const int udp = ev + edo;  // units of dP
+      const char *Qt = buf, *dOt = buf + TB;
+      const float *lse2s = reinterpret_cast<const float *>(buf + 2 * TB);
+      const float *deltas = reinterpret_cast<const float *>(buf + 2 * TB + 256);
+      const int2 *qmeta = reinterpret_cast<const int2 *>(buf + 2 * TB + 512);
+
+      f16x8 pb[2][2], dsb[2][2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if (cls[qb] == 0) {
+      for (int qb = 0; qb < 2; ++qb) {
+        if (cls[qb] == 0) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) pb[qb][hh] = dsb[qb][hh] = zero_f16x8();
-            continue;
-          }
-          f32x16 s = zero_f32x16(), dp = zero_f32x16();
-          const int arow = (32 * qb + kperm(li)) * RS + 8 * g;
-#pragma unroll
-          for (int st = 0; st < NS; ++st) {
-            s = mfma32x32x16(ld_f16x8(&Qs[arow + 16 * st]), kb_[st], s);
-            dp = mfma32x32x16(ld_f16x8(&dOs[arow + 16 * st]), vb_[st], dp);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ql = 32 * qb + acc_row(r, g);
-            const float x = s[r] * fs - lse2s[ql];
-            float pv = __builtin_amdgcn_exp2f(x);
-            float ps = __builtin_amdgcn_exp2f(x + (float)kPExp);
-            if (cls[qb] == 1 && !mask_allows(q0 + ql, qmeta[ql], key, km)) pv = ps = 0.0f;
-            const float ds = ldexpf(pv * (dp[r] - ldexpf(deltas[ql], udp)), -kDsShift);
-            pb[qb][r >> 3][r & 7] = (_Float16)ps;
-            dsb[qb][r >> 3][r & 7] = (_Float16)ds;
-          }
+          for (int hh = 0; hh < 2; ++hh) pb[qb][hh] = dsb[qb][hh] = zero_f16x8();
+          continue;
         }
-        if (edo != uv) {
-          const float f = ldexpf(1.0f, edo - uv);
+        f32x16 s = zero_f32x16(), dp = zero_f32x16();
+        const int r = 32 * qb + kperm(li);
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) dvacc[db] *= f;
-          uv = edo;
-        }
-        if (eq + edo != uk) {
-          const float f = ldexpf(1.0f, eq + edo - uk);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) dkacc[db] *= f;
-          uk = eq + edo;
+        for (int st = 0; st < NS; ++st) {
+          s = mfma32x32x16(tile_row8<D>(Qt, r, 2 * st + g), kb_[st], s);
+          dp = mfma32x32x16(tile_row8<D>(dOt, r, 2 * st + g), vb_[st], dp);
         }
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if (cls[qb] == 0) continue;
+        for (int rr = 0; rr < 16; ++rr) {
+          const int ql = 32 * qb + acc_row(rr, g);
+          const float x = s[rr] * fs - lse2s[ql];
+          float pv = __builtin_amdgcn_exp2f(x);
+          float ps = __builtin_amdgcn_exp2f(x + (float)kPExp);
+          if (cls[qb] == 1) {
+            const int2 qm = qmeta[ql];
+            if (!mask_allows(q0 + ql, TokMeta{qm.x, qm.y}, key, km)) pv = ps = 0.0f;
+          }
+          const float ds = ldexpf(pv * (dp[rr] - ldexpf(deltas[ql], udp)), -kDsShift);
+          pb[qb][rr >> 3][rr & 7] = (_Float16)ps;
+          dsb[qb][rr >> 3][rr & 7] = (_Float16)ds;
+        }
+      }
+      if (edo != uv) {
+        const float f = ldexpf(1.0f, edo - uv);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dvacc[db] *= f;
+        uv = edo;
+      }
+      if (eq + edo != uk) {
+        const float f = ldexpf(1.0f, eq + edo - uk);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dkacc[db] *= f;
+        uk = eq + edo;
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (cls[qb] == 0) continue;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
-            const int arow = (32 * db + li) * TS + 32 * qb + 8 * g;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              dvacc[db] = mfma32x32x16(ld_f16x8(&dOts[arow + 16 * hh]), pb[qb][hh], dvacc[db]);
-              dkacc[db] = mfma32x32x16(ld_f16x8(&Qts[arow + 16 * hh]), dsb[qb][hh], dkacc[db]);
-            }
+            dvacc[db] = mfma32x32x16(tile_col8<D>(dOt, 32 * qb + 16 * hh, 32 * db, lane), pb[qb][hh], dvacc[db]);
+            dkacc[db] = mfma32x32x16(tile_col8<D>(Qt, 32 * qb + 16 * hh, 32 * db, lane), dsb[qb][hh], dkacc[db]);
           }
         }
       }
@@ -170,7 +194,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
   }
 
   if (key < p.L) {
-    const int64_t out = ((row_base + key) * p.Hkv + kvh) * D;
+    const int64_t out = (((int64_t)b * p.L + key) * p.Hkv + kvh) * D;
     const float2 *cs = p.rope + ((int64_t)b * p.Lp + key) * (D / 2);
     const float kscale = ldexpf(p.scale, kDsShift - uk - ev);
     const float vscale = ldexpf(1.0f, -kPExp - uv);
@@ -204,38 +228,46 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnParams p, float *dq) {
-  constexpr int RS = D + 8;
-  constexpr int TS = 64 + 8;
   constexpr int NS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int HALF_DB = NDB / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kts[D * TS];
-  __shared__ TokMeta kmeta[64];
+  constexpr int TB = Tile<D>::BYTES;
+  constexpr int BUF = 2 * TB + 512;  // K' tile, V tile, 64 key records
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  __shared__ uint2 stages[kStageCap];
+  __shared__ int sh_count, sh_next;
 
-  const int m = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t nitems = (int64_t)p.B * p.Hq * p.MT;
+  const int64_t u = xcd_work_item(nitems);
+  if (u >= nitems) return;
+  const int j = (int)(u % p.group);
+  int64_t rest = u / p.group;
+  const int m = (int)(rest % p.MT);
+  rest /= p.MT;
+  const int kvh = (int)(rest % p.Hkv);
+  const int b = (int)(rest / p.Hkv);
+  const int h = kvh * p.group + j;
+
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
-  const int kvh = h / p.group;
   const int q = m * 128 + 32 * w + li;
-  const int64_t row_base = (int64_t)b * p.L;
+  const int nblk = p.Lp / 64;
   const int64_t hq_row = ((int64_t)b * p.Hq + h) * p.Lp + q;
 
-  const int nblk = p.Lp / 64;
   f16x8 qb[NS], dob[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     qb[s] = ld_f16x8(p.qr + hq_row * D + 16 * s + 8 * g);
     dob[s] = ld_f16x8(p.dor + hq_row * D + 16 * s + 8 * g);
   }
+  const float lse2_q = p.lse2[hq_row];
+  const float delta_q = p.delta[hq_row];
   const int eq = p.eq[((int64_t)b * p.Hq + h) * nblk + (q >> 6)];
   const int edo = p.edo[((int64_t)b * p.Hq + h) * nblk + (q >> 6)];
   const int32_t *ekp = p.ek + ((int64_t)b * p.Hkv + kvh) * nblk;
   const int32_t *evp = p.ev + ((int64_t)b * p.Hkv + kvh) * nblk;
+  const int2 qmi = p.meta[(int64_t)b * p.Lp + q];
+  const TokMeta qm = {qmi.x, qmi.y};
   int uq = 0;  // dQ^T accumulator units 2^(uq + edo - kDsShift), uq = e_k + e_v of the block
-  const float lse2_q = p.lse2[hq_row];
-  const float delta_q = p.delta[hq_row];
-  const TokMeta qm = load_meta(p.tok_conv, p.tok_turn, p.tok_type, row_base, q, p.L);
 
   f32x16 dqacc[NDB];
 #pragma unroll
@@ -243,38 +275,54 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnParams p, float *dq
 
   const int64_t trow = (int64_t)b * p.MT + m;
   const int nnz = p.q_nnz[trow];
-  const int64_t kvrow = ((int64_t)b * p.Hkv + kvh) * p.Lp;
-  for (int it = 0; it < nnz; ++it) {
-    const int n = p.q_list[trow * p.NT + it];
-    const uint32_t sub = p.sub_class[trow * p.NT + n];
-#pragma unroll 1
-    for (int kh = 0; kh < 2; ++kh) {
-      if ((sub & (kh ? 0xF0F0F0F0u : 0x0F0F0F0Fu)) == 0) continue;
-      const int k0 = n * 128 + 64 * kh;
-      __syncthreads();
-#pragma unroll
-      for (int c = tid; c < 64 * D / 8; c += 256) {
-        const int r = c / (D / 8), ch = c % (D / 8);
-        const int64_t src = (kvrow + k0 + r) * D + ch * 8;
-        *reinterpret_cast<uint4 *>(&Ks[r * RS + ch * 8]) = *reinterpret_cast<const uint4 *>(p.kr + src);
-        *reinterpret_cast<uint4 *>(&Vs[r * RS + ch * 8]) = *reinterpret_cast<const uint4 *>(p.vr + src);
-      }
-#pragma unroll
-      for (int c = tid; c < D * 8; c += 256) {
-        const int r = c >> 3, ch = c & 7;
-        *reinterpret_cast<uint4 *>(&Kts[r * TS + ch * 8]) =
-            *reinterpret_cast<const uint4 *>(p.kt + kvrow * D + (int64_t)r * p.Lp + k0 + ch * 8);
-      }
-      if (tid < 64) kmeta[tid] = load_meta(p.tok_conv, p.tok_turn, p.tok_type, row_base, k0 + tid, p.L);
-      __syncthreads();
+  const int32_t *lst = p.q_list + trow * p.NT;
+  const uint32_t *subs = p.sub_class + trow * p.NT;
+  const int64_t kvoff = ((int64_t)b * p.Hkv + kvh) * p.Lp;
+  const uint16_t *kbase = p.kr + kvoff * D;
+  const uint16_t *vbase = p.vr + kvoff * D;
+  const int2 *mbase = p.meta + (int64_t)b * p.Lp;
 
-      const uint32_t c0 = (sub >> (2 * (4 * w + 2 * kh))) & 3u;
-      const uint32_t c1 = (sub >> (2 * (4 * w + 2 * kh + 1))) & 3u;
+  int tnext = 0;
+  while (tnext < nnz) {
+    __syncthreads();
+    if (w == 0) {
+      int t = tnext;
+      const int c = build_q_stages(lst, subs, ekp, evp, nnz, &t, stages, lane);
+      if (lane == 0) {
+        sh_count = c;
+        sh_next = t;
+      }
+    }
+    __syncthreads();
+    const int ns = sh_count;
+    tnext = sh_next;
+    if (ns == 0) continue;
+    {
+      const int k0 = (int)stages[0].x;
+      tile_load_async<D>(kbase + (int64_t)k0 * D, smem, w, lane);
+      tile_load_async<D>(vbase + (int64_t)k0 * D, smem + TB, w, lane);
+      if (w == 0) rec8_load_async(mbase + k0, smem + 2 * TB, lane);
+    }
+    for (int i = 0; i < ns; ++i) {
+      wait_all_and_barrier();
+      const char *buf = smem + (i & 1) * BUF;
+      if (i + 1 < ns) {
+        char *nb = smem + ((i + 1) & 1) * BUF;
+        const int k1 = (int)stages[i + 1].x;
+        tile_load_async<D>(kbase + (int64_t)k1 * D, nb, w, lane);
+        tile_load_async<D>(vbase + (int64_t)k1 * D, nb + TB, w, lane);
+        if (w == 0) rec8_load_async(mbase + k1, nb + 2 * TB, lane);
+      }
+      const uint2 desc = stages[i];
+      const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
       if ((c0 | c1) == 0) continue;
       const uint32_t cls[2] = {c0, c1};
-      const int ek = ekp[k0 >> 6], ev = evp[k0 >> 6];
+      const int k0 = (int)desc.x;
+      const int ek = (int)((desc.y >> 16) & 255u) - 128, ev = (int)(desc.y >> 24) - 128;
       const float fs = ldexpf(p.scale_log2, -(eq + ek));
       const float dd = ldexpf(delta_q, ev + edo);  // delta in the units of dP
+      const char *Kt = buf, *Vt = buf + TB;
+      const int2 *kmeta = reinterpret_cast<const int2 *>(buf + 2 * TB);
 
       f16x8 dsb[2][2];
 #pragma unroll
@@ -284,18 +332,21 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnParams p, float *dq
           continue;
         }
         f32x16 s = zero_f32x16(), dpt = zero_f32x16();
-        const int arow = (32 * kb + kperm(li)) * RS + 8 * g;
+        const int r = 32 * kb + kperm(li);
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          s = mfma32x32x16(ld_f16x8(&Ks[arow + 16 * st]), qb[st], s);
-          dpt = mfma32x32x16(ld_f16x8(&Vs[arow + 16 * st]), dob[st], dpt);
+          s = mfma32x32x16(tile_row8<D>(Kt, r, 2 * st + g), qb[st], s);
+          dpt = mfma32x32x16(tile_row8<D>(Vt, r, 2 * st + g), dob[st], dpt);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kl = 32 * kb + acc_row(r, g);
-          float pv = __builtin_amdgcn_exp2f(s[r] * fs - lse2_q);
-          if (cls[kb] == 1 && !mask_allows(q, qm, k0 + kl, kmeta[kl])) pv = 0.0f;
-          dsb[kb][r >> 3][r & 7] = (_Float16)ldexpf(pv * (dpt[r] - dd), -kDsShift);
+        for (int rr = 0; rr < 16; ++rr) {
+          const int kl = 32 * kb + acc_row(rr, g);
+          float pv = __builtin_amdgcn_exp2f(s[rr] * fs - lse2_q);
+          if (cls[kb] == 1) {
+            const int2 kmv = kmeta[kl];
+            if (!mask_allows(q, qm, k0 + kl, TokMeta{kmv.x, kmv.y})) pv = 0.0f;
+          }
+          dsb[kb][rr >> 3][rr & 7] = (_Float16)ldexpf(pv * (dpt[rr] - dd), -kDsShift);
         }
       }
       if (ek + ev != uq) {
@@ -308,17 +359,17 @@ __global__ __launch_bounds__(256, 1) void attn_dq_kernel(AttnParams p, float *dq
       for (int kb = 0; kb < 2; ++kb) {
         if (cls[kb] == 0) continue;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int arow = (32 * db + li) * TS + 32 * kb + 8 * g;
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) dqacc[db] = mfma32x32x16(ld_f16x8(&Kts[arow + 16 * hh]), dsb[kb][hh], dqacc[db]);
+          for (int db = 0; db < NDB; ++db)
+            dqacc[db] = mfma32x32x16(tile_col8<D>(Kt, 32 * kb + 16 * hh, 32 * db, lane), dsb[kb][hh], dqacc[db]);
         }
       }
     }
   }
 
   if (q < p.L) {
-    float *out = dq + ((row_base + q) * p.Hq + h) * D;
+    float *out = dq + (((int64_t)b * p.L + q) * p.Hq + h) * D;
     const float2 *cs = p.rope + ((int64_t)b * p.Lp + q) * (D / 2);
     const float qscale = ldexpf(p.scale, kDsShift - uq - edo);
 #pragma unroll
@@ -350,7 +401,8 @@ hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq
                                    float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev) {
   AttnParams p;
   fill_params(in, scale, ws, &p);
-  const dim3 gk(p.NT, in.Hkv, in.B), gq(p.MT, in.Hq, in.B);
+  const int64_t nk = (int64_t)in.B * in.Hkv * p.NT, nq = (int64_t)in.B * in.Hq * p.MT;
+  const unsigned gk = (unsigned)(8 * ((nk + 7) / 8)), gq = (unsigned)(8 * ((nq + 7) / 8));
   if (ev) hipEventRecord(ev[0], s);
   if (in.D == 64) attn_dkdv_kernel<64><<<gk, 256, 0, s>>>(p, dk, dv);
   else attn_dkdv_kernel<128><<<gk, 256, 0, s>>>(p, dk, dv);

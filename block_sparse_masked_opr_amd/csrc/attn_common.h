@@ -243,7 +243,7 @@ struct AttnParams {
   const int32_t *q_nnz, *q_list, *k_nnz, *k_list;
   const float2 *rope;                    // [B][Lp][D/2]
   // fp16 bits, scaled per 64-token block (see the number format above)
-  const uint16_t *qr, *kr, *vr, *qt, *kt, *dor, *dot;
+  const uint16_t *qr, *kr, *vr, *dor;
   // block exponents [B][H][Lp/64] of q, k, v, dout
   const int32_t *eq, *ek, *ev, *edo;
   const int2 *meta;                      // [B][Lp] (conv, turn * 8 + type); conv -1 for PAD / past L

@@ -21,45 +21,11 @@
 // folded into the score scale, the v exponent into the units of the O
 // accumulator (rescaled together with the softmax correction).
 #include "attn_common.h"
+#include "attn_sched.h"
 #include "opr_internal.h"
 
 namespace opr {
 namespace {
-
-constexpr int kStageCap = 1024;  // stage descriptors per list chunk
-
-// Fills stages[] (wave 0 only) with the non-empty 64-key halves of the tiles
-// q_list[t ...]; returns the count and advances *t past the tiles consumed.
-// Descriptor: (first key, classes | exponents): the 2-bit class of sub-block
-// (wave w, 32-key block kb) at bits 4w + 2kb, the k and v block exponents
-// (+128) at bits 16..23 and 24..31.
-__device__ int build_q_stages(const int32_t *lst, const uint32_t *subs, const int32_t *ekp,
-                              const int32_t *evp, int nnz, int *t, uint2 *stages, int lane) {
-  int count = 0;
-  while (*t < nnz && count + 64 <= kStageCap) {
-    const int tile = *t + (lane >> 1), kh = lane & 1;
-    uint32_t cls = 0;
-    int k0 = 0;
-    if (tile < nnz) {
-      const int n = lst[tile];
-      const uint32_t sub = subs[n];
-      k0 = n * 128 + 64 * kh;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) cls |= ((sub >> (2 * (4 * w + 2 * kh + kb))) & 3u) << (4 * w + 2 * kb);
-    }
-    const uint64_t bal = __ballot(cls != 0);
-    if (cls != 0) {
-      const uint32_t ex = ((uint32_t)(ekp[k0 >> 6] + 128) << 16) | ((uint32_t)(evp[k0 >> 6] + 128) << 24);
-      stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint2((uint32_t)k0, cls | ex);
-    }
-    count += __popcll(bal);
-    *t += 32;
-  }
-  if (*t > nnz) *t = nnz;
-  return count;
-}
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t *o, float *lse) {

@@ -1,7 +1,7 @@
 // Prologue kernels of the attention path: the RoPE table at the strategic
 // position ids, head-major (optionally rotated) fp16 copies of q / k / v / dout
-// with one power-of-two scale per 64-token block, and their transposes, all
-// padded to a whole number of 128-token tiles with zeros; plus the backward
+// with one power-of-two scale per 64-token block, padded to a whole number of
+// 128-token tiles with zeros; the per-token mask records; and the backward
 // preprocessing delta = rowsum(dout * o).
 //
 // RoPE (rotate-half): pair (j, j + D/2) of a head vector is rotated by
@@ -140,33 +140,44 @@ __global__ __launch_bounds__(256) void meta_kernel(int32_t B, int32_t L, int32_t
 // delta[b][h][t] = sum_d dout * o (float32 over bf16 inputs);
 // lse2[b][h][t] = lse * log2(e), +inf where the row has no key (lse = -inf)
 // or t >= L, so that recomputed probabilities are exactly 0 there.
+// One wave per token: D/8 lanes read one head's 16-byte chunks, so a wave
+// covers 64/(D/8) heads per step with fully coalesced row reads.
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_t Lp, int32_t Hq,
                                                     const uint16_t *o, const uint16_t *dout,
                                                     const float *lse, float *delta, float *lse2) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, t, h)
-  if (gid >= (int64_t)B * Lp * Hq) return;
-  const int32_t h = (int32_t)(gid % Hq);
-  const int64_t bt = gid / Hq;
+  constexpr int LPH = D / 8;        // lanes per head
+  constexpr int HPS = 64 / LPH;     // heads per step
+  const int64_t bt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bt >= (int64_t)B * Lp) return;
+  const int lane = threadIdx.x & 63;
   const int32_t t = (int32_t)(bt % Lp);
   const int32_t b = (int32_t)(bt / Lp);
-  float acc = 0.0f, l2 = INFINITY;
-  if (t < L) {
-    const int64_t base = (((int64_t)b * L + t) * Hq + h) * D;
-#pragma unroll
-    for (int c = 0; c < D; c += 8) {
+  const int hl = lane / LPH, part = lane % LPH;
+  for (int h0 = 0; h0 < Hq; h0 += HPS) {
+    const int h = h0 + hl;
+    float acc = 0.0f;
+    if (t < L && h < Hq) {
+      const int64_t base = (((int64_t)b * L + t) * Hq + h) * D + part * 8;
       uint16_t ov[8], dv[8];
-      *reinterpret_cast<uint4 *>(ov) = *reinterpret_cast<const uint4 *>(o + base + c);
-      *reinterpret_cast<uint4 *>(dv) = *reinterpret_cast<const uint4 *>(dout + base + c);
+      *reinterpret_cast<uint4 *>(ov) = *reinterpret_cast<const uint4 *>(o + base);
+      *reinterpret_cast<uint4 *>(dv) = *reinterpret_cast<const uint4 *>(dout + base);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += bf16_to_f32(ov[e]) * bf16_to_f32(dv[e]);
     }
-    const float l = lse[((int64_t)b * Hq + h) * L + t];
-    l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+#pragma unroll
+    for (int off = LPH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (part == 0 && h < Hq) {
+      float l2 = INFINITY;
+      if (t < L) {
+        const float l = lse[((int64_t)b * Hq + h) * L + t];
+        l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+      }
+      const int64_t out = ((int64_t)b * Hq + h) * Lp + t;
+      delta[out] = acc;
+      lse2[out] = l2;
+    }
   }
-  const int64_t out = ((int64_t)b * Hq + h) * Lp + t;
-  delta[out] = acc;
-  lse2[out] = l2;
 }
 
 template <int D>
@@ -205,8 +216,8 @@ void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t
 
 void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
                   const AttnWs &ws, hipStream_t s) {
-  const int64_t total = (int64_t)in.B * ws.Lp * in.Hq;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const int64_t total = (int64_t)in.B * ws.Lp;   // one wave per token
+  const unsigned blocks = (unsigned)((total + 3) / 4);
   const uint16_t *o16 = static_cast<const uint16_t *>(o);
   const uint16_t *d16 = static_cast<const uint16_t *>(dout);
   if (in.D == 64)

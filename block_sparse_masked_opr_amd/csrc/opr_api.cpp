@@ -41,10 +41,7 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   w.meta = cv.take<int2>((size_t)in.B * Lp);
   w.vr = cv.take<uint16_t>(kn);
   if (is_bwd) {
-    w.qt = cv.take<uint16_t>(qn);
-    w.kt = cv.take<uint16_t>(kn);
     w.dor = cv.take<uint16_t>(qn);
-    w.dot = cv.take<uint16_t>(qn);
     w.edo = cv.take<int32_t>(qb);
     w.delta = cv.take<float>((size_t)in.B * in.Hq * Lp);
     w.lse2 = cv.take<float>((size_t)in.B * in.Hq * Lp);
@@ -78,10 +75,7 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->qr = ws.qr;
   p->kr = ws.kr;
   p->vr = ws.vr;
-  p->qt = ws.qt;
-  p->kt = ws.kt;
   p->dor = ws.dor;
-  p->dot = ws.dot;
   p->eq = ws.eq;
   p->ek = ws.ek;
   p->ev = ws.ev;
@@ -95,6 +89,7 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
 static opr_status check_attn_shape(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D) {
   if (B < 1 || L < 1 || Hq < 1 || Hkv < 1 || D < 1) return OPR_E_INVALID;
   if (Hq % Hkv != 0) return OPR_E_INVALID;
+  if (Hq / Hkv > 255) return OPR_E_UNSUPPORTED;  // head-in-group index of a dK/dV stage is 8 bits
   if (D != 64 && D != 128) return OPR_E_UNSUPPORTED;
   if (B > 65535 || Hq > 65535) return OPR_E_UNSUPPORTED;  // grid dimensions
   const int64_t Lp = ((int64_t)L + OPR_ATTN_BLOCK - 1) / OPR_ATTN_BLOCK * OPR_ATTN_BLOCK;
@@ -238,10 +233,10 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   carve_attn_ws(workspace, *in, 1, &ws);
   mark(in, 0, stream);
   launch_rope_table(*in, ws, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, ws.qt, ws.eq, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, ws.kt, ws.ek, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, nullptr, ws.eq, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, nullptr, ws.ek, stream);
   launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, ws.vr, nullptr, ws.ev, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, dout, nullptr, ws.dor, ws.dot, ws.edo, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, dout, nullptr, ws.dor, nullptr, ws.edo, stream);
   launch_delta(*in, o, dout, lse, ws, stream);
   launch_meta(*in, ws, stream);
   if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream,

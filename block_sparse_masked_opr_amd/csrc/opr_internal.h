@@ -57,10 +57,7 @@ struct AttnWs {
   uint16_t *qr;         // [B][Hq][Lp][D]  q after RoPE, head-major, zero past L
   uint16_t *kr;         // [B][Hkv][Lp][D] k after RoPE
   uint16_t *vr;         // [B][Hkv][Lp][D] v head-major
-  uint16_t *qt;         // [B][Hq][D][Lp]  q after RoPE, transposed    (bwd)
-  uint16_t *kt;         // [B][Hkv][D][Lp] k after RoPE, transposed    (bwd)
   uint16_t *dor;        // [B][Hq][Lp][D]  dout head-major             (bwd)
-  uint16_t *dot;        // [B][Hq][D][Lp]  dout transposed             (bwd)
   int32_t *eq, *ek, *ev, *edo;  // block exponents [B][H][Lp/64]   (edo: bwd)
   int2 *meta;           // [B][Lp] (conv, turn * 8 + type), conv -1 for PAD / past L
   float *delta;         // [B][Hq][Lp] rowsum(dout * o)                (bwd)
