@@ -4,14 +4,13 @@
 // operands, fp32 accumulation; the same rate as bf16 on gfx950).  fp16 keeps
 // 11 significant bits where bf16 keeps 8, which is what lets the summed
 // gradients of a GQA group stay within 2e-2 of the exact result.  To keep
-// bf16's range, each 64-token block of every staged operand (q and k after
-// RoPE, v, dout) is stored as fp16(x * 2^e) with its own power-of-two exponent
-// e chosen so that the block's largest magnitude lands in [2^14, 2^15).  The
-// kernels fold the exponents back exactly: into the score scale (q, k), and
-// into the running units of the fp32 accumulators (v, dout), which are
-// rescaled by powers of two when a block with another exponent arrives.
-// Probabilities are stored as fp16(p * 2^15) so that small ones keep full
-// precision (p <= 1).
+// bf16's range, each staged operand (q and k after RoPE, v, dout) is stored
+// as fp16(x * 2^e) with one power-of-two exponent e per row and kv head (for
+// q and dout: per row and kv group, over the group's q heads), chosen from the
+// largest magnitude (an absmax pre-pass) so that it lands in [2^14, 2^15).
+// The kernels fold the exponents back exactly: into the score scale (q, k)
+// and into the fixed units of their fp32 accumulators (v, dout), removed in
+// the epilogues.
 //
 // MFMA v_mfma_f32_32x32x16_f16 computes C[32x32] += A[32x16] * B[16x32].
 // Lane l (g = l / 32, i = l % 32) supplies 8 fp16 of A row i and 8 fp16 of
@@ -35,19 +34,24 @@
 namespace opr {
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const f16x8 &a, const f16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Exponent range of the per-block scales; keeps every folded product of up to
+// Exponent range of the plane scales; keeps every folded product of up to
 // three exponents inside fp32's normal range.
 constexpr int kExpMin = -32, kExpMax = 32;
-// Probabilities are stored scaled by 2^kPExp; dS by 2^-kDsShift on top of the
-// units of v and dout (|v|, |dout| < 2^15 after scaling, so |dP| < 2^37).
-constexpr int kPExp = 15;
+// dS is stored shifted down by 2^kDsShift on top of the units of dP
+// (|v|, |dout| < 2^15 after scaling, so |dP| < 2^37 and |dS| < 2^15).
 constexpr int kDsShift = 22;
+// Softmax: the running maximum is only raised when a new score exceeds it by
+// more than kMaxSlack (log2 units); probabilities are stored as
+// fp16(p * 2^kPExp) with p <= 2^kMaxSlack, i.e. at most 2^15.
+constexpr float kMaxSlack = 8.0f;
+constexpr int kPExp = 7;
 
 // A-operand row order of a 32-row block: swap bits 2 and 3.
 __device__ __forceinline__ int kperm(int i) {
@@ -77,25 +81,16 @@ __device__ __forceinline__ f16x8 zero_f16x8() {
   return z;
 }
 
-__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
-  _Float16 h = (_Float16)f;
-  return *reinterpret_cast<uint16_t *>(&h);
-}
-
-// Exponent e with max_abs * 2^e in [2^14, 2^15) (0 for an all-zero block),
-// clamped to [kExpMin, kExpMax].
-__device__ __forceinline__ int block_exponent(float max_abs) {
-  if (!(max_abs > 0.0f)) return 0;
-  int x;
-  frexpf(max_abs, &x);
-  return min(kExpMax, max(kExpMin, 15 - x));
-}
-
 __device__ __forceinline__ f32x16 zero_f32x16() {
   f32x16 z;
 #pragma unroll
   for (int e = 0; e < 16; ++e) z[e] = 0.0f;
   return z;
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;
+  return *reinterpret_cast<uint16_t *>(&h);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -107,39 +102,53 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return *reinterpret_cast<uint16_t *>(&h);
 }
 
-// Token metadata for the mask predicate: conv (-1 for PAD or past L) and
-// turn * 8 + type.
-struct TokMeta {
-  int32_t conv;
-  int32_t tt;
-};
-
-// Whether query qi may attend to key ki.  With segments stored h, t, r_in,
-// r_out inside a turn, every allowed key precedes its query; across turns
-// only h and r_in (the history H_<i) are visible; inside the turn the only
-// excluded earlier keys are t_i for an r_in_i query and r_in_i for an
-// r_out_i query.  (Derived from the four rules; the tile classes computed
-// from the same rules tell the kernels where this test is needed.)
-__device__ __forceinline__ bool mask_allows(int qi, TokMeta q, int ki, TokMeta k) {
-  if (ki > qi || k.conv != q.conv || q.conv < 0) return false;
-  const int tq = q.tt >> 3, tk = k.tt >> 3;
-  const int yq = q.tt & 7, yk = k.tt & 7;
-  if (tk < tq) return (yk & 1) == 0;               // h (0) or r_in (2)
-  return !(yq >= 2 && yk == yq - 1);               // r_in vs t, r_out vs r_in
+// Exponent e with max_abs * 2^e in [2^14, 2^15) (0 for an all-zero plane),
+// clamped to [kExpMin, kExpMax].  max_abs is stored as the bits of a
+// non-negative float (so that atomicMax on the bits orders them).
+__device__ __forceinline__ int plane_exponent(uint32_t max_abs_bits) {
+  const float m = __uint_as_float(max_abs_bits);
+  if (!(m > 0.0f)) return 0;
+  int x;
+  frexpf(m, &x);
+  return min(kExpMax, max(kExpMin, 15 - x));
 }
 
-__device__ __forceinline__ TokMeta load_meta(const int32_t *conv, const int32_t *turn,
-                                             const uint8_t *type, int64_t row_base, int idx,
-                                             int L) {
-  TokMeta m;
-  if (idx < L) {
-    m.conv = conv[row_base + idx];
-    m.tt = (turn[row_base + idx] << 3) | type[row_base + idx];
-  } else {
-    m.conv = -1;
-    m.tt = 4;
+// Exponent of the largest of n plane maxima (q and dout use one exponent per
+// (row, kv group): the maxima of the group's q heads).
+__device__ __forceinline__ int group_exponent(const uint32_t *pm, int n) {
+  uint32_t m = 0;
+  for (int i = 0; i < n; ++i) m = max(m, pm[i]);
+  return plane_exponent(m);
+}
+
+// Sum of the 8 fp16 values of v (fp32 accumulation).
+__device__ __forceinline__ float sum_f16x8(const f16x8 &v, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const f16x2 pr = {v[e], v[e + 1]};
+    acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
   }
-  return m;
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Mask bits.  For a query (or key) the allowed partners form a few intervals
+// of the packed row; range_bits gives the bits of [a, b) inside the 64-row
+// window starting at base.
+__device__ __forceinline__ uint64_t low_bits(int n) {  // bits [0, n), n in [0, 64]
+  return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+}
+
+__device__ __forceinline__ uint64_t range_bits(int a, int b, int base) {
+  return low_bits(max(0, min(64, b - base))) & ~low_bits(max(0, min(64, a - base)));
+}
+
+// -inf where bit `pos` of the 64-bit mask m is clear, x otherwise.
+__device__ __forceinline__ float mask_select(uint64_t m, int pos, float x) {
+  const uint32_t w = pos < 32 ? (uint32_t)m : (uint32_t)(m >> 32);
+  const int32_t full = __builtin_amdgcn_sbfe((int32_t)w, pos & 31, 1);  // 0 or -1
+  return __uint_as_float((__float_as_uint(x) & (uint32_t)full) | (0xff800000u & ~(uint32_t)full));
 }
 
 // ---------------------------------------------------------------------------
@@ -147,9 +156,10 @@ __device__ __forceinline__ TokMeta load_meta(const int32_t *conv, const int32_t 
 // row r is stored in slot c ^ swz(r), so that 16 lanes reading the same chunk
 // of 16 different rows (MFMA A operand) or 4 rows x 32 bytes (transposing
 // reads) hit distinct banks without padding, and a 1 KB run of LDS is filled
-// by one global_load_lds instruction (lane L writes bytes 16L..16L+15).
+// by one asynchronous copy instruction (lane L writes bytes 16L..16L+15).
 #define OPR_LDS __attribute__((address_space(3)))
 typedef short __attribute__((ext_vector_type(4))) s16x4;
+typedef short __attribute__((ext_vector_type(8))) s16x8;
 
 template <int D>
 struct Tile {
@@ -160,29 +170,40 @@ struct Tile {
   __device__ static __forceinline__ int off(int r, int c) { return r * RB + ((c ^ swz(r)) << 4); }
 };
 
-// Asynchronous copy of 64 consecutive rows (row stride D elements) into a
-// swizzled LDS tile; the four waves of a workgroup share the D/8 instructions.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Asynchronous copies of 64-row tiles from a plane [rows][D] fp16 (buffer
+// resource over the plane) into swizzled LDS tiles.  Each of the 4 waves
+// issues NI of the D/8 one-kilobyte instructions; the per-lane byte offsets
+// inside the 64-row block are fixed, the first row goes in the scalar offset.
 template <int D>
-__device__ __forceinline__ void tile_load_async(const uint16_t *src, char *lds, int w, int lane) {
-  constexpr int NC = Tile<D>::NC, RPI = 1024 / Tile<D>::RB;
+struct TileCopy {
+  static constexpr int NI = Tile<D>::NC / 4;
+  int voff[NI];
+  __device__ __forceinline__ void init(int w, int lane) {
+    constexpr int NC = Tile<D>::NC, RPI = 1024 / Tile<D>::RB;
 #pragma unroll
-  for (int t = w; t < NC; t += 4) {
-    const int r = t * RPI + lane / NC;
-    const int c = (lane % NC) ^ Tile<D>::swz(r);
-    __builtin_amdgcn_global_load_lds(src + r * D + c * 8, (OPR_LDS void *)(lds + t * 1024), 16, 0, 0);
+    for (int i = 0; i < NI; ++i) {
+      const int t = w + 4 * i;
+      const int r = t * RPI + lane / NC;
+      const int c = (lane % NC) ^ Tile<D>::swz(r);
+      voff[i] = (r * D + c * 8) * 2;
+    }
   }
-}
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int row0, char *lds, int w) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (OPR_LDS void *)(lds + (w + 4 * i) * 1024), 16, voff[i],
+                                               row0 * D * 2, 0, 0);
+  }
+};
 
-// Asynchronous copy of 64 consecutive 8-byte records (256 B per instruction).
-__device__ __forceinline__ void rec8_load_async(const void *src, char *lds, int lane) {
+// Asynchronous copy of n_words (<= 64) consecutive 4-byte words.
+__device__ __forceinline__ void words_load_async(const void *src, char *lds, int lane, int n_words) {
   const char *g = static_cast<const char *>(src);
-  __builtin_amdgcn_global_load_lds(g + 4 * lane, (OPR_LDS void *)lds, 4, 0, 0);
-  __builtin_amdgcn_global_load_lds(g + 256 + 4 * lane, (OPR_LDS void *)(lds + 256), 4, 0, 0);
-}
-
-// Asynchronous copy of 64 consecutive floats.
-__device__ __forceinline__ void f32x64_load_async(const float *src, char *lds, int lane) {
-  __builtin_amdgcn_global_load_lds(src + lane, (OPR_LDS void *)lds, 4, 0, 0);
+  if (lane < n_words) __builtin_amdgcn_global_load_lds(g + 4 * lane, (OPR_LDS void *)lds, 4, 0, 0);
 }
 
 // Wait for this thread's outstanding memory operations (including the
@@ -192,30 +213,47 @@ __device__ __forceinline__ void wait_all_and_barrier() {
   __syncthreads();
 }
 
-template <int D>
-__device__ __forceinline__ f16x8 tile_row8(const char *lds, int r, int c) {
-  return *reinterpret_cast<const f16x8 *>(lds + Tile<D>::off(r, c));
+__device__ __forceinline__ f16x8 lds_f16x8(const char *p) {
+  return *reinterpret_cast<const f16x8 *>(p);
 }
 
 __device__ __forceinline__ s16x4 ds_read_tr16(const char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((OPR_LDS s16x4 *)p);
 }
 
-// Transposed MFMA operand from a row-major tile X[row][col]: lane l receives
-// X[r0 + 0..7][col0 + l % 32] with r0 = rbase + 8 * (l / 32) and
-// col0 = cbase; i.e. 8 consecutive rows of its own column.  Built from two
-// ds_read_b64_tr_b16: inside each 16-lane group, the lane that points at
-// row r0 + j / 4, columns c + 4 * (j % 4) .. +3 supplies column entries so
-// that lane i receives rows r0 .. r0 + 3 of column c + i.
+// Per-lane LDS byte offsets of the two operand patterns, fixed for a kernel:
+//  row8[st]: 8 elements (k-step st, lane group g) of row kperm(li) - the A
+//            operand of a product whose k runs along the head dim; the rows
+//            32b + kperm(li) of block b add 32 * RB.
+//  col8[db][s]: the transposing reads for an A operand whose k runs along the
+//            rows: inside each 16-lane group, the lane that points at row
+//            rb + 8g + j/4 (+4 for s = 1), columns 32db + 16(G%2) + 4(j%4)..+3
+//            supplies entries so that lane i receives rows rb + 8g + 0..3
+//            (4..7) of column 32db + li; rb (a multiple of 16) adds rb * RB.
 template <int D>
-__device__ __forceinline__ f16x8 tile_col8(const char *lds, int rbase, int cbase, int lane) {
-  const int G = lane >> 4, j = lane & 15;
-  const int col = cbase + 16 * (G & 1) + 4 * (j & 3);
-  const int r = rbase + 8 * (G >> 1) + (j >> 2);
-  const int cb = (col & 7) * 2;
-  const s16x4 lo = ds_read_tr16(lds + Tile<D>::off(r, col >> 3) + cb);
-  const s16x4 hi = ds_read_tr16(lds + Tile<D>::off(r + 4, col >> 3) + cb);
-  typedef short __attribute__((ext_vector_type(8))) s16x8;
+struct OperandOffsets {
+  static constexpr int NS = D / 16, NDB = D / 32;
+  int row8[NS];
+  int col8[NDB][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 5, li = lane & 31, G = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) row8[st] = Tile<D>::off(kperm(li), 2 * st + g);
+    const int col = 16 * (G & 1) + 4 * (j & 3);
+    const int r = 8 * (G >> 1) + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        col8[db][s] = Tile<D>::off(r + 4 * s, (32 * db + col) >> 3) + ((col & 7) << 1);
+  }
+};
+
+// The transposed operand X[rb + 8g + e][32db + li], e = 0..7, of a tile.
+template <int D>
+__device__ __forceinline__ f16x8 tile_col8(const char *lds, const OperandOffsets<D> &of, int rb, int db) {
+  const s16x4 lo = ds_read_tr16(lds + rb * Tile<D>::RB + of.col8[db][0]);
+  const s16x4 hi = ds_read_tr16(lds + rb * Tile<D>::RB + of.col8[db][1]);
   const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(f16x8, v);
 }
@@ -236,18 +274,19 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct AttnParams {
   int32_t B, L, Lp, Hq, Hkv, group, MT, NT;
   float scale, scale_log2;
-  const int32_t *tok_conv, *tok_turn, *tok_pos;
-  const uint8_t *tok_type;
   const uint8_t *tile_class;
   const uint32_t *sub_class;
   const int32_t *q_nnz, *q_list, *k_nnz, *k_list;
-  const float2 *rope;                    // [B][Lp][D/2]
-  // fp16 bits, scaled per 64-token block (see the number format above)
+  const float2 *rope;          // [B][Lp][D/2] (cos, sin)
+  // fp16 bits, one power-of-two scale per (row, head) plane: [B][H][Lp][D]
   const uint16_t *qr, *kr, *vr, *dor;
-  // block exponents [B][H][Lp/64] of q, k, v, dout
-  const int32_t *eq, *ek, *ev, *edo;
-  const int2 *meta;                      // [B][Lp] (conv, turn * 8 + type); conv -1 for PAD / past L
-  const float *delta, *lse2;
+  // plane maxima (float bits) [B][H] of q', k', v, dout
+  const uint32_t *mq, *mk, *mv, *mdo;
+  const int4 *qiv;             // [B][Lp] per query: allowed keys [cs,ts) & {h,r_in}, [ts,e1), [s2,q]
+  const int4 *kiv;             // [B][Lp] per key: allowed queries [k,x), [y,z), [z,w)
+  const uint64_t *hvb;         // [B][Lp/64] bit i of block j: token 64j+i is h or r_in
+  const float *dsc, *lse2;     // [B][Hq][Lp]: rowsum(dout*o) in the units of dP shifted by
+                               // 2^-kDsShift; log2-domain lse (+inf where no key)
 };
 
 }  // namespace opr

@@ -10,16 +10,15 @@
 // first compacted into a stage list in LDS (a ballot over the tile list and
 // its 32x32 sub-block classes), so the main loop has no dependent global
 // loads.  Stages are double buffered: while stage i is computed, K and V of
-// stage i+1 stream from memory straight into LDS (global_load_lds); one
-// barrier per stage.  Per stage each wave computes S^T = K Q^T on its
-// non-empty 32x32 sub-blocks with fp16 MFMA (fp32 accumulate), applies the
-// mask predicate only on partial sub-blocks, updates the online softmax
-// (base-2 exponent, log2(e) folded into the scale) and accumulates
-// O^T += V^T P^T, reading V^T from the row-major V tile with transposing LDS
-// reads.  The epilogue normalises, writes O (bf16) and the natural-log LSE.
-// Operands are fp16 with per-64-token exponents: the q and k exponents are
-// folded into the score scale, the v exponent into the units of the O
-// accumulator (rescaled together with the softmax correction).
+// stage i+1 stream from memory straight into LDS (buffer loads to LDS with
+// fixed per-lane offsets); one barrier per stage.  Per stage each wave
+// computes S^T = K Q^T on its non-empty 32x32 sub-blocks with fp16 MFMA
+// (fp32 accumulate); partial sub-blocks are masked with a 64-bit mask built
+// from the query's key intervals; the online softmax keeps a running maximum
+// that is only raised when a score exceeds it by more than kMaxSlack (so the
+// O accumulator is rarely rescaled); O^T += V^T P^T reads V^T from the
+// row-major V tile with transposing LDS reads.  The epilogue normalises,
+// writes O (bf16) and the natural-log LSE.
 #include "attn_common.h"
 #include "attn_sched.h"
 #include "opr_internal.h"
@@ -31,9 +30,8 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t *o, float *lse) {
   constexpr int NS = D / 16;   // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;  // 32-wide blocks of the head dim
-  constexpr int TB = Tile<D>::BYTES;
-  // per buffer: K tile, V tile, 64 key records
-  constexpr int BUF = 2 * TB + 512;
+  constexpr int TB = Tile<D>::BYTES, RB = Tile<D>::RB;
+  constexpr int BUF = 2 * TB + 64;  // K tile, V tile, 64 history bits of the keys
   __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
   __shared__ uint2 stages[kStageCap];
   __shared__ int sh_count, sh_next;
@@ -51,7 +49,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int q = m * 128 + 32 * w + li;
-  const int nblk = p.Lp / 64;
+  const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
+  const int eq = group_exponent(p.mq + (int64_t)b * p.Hq + kvh * p.group, p.group);
+  const int ek = plane_exponent(p.mk[kvplane]);
+  const int ev = plane_exponent(p.mv[kvplane]);
+  const float fs = ldexpf(p.scale_log2, -(eq + ek));  // raw score -> log2 units
 
   f16x8 qb[NS];
   {
@@ -59,12 +61,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
 #pragma unroll
     for (int s = 0; s < NS; ++s) qb[s] = ld_f16x8(qrow + 16 * s + 8 * g);
   }
-  const int eq = p.eq[((int64_t)b * p.Hq + h) * nblk + (q >> 6)];
-  const int32_t *ekp = p.ek + ((int64_t)b * p.Hkv + kvh) * nblk;
-  const int32_t *evp = p.ev + ((int64_t)b * p.Hkv + kvh) * nblk;
-  const int2 qmi = p.meta[(int64_t)b * p.Lp + q];
-  const TokMeta qm = {qmi.x, qmi.y};
-  int ev_ref = 0;  // the O accumulator holds O * sum(p) * 2^(kPExp + ev_ref)
+  const int4 iv = p.qiv[(int64_t)b * p.Lp + q];  // [cs,ts) & hist, [ts,e1), [s2,q]
+  OperandOffsets<D> of;
+  of.init(lane);
+  TileCopy<D> tc;
+  tc.init(w, lane);
+  const uint32_t plane_bytes = (uint32_t)p.Lp * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.kr + kvplane * p.Lp * D, plane_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.vr + kvplane * p.Lp * D, plane_bytes);
+  const uint64_t *hvrow = p.hvb + (int64_t)b * (p.Lp / 64);
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -75,17 +80,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
   const int nnz = p.q_nnz[trow];
   const int32_t *lst = p.q_list + trow * p.NT;
   const uint32_t *subs = p.sub_class + trow * p.NT;
-  const int64_t kvoff = ((int64_t)b * p.Hkv + kvh) * p.Lp;
-  const uint16_t *kbase = p.kr + kvoff * D;
-  const uint16_t *vbase = p.vr + kvoff * D;
-  const int2 *mbase = p.meta + (int64_t)b * p.Lp;
+
+  auto issue = [&](int k0, char *nb) {
+    tc.issue(rk, k0, nb, w);
+    tc.issue(rv, k0, nb + TB, w);
+    if (w == 0) words_load_async(hvrow + (k0 >> 6), nb + 2 * TB, lane, 2);
+  };
 
   int tnext = 0;
   while (tnext < nnz) {
-    __syncthreads();  // previous chunk's stages and buffers are no longer read
+    __syncthreads();  // the previous chunk's stages and buffers are no longer read
     if (w == 0) {
       int t = tnext;
-      const int c = build_q_stages(lst, subs, ekp, evp, nnz, &t, stages, lane);
+      const int c = build_q_stages(lst, subs, nnz, &t, stages, lane);
       if (lane == 0) {
         sh_count = c;
         sh_next = t;
@@ -95,78 +102,64 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
     const int ns = sh_count;
     tnext = sh_next;
     if (ns == 0) continue;
-    {
-      const int k0 = (int)stages[0].x;
-      tile_load_async<D>(kbase + (int64_t)k0 * D, smem, w, lane);
-      tile_load_async<D>(vbase + (int64_t)k0 * D, smem + TB, w, lane);
-      if (w == 0) rec8_load_async(mbase + k0, smem + 2 * TB, lane);
-    }
+    issue((int)stages[0].x, smem);
     for (int i = 0; i < ns; ++i) {
       wait_all_and_barrier();
       const char *buf = smem + (i & 1) * BUF;
-      if (i + 1 < ns) {
-        char *nb = smem + ((i + 1) & 1) * BUF;
-        const int k1 = (int)stages[i + 1].x;
-        tile_load_async<D>(kbase + (int64_t)k1 * D, nb, w, lane);
-        tile_load_async<D>(vbase + (int64_t)k1 * D, nb + TB, w, lane);
-        if (w == 0) rec8_load_async(mbase + k1, nb + 2 * TB, lane);
-      }
+      if (i + 1 < ns) issue((int)stages[i + 1].x, smem + ((i + 1) & 1) * BUF);
       const uint2 desc = stages[i];
       const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
       if ((c0 | c1) == 0) continue;
       const uint32_t cls[2] = {c0, c1};
       const int k0 = (int)desc.x;
-      const int ek = (int)((desc.y >> 16) & 255u) - 128, ev = (int)(desc.y >> 24) - 128;
-      const float fs = ldexpf(p.scale_log2, -(eq + ek));
       const char *Kt = buf, *Vt = buf + TB;
-      const int2 *kmeta = reinterpret_cast<const int2 *>(buf + 2 * TB);
 
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = zero_f32x16();
         if (cls[kb] == 0) continue;
-        const int r = 32 * kb + kperm(li);
 #pragma unroll
-        for (int st = 0; st < NS; ++st) s[kb] = mfma32x32x16(tile_row8<D>(Kt, r, 2 * st + g), qb[st], s[kb]);
+        for (int st = 0; st < NS; ++st)
+          s[kb] = mfma32x32x16(lds_f16x8(Kt + kb * 32 * RB + of.row8[st]), qb[st], s[kb]);
+      }
+      if (c0 == 1 || c1 == 1) {
+        const uint64_t hv = *reinterpret_cast<const uint64_t *>(buf + 2 * TB);
+        uint64_t mk = (range_bits(iv.x, iv.y, k0) & hv) | range_bits(iv.y, iv.z, k0) | range_bits(iv.w, q + 1, k0);
+        mk >>= 8 * g;  // lane group g holds keys 16h + 8g + 0..7 of each 32-key block
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (cls[kb] != 1) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] = mask_select(mk, 32 * kb + 16 * (r >> 3) + (r & 7), s[kb][r]);
+        }
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        if (cls[kb] == 0) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][r] * fs;
-          if (cls[kb] == 0) {
-            x = -INFINITY;
-          } else if (cls[kb] == 1) {
-            const int kl = 32 * kb + acc_row(r, g);
-            const int2 km = kmeta[kl];
-            if (!mask_allows(q, qm, k0 + kl, TokMeta{km.x, km.y})) x = -INFINITY;
-          }
-          s[kb][r] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow, mx);
-      const float msafe = (mnew == -INFINITY) ? 0.0f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(mrow - msafe);
-      const float ofac = ldexpf(alpha, ev - ev_ref);  // softmax correction and new v units
-      mrow = mnew;
-      ev_ref = ev;
-      lrow *= alpha;
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * fs;
+      if (__ballot(mx > mrow + kMaxSlack) != 0) {  // raise the running maximum (wave-uniform)
+        const float mnew = fmaxf(mrow, mx);
+        const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mrow - mnew);
+        lrow *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= ofac;
-      const float mshift = msafe - (float)kPExp;
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        mrow = mnew;
+      }
+      // p * 2^kPExp with p = 2^(score - running max) <= 2^kMaxSlack
+      const float cexp = (float)kPExp - (mrow == -INFINITY ? 0.0f : mrow);
       f16x8 pb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        if (cls[kb] == 0) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(s[kb][r] - mshift);  // p * 2^kPExp
-          lrow += pv;
-          pb[kb][r >> 3][r & 7] = (_Float16)pv;
-        }
+        for (int r = 0; r < 16; ++r) pb[kb][r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], fs, cexp));
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) lrow = sum_f16x8(pb[kb][hh], lrow);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -175,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
         for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            oacc[db] = mfma32x32x16(tile_col8<D>(Vt, 32 * kb + 16 * hh, 32 * db, lane), pb[kb][hh], oacc[db]);
+            oacc[db] = mfma32x32x16(tile_col8<D>(Vt, of, 32 * kb + 16 * hh, db), pb[kb][hh], oacc[db]);
         }
       }
     }
@@ -183,7 +176,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
 
   const float lsum = lrow + __shfl_xor(lrow, 32);
   if (q < p.L) {
-    const float inv = lsum > 0.0f ? ldexpf(1.0f / lsum, -ev_ref) : 0.0f;
+    // O = acc / sum, acc in units 2^ev (v) times 2^kPExp (shared with sum)
+    const float inv = lsum > 0.0f ? ldexpf(1.0f / lsum, -ev) : 0.0f;
     uint16_t *orow = o + (((int64_t)b * p.L + q) * p.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

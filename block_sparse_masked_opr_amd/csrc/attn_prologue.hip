@@ -1,24 +1,44 @@
-// Prologue kernels of the attention path: the RoPE table at the strategic
-// position ids, head-major (optionally rotated) fp16 copies of q / k / v / dout
-// with one power-of-two scale per 64-token block, padded to a whole number of
-// 128-token tiles with zeros; the per-token mask records; and the backward
-// preprocessing delta = rowsum(dout * o).
+// Prologue kernels of the attention path:
+//  - the RoPE table at the strategic position ids (and zeroing of the plane
+//    maxima),
+//  - the largest magnitude of every (row, head) plane of q, k, v, dout,
+//  - head-major fp16 copies of q, k (after RoPE), v and dout with one
+//    power-of-two scale per plane, padded with zeros to a whole number of
+//    128-token tiles,
+//  - per-token mask intervals (below) and per-64-token "history" bits,
+//  - the backward preprocessing delta = rowsum(dout * o), scaled.
 //
 // RoPE (rotate-half): pair (j, j + D/2) of a head vector is rotated by
 // pos * theta^(-2j/D).  The angle and its cosine and sine are computed in
 // float64 (positions reach ~2.4e5, where a float32 angle would be off by
 // ~1e-2 rad); the rotation itself runs in float32.
+//
+// Mask intervals.  Segments are stored h, t, r_in, r_out inside a turn and
+// conversations are contiguous, so what a token may see (or be seen by) is a
+// union of intervals of the packed row.  With cs / ce the start / end of the
+// token's conversation, ts / te of its turn and tT, tR, tO the starts of the
+// turn's t, r_in and r_out segments:
+//   query q of type h or t  : keys [cs, ts) that are h or r_in, and [ts, q]
+//   query q of type r_in    : ... and [ts, tT) (h_i) and [tR, q]
+//   query q of type r_out   : ... and [ts, tR) (h_i, t_i) and [tO, q]
+//   key k of type h         : queries [k, te) and [te, ce)
+//   key k of type t         : queries [k, tR) and [tO, te)   (not r_in_i)
+//   key k of type r_in      : queries [k, tO) and [te, ce)   (not r_out_i)
+//   key k of type r_out     : queries [k, te)
+// (Derived from the four visibility rules; PAD tokens get empty intervals.)
 #include "attn_common.h"
 #include "opr_internal.h"
 
 namespace opr {
 namespace {
 
-// table[b][t][j] = (cos, sin) of pos(b, t) * theta^(-2j/D); PAD and t >= L use 0.
-__global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, int32_t Lp,
-                                                         int32_t half, double log2_theta,
-                                                         const int32_t *tok_pos, float2 *table) {
+// table[b][t][j] = (cos, sin) of pos(b, t) * theta^(-2j/D); PAD and t >= L
+// use position 0.  The first n_zero threads also clear zero_words.
+__global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, int32_t Lp, int32_t half,
+                                                         double log2_theta, const int32_t *tok_pos,
+                                                         float2 *table, uint32_t *zero_words, int32_t n_zero) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid < n_zero) zero_words[gid] = 0u;
   const int64_t total = (int64_t)B * Lp * half;
   if (gid >= total) return;
   const int32_t j = (int32_t)(gid % half);
@@ -32,28 +52,53 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, i
   table[gid] = make_float2((float)c, (float)s);
 }
 
-// One workgroup per (64-token block, head, row).  x: [B][L][H][D] bf16.
-// Writes the block as fp16(x' * 2^e), x' = RoPE(x) or x, with the block
-// exponent e (largest |x'| of the block scaled into [2^14, 2^15)) stored in
-// exps[b][h][block]; rows (optional): [B][H][Lp][D]; trans (optional):
-// [B][H][D][Lp].  Tokens t >= L are zero.
-template <int D, bool ROPE>
-__global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H,
-                                                   const uint16_t *x, const float2 *table,
-                                                   uint16_t *rows, uint16_t *trans,
-                                                   int32_t *exps) {
-  constexpr int HALF = D / 2;
-  constexpr int PER = HALF / 4;           // pairs per thread (4 threads per token)
-  constexpr int TS = 64 + 8;              // LDS row stride of the transposed tile
-  __shared__ __attribute__((aligned(16))) uint16_t tile[D * TS];
+// Largest |x| of each (row, head) plane of x [B][L][H][D] bf16, times
+// `factor` (sqrt(2) bound of RoPE on a pair, rounded up), into pmax[b][h] as
+// float bits.  One workgroup per (64 tokens, head, row).
+template <int D>
+__global__ __launch_bounds__(256) void absmax_kernel(int32_t L, int32_t H, const uint16_t *x, float factor,
+                                                     uint32_t *pmax) {
   __shared__ float wmax[4];
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  float m = 0.0f;
+  for (int c = tid; c < 64 * D / 8; c += 256) {
+    const int t = blockIdx.x * 64 + c / (D / 8);
+    if (t < L) {
+      uint16_t v[8];
+      *reinterpret_cast<uint4 *>(v) =
+          *reinterpret_cast<const uint4 *>(x + (((int64_t)b * L + t) * H + h) * D + (c % (D / 8)) * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(bf16_to_f32(v[e])));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])) * factor;
+    if (m > 0.0f) atomicMax(pmax + (int64_t)b * H + h, __float_as_uint(m));
+  }
+}
+
+// One workgroup per (64-token block, head, row).  x: [B][L][H][D] bf16 ->
+// rows [B][H][Lp][D] as fp16(x' * 2^e), x' = RoPE(x) or x, e the exponent of
+// the largest plane maximum of the head's group of `group` heads.  Tokens
+// t >= L are zero.
+template <int D, bool ROPE>
+__global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H, int32_t group,
+                                                   const uint16_t *x, const float2 *table,
+                                                   const uint32_t *pmax, uint16_t *rows) {
+  constexpr int HALF = D / 2;
+  constexpr int PER = HALF / 4;  // pairs per thread (4 threads per token)
   const int t0 = blockIdx.x * 64;
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int tt = tid >> 2, part = tid & 3;
   const int t = t0 + tt;
   const int j0 = part * PER;
-  float lo[PER], hi[PER];
+  const int ex = group_exponent(pmax + (int64_t)b * H + (h / group) * group, group);
+  uint16_t lq[PER], hq[PER];
   if (t < L) {
     const uint16_t *src = x + (((int64_t)b * L + t) * H + h) * D;
     uint16_t lb[PER], hb[PER];
@@ -62,90 +107,103 @@ __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_
       *reinterpret_cast<uint4 *>(&lb[c]) = *reinterpret_cast<const uint4 *>(src + j0 + c);
       *reinterpret_cast<uint4 *>(&hb[c]) = *reinterpret_cast<const uint4 *>(src + HALF + j0 + c);
     }
+    const float2 *cs = table + ((int64_t)b * Lp + t) * HALF + j0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      lo[e] = bf16_to_f32(lb[e]);
-      hi[e] = bf16_to_f32(hb[e]);
-    }
-    if (ROPE) {
-      const float2 *cs = table + ((int64_t)b * Lp + t) * HALF + j0;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
+      float lo = bf16_to_f32(lb[e]), hi = bf16_to_f32(hb[e]);
+      if (ROPE) {
         const float2 r = cs[e];
-        const float x1 = lo[e], x2 = hi[e];
-        lo[e] = x1 * r.x - x2 * r.y;
-        hi[e] = x2 * r.x + x1 * r.y;
+        const float x1 = lo, x2 = hi;
+        lo = x1 * r.x - x2 * r.y;
+        hi = x2 * r.x + x1 * r.y;
       }
+      lq[e] = f32_to_f16_bits(ldexpf(lo, ex));
+      hq[e] = f32_to_f16_bits(ldexpf(hi, ex));
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) lo[e] = hi[e] = 0.0f;
+    for (int e = 0; e < PER; ++e) lq[e] = hq[e] = 0;
   }
-  // block max |x'|: lanes, then the four waves
-  float m = 0.0f;
+  uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) m = fmaxf(m, fmaxf(fabsf(lo[e]), fabsf(hi[e])));
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((tid & 63) == 0) wmax[tid >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const int ex = block_exponent(m);
-  if (tid == 0) exps[((int64_t)b * H + h) * (Lp / 64) + blockIdx.x] = ex;
-  uint16_t lq[PER], hq[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    lq[e] = f32_to_f16_bits(ldexpf(lo[e], ex));
-    hq[e] = f32_to_f16_bits(ldexpf(hi[e], ex));
-  }
-  if (rows) {
-    uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
-#pragma unroll
-    for (int c = 0; c < PER; c += 8) {
-      *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
-      *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
-    }
-  }
-  if (trans) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      tile[(j0 + e) * TS + tt] = lq[e];
-      tile[(HALF + j0 + e) * TS + tt] = hq[e];
-    }
-    __syncthreads();
-    // D rows of 64 tokens (128 bytes = 8 chunks of 16 bytes)
-    for (int c = tid; c < D * 8; c += 256) {
-      const int d = c >> 3, ch = c & 7;
-      uint16_t *dst = trans + (((int64_t)b * H + h) * D + d) * Lp + t0 + ch * 8;
-      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(&tile[d * TS + ch * 8]);
-    }
+  for (int c = 0; c < PER; c += 8) {
+    *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
+    *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
   }
 }
 
-// meta[b][t] = (conv, turn * 8 + type) for t < L, (-1, PAD) past L.
-__global__ __launch_bounds__(256) void meta_kernel(int32_t B, int32_t L, int32_t Lp, const int32_t *conv,
-                                                   const int32_t *turn, const uint8_t *type, int2 *meta) {
+// Sort key of a token along its row: (conv, turn, type) in lexicographic
+// order, which is non-decreasing along the packed conversations; PAD last.
+__device__ __forceinline__ uint64_t tok_key(const int32_t *conv, const int32_t *turn, const uint8_t *type,
+                                            int64_t i) {
+  const int32_t c = conv[i];
+  if (c < 0) return ~0ull;
+  return ((uint64_t)(uint32_t)c << 34) | ((uint64_t)(uint32_t)turn[i] << 3) | (uint64_t)type[i];
+}
+
+// First index in [0, L) of row b whose key is >= k (L if none).
+__device__ __forceinline__ int32_t lower_bound_key(const int32_t *conv, const int32_t *turn,
+                                                   const uint8_t *type, int64_t row, int32_t L, uint64_t k) {
+  int32_t lo = 0, hi = L;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (tok_key(conv, turn, type, row + mid) < k) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// qiv, kiv (may be null) for every token (t < Lp) and the history bits of each
+// 64-token block.
+__global__ __launch_bounds__(256) void intervals_kernel(int32_t B, int32_t L, int32_t Lp, const int32_t *conv,
+                                                        const int32_t *turn, const uint8_t *type, int4 *qiv,
+                                                        int4 *kiv, uint64_t *hvb) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)B * Lp) return;
-  const int32_t t = (int32_t)(gid % Lp);
-  const int64_t b = gid / Lp;
-  int2 m = make_int2(-1, 4);
-  if (t < L) {
-    const int64_t i = b * L + t;
-    m = make_int2(conv[i], (turn[i] << 3) | type[i]);
+  const bool active = gid < (int64_t)B * Lp;
+  const int32_t t = active ? (int32_t)(gid % Lp) : 0;
+  const int64_t b = active ? gid / Lp : 0;
+  const int64_t row = b * L;
+  int4 qi = make_int4(t + 1, t + 1, t + 1, t + 1);
+  int4 ki = make_int4(t, t, t, t);
+  bool hv = false;
+  if (active && t < L && conv[row + t] >= 0) {
+    const uint64_t c = (uint32_t)conv[row + t], i = (uint32_t)turn[row + t];
+    const int y = type[row + t];
+    const uint64_t turn_key = (c << 34) | (i << 3);
+    const int32_t cs = lower_bound_key(conv, turn, type, row, L, c << 34);
+    const int32_t ce = lower_bound_key(conv, turn, type, row, L, (c + 1) << 34);
+    const int32_t ts = lower_bound_key(conv, turn, type, row, L, turn_key);
+    const int32_t te = lower_bound_key(conv, turn, type, row, L, turn_key + 8);
+    const int32_t tT = lower_bound_key(conv, turn, type, row, L, turn_key | OPR_TOK_T);
+    const int32_t tR = lower_bound_key(conv, turn, type, row, L, turn_key | OPR_TOK_RIN);
+    const int32_t tO = lower_bound_key(conv, turn, type, row, L, turn_key | OPR_TOK_ROUT);
+    hv = (y == OPR_TOK_H) || (y == OPR_TOK_RIN);
+    switch (y) {
+      case OPR_TOK_H: qi = make_int4(cs, ts, t + 1, t + 1); ki = make_int4(te, te, te, ce); break;
+      case OPR_TOK_T: qi = make_int4(cs, ts, t + 1, t + 1); ki = make_int4(tR, tO, te, te); break;
+      case OPR_TOK_RIN: qi = make_int4(cs, ts, tT, tR); ki = make_int4(tO, te, te, ce); break;
+      default: qi = make_int4(cs, ts, tR, tO); ki = make_int4(te, te, te, te); break;
+    }
   }
-  meta[gid] = m;
+  if (active) {
+    qiv[gid] = qi;
+    if (kiv) kiv[gid] = ki;  // only the backward pass needs the key intervals
+  }
+  const uint64_t bits = __ballot(hv);
+  if (active && (threadIdx.x & 63) == 0) hvb[gid >> 6] = bits;  // Lp is a multiple of 64
 }
 
-// delta[b][h][t] = sum_d dout * o (float32 over bf16 inputs);
+// dsc[b][h][t] = sum_d dout * o (float32 over bf16 inputs) times
+// 2^(e_dout + e_v - kDsShift): delta in the units of dP = dO V^T computed on
+// the scaled operands, shifted like dS;
 // lse2[b][h][t] = lse * log2(e), +inf where the row has no key (lse = -inf)
 // or t >= L, so that recomputed probabilities are exactly 0 there.
 // One wave per token: D/8 lanes read one head's 16-byte chunks, so a wave
 // covers 64/(D/8) heads per step with fully coalesced row reads.
 template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_t Lp, int32_t Hq,
-                                                    const uint16_t *o, const uint16_t *dout,
-                                                    const float *lse, float *delta, float *lse2) {
+__global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_t Lp, int32_t Hq, int32_t group,
+                                                    const uint16_t *o, const uint16_t *dout, const float *lse,
+                                                    const uint32_t *mdo, const uint32_t *mv, float *dsc,
+                                                    float *lse2) {
   constexpr int LPH = D / 8;        // lanes per head
   constexpr int HPS = 64 / LPH;     // heads per step
   const int64_t bt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -173,57 +231,74 @@ __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_
         const float l = lse[((int64_t)b * Hq + h) * L + t];
         l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
       }
+      const int kv = h / group, Hkv = Hq / group;
+      const int e = group_exponent(mdo + (int64_t)b * Hq + kv * group, group) +
+                    plane_exponent(mv[(int64_t)b * Hkv + kv]) - kDsShift;
       const int64_t out = ((int64_t)b * Hq + h) * Lp + t;
-      delta[out] = acc;
+      dsc[out] = ldexpf(acc, e);
       lse2[out] = l2;
     }
   }
 }
 
 template <int D>
-void launch_pack(bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x,
-                 const float2 *table, uint16_t *rows, uint16_t *trans, int32_t *exps,
-                 hipStream_t s) {
+void launch_absmax_d(int32_t B, int32_t L, int32_t H, const void *x, float factor, uint32_t *pmax,
+                     hipStream_t s) {
+  absmax_kernel<D><<<dim3((L + 63) / 64, H, B), 256, 0, s>>>(L, H, static_cast<const uint16_t *>(x), factor, pmax);
+}
+
+template <int D>
+void launch_pack_d(bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group, const void *x,
+                   const float2 *table, const uint32_t *pmax, uint16_t *rows, hipStream_t s) {
   const dim3 grid(Lp / 64, H, B);
   const uint16_t *src = static_cast<const uint16_t *>(x);
-  if (rope)
-    pack_kernel<D, true><<<grid, 256, 0, s>>>(L, Lp, H, src, table, rows, trans, exps);
-  else
-    pack_kernel<D, false><<<grid, 256, 0, s>>>(L, Lp, H, src, table, rows, trans, exps);
+  if (rope) pack_kernel<D, true><<<grid, 256, 0, s>>>(L, Lp, H, group, src, table, pmax, rows);
+  else pack_kernel<D, false><<<grid, 256, 0, s>>>(L, Lp, H, group, src, table, pmax, rows);
 }
 
 }  // namespace
 
-void launch_meta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
-  const int64_t total = (int64_t)in.B * ws.Lp;
-  meta_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(in.B, in.L, ws.Lp, in.layout.tok_conv,
-                                                              in.layout.tok_turn, in.layout.tok_type, ws.meta);
-}
-
+// RoPE table + clearing of the plane maxima (they must start at zero).
 void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int32_t half = in.D / 2;
   const int64_t total = (int64_t)in.B * ws.Lp * half;
-  rope_table_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
-      in.B, in.L, ws.Lp, half, log2(in.rope_theta), in.layout.tok_pos, ws.rope);
+  const int64_t blocks = ((total > ws.n_pmax ? total : (int64_t)ws.n_pmax) + 255) / 256;
+  rope_table_kernel<<<(unsigned)blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, half, log2(in.rope_theta),
+                                                     in.layout.tok_pos, ws.rope, ws.pmax, ws.n_pmax);
 }
 
-void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x,
-                     const float2 *table, uint16_t *rows, uint16_t *trans, int32_t *exps,
-                     hipStream_t s) {
-  if (D == 64) launch_pack<64>(rope, B, L, Lp, H, x, table, rows, trans, exps, s);
-  else launch_pack<128>(rope, B, L, Lp, H, x, table, rows, trans, exps, s);
+void launch_absmax(int D, int32_t B, int32_t L, int32_t H, const void *x, bool rope, uint32_t *pmax,
+                   hipStream_t s) {
+  const float factor = rope ? 1.4142136f : 1.0f;
+  if (D == 64) launch_absmax_d<64>(B, L, H, x, factor, pmax, s);
+  else launch_absmax_d<128>(B, L, H, x, factor, pmax, s);
+}
+
+void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,
+                     const void *x, const float2 *table, const uint32_t *pmax, uint16_t *rows, hipStream_t s) {
+  if (D == 64) launch_pack_d<64>(rope, B, L, Lp, H, group, x, table, pmax, rows, s);
+  else launch_pack_d<128>(rope, B, L, Lp, H, group, x, table, pmax, rows, s);
+}
+
+void launch_intervals(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+  const int64_t total = (int64_t)in.B * ws.Lp;
+  intervals_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
+      in.B, in.L, ws.Lp, in.layout.tok_conv, in.layout.tok_turn, in.layout.tok_type, ws.qiv, ws.kiv, ws.hvb);
 }
 
 void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
                   const AttnWs &ws, hipStream_t s) {
-  const int64_t total = (int64_t)in.B * ws.Lp;   // one wave per token
+  const int64_t total = (int64_t)in.B * ws.Lp;  // one wave per token
   const unsigned blocks = (unsigned)((total + 3) / 4);
   const uint16_t *o16 = static_cast<const uint16_t *>(o);
   const uint16_t *d16 = static_cast<const uint16_t *>(dout);
+  const int32_t group = in.Hq / in.Hkv;
   if (in.D == 64)
-    delta_kernel<64><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, ws.delta, ws.lse2);
+    delta_kernel<64><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, group, o16, d16, lse, ws.mdo, ws.mv,
+                                            ws.dsc, ws.lse2);
   else
-    delta_kernel<128><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, ws.delta, ws.lse2);
+    delta_kernel<128><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, group, o16, d16, lse, ws.mdo, ws.mv,
+                                             ws.dsc, ws.lse2);
 }
 
 }  // namespace opr

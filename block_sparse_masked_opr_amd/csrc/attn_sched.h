@@ -5,8 +5,6 @@
 // Descriptor (x, y):
 //   y bits 4w + 2b : 2-bit class (empty / partial / full) of the 32 x 32
 //                    sub-block that wave w meets in 32-row block b of the stage
-//   y bits 16..23  : block exponent (+128) of the first streamed operand
-//   y bits 24..31  : block exponent (+128) of the second streamed operand
 //   x              : first streamed row; dK/dV stages add the head (in the
 //                    kv group) at bits 24..31
 #pragma once
@@ -18,10 +16,10 @@ namespace opr {
 constexpr int kStageCap = 1024;  // descriptors per list chunk (8 KB of LDS)
 
 // Query-side kernels (forward, dQ): wave w owns query sub-row w; the stages
-// are the 64-key halves kh of the tiles q_list[t ...], streamed operands K
-// (exponents ekp) and V (evp).  Returns the count; advances *t.
-__device__ inline int build_q_stages(const int32_t *lst, const uint32_t *subs, const int32_t *ekp,
-                                     const int32_t *evp, int nnz, int *t, uint2 *stages, int lane) {
+// are the 64-key halves kh of the tiles q_list[t ...].  Returns the count;
+// advances *t.
+__device__ inline int build_q_stages(const int32_t *lst, const uint32_t *subs, int nnz, int *t,
+                                     uint2 *stages, int lane) {
   int count = 0;
   while (*t < nnz && count + 64 <= kStageCap) {
     const int tile = *t + (lane >> 1), kh = lane & 1;
@@ -37,10 +35,7 @@ __device__ inline int build_q_stages(const int32_t *lst, const uint32_t *subs, c
         for (int kb = 0; kb < 2; ++kb) cls |= ((sub >> (2 * (4 * w + 2 * kh + kb))) & 3u) << (4 * w + 2 * kb);
     }
     const uint64_t bal = __ballot(cls != 0);
-    if (cls != 0) {
-      const uint32_t ex = ((uint32_t)(ekp[k0 >> 6] + 128) << 16) | ((uint32_t)(evp[k0 >> 6] + 128) << 24);
-      stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint2((uint32_t)k0, cls | ex);
-    }
+    if (cls != 0) stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint2((uint32_t)k0, cls);
     count += __popcll(bal);
     *t += 32;
   }
@@ -50,16 +45,14 @@ __device__ inline int build_q_stages(const int32_t *lst, const uint32_t *subs, c
 
 // Key-side kernel (dK/dV) of k-tile n: wave w owns key sub-column w; the
 // stages run over the q-tiles k_list[...] x the G heads of the kv group x the
-// two 64-query halves, flat index f = (tile * G + head) * 2 + half; streamed
-// operands Q (exponents eqp, per head at + head * nblk) and dO (edop).
+// two 64-query halves, flat index f = (tile * G + head) * 2 + half.
 __device__ inline int build_k_stages(const int32_t *lst, const uint32_t *subs_b, int NT, int n, int G,
-                                     const int32_t *eqp, const int32_t *edop, int nblk, int nnz,
-                                     int64_t *f, uint2 *stages, int lane) {
+                                     int nnz, int64_t *f, uint2 *stages, int lane) {
   int count = 0;
   const int64_t total = (int64_t)nnz * G * 2;
   while (*f < total && count + 64 <= kStageCap) {
     const int64_t ff = *f + lane;
-    uint32_t cls = 0, x = 0, ex = 0;
+    uint32_t cls = 0, x = 0;
     if (ff < total) {
       const int qh = (int)(ff & 1);
       const int64_t tj = ff >> 1;
@@ -70,14 +63,10 @@ __device__ inline int build_k_stages(const int32_t *lst, const uint32_t *subs_b,
       for (int w = 0; w < 4; ++w)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) cls |= ((sub >> (2 * (4 * (2 * qh + qb) + w))) & 3u) << (4 * w + 2 * qb);
-      const int q0 = m * 128 + 64 * qh;
-      x = (uint32_t)q0 | ((uint32_t)hj << 24);
-      if (cls != 0)
-        ex = ((uint32_t)(eqp[hj * nblk + (q0 >> 6)] + 128) << 16) |
-             ((uint32_t)(edop[hj * nblk + (q0 >> 6)] + 128) << 24);
+      x = (uint32_t)(m * 128 + 64 * qh) | ((uint32_t)hj << 24);
     }
     const uint64_t bal = __ballot(cls != 0);
-    if (cls != 0) stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint2(x, cls | ex);
+    if (cls != 0) stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint2(x, cls);
     count += __popcll(bal);
     *f += 64;
   }

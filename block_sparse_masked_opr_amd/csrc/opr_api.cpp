@@ -10,10 +10,11 @@ namespace opr {
 
 // launchers defined in the .hip files
 void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
-void launch_meta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
-void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x,
-                     const float2 *table, uint16_t *rows, uint16_t *trans, int32_t *exps,
-                     hipStream_t s);
+void launch_absmax(int D, int32_t B, int32_t L, int32_t H, const void *x, bool rope, uint32_t *pmax,
+                   hipStream_t s);
+void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,
+                     const void *x, const float2 *table, const uint32_t *pmax, uint16_t *rows, hipStream_t s);
+void launch_intervals(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
                   const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, float *lse,
@@ -34,16 +35,21 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   w.rope = cv.take<float2>((size_t)in.B * Lp * (in.D / 2));
   w.qr = cv.take<uint16_t>(qn);
   w.kr = cv.take<uint16_t>(kn);
-  const size_t qb = (size_t)in.B * in.Hq * (Lp / 64), kb = (size_t)in.B * in.Hkv * (Lp / 64);
-  w.eq = cv.take<int32_t>(qb);
-  w.ek = cv.take<int32_t>(kb);
-  w.ev = cv.take<int32_t>(kb);
-  w.meta = cv.take<int2>((size_t)in.B * Lp);
   w.vr = cv.take<uint16_t>(kn);
+  w.n_pmax = 2 * in.B * (in.Hq + in.Hkv);
+  w.pmax = cv.take<uint32_t>((size_t)w.n_pmax);
+  if (w.pmax) {
+    w.mq = w.pmax;
+    w.mk = w.mq + (size_t)in.B * in.Hq;
+    w.mv = w.mk + (size_t)in.B * in.Hkv;
+    w.mdo = w.mv + (size_t)in.B * in.Hkv;
+  }
+  w.qiv = cv.take<int4>((size_t)in.B * Lp);
+  w.hvb = cv.take<uint64_t>((size_t)in.B * (Lp / 64));
   if (is_bwd) {
     w.dor = cv.take<uint16_t>(qn);
-    w.edo = cv.take<int32_t>(qb);
-    w.delta = cv.take<float>((size_t)in.B * in.Hq * Lp);
+    w.kiv = cv.take<int4>((size_t)in.B * Lp);
+    w.dsc = cv.take<float>((size_t)in.B * in.Hq * Lp);
     w.lse2 = cv.take<float>((size_t)in.B * in.Hq * Lp);
   }
   if (o) *o = w;
@@ -61,10 +67,6 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->NT = ws.Lp / OPR_ATTN_BLOCK;
   p->scale = scale;
   p->scale_log2 = scale * kLog2e;
-  p->tok_conv = in.layout.tok_conv;
-  p->tok_turn = in.layout.tok_turn;
-  p->tok_pos = in.layout.tok_pos;
-  p->tok_type = in.layout.tok_type;
   p->tile_class = in.layout.tile_class;
   p->sub_class = in.layout.sub_class;
   p->q_nnz = in.layout.q_nnz;
@@ -76,12 +78,14 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->kr = ws.kr;
   p->vr = ws.vr;
   p->dor = ws.dor;
-  p->eq = ws.eq;
-  p->ek = ws.ek;
-  p->ev = ws.ev;
-  p->edo = ws.edo;
-  p->meta = ws.meta;
-  p->delta = ws.delta;
+  p->mq = ws.mq;
+  p->mk = ws.mk;
+  p->mv = ws.mv;
+  p->mdo = ws.mdo;
+  p->qiv = ws.qiv;
+  p->kiv = ws.kiv;
+  p->hvb = ws.hvb;
+  p->dsc = ws.dsc;
   p->lse2 = ws.lse2;
 }
 
@@ -212,10 +216,13 @@ opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *worksp
   carve_attn_ws(workspace, *in, 0, &ws);
   mark(in, 0, stream);
   launch_rope_table(*in, ws, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, nullptr, ws.eq, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, nullptr, ws.ek, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, ws.vr, nullptr, ws.ev, stream);
-  launch_meta(*in, ws, stream);
+  launch_absmax(in->D, in->B, in->L, in->Hq, in->q, true, ws.mq, stream);
+  launch_absmax(in->D, in->B, in->L, in->Hkv, in->k, true, ws.mk, stream);
+  launch_absmax(in->D, in->B, in->L, in->Hkv, in->v, false, ws.mv, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->Hq / in->Hkv, in->q, ws.rope, ws.mq, ws.qr, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, 1, in->k, ws.rope, ws.mk, ws.kr, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, 1, in->v, ws.rope, ws.mv, ws.vr, stream);
+  launch_intervals(*in, ws, stream);
   mark(in, 1, stream);
   if (launch_attn_fwd_kernel(*in, effective_scale(in), o, lse, ws, stream) != hipSuccess) return OPR_E_HIP;
   mark(in, 2, stream);
@@ -233,12 +240,16 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   carve_attn_ws(workspace, *in, 1, &ws);
   mark(in, 0, stream);
   launch_rope_table(*in, ws, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->q, ws.rope, ws.qr, nullptr, ws.eq, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, in->k, ws.rope, ws.kr, nullptr, ws.ek, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, in->v, nullptr, ws.vr, nullptr, ws.ev, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, dout, nullptr, ws.dor, nullptr, ws.edo, stream);
+  launch_absmax(in->D, in->B, in->L, in->Hq, in->q, true, ws.mq, stream);
+  launch_absmax(in->D, in->B, in->L, in->Hkv, in->k, true, ws.mk, stream);
+  launch_absmax(in->D, in->B, in->L, in->Hkv, in->v, false, ws.mv, stream);
+  launch_absmax(in->D, in->B, in->L, in->Hq, dout, false, ws.mdo, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->Hq / in->Hkv, in->q, ws.rope, ws.mq, ws.qr, stream);
+  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, 1, in->k, ws.rope, ws.mk, ws.kr, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, 1, in->v, ws.rope, ws.mv, ws.vr, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, in->Hq / in->Hkv, dout, ws.rope, ws.mdo, ws.dor, stream);
+  launch_intervals(*in, ws, stream);
   launch_delta(*in, o, dout, lse, ws, stream);
-  launch_meta(*in, ws, stream);
   if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream,
                               in->timing_events ? in->timing_events + 1 : nullptr) != hipSuccess)
     return OPR_E_HIP;

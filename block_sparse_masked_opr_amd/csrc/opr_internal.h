@@ -53,14 +53,20 @@ hipError_t launch_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t bl
 struct AttnWs {
   int32_t Lp;           // L rounded up to OPR_ATTN_BLOCK
   float2 *rope;         // [B][Lp][D/2] (cos, sin) at each token's position id
-  // fp16 copies, one power-of-two scale per 64-token block (exponents below)
-  uint16_t *qr;         // [B][Hq][Lp][D]  q after RoPE, head-major, zero past L
-  uint16_t *kr;         // [B][Hkv][Lp][D] k after RoPE
-  uint16_t *vr;         // [B][Hkv][Lp][D] v head-major
-  uint16_t *dor;        // [B][Hq][Lp][D]  dout head-major             (bwd)
-  int32_t *eq, *ek, *ev, *edo;  // block exponents [B][H][Lp/64]   (edo: bwd)
-  int2 *meta;           // [B][Lp] (conv, turn * 8 + type), conv -1 for PAD / past L
-  float *delta;         // [B][Hq][Lp] rowsum(dout * o)                (bwd)
+  // fp16 copies [B][H][Lp][D], one power-of-two scale per (row, head) plane,
+  // zero past L
+  uint16_t *qr;         // q after RoPE
+  uint16_t *kr;         // k after RoPE
+  uint16_t *vr;         // v
+  uint16_t *dor;        // dout                                   (bwd)
+  // plane maxima (float bits): mq [B][Hq], mk [B][Hkv], mv [B][Hkv],
+  // mdo [B][Hq], contiguous from pmax (n_pmax words)
+  uint32_t *pmax, *mq, *mk, *mv, *mdo;
+  int32_t n_pmax;
+  int4 *qiv;            // [B][Lp] per-query key intervals
+  int4 *kiv;            // [B][Lp] per-key query intervals              (bwd)
+  uint64_t *hvb;        // [B][Lp/64] h / r_in bits
+  float *dsc;           // [B][Hq][Lp] rowsum(dout * o), scaled        (bwd)
   float *lse2;          // [B][Hq][Lp] log2-domain lse, +inf where no key (bwd)
 };
 
