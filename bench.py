@@ -96,8 +96,8 @@ class Runner:
         self.lay = Bd.opr_build_layout(rows, L, 128, 128, device=dev)
         cpr, tpc, turns = I.flatten_rows(rows)
         self.lws = torch.empty(Bd.opr_build_layout_workspace_size(B, L, len(tpc), len(turns)), dtype=torch.uint8, device=dev)
-        self.fws = torch.empty(Bd.opr_attn_workspace_size(B, L, Hq, Hkv, D, False), dtype=torch.uint8, device=dev)
-        self.bws = torch.empty(Bd.opr_attn_workspace_size(B, L, Hq, Hkv, D, True), dtype=torch.uint8, device=dev)
+        # one workspace: the backward reuses the forward state at its start
+        self.ws = torch.empty(Bd.opr_attn_workspace_size(B, L, Hq, Hkv, D, True), dtype=torch.uint8, device=dev)
         self.o = torch.empty_like(t["q"])
         self.lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
         self.dq = torch.empty(t["q"].shape, dtype=torch.float32, device=dev)
@@ -107,10 +107,11 @@ class Runner:
     def step(self, ev_f=None, ev_b=None):
         Bd, t = self.Bd, self.t
         Bd.opr_build_layout(self.rows, self.L, 128, 128, device=self.o.device, workspace=self.lws, out=self.lay)
-        Bd.opr_attn_fwd(t["q"], t["k"], t["v"], self.lay, self.theta, workspace=self.fws,
+        Bd.opr_attn_fwd(t["q"], t["k"], t["v"], self.lay, self.theta, workspace=self.ws,
                         out=(self.o, self.lse), events=ev_f)
         Bd.opr_attn_bwd(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], self.lay, self.theta,
-                        workspace=self.bws, out=(self.dq, self.dk, self.dv), events=ev_b)
+                        workspace=self.ws, out=(self.dq, self.dk, self.dv), events=ev_b,
+                        reuse_fwd_workspace=True)
 
     def time_steps(self, steps, warmup):
         torch = self.torch

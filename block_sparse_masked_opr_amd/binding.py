@@ -47,7 +47,7 @@ class OprAttnIn(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("layout", OprLayout),
                 ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
-                ("timing_events", ctypes.c_void_p)]
+                ("timing_events", ctypes.c_void_p), ("reuse_fwd_workspace", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -159,7 +159,7 @@ def opr_build_layout(rows: Sequence, L: int, block_q: int = OPR_ATTN_BLOCK,
     return lay
 
 
-def _attn_in(q, k, v, lay: Layout, theta: float, scale: float, events=None) -> OprAttnIn:
+def _attn_in(q, k, v, lay: Layout, theta: float, scale: float, events=None, reuse=False) -> OprAttnIn:
     B, L, Hq, D = q.shape
     Hkv = k.shape[2]
     for name, t, H in (("q", q, Hq), ("k", k, Hkv), ("v", v, Hkv)):
@@ -169,7 +169,7 @@ def _attn_in(q, k, v, lay: Layout, theta: float, scale: float, events=None) -> O
         raise ValueError("layout built for a different B or L")
     return OprAttnIn(B, L, Hq, Hkv, D, float(scale), float(theta), q.data_ptr(), k.data_ptr(),
                      v.data_ptr(), lay.c_struct(), lay.block_q, lay.block_k,
-                     None if events is None else ctypes.addressof(events))
+                     None if events is None else ctypes.addressof(events), 1 if reuse else 0)
 
 
 def opr_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lay: Layout,
@@ -194,10 +194,15 @@ def opr_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lay: Layout,
 
 
 def opr_attn_bwd(q, k, v, o, lse, dout, lay: Layout, theta: float = 1.0e6, scale: float = 0.0,
-                 workspace: Optional[torch.Tensor] = None, out=None, events=None):
+                 workspace: Optional[torch.Tensor] = None, out=None, events=None,
+                 reuse_fwd_workspace: bool = False):
     """Returns (dq, dk, dv) fp32 with the shapes of q, k, v.  ``events``:
-    optional ctypes array of 4 hipEvent_t handles recorded around the stages."""
-    a = _attn_in(q, k, v, lay, theta, scale, events)
+    optional ctypes array of 4 hipEvent_t handles recorded around the stages.
+    ``reuse_fwd_workspace``: ``workspace`` is the one the matching
+    opr_attn_fwd call just used (its forward state is reused)."""
+    if reuse_fwd_workspace and workspace is None:
+        raise ValueError("reuse_fwd_workspace needs the forward's workspace")
+    a = _attn_in(q, k, v, lay, theta, scale, events, reuse_fwd_workspace)
     B, L, Hq, D = q.shape
     if dout.dtype != torch.bfloat16 or not dout.is_contiguous() or dout.shape != q.shape:
         raise ValueError("dout must be contiguous bfloat16 shaped like q")

@@ -6,7 +6,8 @@
 //    power-of-two scale per plane, padded with zeros to a whole number of
 //    128-token tiles,
 //  - per-token mask intervals (below) and per-64-token "history" bits,
-//  - the backward preprocessing delta = rowsum(dout * o), scaled.
+//  - the backward preprocessing delta = rowsum(dout * o), scaled, with the
+//    dout plane maxima.
 //
 // RoPE (rotate-half): pair (j, j + D/2) of a head vector is rotated by
 // pos * theta^(-2j/D).  The angle and its cosine and sine are computed in
@@ -54,31 +55,34 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, i
 
 // Largest |x| of each (row, head) plane of x [B][L][H][D] bf16, times
 // `factor` (sqrt(2) bound of RoPE on a pair, rounded up), into pmax[b][h] as
-// float bits.  One workgroup per (64 tokens, head, row).
+// float bits.  A workgroup covers kAbsTokens tokens of HPB heads: thread
+// (head hl, chunk j) reads 16-byte chunk j of head hl of every token, so each
+// 16-lane group reads one head's whole row and a wave reads contiguous runs.
+constexpr int kAbsTokens = 64;
+
 template <int D>
 __global__ __launch_bounds__(256) void absmax_kernel(int32_t L, int32_t H, const uint16_t *x, float factor,
                                                      uint32_t *pmax) {
-  __shared__ float wmax[4];
-  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  constexpr int CPH = D / 8, HPB = 256 / CPH;
+  const int b = blockIdx.z, tid = threadIdx.x;
+  const int hl = tid / CPH, j = tid % CPH;
+  const int h = blockIdx.y * HPB + hl;
+  const int t0 = blockIdx.x * kAbsTokens;
   float m = 0.0f;
-  for (int c = tid; c < 64 * D / 8; c += 256) {
-    const int t = blockIdx.x * 64 + c / (D / 8);
-    if (t < L) {
+  if (h < H) {
+    const uint16_t *src = x + (((int64_t)b * L + t0) * H + h) * D + j * 8;
+    const int nt = min(kAbsTokens, L - t0);
+#pragma unroll 8
+    for (int t = 0; t < nt; ++t) {
       uint16_t v[8];
-      *reinterpret_cast<uint4 *>(v) =
-          *reinterpret_cast<const uint4 *>(x + (((int64_t)b * L + t) * H + h) * D + (c % (D / 8)) * 8);
+      *reinterpret_cast<uint4 *>(v) = *reinterpret_cast<const uint4 *>(src + (int64_t)t * H * D);
 #pragma unroll
       for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(bf16_to_f32(v[e])));
     }
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((tid & 63) == 0) wmax[tid >> 6] = m;
-  __syncthreads();
-  if (tid == 0) {
-    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])) * factor;
-    if (m > 0.0f) atomicMax(pmax + (int64_t)b * H + h, __float_as_uint(m));
-  }
+  for (int off = CPH / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (j == 0 && h < H && m > 0.0f) atomicMax(pmax + (int64_t)b * H + h, __float_as_uint(m * factor));
 }
 
 // One workgroup per (64-token block, head, row).  x: [B][L][H][D] bf16 ->
@@ -192,59 +196,100 @@ __global__ __launch_bounds__(256) void intervals_kernel(int32_t B, int32_t L, in
   if (active && (threadIdx.x & 63) == 0) hvb[gid >> 6] = bits;  // Lp is a multiple of 64
 }
 
-// dsc[b][h][t] = sum_d dout * o (float32 over bf16 inputs) times
-// 2^(e_dout + e_v - kDsShift): delta in the units of dP = dO V^T computed on
-// the scaled operands, shifted like dS;
-// lse2[b][h][t] = lse * log2(e), +inf where the row has no key (lse = -inf)
-// or t >= L, so that recomputed probabilities are exactly 0 there.
+// Backward preprocessing, before dout is packed: per token and q head
+//   dsc[b][h][t]  = sum_d dout * o (float32 over bf16 inputs),
+//   lse2[b][h][t] = lse * log2(e), +inf where the row has no key (lse = -inf)
+//                   or t >= L, so that recomputed probabilities are exactly 0;
+// and the largest |dout| of each (row, head) plane into mdo (float bits).
 // One wave per token: D/8 lanes read one head's 16-byte chunks, so a wave
-// covers 64/(D/8) heads per step with fully coalesced row reads.
+// covers 64/(D/8) heads per step with fully coalesced row reads; the plane
+// maxima are combined in LDS, then once per workgroup in memory.
+constexpr int kMaxHeads = 1024;
+
 template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_t Lp, int32_t Hq, int32_t group,
+__global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_t Lp, int32_t Hq,
                                                     const uint16_t *o, const uint16_t *dout, const float *lse,
-                                                    const uint32_t *mdo, const uint32_t *mv, float *dsc,
-                                                    float *lse2) {
+                                                    uint32_t *mdo, float *dsc, float *lse2) {
   constexpr int LPH = D / 8;        // lanes per head
   constexpr int HPS = 64 / LPH;     // heads per step
-  const int64_t bt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (bt >= (int64_t)B * Lp) return;
+  constexpr int TPW = 4;            // tokens per wave
+  __shared__ uint32_t hmax[kMaxHeads];
+  for (int i = threadIdx.x; i < Hq; i += 256) hmax[i] = 0u;
+  __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int32_t t = (int32_t)(bt % Lp);
-  const int32_t b = (int32_t)(bt / Lp);
   const int hl = lane / LPH, part = lane % LPH;
-  for (int h0 = 0; h0 < Hq; h0 += HPS) {
-    const int h = h0 + hl;
-    float acc = 0.0f;
-    if (t < L && h < Hq) {
-      const int64_t base = (((int64_t)b * L + t) * Hq + h) * D + part * 8;
-      uint16_t ov[8], dv[8];
-      *reinterpret_cast<uint4 *>(ov) = *reinterpret_cast<const uint4 *>(o + base);
-      *reinterpret_cast<uint4 *>(dv) = *reinterpret_cast<const uint4 *>(dout + base);
+  const int64_t bt0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
+  for (int k = 0; k < TPW; ++k) {
+    const int64_t bt = bt0 + k;
+    if (bt >= (int64_t)B * Lp) break;
+    const int32_t t = (int32_t)(bt % Lp);
+    const int32_t b = (int32_t)(bt / Lp);
+    if (b != (int32_t)(bt0 / Lp)) break;  // a workgroup's plane maxima stay within one row
+    for (int h0 = 0; h0 < Hq; h0 += HPS) {
+      const int h = h0 + hl;
+      float acc = 0.0f, mx = 0.0f;
+      if (t < L && h < Hq) {
+        const int64_t base = (((int64_t)b * L + t) * Hq + h) * D + part * 8;
+        uint16_t ov[8], dv[8];
+        *reinterpret_cast<uint4 *>(ov) = *reinterpret_cast<const uint4 *>(o + base);
+        *reinterpret_cast<uint4 *>(dv) = *reinterpret_cast<const uint4 *>(dout + base);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += bf16_to_f32(ov[e]) * bf16_to_f32(dv[e]);
-    }
-#pragma unroll
-    for (int off = LPH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (part == 0 && h < Hq) {
-      float l2 = INFINITY;
-      if (t < L) {
-        const float l = lse[((int64_t)b * Hq + h) * L + t];
-        l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+        for (int e = 0; e < 8; ++e) {
+          const float dd = bf16_to_f32(dv[e]);
+          acc += bf16_to_f32(ov[e]) * dd;
+          mx = fmaxf(mx, fabsf(dd));
+        }
       }
-      const int kv = h / group, Hkv = Hq / group;
-      const int e = group_exponent(mdo + (int64_t)b * Hq + kv * group, group) +
-                    plane_exponent(mv[(int64_t)b * Hkv + kv]) - kDsShift;
-      const int64_t out = ((int64_t)b * Hq + h) * Lp + t;
-      dsc[out] = ldexpf(acc, e);
-      lse2[out] = l2;
+#pragma unroll
+      for (int off = LPH / 2; off > 0; off >>= 1) {
+        acc += __shfl_xor(acc, off);
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+      }
+      if (part == 0 && h < Hq) {
+        float l2 = INFINITY;
+        if (t < L) {
+          const float l = lse[((int64_t)b * Hq + h) * L + t];
+          l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+        }
+        const int64_t out = ((int64_t)b * Hq + h) * Lp + t;
+        dsc[out] = acc;
+        lse2[out] = l2;
+        if (mx > 0.0f) atomicMax(&hmax[h], __float_as_uint(mx));
+      }
     }
   }
+  __syncthreads();
+  const int64_t b = ((int64_t)blockIdx.x * 4 * TPW) / Lp;
+  if (b < B)
+    for (int i = threadIdx.x; i < Hq; i += 256)
+      if (hmax[i]) atomicMax(mdo + b * Hq + i, hmax[i]);
+}
+
+// dsc *= 2^(e_dout + e_v - kDsShift): delta in the units of dP = dO V^T on the
+// scaled operands, shifted like dS.  One thread per (b, h, t).
+__global__ __launch_bounds__(256) void scale_delta_kernel(int32_t B, int32_t Lp, int32_t Hq, int32_t group,
+                                                          const uint32_t *mdo, const uint32_t *mv, float *dsc) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)B * Hq * Lp) return;
+  const int64_t bh = gid / Lp;
+  const int h = (int)(bh % Hq);
+  const int64_t b = bh / Hq;
+  const int kv = h / group, Hkv = Hq / group;
+  const int e = group_exponent(mdo + b * Hq + kv * group, group) + plane_exponent(mv[b * Hkv + kv]) - kDsShift;
+  dsc[gid] = ldexpf(dsc[gid], e);
+}
+
+__global__ void zero_words_kernel(uint32_t *p, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 template <int D>
 void launch_absmax_d(int32_t B, int32_t L, int32_t H, const void *x, float factor, uint32_t *pmax,
                      hipStream_t s) {
-  absmax_kernel<D><<<dim3((L + 63) / 64, H, B), 256, 0, s>>>(L, H, static_cast<const uint16_t *>(x), factor, pmax);
+  constexpr int HPB = 256 / (D / 8);
+  absmax_kernel<D><<<dim3((L + kAbsTokens - 1) / kAbsTokens, (H + HPB - 1) / HPB, B), 256, 0, s>>>(
+      L, H, static_cast<const uint16_t *>(x), factor, pmax);
 }
 
 template <int D>
@@ -286,19 +331,26 @@ void launch_intervals(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
       in.B, in.L, ws.Lp, in.layout.tok_conv, in.layout.tok_turn, in.layout.tok_type, ws.qiv, ws.kiv, ws.hvb);
 }
 
+// delta, lse2 and the dout plane maxima (mdo is cleared first), then dout
+// packing and the delta scaling are done by the caller in that order.
 void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
                   const AttnWs &ws, hipStream_t s) {
-  const int64_t total = (int64_t)in.B * ws.Lp;  // one wave per token
-  const unsigned blocks = (unsigned)((total + 3) / 4);
+  const int32_t nz = in.B * in.Hq;
+  zero_words_kernel<<<(nz + 255) / 256, 256, 0, s>>>(ws.mdo, nz);
+  const int64_t tokens = (int64_t)in.B * ws.Lp;  // 16 tokens per workgroup
+  const unsigned blocks = (unsigned)((tokens + 15) / 16);
   const uint16_t *o16 = static_cast<const uint16_t *>(o);
   const uint16_t *d16 = static_cast<const uint16_t *>(dout);
-  const int32_t group = in.Hq / in.Hkv;
   if (in.D == 64)
-    delta_kernel<64><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, group, o16, d16, lse, ws.mdo, ws.mv,
-                                            ws.dsc, ws.lse2);
+    delta_kernel<64><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, ws.mdo, ws.dsc, ws.lse2);
   else
-    delta_kernel<128><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, group, o16, d16, lse, ws.mdo, ws.mv,
-                                             ws.dsc, ws.lse2);
+    delta_kernel<128><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, ws.mdo, ws.dsc, ws.lse2);
+}
+
+void launch_scale_delta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+  const int64_t total = (int64_t)in.B * in.Hq * ws.Lp;
+  scale_delta_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(in.B, ws.Lp, in.Hq, in.Hq / in.Hkv, ws.mdo,
+                                                                     ws.mv, ws.dsc);
 }
 
 }  // namespace opr

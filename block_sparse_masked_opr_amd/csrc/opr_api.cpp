@@ -15,6 +15,7 @@ void launch_absmax(int D, int32_t B, int32_t L, int32_t H, const void *x, bool r
 void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,
                      const void *x, const float2 *table, const uint32_t *pmax, uint16_t *rows, hipStream_t s);
 void launch_intervals(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
+void launch_scale_delta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
                   const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, float *lse,
@@ -45,10 +46,11 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
     w.mdo = w.mv + (size_t)in.B * in.Hkv;
   }
   w.qiv = cv.take<int4>((size_t)in.B * Lp);
+  w.kiv = cv.take<int4>((size_t)in.B * Lp);
   w.hvb = cv.take<uint64_t>((size_t)in.B * (Lp / 64));
+  // everything above is the forward state; the backward part follows
   if (is_bwd) {
     w.dor = cv.take<uint16_t>(qn);
-    w.kiv = cv.take<int4>((size_t)in.B * Lp);
     w.dsc = cv.take<float>((size_t)in.B * in.Hq * Lp);
     w.lse2 = cv.take<float>((size_t)in.B * in.Hq * Lp);
   }
@@ -95,7 +97,7 @@ static opr_status check_attn_shape(int32_t B, int32_t L, int32_t Hq, int32_t Hkv
   if (Hq % Hkv != 0) return OPR_E_INVALID;
   if (Hq / Hkv > 255) return OPR_E_UNSUPPORTED;  // head-in-group index of a dK/dV stage is 8 bits
   if (D != 64 && D != 128) return OPR_E_UNSUPPORTED;
-  if (B > 65535 || Hq > 65535) return OPR_E_UNSUPPORTED;  // grid dimensions
+  if (B > 65535 || Hq > 1024) return OPR_E_UNSUPPORTED;  // grid dimensions, per-head LDS tables
   const int64_t Lp = ((int64_t)L + OPR_ATTN_BLOCK - 1) / OPR_ATTN_BLOCK * OPR_ATTN_BLOCK;
   // every element index of the largest tensor must fit in int64 with room;
   // row indices (b*L + t) are kept in int32 by the layout
@@ -125,6 +127,20 @@ static float effective_scale(const opr_attn_in *in) {
 
 static void mark(const opr_attn_in *in, int i, hipStream_t s) {
   if (in->timing_events) hipEventRecord(in->timing_events[i], s);
+}
+
+// RoPE table, plane maxima and fp16 copies of q, k, v, mask intervals: the
+// forward state at the start of the workspace.
+static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_t stream) {
+  const int32_t group = in.Hq / in.Hkv;
+  launch_rope_table(in, ws, stream);
+  launch_absmax(in.D, in.B, in.L, in.Hq, in.q, true, ws.mq, stream);
+  launch_absmax(in.D, in.B, in.L, in.Hkv, in.k, true, ws.mk, stream);
+  launch_absmax(in.D, in.B, in.L, in.Hkv, in.v, false, ws.mv, stream);
+  launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hq, group, in.q, ws.rope, ws.mq, ws.qr, stream);
+  launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hkv, 1, in.k, ws.rope, ws.mk, ws.kr, stream);
+  launch_pack_any(in.D, false, in.B, in.L, ws.Lp, in.Hkv, 1, in.v, ws.rope, ws.mv, ws.vr, stream);
+  launch_intervals(in, ws, stream);
 }
 
 static opr_status hip_status() {
@@ -215,14 +231,7 @@ opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *worksp
   AttnWs ws;
   carve_attn_ws(workspace, *in, 0, &ws);
   mark(in, 0, stream);
-  launch_rope_table(*in, ws, stream);
-  launch_absmax(in->D, in->B, in->L, in->Hq, in->q, true, ws.mq, stream);
-  launch_absmax(in->D, in->B, in->L, in->Hkv, in->k, true, ws.mk, stream);
-  launch_absmax(in->D, in->B, in->L, in->Hkv, in->v, false, ws.mv, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->Hq / in->Hkv, in->q, ws.rope, ws.mq, ws.qr, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, 1, in->k, ws.rope, ws.mk, ws.kr, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, 1, in->v, ws.rope, ws.mv, ws.vr, stream);
-  launch_intervals(*in, ws, stream);
+  forward_prologue(*in, ws, stream);
   mark(in, 1, stream);
   if (launch_attn_fwd_kernel(*in, effective_scale(in), o, lse, ws, stream) != hipSuccess) return OPR_E_HIP;
   mark(in, 2, stream);
@@ -239,17 +248,10 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   AttnWs ws;
   carve_attn_ws(workspace, *in, 1, &ws);
   mark(in, 0, stream);
-  launch_rope_table(*in, ws, stream);
-  launch_absmax(in->D, in->B, in->L, in->Hq, in->q, true, ws.mq, stream);
-  launch_absmax(in->D, in->B, in->L, in->Hkv, in->k, true, ws.mk, stream);
-  launch_absmax(in->D, in->B, in->L, in->Hkv, in->v, false, ws.mv, stream);
-  launch_absmax(in->D, in->B, in->L, in->Hq, dout, false, ws.mdo, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hq, in->Hq / in->Hkv, in->q, ws.rope, ws.mq, ws.qr, stream);
-  launch_pack_any(in->D, true, in->B, in->L, ws.Lp, in->Hkv, 1, in->k, ws.rope, ws.mk, ws.kr, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hkv, 1, in->v, ws.rope, ws.mv, ws.vr, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, in->Hq / in->Hkv, dout, ws.rope, ws.mdo, ws.dor, stream);
-  launch_intervals(*in, ws, stream);
+  if (!in->reuse_fwd_workspace) forward_prologue(*in, ws, stream);
   launch_delta(*in, o, dout, lse, ws, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, in->Hq / in->Hkv, dout, ws.rope, ws.mdo, ws.dor, stream);
+  launch_scale_delta(*in, ws, stream);
   if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream,
                               in->timing_events ? in->timing_events + 1 : nullptr) != hipSuccess)
     return OPR_E_HIP;

@@ -137,6 +137,13 @@ typedef struct {
    * opr_attn_bwd records [0] before its prologue, [1] before the dK/dV
    * kernel, [2] before the dQ kernel and [3] after it. */
   hipEvent_t *timing_events;
+  /* opr_attn_bwd only: nonzero when `workspace` is the one the matching
+   * opr_attn_fwd call (same inputs, layout and stream, nothing written to the
+   * workspace in between) just used.  The backward then reuses the fp16
+   * copies of q, k, v, their scales and the mask intervals that the forward
+   * left at the start of the workspace instead of recomputing them.  0 makes
+   * opr_attn_bwd self-contained. */
+  int32_t reuse_fwd_workspace;
 } opr_attn_in;
 
 /*
@@ -166,7 +173,9 @@ opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *worksp
  *  dout    bf16 [B][L][Hq][D].
  *  dq      fp32 [B][L][Hq][D];  dk, dv  fp32 [B][L][Hkv][D].  Every element
  *          is written (PAD rows get 0); nothing is accumulated into them.
- *  workspace  >= opr_attn_workspace_size(B, L, Hq, Hkv, D, 1) bytes.
+ *  workspace  >= opr_attn_workspace_size(B, L, Hq, Hkv, D, 1) bytes; the
+ *             forward part of it is a prefix, so one backward-sized
+ *             workspace serves both calls (see reuse_fwd_workspace).
  * Errors as for opr_attn_fwd.
  */
 opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse,

@@ -88,7 +88,7 @@ def test_layout_workspace_size(Bd):
 def _attn_in(Bd, **kw):
     a = dict(B=1, L=256, Hq=4, Hkv=2, D=128, softmax_scale=0.0, rope_theta=1e6,
              q=FAKE, k=FAKE, v=FAKE, layout=_layout_struct(Bd), block_q=128, block_k=128,
-             timing_events=None)
+             timing_events=None, reuse_fwd_workspace=0)
     a.update(kw)
     return Bd.OprAttnIn(**a)
 

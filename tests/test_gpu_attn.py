@@ -31,15 +31,22 @@ def B():
     return binding
 
 
-def run_gpu(Bd, rows, L, t, bwd=True):
+def run_gpu(Bd, rows, L, t, bwd=True, reuse=False):
+    """Layout, forward and (optionally) backward on the GPU.  reuse: the
+    backward gets the forward's workspace and reuses its state."""
     dev = torch.device("cuda:0")
     lay = Bd.opr_build_layout(rows, L, 128, 128, device=dev)
     q, k, v = (to_device_bf16(t[n], dev) for n in ("q", "k", "v"))
-    o, lse = Bd.opr_attn_fwd(q, k, v, lay, THETA)
+    ws = None
+    if reuse:
+        ws = torch.empty(Bd.opr_attn_workspace_size(len(rows), L, q.shape[2], k.shape[2], q.shape[3], True),
+                         dtype=torch.uint8, device=dev)
+    o, lse = Bd.opr_attn_fwd(q, k, v, lay, THETA, workspace=ws)
     res = {"o": o, "lse": lse}
     if bwd:
         do = to_device_bf16(t["do"], dev)
-        res["dq"], res["dk"], res["dv"] = Bd.opr_attn_bwd(q, k, v, o, lse, do, lay, THETA)
+        res["dq"], res["dk"], res["dv"] = Bd.opr_attn_bwd(q, k, v, o, lse, do, lay, THETA, workspace=ws,
+                                                          reuse_fwd_workspace=reuse)
     torch.cuda.synchronize()
     out = {"o": bf16_f64(from_device_bf16(res["o"])), "lse": res["lse"].cpu().numpy().astype(np.float64)}
     if bwd:
@@ -157,7 +164,7 @@ def test_packed_fwd_bwd(B):
     seed_len, seed_t = I.SEEDS["packed_fwd_bwd"]
     rows = I.packed_rows(s, seed_len)
     t = I.make_tensors(s.B, s.L, s.Hq, s.Hkv, s.D, seed=seed_t)
-    got = run_gpu(B, rows, s.L, t)
+    got = run_gpu(B, rows, s.L, t, reuse=True)  # as the benchmark runs it
     # the PAD tail of each row
     lay = O.layout(rows, s.L)
     pad = lay["type"] == O.PAD
@@ -218,3 +225,14 @@ def test_scaled_inputs(B):
         top = float(np.abs(ref[live]).max())
         assert_close(n, x[live] / top, ref[live] / top, max_abs=5e-3)
     assert_close("LSE", got["lse"].transpose(0, 2, 1)[live], lse.transpose(0, 2, 1)[live])
+
+
+def test_backward_reuse_is_identical(B):
+    """The backward reusing the forward's workspace gives bit-identical results."""
+    rows = [[[(30, 200, 50, 50), (20, 90, 70, 70)], [(64, 64, 64, 64)]], [[(10, 5, 3, 3)]]]
+    L = 900
+    t = I.make_tensors(2, L, 8, 2, 128, seed=31)
+    a = run_gpu(B, rows, L, t, reuse=False)
+    r = run_gpu(B, rows, L, t, reuse=True)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        np.testing.assert_array_equal(a[n], r[n], err_msg=n)
