@@ -43,7 +43,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
   constexpr int TB = Tile<D>::BYTES, RB = Tile<D>::RB;
   // per buffer: Q' tile, dO tile, lse2[64], scaled delta[64]
   constexpr int BUF = 2 * TB + 512;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  // two separate LDS objects so the copy into one provably leaves the other alone
+  __shared__ __attribute__((aligned(1024))) char buf0[BUF];
+  __shared__ __attribute__((aligned(1024))) char buf1[BUF];
   __shared__ uint2 stages[kStageCap];
   __shared__ int sh_count;
   __shared__ int64_t sh_next;
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
   const int kvh = (int)((u / p.NT) % p.Hkv);
   const int b = (int)(u / ((int64_t)p.NT * p.Hkv));
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int key = n * 128 + 32 * w + li;
   const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
   const int64_t hbase = (int64_t)b * p.Hq + (int64_t)kvh * p.group;  // first q head of the group
@@ -117,17 +119,16 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
       }
     }
     __syncthreads();
-    const int ns = sh_count;
-    fnext = sh_next;
+    const int ns = uniform(sh_count);
+    fnext = uniform(sh_next);
     if (ns == 0) continue;
-    issue(stages[0].x, smem);
-    for (int i = 0; i < ns; ++i) {
+    issue(uniform(stages[0].x), buf0);
+    auto stage = [&](int i, const char *buf, char *nxt) {
       wait_all_and_barrier();
-      const char *buf = smem + (i & 1) * BUF;
-      if (i + 1 < ns) issue(stages[i + 1].x, smem + ((i + 1) & 1) * BUF);
-      const uint2 desc = stages[i];
+      if (i + 1 < ns) issue(uniform(stages[i + 1].x), nxt);
+      const uint2 desc = uniform(stages[i]);
       const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
-      if ((c0 | c1) == 0) continue;
+      if ((c0 | c1) == 0) return;
       const uint32_t cls[2] = {c0, c1};
       const int q0 = (int)(desc.x & 0xFFFFFFu);
       const char *Qt = buf, *dOt = buf + TB;
@@ -182,6 +183,10 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
           }
         }
       }
+    };
+    for (int i = 0; i < ns; i += 2) {
+      stage(i, buf0, buf1);
+      if (i + 1 < ns) stage(i + 1, buf1, buf0);
     }
   }
 

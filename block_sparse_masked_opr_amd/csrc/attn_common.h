@@ -54,6 +54,17 @@ constexpr float kMaxSlack = 8.0f;
 constexpr int kPExp = 7;
 
 // A-operand row order of a 32-row block: swap bits 2 and 3.
+// Wave-uniform values that the compiler cannot prove uniform (the wave index,
+// words read from LDS): taking them from lane 0 puts them in scalar registers,
+// so buffer offsets and branches on them need no per-lane loops.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ uint2 uniform(uint2 x) { return make_uint2(uniform(x.x), uniform(x.y)); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  return (int64_t)(((uint64_t)uniform((uint32_t)(u >> 32)) << 32) | uniform((uint32_t)u));
+}
+
 __device__ __forceinline__ int kperm(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
@@ -153,10 +164,16 @@ __device__ __forceinline__ float mask_select(uint64_t m, int pos, float x) {
 
 // ---------------------------------------------------------------------------
 // LDS tiles of 64 rows x D fp16.  A row is D/8 chunks of 16 bytes; chunk c of
-// row r is stored in slot c ^ swz(r), so that 16 lanes reading the same chunk
-// of 16 different rows (MFMA A operand) or 4 rows x 32 bytes (transposing
-// reads) hit distinct banks without padding, and a 1 KB run of LDS is filled
-// by one asynchronous copy instruction (lane L writes bytes 16L..16L+15).
+// row r is stored in slot c ^ swz(r), swz(r) = 2(r mod 4) + bit 3 of r.  A row
+// is a multiple of 128 bytes, so a 16-byte slot's banks depend on slot mod 8
+// only, and the two read patterns touch all 32 banks per access group:
+//  - 16-byte reads (8 lanes per group): one chunk of rows {0-3, 8-11} (+4,
+//    +16k), the rows of the kperm order - swz mod 8 takes 8 distinct values;
+//  - transposing 8-byte reads (16 lanes per group): chunks 2p, 2p+1 of rows
+//    4a..4a+3 - swz/2 mod 4 takes 4 distinct values, so the 4 rows land in
+//    4 different 32-byte bank quarters.
+// No padding is needed, and a 1 KB run of LDS is filled by one asynchronous
+// copy instruction (lane L writes bytes 16L..16L+15).
 #define OPR_LDS __attribute__((address_space(3)))
 typedef short __attribute__((ext_vector_type(4))) s16x4;
 typedef short __attribute__((ext_vector_type(8))) s16x8;
@@ -166,7 +183,7 @@ struct Tile {
   static constexpr int NC = D / 8;       // chunks per row
   static constexpr int RB = 2 * D;       // bytes per row
   static constexpr int BYTES = 64 * RB;
-  __device__ static __forceinline__ int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
   __device__ static __forceinline__ int off(int r, int c) { return r * RB + ((c ^ swz(r)) << 4); }
 };
 

@@ -28,7 +28,9 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   constexpr int HALF_DB = NDB / 2;
   constexpr int TB = Tile<D>::BYTES, RB = Tile<D>::RB;
   constexpr int BUF = 2 * TB + 64;  // K' tile, V tile, 64 history bits of the keys
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  // two separate LDS objects so the copy into one provably leaves the other alone
+  __shared__ __attribute__((aligned(1024))) char buf0[BUF];
+  __shared__ __attribute__((aligned(1024))) char buf1[BUF];
   __shared__ uint2 stages[kStageCap];
   __shared__ int sh_count, sh_next;
 
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   const int b = (int)(rest / p.Hkv);
   const int h = kvh * p.group + j;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int q = m * 128 + 32 * w + li;
   const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
   const int64_t hbase = (int64_t)b * p.Hq + (int64_t)kvh * p.group;
@@ -100,17 +102,16 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
       }
     }
     __syncthreads();
-    const int ns = sh_count;
-    tnext = sh_next;
+    const int ns = uniform(sh_count);
+    tnext = uniform(sh_next);
     if (ns == 0) continue;
-    issue((int)stages[0].x, smem);
-    for (int i = 0; i < ns; ++i) {
+    issue(uniform((int)stages[0].x), buf0);
+    auto stage = [&](int i, const char *buf, char *nxt) {
       wait_all_and_barrier();
-      const char *buf = smem + (i & 1) * BUF;
-      if (i + 1 < ns) issue((int)stages[i + 1].x, smem + ((i + 1) & 1) * BUF);
-      const uint2 desc = stages[i];
+      if (i + 1 < ns) issue(uniform((int)stages[i + 1].x), nxt);
+      const uint2 desc = uniform(stages[i]);
       const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
-      if ((c0 | c1) == 0) continue;
+      if ((c0 | c1) == 0) return;
       const uint32_t cls[2] = {c0, c1};
       const int k0 = (int)desc.x;
       const char *Kt = buf, *Vt = buf + TB;
@@ -150,6 +151,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
             dqacc[db] = mfma32x32x16(tile_col8<D>(Kt, of, 32 * kb + 16 * hh, db), dsb[kb][hh], dqacc[db]);
         }
       }
+    };
+    for (int i = 0; i < ns; i += 2) {
+      stage(i, buf0, buf1);
+      if (i + 1 < ns) stage(i + 1, buf1, buf0);
     }
   }
 

@@ -32,7 +32,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
   constexpr int NDB = D / 32;  // 32-wide blocks of the head dim
   constexpr int TB = Tile<D>::BYTES, RB = Tile<D>::RB;
   constexpr int BUF = 2 * TB + 64;  // K tile, V tile, 64 history bits of the keys
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  // Two separate LDS objects (not one array indexed by stage parity): the
+  // compiler then knows that the asynchronous copy into one buffer does not
+  // write the other, and lets it run under the reads of the current stage.
+  __shared__ __attribute__((aligned(1024))) char buf0[BUF];
+  __shared__ __attribute__((aligned(1024))) char buf1[BUF];
   __shared__ uint2 stages[kStageCap];
   __shared__ int sh_count, sh_next;
 
@@ -47,7 +51,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
   const int b = (int)(rest / p.Hkv);
   const int h = kvh * p.group + j;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int q = m * 128 + 32 * w + li;
   const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
   const int eq = group_exponent(p.mq + (int64_t)b * p.Hq + kvh * p.group, p.group);
@@ -99,17 +103,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
       }
     }
     __syncthreads();
-    const int ns = sh_count;
-    tnext = sh_next;
+    const int ns = uniform(sh_count);
+    tnext = uniform(sh_next);
     if (ns == 0) continue;
-    issue((int)stages[0].x, smem);
-    for (int i = 0; i < ns; ++i) {
+    issue(uniform((int)stages[0].x), buf0);
+    // stage i reads `buf` while stage i+1 streams into `nxt`
+    auto stage = [&](int i, const char *buf, char *nxt) {
       wait_all_and_barrier();
-      const char *buf = smem + (i & 1) * BUF;
-      if (i + 1 < ns) issue((int)stages[i + 1].x, smem + ((i + 1) & 1) * BUF);
-      const uint2 desc = stages[i];
+      if (i + 1 < ns) issue(uniform((int)stages[i + 1].x), nxt);
+      const uint2 desc = uniform(stages[i]);
       const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
-      if ((c0 | c1) == 0) continue;
+      if ((c0 | c1) == 0) return;
       const uint32_t cls[2] = {c0, c1};
       const int k0 = (int)desc.x;
       const char *Kt = buf, *Vt = buf + TB;
@@ -171,6 +175,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
             oacc[db] = mfma32x32x16(tile_col8<D>(Vt, of, 32 * kb + 16 * hh, db), pb[kb][hh], oacc[db]);
         }
       }
+    };
+    for (int i = 0; i < ns; i += 2) {
+      stage(i, buf0, buf1);
+      if (i + 1 < ns) stage(i + 1, buf1, buf0);
     }
   }
 
