@@ -26,6 +26,8 @@
 // units 2^(e_dout + e_v); delta arrives pre-scaled into those units times
 // 2^-kDsShift, and dS is formed as P * 2^-kDsShift * (dP - delta) before the
 // fp16 conversion; P for dV is stored as fp16(P * 2^15).
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_sched.h"
 #include "opr_internal.h"
@@ -129,60 +131,134 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
       const uint2 desc = uniform(stages[i]);
       const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
       if ((c0 | c1) == 0) return;
-      const uint32_t cls[2] = {c0, c1};
       const int q0 = (int)(desc.x & 0xFFFFFFu);
       const char *Qt = buf, *dOt = buf + TB;
       const float *lse2s = reinterpret_cast<const float *>(buf + 2 * TB);
       const float *dscs = reinterpret_cast<const float *>(buf + 2 * TB + 256);
+      const uint64_t mq = (range_bits(key, iv.x, q0) | range_bits(iv.y, iv.z, q0) | range_bits(iv.z, iv.w, q0)) >> (8 * g);
 
-      uint64_t mq = 0;
-      if (c0 == 1 || c1 == 1)
-        mq = (range_bits(key, iv.x, q0) | range_bits(iv.y, iv.z, q0) | range_bits(iv.z, iv.w, q0)) >> (8 * g);
-
-      f16x8 pb[2][2], dsb[2][2];
+      // One straight-line body per case (both sub-blocks, masked or not; a
+      // single sub-block), laid
+      // out as a software pipeline over the present 32-query sub-blocks j:
+      //   A(j): S^T = K' Q'^T and dP^T = V dO^T, operands read in the products
+      //         before (16-byte reads of the row tiles);
+      //   B(j): masking, P and dS (element work), overlapping A(j+1) / C(j-1);
+      //   C(j): dV^T += dO^T P^T, dK^T += Q'^T dS^T (transposing reads).
+      auto body = [&](auto both, auto msk, int QB0) {
+        constexpr int NQ = decltype(both)::value ? 2 : 1;  // sub-blocks QB0 .. QB0 + NQ - 1
+        constexpr bool M = decltype(msk)::value;
+        f16x8 fa[NQ][2 * NS];
+        f32x16 s[NQ], dp[NQ];
+        f16x8 pb[NQ][2], dsb[NQ][2];
+        auto read_a = [&](int j) {
+          const int qb = QB0 + j;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if (cls[qb] == 0) continue;
-        f32x16 s = zero_f32x16(), dp = zero_f32x16();
+          for (int st = 0; st < NS; ++st) {
+            fa[j][st] = lds_f16x8(Qt + qb * 32 * RB + of.row8[st]);
+            fa[j][NS + st] = lds_f16x8(dOt + qb * 32 * RB + of.row8[st]);
+          }
+        };
+        auto products_a = [&](int j) {
+          s[j] = zero_f32x16();
+          dp[j] = zero_f32x16();
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          s = mfma32x32x16(lds_f16x8(Qt + qb * 32 * RB + of.row8[st]), kb_[st], s);
-          dp = mfma32x32x16(lds_f16x8(dOt + qb * 32 * RB + of.row8[st]), vb_[st], dp);
-        }
-        if (cls[qb] == 1) {
+          for (int st = 0; st < NS; ++st) {
+            s[j] = mfma32x32x16(fa[j][st], kb_[st], s[j]);
+            dp[j] = mfma32x32x16(fa[j][NS + st], vb_[st], dp[j]);
+          }
+        };
+        auto elementwise_b = [&](int j) {
+          const int qb = QB0 + j;
+          if (M) {
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) s[rr] = mask_select(mq, 32 * qb + 16 * (rr >> 3) + (rr & 7), s[rr]);
-        }
+            for (int rr = 0; rr < 16; ++rr) s[j][rr] = mask_select(mq, 32 * qb + 16 * (rr >> 3) + (rr & 7), s[j][rr]);
+          }
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int qbase = 32 * qb + 16 * hh + 8 * g;  // rows of registers 8hh .. 8hh+7
-          const float4 l0 = *reinterpret_cast<const float4 *>(lse2s + qbase);
-          const float4 l1 = *reinterpret_cast<const float4 *>(lse2s + qbase + 4);
-          const float4 d0 = *reinterpret_cast<const float4 *>(dscs + qbase);
-          const float4 d1 = *reinterpret_cast<const float4 *>(dscs + qbase + 4);
-          const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-          const float dvv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+          for (int hh = 0; hh < 2; ++hh) {
+            const int qbase = 32 * qb + 16 * hh + 8 * g;  // rows of registers 8hh .. 8hh+7
+            const float4 l0 = *reinterpret_cast<const float4 *>(lse2s + qbase);
+            const float4 l1 = *reinterpret_cast<const float4 *>(lse2s + qbase + 4);
+            const float4 d0 = *reinterpret_cast<const float4 *>(dscs + qbase);
+            const float4 d1 = *reinterpret_cast<const float4 *>(dscs + qbase + 4);
+            const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+            const float dvv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int rr = 8 * hh + e;
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[rr], fs, -lv[e]));
-            pb[qb][hh][e] = (_Float16)(pv * pdv);
-            dsb[qb][hh][e] = (_Float16)(pv * fmaf(dp[rr], dss, -dvv[e]));
+            for (int e = 0; e < 8; ++e) {
+              const int rr = 8 * hh + e;
+              const float pv = __builtin_amdgcn_exp2f(fmaf(s[j][rr], fs, -lv[e]));
+              pb[j][hh][e] = (_Float16)(pv * pdv);
+              dsb[j][hh][e] = (_Float16)(pv * fmaf(dp[j][rr], dss, -dvv[e]));
+            }
+          }
+        };
+        auto products_c = [&](int j) {
+          const int qb = QB0 + j;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              dvacc[db] = mfma32x32x16(tile_col8<D>(dOt, of, 32 * qb + 16 * hh, db), pb[j][hh], dvacc[db]);
+              dkacc[db] = mfma32x32x16(tile_col8<D>(Qt, of, 32 * qb + 16 * hh, db), dsb[j][hh], dkacc[db]);
+            }
+          }
+        };
+        read_a(0);
+        products_a(0);
+        if (NQ == 2) read_a(NQ - 1);
+        if (NQ == 2) products_a(NQ - 1);
+        elementwise_b(0);
+        products_c(0);
+        if (NQ == 2) elementwise_b(NQ - 1);
+        if (NQ == 2) products_c(NQ - 1);
+        // Interleave (one scheduling region): reads of the next phase between
+        // the products of the current one, element work between products.
+        constexpr int NA = 2 * NS;        // products (and 16-byte reads) of A(j)
+        constexpr int NC = 4 * NDB;       // products of C(j); 2 transposing reads each
+        constexpr unsigned kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+        __builtin_amdgcn_sched_group_barrier(kDsRead, NA, 0);
+        if (NQ == 2) {
+#pragma unroll
+          for (int k = 0; k < NA; ++k) {  // A(0) products, A(1) reads
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+          }
+#pragma unroll
+          for (int k = 0; k < NA; ++k) {  // A(1) products, B(0)
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kValu, 7, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
+#pragma unroll
+          for (int k = 0; k < NC; ++k) {  // C(0) products, B(1), C reads ahead
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kValu, 7, 0);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+          }
+#pragma unroll
+          for (int k = 0; k < NC; ++k) {  // C(1) products, C(1) reads ahead
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(kMfma, NA, 0);
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 8, 0);
+#pragma unroll
+          for (int k = 0; k < NA; ++k) {
+            __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+          }
+#pragma unroll
+          for (int k = 0; k < NC; ++k) {
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
           }
         }
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if (cls[qb] == 0) continue;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dvacc[db] = mfma32x32x16(tile_col8<D>(dOt, of, 32 * qb + 16 * hh, db), pb[qb][hh], dvacc[db]);
-            dkacc[db] = mfma32x32x16(tile_col8<D>(Qt, of, 32 * qb + 16 * hh, db), dsb[qb][hh], dkacc[db]);
-          }
-        }
-      }
+      };
+      using T = std::true_type;
+      using F = std::false_type;
+      // Both sub-blocks always: the 64-bit mask is exact, so an empty one
+      // (rare next to a non-empty one) contributes exact zeros.
+      body(T{}, T{}, 0);
     };
     for (int i = 0; i < ns; i += 2) {
       stage(i, buf0, buf1);
