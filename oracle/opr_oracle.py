@@ -135,8 +135,9 @@ _SAME_TURN_WHOLE = {H: (), T: (H,), RIN: (H,), ROUT: (H, T)}
 _HISTORY_TYPES = (H, RIN)
 
 
-def conv_mask(lay, b: int, c: int, q0: int = 0, q1: int = None) -> np.ndarray:
-    """Rows [q0, q1) (local to conversation c) of its dense bool mask [nq, n].
+def conv_mask(lay, b: int, c: int, q0: int = 0, q1: int = None, qidx=None) -> np.ndarray:
+    """Rows of conversation c's dense bool mask [nq, n] (conversation-local
+    indices): the queries q0 .. q1-1, or the listed queries ``qidx``.
 
     Built by set membership: for each (query segment, key segment) pair the
     rules say "all", "causal" (same segment) or "none".  Conversations are
@@ -144,15 +145,15 @@ def conv_mask(lay, b: int, c: int, q0: int = 0, q1: int = None) -> np.ndarray:
     """
     a, e = conv_range(lay, b, c)
     n = e - a
-    if q1 is None:
-        q1 = n
-    M = np.zeros((q1 - q0, n), dtype=bool)
+    if qidx is None:
+        qidx = np.arange(q0, n if q1 is None else q1)
+    qidx = np.asarray(qidx, dtype=np.int64)
+    M = np.zeros((len(qidx), n), dtype=bool)
     segs = _segments(lay, b, a, e)
     for (i, y, qs, qe) in segs:
-        qs_l, qe_l = max(qs - a, q0), min(qe - a, q1)
-        if qs_l >= qe_l:
+        rows = np.nonzero((qidx >= qs - a) & (qidx < qe - a))[0]
+        if len(rows) == 0:
             continue
-        rows = slice(qs_l - q0, qe_l - q0)
         for (j, x, ks, ke) in segs:
             cols = slice(ks - a, ke - a)
             if j < i and x in _HISTORY_TYPES:
@@ -161,7 +162,7 @@ def conv_mask(lay, b: int, c: int, q0: int = 0, q1: int = None) -> np.ndarray:
                 M[rows, cols] = True
             elif j == i and x == y:
                 # causal inside the segment: key index <= query index
-                qi = np.arange(qs_l, qe_l)[:, None]
+                qi = qidx[rows][:, None]
                 ki = np.arange(ks - a, ke - a)[None, :]
                 M[rows, cols] = ki <= qi
     return M
@@ -192,7 +193,7 @@ def _group_sum(M: np.ndarray, start: int, axis: int, g: int):
     return start // g, np.add.reduceat(M.astype(np.int64), cuts, axis=axis)
 
 
-def schedule(lay, b: int, BQ: int, BK: int, row_chunk: int = 2048) -> Dict[str, np.ndarray]:
+def schedule(lay, b: int, BQ: int, BK: int, row_chunk: int = 2048, order: str = "packed") -> Dict[str, np.ndarray]:
     """Tile classes and lists of row b for BQ x BK tiles.
 
     A tile is EMPTY if the mask allows none of its pairs, FULL if it allows all
@@ -200,17 +201,21 @@ def schedule(lay, b: int, BQ: int, BK: int, row_chunk: int = 2048) -> Dict[str, 
     same rule at 32 x 32 gives the sub-block classes, packed two bits each
     (sub-block (i, j) at bit 2*(i*BK/32 + j)).  q_list[m] lists the non-empty
     k-tiles of q-tile m ascending, k_list[n] the non-empty q-tiles of k-tile n.
+    order "packed" tiles the mask over the packed token order; "attention"
+    tiles it over attention order (queries and keys both at their slots).
     """
     L = lay["conv"].shape[1]
     MT, NT = -(-L // BQ), -(-L // BK)
     gg = math.gcd(math.gcd(BQ, BK), SUB)   # counting granularity
     G = np.zeros((MT * BQ // gg, NT * BK // gg), dtype=np.int64)
+    slot = attention_order(lay, b) if order == "attention" else np.arange(L)
     for c in range(n_convs(lay, b)):
         a, e = conv_range(lay, b, c)
         n = e - a
+        inv = np.argsort(slot[a:e] - a)    # local slot -> local token
         for r0 in range(0, n, row_chunk):
             r1 = min(n, r0 + row_chunk)
-            M = conv_mask(lay, b, c, r0, r1)
+            M = conv_mask(lay, b, c, qidx=inv[r0:r1])[:, inv]
             c0, Mc = _group_sum(M, a, 1, gg)
             r0g, Mrc = _group_sum(Mc, a + r0, 0, gg)
             G[r0g:r0g + Mrc.shape[0], c0:c0 + Mrc.shape[1]] += Mrc
@@ -251,6 +256,88 @@ def useful_pairs(lay) -> int:
             for r0 in range(0, n, 2048):
                 P += int(conv_mask(lay, b, c, r0, min(n, r0 + 2048)).sum())
     return P
+
+
+# ----------------------------------------------------------------------------
+# attention order: the same attention over reordered tokens
+# ----------------------------------------------------------------------------
+def attention_order(lay, b: int) -> np.ndarray:
+    """Slot of every token of row b in attention order.
+
+    Attention commutes with any reordering applied to queries and keys alike,
+    so the tokens may be processed in any order.  Attention order keeps every
+    conversation in its own index range and puts first the tokens that later
+    turns may see (h and r_in, in packed order), then the others (t and r_out,
+    in packed order); PAD tokens keep their index.  (Design choice of this
+    library, not of the pages: it makes the mask of every query at most two
+    runs of keys and makes it causal in slot order.)
+    """
+    L = lay["conv"].shape[1]
+    slot = np.arange(L, dtype=np.int64)
+    for c in range(n_convs(lay, b)):
+        a, e = conv_range(lay, b, c)
+        ty = lay["type"][b, a:e]
+        first = np.nonzero((ty == H) | (ty == RIN))[0]
+        second = np.nonzero((ty == T) | (ty == ROUT))[0]
+        local = np.concatenate([first, second])   # slot -> token, local
+        slot[a + local] = a + np.arange(e - a)
+    return slot
+
+
+def _runs(v: np.ndarray) -> List[Tuple[int, int]]:
+    """Maximal runs [lo, hi) of True in a 1-D bool array."""
+    d = np.diff(np.concatenate([[0], v.astype(np.int8), [0]]))
+    return list(zip(np.nonzero(d == 1)[0].tolist(), np.nonzero(d == -1)[0].tolist()))
+
+
+def _two_runs(runs: List[Tuple[int, int]], base: int) -> List[int]:
+    """[lo1, hi1, lo2, hi2] of at most two runs (offset by base); a missing run
+    is written [x, x) with x the end of the one before (0 for none)."""
+    if len(runs) > 2:
+        raise ValueError(f"{len(runs)} runs; attention order gives at most two")
+    out, x = [], 0
+    for k in range(2):
+        if k < len(runs):
+            lo, hi = runs[k][0] + base, runs[k][1] + base
+            out += [lo, hi]
+            x = hi
+        else:
+            out += [x, x]
+    return out
+
+
+def slot_intervals(lay, b: int, row_chunk: int = 2048) -> Tuple[np.ndarray, np.ndarray]:
+    """Mask of row b in attention order as runs of slots, [L, 4] each:
+    qiv[s] = the key slots that query slot s sees, kiv[s] = the query slots
+    that see key slot s, each as [lo1, hi1) and [lo2, hi2) (see _two_runs).
+    Read off the permuted mask row by row (queries) and column by column."""
+    L = lay["conv"].shape[1]
+    qiv = np.zeros((L, 4), dtype=np.int64)
+    kiv = np.zeros((L, 4), dtype=np.int64)
+    slot = attention_order(lay, b)
+    for c in range(n_convs(lay, b)):
+        a, e = conv_range(lay, b, c)
+        n = e - a
+        inv = np.argsort(slot[a:e] - a)
+        col_runs: List[List[Tuple[int, int]]] = [[] for _ in range(n)]
+        open_at = np.full(n, -1, dtype=np.int64)   # start of a column run still open
+        for r0 in range(0, n, row_chunk):
+            r1 = min(n, r0 + row_chunk)
+            M = conv_mask(lay, b, c, qidx=inv[r0:r1])[:, inv]
+            for i in range(r1 - r0):
+                qiv[a + r0 + i] = _two_runs(_runs(M[i]), a)
+                row = M[i]
+                starts = np.nonzero(row & (open_at < 0))[0]
+                ends = np.nonzero(~row & (open_at >= 0))[0]
+                for k in ends.tolist():
+                    col_runs[k].append((int(open_at[k]), r0 + i))
+                open_at[ends] = -1
+                open_at[starts] = r0 + i
+        for k in np.nonzero(open_at >= 0)[0].tolist():
+            col_runs[k].append((int(open_at[k]), n))
+        for k in range(n):
+            kiv[a + k] = _two_runs(col_runs[k], a)
+    return qiv, kiv
 
 
 # ----------------------------------------------------------------------------

@@ -93,6 +93,36 @@ def test_position_set_invariant(rows, extra):
             assert (lay["conv"][b][ks] == lay["conv"][b][q]).all()
 
 
+def _check_schedule(M, s, L, bq, bk):
+    """Tile and 32x32 sub-block classes and lists of schedule s against direct
+    pair counting in the dense mask M (rows queries, columns keys)."""
+    MT, NT = -(-L // bq), -(-L // bk)
+    for m in range(MT):
+        lst = []
+        for n in range(NT):
+            cnt = int(M[m * bq:(m + 1) * bq, n * bk:(n + 1) * bk].sum())
+            want = 0 if cnt == 0 else (2 if cnt == bq * bk else 1)
+            assert s["tile_class"][m, n] == want
+            if cnt:
+                lst.append(n)
+            if bq % 32 == 0 and bk % 32 == 0:
+                word = int(s["sub_class"][m, n])
+                for i in range(bq // 32):
+                    for j in range(bk // 32):
+                        q0, k0 = m * bq + 32 * i, n * bk + 32 * j
+                        c = int(M[q0:q0 + 32, k0:k0 + 32].sum())
+                        w = 0 if c == 0 else (2 if c == 1024 else 1)
+                        assert (word >> (2 * (i * (bk // 32) + j))) & 3 == w
+        assert s["q_nnz"][m] == len(lst)
+        assert list(s["q_list"][m, :len(lst)]) == lst
+        assert (s["q_list"][m, len(lst):] == -1).all()
+    for n in range(NT):
+        lst = [m for m in range(MT) if s["tile_class"][m, n] != 0]
+        assert s["k_nnz"][n] == len(lst)
+        assert list(s["k_list"][n, :len(lst)]) == lst
+        assert (s["k_list"][n, len(lst):] == -1).all()
+
+
 @settings(max_examples=100, deadline=None)
 @given(rows=st.lists(row_st, min_size=1, max_size=2), extra=st.integers(0, 40),
        bq=st.sampled_from([16, 32, 64]), bk=st.sampled_from([16, 32, 64]))
@@ -101,39 +131,88 @@ def test_schedule_brute_force(rows, extra, bq, bk):
     L = _L_for(rows, extra)
     lay = O.layout(rows, L)
     for b in range(len(rows)):
-        M = O.dense_mask(lay, b)
-        s = O.schedule(lay, b, bq, bk)
-        MT, NT = -(-L // bq), -(-L // bk)
-        for m in range(MT):
-            lst = []
-            for n in range(NT):
-                cnt = 0
-                for q in range(m * bq, (m + 1) * bq):
-                    for k in range(n * bk, (n + 1) * bk):
-                        if q < L and k < L and M[q, k]:
-                            cnt += 1
-                want = 0 if cnt == 0 else (2 if cnt == bq * bk else 1)
-                assert s["tile_class"][m, n] == want
-                if cnt:
-                    lst.append(n)
-                if bq % 32 == 0 and bk % 32 == 0:
-                    word = int(s["sub_class"][m, n])
-                    for i in range(bq // 32):
-                        for j in range(bk // 32):
-                            c = 0
-                            for q in range(m * bq + 32 * i, m * bq + 32 * i + 32):
-                                for k in range(n * bk + 32 * j, n * bk + 32 * j + 32):
-                                    if q < L and k < L and M[q, k]:
-                                        c += 1
-                            w = 0 if c == 0 else (2 if c == 1024 else 1)
-                            assert (word >> (2 * (i * (bk // 32) + j))) & 3 == w
-            assert s["q_nnz"][m] == len(lst)
-            assert list(s["q_list"][m, :len(lst)]) == lst
-            assert (s["q_list"][m, len(lst):] == -1).all()
-        for n in range(NT):
-            lst = [m for m in range(MT) if s["tile_class"][m, n] != 0]
-            assert s["k_nnz"][n] == len(lst)
-            assert list(s["k_list"][n, :len(lst)]) == lst
+        _check_schedule(O.dense_mask(lay, b), O.schedule(lay, b, bq, bk), L, bq, bk)
+
+
+# ---------------------------------------------------------------------------
+# attention order (a reordering of this library; the mask itself is unchanged)
+# ---------------------------------------------------------------------------
+def _permuted_mask(lay, b):
+    """Dense mask of row b with queries and keys at their attention-order slots."""
+    M = O.dense_mask(lay, b)
+    slot = O.attention_order(lay, b)
+    P = np.zeros_like(M)
+    P[np.ix_(slot, slot)] = M
+    return P
+
+
+def test_tiny_golden_attention_order():
+    g = _golden()
+    lay = O.layout(I.tiny_rows(), 64)
+    np.testing.assert_array_equal(O.attention_order(lay, 0), _ints(g["slot"]))
+    s = O.schedule(lay, 0, 32, 32, order="attention")
+    np.testing.assert_array_equal(s["counts"].ravel(), _ints(g["slot_tile32_counts"]))
+    np.testing.assert_array_equal(s["tile_class"].ravel(), _ints(g["slot_tile32_class"]))
+
+
+@settings(max_examples=150, deadline=None)
+@given(rows=st.lists(row_st, min_size=1, max_size=2), extra=st.integers(0, 9))
+def test_attention_order_closed_form(rows, extra):
+    """A permutation inside each conversation: h and r_in tokens sit at
+    conversation start + position id (their positions run 0, 1, ... without
+    gaps), t and r_out follow in packed order, PAD keeps its index."""
+    L = _L_for(rows, extra)
+    lay = O.layout(rows, L)
+    for b in range(len(rows)):
+        slot = O.attention_order(lay, b)
+        assert sorted(slot.tolist()) == list(range(L))
+        typ, pos = lay["type"][b], lay["pos"][b]
+        for c in range(O.n_convs(lay, b)):
+            a, e = O.conv_range(lay, b, c)
+            ty = typ[a:e]
+            hist = np.nonzero((ty == O.H) | (ty == O.RIN))[0] + a
+            rest = np.nonzero((ty == O.T) | (ty == O.ROUT))[0] + a
+            np.testing.assert_array_equal(slot[hist], a + pos[hist])
+            np.testing.assert_array_equal(slot[rest], a + len(hist) + np.arange(len(rest)))
+        pad = np.nonzero(typ == O.PAD)[0]
+        np.testing.assert_array_equal(slot[pad], pad)
+
+
+@settings(max_examples=150, deadline=None)
+@given(rows=st.lists(row_st, min_size=1, max_size=2), extra=st.integers(0, 9))
+def test_slot_intervals_reproduce_mask(rows, extra):
+    """In attention order every query row and every key column of the mask is
+    at most two runs (no ValueError), the runs rebuild the mask exactly, and
+    no query sees a key at a later slot."""
+    L = _L_for(rows, extra)
+    lay = O.layout(rows, L)
+    for b in range(len(rows)):
+        P = _permuted_mask(lay, b)
+        qiv, kiv = O.slot_intervals(lay, b, row_chunk=5)
+        R = np.zeros_like(P)
+        C = np.zeros_like(P)
+        for s_ in range(L):
+            x0, x1, x2, x3 = qiv[s_]
+            assert x0 <= x1 <= x2 <= x3
+            R[s_, x0:x1] = True
+            R[s_, x2:x3] = True
+            y0, y1, y2, y3 = kiv[s_]
+            assert y0 <= y1 <= y2 <= y3
+            C[y0:y1, s_] = True
+            C[y2:y3, s_] = True
+        np.testing.assert_array_equal(R, P)
+        np.testing.assert_array_equal(C, P)
+        assert not np.triu(P, 1).any()
+
+
+@settings(max_examples=80, deadline=None)
+@given(rows=st.lists(row_st, min_size=1, max_size=2), extra=st.integers(0, 40),
+       bq=st.sampled_from([16, 32, 64]), bk=st.sampled_from([16, 32, 64]))
+def test_schedule_brute_force_attention_order(rows, extra, bq, bk):
+    L = _L_for(rows, extra)
+    lay = O.layout(rows, L)
+    for b in range(len(rows)):
+        _check_schedule(_permuted_mask(lay, b), O.schedule(lay, b, bq, bk, order="attention"), L, bq, bk)
 
 
 def test_single_turn_is_textbook_causal():
