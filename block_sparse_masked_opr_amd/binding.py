@@ -21,6 +21,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libopr.so"
 OPR_OK, OPR_E_INVALID, OPR_E_CAPACITY, OPR_E_UNSUPPORTED, OPR_E_HIP = 0, -1, -2, -3, -4
 OPR_ATTN_BLOCK = 128
 OPR_SUB_BLOCK = 32
+OPR_ORDER_PACKED, OPR_ORDER_ATTENTION = 0, 1
 
 
 class OprError(RuntimeError):
@@ -36,8 +37,9 @@ class OprTurn(ctypes.Structure):
 
 class OprLayout(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in (
-        "tok_conv", "tok_turn", "tok_pos", "tok_type", "tile_class", "sub_class",
-        "q_nnz", "q_list", "k_nnz", "k_list")]
+        "tok_conv", "tok_turn", "tok_pos", "tok_type", "tok_slot", "slot_tok", "slot_qiv",
+        "slot_kiv", "tile_class", "sub_class", "q_nnz", "q_list", "k_nnz", "k_list")] + [
+        ("order", ctypes.c_int32)]
 
 
 class OprAttnIn(ctypes.Structure):
@@ -102,17 +104,21 @@ def opr_attn_workspace_size(B: int, L: int, Hq: int, Hkv: int, D: int, is_bwd: b
 class Layout:
     """Device tensors filled by opr_build_layout (int32 unless noted)."""
 
-    FIELDS = ("tok_conv", "tok_turn", "tok_pos", "tok_type", "tile_class", "sub_class",
-              "q_nnz", "q_list", "k_nnz", "k_list")
+    FIELDS = ("tok_conv", "tok_turn", "tok_pos", "tok_type", "tok_slot", "slot_tok", "slot_qiv",
+              "slot_kiv", "tile_class", "sub_class", "q_nnz", "q_list", "k_nnz", "k_list")
 
-    def __init__(self, B: int, L: int, block_q: int, block_k: int, device):
-        self.B, self.L, self.block_q, self.block_k = B, L, block_q, block_k
+    def __init__(self, B: int, L: int, block_q: int, block_k: int, device, order: int = OPR_ORDER_ATTENTION):
+        self.B, self.L, self.block_q, self.block_k, self.order = B, L, block_q, block_k, order
         self.MT, self.NT = -(-L // block_q), -(-L // block_k)
         e = dict(device=device)
         self.tok_conv = torch.empty((B, L), dtype=torch.int32, **e)
         self.tok_turn = torch.empty((B, L), dtype=torch.int32, **e)
         self.tok_pos = torch.empty((B, L), dtype=torch.int32, **e)
         self.tok_type = torch.empty((B, L), dtype=torch.uint8, **e)
+        self.tok_slot = torch.empty((B, L), dtype=torch.int32, **e)
+        self.slot_tok = torch.empty((B, L), dtype=torch.int32, **e)
+        self.slot_qiv = torch.empty((B, L, 4), dtype=torch.int32, **e)
+        self.slot_kiv = torch.empty((B, L, 4), dtype=torch.int32, **e)
         self.tile_class = torch.empty((B, self.MT, self.NT), dtype=torch.uint8, **e)
         # uint32 bit words, held as int32 (same bits)
         self.sub_class = torch.empty((B, self.MT, self.NT), dtype=torch.int32, **e)
@@ -122,7 +128,7 @@ class Layout:
         self.k_list = torch.empty((B, self.NT, self.MT), dtype=torch.int32, **e)
 
     def c_struct(self) -> OprLayout:
-        return OprLayout(*[getattr(self, f).data_ptr() for f in self.FIELDS])
+        return OprLayout(*[getattr(self, f).data_ptr() for f in self.FIELDS], self.order)
 
     def numpy(self) -> Dict[str, np.ndarray]:
         out = {f: getattr(self, f).cpu().numpy() for f in self.FIELDS}
@@ -132,17 +138,20 @@ class Layout:
 
 def opr_build_layout(rows: Sequence, L: int, block_q: int = OPR_ATTN_BLOCK,
                      block_k: int = OPR_ATTN_BLOCK, device="cuda",
-                     workspace: Optional[torch.Tensor] = None, out: Optional[Layout] = None) -> Layout:
+                     workspace: Optional[torch.Tensor] = None, out: Optional[Layout] = None,
+                     order: int = OPR_ORDER_ATTENTION) -> Layout:
     """rows: list of rows, each a list of conversations of (h, t, r_in, r_out)
-    turns.  ``out``: a Layout of the same (B, L, block_q, block_k) to refill."""
+    turns.  ``out``: a Layout of the same (B, L, block_q, block_k, order) to
+    refill.  ``order``: OPR_ORDER_ATTENTION (what the attention calls need) or
+    OPR_ORDER_PACKED (the tile schedule over the packed rows)."""
     device = torch.device(device)
     B = len(rows)
     cpr, tpc, turns = inputs.flatten_rows(rows)
     C, T = len(tpc), len(turns)
-    if out is not None and (out.B, out.L, out.block_q, out.block_k) == (B, L, block_q, block_k):
+    if out is not None and (out.B, out.L, out.block_q, out.block_k, out.order) == (B, L, block_q, block_k, order):
         lay = out
     else:
-        lay = Layout(B, L, block_q, block_k, device)
+        lay = Layout(B, L, block_q, block_k, device, order)
     need = opr_build_layout_workspace_size(B, L, C, T)
     if need == 0:
         raise OprError(OPR_E_INVALID, "opr_build_layout_workspace_size")

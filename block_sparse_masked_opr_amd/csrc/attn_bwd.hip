@@ -6,8 +6,10 @@
 //   dQ' = scale * dS K',  dK' = scale * sum over the group of dS^T Q'
 // and dQ, dK are rotated back by the transposed RoPE rotation.
 //
+// Both kernels run in attention order (tiles of slots; results are written
+// at the slot's token).
 // attn_dkdv_kernel: one workgroup per (128-key tile n, kv head, row); wave w
-//   owns keys n*128 + 32w .. +31, one key per lane column, K' and V of its
+//   owns key slots n*128 + 32w .. +31, one per lane column, K' and V of its
 //   key in registers.  Its stages are (q-tile of k_list, head of the group,
 //   64-query half) with a non-empty sub-block; each streams the Q' and dO rows
 //   of the stage into LDS (double buffered, buffer loads to LDS) and reads
@@ -19,7 +21,7 @@
 //   are recomputed per non-empty sub-block and dQ^T += K'^T dS^T.
 // Work items are remapped so each XCD walks a contiguous range (shared tiles
 // stay in that XCD's L2).  Partial sub-blocks are masked with 64-bit masks
-// built from the per-token intervals.
+// built from the two runs of slots of each query or key.
 //
 // Units: q' and dout carry one exponent per (row, kv group), k' and v one per
 // (row, kv head), all constant inside a workgroup.  dP = dO V^T comes out in
@@ -80,7 +82,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
       vb_[s] = ld_f16x8(p.vr + off + 16 * s + 8 * g);
     }
   }
-  const int4 iv = p.kiv[(int64_t)b * p.Lp + key];  // queries [key,x), [y,z), [z,w)
+  // query slots that see this key: [iv.x, iv.y) and [iv.z, iv.w)
+  const int4 iv = key < p.L ? p.kiv[(int64_t)b * p.L + key] : make_int4(0, 0, 0, 0);
   OperandOffsets<D> of;
   of.init(lane);
   TileCopy<D> tc;
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
       const char *Qt = buf, *dOt = buf + TB;
       const float *lse2s = reinterpret_cast<const float *>(buf + 2 * TB);
       const float *dscs = reinterpret_cast<const float *>(buf + 2 * TB + 256);
-      const uint64_t mq = (range_bits(key, iv.x, q0) | range_bits(iv.y, iv.z, q0) | range_bits(iv.z, iv.w, q0)) >> (8 * g);
+      const uint64_t mq = (range_bits(iv.x, iv.y, q0) | range_bits(iv.z, iv.w, q0)) >> (8 * g);
 
       // One straight-line body per case (both sub-blocks, masked or not; a
       // single sub-block), laid
@@ -267,7 +270,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
   }
 
   if (key < p.L) {
-    const int64_t out = (((int64_t)b * p.L + key) * p.Hkv + kvh) * D;
+    const int tok = p.slot_tok[(int64_t)b * p.L + key];
+    const int64_t out = (((int64_t)b * p.L + tok) * p.Hkv + kvh) * D;
     const float2 *cs = p.rope + ((int64_t)b * p.Lp + key) * (D / 2);
     // dK^T in units 2^(eq + edo + ev - kDsShift), dV^T in 2^(kPdvExp + edo)
     const float kscale = ldexpf(p.scale, kDsShift - eq - edo - ev);

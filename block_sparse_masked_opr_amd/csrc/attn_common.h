@@ -294,14 +294,16 @@ struct AttnParams {
   const uint8_t *tile_class;
   const uint32_t *sub_class;
   const int32_t *q_nnz, *q_list, *k_nnz, *k_list;
+  // Everything is indexed by slot (attention order) except the outputs,
+  // which are written at token slot_tok[s].
+  const int32_t *slot_tok;     // [B][L] token at each slot
+  const int4 *qiv;             // [B][L] key slots a query slot sees: [x, y) and [z, w)
+  const int4 *kiv;             // [B][L] query slots that see a key slot: [x, y) and [z, w)
   const float2 *rope;          // [B][Lp][D/2] (cos, sin)
   // fp16 bits, one power-of-two scale per (row, head) plane: [B][H][Lp][D]
   const uint16_t *qr, *kr, *vr, *dor;
   // plane maxima (float bits) [B][H] of q', k', v, dout
   const uint32_t *mq, *mk, *mv, *mdo;
-  const int4 *qiv;             // [B][Lp] per query: allowed keys [cs,ts) & {h,r_in}, [ts,e1), [s2,q]
-  const int4 *kiv;             // [B][Lp] per key: allowed queries [k,x), [y,z), [z,w)
-  const uint64_t *hvb;         // [B][Lp/64] bit i of block j: token 64j+i is h or r_in
   const float *dsc, *lse2;     // [B][Hq][Lp]: rowsum(dout*o) in the units of dP shifted by
                                // 2^-kDsShift; log2-domain lse (+inf where no key)
 };

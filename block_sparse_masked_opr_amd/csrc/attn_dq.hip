@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   constexpr int NDB = D / 32;
   constexpr int HALF_DB = NDB / 2;
   constexpr int TB = Tile<D>::BYTES, RB = Tile<D>::RB;
-  constexpr int BUF = 2 * TB + 64;  // K' tile, V tile, 64 history bits of the keys
+  constexpr int BUF = 2 * TB;  // K' tile, V tile
   // two separate LDS objects so the copy into one provably leaves the other alone
   __shared__ __attribute__((aligned(1024))) char buf0[BUF];
   __shared__ __attribute__((aligned(1024))) char buf1[BUF];
@@ -65,7 +65,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   }
   const float lse2_q = p.lse2[hq_row];
   const float dsc_q = p.dsc[hq_row];
-  const int4 iv = p.qiv[(int64_t)b * p.Lp + q];
+  // key slots this query sees: [iv.x, iv.y) and [iv.z, iv.w)
+  const int4 iv = q < p.L ? p.qiv[(int64_t)b * p.L + q] : make_int4(0, 0, 0, 0);
   OperandOffsets<D> of;
   of.init(lane);
   TileCopy<D> tc;
@@ -73,7 +74,6 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   const uint32_t plane_bytes = (uint32_t)p.Lp * D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.kr + kvplane * p.Lp * D, plane_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.vr + kvplane * p.Lp * D, plane_bytes);
-  const uint64_t *hvrow = p.hvb + (int64_t)b * (p.Lp / 64);
 
   f32x16 dqacc[NDB];
 #pragma unroll
@@ -87,7 +87,6 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   auto issue = [&](int k0, char *nb) {
     tc.issue(rk, k0, nb, w);
     tc.issue(rv, k0, nb + TB, w);
-    if (w == 0) words_load_async(hvrow + (k0 >> 6), nb + 2 * TB, lane, 2);
   };
 
   int tnext = 0;
@@ -117,10 +116,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
       const char *Kt = buf, *Vt = buf + TB;
 
       uint64_t mk = 0;
-      if (c0 == 1 || c1 == 1) {
-        const uint64_t hv = *reinterpret_cast<const uint64_t *>(buf + 2 * TB);
-        mk = ((range_bits(iv.x, iv.y, k0) & hv) | range_bits(iv.y, iv.z, k0) | range_bits(iv.w, q + 1, k0)) >> (8 * g);
-      }
+      if (c0 == 1 || c1 == 1) mk = (range_bits(iv.x, iv.y, k0) | range_bits(iv.z, iv.w, k0)) >> (8 * g);
       f16x8 dsb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -159,7 +155,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   }
 
   if (q < p.L) {
-    float *out = dq + (((int64_t)b * p.L + q) * p.Hq + h) * D;
+    const int tok = p.slot_tok[(int64_t)b * p.L + q];
+    float *out = dq + (((int64_t)b * p.L + tok) * p.Hq + h) * D;
     const float2 *cs = p.rope + ((int64_t)b * p.Lp + q) * (D / 2);
     // dQ^T in units 2^(ek + ev + edo - kDsShift)
     const float qscale = ldexpf(p.scale, kDsShift - ek - ev - edo);

@@ -1,7 +1,9 @@
 // Forward kernel of the one-pass masked attention (gfx950).
 //
-// One workgroup of 4 waves per (128-query tile m, q head h, row b); wave w
-// owns queries m*128 + 32w .. +31, one query per lane column.  Work items are
+// The kernel runs in attention order: q-tile m is query slots m*128 .. +127
+// and K/V rows are slots; results go to the slot's token.  One workgroup of
+// 4 waves per (128-slot query tile m, q head h, row b); wave w owns query
+// slots m*128 + 32w .. +31, one per lane column.  Work items are
 // remapped so each XCD walks a contiguous range of (row, kv head, q-tile,
 // head-in-group): the heads of one kv group and neighbouring q-tiles run side
 // by side and share K/V tiles in that XCD's L2.
@@ -14,7 +16,7 @@
 // fixed per-lane offsets); one barrier per stage.  Per stage each wave
 // computes S^T = K Q^T on its non-empty 32x32 sub-blocks with fp16 MFMA
 // (fp32 accumulate); partial sub-blocks are masked with a 64-bit mask built
-// from the query's key intervals; the online softmax keeps a running maximum
+// from the query's two runs of key slots; the online softmax keeps a running maximum
 // that is only raised when a score exceeds it by more than kMaxSlack (so the
 // O accumulator is rarely rescaled); O^T += V^T P^T reads V^T from the
 // row-major V tile with transposing LDS reads.  The epilogue normalises,
@@ -31,7 +33,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
   constexpr int NS = D / 16;   // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;  // 32-wide blocks of the head dim
   constexpr int TB = Tile<D>::BYTES, RB = Tile<D>::RB;
-  constexpr int BUF = 2 * TB + 64;  // K tile, V tile, 64 history bits of the keys
+  constexpr int BUF = 2 * TB;  // K tile, V tile
   // Two separate LDS objects (not one array indexed by stage parity): the
   // compiler then knows that the asynchronous copy into one buffer does not
   // write the other, and lets it run under the reads of the current stage.
@@ -65,7 +67,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
 #pragma unroll
     for (int s = 0; s < NS; ++s) qb[s] = ld_f16x8(qrow + 16 * s + 8 * g);
   }
-  const int4 iv = p.qiv[(int64_t)b * p.Lp + q];  // [cs,ts) & hist, [ts,e1), [s2,q]
+  // key slots this query sees: [iv.x, iv.y) and [iv.z, iv.w)
+  const int4 iv = q < p.L ? p.qiv[(int64_t)b * p.L + q] : make_int4(0, 0, 0, 0);
   OperandOffsets<D> of;
   of.init(lane);
   TileCopy<D> tc;
@@ -73,7 +76,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
   const uint32_t plane_bytes = (uint32_t)p.Lp * D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.kr + kvplane * p.Lp * D, plane_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.vr + kvplane * p.Lp * D, plane_bytes);
-  const uint64_t *hvrow = p.hvb + (int64_t)b * (p.Lp / 64);
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -88,7 +90,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
   auto issue = [&](int k0, char *nb) {
     tc.issue(rk, k0, nb, w);
     tc.issue(rv, k0, nb + TB, w);
-    if (w == 0) words_load_async(hvrow + (k0 >> 6), nb + 2 * TB, lane, 2);
   };
 
   int tnext = 0;
@@ -128,8 +129,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
           s[kb] = mfma32x32x16(lds_f16x8(Kt + kb * 32 * RB + of.row8[st]), qb[st], s[kb]);
       }
       if (c0 == 1 || c1 == 1) {
-        const uint64_t hv = *reinterpret_cast<const uint64_t *>(buf + 2 * TB);
-        uint64_t mk = (range_bits(iv.x, iv.y, k0) & hv) | range_bits(iv.y, iv.z, k0) | range_bits(iv.w, q + 1, k0);
+        uint64_t mk = range_bits(iv.x, iv.y, k0) | range_bits(iv.z, iv.w, k0);
         mk >>= 8 * g;  // lane group g holds keys 16h + 8g + 0..7 of each 32-key block
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -184,9 +184,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
 
   const float lsum = lrow + __shfl_xor(lrow, 32);
   if (q < p.L) {
+    const int tok = p.slot_tok[(int64_t)b * p.L + q];
     // O = acc / sum, acc in units 2^ev (v) times 2^kPExp (shared with sum)
     const float inv = lsum > 0.0f ? ldexpf(1.0f / lsum, -ev) : 0.0f;
-    uint16_t *orow = o + (((int64_t)b * p.L + q) * p.Hq + h) * D;
+    uint16_t *orow = o + (((int64_t)b * p.L + tok) * p.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
       }
     }
     if (g == 0)
-      lse[((int64_t)b * p.Hq + h) * p.L + q] =
+      lse[((int64_t)b * p.Hq + h) * p.L + tok] =
           lsum > 0.0f ? (mrow + log2f(lsum) - (float)kPExp) * kLn2 : -INFINITY;
   }
 }

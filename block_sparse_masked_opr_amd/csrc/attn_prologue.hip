@@ -1,11 +1,11 @@
-// Prologue kernels of the attention path:
-//  - the RoPE table at the strategic position ids (and zeroing of the plane
-//    maxima),
+// Prologue kernels of the attention path.  Everything here is indexed by
+// slot (attention order): slot s < L holds token slot_tok[s] of the layout,
+// slots L .. Lp-1 are empty and padded with zeros.
+//  - the RoPE table at the slots' strategic position ids (and zeroing of the
+//    plane maxima),
 //  - the largest magnitude of every (row, head) plane of q, k, v, dout,
-//  - head-major fp16 copies of q, k (after RoPE), v and dout with one
-//    power-of-two scale per plane, padded with zeros to a whole number of
-//    128-token tiles,
-//  - per-token mask intervals (below) and per-64-token "history" bits,
+//  - head-major fp16 copies of q, k (after RoPE), v and dout in slot order,
+//    with one power-of-two scale per plane,
 //  - the backward preprocessing delta = rowsum(dout * o), scaled, with the
 //    dout plane maxima.
 //
@@ -13,31 +13,18 @@
 // pos * theta^(-2j/D).  The angle and its cosine and sine are computed in
 // float64 (positions reach ~2.4e5, where a float32 angle would be off by
 // ~1e-2 rad); the rotation itself runs in float32.
-//
-// Mask intervals.  Segments are stored h, t, r_in, r_out inside a turn and
-// conversations are contiguous, so what a token may see (or be seen by) is a
-// union of intervals of the packed row.  With cs / ce the start / end of the
-// token's conversation, ts / te of its turn and tT, tR, tO the starts of the
-// turn's t, r_in and r_out segments:
-//   query q of type h or t  : keys [cs, ts) that are h or r_in, and [ts, q]
-//   query q of type r_in    : ... and [ts, tT) (h_i) and [tR, q]
-//   query q of type r_out   : ... and [ts, tR) (h_i, t_i) and [tO, q]
-//   key k of type h         : queries [k, te) and [te, ce)
-//   key k of type t         : queries [k, tR) and [tO, te)   (not r_in_i)
-//   key k of type r_in      : queries [k, tO) and [te, ce)   (not r_out_i)
-//   key k of type r_out     : queries [k, te)
-// (Derived from the four visibility rules; PAD tokens get empty intervals.)
 #include "attn_common.h"
 #include "opr_internal.h"
 
 namespace opr {
 namespace {
 
-// table[b][t][j] = (cos, sin) of pos(b, t) * theta^(-2j/D); PAD and t >= L
-// use position 0.  The first n_zero threads also clear zero_words.
+// table[b][s][j] = (cos, sin) of pos(b, slot_tok[s]) * theta^(-2j/D); PAD
+// and s >= L use position 0.  The first n_zero threads also clear zero_words.
 __global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, int32_t Lp, int32_t half,
                                                          double log2_theta, const int32_t *tok_pos,
-                                                         float2 *table, uint32_t *zero_words, int32_t n_zero) {
+                                                         const int32_t *slot_tok, float2 *table,
+                                                         uint32_t *zero_words, int32_t n_zero) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid < n_zero) zero_words[gid] = 0u;
   const int64_t total = (int64_t)B * Lp * half;
@@ -46,7 +33,7 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, i
   const int64_t bt = gid / half;
   const int32_t t = (int32_t)(bt % Lp);
   const int32_t b = (int32_t)(bt / Lp);
-  const int32_t pos = t < L ? tok_pos[(int64_t)b * L + t] : 0;
+  const int32_t pos = t < L ? tok_pos[(int64_t)b * L + slot_tok[(int64_t)b * L + t]] : 0;
   const double inv_freq = exp2(-(2.0 * j / (2.0 * half)) * log2_theta);
   double s, c;
   sincos((double)pos * inv_freq, &s, &c);
@@ -85,14 +72,15 @@ __global__ __launch_bounds__(256) void absmax_kernel(int32_t L, int32_t H, const
   if (j == 0 && h < H && m > 0.0f) atomicMax(pmax + (int64_t)b * H + h, __float_as_uint(m * factor));
 }
 
-// One workgroup per (64-token block, head, row).  x: [B][L][H][D] bf16 ->
-// rows [B][H][Lp][D] as fp16(x' * 2^e), x' = RoPE(x) or x, e the exponent of
-// the largest plane maximum of the head's group of `group` heads.  Tokens
-// t >= L are zero.
+// One workgroup per (64-slot block, head, row).  x: [B][L][H][D] bf16 ->
+// rows [B][H][Lp][D] in slot order, fp16(x' * 2^e), x' = RoPE(x) or x, e the
+// exponent of the largest plane maximum of the head's group of `group`
+// heads.  Slots s >= L are zero.
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H, int32_t group,
-                                                   const uint16_t *x, const float2 *table,
-                                                   const uint32_t *pmax, uint16_t *rows) {
+                                                   const uint16_t *x, const int32_t *slot_tok,
+                                                   const float2 *table, const uint32_t *pmax,
+                                                   uint16_t *rows) {
   constexpr int HALF = D / 2;
   constexpr int PER = HALF / 4;  // pairs per thread (4 threads per token)
   const int t0 = blockIdx.x * 64;
@@ -104,7 +92,8 @@ __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_
   const int ex = group_exponent(pmax + (int64_t)b * H + (h / group) * group, group);
   uint16_t lq[PER], hq[PER];
   if (t < L) {
-    const uint16_t *src = x + (((int64_t)b * L + t) * H + h) * D;
+    const int32_t tok = slot_tok[(int64_t)b * L + t];
+    const uint16_t *src = x + (((int64_t)b * L + tok) * H + h) * D;
     uint16_t lb[PER], hb[PER];
 #pragma unroll
     for (int c = 0; c < PER; c += 8) {
@@ -136,72 +125,13 @@ __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_
   }
 }
 
-// Sort key of a token along its row: (conv, turn, type) in lexicographic
-// order, which is non-decreasing along the packed conversations; PAD last.
-__device__ __forceinline__ uint64_t tok_key(const int32_t *conv, const int32_t *turn, const uint8_t *type,
-                                            int64_t i) {
-  const int32_t c = conv[i];
-  if (c < 0) return ~0ull;
-  return ((uint64_t)(uint32_t)c << 34) | ((uint64_t)(uint32_t)turn[i] << 3) | (uint64_t)type[i];
-}
-
-// First index in [0, L) of row b whose key is >= k (L if none).
-__device__ __forceinline__ int32_t lower_bound_key(const int32_t *conv, const int32_t *turn,
-                                                   const uint8_t *type, int64_t row, int32_t L, uint64_t k) {
-  int32_t lo = 0, hi = L;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi) >> 1;
-    if (tok_key(conv, turn, type, row + mid) < k) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
-// qiv, kiv (may be null) for every token (t < Lp) and the history bits of each
-// 64-token block.
-__global__ __launch_bounds__(256) void intervals_kernel(int32_t B, int32_t L, int32_t Lp, const int32_t *conv,
-                                                        const int32_t *turn, const uint8_t *type, int4 *qiv,
-                                                        int4 *kiv, uint64_t *hvb) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool active = gid < (int64_t)B * Lp;
-  const int32_t t = active ? (int32_t)(gid % Lp) : 0;
-  const int64_t b = active ? gid / Lp : 0;
-  const int64_t row = b * L;
-  int4 qi = make_int4(t + 1, t + 1, t + 1, t + 1);
-  int4 ki = make_int4(t, t, t, t);
-  bool hv = false;
-  if (active && t < L && conv[row + t] >= 0) {
-    const uint64_t c = (uint32_t)conv[row + t], i = (uint32_t)turn[row + t];
-    const int y = type[row + t];
-    const uint64_t turn_key = (c << 34) | (i << 3);
-    const int32_t cs = lower_bound_key(conv, turn, type, row, L, c << 34);
-    const int32_t ce = lower_bound_key(conv, turn, type, row, L, (c + 1) << 34);
-    const int32_t ts = lower_bound_key(conv, turn, type, row, L, turn_key);
-    const int32_t te = lower_bound_key(conv, turn, type, row, L, turn_key + 8);
-    const int32_t tT = lower_bound_key(conv, turn, type, row, L, turn_key | OPR_TOK_T);
-    const int32_t tR = lower_bound_key(conv, turn, type, row, L, turn_key | OPR_TOK_RIN);
-    const int32_t tO = lower_bound_key(conv, turn, type, row, L, turn_key | OPR_TOK_ROUT);
-    hv = (y == OPR_TOK_H) || (y == OPR_TOK_RIN);
-    switch (y) {
-      case OPR_TOK_H: qi = make_int4(cs, ts, t + 1, t + 1); ki = make_int4(te, te, te, ce); break;
-      case OPR_TOK_T: qi = make_int4(cs, ts, t + 1, t + 1); ki = make_int4(tR, tO, te, te); break;
-      case OPR_TOK_RIN: qi = make_int4(cs, ts, tT, tR); ki = make_int4(tO, te, te, ce); break;
-      default: qi = make_int4(cs, ts, tR, tO); ki = make_int4(te, te, te, te); break;
-    }
-  }
-  if (active) {
-    qiv[gid] = qi;
-    if (kiv) kiv[gid] = ki;  // only the backward pass needs the key intervals
-  }
-  const uint64_t bits = __ballot(hv);
-  if (active && (threadIdx.x & 63) == 0) hvb[gid >> 6] = bits;  // Lp is a multiple of 64
-}
-
-// Backward preprocessing, before dout is packed: per token and q head
-//   dsc[b][h][t]  = sum_d dout * o (float32 over bf16 inputs),
-//   lse2[b][h][t] = lse * log2(e), +inf where the row has no key (lse = -inf)
-//                   or t >= L, so that recomputed probabilities are exactly 0;
+// Backward preprocessing, before dout is packed: per slot s and q head, with
+// t = slot_tok[s] the token there,
+//   dsc[b][h][s]  = sum_d dout * o of token t (float32 over bf16 inputs),
+//   lse2[b][h][s] = lse * log2(e), +inf where the row has no key (lse = -inf)
+//                   or s >= L, so that recomputed probabilities are exactly 0;
 // and the largest |dout| of each (row, head) plane into mdo (float bits).
-// One wave per token: D/8 lanes read one head's 16-byte chunks, so a wave
+// One wave per slot: D/8 lanes read one head's 16-byte chunks, so a wave
 // covers 64/(D/8) heads per step with fully coalesced row reads; the plane
 // maxima are combined in LDS, then once per workgroup in memory.
 constexpr int kMaxHeads = 1024;
@@ -209,7 +139,8 @@ constexpr int kMaxHeads = 1024;
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_t Lp, int32_t Hq,
                                                     const uint16_t *o, const uint16_t *dout, const float *lse,
-                                                    uint32_t *mdo, float *dsc, float *lse2) {
+                                                    const int32_t *slot_tok, uint32_t *mdo, float *dsc,
+                                                    float *lse2) {
   constexpr int LPH = D / 8;        // lanes per head
   constexpr int HPS = 64 / LPH;     // heads per step
   constexpr int TPW = 4;            // tokens per wave
@@ -222,9 +153,10 @@ __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_
   for (int k = 0; k < TPW; ++k) {
     const int64_t bt = bt0 + k;
     if (bt >= (int64_t)B * Lp) break;
-    const int32_t t = (int32_t)(bt % Lp);
+    const int32_t sl = (int32_t)(bt % Lp);
     const int32_t b = (int32_t)(bt / Lp);
     if (b != (int32_t)(bt0 / Lp)) break;  // a workgroup's plane maxima stay within one row
+    const int32_t t = sl < L ? slot_tok[(int64_t)b * L + sl] : L;  // token at the slot
     for (int h0 = 0; h0 < Hq; h0 += HPS) {
       const int h = h0 + hl;
       float acc = 0.0f, mx = 0.0f;
@@ -251,7 +183,7 @@ __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_
           const float l = lse[((int64_t)b * Hq + h) * L + t];
           l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
         }
-        const int64_t out = ((int64_t)b * Hq + h) * Lp + t;
+        const int64_t out = ((int64_t)b * Hq + h) * Lp + sl;
         dsc[out] = acc;
         lse2[out] = l2;
         if (mx > 0.0f) atomicMax(&hmax[h], __float_as_uint(mx));
@@ -294,11 +226,12 @@ void launch_absmax_d(int32_t B, int32_t L, int32_t H, const void *x, float facto
 
 template <int D>
 void launch_pack_d(bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group, const void *x,
-                   const float2 *table, const uint32_t *pmax, uint16_t *rows, hipStream_t s) {
+                   const int32_t *slot_tok, const float2 *table, const uint32_t *pmax, uint16_t *rows,
+                   hipStream_t s) {
   const dim3 grid(Lp / 64, H, B);
   const uint16_t *src = static_cast<const uint16_t *>(x);
-  if (rope) pack_kernel<D, true><<<grid, 256, 0, s>>>(L, Lp, H, group, src, table, pmax, rows);
-  else pack_kernel<D, false><<<grid, 256, 0, s>>>(L, Lp, H, group, src, table, pmax, rows);
+  if (rope) pack_kernel<D, true><<<grid, 256, 0, s>>>(L, Lp, H, group, src, slot_tok, table, pmax, rows);
+  else pack_kernel<D, false><<<grid, 256, 0, s>>>(L, Lp, H, group, src, slot_tok, table, pmax, rows);
 }
 
 }  // namespace
@@ -309,7 +242,8 @@ void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int64_t total = (int64_t)in.B * ws.Lp * half;
   const int64_t blocks = ((total > ws.n_pmax ? total : (int64_t)ws.n_pmax) + 255) / 256;
   rope_table_kernel<<<(unsigned)blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, half, log2(in.rope_theta),
-                                                     in.layout.tok_pos, ws.rope, ws.pmax, ws.n_pmax);
+                                                     in.layout.tok_pos, in.layout.slot_tok, ws.rope, ws.pmax,
+                                                     ws.n_pmax);
 }
 
 void launch_absmax(int D, int32_t B, int32_t L, int32_t H, const void *x, bool rope, uint32_t *pmax,
@@ -320,15 +254,10 @@ void launch_absmax(int D, int32_t B, int32_t L, int32_t H, const void *x, bool r
 }
 
 void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,
-                     const void *x, const float2 *table, const uint32_t *pmax, uint16_t *rows, hipStream_t s) {
-  if (D == 64) launch_pack_d<64>(rope, B, L, Lp, H, group, x, table, pmax, rows, s);
-  else launch_pack_d<128>(rope, B, L, Lp, H, group, x, table, pmax, rows, s);
-}
-
-void launch_intervals(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
-  const int64_t total = (int64_t)in.B * ws.Lp;
-  intervals_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
-      in.B, in.L, ws.Lp, in.layout.tok_conv, in.layout.tok_turn, in.layout.tok_type, ws.qiv, ws.kiv, ws.hvb);
+                     const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
+                     uint16_t *rows, hipStream_t s) {
+  if (D == 64) launch_pack_d<64>(rope, B, L, Lp, H, group, x, slot_tok, table, pmax, rows, s);
+  else launch_pack_d<128>(rope, B, L, Lp, H, group, x, slot_tok, table, pmax, rows, s);
 }
 
 // delta, lse2 and the dout plane maxima (mdo is cleared first), then dout
@@ -342,9 +271,11 @@ void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const 
   const uint16_t *o16 = static_cast<const uint16_t *>(o);
   const uint16_t *d16 = static_cast<const uint16_t *>(dout);
   if (in.D == 64)
-    delta_kernel<64><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, ws.mdo, ws.dsc, ws.lse2);
+    delta_kernel<64><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, in.layout.slot_tok,
+                                            ws.mdo, ws.dsc, ws.lse2);
   else
-    delta_kernel<128><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, ws.mdo, ws.dsc, ws.lse2);
+    delta_kernel<128><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, in.layout.slot_tok,
+                                             ws.mdo, ws.dsc, ws.lse2);
 }
 
 void launch_scale_delta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {

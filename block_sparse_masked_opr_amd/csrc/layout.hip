@@ -7,10 +7,13 @@
 //   layout_prep      one workgroup: prefix sums over rows, conversations and
 //                    turns (token starts, position starts, history counts)
 //   layout_fill      one thread per token: binary search for its turn, then
-//                    conversation, turn, type and position id
+//                    conversation, turn, type, position id, attention-order
+//                    slot and the two runs of slots of its query and key
 //   layout_classify  one workgroup per tile, one thread per query row: counts
 //                    the allowed keys of each 32-key sub-block with interval
 //                    arithmetic, then sums per 32x32 sub-block and per tile
+//                    (layout_classify_attention: the same over attention
+//                    order, from the query's two runs of slots)
 //   layout_compact_q/k  one wave per tile row / column: ballot compaction of
 //                    the non-empty tiles into ascending lists
 //
@@ -87,7 +90,31 @@ __global__ __launch_bounds__(kPrepThreads) void layout_prep(int32_t B, int32_t C
   for (int b = threadIdx.x; b <= B; b += kPrepThreads) ws.row_turn0[b] = ws.conv_turn0[ws.row_conv0[b]];
 }
 
-// Per-token fields of token x (row-local index) in row b.
+// Two runs [x0, x1) and [x2, x3) in the canonical form of the layout: the
+// runs are disjoint and ascending (x1 <= x2); an empty first run is dropped,
+// touching runs are merged and a missing run is written [x, x) with x the end
+// of the run before it (0 if none).
+__device__ inline int4 two_runs(int32_t x0, int32_t x1, int32_t x2, int32_t x3) {
+  if (x0 >= x1) { x0 = x2; x1 = x3; x2 = x3; }  // first run empty
+  if (x0 >= x1) return make_int4(0, 0, 0, 0);
+  if (x2 >= x3) return make_int4(x0, x1, x1, x1);
+  if (x1 == x2) return make_int4(x0, x3, x3, x3);
+  return make_int4(x0, x1, x2, x3);
+}
+
+// Per-token fields of token x (row-local index) in row b, its attention-order
+// slot and the mask of that slot as runs of slots.
+//
+// Attention order of a conversation at [a, e): the h and r_in tokens first -
+// their position ids run 0 .. N1-1 without gaps, so a token of them sits at
+// slot a + pos - then the t and r_out tokens, turn by turn: turn i's t_i and
+// r_out_i occupy [p2(i), p2(i+1)) with p2(i) = a + N1 + (t and r_out tokens of
+// the turns before i).  In slot order the rules become:
+//   query h_i / r_in_i : keys [a, s]
+//   query t_i / r_out_i: keys [a, a + s_t(i)) (H_<i and h_i) and [p2(i), s]
+//   key h_j    : queries [s, a + N1) and [p2(j), e)      (later turns' t, r_out)
+//   key r_in_j : queries [s, a + N1) and [p2(j+1), e)
+//   key t_j / r_out_j: queries [s, p2(j+1))
 __global__ __launch_bounds__(256) void layout_fill(int32_t B, int32_t L, LayoutWs ws,
                                                    opr_layout out) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -96,12 +123,13 @@ __global__ __launch_bounds__(256) void layout_fill(int32_t B, int32_t L, LayoutW
   const int32_t x = (int32_t)(gid - (int64_t)b * L);
   const int32_t t0 = ws.row_turn0[b], t1 = ws.row_turn0[b + 1];
   const int32_t r0 = ws.tok_g[t0];
-  int32_t conv = -1, turn = -1, pos = 0, gt = -1;
+  int32_t conv = -1, turn = -1, pos = 0, gt = -1, slot = x;
+  int4 qiv = make_int4(0, 0, 0, 0), kiv = make_int4(0, 0, 0, 0);
   uint8_t type = OPR_TOK_PAD;
   if (x < ws.tok_g[t1] - r0) {
     gt = last_le(ws.tok_g, t0, t1, r0 + x);
     const int32_t c = ws.turn_conv[gt];
-    const int32_t c0 = ws.conv_turn0[c];
+    const int32_t c0 = ws.conv_turn0[c], c1 = ws.conv_turn0[c + 1];
     conv = c - ws.row_conv0[b];
     turn = gt - c0;
     const int4 u = ws.turns[gt];
@@ -116,11 +144,30 @@ __global__ __launch_bounds__(256) void layout_fill(int32_t B, int32_t L, LayoutW
     } else {                                              // r_out_i: starts after t_i
       type = OPR_TOK_ROUT; pos = s_h + u.x + u.y + (o - u.x - u.y - u.z);
     }
+    // attention order
+    const int32_t a = ws.tok_g[c0] - r0, e = ws.tok_g[c1] - r0;
+    const int32_t n1 = ws.pos_g[c1] - ws.pos_g[c0];                       // h and r_in tokens
+    const int32_t p2 = a + n1 + (ws.tok_g[gt] - ws.tok_g[c0]) - (ws.pos_g[gt] - ws.pos_g[c0]);
+    const int32_t p2n = p2 + u.y + u.w;                                   // p2(i+1)
+    if (type == OPR_TOK_H || type == OPR_TOK_RIN) {
+      slot = a + pos;
+      qiv = two_runs(a, slot + 1, slot + 1, slot + 1);
+      kiv = two_runs(slot, a + n1, type == OPR_TOK_H ? p2 : p2n, e);
+    } else {
+      slot = type == OPR_TOK_T ? p2 + (o - u.x) : p2 + u.y + (o - u.x - u.y - u.z);
+      qiv = two_runs(a, a + s_h + u.x, p2, slot + 1);
+      kiv = two_runs(slot, p2n, p2n, p2n);
+    }
   }
   out.tok_conv[gid] = conv;
   out.tok_turn[gid] = turn;
   out.tok_pos[gid] = pos;
   out.tok_type[gid] = type;
+  out.tok_slot[gid] = slot;
+  const int64_t sg = (int64_t)b * L + slot;
+  out.slot_tok[sg] = x;
+  reinterpret_cast<int4 *>(out.slot_qiv)[sg] = qiv;
+  reinterpret_cast<int4 *>(out.slot_kiv)[sg] = kiv;
   ws.gturn[gid] = gt;
 }
 
@@ -218,6 +265,50 @@ __global__ __launch_bounds__(BQ) void layout_classify(int32_t B, int32_t L, int3
   }
 }
 
+// Tile classes over attention order: one workgroup of BQ threads per tile,
+// thread r is query slot m*BQ + r, whose allowed keys are its two runs of
+// slots; tiles after the diagonal are empty (no query sees a later slot).
+template <int BQ, int BK>
+__global__ __launch_bounds__(BQ) void layout_classify_attention(int32_t B, int32_t L, int32_t MT,
+                                                                int32_t NT, opr_layout out) {
+  constexpr int SQ = BQ / OPR_SUB_BLOCK, SK = BK / OPR_SUB_BLOCK;
+  __shared__ int32_t cnt[SQ * SK];
+  const int64_t tile = blockIdx.x;
+  const int32_t n = (int32_t)(tile % NT);
+  const int32_t m = (int32_t)((tile / NT) % MT);
+  const int32_t b = (int32_t)(tile / ((int64_t)NT * MT));
+  const int tid = threadIdx.x;
+  if (tid < SQ * SK) cnt[tid] = 0;
+  __syncthreads();
+  const int32_t q = m * BQ + tid;
+  const int32_t k_begin = n * BK;
+  if (k_begin <= m * BQ + BQ - 1 && q < L) {
+    const int4 iv = reinterpret_cast<const int4 *>(out.slot_qiv)[(int64_t)b * L + q];
+#pragma unroll
+    for (int j = 0; j < SK; ++j) {
+      const int32_t a = k_begin + j * OPR_SUB_BLOCK;
+      const int32_t e = min(a + OPR_SUB_BLOCK, L);
+      const int32_t c_ = overlap(a, e, iv.x, iv.y) + overlap(a, e, iv.z, iv.w);
+      if (c_) atomicAdd(&cnt[(tid / OPR_SUB_BLOCK) * SK + j], c_);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t word = 0;
+    int32_t total = 0;
+    for (int i = 0; i < SQ * SK; ++i) {
+      const int32_t v = cnt[i];
+      total += v;
+      const uint32_t cls = v == 0 ? OPR_TILE_EMPTY
+                         : (v == OPR_SUB_BLOCK * OPR_SUB_BLOCK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
+      word |= cls << (2 * i);
+    }
+    const uint8_t tcls = total == 0 ? OPR_TILE_EMPTY : (total == BQ * BK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
+    out.tile_class[tile] = tcls;
+    out.sub_class[tile] = word;
+  }
+}
+
 // One wave per (b, m): k-tile indices of the non-empty tiles of q-tile row m.
 __global__ __launch_bounds__(64) void layout_compact_q(int32_t MT, int32_t NT, opr_layout out) {
   const int64_t row = blockIdx.x;  // b * MT + m
@@ -261,7 +352,10 @@ __global__ __launch_bounds__(64) void layout_compact_k(int32_t MT, int32_t NT, o
 template <int BQ, int BK>
 void launch_classify(int64_t tiles, int32_t B, int32_t L, int32_t MT, int32_t NT,
                      const LayoutWs &ws, const opr_layout &out, hipStream_t s) {
-  layout_classify<BQ, BK><<<dim3((unsigned)tiles), dim3(BQ), 0, s>>>(B, L, MT, NT, ws, out);
+  if (out.order == OPR_ORDER_ATTENTION)
+    layout_classify_attention<BQ, BK><<<dim3((unsigned)tiles), dim3(BQ), 0, s>>>(B, L, MT, NT, out);
+  else
+    layout_classify<BQ, BK><<<dim3((unsigned)tiles), dim3(BQ), 0, s>>>(B, L, MT, NT, ws, out);
 }
 
 }  // namespace

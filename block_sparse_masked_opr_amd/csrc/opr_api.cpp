@@ -1,6 +1,7 @@
 // Host entry points of libopr: argument validation (before any HIP call),
 // workspace carving and kernel launch order.  See include/opr.h.
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "attn_common.h"
@@ -13,8 +14,8 @@ void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_absmax(int D, int32_t B, int32_t L, int32_t H, const void *x, bool rope, uint32_t *pmax,
                    hipStream_t s);
 void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,
-                     const void *x, const float2 *table, const uint32_t *pmax, uint16_t *rows, hipStream_t s);
-void launch_intervals(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
+                     const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
+                     uint16_t *rows, hipStream_t s);
 void launch_scale_delta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
                   const AttnWs &ws, hipStream_t s);
@@ -24,6 +25,9 @@ hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq
                                    float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev);
 
 static bool valid_block(int32_t b) { return b == 32 || b == 64 || b == 128; }
+
+// The runs of slots are read and written as 16-byte vectors.
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   Carver cv(p);
@@ -45,9 +49,6 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
     w.mv = w.mk + (size_t)in.B * in.Hkv;
     w.mdo = w.mv + (size_t)in.B * in.Hkv;
   }
-  w.qiv = cv.take<int4>((size_t)in.B * Lp);
-  w.kiv = cv.take<int4>((size_t)in.B * Lp);
-  w.hvb = cv.take<uint64_t>((size_t)in.B * (Lp / 64));
   // everything above is the forward state; the backward part follows
   if (is_bwd) {
     w.dor = cv.take<uint16_t>(qn);
@@ -84,9 +85,9 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->mk = ws.mk;
   p->mv = ws.mv;
   p->mdo = ws.mdo;
-  p->qiv = ws.qiv;
-  p->kiv = ws.kiv;
-  p->hvb = ws.hvb;
+  p->slot_tok = in.layout.slot_tok;
+  p->qiv = reinterpret_cast<const int4 *>(in.layout.slot_qiv);
+  p->kiv = reinterpret_cast<const int4 *>(in.layout.slot_kiv);
   p->dsc = ws.dsc;
   p->lse2 = ws.lse2;
 }
@@ -112,9 +113,11 @@ static opr_status check_attn_in(const opr_attn_in *in) {
   if (st != OPR_OK) return st;
   if (!in->q || !in->k || !in->v) return OPR_E_INVALID;
   const opr_layout &l = in->layout;
-  if (!l.tok_conv || !l.tok_turn || !l.tok_pos || !l.tok_type || !l.tile_class || !l.sub_class ||
+  if (!l.tok_pos || !l.slot_tok || !l.slot_qiv || !l.slot_kiv || !l.tile_class || !l.sub_class ||
       !l.q_nnz || !l.q_list || !l.k_nnz || !l.k_list)
     return OPR_E_INVALID;
+  if (l.order != OPR_ORDER_ATTENTION) return OPR_E_INVALID;
+  if (!aligned16(l.slot_qiv) || !aligned16(l.slot_kiv)) return OPR_E_INVALID;
   if (!(in->rope_theta > 0.0) || !isfinite(in->rope_theta)) return OPR_E_INVALID;
   if (!(in->softmax_scale >= 0.0f) || !isfinite(in->softmax_scale)) return OPR_E_INVALID;
   if (in->block_q != OPR_ATTN_BLOCK || in->block_k != OPR_ATTN_BLOCK) return OPR_E_UNSUPPORTED;
@@ -129,7 +132,7 @@ static void mark(const opr_attn_in *in, int i, hipStream_t s) {
   if (in->timing_events) hipEventRecord(in->timing_events[i], s);
 }
 
-// RoPE table, plane maxima and fp16 copies of q, k, v, mask intervals: the
+// RoPE table, plane maxima and fp16 copies of q, k, v in slot order: the
 // forward state at the start of the workspace.
 static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_t stream) {
   const int32_t group = in.Hq / in.Hkv;
@@ -137,10 +140,10 @@ static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_
   launch_absmax(in.D, in.B, in.L, in.Hq, in.q, true, ws.mq, stream);
   launch_absmax(in.D, in.B, in.L, in.Hkv, in.k, true, ws.mk, stream);
   launch_absmax(in.D, in.B, in.L, in.Hkv, in.v, false, ws.mv, stream);
-  launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hq, group, in.q, ws.rope, ws.mq, ws.qr, stream);
-  launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hkv, 1, in.k, ws.rope, ws.mk, ws.kr, stream);
-  launch_pack_any(in.D, false, in.B, in.L, ws.Lp, in.Hkv, 1, in.v, ws.rope, ws.mv, ws.vr, stream);
-  launch_intervals(in, ws, stream);
+  const int32_t *st = in.layout.slot_tok;
+  launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hq, group, in.q, st, ws.rope, ws.mq, ws.qr, stream);
+  launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hkv, 1, in.k, st, ws.rope, ws.mk, ws.kr, stream);
+  launch_pack_any(in.D, false, in.B, in.L, ws.Lp, in.Hkv, 1, in.v, st, ws.rope, ws.mv, ws.vr, stream);
 }
 
 static opr_status hip_status() {
@@ -168,9 +171,12 @@ opr_status opr_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block
   if ((int64_t)B * L >= (int64_t)1 << 31) return OPR_E_UNSUPPORTED;
   if (!valid_block(block_q) || !valid_block(block_k)) return OPR_E_UNSUPPORTED;
   if (!convs_per_row || !workspace || !out) return OPR_E_INVALID;
-  if (!out->tok_conv || !out->tok_turn || !out->tok_pos || !out->tok_type || !out->tile_class ||
-      !out->sub_class || !out->q_nnz || !out->q_list || !out->k_nnz || !out->k_list)
+  if (!out->tok_conv || !out->tok_turn || !out->tok_pos || !out->tok_type || !out->tok_slot ||
+      !out->slot_tok || !out->slot_qiv || !out->slot_kiv || !out->tile_class || !out->sub_class ||
+      !out->q_nnz || !out->q_list || !out->k_nnz || !out->k_list)
     return OPR_E_INVALID;
+  if (out->order != OPR_ORDER_PACKED && out->order != OPR_ORDER_ATTENTION) return OPR_E_INVALID;
+  if (!aligned16(out->slot_qiv) || !aligned16(out->slot_kiv)) return OPR_E_INVALID;
   const int64_t MT = ((int64_t)L + block_q - 1) / block_q, NT = ((int64_t)L + block_k - 1) / block_k;
   if ((int64_t)B * MT * NT >= (int64_t)1 << 31) return OPR_E_UNSUPPORTED;
   // count conversations and turns, check every length and each row's capacity
@@ -250,7 +256,8 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   mark(in, 0, stream);
   if (!in->reuse_fwd_workspace) forward_prologue(*in, ws, stream);
   launch_delta(*in, o, dout, lse, ws, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, in->Hq / in->Hkv, dout, ws.rope, ws.mdo, ws.dor, stream);
+  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, in->Hq / in->Hkv, dout, in->layout.slot_tok,
+                  ws.rope, ws.mdo, ws.dor, stream);
   launch_scale_delta(*in, ws, stream);
   if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream,
                               in->timing_events ? in->timing_events + 1 : nullptr) != hipSuccess)

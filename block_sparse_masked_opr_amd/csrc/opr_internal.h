@@ -52,7 +52,8 @@ hipError_t launch_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t bl
 // ---------------------------------------------------------------- attention
 struct AttnWs {
   int32_t Lp;           // L rounded up to OPR_ATTN_BLOCK
-  float2 *rope;         // [B][Lp][D/2] (cos, sin) at each token's position id
+  // everything below is in slot (attention) order
+  float2 *rope;         // [B][Lp][D/2] (cos, sin) at each slot's position id
   // fp16 copies [B][H][Lp][D], one power-of-two scale per (row, head) plane,
   // zero past L
   uint16_t *qr;         // q after RoPE
@@ -63,9 +64,6 @@ struct AttnWs {
   // mdo [B][Hq], contiguous from pmax (n_pmax words)
   uint32_t *pmax, *mq, *mk, *mv, *mdo;
   int32_t n_pmax;
-  int4 *qiv;            // [B][Lp] per-query key intervals
-  int4 *kiv;            // [B][Lp] per-key query intervals              (bwd)
-  uint64_t *hvb;        // [B][Lp/64] h / r_in bits
   float *dsc;           // [B][Hq][Lp] rowsum(dout * o), scaled        (bwd)
   float *lse2;          // [B][Hq][Lp] log2-domain lse, +inf where no key (bwd)
 };

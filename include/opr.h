@@ -63,8 +63,21 @@ enum { OPR_TILE_EMPTY = 0, OPR_TILE_PARTIAL = 1, OPR_TILE_FULL = 2 };
 #define OPR_SUB_BLOCK 32
 
 /* Attention tile the kernels run on: opr_attn_* need a layout built with
- * block_q == block_k == OPR_ATTN_BLOCK. */
+ * block_q == block_k == OPR_ATTN_BLOCK and order OPR_ORDER_ATTENTION. */
 #define OPR_ATTN_BLOCK 128
+
+/* The token order a tile schedule covers.
+ *  OPR_ORDER_PACKED     the packed rows as the pages draw the mask.
+ *  OPR_ORDER_ATTENTION  attention order: inside each conversation's index
+ *      range, first its h and r_in tokens (the ones later turns may see), in
+ *      packed order, then its t and r_out tokens, in packed order; PAD tokens
+ *      keep their index.  Attention commutes with reordering queries and keys
+ *      alike, so this changes no result; it is the order the attention kernels
+ *      run in, because there every query sees at most two runs of key slots,
+ *      all at or before its own slot, and the non-empty tiles are fewer and
+ *      denser.  (A choice of this library, not of the pages; the h and r_in
+ *      slots are conversation start + position id.) */
+enum { OPR_ORDER_PACKED = 0, OPR_ORDER_ATTENTION = 1 };
 
 /* Segment lengths of one turn, each >= 0.  An ordinary turn has
  * r_in == r_out (the response stored twice); a history-only turn of a K-pass
@@ -74,19 +87,30 @@ typedef struct {
 } opr_turn;
 
 /* Outputs of opr_build_layout for B rows of L tokens and block_q x block_k
- * tiles; MT = ceil(L / block_q), NT = ceil(L / block_k). */
+ * tiles; MT = ceil(L / block_q), NT = ceil(L / block_k).  A "slot" is an
+ * index in attention order.  Two runs [x0, x1) and [x2, x3) of slots are
+ * stored as int32 [4] with x0 <= x1 <= x2 <= x3, maximal and ascending; a
+ * missing run is written [x, x) with x the end of the run before it (0 if
+ * there is none). */
 typedef struct {
   int32_t *tok_conv;   /* [B][L] conversation index within the row; -1 for PAD */
   int32_t *tok_turn;   /* [B][L] turn index within the conversation; -1 for PAD */
   int32_t *tok_pos;    /* [B][L] strategic position id; 0 for PAD */
   uint8_t *tok_type;   /* [B][L] OPR_TOK_* */
-  uint8_t *tile_class; /* [B][MT][NT] OPR_TILE_* */
+  int32_t *tok_slot;   /* [B][L] slot of each token in attention order */
+  int32_t *slot_tok;   /* [B][L] token at each slot (the inverse permutation) */
+  int32_t *slot_qiv;   /* [B][L][4] key slots the query at slot s sees (two runs);
+                          16-byte aligned */
+  int32_t *slot_kiv;   /* [B][L][4] query slots that see the key at slot s (two
+                          runs); 16-byte aligned */
+  uint8_t *tile_class; /* [B][MT][NT] OPR_TILE_*, tiles over the order `order` */
   uint32_t *sub_class; /* [B][MT][NT] two bits per 32x32 sub-block (i, j) at bit
                           2*(i*(block_k/32) + j), same codes as tile_class */
   int32_t *q_nnz;      /* [B][MT] number of non-empty tiles in q-tile row m */
   int32_t *q_list;     /* [B][MT][NT] their k-tile indices ascending, then -1 */
   int32_t *k_nnz;      /* [B][NT] number of non-empty tiles in k-tile column n */
   int32_t *k_list;     /* [B][NT][MT] their q-tile indices ascending, then -1 */
+  int32_t order;       /* set by the caller: OPR_ORDER_* of the tile fields */
 } opr_layout;
 
 /*
@@ -94,10 +118,12 @@ typedef struct {
  *
  * Packs each row's conversations back to back (segments of a turn in the
  * order h, t, r_in, r_out; the rest of the row is PAD), assigns the strategic
- * position ids above, and classifies every block_q x block_k tile of the
- * block-sparse mask as empty / partial / full, with 32x32 sub-block classes
- * and the per-row and per-column lists of non-empty tiles.  Everything is
- * computed on the device from the segment lengths; no dense mask is formed.
+ * position ids above and the attention-order slots, writes the mask of every
+ * slot as two runs of slots (for its query and for its key), and classifies
+ * every block_q x block_k tile of the block-sparse mask, in the order
+ * out->order, as empty / partial / full, with 32x32 sub-block classes and the
+ * per-row and per-column lists of non-empty tiles.  Everything is computed on
+ * the device from the segment lengths; no dense mask is formed.
  *
  *  B, L            rows and tokens per row; B >= 1, L >= 1, B*L < 2^31.
  *  block_q/block_k tile edges, each 32, 64 or 128.
@@ -105,8 +131,10 @@ typedef struct {
  *                  >= 0.  turns host [sum turns_per_conv].  Conversations are
  *                  listed row by row, turns conversation by conversation.
  *  workspace       device, at least opr_build_layout_workspace_size(...) bytes.
- *  out             host struct of device pointers, all non-NULL.
- * Errors: OPR_E_INVALID (null pointer, negative count or length, bad B/L),
+ *  out             host struct of device pointers, all non-NULL, and the
+ *                  order (OPR_ORDER_*) of the tile schedule to build.
+ * Errors: OPR_E_INVALID (null pointer, misaligned slot_qiv / slot_kiv,
+ * negative count or length, bad B/L, unknown order),
  * OPR_E_UNSUPPORTED (block size), OPR_E_CAPACITY (a row longer than L, or
  * ws_bytes too small), OPR_E_HIP.  The host arrays are copied to the
  * workspace with hipMemcpyAsync before the call returns control.
@@ -129,7 +157,8 @@ typedef struct {
   const void *q;            /* bf16 [B][L][Hq][D], before RoPE */
   const void *k;            /* bf16 [B][L][Hkv][D], before RoPE */
   const void *v;            /* bf16 [B][L][Hkv][D] */
-  opr_layout layout;        /* from opr_build_layout(B, L, block_q, block_k, ...) */
+  opr_layout layout;        /* from opr_build_layout(B, L, block_q, block_k, ...)
+                               with order OPR_ORDER_ATTENTION */
   int32_t block_q, block_k; /* must both be OPR_ATTN_BLOCK */
   /* Optional instrumentation, may be NULL: host array of events created by
    * the caller (hipEventCreate).  opr_attn_fwd records [0] before its
@@ -152,14 +181,17 @@ typedef struct {
  * RoPE (rotate-half pairs (j, j + D/2), angle pos * theta^(-2j/D)) is applied
  * to q and k at the layout's position ids; then for every query token and q
  * head, softmax(scale * q k^T) over exactly the keys the mask allows, times v.
- * Empty tiles are skipped, full tiles run without a mask, partial tiles test
- * the mask per element from the per-token (conversation, turn, type).
+ * The kernels run in attention order: q, k, v are gathered into slot order,
+ * empty tiles are skipped, and partial 32x32 sub-blocks test the mask per
+ * element from the two runs of slots of the layout; results are written back
+ * at the tokens' own rows.
  *
  *  o    bf16 [B][L][Hq][D]   attention output; PAD rows get 0.
  *  lse  fp32 [B][Hq][L]      natural-log sum of exp of the scaled scores of
  *                            the allowed keys; -inf for PAD rows.
  *  workspace  >= opr_attn_workspace_size(B, L, Hq, Hkv, D, 0) bytes.
- * Errors: OPR_E_INVALID, OPR_E_UNSUPPORTED (D, block sizes), OPR_E_CAPACITY
+ * Errors: OPR_E_INVALID (including a layout of another order),
+ * OPR_E_UNSUPPORTED (D, block sizes), OPR_E_CAPACITY
  * (ws_bytes), OPR_E_HIP.
  */
 opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *workspace,

@@ -45,8 +45,8 @@ def test_status_strings(Bd):
 FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 
-def _layout_struct(Bd, null_field=None):
-    lay = Bd.OprLayout(*[FAKE] * 10)
+def _layout_struct(Bd, null_field=None, order=1):
+    lay = Bd.OprLayout(*[FAKE] * 14, order)
     if null_field:
         setattr(lay, null_field, None)
     return lay
@@ -76,6 +76,13 @@ def test_build_layout_errors(Bd):
     assert _build(Bd, ws_bytes=16) == Bd.OPR_E_CAPACITY
     assert _build(Bd, ws=None) == Bd.OPR_E_INVALID
     assert _build(Bd, out=_layout_struct(Bd, "q_list")) == Bd.OPR_E_INVALID
+    for f in ("tok_slot", "slot_tok", "slot_qiv", "slot_kiv"):
+        assert _build(Bd, out=_layout_struct(Bd, f)) == Bd.OPR_E_INVALID
+    assert _build(Bd, out=_layout_struct(Bd, order=2)) == Bd.OPR_E_INVALID
+    assert _build(Bd, out=_layout_struct(Bd, order=-1)) == Bd.OPR_E_INVALID
+    odd = _layout_struct(Bd)
+    odd.slot_kiv = FAKE + 8
+    assert _build(Bd, out=odd) == Bd.OPR_E_INVALID
     assert _build(Bd, B=1 << 16, L=1 << 15, cpr=(0,) * (1 << 16)) == Bd.OPR_E_UNSUPPORTED
 
 
@@ -113,6 +120,11 @@ def test_attn_errors(Bd):
         assert f(Bd, softmax_scale=-1.0) == Bd.OPR_E_INVALID
         assert f(Bd, q=None) == Bd.OPR_E_INVALID
         assert f(Bd, layout=_layout_struct(Bd, "sub_class")) == Bd.OPR_E_INVALID
+        assert f(Bd, layout=_layout_struct(Bd, "slot_tok")) == Bd.OPR_E_INVALID
+        assert f(Bd, layout=_layout_struct(Bd, order=0)) == Bd.OPR_E_INVALID   # packed-order tiles
+        odd = _layout_struct(Bd)
+        odd.slot_qiv = FAKE + 4                                                # runs need 16-byte alignment
+        assert f(Bd, layout=odd) == Bd.OPR_E_INVALID
         assert f(Bd, ws_bytes=1024) == Bd.OPR_E_CAPACITY
         assert f(Bd, B=0) == Bd.OPR_E_INVALID
     assert _bwd(Bd, dq=None) == Bd.OPR_E_INVALID
