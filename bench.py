@@ -35,6 +35,88 @@ from block_sparse_masked_opr_amd import inputs as I  # noqa: E402  (no torch, no
 PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
+CSRC = os.path.join(ROOT, "block_sparse_masked_opr_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+# sources compiled into each attention kernel (a change voids its counters)
+KERNEL_SOURCES = {
+    "attn_fwd": ("attn_fwd.hip", "attn_common.h", "attn_sched.h"),
+    "attn_dkdv": ("attn_bwd.hip", "attn_common.h", "attn_sched.h"),
+    "attn_dq": ("attn_dq.hip", "attn_common.h", "attn_sched.h"),
+}
+COPY_PROBE_BYTES = 1 << 30    # bytes read (and written) per copy-probe dispatch
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(kernel):
+    return os.path.join(PROFILES, f"{kernel}_packed_fwd_bwd_traffic.json")
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch of `kernel` from its committed counter summary,
+    or None if there is none or the kernel's sources changed since."""
+    try:
+        with open(traffic_file(kernel)) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha") != source_hash(kernel):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def copy_probe(steps=5):
+    """A plain device copy of COPY_PROBE_BYTES, to calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: {steps} copies of {COPY_PROBE_BYTES} bytes")
+
+
+def summarize_traffic(run_dir, kernel):
+    """Write profiles/<kernel>_packed_fwd_bwd_traffic.json from four rocprofv3
+    --pmc runs under run_dir: fetch/ and write/ of the benchmark (FETCH_SIZE,
+    WRITE_SIZE) and copy_fetch/ and copy_write/ of --copy-probe.  Counters are
+    KiB per dispatch; each is scaled by (probe bytes) / (probe counter)."""
+    import csv
+    import glob
+
+    def per_dispatch(sub, counter, match):
+        vals = []
+        for f in glob.glob(os.path.join(run_dir, sub, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] == counter and match(row["Kernel_Name"]):
+                    vals.append(float(row["Counter_Value"]))
+        if not vals:
+            raise SystemExit(f"no {counter} rows in {sub}")
+        return sum(vals) / len(vals)
+
+    is_kernel = lambda name: (kernel + "_kernel") in name                       # noqa: E731
+    # the probe's copy kernel only (not the fill that initialises its source)
+    is_copy = lambda name: "copy" in name.lower() and "fill" not in name.lower()  # noqa: E731
+    fetch = per_dispatch("fetch", "FETCH_SIZE", is_kernel)
+    write = per_dispatch("write", "WRITE_SIZE", is_kernel)
+    cf = COPY_PROBE_BYTES / per_dispatch("copy_fetch", "FETCH_SIZE", is_copy)
+    cw = COPY_PROBE_BYTES / per_dispatch("copy_write", "WRITE_SIZE", is_copy)
+    d = {"kernel": kernel, "workload": "packed_fwd_bwd", "source_sha": source_hash(kernel),
+         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+         "copy_probe_bytes": COPY_PROBE_BYTES, "fetch_bytes_per_kib": cf, "write_bytes_per_kib": cw,
+         "bytes_per_launch": round(fetch * cf + write * cw)}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_file(kernel), "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps(d))
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -203,12 +285,23 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the depth and K-pass sweeps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep-steps", type=int, default=3)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--summarize-traffic", metavar="RUN_DIR",
+                    help="write the HBM traffic summary of the dK/dV kernel from --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic, "attn_dkdv")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the one-pass attention path runs on a single MI355X; "
               "multi-GPU sharding is a design note only (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import torch
     from block_sparse_masked_opr_amd import binding as Bd
@@ -258,9 +351,10 @@ def main():
     per_pair = {"attn_fwd": 4.0, "attn_dkdv": 6.0, "attn_dq": 2.0}
     dom = max(per_pair, key=lambda k: stages[k])
     achieved = per_pair[dom] * shape.D * shape.Hq * P / (stages[dom] * 1e-3) / 1e12
+    traffic = load_traffic(dom)
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None,
-                "avg_ms": round(stages[dom], 4)}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch", "avg_ms": round(stages[dom], 4)}
 
     result = {
         "metric": "masked-attn fwd+bwd useful TFLOP/s & tokens/s; 1-pass vs N-pass speedup",
