@@ -19,8 +19,8 @@
 // attn_dq_kernel (attn_dq.hip): one workgroup per (128-query tile, q head,
 //   row), pipelined like the forward kernel over the K' / V tiles; S and dP^T
 //   are recomputed per non-empty sub-block and dQ^T += K'^T dS^T.
-// Work items are remapped so each XCD walks a contiguous range (shared tiles
-// stay in that XCD's L2).  Partial sub-blocks are masked with 64-bit masks
+// Work items start longest first, round-robin over the XCDs (q_order and
+// k_order of the prologue).  Partial sub-blocks are masked with 64-bit masks
 // built from the two runs of slots of each query or key.
 //
 // Units: q' and dout carry one exponent per (row, kv group), k' and v one per
@@ -54,12 +54,12 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_kernel(AttnParams p, float *
   __shared__ int sh_count;
   __shared__ int64_t sh_next;
 
-  const int64_t nitems = (int64_t)p.B * p.Hkv * p.NT;
-  const int64_t u = xcd_work_item(nitems);
-  if (u >= nitems) return;
-  const int n = (int)(u % p.NT);
-  const int kvh = (int)((u / p.NT) % p.Hkv);
-  const int b = (int)(u / ((int64_t)p.NT * p.Hkv));
+  const int64_t R = blockIdx.x;  // rank: longest columns first, round-robin over the XCDs
+  if (R >= (int64_t)p.B * p.NT * p.Hkv) return;
+  const int32_t col = p.k_order[R / p.Hkv];
+  const int kvh = (int)(R % p.Hkv);
+  const int b = col / p.NT;
+  const int n = col - b * p.NT;
 
   const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int key = n * 128 + 32 * w + li;
@@ -315,8 +315,7 @@ hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq
                                    float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev) {
   AttnParams p;
   fill_params(in, scale, ws, &p);
-  const int64_t nk = (int64_t)in.B * in.Hkv * p.NT;
-  const unsigned gk = (unsigned)(8 * ((nk + 7) / 8));
+  const unsigned gk = (unsigned)((int64_t)in.B * in.Hkv * p.NT);
   if (ev) (void)hipEventRecord(ev[0], s);
   if (in.D == 64) attn_dkdv_kernel<64><<<gk, 256, 0, s>>>(p, dk, dv);
   else attn_dkdv_kernel<128><<<gk, 256, 0, s>>>(p, dk, dv);

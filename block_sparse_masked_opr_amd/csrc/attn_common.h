@@ -275,13 +275,39 @@ __device__ __forceinline__ f16x8 tile_col8(const char *lds, const OperandOffsets
   return __builtin_bit_cast(f16x8, v);
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Remap the linear block id so that each XCD walks a contiguous range
-// of work items: neighbouring items share K/V (or Q/dO) tiles in that L2.
-__device__ __forceinline__ int64_t xcd_work_item(int64_t nitems) {
-  const int64_t per = (nitems + 7) / 8;
-  const int64_t bid = blockIdx.x;
-  return (bid & 7) * per + (bid >> 3);
+// Work order.  Workgroups are dispatched round-robin over the 8 XCDs (block
+// b goes to XCD b mod 8, each XCD with its own L2), and a kernel lasts as
+// long as its slowest CU.  The work items are therefore handed out longest
+// first: q_order / k_order list the q-tile rows / k-tile columns (b*MT + m,
+// b*NT + n) by decreasing number of stages, and consecutive ranks go to
+// consecutive XCDs.
+//
+// dK/dV: rank R = block id; item (k_order[R / Hkv], kv head R % Hkv).
+// Forward and dQ: super-rank R = (i / group) * 8 + x for block 8i + x, head
+// j = i % group of kv head R % Hkv of row k = q_order[R / Hkv]: the q heads
+// of one kv group sit on one XCD back to back and share its K/V tiles in L2.
+struct QItem {
+  int b, m, kvh, j;
+  bool valid;
+};
+
+__device__ __forceinline__ QItem q_work_item(const int32_t *q_order, int MT, int Hkv, int group, int64_t n_rows) {
+  const int64_t bid = blockIdx.x, i = bid >> 3;
+  const int64_t R = (i / group) * 8 + (bid & 7);
+  QItem it;
+  it.valid = R < n_rows * Hkv;
+  if (!it.valid) return it;
+  const int32_t row = q_order[R / Hkv];
+  it.kvh = (int)(R % Hkv);
+  it.j = (int)(i % group);
+  it.b = row / MT;
+  it.m = row - it.b * MT;
+  return it;
+}
+
+// Blocks of the forward / dQ grid for n_rows q-tile rows.
+inline int64_t q_grid(int64_t n_rows, int Hkv, int group) {
+  return 8 * group * ((n_rows * Hkv + 7) / 8);
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -296,6 +322,8 @@ struct AttnParams {
   const int32_t *q_nnz, *q_list, *k_nnz, *k_list;
   // Everything is indexed by slot (attention order) except the outputs,
   // which are written at token slot_tok[s].
+  const int32_t *q_order;      // [B*MT] q-tile rows, most stages first
+  const int32_t *k_order;      // [B*NT] k-tile columns, most stages first
   const int32_t *slot_tok;     // [B][L] token at each slot
   const int4 *qiv;             // [B][L] key slots a query slot sees: [x, y) and [z, w)
   const int4 *kiv;             // [B][L] query slots that see a key slot: [x, y) and [z, w)

@@ -34,15 +34,9 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   __shared__ uint2 stages[kStageCap];
   __shared__ int sh_count, sh_next;
 
-  const int64_t nitems = (int64_t)p.B * p.Hq * p.MT;
-  const int64_t u = xcd_work_item(nitems);
-  if (u >= nitems) return;
-  const int j = (int)(u % p.group);
-  int64_t rest = u / p.group;
-  const int m = (int)(rest % p.MT);
-  rest /= p.MT;
-  const int kvh = (int)(rest % p.Hkv);
-  const int b = (int)(rest / p.Hkv);
+  const QItem it = q_work_item(p.q_order, p.MT, p.Hkv, p.group, (int64_t)p.B * p.MT);
+  if (!it.valid) return;
+  const int j = it.j, m = it.m, kvh = it.kvh, b = it.b;
   const int h = kvh * p.group + j;
 
   const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
@@ -183,8 +177,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
 }  // namespace
 
 void launch_attn_dq_kernel(const AttnParams &p, int D, float *dq, hipStream_t s) {
-  const int64_t nq = (int64_t)p.B * p.Hq * p.MT;
-  const unsigned gq = (unsigned)(8 * ((nq + 7) / 8));
+  const unsigned gq = (unsigned)q_grid((int64_t)p.B * p.MT, p.Hkv, p.group);
   if (D == 64) attn_dq_kernel<64><<<gq, 256, 0, s>>>(p, dq);
   else attn_dq_kernel<128><<<gq, 256, 0, s>>>(p, dq);
 }

@@ -3,10 +3,9 @@
 // The kernel runs in attention order: q-tile m is query slots m*128 .. +127
 // and K/V rows are slots; results go to the slot's token.  One workgroup of
 // 4 waves per (128-slot query tile m, q head h, row b); wave w owns query
-// slots m*128 + 32w .. +31, one per lane column.  Work items are
-// remapped so each XCD walks a contiguous range of (row, kv head, q-tile,
-// head-in-group): the heads of one kv group and neighbouring q-tiles run side
-// by side and share K/V tiles in that XCD's L2.
+// slots m*128 + 32w .. +31, one per lane column.  Work items start longest
+// first, spread over the XCDs, with the q heads of one kv group side by side
+// on one XCD so that they share K/V tiles in its L2 (q_work_item).
 //
 // The non-empty 64-key halves of the q-tile's non-empty 128-key tiles are
 // first compacted into a stage list in LDS (a ballot over the tile list and
@@ -42,15 +41,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
   __shared__ uint2 stages[kStageCap];
   __shared__ int sh_count, sh_next;
 
-  const int64_t nitems = (int64_t)p.B * p.Hq * p.MT;
-  const int64_t u = xcd_work_item(nitems);
-  if (u >= nitems) return;
-  const int j = (int)(u % p.group);
-  int64_t rest = u / p.group;
-  const int m = (int)(rest % p.MT);
-  rest /= p.MT;
-  const int kvh = (int)(rest % p.Hkv);
-  const int b = (int)(rest / p.Hkv);
+  const QItem it = q_work_item(p.q_order, p.MT, p.Hkv, p.group, (int64_t)p.B * p.MT);
+  if (!it.valid) return;
+  const int j = it.j, m = it.m, kvh = it.kvh, b = it.b;
   const int h = kvh * p.group + j;
 
   const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
@@ -212,8 +205,7 @@ hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, f
                                   const AttnWs &ws, hipStream_t s) {
   AttnParams p;
   fill_params(in, scale, ws, &p);
-  const int64_t nitems = (int64_t)in.B * in.Hq * p.MT;
-  const unsigned grid = (unsigned)(8 * ((nitems + 7) / 8));
+  const unsigned grid = (unsigned)q_grid((int64_t)in.B * p.MT, in.Hkv, p.group);
   uint16_t *o16 = static_cast<uint16_t *>(o);
   if (in.D == 64) attn_fwd_kernel<64><<<grid, 256, 0, s>>>(p, o16, lse);
   else attn_fwd_kernel<128><<<grid, 256, 0, s>>>(p, o16, lse);

@@ -211,6 +211,83 @@ __global__ __launch_bounds__(256) void scale_delta_kernel(int32_t B, int32_t Lp,
   dsc[gid] = ldexpf(dsc[gid], e);
 }
 
+// Longest-first work order (see q_work_item): the q-tile rows (b*MT + m) by
+// decreasing number of non-empty 64-key halves over their tile lists - the
+// stages of a forward or dQ workgroup - and the k-tile columns (b*NT + n) by
+// decreasing number of non-empty 64-query halves - the stages of a dK/dV
+// workgroup.  One workgroup: per-item costs, then a counting sort (costs
+// above kOrderBins - 1 share the last bin; ties in any order).
+constexpr int kOrderThreads = 1024, kOrderBins = 4096;
+
+__global__ __launch_bounds__(kOrderThreads) void work_order_kernel(int32_t n_rows, int32_t n_cols, int32_t MT,
+                                                                   int32_t NT, const uint32_t *sub_class,
+                                                                   const int32_t *q_nnz, const int32_t *q_list,
+                                                                   const int32_t *k_nnz, const int32_t *k_list,
+                                                                   int32_t *cost, int32_t *q_order,
+                                                                   int32_t *k_order) {
+  __shared__ int32_t bins[kOrderBins];
+  __shared__ int32_t wave_sum[kOrderThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int32_t n = pass == 0 ? n_rows : n_cols;
+    int32_t *order = pass == 0 ? q_order : k_order;
+    int32_t *c = cost + (pass == 0 ? 0 : n_rows);
+    for (int i = tid; i < kOrderBins; i += kOrderThreads) bins[i] = 0;
+    __syncthreads();
+    for (int32_t it = tid; it < n; it += kOrderThreads) {
+      int32_t k = 0;
+      if (pass == 0) {  // row it: key halves are sub-block columns {0,1} and {2,3}
+        const int32_t cnt = q_nnz[it];
+        const int32_t *lst = q_list + (int64_t)it * NT;
+        const uint32_t *subs = sub_class + (int64_t)it * NT;
+        for (int32_t t = 0; t < cnt; ++t) {
+          const uint32_t w = subs[lst[t]];
+          k += ((w & 0x0F0F0F0Fu) != 0) + ((w & 0xF0F0F0F0u) != 0);
+        }
+      } else {          // column it: query halves are sub-block rows {0,1} and {2,3}
+        const int32_t b = it / NT, col = it - b * NT;
+        const int32_t cnt = k_nnz[it];
+        const int32_t *lst = k_list + (int64_t)it * MT;
+        for (int32_t t = 0; t < cnt; ++t) {
+          const uint32_t w = sub_class[((int64_t)b * MT + lst[t]) * NT + col];
+          k += ((w & 0x0000FFFFu) != 0) + ((w & 0xFFFF0000u) != 0);
+        }
+      }
+      k = min(k, kOrderBins - 1);
+      c[it] = k;
+      atomicAdd(&bins[kOrderBins - 1 - k], 1);  // bin 0 holds the largest cost
+    }
+    __syncthreads();
+    // exclusive scan of the bins: 4 per thread, then over the threads
+    constexpr int PER = kOrderBins / kOrderThreads;
+    int32_t v[PER], run = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      v[e] = bins[tid * PER + e];
+      run += v[e];
+    }
+    int32_t incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wave_sum[wv] = incl;
+    __syncthreads();
+    int32_t base = 0;
+    for (int i = 0; i < wv; ++i) base += wave_sum[i];
+    int32_t start = base + incl - run;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      bins[tid * PER + e] = start;
+      start += v[e];
+    }
+    __syncthreads();
+    for (int32_t it = tid; it < n; it += kOrderThreads) order[atomicAdd(&bins[kOrderBins - 1 - c[it]], 1)] = it;
+    __syncthreads();
+  }
+}
+
 __global__ void zero_words_kernel(uint32_t *p, int32_t n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -258,6 +335,13 @@ void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t
                      uint16_t *rows, hipStream_t s) {
   if (D == 64) launch_pack_d<64>(rope, B, L, Lp, H, group, x, slot_tok, table, pmax, rows, s);
   else launch_pack_d<128>(rope, B, L, Lp, H, group, x, slot_tok, table, pmax, rows, s);
+}
+
+void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+  const int32_t MT = ws.Lp / OPR_ATTN_BLOCK, NT = MT;
+  work_order_kernel<<<1, kOrderThreads, 0, s>>>(in.B * MT, in.B * NT, MT, NT, in.layout.sub_class, in.layout.q_nnz,
+                                               in.layout.q_list, in.layout.k_nnz, in.layout.k_list, ws.order_cost,
+                                               ws.q_order, ws.k_order);
 }
 
 // delta, lse2 and the dout plane maxima (mdo is cleared first), then dout

@@ -17,6 +17,7 @@ void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t
                      const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
                      uint16_t *rows, hipStream_t s);
 void launch_scale_delta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
+void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
                   const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, float *lse,
@@ -49,6 +50,10 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
     w.mv = w.mk + (size_t)in.B * in.Hkv;
     w.mdo = w.mv + (size_t)in.B * in.Hkv;
   }
+  const size_t tiles = (size_t)in.B * (Lp / OPR_ATTN_BLOCK);
+  w.q_order = cv.take<int32_t>(tiles);
+  w.k_order = cv.take<int32_t>(tiles);
+  w.order_cost = cv.take<int32_t>(2 * tiles);
   // everything above is the forward state; the backward part follows
   if (is_bwd) {
     w.dor = cv.take<uint16_t>(qn);
@@ -85,6 +90,8 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->mk = ws.mk;
   p->mv = ws.mv;
   p->mdo = ws.mdo;
+  p->q_order = ws.q_order;
+  p->k_order = ws.k_order;
   p->slot_tok = in.layout.slot_tok;
   p->qiv = reinterpret_cast<const int4 *>(in.layout.slot_qiv);
   p->kiv = reinterpret_cast<const int4 *>(in.layout.slot_kiv);
@@ -132,8 +139,8 @@ static void mark(const opr_attn_in *in, int i, hipStream_t s) {
   if (in->timing_events) hipEventRecord(in->timing_events[i], s);
 }
 
-// RoPE table, plane maxima and fp16 copies of q, k, v in slot order: the
-// forward state at the start of the workspace.
+// RoPE table, plane maxima, fp16 copies of q, k, v in slot order and the
+// work order: the forward state at the start of the workspace.
 static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_t stream) {
   const int32_t group = in.Hq / in.Hkv;
   launch_rope_table(in, ws, stream);
@@ -144,6 +151,7 @@ static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_
   launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hq, group, in.q, st, ws.rope, ws.mq, ws.qr, stream);
   launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hkv, 1, in.k, st, ws.rope, ws.mk, ws.kr, stream);
   launch_pack_any(in.D, false, in.B, in.L, ws.Lp, in.Hkv, 1, in.v, st, ws.rope, ws.mv, ws.vr, stream);
+  launch_work_order(in, ws, stream);
 }
 
 static opr_status hip_status() {

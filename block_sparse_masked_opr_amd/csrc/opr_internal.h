@@ -64,6 +64,9 @@ struct AttnWs {
   // mdo [B][Hq], contiguous from pmax (n_pmax words)
   uint32_t *pmax, *mq, *mk, *mv, *mdo;
   int32_t n_pmax;
+  int32_t *q_order;     // [B*MT] q-tile rows, most stages first
+  int32_t *k_order;     // [B*NT] k-tile columns, most stages first
+  int32_t *order_cost;  // [B*MT + B*NT] their stage counts
   float *dsc;           // [B][Hq][Lp] rowsum(dout * o), scaled        (bwd)
   float *lse2;          // [B][Hq][Lp] log2-domain lse, +inf where no key (bwd)
 };
