@@ -164,14 +164,16 @@ __device__ __forceinline__ float mask_select(uint64_t m, int pos, float x) {
 
 // ---------------------------------------------------------------------------
 // LDS tiles of 64 rows x D fp16.  A row is D/8 chunks of 16 bytes; chunk c of
-// row r is stored in slot c ^ swz(r), swz(r) = 2(r mod 4) + bit 3 of r.  A row
-// is a multiple of 128 bytes, so a 16-byte slot's banks depend on slot mod 8
-// only, and the two read patterns touch all 32 banks per access group:
-//  - 16-byte reads (8 lanes per group): one chunk of rows {0-3, 8-11} (+4,
-//    +16k), the rows of the kperm order - swz mod 8 takes 8 distinct values;
-//  - transposing 8-byte reads (16 lanes per group): chunks 2p, 2p+1 of rows
-//    4a..4a+3 - swz/2 mod 4 takes 4 distinct values, so the 4 rows land in
-//    4 different 32-byte bank quarters.
+// row r is stored in slot c ^ swz(r).  The LDS has 64 four-byte banks (256
+// bytes per clock); a 16-byte read is served 16 lanes at a time and the
+// transposing 8-byte read 32 lanes at a time, so conflict-free means:
+//  - 16-byte reads: one chunk of the 16 rows kperm(0..15) (+16k) per group -
+//    their 16 slots must fall in distinct 16-byte bank quads;
+//  - transposing reads: 32 bytes of each of rows 4a..4a+3 (chunks 4q..4q+3
+//    for D = 128) per group - the 4 rows must land in distinct 64-byte quarters.
+// D = 128 (256-byte rows): swz(r) = 4(r mod 4) + (r div 4) mod 4.
+// D = 64 (128-byte rows, two rows per bank cycle): swz(r) = 4((r div 2) mod 2)
+// + (r div 4) mod 4.  Both were checked with the LDS bank-conflict counter.
 // No padding is needed, and a 1 KB run of LDS is filled by one asynchronous
 // copy instruction (lane L writes bytes 16L..16L+15).
 #define OPR_LDS __attribute__((address_space(3)))
@@ -183,7 +185,9 @@ struct Tile {
   static constexpr int NC = D / 8;       // chunks per row
   static constexpr int RB = 2 * D;       // bytes per row
   static constexpr int BYTES = 64 * RB;
-  __device__ static __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 3) & 1); }
+  __device__ static __forceinline__ int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
   __device__ static __forceinline__ int off(int r, int c) { return r * RB + ((c ^ swz(r)) << 4); }
 };
 
