@@ -196,18 +196,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 // Asynchronous copies of 64-row tiles from a plane [rows][D] fp16 (buffer
-// resource over the plane) into swizzled LDS tiles.  Each of the 4 waves
+// resource over the plane) into swizzled LDS tiles.  Each of the NW waves
 // issues NI of the D/8 one-kilobyte instructions; the per-lane byte offsets
 // inside the 64-row block are fixed, the first row goes in the scalar offset.
-template <int D>
+template <int D, int NW = 4>
 struct TileCopy {
-  static constexpr int NI = Tile<D>::NC / 4;
+  static constexpr int NI = Tile<D>::NC / NW;
+  static_assert(NI >= 1 && NI * NW == Tile<D>::NC, "waves must split the tile's instructions evenly");
   int voff[NI];
   __device__ __forceinline__ void init(int w, int lane) {
     constexpr int NC = Tile<D>::NC, RPI = 1024 / Tile<D>::RB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int t = w + 4 * i;
+      const int t = w + NW * i;
       const int r = t * RPI + lane / NC;
       const int c = (lane % NC) ^ Tile<D>::swz(r);
       voff[i] = (r * D + c * 8) * 2;
@@ -216,7 +217,7 @@ struct TileCopy {
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int row0, char *lds, int w) const {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (OPR_LDS void *)(lds + (w + 4 * i) * 1024), 16, voff[i],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (OPR_LDS void *)(lds + (w + NW * i) * 1024), 16, voff[i],
                                                row0 * D * 2, 0, 0);
   }
 };
