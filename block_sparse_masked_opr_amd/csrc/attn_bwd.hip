@@ -163,15 +163,21 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     const char *Qt = buf, *dOt = buf + TB;
     const float *dscs = reinterpret_cast<const float *>(buf + 2 * TB + 256);
     const char *Pw = buf + 2 * TB + 512 + w * PSTRIDE;
+    // both products first, then both element blocks, then both updates: the
+    // element work falls where the P-wave on the same SIMD runs products
+    f32x16 dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f16x8 df[NS];
 #pragma unroll
       for (int st = 0; st < NS; ++st) df[st] = lds_f16x8(dOt + qb * 32 * RB + of.row8[st]);
-      f32x16 dp = zero_f32x16();
+      dp[qb] = zero_f32x16();
 #pragma unroll
-      for (int st = 0; st < NS; ++st) dp = mfma32x32x16(df[st], frag[st], dp);
-      f16x8 dsb[2];
+      for (int st = 0; st < NS; ++st) dp[qb] = mfma32x32x16(df[st], frag[st], dp[qb]);
+    }
+    f16x8 dsb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int qbase = 32 * qb + 16 * hh + 8 * g;
@@ -183,14 +189,17 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
         for (int e = 0; e < 8; ++e) {
           const int rr = 8 * hh + e;
           // P * 2^kPdvExp times (dP * 2^-kDsShift - delta) * 2^-kPdvExp
-          dsb[hh][e] = (_Float16)((float)pv[e] * fmaf(dp[rr], dss, -dvv[e] * dsc_unit));
+          dsb[qb][hh][e] = (_Float16)((float)pv[e] * fmaf(dp[qb][rr], dss, -dvv[e] * dsc_unit));
         }
       }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          acc[db] = mfma32x32x16(tile_col8<D>(Qt, of, 32 * qb + 16 * hh, db), dsb[hh], acc[db]);
+          acc[db] = mfma32x32x16(tile_col8<D>(Qt, of, 32 * qb + 16 * hh, db), dsb[qb][hh], acc[db]);
       }
     }
   };

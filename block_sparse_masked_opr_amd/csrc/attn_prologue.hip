@@ -47,13 +47,29 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, i
 // 16-lane group reads one head's whole row and a wave reads contiguous runs.
 constexpr int kAbsTokens = 64;
 
+// One launch covers q, k and v: blockIdx.y runs over the head blocks of
+// job 0, then job 1, then job 2.
+struct AbsmaxJob {
+  const uint16_t *x;  // [B][L][H][D] bf16
+  uint32_t *pmax;     // [B][H]
+  int32_t H;
+  int32_t hb_end;     // one past this job's last head block (cumulative)
+  float factor;
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void absmax_kernel(int32_t L, int32_t H, const uint16_t *x, float factor,
-                                                     uint32_t *pmax) {
+__global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, AbsmaxJob j1, AbsmaxJob j2) {
   constexpr int CPH = D / 8, HPB = 256 / CPH;
+  const int yb = blockIdx.y;
+  const bool in0 = yb < j0.hb_end, in1 = !in0 && yb < j1.hb_end;
+  const uint16_t *x = in0 ? j0.x : (in1 ? j1.x : j2.x);
+  uint32_t *pmax = in0 ? j0.pmax : (in1 ? j1.pmax : j2.pmax);
+  const int32_t H = in0 ? j0.H : (in1 ? j1.H : j2.H);
+  const float factor = in0 ? j0.factor : (in1 ? j1.factor : j2.factor);
+  const int hb = yb - (in0 ? 0 : (in1 ? j0.hb_end : j1.hb_end));
   const int b = blockIdx.z, tid = threadIdx.x;
   const int hl = tid / CPH, j = tid % CPH;
-  const int h = blockIdx.y * HPB + hl;
+  const int h = hb * HPB + hl;
   const int t0 = blockIdx.x * kAbsTokens;
   float m = 0.0f;
   if (h < H) {
@@ -72,7 +88,9 @@ __global__ __launch_bounds__(256) void absmax_kernel(int32_t L, int32_t H, const
   if (j == 0 && h < H && m > 0.0f) atomicMax(pmax + (int64_t)b * H + h, __float_as_uint(m * factor));
 }
 
-// One workgroup per (64-slot block, head, row).  x: [B][L][H][D] bf16 ->
+// One workgroup per (head, 64-slot block, row); the heads of one slot block
+// are consecutive blocks, so its RoPE table rows stay in L2 across heads.
+// x: [B][L][H][D] bf16 ->
 // rows [B][H][Lp][D] in slot order, fp16(x' * 2^e), x' = RoPE(x) or x, e the
 // exponent of the largest plane maximum of the head's group of `group`
 // heads.  Slots s >= L are zero.
@@ -83,8 +101,7 @@ __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_
                                                    uint16_t *rows) {
   constexpr int HALF = D / 2;
   constexpr int PER = HALF / 4;  // pairs per thread (4 threads per token)
-  const int t0 = blockIdx.x * 64;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int h = (int)(blockIdx.x % (unsigned)H), t0 = (int)(blockIdx.x / (unsigned)H) * 64, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int tt = tid >> 2, part = tid & 3;
   const int t = t0 + tt;
@@ -294,18 +311,16 @@ __global__ void zero_words_kernel(uint32_t *p, int32_t n) {
 }
 
 template <int D>
-void launch_absmax_d(int32_t B, int32_t L, int32_t H, const void *x, float factor, uint32_t *pmax,
-                     hipStream_t s) {
-  constexpr int HPB = 256 / (D / 8);
-  absmax_kernel<D><<<dim3((L + kAbsTokens - 1) / kAbsTokens, (H + HPB - 1) / HPB, B), 256, 0, s>>>(
-      L, H, static_cast<const uint16_t *>(x), factor, pmax);
+void launch_absmax_d(int32_t B, int32_t L, const AbsmaxJob *jobs, hipStream_t s) {
+  absmax_kernel<D><<<dim3((L + kAbsTokens - 1) / kAbsTokens, jobs[2].hb_end, B), 256, 0, s>>>(L, jobs[0], jobs[1],
+                                                                                             jobs[2]);
 }
 
 template <int D>
 void launch_pack_d(bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group, const void *x,
                    const int32_t *slot_tok, const float2 *table, const uint32_t *pmax, uint16_t *rows,
                    hipStream_t s) {
-  const dim3 grid(Lp / 64, H, B);
+  const dim3 grid((unsigned)H * (unsigned)(Lp / 64), 1, B);
   const uint16_t *src = static_cast<const uint16_t *>(x);
   if (rope) pack_kernel<D, true><<<grid, 256, 0, s>>>(L, Lp, H, group, src, slot_tok, table, pmax, rows);
   else pack_kernel<D, false><<<grid, 256, 0, s>>>(L, Lp, H, group, src, slot_tok, table, pmax, rows);
@@ -323,11 +338,20 @@ void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
                                                      ws.n_pmax);
 }
 
-void launch_absmax(int D, int32_t B, int32_t L, int32_t H, const void *x, bool rope, uint32_t *pmax,
-                   hipStream_t s) {
-  const float factor = rope ? 1.4142136f : 1.0f;
-  if (D == 64) launch_absmax_d<64>(B, L, H, x, factor, pmax, s);
-  else launch_absmax_d<128>(B, L, H, x, factor, pmax, s);
+// Plane maxima of q and k (times sqrt(2), the RoPE bound) and of v.
+void launch_absmax_qkv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+  const int HPB = 256 / (in.D / 8);
+  AbsmaxJob jobs[3];
+  const void *xs[3] = {in.q, in.k, in.v};
+  uint32_t *ms[3] = {ws.mq, ws.mk, ws.mv};
+  const int32_t hs[3] = {in.Hq, in.Hkv, in.Hkv};
+  int32_t end = 0;
+  for (int i = 0; i < 3; ++i) {
+    end += (hs[i] + HPB - 1) / HPB;
+    jobs[i] = AbsmaxJob{static_cast<const uint16_t *>(xs[i]), ms[i], hs[i], end, i < 2 ? 1.4142136f : 1.0f};
+  }
+  if (in.D == 64) launch_absmax_d<64>(in.B, in.L, jobs, s);
+  else launch_absmax_d<128>(in.B, in.L, jobs, s);
 }
 
 void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,

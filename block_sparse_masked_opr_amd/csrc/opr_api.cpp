@@ -11,8 +11,7 @@ namespace opr {
 
 // launchers defined in the .hip files
 void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
-void launch_absmax(int D, int32_t B, int32_t L, int32_t H, const void *x, bool rope, uint32_t *pmax,
-                   hipStream_t s);
+void launch_absmax_qkv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,
                      const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
                      uint16_t *rows, hipStream_t s);
@@ -144,9 +143,7 @@ static void mark(const opr_attn_in *in, int i, hipStream_t s) {
 static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_t stream) {
   const int32_t group = in.Hq / in.Hkv;
   launch_rope_table(in, ws, stream);
-  launch_absmax(in.D, in.B, in.L, in.Hq, in.q, true, ws.mq, stream);
-  launch_absmax(in.D, in.B, in.L, in.Hkv, in.k, true, ws.mk, stream);
-  launch_absmax(in.D, in.B, in.L, in.Hkv, in.v, false, ws.mv, stream);
+  launch_absmax_qkv(in, ws, stream);
   const int32_t *st = in.layout.slot_tok;
   launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hq, group, in.q, st, ws.rope, ws.mq, ws.qr, stream);
   launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hkv, 1, in.k, st, ws.rope, ws.mk, ws.kr, stream);
