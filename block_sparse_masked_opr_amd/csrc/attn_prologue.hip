@@ -88,57 +88,69 @@ __global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, Ab
   if (j == 0 && h < H && m > 0.0f) atomicMax(pmax + (int64_t)b * H + h, __float_as_uint(m * factor));
 }
 
-// One workgroup per (head, 64-slot block, row); the heads of one slot block
-// are consecutive blocks, so its RoPE table rows stay in L2 across heads.
-// x: [B][L][H][D] bf16 ->
+// One workgroup per (64-slot block, group of kPackHeads heads, row): 4
+// threads per slot, each owning D/8 rotation pairs, keep the slot's RoPE
+// cosines and sines in registers and walk the heads.  x: [B][L][H][D] bf16 ->
 // rows [B][H][Lp][D] in slot order, fp16(x' * 2^e), x' = RoPE(x) or x, e the
 // exponent of the largest plane maximum of the head's group of `group`
 // heads.  Slots s >= L are zero.
+constexpr int kPackHeads = 8;
+
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H, int32_t group,
                                                    const uint16_t *x, const int32_t *slot_tok,
                                                    const float2 *table, const uint32_t *pmax,
                                                    uint16_t *rows) {
   constexpr int HALF = D / 2;
-  constexpr int PER = HALF / 4;  // pairs per thread (4 threads per token)
-  const int h = (int)(blockIdx.x % (unsigned)H), t0 = (int)(blockIdx.x / (unsigned)H) * 64, b = blockIdx.z;
+  constexpr int PER = HALF / 4;  // pairs per thread (4 threads per slot)
+  const int hgroups = (H + kPackHeads - 1) / kPackHeads;
+  const int h0 = (int)(blockIdx.x % (unsigned)hgroups) * kPackHeads;
+  const int t0 = (int)(blockIdx.x / (unsigned)hgroups) * 64, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int tt = tid >> 2, part = tid & 3;
   const int t = t0 + tt;
   const int j0 = part * PER;
-  const int ex = group_exponent(pmax + (int64_t)b * H + (h / group) * group, group);
-  uint16_t lq[PER], hq[PER];
-  if (t < L) {
-    const int32_t tok = slot_tok[(int64_t)b * L + t];
-    const uint16_t *src = x + (((int64_t)b * L + tok) * H + h) * D;
-    uint16_t lb[PER], hb[PER];
+  const int32_t tok = t < L ? slot_tok[(int64_t)b * L + t] : -1;
+  float2 cs[PER];
+  if (ROPE) {
+    const float2 *row = table + ((int64_t)b * Lp + t) * HALF + j0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) cs[e] = row[e];
+  }
+  const int h1 = min(H, h0 + kPackHeads);
+#pragma unroll 2
+  for (int h = h0; h < h1; ++h) {
+    const int ex = group_exponent(pmax + (int64_t)b * H + (h / group) * group, group);
+    uint16_t lq[PER], hq[PER];
+    if (tok >= 0) {
+      const uint16_t *src = x + (((int64_t)b * L + tok) * H + h) * D;
+      uint16_t lb[PER], hb[PER];
+#pragma unroll
+      for (int c = 0; c < PER; c += 8) {
+        *reinterpret_cast<uint4 *>(&lb[c]) = *reinterpret_cast<const uint4 *>(src + j0 + c);
+        *reinterpret_cast<uint4 *>(&hb[c]) = *reinterpret_cast<const uint4 *>(src + HALF + j0 + c);
+      }
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        float lo = bf16_to_f32(lb[e]), hi = bf16_to_f32(hb[e]);
+        if (ROPE) {
+          const float x1 = lo, x2 = hi;
+          lo = x1 * cs[e].x - x2 * cs[e].y;
+          hi = x2 * cs[e].x + x1 * cs[e].y;
+        }
+        lq[e] = f32_to_f16_bits(ldexpf(lo, ex));
+        hq[e] = f32_to_f16_bits(ldexpf(hi, ex));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) lq[e] = hq[e] = 0;
+    }
+    uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
 #pragma unroll
     for (int c = 0; c < PER; c += 8) {
-      *reinterpret_cast<uint4 *>(&lb[c]) = *reinterpret_cast<const uint4 *>(src + j0 + c);
-      *reinterpret_cast<uint4 *>(&hb[c]) = *reinterpret_cast<const uint4 *>(src + HALF + j0 + c);
+      *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
+      *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
     }
-    const float2 *cs = table + ((int64_t)b * Lp + t) * HALF + j0;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      float lo = bf16_to_f32(lb[e]), hi = bf16_to_f32(hb[e]);
-      if (ROPE) {
-        const float2 r = cs[e];
-        const float x1 = lo, x2 = hi;
-        lo = x1 * r.x - x2 * r.y;
-        hi = x2 * r.x + x1 * r.y;
-      }
-      lq[e] = f32_to_f16_bits(ldexpf(lo, ex));
-      hq[e] = f32_to_f16_bits(ldexpf(hi, ex));
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) lq[e] = hq[e] = 0;
-  }
-  uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
-#pragma unroll
-  for (int c = 0; c < PER; c += 8) {
-    *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
-    *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
   }
 }
 
@@ -174,6 +186,7 @@ __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_
     const int32_t b = (int32_t)(bt / Lp);
     if (b != (int32_t)(bt0 / Lp)) break;  // a workgroup's plane maxima stay within one row
     const int32_t t = sl < L ? slot_tok[(int64_t)b * L + sl] : L;  // token at the slot
+#pragma unroll 4
     for (int h0 = 0; h0 < Hq; h0 += HPS) {
       const int h = h0 + hl;
       float acc = 0.0f, mx = 0.0f;
@@ -251,13 +264,15 @@ __global__ __launch_bounds__(kOrderThreads) void work_order_kernel(int32_t n_row
     int32_t *c = cost + (pass == 0 ? 0 : n_rows);
     for (int i = tid; i < kOrderBins; i += kOrderThreads) bins[i] = 0;
     __syncthreads();
-    for (int32_t it = tid; it < n; it += kOrderThreads) {
+    // 8 lanes per item, each summing every 8th entry of its tile list
+    const int sub = tid & 7;
+    for (int32_t it = tid >> 3; it < n; it += kOrderThreads / 8) {
       int32_t k = 0;
       if (pass == 0) {  // row it: key halves are sub-block columns {0,1} and {2,3}
         const int32_t cnt = q_nnz[it];
         const int32_t *lst = q_list + (int64_t)it * NT;
         const uint32_t *subs = sub_class + (int64_t)it * NT;
-        for (int32_t t = 0; t < cnt; ++t) {
+        for (int32_t t = sub; t < cnt; t += 8) {
           const uint32_t w = subs[lst[t]];
           k += ((w & 0x0F0F0F0Fu) != 0) + ((w & 0xF0F0F0F0u) != 0);
         }
@@ -265,14 +280,19 @@ __global__ __launch_bounds__(kOrderThreads) void work_order_kernel(int32_t n_row
         const int32_t b = it / NT, col = it - b * NT;
         const int32_t cnt = k_nnz[it];
         const int32_t *lst = k_list + (int64_t)it * MT;
-        for (int32_t t = 0; t < cnt; ++t) {
+        for (int32_t t = sub; t < cnt; t += 8) {
           const uint32_t w = sub_class[((int64_t)b * MT + lst[t]) * NT + col];
           k += ((w & 0x0000FFFFu) != 0) + ((w & 0xFFFF0000u) != 0);
         }
       }
-      k = min(k, kOrderBins - 1);
-      c[it] = k;
-      atomicAdd(&bins[kOrderBins - 1 - k], 1);  // bin 0 holds the largest cost
+      k += __shfl_xor(k, 1);
+      k += __shfl_xor(k, 2);
+      k += __shfl_xor(k, 4);
+      if (sub == 0) {
+        k = min(k, kOrderBins - 1);
+        c[it] = k;
+        atomicAdd(&bins[kOrderBins - 1 - k], 1);  // bin 0 holds the largest cost
+      }
     }
     __syncthreads();
     // exclusive scan of the bins: 4 per thread, then over the threads
@@ -320,7 +340,8 @@ template <int D>
 void launch_pack_d(bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group, const void *x,
                    const int32_t *slot_tok, const float2 *table, const uint32_t *pmax, uint16_t *rows,
                    hipStream_t s) {
-  const dim3 grid((unsigned)H * (unsigned)(Lp / 64), 1, B);
+  const unsigned hgroups = (unsigned)((H + kPackHeads - 1) / kPackHeads);
+  const dim3 grid(hgroups * (unsigned)(Lp / 64), 1, B);
   const uint16_t *src = static_cast<const uint16_t *>(x);
   if (rope) pack_kernel<D, true><<<grid, 256, 0, s>>>(L, Lp, H, group, src, slot_tok, table, pmax, rows);
   else pack_kernel<D, false><<<grid, 256, 0, s>>>(L, Lp, H, group, src, slot_tok, table, pmax, rows);
