@@ -105,35 +105,44 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
       const uint2 desc = uniform(stages[i]);
       const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
       if ((c0 | c1) == 0) return;
-      const uint32_t cls[2] = {c0, c1};
       const int k0 = (int)desc.x;
       const char *Kt = buf, *Vt = buf + TB;
 
-      uint64_t mk = 0;
-      if (c0 == 1 || c1 == 1) mk = (range_bits(iv.x, iv.y, k0) | range_bits(iv.z, iv.w, k0)) >> (8 * g);
+      // Both 32-key sub-blocks always (straight-line code): the mask is exact,
+      // so an empty one gives p = 0 and dS = 0.
+      f32x16 s[2], dpt[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = zero_f32x16();
+        dpt[kb] = zero_f32x16();
+      }
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = mfma32x32x16(lds_f16x8(Kt + kb * 32 * RB + of.row8[st]), qb[st], s[kb]);
+          dpt[kb] = mfma32x32x16(lds_f16x8(Vt + kb * 32 * RB + of.row8[st]), dob[st], dpt[kb]);
+        }
+      }
+      if (c0 != 2 || c1 != 2) {
+        const uint64_t mk = (range_bits(iv.x, iv.y, k0) | range_bits(iv.z, iv.w, k0)) >> (8 * g);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) s[kb][rr] = mask_select(mk, 32 * kb + 16 * (rr >> 3) + (rr & 7), s[kb][rr]);
+        }
+      }
       f16x8 dsb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        if (cls[kb] == 0) continue;
-        f32x16 s = zero_f32x16(), dpt = zero_f32x16();
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          s = mfma32x32x16(lds_f16x8(Kt + kb * 32 * RB + of.row8[st]), qb[st], s);
-          dpt = mfma32x32x16(lds_f16x8(Vt + kb * 32 * RB + of.row8[st]), dob[st], dpt);
-        }
-        if (cls[kb] == 1) {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) s[rr] = mask_select(mk, 32 * kb + 16 * (rr >> 3) + (rr & 7), s[rr]);
-        }
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[rr], fs, -lse2_q));
-          dsb[kb][rr >> 3][rr & 7] = (_Float16)(pv * fmaf(dpt[rr], dss, -dsc_q));
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][rr], fs, -lse2_q));
+          dsb[kb][rr >> 3][rr & 7] = (_Float16)(pv * fmaf(dpt[kb][rr], dss, -dsc_q));
         }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        if (cls[kb] == 0) continue;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll

@@ -108,25 +108,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
       const uint2 desc = uniform(stages[i]);
       const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
       if ((c0 | c1) == 0) return;
-      const uint32_t cls[2] = {c0, c1};
       const int k0 = (int)desc.x;
       const char *Kt = buf, *Vt = buf + TB;
 
+      // Both 32-key sub-blocks always (straight-line code): the mask is exact,
+      // so an empty one gives -inf scores and p = 0.
       f32x16 s[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = zero_f32x16();
-        if (cls[kb] == 0) continue;
+      for (int kb = 0; kb < 2; ++kb) s[kb] = zero_f32x16();
 #pragma unroll
-        for (int st = 0; st < NS; ++st)
+      for (int st = 0; st < NS; ++st) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
           s[kb] = mfma32x32x16(lds_f16x8(Kt + kb * 32 * RB + of.row8[st]), qb[st], s[kb]);
       }
-      if (c0 == 1 || c1 == 1) {
+      if (c0 != 2 || c1 != 2) {
         uint64_t mk = range_bits(iv.x, iv.y, k0) | range_bits(iv.z, iv.w, k0);
         mk >>= 8 * g;  // lane group g holds keys 16h + 8g + 0..7 of each 32-key block
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          if (cls[kb] != 1) continue;
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[kb][r] = mask_select(mk, 32 * kb + 16 * (r >> 3) + (r & 7), s[kb][r]);
         }
@@ -134,7 +134,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        if (cls[kb] == 0) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       }
@@ -152,7 +151,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
       f16x8 pb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        if (cls[kb] == 0) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) pb[kb][r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], fs, cexp));
 #pragma unroll
@@ -160,7 +158,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        if (cls[kb] == 0) continue;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
