@@ -54,6 +54,25 @@ constexpr float kMaxSlack = 8.0f;
 constexpr int kPExp = 7;
 
 // A-operand row order of a 32-row block: swap bits 2 and 3.
+// bf16 helpers on packed words.  dot2_bf16: a.lo*b.lo + a.hi*b.hi + c in
+// float32 (the products of bf16 values are exact in float32).
+// absmax8_bf16_bits: the largest |x| of 8 bf16 values as float bits - a bf16
+// value is the top half of its float, and for finite values the magnitude
+// bits order like the magnitudes, so a packed 16-bit integer max suffices.
+typedef __bf16 __attribute__((ext_vector_type(2))) bf16x2;
+typedef unsigned short __attribute__((ext_vector_type(2))) u16x2;
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+__device__ __forceinline__ uint32_t absmax8_bf16_bits(uint4 v) {
+  const u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu),
+                                            __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
+  const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu),
+                                            __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
+  const u16x2 m = __builtin_elementwise_max(a, b);
+  return (uint32_t)(m.x > m.y ? m.x : m.y) << 16;
+}
+
 // Wave-uniform values that the compiler cannot prove uniform (the wave index,
 // words read from LDS): taking them from lane 0 puts them in scalar registers,
 // so buffer offsets and branches on them need no per-lane loops.

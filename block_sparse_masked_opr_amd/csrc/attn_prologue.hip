@@ -71,21 +71,17 @@ __global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, Ab
   const int hl = tid / CPH, j = tid % CPH;
   const int h = hb * HPB + hl;
   const int t0 = blockIdx.x * kAbsTokens;
-  float m = 0.0f;
+  uint32_t m = 0u;  // float bits of the largest |x| (non-negative: integer order)
   if (h < H) {
     const uint16_t *src = x + (((int64_t)b * L + t0) * H + h) * D + j * 8;
     const int nt = min(kAbsTokens, L - t0);
 #pragma unroll 8
-    for (int t = 0; t < nt; ++t) {
-      uint16_t v[8];
-      *reinterpret_cast<uint4 *>(v) = *reinterpret_cast<const uint4 *>(src + (int64_t)t * H * D);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(bf16_to_f32(v[e])));
-    }
+    for (int t = 0; t < nt; ++t)
+      m = max(m, absmax8_bf16_bits(*reinterpret_cast<const uint4 *>(src + (int64_t)t * H * D)));
   }
 #pragma unroll
-  for (int off = CPH / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (j == 0 && h < H && m > 0.0f) atomicMax(pmax + (int64_t)b * H + h, __float_as_uint(m * factor));
+  for (int off = CPH / 2; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if (j == 0 && h < H && m > 0u) atomicMax(pmax + (int64_t)b * H + h, __float_as_uint(__uint_as_float(m) * factor));
 }
 
 // One workgroup per (64-slot block, group of kPackHeads heads, row): 4
@@ -189,23 +185,22 @@ __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_
 #pragma unroll 4
     for (int h0 = 0; h0 < Hq; h0 += HPS) {
       const int h = h0 + hl;
-      float acc = 0.0f, mx = 0.0f;
+      float acc = 0.0f;
+      uint32_t mx = 0u;  // float bits of the largest |dout|
       if (t < L && h < Hq) {
         const int64_t base = (((int64_t)b * L + t) * Hq + h) * D + part * 8;
-        uint16_t ov[8], dv[8];
-        *reinterpret_cast<uint4 *>(ov) = *reinterpret_cast<const uint4 *>(o + base);
-        *reinterpret_cast<uint4 *>(dv) = *reinterpret_cast<const uint4 *>(dout + base);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float dd = bf16_to_f32(dv[e]);
-          acc += bf16_to_f32(ov[e]) * dd;
-          mx = fmaxf(mx, fabsf(dd));
-        }
+        const uint4 ov = *reinterpret_cast<const uint4 *>(o + base);
+        const uint4 dv = *reinterpret_cast<const uint4 *>(dout + base);
+        acc = dot2_bf16(ov.x, dv.x, acc);
+        acc = dot2_bf16(ov.y, dv.y, acc);
+        acc = dot2_bf16(ov.z, dv.z, acc);
+        acc = dot2_bf16(ov.w, dv.w, acc);
+        mx = absmax8_bf16_bits(dv);
       }
 #pragma unroll
       for (int off = LPH / 2; off > 0; off >>= 1) {
         acc += __shfl_xor(acc, off);
-        mx = fmaxf(mx, __shfl_xor(mx, off));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
       }
       if (part == 0 && h < Hq) {
         float l2 = INFINITY;
@@ -216,7 +211,7 @@ __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_
         const int64_t out = ((int64_t)b * Hq + h) * Lp + sl;
         dsc[out] = acc;
         lse2[out] = l2;
-        if (mx > 0.0f) atomicMax(&hmax[h], __float_as_uint(mx));
+        if (mx > 0u) atomicMax(&hmax[h], mx);
       }
     }
   }
