@@ -27,7 +27,7 @@
 // (row, kv head), all constant inside a workgroup.  dP = dO V^T comes out in
 // units 2^(e_dout + e_v); delta arrives pre-scaled into those units times
 // 2^-kDsShift, and dS is formed as P * 2^-kDsShift * (dP - delta) before the
-// fp16 conversion; P for dV is stored as fp16(P * 2^15).
+// fp16 conversion; P for dV is stored as fp16(P * 2^kPdvExp).
 #include "attn_common.h"
 #include "attn_sched.h"
 #include "opr_internal.h"
@@ -35,7 +35,7 @@
 namespace opr {
 namespace {
 
-constexpr int kPdvExp = 15;  // P (<= 1) enters dV as fp16(P * 2^15)
+constexpr int kReadsAhead = 4;  // dV / dK products whose operand reads are in flight
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *dk, float *dv) {
@@ -44,14 +44,19 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   constexpr int HALF_DB = NDB / 2;
   constexpr int TB = Tile<D>::BYTES, RB = Tile<D>::RB;
   constexpr int PSTRIDE = 4096;  // P of one key block: [qb][hh][lane] x 16 bytes
-  // per stage buffer: Q' tile, dO tile, lse2[64], scaled delta[64], P of the 4 key blocks
-  constexpr int BUF = 2 * TB + 512 + 4 * PSTRIDE;
-  // three separate LDS objects (a ring: the P-waves read stage i, the dS-waves
-  // stage i-1, stage i+1 streams in); separate objects let the compiler see
-  // that the copy into one leaves the others alone
+  // per stage buffer: Q' tile, dO tile, lse2[64], scaled delta[64]
+  constexpr int BUF = 2 * TB + 512;
+  // Separate LDS objects, so that the compiler sees that a copy or a store
+  // into one leaves the others alone: a ring of three stage buffers (the
+  // P-waves read stage i, the dS-waves stage i-1, stage i+1 streams in) and
+  // a ring of three P buffers of the 4 key blocks (written by the P-waves at
+  // step i, read by the dS-waves at step i+1).
   __shared__ __attribute__((aligned(1024))) char buf0[BUF];
   __shared__ __attribute__((aligned(1024))) char buf1[BUF];
   __shared__ __attribute__((aligned(1024))) char buf2[BUF];
+  __shared__ __attribute__((aligned(1024))) char pbf0[4 * PSTRIDE];
+  __shared__ __attribute__((aligned(1024))) char pbf1[4 * PSTRIDE];
+  __shared__ __attribute__((aligned(1024))) char pbf2[4 * PSTRIDE];
   __shared__ uint2 stages[kStageCap];
   __shared__ int sh_count;
   __shared__ int64_t sh_next;
@@ -74,9 +79,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   const int ek = plane_exponent(p.mk[kvplane]);
   const int ev = plane_exponent(p.mv[kvplane]);
   const float fs = ldexpf(p.scale_log2, -(eq + ek));
-  const float pdv = ldexpf(1.0f, kPdvExp);
   const float dss = ldexpf(1.0f, -kDsShift - kPdvExp);
-  const float dsc_unit = ldexpf(1.0f, -kPdvExp);
 
   // K' rows (P-waves) or V rows (dS-waves) of the lane's key, as B operands
   f16x8 frag[NS];
@@ -107,30 +110,35 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     const int64_t plane = hbase + hj;
     tc.issue(make_rsrc(p.qr + plane * p.Lp * D, plane_bytes), q0, nb, wave);
     tc.issue(make_rsrc(p.dor + plane * p.Lp * D, plane_bytes), q0, nb + TB, wave);
-    if (wave == 0) words_load_async(p.lse2 + plane * p.Lp + q0, nb + 2 * TB, lane, 64);
-    else if (wave == 1) words_load_async(p.dsc + plane * p.Lp + q0, nb + 2 * TB + 256, lane, 64);
+    // lse2 (wave 0) and delta (wave 1) of the stage's 64 query slots
+    if (wave < 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc((wave == 0 ? p.lse2 : p.dsc) + plane * p.Lp, (uint32_t)p.Lp * 4),
+                                               (OPR_LDS void *)(nb + 2 * TB + 256 * wave), 4, 4 * lane, 4 * q0, 0, 0);
   };
 
-  // P-wave stage: S^T = K' Q'^T (keys x queries) per 32-query sub-block,
-  // P = exp2(S * scale * log2 e - lse2) masked by the key's runs, published to
-  // LDS as fp16(P * 2^kPdvExp) for the dS-wave, and dV^T += dO^T P^T.
-  auto p_stage = [&](uint2 desc, char *buf) {
-    const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
-    if ((c0 | c1) == 0) return;
+  // P-wave element work of a stage: S^T = K' Q'^T (keys x queries) per
+  // 32-query sub-block, P = exp2(S * scale * log2 e - lse2) masked by the
+  // key's runs, as fp16(P * 2^kPdvExp) (lse2 carries the -kPdvExp) into op and
+  // into LDS for the dS-wave.  The update that follows is dV^T += dO^T P^T.
+  auto p_elem = [&](uint2 desc, const char *buf, char *pout, f16x8 (&op)[2][2]) {
     const int q0 = (int)(desc.x & 0xFFFFFFu);
-    const char *Qt = buf, *dOt = buf + TB;
+    const char *Qt = buf;
     const float *lse2s = reinterpret_cast<const float *>(buf + 2 * TB);
-    char *Pw = buf + 2 * TB + 512 + w * PSTRIDE;
+    char *Pw = pout + w * PSTRIDE;
     const uint64_t mq = (range_bits(iv.x, iv.y, q0) | range_bits(iv.z, iv.w, q0)) >> (8 * g);
+    // both products first, then both element blocks
+    f32x16 s[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f16x8 qf[NS];
 #pragma unroll
       for (int st = 0; st < NS; ++st) qf[st] = lds_f16x8(Qt + qb * 32 * RB + of.row8[st]);
-      f32x16 s = zero_f32x16();
+      s[qb] = zero_f32x16();
 #pragma unroll
-      for (int st = 0; st < NS; ++st) s = mfma32x32x16(qf[st], frag[st], s);
-      f16x8 pb[2];
+      for (int st = 0; st < NS; ++st) s[qb] = mfma32x32x16(qf[st], frag[st], s[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int qbase = 32 * qb + 16 * hh + 8 * g;  // query rows of registers 8hh .. 8hh+7
@@ -139,32 +147,22 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
         const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int rr = 8 * hh + e;
-          const float sm = mask_select(mq, 32 * qb + 16 * hh + e, s[rr]);
-          pb[hh][e] = (_Float16)(__builtin_amdgcn_exp2f(fmaf(sm, fs, -lv[e])) * pdv);
+          const float sm = mask_select(mq, 32 * qb + 16 * hh + e, s[qb][8 * hh + e]);
+          op[qb][hh][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sm, fs, -lv[e]));
         }
-        *reinterpret_cast<f16x8 *>(Pw + (2 * qb + hh) * 1024 + lane * 16) = pb[hh];
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          acc[db] = mfma32x32x16(tile_col8<D>(dOt, of, 32 * qb + 16 * hh, db), pb[hh], acc[db]);
+        *reinterpret_cast<f16x8 *>(Pw + (2 * qb + hh) * 1024 + lane * 16) = op[qb][hh];
       }
     }
   };
 
-  // dS-wave stage (one stage behind): dP^T = V dO^T, dS = P * (dP - delta)
-  // with P read back from the P-wave of the same key block, dK^T += Q'^T dS^T.
-  // Masked entries have P = 0 and so dS = 0.
-  auto ds_stage = [&](uint2 desc, const char *buf) {
-    const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
-    if ((c0 | c1) == 0) return;
-    const char *Qt = buf, *dOt = buf + TB;
+  // dS-wave element work of a stage (one stage behind): dP^T = V dO^T and
+  // dS = P * (dP - delta) into op, with P read back from the P-wave of the same
+  // key block (masked entries have P = 0 and so dS = 0).  The update that
+  // follows is dK^T += Q'^T dS^T.
+  auto ds_elem = [&](const char *buf, const char *pin, f16x8 (&op)[2][2]) {
+    const char *dOt = buf + TB;
     const float *dscs = reinterpret_cast<const float *>(buf + 2 * TB + 256);
-    const char *Pw = buf + 2 * TB + 512 + w * PSTRIDE;
-    // both products first, then both element blocks, then both updates: the
-    // element work falls where the P-wave on the same SIMD runs products
+    const char *Pw = pin + w * PSTRIDE;
     f32x16 dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -175,7 +173,6 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
 #pragma unroll
       for (int st = 0; st < NS; ++st) dp[qb] = mfma32x32x16(df[st], frag[st], dp[qb]);
     }
-    f16x8 dsb[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -187,21 +184,44 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
         const float dvv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int rr = 8 * hh + e;
           // P * 2^kPdvExp times (dP * 2^-kDsShift - delta) * 2^-kPdvExp
-          dsb[qb][hh][e] = (_Float16)((float)pv[e] * fmaf(dp[qb][rr], dss, -dvv[e] * dsc_unit));
+          op[qb][hh][e] = (_Float16)((float)pv[e] * fmaf(dp[qb][8 * hh + e], dss, -dvv[e]));
         }
       }
     }
+  };
+
+  // Step i of a wave: the P-wave runs stage i (buf[i % 3] -> pbf[i % 3]) and
+  // updates dV^T with dO^T; the dS-wave runs stage i - 1 (buf[(i - 1) % 3],
+  // pbf[(i - 1) % 3]) and updates dK^T with Q'^T; a wave whose key block sees
+  // no query of the stage skips it.  Both roles share the accumulator update
+  // (one copy of the code, so the accumulators stay in place across the role
+  // branch).
+  auto wave_step = [&](int i, int ns, const char *ba, const char *bb, char *pa, const char *pr) {
+    if (pwave ? i >= ns : i < 1) return;
+    const uint2 desc = uniform(stages[pwave ? i : i - 1]);
+    if (((desc.y >> (4 * w)) & 15u) == 0) return;
+    f16x8 op[2][2];
+    const char *T;
+    if (pwave) {
+      p_elem(desc, ba, pa, op);
+      T = ba + TB;
+    } else {
+      ds_elem(bb, pr, op);
+      T = bb;
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          acc[db] = mfma32x32x16(tile_col8<D>(Qt, of, 32 * qb + 16 * hh, db), dsb[qb][hh], acc[db]);
+          acc[db] = mfma32x32x16(tile_col8<D>(T, of, 32 * qb + 16 * hh, db), op[qb][hh], acc[db]);
       }
     }
+    sched_lds_reads_ahead<4 * NDB, kReadsAhead>();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   int64_t fnext = 0;
@@ -221,21 +241,17 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     fnext = uniform(sh_next);
     if (ns == 0) continue;
     issue(uniform(stages[0].x), buf0);
-    // step i: P-waves run stage i from buf[i % 3], dS-waves stage i - 1 from
-    // buf[(i - 1) % 3], stage i + 1 streams into buf[(i + 1) % 3]
-    auto step = [&](int i, char *ba, const char *bb, char *bl) {
+    // step i: stage i + 1 streams into buf[(i + 1) % 3] while the waves run
+    // their stages (wave_step)
+    auto step = [&](int i, const char *ba, const char *bb, char *bl, char *pa, const char *pr) {
       wait_all_and_barrier();
       if (i + 1 < ns) issue(uniform((int)stages[i + 1].x), bl);
-      if (pwave) {
-        if (i < ns) p_stage(uniform(stages[i]), ba);
-      } else if (i >= 1) {
-        ds_stage(uniform(stages[i - 1]), bb);
-      }
+      wave_step(i, ns, ba, bb, pa, pr);
     };
     for (int i = 0; i <= ns; i += 3) {
-      step(i, buf0, buf2, buf1);
-      if (i + 1 <= ns) step(i + 1, buf1, buf0, buf2);
-      if (i + 2 <= ns) step(i + 2, buf2, buf1, buf0);
+      step(i, buf0, buf2, buf1, pbf0, pbf2);
+      if (i + 1 <= ns) step(i + 1, buf1, buf0, buf2, pbf1, pbf0);
+      if (i + 2 <= ns) step(i + 2, buf2, buf1, buf0, pbf2, pbf1);
     }
   }
 

@@ -47,6 +47,10 @@ constexpr int kExpMin = -32, kExpMax = 32;
 // dS is stored shifted down by 2^kDsShift on top of the units of dP
 // (|v|, |dout| < 2^15 after scaling, so |dP| < 2^37 and |dS| < 2^15).
 constexpr int kDsShift = 22;
+// The backward kernels recompute P (<= 1) for dV as fp16(P * 2^kPdvExp); the
+// stored lse2 and delta carry that factor (lse2 - kPdvExp, delta * 2^-kPdvExp)
+// so that the per-element products need no extra scaling.
+constexpr int kPdvExp = 15;
 // Softmax: the running maximum is only raised when a new score exceeds it by
 // more than kMaxSlack (log2 units); probabilities are stored as
 // fp16(p * 2^kPExp) with p <= 2^kMaxSlack, i.e. at most 2^15.
@@ -241,10 +245,21 @@ struct TileCopy {
   }
 };
 
-// Asynchronous copy of n_words (<= 64) consecutive 4-byte words.
-__device__ __forceinline__ void words_load_async(const void *src, char *lds, int lane, int n_words) {
-  const char *g = static_cast<const char *>(src);
-  if (lane < n_words) __builtin_amdgcn_global_load_lds(g + 4 * lane, (OPR_LDS void *)lds, 4, 0, 0);
+// Scheduling of a run of N matrix instructions that each take one operand
+// from two LDS reads (the scheduling region ends here): the reads of the
+// first AHEAD products go first, then every product is followed by the reads
+// of the product AHEAD places later, so that LDS latency hides behind the
+// matrix core instead of one wait per product.
+template <int N, int AHEAD>
+__device__ __forceinline__ void sched_lds_reads_ahead() {
+  constexpr int kMfma = 0x008, kDsRead = 0x100;  // instruction classes of the scheduler
+  __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * AHEAD, 0);
+#pragma unroll
+  for (int j = 0; j < N - AHEAD; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
 }
 
 // Wait for this thread's outstanding memory operations (including the
@@ -357,7 +372,8 @@ struct AttnParams {
   // plane maxima (float bits) [B][H] of q', k', v, dout
   const uint32_t *mq, *mk, *mv, *mdo;
   const float *dsc, *lse2;     // [B][Hq][Lp]: rowsum(dout*o) in the units of dP shifted by
-                               // 2^-kDsShift; log2-domain lse (+inf where no key)
+                               // 2^-(kDsShift + kPdvExp); log2-domain lse minus kPdvExp
+                               // (+inf where no key)
 };
 
 }  // namespace opr

@@ -57,8 +57,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
     qb[s] = ld_f16x8(p.qr + hq_row * D + 16 * s + 8 * g);
     dob[s] = ld_f16x8(p.dor + hq_row * D + 16 * s + 8 * g);
   }
-  const float lse2_q = p.lse2[hq_row];
-  const float dsc_q = p.dsc[hq_row];
+  const float lse2_q = p.lse2[hq_row] + (float)kPdvExp;
+  const float dsc_q = ldexpf(p.dsc[hq_row], kPdvExp);
   // key slots this query sees: [iv.x, iv.y) and [iv.z, iv.w)
   const int4 iv = q < p.L ? p.qiv[(int64_t)b * p.L + q] : make_int4(0, 0, 0, 0);
   OperandOffsets<D> of;

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_
 // Backward preprocessing, before dout is packed: per slot s and q head, with
 // t = slot_tok[s] the token there,
 //   dsc[b][h][s]  = sum_d dout * o of token t (float32 over bf16 inputs),
-//   lse2[b][h][s] = lse * log2(e), +inf where the row has no key (lse = -inf)
+//   lse2[b][h][s] = lse * log2(e) - kPdvExp, +inf where the row has no key (lse = -inf)
 //                   or s >= L, so that recomputed probabilities are exactly 0;
 // and the largest |dout| of each (row, head) plane into mdo (float bits).
 // One wave per slot: D/8 lanes read one head's 16-byte chunks, so a wave
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_
         float l2 = INFINITY;
         if (t < L) {
           const float l = lse[((int64_t)b * Hq + h) * L + t];
-          l2 = (l == -INFINITY) ? INFINITY : l * kLog2e;
+          l2 = (l == -INFINITY) ? INFINITY : l * kLog2e - (float)kPdvExp;
         }
         const int64_t out = ((int64_t)b * Hq + h) * Lp + sl;
         dsc[out] = acc;
@@ -222,8 +222,9 @@ __global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_
       if (hmax[i]) atomicMax(mdo + b * Hq + i, hmax[i]);
 }
 
-// dsc *= 2^(e_dout + e_v - kDsShift): delta in the units of dP = dO V^T on the
-// scaled operands, shifted like dS.  One thread per (b, h, t).
+// dsc *= 2^(e_dout + e_v - kDsShift - kPdvExp): delta in the units of dP = dO V^T
+// on the scaled operands, shifted like dS, times the 2^-kPdvExp that the
+// fp16(P * 2^kPdvExp) of the dK/dV kernel cancels.  One thread per (b, h, t).
 __global__ __launch_bounds__(256) void scale_delta_kernel(int32_t B, int32_t Lp, int32_t Hq, int32_t group,
                                                           const uint32_t *mdo, const uint32_t *mv, float *dsc) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(256) void scale_delta_kernel(int32_t B, int32_t Lp,
   const int h = (int)(bh % Hq);
   const int64_t b = bh / Hq;
   const int kv = h / group, Hkv = Hq / group;
-  const int e = group_exponent(mdo + b * Hq + kv * group, group) + plane_exponent(mv[b * Hkv + kv]) - kDsShift;
+  const int e = group_exponent(mdo + b * Hq + kv * group, group) + plane_exponent(mv[b * Hkv + kv]) - kDsShift - kPdvExp;
   dsc[gid] = ldexpf(dsc[gid], e);
 }
 
