@@ -118,14 +118,13 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
 
   // P-wave element work of a stage: S^T = K' Q'^T (keys x queries) per
   // 32-query sub-block, P = exp2(S * scale * log2 e - lse2) masked by the
-  // key's runs, as fp16(P * 2^kPdvExp) (lse2 carries the -kPdvExp) into op and
+  // key's runs (unless both sub-blocks are full), as fp16(P * 2^kPdvExp) (lse2 carries the -kPdvExp) into op and
   // into LDS for the dS-wave.  The update that follows is dV^T += dO^T P^T.
   auto p_elem = [&](uint2 desc, const char *buf, char *pout, f16x8 (&op)[2][2]) {
     const int q0 = (int)(desc.x & 0xFFFFFFu);
     const char *Qt = buf;
     const float *lse2s = reinterpret_cast<const float *>(buf + 2 * TB);
     char *Pw = pout + w * PSTRIDE;
-    const uint64_t mq = (range_bits(iv.x, iv.y, q0) | range_bits(iv.z, iv.w, q0)) >> (8 * g);
     // both products first, then both element blocks
     f32x16 s[2];
 #pragma unroll
@@ -137,6 +136,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
 #pragma unroll
       for (int st = 0; st < NS; ++st) s[qb] = mfma32x32x16(qf[st], frag[st], s[qb]);
     }
+    if (((desc.y >> (4 * w)) & 15u) != 10u) {  // a sub-block is not full: mask by the key's runs
+      const uint64_t mq = (range_bits(iv.x, iv.y, q0) | range_bits(iv.z, iv.w, q0)) >> (8 * g);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][r] = mask_select(mq, 32 * qb + 16 * (r >> 3) + (r & 7), s[qb][r]);
+      }
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -147,8 +154,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
         const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float sm = mask_select(mq, 32 * qb + 16 * hh + e, s[qb][8 * hh + e]);
-          op[qb][hh][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sm, fs, -lv[e]));
+          op[qb][hh][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * hh + e], fs, -lv[e]));
         }
         *reinterpret_cast<f16x8 *>(Pw + (2 * qb + hh) * 1024 + lane * 16) = op[qb][hh];
       }

@@ -246,18 +246,18 @@ struct TileCopy {
 };
 
 // Scheduling of a run of N matrix instructions that each take one operand
-// from two LDS reads (the scheduling region ends here): the reads of the
+// from READS LDS reads (the scheduling region ends here): the reads of the
 // first AHEAD products go first, then every product is followed by the reads
 // of the product AHEAD places later, so that LDS latency hides behind the
 // matrix core instead of one wait per product.
-template <int N, int AHEAD>
+template <int N, int AHEAD, int READS = 2>
 __device__ __forceinline__ void sched_lds_reads_ahead() {
   constexpr int kMfma = 0x008, kDsRead = 0x100;  // instruction classes of the scheduler
-  __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * AHEAD, 0);
+  __builtin_amdgcn_sched_group_barrier(kDsRead, READS * AHEAD, 0);
 #pragma unroll
   for (int j = 0; j < N - AHEAD; ++j) {
     __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, READS, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
 }

@@ -21,6 +21,8 @@
 namespace opr {
 namespace {
 
+constexpr int kReadsAhead = 4;  // S / dP products whose K' / V operand reads are in flight
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq) {
   constexpr int NS = D / 16;
@@ -116,6 +118,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
         s[kb] = zero_f32x16();
         dpt[kb] = zero_f32x16();
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
 #pragma unroll
@@ -124,6 +127,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
           dpt[kb] = mfma32x32x16(lds_f16x8(Vt + kb * 32 * RB + of.row8[st]), dob[st], dpt[kb]);
         }
       }
+      sched_lds_reads_ahead<4 * NS, kReadsAhead, 1>();
+      __builtin_amdgcn_sched_barrier(0);
       if (c0 != 2 || c1 != 2) {
         const uint64_t mk = (range_bits(iv.x, iv.y, k0) | range_bits(iv.z, iv.w, k0)) >> (8 * g);
 #pragma unroll

@@ -27,6 +27,8 @@
 namespace opr {
 namespace {
 
+constexpr int kReadsAhead = 4;  // S products whose K' operand reads are in flight
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t *o, float *lse) {
   constexpr int NS = D / 16;   // MFMA k-steps over the head dim
@@ -116,12 +118,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) s[kb] = zero_f32x16();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           s[kb] = mfma32x32x16(lds_f16x8(Kt + kb * 32 * RB + of.row8[st]), qb[st], s[kb]);
       }
+      sched_lds_reads_ahead<2 * NS, kReadsAhead, 1>();
+      __builtin_amdgcn_sched_barrier(0);
       if (c0 != 2 || c1 != 2) {
         uint64_t mk = range_bits(iv.x, iv.y, k0) | range_bits(iv.z, iv.w, k0);
         mk >>= 8 * g;  // lane group g holds keys 16h + 8g + 0..7 of each 32-key block
