@@ -188,10 +188,16 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
         const float4 d0 = *reinterpret_cast<const float4 *>(dscs + qbase);
         const float4 d1 = *reinterpret_cast<const float4 *>(dscs + qbase + 4);
         const float dvv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        // P * 2^kPdvExp times (dP * 2^-kDsShift - delta) * 2^-kPdvExp: the
+        // second factor in fp32, then both multiplied as packed fp16 pairs
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // P * 2^kPdvExp times (dP * 2^-kDsShift - delta) * 2^-kPdvExp
-          op[qb][hh][e] = (_Float16)((float)pv[e] * fmaf(dp[qb][8 * hh + e], dss, -dvv[e]));
+        for (int e = 0; e < 8; e += 2) {
+          const f16x2 t = {(_Float16)fmaf(dp[qb][8 * hh + e], dss, -dvv[e]),
+                           (_Float16)fmaf(dp[qb][8 * hh + e + 1], dss, -dvv[e + 1])};
+          const f16x2 pp = {pv[e], pv[e + 1]};
+          const f16x2 d = t * pp;
+          op[qb][hh][e] = d[0];
+          op[qb][hh][e + 1] = d[1];
         }
       }
     }
