@@ -104,21 +104,6 @@ __device__ __forceinline__ constexpr int acc_dim(int db, int r, int g) {
   return 32 * db + 8 * (r >> 2) + 4 * g + (r & 3);
 }
 
-// Part k (0..3) of an f32x16 register block viewed as four f16x8 (a carry of
-// fp16 operands in registers sized for one accumulator).
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-__device__ __forceinline__ f16x8 f16x8_part(const f32x16 &v, int k) {
-  const f32x4 x = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
-  return __builtin_bit_cast(f16x8, x);
-}
-__device__ __forceinline__ void set_f16x8_part(f32x16 &v, int k, const f16x8 &h) {
-  const f32x4 x = __builtin_bit_cast(f32x4, h);
-  v[4 * k] = x[0];
-  v[4 * k + 1] = x[1];
-  v[4 * k + 2] = x[2];
-  v[4 * k + 3] = x[3];
-}
-
 __device__ __forceinline__ f16x8 ld_f16x8(const uint16_t *p) {
   return *reinterpret_cast<const f16x8 *>(p);
 }
@@ -277,24 +262,6 @@ __device__ __forceinline__ void sched_lds_reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
 }
 
-// Interleaving of a run of N matrix instructions with the vector work that
-// does not depend on them: after each product, up to R LDS reads, V vector
-// ALU instructions and W LDS writes.  The matrix core runs a product for 32
-// cycles (8 passes) while the SIMD issues the other wave-instructions, so
-// element-wise work placed between independent products costs little;
-// grouped after them it adds to the products' time.
-template <int N, int R, int V, int W = 0>
-__device__ __forceinline__ void sched_interleave() {
-  constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100, kDsWrite = 0x200;
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
-    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(kValu, V, 0);
-    if constexpr (W > 0) __builtin_amdgcn_sched_group_barrier(kDsWrite, W, 0);
-  }
-}
-
 // Wait for this thread's outstanding memory operations (including the
 // asynchronous LDS fills), then for the whole workgroup.
 __device__ __forceinline__ void wait_all_and_barrier() {
@@ -324,11 +291,6 @@ struct OperandOffsets {
   static constexpr int NS = D / 16, NDB = D / 32;
   int row8[NS];
   int col8[NDB][2];
-  // row8[st] from row8[0] alone: the swizzle flips only the 16-byte chunk
-  // bits of a row, and chunk 2 st + g differs from chunk g by st in the bits
-  // above the lowest, so row8[st] = row8[0] ^ 32 st (one register instead of
-  // NS, at one XOR per read).
-  __device__ __forceinline__ int row8x(int st) const { return row8[0] ^ (32 * st); }
   __device__ __forceinline__ void init(int lane) {
     const int g = lane >> 5, li = lane & 31, G = lane >> 4, j = lane & 15;
 #pragma unroll
