@@ -209,6 +209,38 @@ class Runner:
         return s.elapsed_time(e) / steps
 
 
+def loss_step(torch, Bd, r, shape, steps, dev):
+    """opr_token_ce on the forward's output: per-token loss of a V = 32 head on
+    the t and r_out rows and its gradient (the loss step of training); bound
+    by HBM: it reads o once and writes dout once."""
+    B, L, F, V = shape.B, shape.L, shape.Hq * shape.D, 32
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    w = (torch.randn((V, F), generator=g, device=dev) / math.sqrt(F)).to(torch.bfloat16)
+    labels = torch.randint(0, V, (B, L), generator=g, device=dev, dtype=torch.int32)
+    ws = torch.empty(Bd.opr_token_ce_workspace_size(F, V), dtype=torch.uint8, device=dev)
+    loss = torch.empty((B, L), dtype=torch.float32, device=dev)
+    dout = torch.empty_like(r.o)
+    for _ in range(3):
+        Bd.opr_token_ce(r.o, w, labels, r.lay, 1.0, workspace=ws, out=(loss, dout))
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        Bd.opr_token_ce(r.o, w, labels, r.lay, 1.0, workspace=ws, out=(loss, dout))
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    scored = int(((r.lay.tok_type == 1) | (r.lay.tok_type == 3)).sum().item())
+    # algorithmic bytes: o read and dout written (bf16), labels and types read, loss written,
+    # W read and its transpose written
+    nbytes = B * L * F * 2 * 2 + B * L * (4 + 1 + 4) + V * F * 2 * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "token_ce", "ms": round(ms, 4), "rows": B * L, "scored_rows": scored, "F": F, "V": V,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+
+
 def cpu_baseline(rows, L, shape, t_np):
     """The fp64 oracle on a bounded sample: one conversation, one kv group."""
     from oracle import opr_oracle as O
@@ -379,6 +411,8 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
     }
+    result["loss_step"] = loss_step(torch, Bd, r, shape, args.steps, dev)
+    log(f"loss step {result['loss_step']['ms']:.4f} ms, {result['loss_step']['roofline']['achieved']} GB/s")
     del r
     torch.cuda.empty_cache()
     if not args.no_sweep:

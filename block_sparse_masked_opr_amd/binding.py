@@ -69,6 +69,10 @@ def _load() -> ctypes.CDLL:
     lib.opr_attn_bwd.argtypes = [ctypes.POINTER(OprAttnIn), vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.opr_attn_workspace_size.restype = sz
     lib.opr_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.opr_token_ce.restype = i32
+    lib.opr_token_ce.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.opr_token_ce_workspace_size.restype = sz
+    lib.opr_token_ce_workspace_size.argtypes = [i32, i32]
     lib.opr_status_string.restype = ctypes.c_char_p
     lib.opr_status_string.argtypes = [i32]
     return lib
@@ -77,7 +81,8 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 EXPORTED = ("opr_build_layout", "opr_build_layout_workspace_size", "opr_attn_fwd",
-            "opr_attn_bwd", "opr_attn_workspace_size", "opr_status_string")
+            "opr_attn_bwd", "opr_attn_workspace_size", "opr_token_ce", "opr_token_ce_workspace_size",
+            "opr_status_string")
 
 
 def opr_status_string(status: int) -> str:
@@ -229,3 +234,43 @@ def opr_attn_bwd(q, k, v, o, lse, dout, lay: Layout, theta: float = 1.0e6, scale
                           workspace.numel(), _stream(q.device))
     _check(st, "opr_attn_bwd")
     return dq, dk, dv
+
+
+def opr_token_ce_workspace_size(F: int, V: int) -> int:
+    return int(LIB.opr_token_ce_workspace_size(F, V))
+
+
+def opr_token_ce(o: torch.Tensor, w: torch.Tensor, labels: torch.Tensor, lay: Layout,
+                 grad_scale: float = 1.0, with_grad: bool = True,
+                 workspace: Optional[torch.Tensor] = None, out=None):
+    """Per-token loss of the head w (bf16 [V, F]) on o (bf16 [B, L, Hq, D] or
+    [B, L, F]) at int32 labels [B, L]; scored rows are the layout's t and
+    r_out tokens.  Returns (loss fp32 [B, L], dout bf16 shaped like o, or None
+    without the gradient)."""
+    B, L = o.shape[0], o.shape[1]
+    F = o[0, 0].numel()
+    V = w.shape[0]
+    if o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("o must be contiguous bfloat16")
+    if w.dtype != torch.bfloat16 or not w.is_contiguous() or w.dim() != 2 or w.shape[1] != F:
+        raise ValueError("w must be contiguous bfloat16 [V, F]")
+    if labels.dtype != torch.int32 or not labels.is_contiguous() or tuple(labels.shape) != (B, L):
+        raise ValueError("labels must be contiguous int32 [B, L]")
+    if (lay.B, lay.L) != (B, L):
+        raise ValueError("layout and o disagree on B, L")
+    if out is None:
+        loss = torch.empty((B, L), dtype=torch.float32, device=o.device)
+        dout = torch.empty_like(o) if with_grad else None
+    else:
+        loss, dout = out
+    ws_ptr, ws_n = None, 0
+    if dout is not None:
+        need = opr_token_ce_workspace_size(F, V)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=o.device)
+        ws_ptr, ws_n = workspace.data_ptr(), workspace.numel()
+    st = LIB.opr_token_ce(B, L, F, V, o.data_ptr(), w.data_ptr(), labels.data_ptr(),
+                          lay.tok_type.data_ptr(), float(grad_scale), loss.data_ptr(),
+                          None if dout is None else dout.data_ptr(), ws_ptr, ws_n, _stream(o.device))
+    _check(st, "opr_token_ce")
+    return loss, dout

@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libopr.so")
 ARCH = "gfx950"
 
-SOURCES = ["opr_api.cpp", "layout.hip", "attn_prologue.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_dq.hip"]
+SOURCES = ["opr_api.cpp", "layout.hip", "attn_prologue.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_dq.hip",
+           "token_ce.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

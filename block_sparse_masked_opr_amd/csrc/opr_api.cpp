@@ -23,6 +23,10 @@ hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, f
                                   const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq, float *dk,
                                    float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev);
+size_t token_ce_ws_bytes(int32_t F, int32_t V);
+hipError_t launch_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const void *o, const void *w,
+                           const int32_t *labels, const uint8_t *tok_type, float grad_scale, float *loss,
+                           void *dout, void *workspace, hipStream_t s);
 
 static bool valid_block(int32_t b) { return b == 32 || b == 64 || b == 128; }
 
@@ -266,6 +270,32 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   launch_scale_delta(*in, ws, stream);
   if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream,
                               in->timing_events ? in->timing_events + 1 : nullptr) != hipSuccess)
+    return OPR_E_HIP;
+  return hip_status();
+}
+
+size_t opr_token_ce_workspace_size(int32_t F, int32_t V) {
+  if (F < 64 || F % 64 != 0 || F > (1 << 20)) return 0;
+  if (V != 32 && V != 64 && V != 128) return 0;
+  return token_ce_ws_bytes(F, V);
+}
+
+opr_status opr_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const void *o, const void *w,
+                        const int32_t *labels, const uint8_t *tok_type, float grad_scale, float *loss,
+                        void *dout, void *workspace, size_t ws_bytes, hipStream_t stream) {
+  if (B < 1 || L < 1) return OPR_E_INVALID;
+  if ((int64_t)B * L >= (int64_t)1 << 31) return OPR_E_UNSUPPORTED;
+  if (F < 64 || F % 64 != 0 || F > (1 << 20)) return OPR_E_UNSUPPORTED;
+  if (V != 32 && V != 64 && V != 128) return OPR_E_UNSUPPORTED;
+  if (!o || !w || !labels || !tok_type || !loss) return OPR_E_INVALID;
+  if (!aligned16(o) || !aligned16(w) || (dout && !aligned16(dout))) return OPR_E_INVALID;
+  if (!isfinite(grad_scale)) return OPR_E_INVALID;
+  if (dout && (!workspace || ws_bytes < token_ce_ws_bytes(F, V))) {
+    if (!workspace) return OPR_E_INVALID;
+    return OPR_E_CAPACITY;
+  }
+  if (launch_token_ce(B, L, F, V, o, w, labels, tok_type, grad_scale, loss, dout, workspace, stream) !=
+      hipSuccess)
     return OPR_E_HIP;
   return hip_status();
 }

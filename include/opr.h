@@ -219,6 +219,50 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse,
 size_t opr_attn_workspace_size(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D,
                                int is_bwd);
 
+/*
+ * opr_token_ce - per-token cross entropy of a linear head on the attention
+ * output, and its gradient: the loss step that follows opr_attn_fwd and
+ * feeds opr_attn_bwd.
+ *
+ * The pages state that one pass gives every token the same loss as the N
+ * separate passes (wiki summary, section "理论保证", Theorem 2.1).  The
+ * scored rows are the tokens of type OPR_TOK_T and OPR_TOK_ROUT: the
+ * reasoning and the generation copy of each response (section "Token 复制":
+ * the generation copy is the one in the loss; the context copy r_in and the
+ * human messages are context only).  For a scored row p, with o_p its
+ * F = Hq * D attention outputs in the order o stores them and W the head:
+ *     z_p       = W o_p                       (V logits, fp32)
+ *     loss[p]   = logsumexp(z_p) - z_p[labels[p]]
+ *     dout[p]   = grad_scale * (softmax(z_p) - onehot(labels[p]))^T W
+ * Every other row gets loss 0 and dout 0.  Logits are bf16 products with
+ * fp32 accumulation; dout is rounded to bf16 once.
+ *
+ *  B, L        rows and tokens per row of the layout; B*L < 2^31.
+ *  F, V        features per token (F % 64 == 0, 64 <= F <= 2^20) and logits
+ *              (V in {32, 64, 128}).
+ *  o           bf16 [B][L][F] (opr_attn_fwd's o with F = Hq * D); 16-byte aligned.
+ *  w           bf16 [V][F], one row of weights per logit (the layout of a
+ *              linear layer's weight); 16-byte aligned.
+ *  labels      int32 [B][L]; read on scored rows only.  A label outside
+ *              [0, V) gives that row loss NaN and dout 0.
+ *  tok_type    uint8 [B][L], the layout's tok_type.
+ *  grad_scale  factor on dout (1 for the gradient of the summed loss).
+ *  loss        fp32 [B][L], every element written.
+ *  dout        bf16 [B][L][F], every element written, or NULL to skip the
+ *              gradient; 16-byte aligned.
+ *  workspace   device, >= opr_token_ce_workspace_size(F, V) bytes when dout
+ *              is not NULL (it receives W transposed); may be NULL otherwise.
+ * Errors: OPR_E_INVALID (null or misaligned pointer, B/L, non-finite
+ * grad_scale), OPR_E_UNSUPPORTED (F, V, B*L), OPR_E_CAPACITY (ws_bytes),
+ * OPR_E_HIP.
+ */
+opr_status opr_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const void *o, const void *w,
+                        const int32_t *labels, const uint8_t *tok_type, float grad_scale, float *loss,
+                        void *dout, void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for opr_token_ce with a gradient; 0 if F or V is invalid. */
+size_t opr_token_ce_workspace_size(int32_t F, int32_t V);
+
 /* Static, human-readable name of a status code. */
 const char *opr_status_string(opr_status status);
 

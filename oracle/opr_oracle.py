@@ -554,3 +554,16 @@ def loss_rows_1pass(lay, b: int) -> np.ndarray:
     the reasoning is generated text too, so both are scored."""
     typ = lay["type"][b]
     return np.nonzero((typ == T) | (typ == ROUT))[0]
+
+
+def token_ce_grad(feats: np.ndarray, W: np.ndarray, labels: np.ndarray) -> np.ndarray:
+    """Gradient of sum_p token_ce(feats, W, labels)[p] with respect to feats.
+
+    For logits z = feats @ W, d/dz of (logsumexp(z) - z[y]) is softmax(z) minus
+    the one-hot vector of y, so the gradient is (softmax(z) - onehot(y)) @ W^T,
+    row by row."""
+    z = _f64(feats) @ _f64(W)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    p[np.arange(len(labels)), labels] -= 1.0
+    return p @ _f64(W).T

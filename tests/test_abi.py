@@ -30,7 +30,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(Bd):
     names = declared_entry_points()
-    assert len(names) == 6, names
+    assert len(names) == 8, names
     lib = ctypes.CDLL(Bd._LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -136,3 +136,32 @@ def test_attn_workspace_size(Bd):
     assert 0 < f < b
     assert Bd.opr_attn_workspace_size(1, 100, 3, 2, 128, False) == 0
     assert Bd.opr_attn_workspace_size(1, 100, 4, 2, 80, True) == 0
+
+
+def _ce(Bd, B=2, L=64, F=4096, V=32, o=FAKE, w=FAKE, labels=FAKE, typ=FAKE, gs=1.0, loss=FAKE,
+        dout=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return Bd.LIB.opr_token_ce(B, L, F, V, o, w, labels, typ, gs, loss, dout, ws, ws_bytes, None)
+
+
+def test_token_ce_errors(Bd):
+    assert _ce(Bd, B=0) == Bd.OPR_E_INVALID
+    assert _ce(Bd, L=0) == Bd.OPR_E_INVALID
+    assert _ce(Bd, F=96) == Bd.OPR_E_UNSUPPORTED       # F % 64 != 0
+    assert _ce(Bd, F=0) == Bd.OPR_E_UNSUPPORTED
+    assert _ce(Bd, V=48) == Bd.OPR_E_UNSUPPORTED
+    assert _ce(Bd, V=256) == Bd.OPR_E_UNSUPPORTED
+    for arg in ("o", "w", "labels", "typ", "loss"):
+        assert _ce(Bd, **{arg: None}) == Bd.OPR_E_INVALID
+    assert _ce(Bd, o=FAKE + 8) == Bd.OPR_E_INVALID      # 16-byte alignment
+    assert _ce(Bd, w=FAKE + 2) == Bd.OPR_E_INVALID
+    assert _ce(Bd, dout=FAKE + 4) == Bd.OPR_E_INVALID
+    assert _ce(Bd, gs=float("nan")) == Bd.OPR_E_INVALID
+    assert _ce(Bd, ws=None) == Bd.OPR_E_INVALID         # the gradient needs the workspace
+    assert _ce(Bd, ws_bytes=1024) == Bd.OPR_E_CAPACITY
+    assert _ce(Bd, B=1 << 16, L=1 << 15) == Bd.OPR_E_UNSUPPORTED
+
+
+def test_token_ce_workspace_size(Bd):
+    assert Bd.opr_token_ce_workspace_size(4096, 32) >= 4096 * 32 * 2
+    assert Bd.opr_token_ce_workspace_size(4000, 32) == 0
+    assert Bd.opr_token_ce_workspace_size(4096, 40) == 0

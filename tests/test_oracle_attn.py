@@ -302,3 +302,46 @@ def test_kpass_with_k_equal_n_reproduces_npass_rows():
             rows_c = np.nonzero((lay["type"][0] == y) & (lay["turn"][0] == i))[0]
             rows_n = np.nonzero((passes[i]["role"] == y) & (full["turn"][0, passes[i]["idx"]] == i))[0]
             np.testing.assert_allclose(oc[0, rows_c], on[rows_n], atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# per-token loss: gradient pins
+# ----------------------------------------------------------------------------
+def test_token_ce_matches_definition_and_grad_finite_differences():
+    """token_ce is -log softmax(feats @ W)[label] (checked against a direct
+    evaluation of the softmax), and token_ce_grad matches central finite
+    differences of the summed loss."""
+    rng = np.random.default_rng(11)
+    n, F, V = 5, 12, 7
+    feats = rng.standard_normal((n, F))
+    W = rng.standard_normal((F, V)) * 0.5
+    labels = rng.integers(0, V, n)
+    z = feats @ W
+    ref = np.array([-np.log(np.exp(z[i, labels[i]]) / np.exp(z[i]).sum()) for i in range(n)])
+    np.testing.assert_allclose(O.token_ce(feats, W, labels), ref, atol=1e-12)
+    g = O.token_ce_grad(feats, W, labels)
+    eps = 1e-6
+    for i in range(n):
+        for f in range(F):
+            fp, fm = feats.copy(), feats.copy()
+            fp[i, f] += eps
+            fm[i, f] -= eps
+            num = (O.token_ce(fp, W, labels).sum() - O.token_ce(fm, W, labels).sum()) / (2 * eps)
+            assert abs(num - g[i, f]) < 1e-7, (i, f, num, g[i, f])
+
+
+def test_token_ce_grad_special_cases():
+    """Uniform logits: the loss is log V and the gradient is (1/V - onehot) W^T.
+    Softmax is shift-invariant, so adding the same column to every logit (a
+    shift of W by one column broadcast over V) leaves the loss unchanged."""
+    rng = np.random.default_rng(12)
+    n, F, V = 4, 6, 5
+    W = rng.standard_normal((F, V))
+    feats = np.zeros((n, F))
+    labels = np.array([0, 1, 4, 2])
+    np.testing.assert_allclose(O.token_ce(feats, W, labels), np.log(V), atol=1e-12)
+    onehot = np.eye(V)[labels]
+    np.testing.assert_allclose(O.token_ce_grad(feats, W, labels), (1.0 / V - onehot) @ W.T, atol=1e-12)
+    feats = rng.standard_normal((n, F))
+    shift = rng.standard_normal((F, 1))
+    np.testing.assert_allclose(O.token_ce(feats, W + shift, labels), O.token_ce(feats, W, labels), atol=1e-12)
