@@ -24,7 +24,9 @@
 //     8j .. 8j + 7 of a logit block are directly the B operand of a product
 //     whose 16 k values are logits 16 j + {0..3, 8..11} (lane group 0) and
 //     16 j + {4..7, 12..15} (lane group 1); A comes from W^T (transposed once
-//     into the workspace), two 8-byte reads per lane.
+//     into the workspace), two 8-byte reads per lane.  Each 64-feature group
+//     goes through LDS into row-major order, so dout is written in full
+//     128-byte row pieces.
 // The kernel is bound by HBM: it reads o once and writes dout once.
 #include "attn_common.h"
 #include "opr_internal.h"
@@ -92,6 +94,7 @@ __global__ __launch_bounds__(256) void token_ce_kernel(const uint16_t *__restric
 #pragma unroll
   for (int vb = 0; vb < NVB; ++vb) acc[vb] = zero_f32x16();
   const int ngroups = F / kGroup;
+#pragma unroll 2
   for (int G = wave; G < ngroups; G += kWaves) {
     uint4 ov[4];
 #pragma unroll
@@ -157,7 +160,11 @@ __global__ __launch_bounds__(256) void token_ce_kernel(const uint16_t *__restric
       gb[vb][r >> 3][r & 7] = (__bf16)(grad ? grad_scale * pv : 0.0f);
     }
 
-  // 3. dout^T[f][row] over this wave's feature groups, 32 features at a time
+  // 3. dout^T[f][row] over this wave's feature groups, 32 features at a time;
+  // each 64-feature group is turned into row-major bf16 in LDS (the wave's
+  // own 32 x 64 tile) and written as full 128-byte row pieces
+  __syncthreads();  // the partial-sum buffer is reused for the tiles
+  uint16_t *tile = reinterpret_cast<uint16_t *>(&red[0][0][0][0]) + wave * (kRows * kGroup);
   for (int G = wave; G < ngroups; G += kWaves) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -173,16 +180,21 @@ __global__ __launch_bounds__(256) void token_ce_kernel(const uint16_t *__restric
           const uint2 hi = *reinterpret_cast<const uint2 *>(wr + 32 * vb + 16 * j + 8);
           c = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), gb[vb][j], c);
         }
-      if (in_range) {
-        uint16_t *dr = dout + row * F + fb + 4 * g;
+      // register r holds feature fb + 8 (r / 4) + 4 g + r % 4 of row li
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          uint16_t b4[4];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint16_t b4[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) b4[e] = f32_to_bf16(c[4 * q4 + e]);
-          *reinterpret_cast<uint2 *>(dr + 8 * q4) = *reinterpret_cast<const uint2 *>(b4);
-        }
+        for (int e = 0; e < 4; ++e) b4[e] = f32_to_bf16(c[4 * q4 + e]);
+        *reinterpret_cast<uint2 *>(tile + li * kGroup + 32 * h + 8 * q4 + 4 * g) = *reinterpret_cast<const uint2 *>(b4);
       }
+    }
+    // the tile's 32 rows of 128 bytes: lane l writes 16 bytes of row 8 k + l / 8
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rr = 8 * k + (lane >> 3), c8 = (lane & 7) * 8;
+      const uint4 val = *reinterpret_cast<const uint4 *>(tile + rr * kGroup + c8);
+      if (r0 + rr < n_rows) *reinterpret_cast<uint4 *>(dout + (r0 + rr) * F + G * kGroup + c8) = val;
     }
   }
 }
