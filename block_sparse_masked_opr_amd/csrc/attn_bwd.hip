@@ -23,11 +23,17 @@
 // k_order of the prologue).  Partial sub-blocks are masked with 64-bit masks
 // built from the two runs of slots of each query or key.
 //
-// Units: q' and dout carry one exponent per (row, kv group), k' and v one per
-// (row, kv head), all constant inside a workgroup.  dP = dO V^T comes out in
-// units 2^(e_dout + e_v); delta arrives pre-scaled into those units times
-// 2^-kDsShift, and dS is formed as P * 2^-kDsShift * (dP - delta) before the
-// fp16 conversion; P for dV is stored as fp16(P * 2^kPdvExp).
+// Units: k' and v carry one exponent per (row, kv head), constant inside a
+// workgroup; q' and dout one per 64-slot tile and q head, so they change from
+// stage to stage (eq, edo of the stage; eqr, edor their minima over the kv
+// group).  The products are brought to group-wide units like this:
+//   S: the score scale is 2^-(eq + ek) per stage;
+//   dV^T += dO'^T P'^T with P' = fp16(P * 2^(kPdvExp - (edo - edor))) (the
+//       stored lse2 carries the shift), so dV is in units 2^(kPdvExp + edor);
+//   dS' = P' (dP' dss - delta') with dP' = dO' V'^T in units 2^(edo + ev),
+//       dss = 2^-(kDsShift + kPdvExp + eq - eqr) per stage and delta' stored
+//       in the matching units, so dS' = dS 2^(eqr + edor + ev - kDsShift - eq)
+//       and dK^T += Q'^T dS'^T is in units 2^(eqr + edor + ev - kDsShift).
 #include "attn_common.h"
 #include "attn_sched.h"
 #include "opr_internal.h"
@@ -74,12 +80,11 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   const int key = n * 128 + 32 * w + li;
   const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
   const int64_t hbase = (int64_t)b * p.Hq + (int64_t)kvh * p.group;  // first q head of the group
-  const int eq = group_exponent(p.mq + hbase, p.group);
-  const int edo = group_exponent(p.mdo + hbase, p.group);
+  // q' and dout scales vary by stage (one per 64-slot tile, carried in the
+  // stage descriptor); eqr, edor are their minima over the group
+  const int eqr = p.eref[2 * kvplane], edor = p.eref[2 * kvplane + 1];
   const int ek = plane_exponent(p.mk[kvplane]);
   const int ev = plane_exponent(p.mv[kvplane]);
-  const float fs = ldexpf(p.scale_log2, -(eq + ek));
-  const float dss = ldexpf(1.0f, -kDsShift - kPdvExp);
 
   // K' rows (P-waves) or V rows (dS-waves) of the lane's key, as B operands
   f16x8 frag[NS];
@@ -122,6 +127,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   // into LDS for the dS-wave.  The update that follows is dV^T += dO^T P^T.
   auto p_elem = [&](uint2 desc, const char *buf, char *pout, f16x8 (&op)[2][2]) {
     const int q0 = (int)(desc.x & 0xFFFFFFu);
+    const int eq_s = (int)((desc.y >> 16) & 0xFFu) - 64;
+    const float fs = ldexpf(p.scale_log2, -(eq_s + ek));  // raw score -> log2 units
     const char *Qt = buf;
     const float *lse2s = reinterpret_cast<const float *>(buf + 2 * TB);
     char *Pw = pout + w * PSTRIDE;
@@ -165,7 +172,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   // dS = P * (dP - delta) into op, with P read back from the P-wave of the same
   // key block (masked entries have P = 0 and so dS = 0).  The update that
   // follows is dK^T += Q'^T dS^T.
-  auto ds_elem = [&](const char *buf, const char *pin, f16x8 (&op)[2][2]) {
+  auto ds_elem = [&](uint2 desc, const char *buf, const char *pin, f16x8 (&op)[2][2]) {
+    const int eq_s = (int)((desc.y >> 16) & 0xFFu) - 64;
+    const float dss = ldexpf(1.0f, -kDsShift - kPdvExp - (eq_s - eqr));
     const char *dOt = buf + TB;
     const float *dscs = reinterpret_cast<const float *>(buf + 2 * TB + 256);
     const char *Pw = pin + w * PSTRIDE;
@@ -219,7 +228,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
       p_elem(desc, ba, pa, op);
       T = ba + TB;
     } else {
-      ds_elem(bb, pr, op);
+      ds_elem(desc, bb, pr, op);
       T = bb;
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -242,7 +251,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     __syncthreads();
     if (wave == 0) {
       int64_t f = fnext;
-      const int c = build_k_stages(lst, subs_b, p.NT, n, p.group, nnz, &f, stages, lane);
+      const int c = build_k_stages(lst, subs_b, p.NT, n, p.group, nnz, p.eqt + hbase * p.MT64,
+                                   p.edot + hbase * p.MT64, p.MT64, &f, stages, lane);
       if (lane == 0) {
         sh_count = c;
         sh_next = f;
@@ -271,9 +281,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     const int tok = p.slot_tok[(int64_t)b * p.L + key];
     const int64_t out = (((int64_t)b * p.L + tok) * p.Hkv + kvh) * D;
     if (!pwave) {
-      // dK^T in units 2^(eq + edo + ev - kDsShift), rotated back by RoPE
+      // dK^T in units 2^(eqr + edor + ev - kDsShift), rotated back by RoPE
       const float2 *cs = p.rope + ((int64_t)b * p.Lp + key) * (D / 2);
-      const float kscale = ldexpf(p.scale, kDsShift - eq - edo - ev);
+      const float kscale = ldexpf(p.scale, kDsShift - eqr - edor - ev);
 #pragma unroll
       for (int db = 0; db < HALF_DB; ++db) {
 #pragma unroll
@@ -293,8 +303,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
         }
       }
     } else {
-      // dV^T in units 2^(kPdvExp + edo)
-      const float vscale = ldexpf(1.0f, -kPdvExp - edo);
+      // dV^T in units 2^(kPdvExp + edor)
+      const float vscale = ldexpf(1.0f, -kPdvExp - edor);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll

@@ -5,9 +5,10 @@
 // 11 significant bits where bf16 keeps 8, which is what lets the summed
 // gradients of a GQA group stay within 2e-2 of the exact result.  To keep
 // bf16's range, each staged operand (q and k after RoPE, v, dout) is stored
-// as fp16(x * 2^e) with one power-of-two exponent e per row and kv head (for
-// q and dout: per row and kv group, over the group's q heads), chosen from the
-// largest magnitude (an absmax pre-pass) so that it lands in [2^14, 2^15).
+// as fp16(x * 2^e) with a power-of-two exponent e chosen from the largest
+// magnitude it covers, so that this lands in [2^14, 2^15): for k and v one
+// per (row, kv head) plane (an absmax pre-pass), for q and dout one per
+// 64-slot tile of each (row, q head) (found while the tile is converted).
 // The kernels fold the exponents back exactly: into the score scale (q, k)
 // and into the fixed units of their fp32 accumulators (v, dout), removed in
 // the epilogues.
@@ -145,14 +146,6 @@ __device__ __forceinline__ int plane_exponent(uint32_t max_abs_bits) {
   int x;
   frexpf(m, &x);
   return min(kExpMax, max(kExpMin, 15 - x));
-}
-
-// Exponent of the largest of n plane maxima (q and dout use one exponent per
-// (row, kv group): the maxima of the group's q heads).
-__device__ __forceinline__ int group_exponent(const uint32_t *pm, int n) {
-  uint32_t m = 0;
-  for (int i = 0; i < n; ++i) m = max(m, pm[i]);
-  return plane_exponent(m);
 }
 
 // Sum of the 8 fp16 values of v (fp32 accumulation).
@@ -369,11 +362,14 @@ struct AttnParams {
   const float2 *rope;          // [B][Lp][D/2] (cos, sin)
   // fp16 bits, one power-of-two scale per (row, head) plane: [B][H][Lp][D]
   const uint16_t *qr, *kr, *vr, *dor;
-  // plane maxima (float bits) [B][H] of q', k', v, dout
-  const uint32_t *mq, *mk, *mv, *mdo;
-  const float *dsc, *lse2;     // [B][Hq][Lp]: rowsum(dout*o) in the units of dP shifted by
-                               // 2^-(kDsShift + kPdvExp); log2-domain lse minus kPdvExp
-                               // (+inf where no key)
+  // plane maxima (float bits) [B][Hkv] of k', v
+  const uint32_t *mk, *mv;
+  // tile exponents [B][Hq][Lp/64] of q' and dout; their minima over the kv
+  // group, eref [B][Hkv][2] = (q, dout)
+  const int32_t *eqt, *edot, *eref;
+  int32_t MT64;                // Lp / 64
+  const float *dsc, *lse2;     // [B][Hq][Lp], see the backward units in attn_bwd.hip
+                               // (lse2 is +inf where no key)
 };
 
 }  // namespace opr

@@ -10,10 +10,10 @@
 // LDS reads.  The epilogue removes the operand units, applies the softmax
 // scale and rotates dQ back by the transposed RoPE rotation.
 //
-// Units: q' and dout carry one exponent per (row, kv group), k' and v one per
-// (row, kv head).  dP comes out in units 2^(e_dout + e_v); delta arrives
-// pre-scaled into those units times 2^-kDsShift, and dS is formed as
-// P * (dP * 2^-kDsShift - delta) before the fp16 conversion.
+// Units: q' and dout carry one exponent per 64-slot tile and q head (constant
+// inside a wave), k' and v one per (row, kv head).  dP comes out in units
+// 2^(e_dout + e_v); delta is brought into those units times 2^-kDsShift, and
+// dS is formed as P * (dP * 2^-kDsShift - delta) before the fp16 conversion.
 #include "attn_common.h"
 #include "attn_sched.h"
 #include "opr_internal.h"
@@ -44,9 +44,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int q = m * 128 + 32 * w + li;
   const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
-  const int64_t hbase = (int64_t)b * p.Hq + (int64_t)kvh * p.group;
-  const int eq = group_exponent(p.mq + hbase, p.group);
-  const int edo = group_exponent(p.mdo + hbase, p.group);
+  // q' and dout scales of the wave's 64-slot tile, and their kv-group minima
+  const int64_t tix = ((int64_t)b * p.Hq + h) * p.MT64 + 2 * m + (w >> 1);
+  const int eq = p.eqt[tix], edo = p.edot[tix];
+  const int eqr = p.eref[2 * kvplane], edor = p.eref[2 * kvplane + 1];
   const int ek = plane_exponent(p.mk[kvplane]);
   const int ev = plane_exponent(p.mv[kvplane]);
   const float fs = ldexpf(p.scale_log2, -(eq + ek));
@@ -59,8 +60,9 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
     qb[s] = ld_f16x8(p.qr + hq_row * D + 16 * s + 8 * g);
     dob[s] = ld_f16x8(p.dor + hq_row * D + 16 * s + 8 * g);
   }
-  const float lse2_q = p.lse2[hq_row] + (float)kPdvExp;
-  const float dsc_q = ldexpf(p.dsc[hq_row], kPdvExp);
+  // the stored lse2 and delta are in the dK/dV kernel's units: undo them
+  const float lse2_q = p.lse2[hq_row] + (float)(kPdvExp - (edo - edor));
+  const float dsc_q = ldexpf(p.dsc[hq_row], kPdvExp + (eq - eqr));
   // key slots this query sees: [iv.x, iv.y) and [iv.z, iv.w)
   const int4 iv = q < p.L ? p.qiv[(int64_t)b * p.L + q] : make_int4(0, 0, 0, 0);
   OperandOffsets<D> of;

@@ -1,13 +1,14 @@
 // Prologue kernels of the attention path.  Everything here is indexed by
 // slot (attention order): slot s < L holds token slot_tok[s] of the layout,
 // slots L .. Lp-1 are empty and padded with zeros.
-//  - the RoPE table at the slots' strategic position ids (and zeroing of the
-//    plane maxima),
-//  - the largest magnitude of every (row, head) plane of q, k, v, dout,
-//  - head-major fp16 copies of q, k (after RoPE), v and dout in slot order,
-//    with one power-of-two scale per plane,
-//  - the backward preprocessing delta = rowsum(dout * o), scaled, with the
-//    dout plane maxima.
+//  - the RoPE table at the slots' strategic position ids (and the reset of
+//    the plane maxima and of the tile exponent minima),
+//  - the largest magnitude of every (row, kv head) plane of k and v,
+//  - head-major fp16 copies of q, k (after RoPE), v and dout in slot order:
+//    k and v with one power-of-two scale per plane, q and dout with one per
+//    64-slot tile of each (row, head), found while the tile is converted,
+//  - the backward preprocessing delta = rowsum(dout * o), fused with the dout
+//    copy, and its scaling into the units of the backward kernels.
 //
 // RoPE (rotate-half): pair (j, j + D/2) of a head vector is rotated by
 // pos * theta^(-2j/D).  The angle and its cosine and sine are computed in
@@ -20,13 +21,17 @@ namespace opr {
 namespace {
 
 // table[b][s][j] = (cos, sin) of pos(b, slot_tok[s]) * theta^(-2j/D); PAD
-// and s >= L use position 0.  The first n_zero threads also clear zero_words.
+// and s >= L use position 0.  The first n_zero threads also clear zero_words
+// (plane maxima start at 0) and the first n_emax set emax to kExpMax (tile
+// exponent minima start above every exponent).
 __global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, int32_t Lp, int32_t half,
                                                          double log2_theta, const int32_t *tok_pos,
                                                          const int32_t *slot_tok, float2 *table,
-                                                         uint32_t *zero_words, int32_t n_zero) {
+                                                         uint32_t *zero_words, int32_t n_zero, int32_t *emax,
+                                                         int32_t n_emax) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid < n_zero) zero_words[gid] = 0u;
+  if (gid < n_emax) emax[gid] = kExpMax;
   const int64_t total = (int64_t)B * Lp * half;
   if (gid >= total) return;
   const int32_t j = (int32_t)(gid % half);
@@ -47,8 +52,8 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, i
 // 16-lane group reads one head's whole row and a wave reads contiguous runs.
 constexpr int kAbsTokens = 64;
 
-// One launch covers q, k and v: blockIdx.y runs over the head blocks of
-// job 0, then job 1, then job 2.
+// One launch covers k and v: blockIdx.y runs over the head blocks of job 0,
+// then job 1.
 struct AbsmaxJob {
   const uint16_t *x;  // [B][L][H][D] bf16
   uint32_t *pmax;     // [B][H]
@@ -58,15 +63,15 @@ struct AbsmaxJob {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, AbsmaxJob j1, AbsmaxJob j2) {
+__global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, AbsmaxJob j1) {
   constexpr int CPH = D / 8, HPB = 256 / CPH;
   const int yb = blockIdx.y;
-  const bool in0 = yb < j0.hb_end, in1 = !in0 && yb < j1.hb_end;
-  const uint16_t *x = in0 ? j0.x : (in1 ? j1.x : j2.x);
-  uint32_t *pmax = in0 ? j0.pmax : (in1 ? j1.pmax : j2.pmax);
-  const int32_t H = in0 ? j0.H : (in1 ? j1.H : j2.H);
-  const float factor = in0 ? j0.factor : (in1 ? j1.factor : j2.factor);
-  const int hb = yb - (in0 ? 0 : (in1 ? j0.hb_end : j1.hb_end));
+  const bool in0 = yb < j0.hb_end;
+  const uint16_t *x = in0 ? j0.x : j1.x;
+  uint32_t *pmax = in0 ? j0.pmax : j1.pmax;
+  const int32_t H = in0 ? j0.H : j1.H;
+  const float factor = in0 ? j0.factor : j1.factor;
+  const int hb = yb - (in0 ? 0 : j0.hb_end);
   const int b = blockIdx.z, tid = threadIdx.x;
   const int hl = tid / CPH, j = tid % CPH;
   const int h = hb * HPB + hl;
@@ -86,155 +91,252 @@ __global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, Ab
 
 // One workgroup per (64-slot block, group of kPackHeads heads, row): 4
 // threads per slot, each owning D/8 rotation pairs, keep the slot's RoPE
-// cosines and sines in registers and walk the heads.  x: [B][L][H][D] bf16 ->
-// rows [B][H][Lp][D] in slot order, fp16(x' * 2^e), x' = RoPE(x) or x, e the
-// exponent of the largest plane maximum of the head's group of `group`
-// heads.  Slots s >= L are zero.
+// cosines and sines in registers and walk the heads in batches of
+// kPackBatch, whose rows are all loaded before any is converted.
+// x: [B][L][H][D] bf16 -> rows [B][H][Lp][D] in slot order, fp16(x' * 2^e),
+// x' = RoPE(x) or x.
+// TILE = false: e is the exponent of the head's plane maximum pmax[b][h].
+// TILE = true: e is the exponent of the largest |x'| of the workgroup's 64
+// slots of the head (kExpMax for an all-zero tile), reduced over the
+// workgroup (one barrier per batch); it is stored in etile[b][h][block] and
+// folded into emin[b][h / group] (atomic minimum).  Slots s >= L are zero.
 constexpr int kPackHeads = 8;
+constexpr int kPackBatch = 1;
 
-template <int D, bool ROPE>
+// Rotated (or plain) pair e of a thread's bf16 words: low halves in words
+// 0 .. PER/8 - 1, high halves after them.
+template <int PER, bool ROPE>
+__device__ __forceinline__ void pair_at(const uint4 (&w)[PER / 4], const float2 (&cs)[PER], int e, float &lo,
+                                        float &hi) {
+  const uint16_t *u = reinterpret_cast<const uint16_t *>(w);
+  lo = bf16_to_f32(u[e]);
+  hi = bf16_to_f32(u[PER + e]);
+  if (ROPE) {
+    const float x1 = lo, x2 = hi;
+    lo = x1 * cs[e].x - x2 * cs[e].y;
+    hi = x2 * cs[e].x + x1 * cs[e].y;
+  }
+}
+
+template <int D, bool ROPE, bool TILE>
 __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H, int32_t group,
                                                    const uint16_t *x, const int32_t *slot_tok,
                                                    const float2 *table, const uint32_t *pmax,
-                                                   uint16_t *rows) {
+                                                   uint16_t *rows, int32_t *etile, int32_t *emin) {
   constexpr int HALF = D / 2;
   constexpr int PER = HALF / 4;  // pairs per thread (4 threads per slot)
+  __shared__ uint32_t wmax[kPackBatch][4];
   const int hgroups = (H + kPackHeads - 1) / kPackHeads;
   const int h0 = (int)(blockIdx.x % (unsigned)hgroups) * kPackHeads;
-  const int t0 = (int)(blockIdx.x / (unsigned)hgroups) * 64, b = blockIdx.z;
-  const int tid = threadIdx.x;
+  const int blk = (int)(blockIdx.x / (unsigned)hgroups);
+  const int t0 = blk * 64, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tt = tid >> 2, part = tid & 3;
   const int t = t0 + tt;
   const int j0 = part * PER;
   const int32_t tok = t < L ? slot_tok[(int64_t)b * L + t] : -1;
   float2 cs[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) cs[e] = make_float2(1.0f, 0.0f);
   if (ROPE) {
     const float2 *row = table + ((int64_t)b * Lp + t) * HALF + j0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) cs[e] = row[e];
   }
   const int h1 = min(H, h0 + kPackHeads);
-#pragma unroll 2
-  for (int h = h0; h < h1; ++h) {
-    const int ex = group_exponent(pmax + (int64_t)b * H + (h / group) * group, group);
-    uint16_t lq[PER], hq[PER];
-    if (tok >= 0) {
-      const uint16_t *src = x + (((int64_t)b * L + tok) * H + h) * D;
-      uint16_t lb[PER], hb[PER];
+  for (int hb = h0; hb < h1; hb += kPackBatch) {
+    uint4 raw[kPackBatch][PER / 4];
 #pragma unroll
-      for (int c = 0; c < PER; c += 8) {
-        *reinterpret_cast<uint4 *>(&lb[c]) = *reinterpret_cast<const uint4 *>(src + j0 + c);
-        *reinterpret_cast<uint4 *>(&hb[c]) = *reinterpret_cast<const uint4 *>(src + HALF + j0 + c);
+    for (int k = 0; k < kPackBatch; ++k) {
+#pragma unroll
+      for (int c = 0; c < PER / 4; ++c) raw[k][c] = make_uint4(0, 0, 0, 0);
+      if (hb + k < h1 && tok >= 0) {
+        const uint16_t *src = x + (((int64_t)b * L + tok) * H + hb + k) * D;
+#pragma unroll
+        for (int c = 0; c < PER / 8; ++c) {
+          raw[k][c] = *reinterpret_cast<const uint4 *>(src + j0 + 8 * c);
+          raw[k][PER / 8 + c] = *reinterpret_cast<const uint4 *>(src + HALF + j0 + 8 * c);
+        }
       }
+    }
+    if (TILE) {
+#pragma unroll
+      for (int k = 0; k < kPackBatch; ++k) {
+        uint32_t m = 0u;  // float bits of the largest magnitude (integer order)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          float lo, hi;
+          pair_at<PER, ROPE>(raw[k], cs, e, lo, hi);
+          m = max(m, max(__float_as_uint(fabsf(lo)), __float_as_uint(fabsf(hi))));
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+        if (lane == 0) wmax[k][wave] = m;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < kPackBatch; ++k) {
+      const int h = hb + k;
+      if (h >= h1) break;
+      int ex;
+      if (TILE) {
+        const uint32_t m = max(max(wmax[k][0], wmax[k][1]), max(wmax[k][2], wmax[k][3]));
+        ex = m > 0u ? plane_exponent(m) : kExpMax;
+        if (tid == 0) {
+          etile[((int64_t)b * H + h) * (Lp / 64) + blk] = ex;
+          atomicMin(emin + 2 * ((int64_t)b * (H / group) + h / group), ex);
+        }
+      } else {
+        ex = plane_exponent(pmax[(int64_t)b * H + h]);
+      }
+      uint16_t lq[PER], hq[PER];
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        float lo = bf16_to_f32(lb[e]), hi = bf16_to_f32(hb[e]);
-        if (ROPE) {
-          const float x1 = lo, x2 = hi;
-          lo = x1 * cs[e].x - x2 * cs[e].y;
-          hi = x2 * cs[e].x + x1 * cs[e].y;
-        }
+        float lo, hi;
+        pair_at<PER, ROPE>(raw[k], cs, e, lo, hi);
         lq[e] = f32_to_f16_bits(ldexpf(lo, ex));
         hq[e] = f32_to_f16_bits(ldexpf(hi, ex));
       }
-    } else {
+      uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) lq[e] = hq[e] = 0;
+      for (int c = 0; c < PER; c += 8) {
+        *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
+        *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
+      }
     }
-    uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
-#pragma unroll
-    for (int c = 0; c < PER; c += 8) {
-      *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
-      *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
-    }
+    if (TILE) __syncthreads();  // wmax is reused by the next batch
   }
 }
 
-// Backward preprocessing, before dout is packed: per slot s and q head, with
-// t = slot_tok[s] the token there,
-//   dsc[b][h][s]  = sum_d dout * o of token t (float32 over bf16 inputs),
-//   lse2[b][h][s] = lse * log2(e) - kPdvExp, +inf where the row has no key (lse = -inf)
-//                   or s >= L, so that recomputed probabilities are exactly 0;
-// and the largest |dout| of each (row, head) plane into mdo (float bits).
-// One wave per slot: D/8 lanes read one head's 16-byte chunks, so a wave
-// covers 64/(D/8) heads per step with fully coalesced row reads; the plane
-// maxima are combined in LDS, then once per workgroup in memory.
-constexpr int kMaxHeads = 1024;
-
+// Backward preprocessing, one workgroup per (64-slot block, group of
+// kPackHeads q heads, row) with the thread layout of pack_kernel, in batches
+// of kPackBatch heads whose dout and o rows are all loaded first; per slot s,
+// with t = slot_tok[s] the token there,
+//   dsc[b][h][s] = sum_d dout * o of token t (float32 over bf16 inputs; the
+//                  units are applied by scale_delta_kernel),
+// and dout goes to its fp16 copy with the exponent of the block's largest
+// |dout| (kExpMax for an all-zero block), stored in etile[b][h][block] and
+// folded into emin[b][h / group] (atomic minimum).
 template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(int32_t B, int32_t L, int32_t Lp, int32_t Hq,
-                                                    const uint16_t *o, const uint16_t *dout, const float *lse,
-                                                    const int32_t *slot_tok, uint32_t *mdo, float *dsc,
-                                                    float *lse2) {
-  constexpr int LPH = D / 8;        // lanes per head
-  constexpr int HPS = 64 / LPH;     // heads per step
-  constexpr int TPW = 4;            // tokens per wave
-  __shared__ uint32_t hmax[kMaxHeads];
-  for (int i = threadIdx.x; i < Hq; i += 256) hmax[i] = 0u;
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int hl = lane / LPH, part = lane % LPH;
-  const int64_t bt0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
-  for (int k = 0; k < TPW; ++k) {
-    const int64_t bt = bt0 + k;
-    if (bt >= (int64_t)B * Lp) break;
-    const int32_t sl = (int32_t)(bt % Lp);
-    const int32_t b = (int32_t)(bt / Lp);
-    if (b != (int32_t)(bt0 / Lp)) break;  // a workgroup's plane maxima stay within one row
-    const int32_t t = sl < L ? slot_tok[(int64_t)b * L + sl] : L;  // token at the slot
-#pragma unroll 4
-    for (int h0 = 0; h0 < Hq; h0 += HPS) {
-      const int h = h0 + hl;
-      float acc = 0.0f;
-      uint32_t mx = 0u;  // float bits of the largest |dout|
-      if (t < L && h < Hq) {
-        const int64_t base = (((int64_t)b * L + t) * Hq + h) * D + part * 8;
-        const uint4 ov = *reinterpret_cast<const uint4 *>(o + base);
-        const uint4 dv = *reinterpret_cast<const uint4 *>(dout + base);
-        acc = dot2_bf16(ov.x, dv.x, acc);
-        acc = dot2_bf16(ov.y, dv.y, acc);
-        acc = dot2_bf16(ov.z, dv.z, acc);
-        acc = dot2_bf16(ov.w, dv.w, acc);
-        mx = absmax8_bf16_bits(dv);
-      }
+__global__ __launch_bounds__(256) void delta_pack_kernel(int32_t L, int32_t Lp, int32_t H, int32_t group,
+                                                         const uint16_t *o, const uint16_t *dout,
+                                                         const int32_t *slot_tok, uint16_t *rows, float *dsc,
+                                                         int32_t *etile, int32_t *emin) {
+  constexpr int HALF = D / 2;
+  constexpr int PER = HALF / 4;
+  __shared__ uint32_t wmax[kPackBatch][4];
+  const int hgroups = (H + kPackHeads - 1) / kPackHeads;
+  const int h0 = (int)(blockIdx.x % (unsigned)hgroups) * kPackHeads;
+  const int blk = (int)(blockIdx.x / (unsigned)hgroups);
+  const int t0 = blk * 64, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tt = tid >> 2, part = tid & 3;
+  const int t = t0 + tt;
+  const int j0 = part * PER;
+  const int32_t tok = t < L ? slot_tok[(int64_t)b * L + t] : -1;
+  const int h1 = min(H, h0 + kPackHeads);
+  for (int hb = h0; hb < h1; hb += kPackBatch) {
+    uint4 dw[kPackBatch][PER / 4], ow[kPackBatch][PER / 4];  // bf16 words, low halves then high halves
 #pragma unroll
-      for (int off = LPH / 2; off > 0; off >>= 1) {
-        acc += __shfl_xor(acc, off);
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
-      }
-      if (part == 0 && h < Hq) {
-        float l2 = INFINITY;
-        if (t < L) {
-          const float l = lse[((int64_t)b * Hq + h) * L + t];
-          l2 = (l == -INFINITY) ? INFINITY : l * kLog2e - (float)kPdvExp;
+    for (int k = 0; k < kPackBatch; ++k) {
+#pragma unroll
+      for (int c = 0; c < PER / 4; ++c) dw[k][c] = ow[k][c] = make_uint4(0, 0, 0, 0);
+      if (hb + k < h1 && tok >= 0) {
+        const int64_t base = (((int64_t)b * L + tok) * H + hb + k) * D;
+#pragma unroll
+        for (int c = 0; c < PER / 8; ++c) {
+          dw[k][c] = *reinterpret_cast<const uint4 *>(dout + base + j0 + 8 * c);
+          dw[k][PER / 8 + c] = *reinterpret_cast<const uint4 *>(dout + base + HALF + j0 + 8 * c);
+          ow[k][c] = *reinterpret_cast<const uint4 *>(o + base + j0 + 8 * c);
+          ow[k][PER / 8 + c] = *reinterpret_cast<const uint4 *>(o + base + HALF + j0 + 8 * c);
         }
-        const int64_t out = ((int64_t)b * Hq + h) * Lp + sl;
-        dsc[out] = acc;
-        lse2[out] = l2;
-        if (mx > 0u) atomicMax(&hmax[h], mx);
       }
     }
+    float acc[kPackBatch];
+#pragma unroll
+    for (int k = 0; k < kPackBatch; ++k) {
+      float a = 0.0f;
+      uint32_t m = 0u;
+#pragma unroll
+      for (int c = 0; c < PER / 4; ++c) {
+        a = dot2_bf16(ow[k][c].x, dw[k][c].x, a);
+        a = dot2_bf16(ow[k][c].y, dw[k][c].y, a);
+        a = dot2_bf16(ow[k][c].z, dw[k][c].z, a);
+        a = dot2_bf16(ow[k][c].w, dw[k][c].w, a);
+        m = max(m, absmax8_bf16_bits(dw[k][c]));
+      }
+      a += __shfl_xor(a, 1);  // the 4 threads of a slot
+      a += __shfl_xor(a, 2);
+      acc[k] = a;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+      if (lane == 0) wmax[k][wave] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPackBatch; ++k) {
+      const int h = hb + k;
+      if (h >= h1) break;
+      const uint32_t m = max(max(wmax[k][0], wmax[k][1]), max(wmax[k][2], wmax[k][3]));
+      const int ex = m > 0u ? plane_exponent(m) : kExpMax;
+      if (tid == 0) {
+        etile[((int64_t)b * H + h) * (Lp / 64) + blk] = ex;
+        atomicMin(emin + 2 * ((int64_t)b * (H / group) + h / group) + 1, ex);
+      }
+      if (part == 0) dsc[((int64_t)b * H + h) * Lp + t] = acc[k];
+      const uint16_t *dl = reinterpret_cast<const uint16_t *>(dw[k]);
+      uint16_t lq[PER], hq[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        lq[e] = f32_to_f16_bits(ldexpf(bf16_to_f32(dl[e]), ex));
+        hq[e] = f32_to_f16_bits(ldexpf(bf16_to_f32(dl[PER + e]), ex));
+      }
+      uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
+#pragma unroll
+      for (int c = 0; c < PER; c += 8) {
+        *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
+        *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
+      }
+    }
+    __syncthreads();  // wmax is reused by the next batch
   }
-  __syncthreads();
-  const int64_t b = ((int64_t)blockIdx.x * 4 * TPW) / Lp;
-  if (b < B)
-    for (int i = threadIdx.x; i < Hq; i += 256)
-      if (hmax[i]) atomicMax(mdo + b * Hq + i, hmax[i]);
 }
 
-// dsc *= 2^(e_dout + e_v - kDsShift - kPdvExp): delta in the units of dP = dO V^T
-// on the scaled operands, shifted like dS, times the 2^-kPdvExp that the
-// fp16(P * 2^kPdvExp) of the dK/dV kernel cancels.  One thread per (b, h, t).
-__global__ __launch_bounds__(256) void scale_delta_kernel(int32_t B, int32_t Lp, int32_t Hq, int32_t group,
-                                                          const uint32_t *mdo, const uint32_t *mv, float *dsc) {
+// Units of the backward, per slot s of q head h in kv group kv, with eq, edo
+// the tile exponents of q and dout at s and eqr, edor their group minima:
+//   lse2[b][h][s] = lse * log2(e) - kPdvExp + (edo - edor): the dK/dV kernel's
+//       fp16(P * 2^(kPdvExp - (edo - edor))) then cancels the dout tile scale in
+//       dV^T += dO'^T P^T; +inf where the row has no key or s >= L, so that
+//       recomputed probabilities are exactly 0;
+//   dsc[b][h][s] *= 2^(edo + ev - kDsShift - kPdvExp - (eq - eqr)): delta in
+//       the units of dP = dO' V'^T of that slot, shifted so that
+//       dS' = P' (dP dss - delta) comes out in units that Q' turns into the
+//       group-wide units of dK.
+// One thread per (b, h, s).
+__global__ __launch_bounds__(256) void scale_delta_kernel(int32_t B, int32_t L, int32_t Lp, int32_t Hq, int32_t group,
+                                                          const float *lse, const int32_t *slot_tok,
+                                                          const int32_t *eqt, const int32_t *edot,
+                                                          const int32_t *eref, const uint32_t *mv, float *dsc,
+                                                          float *lse2) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)B * Hq * Lp) return;
+  const int32_t sl = (int32_t)(gid % Lp);
   const int64_t bh = gid / Lp;
   const int h = (int)(bh % Hq);
   const int64_t b = bh / Hq;
   const int kv = h / group, Hkv = Hq / group;
-  const int e = group_exponent(mdo + b * Hq + kv * group, group) + plane_exponent(mv[b * Hkv + kv]) - kDsShift - kPdvExp;
-  dsc[gid] = ldexpf(dsc[gid], e);
+  const int64_t tix = bh * (Lp / 64) + sl / 64;
+  const int eq = eqt[tix], edo = edot[tix];
+  const int eqr = eref[2 * (b * Hkv + kv)], edor = eref[2 * (b * Hkv + kv) + 1];
+  const int ev = plane_exponent(mv[b * Hkv + kv]);
+  float l2 = INFINITY;
+  if (sl < L) {
+    const float l = lse[bh * L + slot_tok[b * L + sl]];
+    if (l != -INFINITY) l2 = l * kLog2e - (float)kPdvExp + (float)(edo - edor);
+  }
+  lse2[gid] = l2;
+  dsc[gid] = ldexpf(dsc[gid], edo + ev - kDsShift - kPdvExp - (eq - eqr));
 }
 
 // Longest-first work order (see q_work_item): the q-tile rows (b*MT + m) by
@@ -321,61 +423,74 @@ __global__ __launch_bounds__(kOrderThreads) void work_order_kernel(int32_t n_row
   }
 }
 
-__global__ void zero_words_kernel(uint32_t *p, int32_t n) {
+// p[i * stride] = value for i < n
+__global__ void set_words_kernel(int32_t *p, int32_t n, int32_t stride, int32_t value) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+  if (i < n) p[(int64_t)i * stride] = value;
 }
 
 template <int D>
 void launch_absmax_d(int32_t B, int32_t L, const AbsmaxJob *jobs, hipStream_t s) {
-  absmax_kernel<D><<<dim3((L + kAbsTokens - 1) / kAbsTokens, jobs[2].hb_end, B), 256, 0, s>>>(L, jobs[0], jobs[1],
-                                                                                             jobs[2]);
+  absmax_kernel<D><<<dim3((L + kAbsTokens - 1) / kAbsTokens, jobs[1].hb_end, B), 256, 0, s>>>(L, jobs[0], jobs[1]);
 }
 
-template <int D>
-void launch_pack_d(bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group, const void *x,
+template <int D, bool ROPE, bool TILE>
+void launch_pack_d(int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group, const void *x,
                    const int32_t *slot_tok, const float2 *table, const uint32_t *pmax, uint16_t *rows,
-                   hipStream_t s) {
+                   int32_t *etile, int32_t *emin, hipStream_t s) {
   const unsigned hgroups = (unsigned)((H + kPackHeads - 1) / kPackHeads);
   const dim3 grid(hgroups * (unsigned)(Lp / 64), 1, B);
-  const uint16_t *src = static_cast<const uint16_t *>(x);
-  if (rope) pack_kernel<D, true><<<grid, 256, 0, s>>>(L, Lp, H, group, src, slot_tok, table, pmax, rows);
-  else pack_kernel<D, false><<<grid, 256, 0, s>>>(L, Lp, H, group, src, slot_tok, table, pmax, rows);
+  pack_kernel<D, ROPE, TILE><<<grid, 256, 0, s>>>(L, Lp, H, group, static_cast<const uint16_t *>(x), slot_tok, table,
+                                                 pmax, rows, etile, emin);
 }
 
 }  // namespace
 
-// RoPE table + clearing of the plane maxima (they must start at zero).
+// RoPE table + clearing of the plane maxima (they start at zero) and of the
+// tile exponent minima (they start at kExpMax).
 void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int32_t half = in.D / 2;
   const int64_t total = (int64_t)in.B * ws.Lp * half;
-  const int64_t blocks = ((total > ws.n_pmax ? total : (int64_t)ws.n_pmax) + 255) / 256;
-  rope_table_kernel<<<(unsigned)blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, half, log2(in.rope_theta),
-                                                     in.layout.tok_pos, in.layout.slot_tok, ws.rope, ws.pmax,
-                                                     ws.n_pmax);
+  const int32_t n_emax = 2 * in.B * in.Hkv;
+  int64_t n = total > ws.n_pmax ? total : (int64_t)ws.n_pmax;
+  if (n < n_emax) n = n_emax;
+  rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(in.B, in.L, ws.Lp, half, log2(in.rope_theta),
+                                                                in.layout.tok_pos, in.layout.slot_tok, ws.rope,
+                                                                ws.pmax, ws.n_pmax, ws.eref, n_emax);
 }
 
-// Plane maxima of q and k (times sqrt(2), the RoPE bound) and of v.
-void launch_absmax_qkv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+// Plane maxima of k (times sqrt(2), the RoPE bound) and of v.
+void launch_absmax_kv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int HPB = 256 / (in.D / 8);
-  AbsmaxJob jobs[3];
-  const void *xs[3] = {in.q, in.k, in.v};
-  uint32_t *ms[3] = {ws.mq, ws.mk, ws.mv};
-  const int32_t hs[3] = {in.Hq, in.Hkv, in.Hkv};
-  int32_t end = 0;
-  for (int i = 0; i < 3; ++i) {
-    end += (hs[i] + HPB - 1) / HPB;
-    jobs[i] = AbsmaxJob{static_cast<const uint16_t *>(xs[i]), ms[i], hs[i], end, i < 2 ? 1.4142136f : 1.0f};
-  }
+  const int32_t hb = (in.Hkv + HPB - 1) / HPB;
+  AbsmaxJob jobs[2] = {{static_cast<const uint16_t *>(in.k), ws.mk, in.Hkv, hb, 1.4142136f},
+                       {static_cast<const uint16_t *>(in.v), ws.mv, in.Hkv, 2 * hb, 1.0f}};
   if (in.D == 64) launch_absmax_d<64>(in.B, in.L, jobs, s);
   else launch_absmax_d<128>(in.B, in.L, jobs, s);
 }
 
+// q after RoPE, one scale per 64-slot tile of each (row, head).
+void launch_pack_q(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+  const int32_t group = in.Hq / in.Hkv;
+  if (in.D == 64)
+    launch_pack_d<64, true, true>(in.B, in.L, ws.Lp, in.Hq, group, in.q, in.layout.slot_tok, ws.rope, nullptr,
+                                  ws.qr, ws.eqt, ws.eref, s);
+  else
+    launch_pack_d<128, true, true>(in.B, in.L, ws.Lp, in.Hq, group, in.q, in.layout.slot_tok, ws.rope, nullptr,
+                                   ws.qr, ws.eqt, ws.eref, s);
+}
+
+// k (RoPE) or v, one scale per plane.
 void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,
                      const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
                      uint16_t *rows, hipStream_t s) {
-  if (D == 64) launch_pack_d<64>(rope, B, L, Lp, H, group, x, slot_tok, table, pmax, rows, s);
-  else launch_pack_d<128>(rope, B, L, Lp, H, group, x, slot_tok, table, pmax, rows, s);
+  if (D == 64) {
+    if (rope) launch_pack_d<64, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
+    else launch_pack_d<64, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
+  } else {
+    if (rope) launch_pack_d<128, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
+    else launch_pack_d<128, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
+  }
 }
 
 void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
@@ -385,28 +500,30 @@ void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
                                                ws.q_order, ws.k_order);
 }
 
-// delta, lse2 and the dout plane maxima (mdo is cleared first), then dout
-// packing and the delta scaling are done by the caller in that order.
-void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
-                  const AttnWs &ws, hipStream_t s) {
-  const int32_t nz = in.B * in.Hq;
-  zero_words_kernel<<<(nz + 255) / 256, 256, 0, s>>>(ws.mdo, nz);
-  const int64_t tokens = (int64_t)in.B * ws.Lp;  // 16 tokens per workgroup
-  const unsigned blocks = (unsigned)((tokens + 15) / 16);
+// delta and the fp16 dout copy with its tile exponents (their group minima
+// are reset first: a backward may follow another on the same workspace).
+void launch_delta_pack(const opr_attn_in &in, const void *o, const void *dout, const AttnWs &ws,
+                       hipStream_t s) {
+  const int32_t n = 2 * in.B * in.Hkv;
+  set_words_kernel<<<(n + 255) / 256, 256, 0, s>>>(ws.eref + 1, n / 2, 2, kExpMax);
+  const int32_t group = in.Hq / in.Hkv;
+  const unsigned hgroups = (unsigned)((in.Hq + kPackHeads - 1) / kPackHeads);
+  const dim3 grid(hgroups * (unsigned)(ws.Lp / 64), 1, in.B);
   const uint16_t *o16 = static_cast<const uint16_t *>(o);
   const uint16_t *d16 = static_cast<const uint16_t *>(dout);
   if (in.D == 64)
-    delta_kernel<64><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, in.layout.slot_tok,
-                                            ws.mdo, ws.dsc, ws.lse2);
+    delta_pack_kernel<64><<<grid, 256, 0, s>>>(in.L, ws.Lp, in.Hq, group, o16, d16, in.layout.slot_tok, ws.dor,
+                                               ws.dsc, ws.edot, ws.eref);
   else
-    delta_kernel<128><<<blocks, 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, o16, d16, lse, in.layout.slot_tok,
-                                             ws.mdo, ws.dsc, ws.lse2);
+    delta_pack_kernel<128><<<grid, 256, 0, s>>>(in.L, ws.Lp, in.Hq, group, o16, d16, in.layout.slot_tok, ws.dor,
+                                                ws.dsc, ws.edot, ws.eref);
 }
 
-void launch_scale_delta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+void launch_scale_delta(const opr_attn_in &in, const float *lse, const AttnWs &ws, hipStream_t s) {
   const int64_t total = (int64_t)in.B * in.Hq * ws.Lp;
-  scale_delta_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(in.B, ws.Lp, in.Hq, in.Hq / in.Hkv, ws.mdo,
-                                                                     ws.mv, ws.dsc);
+  scale_delta_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, in.Hq / in.Hkv, lse,
+                                                                     in.layout.slot_tok, ws.eqt, ws.edot, ws.eref,
+                                                                     ws.mv, ws.dsc, ws.lse2);
 }
 
 }  // namespace opr

@@ -11,14 +11,15 @@ namespace opr {
 
 // launchers defined in the .hip files
 void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
-void launch_absmax_qkv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
+void launch_absmax_kv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
+void launch_pack_q(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,
                      const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
                      uint16_t *rows, hipStream_t s);
-void launch_scale_delta(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
-void launch_delta(const opr_attn_in &in, const void *o, const void *dout, const float *lse,
-                  const AttnWs &ws, hipStream_t s);
+void launch_delta_pack(const opr_attn_in &in, const void *o, const void *dout, const AttnWs &ws,
+                       hipStream_t s);
+void launch_scale_delta(const opr_attn_in &in, const float *lse, const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, float *lse,
                                   const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq, float *dk,
@@ -45,14 +46,15 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   w.qr = cv.take<uint16_t>(qn);
   w.kr = cv.take<uint16_t>(kn);
   w.vr = cv.take<uint16_t>(kn);
-  w.n_pmax = 2 * in.B * (in.Hq + in.Hkv);
+  w.n_pmax = 2 * in.B * in.Hkv;
   w.pmax = cv.take<uint32_t>((size_t)w.n_pmax);
   if (w.pmax) {
-    w.mq = w.pmax;
-    w.mk = w.mq + (size_t)in.B * in.Hq;
+    w.mk = w.pmax;
     w.mv = w.mk + (size_t)in.B * in.Hkv;
-    w.mdo = w.mv + (size_t)in.B * in.Hkv;
   }
+  const size_t tiles64 = (size_t)in.B * in.Hq * (Lp / 64);
+  w.eqt = cv.take<int32_t>(tiles64);
+  w.eref = cv.take<int32_t>((size_t)2 * in.B * in.Hkv);
   const size_t tiles = (size_t)in.B * (Lp / OPR_ATTN_BLOCK);
   w.q_order = cv.take<int32_t>(tiles);
   w.k_order = cv.take<int32_t>(tiles);
@@ -60,6 +62,7 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   // everything above is the forward state; the backward part follows
   if (is_bwd) {
     w.dor = cv.take<uint16_t>(qn);
+    w.edot = cv.take<int32_t>(tiles64);
     w.dsc = cv.take<float>((size_t)in.B * in.Hq * Lp);
     w.lse2 = cv.take<float>((size_t)in.B * in.Hq * Lp);
   }
@@ -89,10 +92,12 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->kr = ws.kr;
   p->vr = ws.vr;
   p->dor = ws.dor;
-  p->mq = ws.mq;
   p->mk = ws.mk;
   p->mv = ws.mv;
-  p->mdo = ws.mdo;
+  p->eqt = ws.eqt;
+  p->edot = ws.edot;
+  p->eref = ws.eref;
+  p->MT64 = ws.Lp / 64;
   p->q_order = ws.q_order;
   p->k_order = ws.k_order;
   p->slot_tok = in.layout.slot_tok;
@@ -142,14 +147,14 @@ static void mark(const opr_attn_in *in, int i, hipStream_t s) {
   if (in->timing_events) hipEventRecord(in->timing_events[i], s);
 }
 
-// RoPE table, plane maxima, fp16 copies of q, k, v in slot order and the
-// work order: the forward state at the start of the workspace.
+// RoPE table, plane maxima of k and v, fp16 copies of q (per-tile scales),
+// k and v in slot order and the work order: the forward state at the start of
+// the workspace.
 static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_t stream) {
-  const int32_t group = in.Hq / in.Hkv;
   launch_rope_table(in, ws, stream);
-  launch_absmax_qkv(in, ws, stream);
+  launch_absmax_kv(in, ws, stream);
+  launch_pack_q(in, ws, stream);
   const int32_t *st = in.layout.slot_tok;
-  launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hq, group, in.q, st, ws.rope, ws.mq, ws.qr, stream);
   launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hkv, 1, in.k, st, ws.rope, ws.mk, ws.kr, stream);
   launch_pack_any(in.D, false, in.B, in.L, ws.Lp, in.Hkv, 1, in.v, st, ws.rope, ws.mv, ws.vr, stream);
   launch_work_order(in, ws, stream);
@@ -264,10 +269,8 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   carve_attn_ws(workspace, *in, 1, &ws);
   mark(in, 0, stream);
   if (!in->reuse_fwd_workspace) forward_prologue(*in, ws, stream);
-  launch_delta(*in, o, dout, lse, ws, stream);
-  launch_pack_any(in->D, false, in->B, in->L, ws.Lp, in->Hq, in->Hq / in->Hkv, dout, in->layout.slot_tok,
-                  ws.rope, ws.mdo, ws.dor, stream);
-  launch_scale_delta(*in, ws, stream);
+  launch_delta_pack(*in, o, dout, ws, stream);
+  launch_scale_delta(*in, lse, ws, stream);
   if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream,
                               in->timing_events ? in->timing_events + 1 : nullptr) != hipSuccess)
     return OPR_E_HIP;

@@ -54,16 +54,22 @@ struct AttnWs {
   int32_t Lp;           // L rounded up to OPR_ATTN_BLOCK
   // everything below is in slot (attention) order
   float2 *rope;         // [B][Lp][D/2] (cos, sin) at each slot's position id
-  // fp16 copies [B][H][Lp][D], one power-of-two scale per (row, head) plane,
-  // zero past L
+  // fp16 copies [B][H][Lp][D], zero past L: k and v with one power-of-two
+  // scale per (row, kv head) plane, q and dout with one per 64-slot tile of
+  // each (row, q head)
   uint16_t *qr;         // q after RoPE
   uint16_t *kr;         // k after RoPE
   uint16_t *vr;         // v
   uint16_t *dor;        // dout                                   (bwd)
-  // plane maxima (float bits): mq [B][Hq], mk [B][Hkv], mv [B][Hkv],
-  // mdo [B][Hq], contiguous from pmax (n_pmax words)
-  uint32_t *pmax, *mq, *mk, *mv, *mdo;
+  // plane maxima (float bits): mk [B][Hkv], mv [B][Hkv], contiguous from pmax
+  // (n_pmax words)
+  uint32_t *pmax, *mk, *mv;
   int32_t n_pmax;
+  // tile exponents [B][Hq][Lp/64] of q (eqt) and dout (edot), and their
+  // minima over each kv group's heads and tiles, eref [B][Hkv][2] = (q, dout)
+  int32_t *eqt;
+  int32_t *edot;        //                                        (bwd)
+  int32_t *eref;
   int32_t *q_order;     // [B*MT] q-tile rows, most stages first
   int32_t *k_order;     // [B*NT] k-tile columns, most stages first
   int32_t *order_cost;  // [B*MT + B*NT] their stage counts
