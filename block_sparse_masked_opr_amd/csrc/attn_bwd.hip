@@ -24,14 +24,14 @@
 // built from the two runs of slots of each query or key.
 //
 // Units: k' and v carry one exponent per (row, kv head), constant inside a
-// workgroup; q' and dout one per 64-slot tile and q head, so they change from
-// stage to stage (eq, edo of the stage; eqr, edor their minima over the kv
-// group).  The products are brought to group-wide units like this:
-//   S: the score scale is 2^-(eq + ek) per stage;
+// workgroup; q' and dout one per 16-slot tile and q head, so they change
+// inside a stage (eq, edo of the tile; eqr, edor their minima over the kv
+// group; the stage descriptor carries the four tiles' eq and edo).  The products are brought to group-wide units like this:
+//   S: the score scale is 2^-(eq + ek) per tile;
 //   dV^T += dO'^T P'^T with P' = fp16(P * 2^(kPdvExp - (edo - edor))) (the
 //       stored lse2 carries the shift), so dV is in units 2^(kPdvExp + edor);
 //   dS' = P' (dP' dss - delta') with dP' = dO' V'^T in units 2^(edo + ev),
-//       dss = 2^-(kDsShift + kPdvExp + eq - eqr) per stage and delta' stored
+//       dss = 2^-(kDsShift + kPdvExp + eq - eqr) per tile and delta' stored
 //       in the matching units, so dS' = dS 2^(eqr + edor + ev - kDsShift - eq)
 //       and dK^T += Q'^T dS'^T is in units 2^(eqr + edor + ev - kDsShift).
 #include "attn_common.h"
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   __shared__ __attribute__((aligned(1024))) char pbf0[4 * PSTRIDE];
   __shared__ __attribute__((aligned(1024))) char pbf1[4 * PSTRIDE];
   __shared__ __attribute__((aligned(1024))) char pbf2[4 * PSTRIDE];
-  __shared__ uint2 stages[kStageCap];
+  __shared__ uint4 stages[kKStageCap];
   __shared__ int sh_count;
   __shared__ int64_t sh_next;
 
@@ -125,10 +125,12 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   // 32-query sub-block, P = exp2(S * scale * log2 e - lse2) masked by the
   // key's runs (unless both sub-blocks are full), as fp16(P * 2^kPdvExp) (lse2 carries the -kPdvExp) into op and
   // into LDS for the dS-wave.  The update that follows is dV^T += dO^T P^T.
-  auto p_elem = [&](uint2 desc, const char *buf, char *pout, f16x8 (&op)[2][2]) {
+  auto p_elem = [&](uint4 desc, const char *buf, char *pout, f16x8 (&op)[2][2]) {
     const int q0 = (int)(desc.x & 0xFFFFFFu);
-    const int eq_s = (int)((desc.y >> 16) & 0xFFu) - 64;
-    const float fs = ldexpf(p.scale_log2, -(eq_s + ek));  // raw score -> log2 units
+    // raw score -> log2 units, per 16-query tile 2 qb + hh (its q' exponent)
+    float fs[2][2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) fs[k >> 1][k & 1] = ldexpf(p.scale_log2, -(stage_exponent(desc.z, k) + ek));
     const char *Qt = buf;
     const float *lse2s = reinterpret_cast<const float *>(buf + 2 * TB);
     char *Pw = pout + w * PSTRIDE;
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
         const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          op[qb][hh][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * hh + e], fs, -lv[e]));
+          op[qb][hh][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * hh + e], fs[qb][hh], -lv[e]));
         }
         *reinterpret_cast<f16x8 *>(Pw + (2 * qb + hh) * 1024 + lane * 16) = op[qb][hh];
       }
@@ -172,9 +174,11 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   // dS = P * (dP - delta) into op, with P read back from the P-wave of the same
   // key block (masked entries have P = 0 and so dS = 0).  The update that
   // follows is dK^T += Q'^T dS^T.
-  auto ds_elem = [&](uint2 desc, const char *buf, const char *pin, f16x8 (&op)[2][2]) {
-    const int eq_s = (int)((desc.y >> 16) & 0xFFu) - 64;
-    const float dss = ldexpf(1.0f, -kDsShift - kPdvExp - (eq_s - eqr));
+  auto ds_elem = [&](uint4 desc, const char *buf, const char *pin, f16x8 (&op)[2][2]) {
+    // dP' -> dS' units, per 16-query tile 2 qb + hh (its q' exponent)
+    float dss[2][2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dss[k >> 1][k & 1] = ldexpf(1.0f, -kDsShift - kPdvExp - (stage_exponent(desc.z, k) - eqr));
     const char *dOt = buf + TB;
     const float *dscs = reinterpret_cast<const float *>(buf + 2 * TB + 256);
     const char *Pw = pin + w * PSTRIDE;
@@ -201,8 +205,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
         // second factor in fp32, then both multiplied as packed fp16 pairs
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const f16x2 t = {(_Float16)fmaf(dp[qb][8 * hh + e], dss, -dvv[e]),
-                           (_Float16)fmaf(dp[qb][8 * hh + e + 1], dss, -dvv[e + 1])};
+          const f16x2 t = {(_Float16)fmaf(dp[qb][8 * hh + e], dss[qb][hh], -dvv[e]),
+                           (_Float16)fmaf(dp[qb][8 * hh + e + 1], dss[qb][hh], -dvv[e + 1])};
           const f16x2 pp = {pv[e], pv[e + 1]};
           const f16x2 d = t * pp;
           op[qb][hh][e] = d[0];
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   // branch).
   auto wave_step = [&](int i, int ns, const char *ba, const char *bb, char *pa, const char *pr) {
     if (pwave ? i >= ns : i < 1) return;
-    const uint2 desc = uniform(stages[pwave ? i : i - 1]);
+    const uint4 desc = uniform(stages[pwave ? i : i - 1]);
     if (((desc.y >> (4 * w)) & 15u) == 0) return;
     f16x8 op[2][2];
     const char *T;
@@ -251,8 +255,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     __syncthreads();
     if (wave == 0) {
       int64_t f = fnext;
-      const int c = build_k_stages(lst, subs_b, p.NT, n, p.group, nnz, p.eqt + hbase * p.MT64,
-                                   p.edot + hbase * p.MT64, p.MT64, &f, stages, lane);
+      const int c = build_k_stages(lst, subs_b, p.NT, n, p.group, nnz, p.eqt + hbase * p.MTS,
+                                   p.edot + hbase * p.MTS, p.MTS, &f, stages, lane);
       if (lane == 0) {
         sh_count = c;
         sh_next = f;

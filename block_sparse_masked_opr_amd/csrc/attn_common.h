@@ -8,7 +8,8 @@
 // as fp16(x * 2^e) with a power-of-two exponent e chosen from the largest
 // magnitude it covers, so that this lands in [2^14, 2^15): for k and v one
 // per (row, kv head) plane (an absmax pre-pass), for q and dout one per
-// 64-slot tile of each (row, q head) (found while the tile is converted).
+// kTile-slot tile of each (row, q head) (found by the one wave that converts
+// the tile).
 // The kernels fold the exponents back exactly: into the score scale (q, k)
 // and into the fixed units of their fp32 accumulators (v, dout), removed in
 // the epilogues.
@@ -57,6 +58,10 @@ constexpr int kPdvExp = 15;
 // fp16(p * 2^kPExp) with p <= 2^kMaxSlack, i.e. at most 2^15.
 constexpr float kMaxSlack = 8.0f;
 constexpr int kPExp = 7;
+// Slots per exponent tile of q' and dout: half of a forward or dQ wave's 32
+// queries (lane i uses tile i / 16), a quarter of a dK/dV stage (accumulator
+// registers 8h .. 8h + 7 of 32-query block b hold tile 2b + h).
+constexpr int kTile = 16;
 
 // A-operand row order of a 32-row block: swap bits 2 and 3.
 // bf16 helpers on packed words.  dot2_bf16: a.lo*b.lo + a.hi*b.hi + c in
@@ -84,6 +89,9 @@ __device__ __forceinline__ uint32_t absmax8_bf16_bits(uint4 v) {
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 __device__ __forceinline__ uint2 uniform(uint2 x) { return make_uint2(uniform(x.x), uniform(x.y)); }
+__device__ __forceinline__ uint4 uniform(uint4 x) {
+  return make_uint4(uniform(x.x), uniform(x.y), uniform(x.z), uniform(x.w));
+}
 __device__ __forceinline__ int64_t uniform(int64_t x) {
   const uint64_t u = (uint64_t)x;
   return (int64_t)(((uint64_t)uniform((uint32_t)(u >> 32)) << 32) | uniform((uint32_t)u));
@@ -364,10 +372,10 @@ struct AttnParams {
   const uint16_t *qr, *kr, *vr, *dor;
   // plane maxima (float bits) [B][Hkv] of k', v
   const uint32_t *mk, *mv;
-  // tile exponents [B][Hq][Lp/64] of q' and dout; their minima over the kv
+  // tile exponents [B][Hq][MTS] of q' and dout; their minima over the kv
   // group, eref [B][Hkv][2] = (q, dout)
   const int32_t *eqt, *edot, *eref;
-  int32_t MT64;                // Lp / 64
+  int32_t MTS;                 // tiles per row: Lp / kTile
   const float *dsc, *lse2;     // [B][Hq][Lp], see the backward units in attn_bwd.hip
                                // (lse2 is +inf where no key)
 };

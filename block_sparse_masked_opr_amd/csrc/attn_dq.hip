@@ -10,8 +10,8 @@
 // LDS reads.  The epilogue removes the operand units, applies the softmax
 // scale and rotates dQ back by the transposed RoPE rotation.
 //
-// Units: q' and dout carry one exponent per 64-slot tile and q head (constant
-// inside a wave), k' and v one per (row, kv head).  dP comes out in units
+// Units: q' and dout carry one exponent per 16-slot tile and q head (one per
+// lane's query), k' and v one per (row, kv head).  dP comes out in units
 // 2^(e_dout + e_v); delta is brought into those units times 2^-kDsShift, and
 // dS is formed as P * (dP * 2^-kDsShift - delta) before the fp16 conversion.
 #include "attn_common.h"
@@ -44,8 +44,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int q = m * 128 + 32 * w + li;
   const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
-  // q' and dout scales of the wave's 64-slot tile, and their kv-group minima
-  const int64_t tix = ((int64_t)b * p.Hq + h) * p.MT64 + 2 * m + (w >> 1);
+  // q' and dout scales of the lane's tile (query slot q), and their kv-group minima
+  const int64_t tix = ((int64_t)b * p.Hq + h) * p.MTS + q / kTile;
   const int eq = p.eqt[tix], edo = p.edot[tix];
   const int eqr = p.eref[2 * kvplane], edor = p.eref[2 * kvplane + 1];
   const int ek = plane_exponent(p.mk[kvplane]);

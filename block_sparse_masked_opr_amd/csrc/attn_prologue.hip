@@ -2,7 +2,7 @@
 // slot (attention order): slot s < L holds token slot_tok[s] of the layout,
 // slots L .. Lp-1 are empty and padded with zeros.
 //  - the RoPE table at the slots' strategic position ids (and the reset of
-//    the plane maxima and of the tile exponent minima),
+//    the plane maxima),
 //  - the largest magnitude of every (row, kv head) plane of k and v,
 //  - head-major fp16 copies of q, k (after RoPE), v and dout in slot order:
 //    k and v with one power-of-two scale per plane, q and dout with one per
@@ -22,16 +22,13 @@ namespace {
 
 // table[b][s][j] = (cos, sin) of pos(b, slot_tok[s]) * theta^(-2j/D); PAD
 // and s >= L use position 0.  The first n_zero threads also clear zero_words
-// (plane maxima start at 0) and the first n_emax set emax to kExpMax (tile
-// exponent minima start above every exponent).
+// (the plane maxima start at 0).
 __global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, int32_t Lp, int32_t half,
                                                          double log2_theta, const int32_t *tok_pos,
                                                          const int32_t *slot_tok, float2 *table,
-                                                         uint32_t *zero_words, int32_t n_zero, int32_t *emax,
-                                                         int32_t n_emax) {
+                                                         uint32_t *zero_words, int32_t n_zero) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid < n_zero) zero_words[gid] = 0u;
-  if (gid < n_emax) emax[gid] = kExpMax;
   const int64_t total = (int64_t)B * Lp * half;
   if (gid >= total) return;
   const int32_t j = (int32_t)(gid % half);
@@ -90,217 +87,181 @@ __global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, Ab
 }
 
 // One workgroup per (64-slot block, group of kPackHeads heads, row): 4
-// threads per slot, each owning D/8 rotation pairs, keep the slot's RoPE
-// cosines and sines in registers and walk the heads in batches of
-// kPackBatch, whose rows are all loaded before any is converted.
+// threads per slot, each owning D/8 rotation pairs (j, j + D/2), so that a
+// wave covers exactly one kTile-slot tile.  The threads keep the slot's RoPE
+// cosines and sines in registers and walk the heads.
 // x: [B][L][H][D] bf16 -> rows [B][H][Lp][D] in slot order, fp16(x' * 2^e),
 // x' = RoPE(x) or x.
 // TILE = false: e is the exponent of the head's plane maximum pmax[b][h].
-// TILE = true: e is the exponent of the largest |x'| of the workgroup's 64
-// slots of the head (kExpMax for an all-zero tile), reduced over the
-// workgroup (one barrier per batch); it is stored in etile[b][h][block] and
-// folded into emin[b][h / group] (atomic minimum).  Slots s >= L are zero.
+// TILE = true: e is the exponent of the largest |x'| of the wave's tile of the
+// head (kExpMax for an all-zero tile), reduced inside the wave; it is stored
+// in etile[b][h][tile] (group_min_kernel takes the minimum over each group).
+// Slots s >= L are zero.
 constexpr int kPackHeads = 8;
-constexpr int kPackBatch = 1;
-
-// Rotated (or plain) pair e of a thread's bf16 words: low halves in words
-// 0 .. PER/8 - 1, high halves after them.
-template <int PER, bool ROPE>
-__device__ __forceinline__ void pair_at(const uint4 (&w)[PER / 4], const float2 (&cs)[PER], int e, float &lo,
-                                        float &hi) {
-  const uint16_t *u = reinterpret_cast<const uint16_t *>(w);
-  lo = bf16_to_f32(u[e]);
-  hi = bf16_to_f32(u[PER + e]);
-  if (ROPE) {
-    const float x1 = lo, x2 = hi;
-    lo = x1 * cs[e].x - x2 * cs[e].y;
-    hi = x2 * cs[e].x + x1 * cs[e].y;
-  }
-}
+constexpr int kPackSlots = 64;
 
 template <int D, bool ROPE, bool TILE>
 __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H, int32_t group,
                                                    const uint16_t *x, const int32_t *slot_tok,
                                                    const float2 *table, const uint32_t *pmax,
-                                                   uint16_t *rows, int32_t *etile, int32_t *emin) {
+                                                   uint16_t *rows, int32_t *etile) {
   constexpr int HALF = D / 2;
   constexpr int PER = HALF / 4;  // pairs per thread (4 threads per slot)
-  __shared__ uint32_t wmax[kPackBatch][4];
+  static_assert(kPackSlots == 4 * kTile, "a wave covers one tile");
   const int hgroups = (H + kPackHeads - 1) / kPackHeads;
   const int h0 = (int)(blockIdx.x % (unsigned)hgroups) * kPackHeads;
   const int blk = (int)(blockIdx.x / (unsigned)hgroups);
-  const int t0 = blk * 64, b = blockIdx.z;
+  const int t0 = blk * kPackSlots, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tt = tid >> 2, part = tid & 3;
   const int t = t0 + tt;
   const int j0 = part * PER;
   const int32_t tok = t < L ? slot_tok[(int64_t)b * L + t] : -1;
   float2 cs[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) cs[e] = make_float2(1.0f, 0.0f);
   if (ROPE) {
     const float2 *row = table + ((int64_t)b * Lp + t) * HALF + j0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) cs[e] = row[e];
   }
   const int h1 = min(H, h0 + kPackHeads);
-  for (int hb = h0; hb < h1; hb += kPackBatch) {
-    uint4 raw[kPackBatch][PER / 4];
+#pragma unroll 2
+  for (int h = h0; h < h1; ++h) {
+    float lo[PER], hi[PER];
 #pragma unroll
-    for (int k = 0; k < kPackBatch; ++k) {
-#pragma unroll
-      for (int c = 0; c < PER / 4; ++c) raw[k][c] = make_uint4(0, 0, 0, 0);
-      if (hb + k < h1 && tok >= 0) {
-        const uint16_t *src = x + (((int64_t)b * L + tok) * H + hb + k) * D;
-#pragma unroll
-        for (int c = 0; c < PER / 8; ++c) {
-          raw[k][c] = *reinterpret_cast<const uint4 *>(src + j0 + 8 * c);
-          raw[k][PER / 8 + c] = *reinterpret_cast<const uint4 *>(src + HALF + j0 + 8 * c);
-        }
-      }
-    }
-    if (TILE) {
-#pragma unroll
-      for (int k = 0; k < kPackBatch; ++k) {
-        uint32_t m = 0u;  // float bits of the largest magnitude (integer order)
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          float lo, hi;
-          pair_at<PER, ROPE>(raw[k], cs, e, lo, hi);
-          m = max(m, max(__float_as_uint(fabsf(lo)), __float_as_uint(fabsf(hi))));
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-        if (lane == 0) wmax[k][wave] = m;
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int k = 0; k < kPackBatch; ++k) {
-      const int h = hb + k;
-      if (h >= h1) break;
-      int ex;
-      if (TILE) {
-        const uint32_t m = max(max(wmax[k][0], wmax[k][1]), max(wmax[k][2], wmax[k][3]));
-        ex = m > 0u ? plane_exponent(m) : kExpMax;
-        if (tid == 0) {
-          etile[((int64_t)b * H + h) * (Lp / 64) + blk] = ex;
-          atomicMin(emin + 2 * ((int64_t)b * (H / group) + h / group), ex);
-        }
-      } else {
-        ex = plane_exponent(pmax[(int64_t)b * H + h]);
-      }
-      uint16_t lq[PER], hq[PER];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        float lo, hi;
-        pair_at<PER, ROPE>(raw[k], cs, e, lo, hi);
-        lq[e] = f32_to_f16_bits(ldexpf(lo, ex));
-        hq[e] = f32_to_f16_bits(ldexpf(hi, ex));
-      }
-      uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
+    for (int e = 0; e < PER; ++e) lo[e] = hi[e] = 0.0f;
+    if (tok >= 0) {
+      const uint16_t *src = x + (((int64_t)b * L + tok) * H + h) * D;
+      uint16_t lb[PER], hb[PER];
 #pragma unroll
       for (int c = 0; c < PER; c += 8) {
-        *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
-        *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
+        *reinterpret_cast<uint4 *>(&lb[c]) = *reinterpret_cast<const uint4 *>(src + j0 + c);
+        *reinterpret_cast<uint4 *>(&hb[c]) = *reinterpret_cast<const uint4 *>(src + HALF + j0 + c);
+      }
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        lo[e] = bf16_to_f32(lb[e]);
+        hi[e] = bf16_to_f32(hb[e]);
+        if (ROPE) {
+          const float x1 = lo[e], x2 = hi[e];
+          lo[e] = x1 * cs[e].x - x2 * cs[e].y;
+          hi[e] = x2 * cs[e].x + x1 * cs[e].y;
+        }
       }
     }
-    if (TILE) __syncthreads();  // wmax is reused by the next batch
+    int ex;
+    if (TILE) {
+      uint32_t m = 0u;  // float bits of the largest magnitude (integer order)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) m = max(m, max(__float_as_uint(fabsf(lo[e])), __float_as_uint(fabsf(hi[e]))));
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+      ex = m > 0u ? plane_exponent(m) : kExpMax;
+      if (lane == 0) etile[((int64_t)b * H + h) * (Lp / kTile) + t0 / kTile + wave] = ex;
+    } else {
+      ex = plane_exponent(pmax[(int64_t)b * H + h]);
+    }
+    uint16_t lq[PER], hq[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      lq[e] = f32_to_f16_bits(ldexpf(lo[e], ex));
+      hq[e] = f32_to_f16_bits(ldexpf(hi[e], ex));
+    }
+    uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
+#pragma unroll
+    for (int c = 0; c < PER; c += 8) {
+      *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
+      *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
+    }
   }
 }
 
 // Backward preprocessing, one workgroup per (64-slot block, group of
-// kPackHeads q heads, row) with the thread layout of pack_kernel, in batches
-// of kPackBatch heads whose dout and o rows are all loaded first; per slot s,
-// with t = slot_tok[s] the token there,
+// kPackHeads q heads, row) with the thread layout of pack_kernel (a wave per
+// tile): per head and slot s, with t = slot_tok[s] the token there,
 //   dsc[b][h][s] = sum_d dout * o of token t (float32 over bf16 inputs; the
 //                  units are applied by scale_delta_kernel),
-// and dout goes to its fp16 copy with the exponent of the block's largest
-// |dout| (kExpMax for an all-zero block), stored in etile[b][h][block] and
-// folded into emin[b][h / group] (atomic minimum).
+// and dout goes to its fp16 copy with the exponent of the tile's largest
+// |dout| (kExpMax for an all-zero tile), stored in etile[b][h][tile].
 template <int D>
 __global__ __launch_bounds__(256) void delta_pack_kernel(int32_t L, int32_t Lp, int32_t H, int32_t group,
                                                          const uint16_t *o, const uint16_t *dout,
                                                          const int32_t *slot_tok, uint16_t *rows, float *dsc,
-                                                         int32_t *etile, int32_t *emin) {
+                                                         int32_t *etile) {
   constexpr int HALF = D / 2;
   constexpr int PER = HALF / 4;
-  __shared__ uint32_t wmax[kPackBatch][4];
   const int hgroups = (H + kPackHeads - 1) / kPackHeads;
   const int h0 = (int)(blockIdx.x % (unsigned)hgroups) * kPackHeads;
   const int blk = (int)(blockIdx.x / (unsigned)hgroups);
-  const int t0 = blk * 64, b = blockIdx.z;
+  const int t0 = blk * kPackSlots, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tt = tid >> 2, part = tid & 3;
   const int t = t0 + tt;
   const int j0 = part * PER;
   const int32_t tok = t < L ? slot_tok[(int64_t)b * L + t] : -1;
   const int h1 = min(H, h0 + kPackHeads);
-  for (int hb = h0; hb < h1; hb += kPackBatch) {
-    uint4 dw[kPackBatch][PER / 4], ow[kPackBatch][PER / 4];  // bf16 words, low halves then high halves
+#pragma unroll 2
+  for (int h = h0; h < h1; ++h) {
+    uint4 dw[PER / 4], ow[PER / 4];  // bf16 words, low halves then high halves
 #pragma unroll
-    for (int k = 0; k < kPackBatch; ++k) {
+    for (int c = 0; c < PER / 4; ++c) dw[c] = ow[c] = make_uint4(0, 0, 0, 0);
+    if (tok >= 0) {
+      const int64_t base = (((int64_t)b * L + tok) * H + h) * D;
 #pragma unroll
-      for (int c = 0; c < PER / 4; ++c) dw[k][c] = ow[k][c] = make_uint4(0, 0, 0, 0);
-      if (hb + k < h1 && tok >= 0) {
-        const int64_t base = (((int64_t)b * L + tok) * H + hb + k) * D;
-#pragma unroll
-        for (int c = 0; c < PER / 8; ++c) {
-          dw[k][c] = *reinterpret_cast<const uint4 *>(dout + base + j0 + 8 * c);
-          dw[k][PER / 8 + c] = *reinterpret_cast<const uint4 *>(dout + base + HALF + j0 + 8 * c);
-          ow[k][c] = *reinterpret_cast<const uint4 *>(o + base + j0 + 8 * c);
-          ow[k][PER / 8 + c] = *reinterpret_cast<const uint4 *>(o + base + HALF + j0 + 8 * c);
-        }
+      for (int c = 0; c < PER / 8; ++c) {
+        dw[c] = *reinterpret_cast<const uint4 *>(dout + base + j0 + 8 * c);
+        dw[PER / 8 + c] = *reinterpret_cast<const uint4 *>(dout + base + HALF + j0 + 8 * c);
+        ow[c] = *reinterpret_cast<const uint4 *>(o + base + j0 + 8 * c);
+        ow[PER / 8 + c] = *reinterpret_cast<const uint4 *>(o + base + HALF + j0 + 8 * c);
       }
     }
-    float acc[kPackBatch];
+    float acc = 0.0f;
+    uint32_t m = 0u;
 #pragma unroll
-    for (int k = 0; k < kPackBatch; ++k) {
-      float a = 0.0f;
-      uint32_t m = 0u;
-#pragma unroll
-      for (int c = 0; c < PER / 4; ++c) {
-        a = dot2_bf16(ow[k][c].x, dw[k][c].x, a);
-        a = dot2_bf16(ow[k][c].y, dw[k][c].y, a);
-        a = dot2_bf16(ow[k][c].z, dw[k][c].z, a);
-        a = dot2_bf16(ow[k][c].w, dw[k][c].w, a);
-        m = max(m, absmax8_bf16_bits(dw[k][c]));
-      }
-      a += __shfl_xor(a, 1);  // the 4 threads of a slot
-      a += __shfl_xor(a, 2);
-      acc[k] = a;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-      if (lane == 0) wmax[k][wave] = m;
+    for (int c = 0; c < PER / 4; ++c) {
+      acc = dot2_bf16(ow[c].x, dw[c].x, acc);
+      acc = dot2_bf16(ow[c].y, dw[c].y, acc);
+      acc = dot2_bf16(ow[c].z, dw[c].z, acc);
+      acc = dot2_bf16(ow[c].w, dw[c].w, acc);
+      m = max(m, absmax8_bf16_bits(dw[c]));
     }
-    __syncthreads();
+    acc += __shfl_xor(acc, 1);  // the 4 threads of a slot
+    acc += __shfl_xor(acc, 2);
 #pragma unroll
-    for (int k = 0; k < kPackBatch; ++k) {
-      const int h = hb + k;
-      if (h >= h1) break;
-      const uint32_t m = max(max(wmax[k][0], wmax[k][1]), max(wmax[k][2], wmax[k][3]));
-      const int ex = m > 0u ? plane_exponent(m) : kExpMax;
-      if (tid == 0) {
-        etile[((int64_t)b * H + h) * (Lp / 64) + blk] = ex;
-        atomicMin(emin + 2 * ((int64_t)b * (H / group) + h / group) + 1, ex);
-      }
-      if (part == 0) dsc[((int64_t)b * H + h) * Lp + t] = acc[k];
-      const uint16_t *dl = reinterpret_cast<const uint16_t *>(dw[k]);
-      uint16_t lq[PER], hq[PER];
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    const int ex = m > 0u ? plane_exponent(m) : kExpMax;
+    if (lane == 0) etile[((int64_t)b * H + h) * (Lp / kTile) + t0 / kTile + wave] = ex;
+    if (part == 0) dsc[((int64_t)b * H + h) * Lp + t] = acc;
+    const uint16_t *dl = reinterpret_cast<const uint16_t *>(dw);
+    uint16_t lq[PER], hq[PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        lq[e] = f32_to_f16_bits(ldexpf(bf16_to_f32(dl[e]), ex));
-        hq[e] = f32_to_f16_bits(ldexpf(bf16_to_f32(dl[PER + e]), ex));
-      }
-      uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
-#pragma unroll
-      for (int c = 0; c < PER; c += 8) {
-        *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
-        *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
-      }
+    for (int e = 0; e < PER; ++e) {
+      lq[e] = f32_to_f16_bits(ldexpf(bf16_to_f32(dl[e]), ex));
+      hq[e] = f32_to_f16_bits(ldexpf(bf16_to_f32(dl[PER + e]), ex));
     }
-    __syncthreads();  // wmax is reused by the next batch
+    uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
+#pragma unroll
+    for (int c = 0; c < PER; c += 8) {
+      *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
+      *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
+    }
   }
+}
+
+// emin[2 * (b * Hkv + kv)] = the smallest tile exponent of the kv group's
+// heads, etile [B][Hq][MTS]: one workgroup per (row, kv group).
+__global__ __launch_bounds__(256) void group_min_kernel(int32_t Hq, int32_t group, int32_t MTS,
+                                                        const int32_t *etile, int32_t *emin) {
+  __shared__ int32_t wmin[4];
+  const int64_t gk = blockIdx.x;  // b * Hkv + kv
+  const int64_t n = (int64_t)group * MTS;
+  const int32_t *src = etile + gk * n;  // the group's heads are consecutive
+  int32_t m = kExpMax;
+  for (int64_t i = threadIdx.x; i < n; i += 256) m = min(m, src[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = min(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) wmin[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) emin[2 * gk] = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
 }
 
 // Units of the backward, per slot s of q head h in kv group kv, with eq, edo
@@ -326,7 +287,7 @@ __global__ __launch_bounds__(256) void scale_delta_kernel(int32_t B, int32_t L, 
   const int h = (int)(bh % Hq);
   const int64_t b = bh / Hq;
   const int kv = h / group, Hkv = Hq / group;
-  const int64_t tix = bh * (Lp / 64) + sl / 64;
+  const int64_t tix = bh * (Lp / kTile) + sl / kTile;
   const int eq = eqt[tix], edo = edot[tix];
   const int eqr = eref[2 * (b * Hkv + kv)], edor = eref[2 * (b * Hkv + kv) + 1];
   const int ev = plane_exponent(mv[b * Hkv + kv]);
@@ -423,11 +384,6 @@ __global__ __launch_bounds__(kOrderThreads) void work_order_kernel(int32_t n_row
   }
 }
 
-// p[i * stride] = value for i < n
-__global__ void set_words_kernel(int32_t *p, int32_t n, int32_t stride, int32_t value) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[(int64_t)i * stride] = value;
-}
 
 template <int D>
 void launch_absmax_d(int32_t B, int32_t L, const AbsmaxJob *jobs, hipStream_t s) {
@@ -437,26 +393,23 @@ void launch_absmax_d(int32_t B, int32_t L, const AbsmaxJob *jobs, hipStream_t s)
 template <int D, bool ROPE, bool TILE>
 void launch_pack_d(int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group, const void *x,
                    const int32_t *slot_tok, const float2 *table, const uint32_t *pmax, uint16_t *rows,
-                   int32_t *etile, int32_t *emin, hipStream_t s) {
+                   int32_t *etile, hipStream_t s) {
   const unsigned hgroups = (unsigned)((H + kPackHeads - 1) / kPackHeads);
-  const dim3 grid(hgroups * (unsigned)(Lp / 64), 1, B);
+  const dim3 grid(hgroups * (unsigned)(Lp / kPackSlots), 1, B);
   pack_kernel<D, ROPE, TILE><<<grid, 256, 0, s>>>(L, Lp, H, group, static_cast<const uint16_t *>(x), slot_tok, table,
-                                                 pmax, rows, etile, emin);
+                                                 pmax, rows, etile);
 }
 
 }  // namespace
 
-// RoPE table + clearing of the plane maxima (they start at zero) and of the
-// tile exponent minima (they start at kExpMax).
+// RoPE table + clearing of the plane maxima (they start at zero).
 void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int32_t half = in.D / 2;
   const int64_t total = (int64_t)in.B * ws.Lp * half;
-  const int32_t n_emax = 2 * in.B * in.Hkv;
-  int64_t n = total > ws.n_pmax ? total : (int64_t)ws.n_pmax;
-  if (n < n_emax) n = n_emax;
+  const int64_t n = total > ws.n_pmax ? total : (int64_t)ws.n_pmax;
   rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(in.B, in.L, ws.Lp, half, log2(in.rope_theta),
                                                                 in.layout.tok_pos, in.layout.slot_tok, ws.rope,
-                                                                ws.pmax, ws.n_pmax, ws.eref, n_emax);
+                                                                ws.pmax, ws.n_pmax);
 }
 
 // Plane maxima of k (times sqrt(2), the RoPE bound) and of v.
@@ -474,10 +427,11 @@ void launch_pack_q(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int32_t group = in.Hq / in.Hkv;
   if (in.D == 64)
     launch_pack_d<64, true, true>(in.B, in.L, ws.Lp, in.Hq, group, in.q, in.layout.slot_tok, ws.rope, nullptr,
-                                  ws.qr, ws.eqt, ws.eref, s);
+                                  ws.qr, ws.eqt, s);
   else
     launch_pack_d<128, true, true>(in.B, in.L, ws.Lp, in.Hq, group, in.q, in.layout.slot_tok, ws.rope, nullptr,
-                                   ws.qr, ws.eqt, ws.eref, s);
+                                   ws.qr, ws.eqt, s);
+  group_min_kernel<<<(unsigned)(in.B * in.Hkv), 256, 0, s>>>(in.Hq, group, ws.Lp / kTile, ws.eqt, ws.eref);
 }
 
 // k (RoPE) or v, one scale per plane.
@@ -485,11 +439,11 @@ void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t
                      const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
                      uint16_t *rows, hipStream_t s) {
   if (D == 64) {
-    if (rope) launch_pack_d<64, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
-    else launch_pack_d<64, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
+    if (rope) launch_pack_d<64, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, s);
+    else launch_pack_d<64, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, s);
   } else {
-    if (rope) launch_pack_d<128, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
-    else launch_pack_d<128, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
+    if (rope) launch_pack_d<128, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, s);
+    else launch_pack_d<128, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, s);
   }
 }
 
@@ -500,23 +454,21 @@ void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
                                                ws.q_order, ws.k_order);
 }
 
-// delta and the fp16 dout copy with its tile exponents (their group minima
-// are reset first: a backward may follow another on the same workspace).
+// delta and the fp16 dout copy with its tile exponents and their group minima.
 void launch_delta_pack(const opr_attn_in &in, const void *o, const void *dout, const AttnWs &ws,
                        hipStream_t s) {
-  const int32_t n = 2 * in.B * in.Hkv;
-  set_words_kernel<<<(n + 255) / 256, 256, 0, s>>>(ws.eref + 1, n / 2, 2, kExpMax);
   const int32_t group = in.Hq / in.Hkv;
   const unsigned hgroups = (unsigned)((in.Hq + kPackHeads - 1) / kPackHeads);
-  const dim3 grid(hgroups * (unsigned)(ws.Lp / 64), 1, in.B);
+  const dim3 grid(hgroups * (unsigned)(ws.Lp / kPackSlots), 1, in.B);
   const uint16_t *o16 = static_cast<const uint16_t *>(o);
   const uint16_t *d16 = static_cast<const uint16_t *>(dout);
   if (in.D == 64)
     delta_pack_kernel<64><<<grid, 256, 0, s>>>(in.L, ws.Lp, in.Hq, group, o16, d16, in.layout.slot_tok, ws.dor,
-                                               ws.dsc, ws.edot, ws.eref);
+                                               ws.dsc, ws.edot);
   else
     delta_pack_kernel<128><<<grid, 256, 0, s>>>(in.L, ws.Lp, in.Hq, group, o16, d16, in.layout.slot_tok, ws.dor,
-                                                ws.dsc, ws.edot, ws.eref);
+                                                ws.dsc, ws.edot);
+  group_min_kernel<<<(unsigned)(in.B * in.Hkv), 256, 0, s>>>(in.Hq, group, ws.Lp / kTile, ws.edot, ws.eref + 1);
 }
 
 void launch_scale_delta(const opr_attn_in &in, const float *lse, const AttnWs &ws, hipStream_t s) {

@@ -5,7 +5,6 @@
 // Descriptor (x, y):
 //   y bits 4w + 2b : 2-bit class (empty / partial / full) of the 32 x 32
 //                    sub-block that wave w meets in 32-row block b of the stage
-//   y bits 16..31  : dK/dV stages: the q' and dout tile exponents (+ 64)
 //   x              : first streamed row; dK/dV stages add the head (in the
 //                    kv group) at bits 24..31
 #pragma once
@@ -47,17 +46,19 @@ __device__ inline int build_q_stages(const int32_t *lst, const uint32_t *subs, i
 // Key-side kernel (dK/dV) of k-tile n: wave w owns key sub-column w; the
 // stages run over the q-tiles k_list[...] x the G heads of the kv group x the
 // two 64-query halves, flat index f = (tile * G + head) * 2 + half.  The
-// stage's 64 queries are one 64-slot tile of one head; the descriptor also
-// carries that tile's q' and dout exponents (eqt_g, edot_g: [G][MT64] of the
-// group) + 64 in y bits 16..23 and 24..31.
+// descriptor is (x, y, z, w): x and y as above, z the q' and w the dout
+// exponents (+ 64, one byte each) of the stage's four 16-query tiles
+// (eqt_g, edot_g: the group's [G][MTS] tile exponents).
+constexpr int kKStageCap = 512;  // dK/dV descriptors per list chunk (8 KB of LDS)
+
 __device__ inline int build_k_stages(const int32_t *lst, const uint32_t *subs_b, int NT, int n, int G,
-                                     int nnz, const int32_t *eqt_g, const int32_t *edot_g, int MT64,
-                                     int64_t *f, uint2 *stages, int lane) {
+                                     int nnz, const int32_t *eqt_g, const int32_t *edot_g, int MTS,
+                                     int64_t *f, uint4 *stages, int lane) {
   int count = 0;
   const int64_t total = (int64_t)nnz * G * 2;
-  while (*f < total && count + 64 <= kStageCap) {
+  while (*f < total && count + 64 <= kKStageCap) {
     const int64_t ff = *f + lane;
-    uint32_t cls = 0, x = 0;
+    uint32_t cls = 0, x = 0, z = 0, zw = 0;
     if (ff < total) {
       const int qh = (int)(ff & 1);
       const int64_t tj = ff >> 1;
@@ -70,17 +71,24 @@ __device__ inline int build_k_stages(const int32_t *lst, const uint32_t *subs_b,
         for (int qb = 0; qb < 2; ++qb) cls |= ((sub >> (2 * (4 * (2 * qh + qb) + w))) & 3u) << (4 * w + 2 * qb);
       x = (uint32_t)(m * 128 + 64 * qh) | ((uint32_t)hj << 24);
       if (cls != 0) {
-        const int64_t tix = (int64_t)hj * MT64 + 2 * m + qh;
-        cls |= ((uint32_t)(eqt_g[tix] + 64) << 16) | ((uint32_t)(edot_g[tix] + 64) << 24);
+        const int64_t tix = (int64_t)hj * MTS + (m * 128 + 64 * qh) / kTile;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          z |= (uint32_t)(eqt_g[tix + k] + 64) << (8 * k);
+          zw |= (uint32_t)(edot_g[tix + k] + 64) << (8 * k);
+        }
       }
     }
     const uint64_t bal = __ballot(cls != 0);
-    if (cls != 0) stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint2(x, cls);
+    if (cls != 0) stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint4(x, cls, z, zw);
     count += __popcll(bal);
     *f += 64;
   }
   if (*f > total) *f = total;
   return count;
 }
+
+// Exponent byte k (0..3) of a dK/dV descriptor's z or w word.
+__device__ __forceinline__ int stage_exponent(uint32_t z, int k) { return (int)((z >> (8 * k)) & 0xFFu) - 64; }
 
 }  // namespace opr

@@ -52,8 +52,8 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
     w.mk = w.pmax;
     w.mv = w.mk + (size_t)in.B * in.Hkv;
   }
-  const size_t tiles64 = (size_t)in.B * in.Hq * (Lp / 64);
-  w.eqt = cv.take<int32_t>(tiles64);
+  const size_t etiles = (size_t)in.B * in.Hq * (Lp / kTile);
+  w.eqt = cv.take<int32_t>(etiles);
   w.eref = cv.take<int32_t>((size_t)2 * in.B * in.Hkv);
   const size_t tiles = (size_t)in.B * (Lp / OPR_ATTN_BLOCK);
   w.q_order = cv.take<int32_t>(tiles);
@@ -62,7 +62,7 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   // everything above is the forward state; the backward part follows
   if (is_bwd) {
     w.dor = cv.take<uint16_t>(qn);
-    w.edot = cv.take<int32_t>(tiles64);
+    w.edot = cv.take<int32_t>(etiles);
     w.dsc = cv.take<float>((size_t)in.B * in.Hq * Lp);
     w.lse2 = cv.take<float>((size_t)in.B * in.Hq * Lp);
   }
@@ -97,7 +97,7 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->eqt = ws.eqt;
   p->edot = ws.edot;
   p->eref = ws.eref;
-  p->MT64 = ws.Lp / 64;
+  p->MTS = ws.Lp / kTile;
   p->q_order = ws.q_order;
   p->k_order = ws.k_order;
   p->slot_tok = in.layout.slot_tok;

@@ -55,7 +55,7 @@ struct AttnWs {
   // everything below is in slot (attention) order
   float2 *rope;         // [B][Lp][D/2] (cos, sin) at each slot's position id
   // fp16 copies [B][H][Lp][D], zero past L: k and v with one power-of-two
-  // scale per (row, kv head) plane, q and dout with one per 64-slot tile of
+  // scale per (row, kv head) plane, q and dout with one per 16-slot tile of
   // each (row, q head)
   uint16_t *qr;         // q after RoPE
   uint16_t *kr;         // k after RoPE
@@ -65,8 +65,9 @@ struct AttnWs {
   // (n_pmax words)
   uint32_t *pmax, *mk, *mv;
   int32_t n_pmax;
-  // tile exponents [B][Hq][Lp/64] of q (eqt) and dout (edot), and their
-  // minima over each kv group's heads and tiles, eref [B][Hkv][2] = (q, dout)
+  // tile exponents [B][Hq][Lp/16] of q (eqt) and dout (edot), one per 16-slot
+  // tile, and their minima over each kv group's heads and tiles,
+  // eref [B][Hkv][2] = (q, dout)
   int32_t *eqt;
   int32_t *edot;        //                                        (bwd)
   int32_t *eref;
