@@ -267,12 +267,15 @@ def cpu_baseline(rows, L, shape, t_np):
 
 
 def depth_sweep(torch, Bd, dev, Ns, steps):
+    """One conversation of N turns: one pass (as packed, and without the last
+    turn's context copy, which nothing sees) against the N passes."""
     out = []
     Hq, Hkv, D = I.DEPTH_HEADS["Hq"], I.DEPTH_HEADS["Hkv"], I.DEPTH_HEADS["D"]
     for N in Ns:
         conv = I.depth_conversation(N)
         rec = {"N": N}
-        for kind, rows in (("one_pass", [[conv]]), ("n_pass", [I.npass_conversations(conv)])):
+        for kind, rows in (("one_pass", [[conv]]), ("one_pass_elided", [[I.chunk_conversation(conv, 0, N, True)]]),
+                           ("n_pass", [I.npass_conversations(conv)])):
             L = I.row_used(rows[0])
             t = device_inputs(torch, 1, L, Hq, Hkv, D, I.SEEDS["depth"][1], dev)
             r = Runner(torch, Bd, rows, L, Hq, Hkv, D, t, dev)
@@ -282,27 +285,52 @@ def depth_sweep(torch, Bd, dev, Ns, steps):
             del r, t
             torch.cuda.empty_cache()
         rec["speedup"] = round(rec["n_pass"]["ms"] / rec["one_pass"]["ms"], 3)
+        rec["speedup_elided"] = round(rec["n_pass"]["ms"] / rec["one_pass_elided"]["ms"], 3)
         log(f"depth N={N}: {rec}")
         out.append(rec)
     return out
 
 
 def kpass_sweep(torch, Bd, dev, steps):
-    out = []
+    """K-pass rows of 32768 tokens: equal-turn splits for K in {1, 2, 4} (as
+    packed and with each chunk's last context copy left out), the N-pass rows,
+    and planned splits (opr_kpass_plan) under the longest sequence of each
+    elided equal split as the cap.  The planner's token weight is fitted from
+    the equal splits' times, ms ~ a * pairs + b * tokens."""
     Hq, Hkv, D = I.KPASS_HEADS["Hq"], I.KPASS_HEADS["Hkv"], I.KPASS_HEADS["D"]
     L = I.KPASS_ROW_LEN
-    for K in (1, 2, 4, "N"):
-        rows = I.kpass_rows(K)
+
+    def run(rec, rows):
         t = device_inputs(torch, len(rows), L, Hq, Hkv, D, I.SEEDS["kpass"][1], dev)
         r = Runner(torch, Bd, rows, L, Hq, Hkv, D, t, dev)
         ms = r.time_steps(steps, 1)
-        packed = sum(I.row_used(row) for row in rows)
-        longest = max(I.conv_len(c) for row in rows for c in row)
-        out.append({"K": K, "rows": len(rows), "packed_tokens": packed, "longest_sequence": longest,
-                    "ms": round(ms, 4)})
-        log(f"kpass K={K}: {out[-1]}")
+        rec.update({"rows": len(rows), "packed_tokens": sum(I.row_used(row) for row in rows),
+                    "longest_sequence": max(I.conv_len(c) for row in rows for c in row),
+                    "pairs": useful_pairs(torch, r.lay), "ms": round(ms, 4)})
+        log(f"kpass {rec}")
         del r, t
         torch.cuda.empty_cache()
+        return rec
+
+    out = []
+    for K in (1, 2, 4, "N"):
+        out.append(run({"K": K, "policy": "equal", "elide_last_rin": False}, I.kpass_rows(K)))
+    for K in (1, 2, 4):
+        out.append(run({"K": K, "policy": "equal", "elide_last_rin": True}, I.kpass_rows(K, elide_last_rin=True)))
+    eq = [x for x in out if x["policy"] == "equal"]
+    A = np.array([[x["pairs"], x["packed_tokens"]] for x in eq], dtype=np.float64)
+    coef, *_ = np.linalg.lstsq(A, np.array([x["ms"] for x in eq]), rcond=None)
+    weight = float(max(coef[1], 0.0) / coef[0]) if coef[0] > 0 else 0.0
+    convs = I.kpass_base_conversations(I.SEEDS["kpass"][0], L=L)
+    for cap_of in (1, 2, 4):
+        cap = next(x["longest_sequence"] for x in out if x["K"] == cap_of and x["elide_last_rin"])
+        chunks = []
+        for c in convs:
+            plan, _ = Bd.opr_kpass_plan(c, max_tokens=cap, tokens_weight=weight, elide_last_rin=True)
+            chunks += [I.chunk_conversation(c, p["first_turn"], p["first_turn"] + p["n_turns"], True) for p in plan]
+        rec = {"K": None, "policy": "planned", "elide_last_rin": True, "cap": cap, "tokens_weight": round(weight, 2),
+               "chunks": len(chunks)}
+        out.append(run(rec, I.pack_first_fit_decreasing(chunks, L)))
     base = next(x for x in out if x["K"] == "N")["ms"]
     for x in out:
         x["speedup_vs_npass"] = round(base / x["ms"], 3)

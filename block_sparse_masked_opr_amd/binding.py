@@ -52,6 +52,11 @@ class OprAttnIn(ctypes.Structure):
                 ("timing_events", ctypes.c_void_p), ("reuse_fwd_workspace", ctypes.c_int32)]
 
 
+class OprChunk(ctypes.Structure):
+    _fields_ = [("first_turn", ctypes.c_int32), ("n_turns", ctypes.c_int32),
+                ("tokens", ctypes.c_int32), ("rin_elided", ctypes.c_int32), ("pairs", ctypes.c_int64)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"libopr.so is not built ({_LIB_PATH}); run "
@@ -73,6 +78,10 @@ def _load() -> ctypes.CDLL:
     lib.opr_token_ce.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.opr_token_ce_workspace_size.restype = sz
     lib.opr_token_ce_workspace_size.argtypes = [i32, i32]
+    lib.opr_kpass_plan.restype = i32
+    lib.opr_kpass_plan.argtypes = [ctypes.POINTER(OprTurn), i32, i32, i32, ctypes.c_double, i32,
+                                   ctypes.POINTER(OprChunk), ctypes.POINTER(i32),
+                                   ctypes.POINTER(ctypes.c_double)]
     lib.opr_status_string.restype = ctypes.c_char_p
     lib.opr_status_string.argtypes = [i32]
     return lib
@@ -82,7 +91,7 @@ LIB = _load()
 
 EXPORTED = ("opr_build_layout", "opr_build_layout_workspace_size", "opr_attn_fwd",
             "opr_attn_bwd", "opr_attn_workspace_size", "opr_token_ce", "opr_token_ce_workspace_size",
-            "opr_status_string")
+            "opr_kpass_plan", "opr_status_string")
 
 
 def opr_status_string(status: int) -> str:
@@ -96,6 +105,25 @@ def _check(status: int, what: str) -> None:
 
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def opr_kpass_plan(conv: Sequence[Sequence[int]], n_chunks: int = 0, max_tokens: int = 0,
+                   tokens_weight: float = 0.0, elide_last_rin: bool = True):
+    """Chunk plan of one conversation (a list of (h, t, r_in, r_out) turns).
+
+    Returns (chunks, cost) with chunks a list of dicts (first_turn, n_turns,
+    tokens, rin_elided, pairs); raises OprError on invalid input or when no
+    split meets max_tokens."""
+    n = len(conv)
+    arr = (OprTurn * max(n, 1))(*[OprTurn(*map(int, t)) for t in conv])
+    out = (OprChunk * max(n, 1))()
+    n_out = ctypes.c_int32(0)
+    cost = ctypes.c_double(0.0)
+    _check(LIB.opr_kpass_plan(arr, n, int(n_chunks), int(max_tokens), float(tokens_weight),
+                              1 if elide_last_rin else 0, out, ctypes.byref(n_out), ctypes.byref(cost)),
+           "opr_kpass_plan")
+    chunks = [{f: getattr(out[i], f) for f, _ in OprChunk._fields_} for i in range(n_out.value)]
+    return chunks, cost.value
 
 
 def opr_build_layout_workspace_size(B: int, L: int, n_convs: int, n_turns: int) -> int:

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libopr.so")
 ARCH = "gfx950"
 
 SOURCES = ["opr_api.cpp", "layout.hip", "attn_prologue.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_dq.hip",
-           "token_ce.hip"]
+           "token_ce.hip", "kpass_plan.cpp"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

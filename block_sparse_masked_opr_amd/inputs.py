@@ -181,21 +181,32 @@ def npass_conversations(conv: Conversation) -> List[Conversation]:
     return out
 
 
-def kpass_conversations(conv: Conversation, K: int) -> List[Conversation]:
+def chunk_conversation(conv: Conversation, a: int, b: int, elide_last_rin: bool = False) -> Conversation:
+    """The sequence of a K-pass chunk that trains turns [a, b) of a conversation.
+
+    The turns before a are history written (h, 0, r_in, 0); turns a .. b-1 keep
+    every segment.  With elide_last_rin, turn b-1 loses its context copy r_in
+    (written (h, t, 0, r_out)), which no token of the sequence sees.
+    """
+    if not 0 <= a < b <= len(conv):
+        raise ValueError(f"chunk [{a}, {b}) of a {len(conv)}-turn conversation")
+    hist = [(h, 0, r_in, 0) for (h, _t, r_in, _r) in conv[:a]]
+    own = [tuple(x) for x in conv[a:b]]
+    if elide_last_rin:
+        h, t, _r_in, r_out = own[-1]
+        own[-1] = (h, t, 0, r_out)
+    return hist + own
+
+
+def kpass_conversations(conv: Conversation, K: int, elide_last_rin: bool = False) -> List[Conversation]:
     """Split a conversation into K contiguous chunks of near-equal turn count.
 
-    Chunk k holds turns [floor(kN/K), floor((k+1)N/K)); the turns before it are
-    history written (h, 0, r, 0); the chunk's own turns keep both response
-    copies.  K is capped at N.
+    Chunk k holds turns [floor(kN/K), floor((k+1)N/K)) (see chunk_conversation).
+    K is capped at N.
     """
     N = len(conv)
     K = max(1, min(K, N))
-    out = []
-    for k in range(K):
-        a, b = (k * N) // K, ((k + 1) * N) // K
-        hist = [(h, 0, r_in, 0) for (h, _t, r_in, _r) in conv[:a]]
-        out.append(hist + list(conv[a:b]))
-    return out
+    return [chunk_conversation(conv, (k * N) // K, ((k + 1) * N) // K, elide_last_rin) for k in range(K)]
 
 
 def _kpass_sampler(rng):
@@ -218,12 +229,12 @@ def kpass_base_conversations(seed: int = 401, rows: int = 4, L: int = KPASS_ROW_
     return [c for row in packed for c in row]
 
 
-def kpass_rows(K, seed: int = 401, L: int = KPASS_ROW_LEN) -> List[Row]:
+def kpass_rows(K, seed: int = 401, L: int = KPASS_ROW_LEN, elide_last_rin: bool = False) -> List[Row]:
     """Rows of L tokens for K in {1, 2, 4, ...} or K == 'N' (N-pass)."""
     convs = kpass_base_conversations(seed, L=L)
     chunks = []
     for c in convs:
-        chunks.extend(npass_conversations(c) if K == "N" else kpass_conversations(c, int(K)))
+        chunks.extend(npass_conversations(c) if K == "N" else kpass_conversations(c, int(K), elide_last_rin))
     return pack_first_fit_decreasing(chunks, L)
 
 

@@ -263,6 +263,52 @@ opr_status opr_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const void *
 /* Workspace bytes for opr_token_ce with a gradient; 0 if F or V is invalid. */
 size_t opr_token_ce_workspace_size(int32_t F, int32_t V);
 
+/* One chunk of a K-pass plan (see opr_kpass_plan). */
+typedef struct {
+  int32_t first_turn; /* the chunk trains turns [first_turn, first_turn + n_turns) */
+  int32_t n_turns;
+  int32_t tokens;     /* packed tokens of the chunk's sequence */
+  int32_t rin_elided; /* 1 if r_in of its last turn is left out */
+  int64_t pairs;      /* allowed (query, key) pairs of the sequence */
+} opr_chunk;
+
+/*
+ * opr_kpass_plan - split one conversation into K-pass chunks (host only; no
+ * HIP call).
+ *
+ * The K-pass variant trains a conversation in K sequences instead of one,
+ * trading speed for memory between the one-pass and N-pass extremes (wiki
+ * summary, section "实验结果", K-Pass; section "关键洞察", item 3).  The
+ * sequence of a chunk of turns [a, b) is the history turns j < a written
+ * (h_j, 0, r_in_j, 0), context only, followed by turns a .. b-1 unchanged;
+ * with elide_last_rin, turn b-1 is written (h, t, 0, r_out): its context copy
+ * is seen by no query of the sequence (only later turns see a turn's r_in,
+ * and it is not scored), so dropping it changes no other token's position id
+ * or result.  Passing these turn lists to opr_build_layout builds the rows.
+ *
+ * Among all splits into contiguous chunks, the call returns one that
+ * minimises sum over chunks of (pairs + tokens_weight * tokens), where pairs
+ * is the number of allowed (query, key) pairs of the chunk's sequence (every
+ * token sees its position id + 1 keys) and tokens its length, subject to
+ * tokens <= max_tokens for every chunk.  Ties go to fewer chunks.
+ *
+ *  turns          host [n_turns], n_turns >= 1, every length >= 0, and the
+ *                 sum of all lengths < 2^31.
+ *  n_chunks       exactly this many chunks (1 .. n_turns), or 0 for any number.
+ *  max_tokens     cap on a chunk sequence's length; 0 for none.
+ *  tokens_weight  >= 0, finite: the cost of a token in units of one pair.
+ *  chunks         host [n_turns] (room for the most chunks a plan can have);
+ *                 entries [0, *n_out) are written in turn order.
+ *  n_out          host, the number of chunks.
+ *  cost           host, may be NULL: the minimised objective.
+ * Errors: OPR_E_INVALID (null pointer, counts, lengths, weight),
+ * OPR_E_CAPACITY (no split meets max_tokens: some turn's sequence alone is
+ * longer, or n_chunks chunks cannot all fit).  On error nothing is written.
+ */
+opr_status opr_kpass_plan(const opr_turn *turns, int32_t n_turns, int32_t n_chunks, int32_t max_tokens,
+                          double tokens_weight, int32_t elide_last_rin, opr_chunk *chunks, int32_t *n_out,
+                          double *cost);
+
 /* Static, human-readable name of a status code. */
 const char *opr_status_string(opr_status status);
 

@@ -567,3 +567,69 @@ def token_ce_grad(feats: np.ndarray, W: np.ndarray, labels: np.ndarray) -> np.nd
     p /= p.sum(axis=1, keepdims=True)
     p[np.arange(len(labels)), labels] -= 1.0
     return p @ _f64(W).T
+
+
+# ----------------------------------------------------------------------------
+# K-pass chunks (wiki summary, "实验结果": K-Pass; "关键洞察", item 3)
+# ----------------------------------------------------------------------------
+def kpass_chunk(turns, a: int, b: int, elide_last_rin: bool):
+    """The sequence that trains turns [a, b) of a conversation in the K-pass variant.
+
+    The earlier turns are context only: their human message and the context copy
+    of their response, no reasoning and no generation copy (the same history an
+    N-pass sequence carries, "问题背景").  Turns a .. b-1 are stored in full.
+    With elide_last_rin the context copy of turn b-1 is left out: only later
+    turns may see a context copy, and there are none in this sequence.
+    """
+    seq = [(h, 0, r_in, 0) for (h, _t, r_in, _r) in turns[:a]]
+    for j in range(a, b):
+        h, t, r_in, r_out = turns[j]
+        if elide_last_rin and j == b - 1:
+            r_in = 0
+        seq.append((h, t, r_in, r_out))
+    return seq
+
+
+def kpass_chunk_size(turns, a: int, b: int, elide_last_rin: bool) -> Tuple[int, int]:
+    """(tokens, allowed pairs) of a chunk's sequence, the pairs counted from its mask."""
+    seq = kpass_chunk(turns, a, b, elide_last_rin)
+    n = sum(sum(x) for x in seq)
+    if n == 0:
+        return 0, 0
+    return n, useful_pairs(layout([[seq]], n))
+
+
+def kpass_best_splits(turns, n_chunks: int, max_tokens: int, weight: float, elide_last_rin: bool):
+    """Every split of the turns into contiguous chunks, scored by brute force.
+
+    A split's cost is the sum over its chunks of pairs + weight * tokens; a
+    split is admissible when every chunk has at most max_tokens tokens (0: no
+    cap) and, if n_chunks > 0, it has exactly n_chunks chunks.  Returns
+    (least cost, the admissible splits of least cost as lists of chunk starts),
+    or (inf, []) when none is admissible.  Exponential in the turn count: for
+    small conversations only.
+    """
+    N = len(turns)
+    size = {}
+    best, arg = math.inf, []
+    for bits in range(1 << (N - 1)):
+        starts = [0] + [j for j in range(1, N) if bits >> (j - 1) & 1]
+        if n_chunks > 0 and len(starts) != n_chunks:
+            continue
+        ends = starts[1:] + [N]
+        cost, ok = 0.0, True
+        for a, b in zip(starts, ends):
+            if (a, b) not in size:
+                size[(a, b)] = kpass_chunk_size(turns, a, b, elide_last_rin)
+            tok, pairs = size[(a, b)]
+            if max_tokens > 0 and tok > max_tokens:
+                ok = False
+                break
+            cost += pairs + weight * tok
+        if not ok:
+            continue
+        if cost < best:
+            best, arg = cost, [starts]
+        elif cost == best:
+            arg.append(starts)
+    return best, arg

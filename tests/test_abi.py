@@ -30,7 +30,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(Bd):
     names = declared_entry_points()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     lib = ctypes.CDLL(Bd._LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
