@@ -12,7 +12,10 @@ Prints one JSON line: useful TFLOP/s (12 * D * Hq * P, P = allowed query-key
 pairs, recomputation not counted), conversation tokens/s, the roofline of the
 dominant kernel (timed with HIP events on its own stream), the fp64 CPU oracle
 timed on a bounded sample, and (unless --no-sweep) the one-pass vs N-pass
-speedup across conversation depth and the K-pass trade-off.
+speedup across conversation depth and the K-pass trade-off.  Beside the
+headline it also times the per-token loss step and (unless --no-block) the
+same rows through a whole attention block (projections, q/k norms, attention;
+opr_block_fwd / opr_block_bwd), and the block's one-pass vs N-pass speedup.
 """
 from __future__ import annotations
 
@@ -209,6 +212,128 @@ class Runner:
         return s.elapsed_time(e) / steps
 
 
+class BlockRunner:
+    """The attention block (hipBLASLt projections, per-head RMS norms of q and
+    k, the masked attention, output projection) on seeded synthetic weights and
+    rows drawn on the device; step() = layout + block fwd + block bwd."""
+
+    FWD = ("qkv_proj", "qk_norm", "attn_fwd", "o_proj")
+    BWD = ("o_proj_grad", "qk_norm_recompute", "attn_bwd", "qk_norm_grad", "qkv_proj_grad")
+
+    def __init__(self, torch, Bd, rows, L, Hq, Hkv, D, dm, dev, seed=701, theta=1.0e6):
+        self.torch, self.Bd, self.rows, self.L, self.theta = torch, Bd, rows, L, theta
+        self.Hq, self.Hkv, self.D, self.dm = Hq, Hkv, D, dm
+        B = len(rows)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+
+        def rn(shape, s):
+            return (torch.randn(shape, generator=g, device=dev) * s).to(torch.bfloat16)
+
+        self.wts = Bd.BlockWeights(rn(((Hq + 2 * Hkv) * D, dm), 1.0 / math.sqrt(dm)),
+                                   rn((dm, Hq * D), 1.0 / math.sqrt(Hq * D)),
+                                   torch.rand(D, generator=g, device=dev) + 0.5,
+                                   torch.rand(D, generator=g, device=dev) + 0.5, Hq, Hkv, D)
+        self.x, self.dy = rn((B, L, dm), 1.0), rn((B, L, dm), 1.0)
+        self.lay = Bd.opr_build_layout(rows, L, 128, 128, device=dev)
+        cpr, tpc, turns = I.flatten_rows(rows)
+        self.lws = torch.empty(Bd.opr_build_layout_workspace_size(B, L, len(tpc), len(turns)), dtype=torch.uint8,
+                               device=dev)
+        self.ws = torch.empty(Bd.opr_block_workspace_size(B, L, Hq, Hkv, D, dm, True), dtype=torch.uint8, device=dev)
+        e = dict(device=dev)
+        self.fwd_out = (torch.empty((B, L, dm), dtype=torch.bfloat16, **e),
+                        torch.empty((B, L, (Hq + 2 * Hkv) * D), dtype=torch.bfloat16, **e),
+                        torch.empty((B, L, Hq, D), dtype=torch.bfloat16, **e),
+                        torch.empty((B, Hq, L), dtype=torch.float32, **e))
+        self.bwd_out = (torch.empty_like(self.x), torch.empty(self.wts.w_qkv.shape, dtype=torch.float32, **e),
+                        torch.empty(self.wts.w_o.shape, dtype=torch.float32, **e),
+                        torch.empty((D,), dtype=torch.float32, **e), torch.empty((D,), dtype=torch.float32, **e))
+
+    def step(self, ev_f=None, ev_b=None):
+        Bd = self.Bd
+        Bd.opr_build_layout(self.rows, self.L, 128, 128, device=self.x.device, workspace=self.lws, out=self.lay)
+        y, qkv, o, lse = Bd.opr_block_fwd(self.x, self.wts, self.lay, self.theta, workspace=self.ws,
+                                          out=self.fwd_out, events=ev_f)
+        Bd.opr_block_bwd(self.x, self.wts, self.lay, qkv, o, lse, self.dy, self.theta, workspace=self.ws,
+                         out=self.bwd_out, events=ev_b, reuse_fwd_workspace=True)
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            self.step()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps
+
+    def stage_ms(self, ev, n):
+        """Mean time of each stage over n steps with HIP events (recorded by the library)."""
+        out = {k: 0.0 for k in self.FWD + self.BWD}
+        f, b = ev.array(5), ev.array(6)
+        for _ in range(n):
+            self.step(f, b)
+            self.torch.cuda.synchronize()
+            for i, k in enumerate(self.FWD):
+                out[k] += ev.ms(f[i], f[i + 1]) / n
+            for i, k in enumerate(self.BWD):
+                out[k] += ev.ms(b[i], b[i + 1]) / n
+        ev.free(f)
+        ev.free(b)
+        return out
+
+    def gemm_flops(self):
+        T = self.x.shape[0] * self.x.shape[1]
+        return 6.0 * T * self.dm * ((self.Hq + 2 * self.Hkv) * self.D + self.Hq * self.D)
+
+
+def block_step(torch, Bd, dev, rows, shape, steps, warmup):
+    """The 2 x 16384 workload through the whole attention block (d_model of
+    the Qwen-3 model with these heads), fwd + bwd."""
+    dm = I.BLOCK_D_MODEL[shape.Hq]
+    r = BlockRunner(torch, Bd, rows, shape.L, shape.Hq, shape.Hkv, shape.D, dm, dev)
+    ms = r.time_steps(steps, warmup)
+    st = r.stage_ms(HipEvents(torch), 5)
+    P = useful_pairs(torch, r.lay)
+    gemm_ms = sum(st[k] for k in ("qkv_proj", "o_proj", "o_proj_grad", "qkv_proj_grad"))
+    attn_ms = st["attn_fwd"] + st["attn_bwd"]
+    conv_tokens = sum(I.conv_logical_tokens(c) for row in rows for c in row)
+    out = {"workload": f"packed_fwd_bwd rows through one block, d_model {dm}", "d_model": dm, "ms": round(ms, 4),
+           "tokens_per_s": round(conv_tokens / (ms * 1e-3), 1),
+           "stages_ms": {k: round(v, 4) for k, v in st.items()},
+           "gemm": {"ms": round(gemm_ms, 4), "tflops": round(r.gemm_flops() / (gemm_ms * 1e-3) / 1e12, 1),
+                    "frac_of_bf16_peak": round(r.gemm_flops() / (gemm_ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4)},
+           "attention": {"ms": round(attn_ms, 4),
+                         "useful_tflops": round(12.0 * shape.D * shape.Hq * P / (attn_ms * 1e-3) / 1e12, 1)}}
+    log(f"block step {out}")
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
+def block_depth(torch, Bd, dev, Ns, steps):
+    """One conversation of N turns through the block: one pass against N passes."""
+    Hq, Hkv, D = I.DEPTH_HEADS["Hq"], I.DEPTH_HEADS["Hkv"], I.DEPTH_HEADS["D"]
+    dm = I.BLOCK_D_MODEL[Hq]
+    out = []
+    for N in Ns:
+        conv = I.depth_conversation(N)
+        rec = {"N": N, "d_model": dm}
+        for kind, rows in (("one_pass", [[conv]]), ("n_pass", [I.npass_conversations(conv)])):
+            L = I.row_used(rows[0])
+            r = BlockRunner(torch, Bd, rows, L, Hq, Hkv, D, dm, dev)
+            rec[kind] = {"tokens": L, "ms": round(r.time_steps(steps, 1), 4)}
+            del r
+            torch.cuda.empty_cache()
+        rec["speedup"] = round(rec["n_pass"]["ms"] / rec["one_pass"]["ms"], 3)
+        log(f"block depth N={N}: {rec}")
+        out.append(rec)
+    return out
+
+
 def loss_step(torch, Bd, r, shape, steps, dev):
     """opr_token_ce on the forward's output: per-token loss of a V = 32 head on
     the t and r_out rows and its gradient (the loss step of training); bound
@@ -344,6 +469,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true", help="skip the depth and K-pass sweeps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-block", action="store_true", help="skip the attention-block measurements")
     ap.add_argument("--sweep-steps", type=int, default=3)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
@@ -443,9 +569,13 @@ def main():
     log(f"loss step {result['loss_step']['ms']:.4f} ms, {result['loss_step']['roofline']['achieved']} GB/s")
     del r
     torch.cuda.empty_cache()
+    if not args.no_block:
+        result["block_step"] = block_step(torch, Bd, dev, rows, shape, args.steps, args.warmup)
     if not args.no_sweep:
         result["depth_sweep"] = depth_sweep(torch, Bd, dev, [2, 4, 8, 16, 32], args.sweep_steps)
         result["kpass"] = kpass_sweep(torch, Bd, dev, args.sweep_steps)
+        if not args.no_block:
+            result["block_depth"] = block_depth(torch, Bd, dev, [2, 4, 8, 16, 32], args.sweep_steps)
     if not args.no_cpu:
         log("timing the CPU oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(rows, shape.L, shape, t_np)

@@ -52,6 +52,18 @@ class OprAttnIn(ctypes.Structure):
                 ("timing_events", ctypes.c_void_p), ("reuse_fwd_workspace", ctypes.c_int32)]
 
 
+class OprBlockIn(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("L", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("rope_theta", ctypes.c_double),
+                ("norm_eps", ctypes.c_float),
+                ("x", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p),
+                ("g_q", ctypes.c_void_p), ("g_k", ctypes.c_void_p),
+                ("layout", OprLayout),
+                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("timing_events", ctypes.c_void_p), ("reuse_fwd_workspace", ctypes.c_int32)]
+
+
 class OprChunk(ctypes.Structure):
     _fields_ = [("first_turn", ctypes.c_int32), ("n_turns", ctypes.c_int32),
                 ("tokens", ctypes.c_int32), ("rin_elided", ctypes.c_int32), ("pairs", ctypes.c_int64)]
@@ -78,6 +90,12 @@ def _load() -> ctypes.CDLL:
     lib.opr_token_ce.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.opr_token_ce_workspace_size.restype = sz
     lib.opr_token_ce_workspace_size.argtypes = [i32, i32]
+    lib.opr_block_fwd.restype = i32
+    lib.opr_block_fwd.argtypes = [ctypes.POINTER(OprBlockIn), vp, vp, vp, vp, vp, sz, vp]
+    lib.opr_block_bwd.restype = i32
+    lib.opr_block_bwd.argtypes = [ctypes.POINTER(OprBlockIn), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.opr_block_workspace_size.restype = sz
+    lib.opr_block_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int]
     lib.opr_kpass_plan.restype = i32
     lib.opr_kpass_plan.argtypes = [ctypes.POINTER(OprTurn), i32, i32, i32, ctypes.c_double, i32,
                                    ctypes.POINTER(OprChunk), ctypes.POINTER(i32),
@@ -91,7 +109,8 @@ LIB = _load()
 
 EXPORTED = ("opr_build_layout", "opr_build_layout_workspace_size", "opr_attn_fwd",
             "opr_attn_bwd", "opr_attn_workspace_size", "opr_token_ce", "opr_token_ce_workspace_size",
-            "opr_kpass_plan", "opr_status_string")
+            "opr_block_fwd", "opr_block_bwd", "opr_block_workspace_size", "opr_kpass_plan",
+            "opr_status_string")
 
 
 def opr_status_string(status: int) -> str:
@@ -302,3 +321,97 @@ def opr_token_ce(o: torch.Tensor, w: torch.Tensor, labels: torch.Tensor, lay: La
                           None if dout is None else dout.data_ptr(), ws_ptr, ws_n, _stream(o.device))
     _check(st, "opr_token_ce")
     return loss, dout
+
+
+# ----------------------------------------------------------------------------
+# attention block
+# ----------------------------------------------------------------------------
+def opr_block_workspace_size(B: int, L: int, Hq: int, Hkv: int, D: int, d_model: int, is_bwd: bool) -> int:
+    return int(LIB.opr_block_workspace_size(B, L, Hq, Hkv, D, d_model, 1 if is_bwd else 0))
+
+
+class BlockWeights:
+    """Weights of one attention block: w_qkv bf16 [(Hq + 2 Hkv) D, d_model],
+    w_o bf16 [d_model, Hq D], g_q and g_k fp32 [D]."""
+
+    def __init__(self, w_qkv, w_o, g_q, g_k, Hq: int, Hkv: int, D: int):
+        self.w_qkv, self.w_o, self.g_q, self.g_k = w_qkv, w_o, g_q, g_k
+        self.Hq, self.Hkv, self.D = Hq, Hkv, D
+        self.d_model = w_qkv.shape[1]
+        if tuple(w_qkv.shape) != ((Hq + 2 * Hkv) * D, self.d_model) or tuple(w_o.shape) != (self.d_model, Hq * D):
+            raise ValueError("w_qkv must be [(Hq + 2 Hkv) D, d_model] and w_o [d_model, Hq D]")
+        for name, t in (("w_qkv", w_qkv), ("w_o", w_o)):
+            if t.dtype != torch.bfloat16 or not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous bfloat16")
+        for name, t in (("g_q", g_q), ("g_k", g_k)):
+            if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (D,):
+                raise ValueError(f"{name} must be contiguous float32 [D]")
+
+
+def _block_in(x, wts: BlockWeights, lay: Layout, theta, scale, eps, events, reuse=False) -> OprBlockIn:
+    B, L, d = x.shape
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or d != wts.d_model:
+        raise ValueError("x must be contiguous bfloat16 [B, L, d_model]")
+    if (lay.B, lay.L) != (B, L):
+        raise ValueError("layout built for a different B or L")
+    return OprBlockIn(B, L, wts.Hq, wts.Hkv, wts.D, d, float(scale), float(theta), float(eps),
+                      x.data_ptr(), wts.w_qkv.data_ptr(), wts.w_o.data_ptr(), wts.g_q.data_ptr(),
+                      wts.g_k.data_ptr(), lay.c_struct(), lay.block_q, lay.block_k,
+                      None if events is None else ctypes.addressof(events), 1 if reuse else 0)
+
+
+def opr_block_fwd(x, wts: BlockWeights, lay: Layout, theta: float = 1.0e6, scale: float = 0.0,
+                  eps: float = 1.0e-6, workspace: Optional[torch.Tensor] = None, out=None, events=None):
+    """Returns (y bf16 [B, L, d_model], qkv bf16 [B, L, (Hq + 2 Hkv) D],
+    o bf16 [B, L, Hq, D], lse fp32 [B, Hq, L]); qkv, o and lse feed
+    opr_block_bwd.  ``events``: optional ctypes array of 5 hipEvent_t."""
+    a = _block_in(x, wts, lay, theta, scale, eps, events)
+    B, L, d = x.shape
+    need = opr_block_workspace_size(B, L, wts.Hq, wts.Hkv, wts.D, d, False)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if out is None:
+        e = dict(device=x.device)
+        y = torch.empty((B, L, d), dtype=torch.bfloat16, **e)
+        qkv = torch.empty((B, L, (wts.Hq + 2 * wts.Hkv) * wts.D), dtype=torch.bfloat16, **e)
+        o = torch.empty((B, L, wts.Hq, wts.D), dtype=torch.bfloat16, **e)
+        lse = torch.empty((B, wts.Hq, L), dtype=torch.float32, **e)
+    else:
+        y, qkv, o, lse = out
+    st = LIB.opr_block_fwd(ctypes.byref(a), y.data_ptr(), qkv.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           workspace.data_ptr(), workspace.numel(), _stream(x.device))
+    _check(st, "opr_block_fwd")
+    return y, qkv, o, lse
+
+
+def opr_block_bwd(x, wts: BlockWeights, lay: Layout, qkv, o, lse, dy, theta: float = 1.0e6, scale: float = 0.0,
+                  eps: float = 1.0e-6, workspace: Optional[torch.Tensor] = None, out=None, events=None,
+                  reuse_fwd_workspace: bool = False):
+    """Returns (dx bf16 like x, dw_qkv fp32 like w_qkv, dw_o fp32 like w_o,
+    dg_q fp32 [D], dg_k fp32 [D]).  ``events``: optional ctypes array of 6.
+    ``reuse_fwd_workspace``: ``workspace`` is the one the matching
+    opr_block_fwd call just used (its normalised q, k, v and attention state
+    are reused)."""
+    if reuse_fwd_workspace and workspace is None:
+        raise ValueError("reuse_fwd_workspace needs the forward's workspace")
+    a = _block_in(x, wts, lay, theta, scale, eps, events, reuse_fwd_workspace)
+    B, L, d = x.shape
+    if dy.dtype != torch.bfloat16 or not dy.is_contiguous() or dy.shape != x.shape:
+        raise ValueError("dy must be contiguous bfloat16 shaped like x")
+    need = opr_block_workspace_size(B, L, wts.Hq, wts.Hkv, wts.D, d, True)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if out is None:
+        e = dict(device=x.device)
+        dx = torch.empty_like(x)
+        dw_qkv = torch.empty(wts.w_qkv.shape, dtype=torch.float32, **e)
+        dw_o = torch.empty(wts.w_o.shape, dtype=torch.float32, **e)
+        dg_q = torch.empty((wts.D,), dtype=torch.float32, **e)
+        dg_k = torch.empty((wts.D,), dtype=torch.float32, **e)
+    else:
+        dx, dw_qkv, dw_o, dg_q, dg_k = out
+    st = LIB.opr_block_bwd(ctypes.byref(a), qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), dy.data_ptr(),
+                           dx.data_ptr(), dw_qkv.data_ptr(), dw_o.data_ptr(), dg_q.data_ptr(), dg_k.data_ptr(),
+                           workspace.data_ptr(), workspace.numel(), _stream(x.device))
+    _check(st, "opr_block_bwd")
+    return dx, dw_qkv, dw_o, dg_q, dg_k

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libopr.so")
 ARCH = "gfx950"
 
 SOURCES = ["opr_api.cpp", "layout.hip", "attn_prologue.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_dq.hip",
-           "token_ce.hip", "kpass_plan.cpp"]
+           "token_ce.hip", "kpass_plan.cpp", "gemm.cpp", "block.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -56,7 +56,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
-           "-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
+           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

@@ -25,6 +25,14 @@ hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, f
 hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq, float *dk,
                                    float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev);
 size_t token_ce_ws_bytes(int32_t F, int32_t V);
+bool gemm_bf16(bool trans_a, bool trans_b, int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
+               bool c_f32, void *ws, size_t ws_bytes, hipStream_t s);
+int block_norm_grid(int D, int64_t T, int NH);
+hipError_t launch_qk_norm_fwd(int D, int64_t T, int Hq, int Hkv, float eps, const void *qkv, const float *gq,
+                              const float *gk, void *qn, void *kn, void *v, hipStream_t s);
+hipError_t launch_qk_norm_bwd(int D, int64_t T, int Hq, int Hkv, float eps, const void *qkv, const float *gq,
+                              const float *gk, const float *dqn, const float *dkn, const float *dv, void *dqkv,
+                              float *part, float *dgq, float *dgk, hipStream_t s);
 hipError_t launch_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const void *o, const void *w,
                            const int32_t *labels, const uint8_t *tok_type, float grad_scale, float *loss,
                            void *dout, void *workspace, hipStream_t s);
@@ -165,6 +173,85 @@ static opr_status hip_status() {
   return e == hipSuccess ? OPR_OK : OPR_E_HIP;
 }
 
+// ---------------------------------------------------------------- attention block
+constexpr size_t kGemmWs = (size_t)64 << 20;  // hipBLASLt scratch
+
+// Block workspace: the hipBLASLt scratch, the attention's q, k, v and the
+// attention's own workspace come first, at the same offsets for the forward
+// and the backward sizes, so that a backward given the forward's workspace can
+// reuse the normalised q, k, v and the attention's forward state.
+struct BlockWs {
+  void *gemm;                 // hipBLASLt scratch
+  uint16_t *qn, *kn, *v;      // the attention's q, k, v: bf16 [T][H][D]
+  void *attn;                 // the attention's own workspace (forward state first)
+  size_t attn_bytes;
+  uint16_t *dout;             // d(o), bf16 [T][Hq][D]              (bwd)
+  float *dqn, *dkn, *dv;      // the attention's gradients, fp32    (bwd)
+  uint16_t *dqkv;             // bf16 [T][Hq + 2 Hkv][D]            (bwd)
+  float *part;                // [norm grid][2][D] partial dg sums  (bwd)
+};
+
+static size_t carve_block_ws(void *p, const opr_block_in &in, int is_bwd, BlockWs *o) {
+  Carver cv(p);
+  BlockWs w;
+  memset(&w, 0, sizeof(w));
+  const int64_t T = (int64_t)in.B * in.L;
+  const int NH = in.Hq + 2 * in.Hkv;
+  w.gemm = cv.take<char>(kGemmWs);
+  w.qn = cv.take<uint16_t>((size_t)(T * in.Hq * in.D));
+  w.kn = cv.take<uint16_t>((size_t)(T * in.Hkv * in.D));
+  w.v = cv.take<uint16_t>((size_t)(T * in.Hkv * in.D));
+  w.attn_bytes = opr_attn_workspace_size(in.B, in.L, in.Hq, in.Hkv, in.D, is_bwd);
+  w.attn = cv.take<char>(w.attn_bytes);
+  if (is_bwd) {
+    w.dout = cv.take<uint16_t>((size_t)(T * in.Hq * in.D));
+    w.dqn = cv.take<float>((size_t)(T * in.Hq * in.D));
+    w.dkn = cv.take<float>((size_t)(T * in.Hkv * in.D));
+    w.dv = cv.take<float>((size_t)(T * in.Hkv * in.D));
+    w.dqkv = cv.take<uint16_t>((size_t)(T * NH * in.D));
+    w.part = cv.take<float>((size_t)block_norm_grid(in.D, T, NH) * 2 * in.D);
+  }
+  if (o) *o = w;
+  return cv.off;
+}
+
+static opr_attn_in attn_in_of(const opr_block_in &b, const void *q, const void *k, const void *v) {
+  opr_attn_in a;
+  memset(&a, 0, sizeof(a));
+  a.B = b.B; a.L = b.L; a.Hq = b.Hq; a.Hkv = b.Hkv; a.D = b.D;
+  a.softmax_scale = b.softmax_scale;
+  a.rope_theta = b.rope_theta;
+  a.q = q; a.k = k; a.v = v;
+  a.layout = b.layout;
+  a.block_q = b.block_q;
+  a.block_k = b.block_k;
+  return a;
+}
+
+static opr_status check_block_shape(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t d_model) {
+  const opr_status st = check_attn_shape(B, L, Hq, Hkv, D);
+  if (st != OPR_OK) return st;
+  if (d_model < 64 || d_model % 64 != 0) return OPR_E_INVALID;
+  if (d_model > (1 << 16) || (Hq + 2 * Hkv) * D > (1 << 18)) return OPR_E_UNSUPPORTED;
+  return OPR_OK;
+}
+
+static opr_status check_block_in(const opr_block_in *in) {
+  if (!in) return OPR_E_INVALID;
+  opr_status st = check_block_shape(in->B, in->L, in->Hq, in->Hkv, in->D, in->d_model);
+  if (st != OPR_OK) return st;
+  if (!in->x || !in->w_qkv || !in->w_o || !in->g_q || !in->g_k) return OPR_E_INVALID;
+  if (!aligned16(in->x) || !aligned16(in->w_qkv) || !aligned16(in->w_o)) return OPR_E_INVALID;
+  if (!(in->norm_eps > 0.0f) || !isfinite(in->norm_eps)) return OPR_E_INVALID;
+  // the attention's own checks, with the block input standing in for q, k, v
+  const opr_attn_in a = attn_in_of(*in, in->x, in->x, in->x);
+  return check_attn_in(&a);
+}
+
+static void bmark(const opr_block_in *in, int i, hipStream_t s) {
+  if (in->timing_events) hipEventRecord(in->timing_events[i], s);
+}
+
 }  // namespace opr
 
 using namespace opr;
@@ -274,6 +361,86 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream,
                               in->timing_events ? in->timing_events + 1 : nullptr) != hipSuccess)
     return OPR_E_HIP;
+  return hip_status();
+}
+
+size_t opr_block_workspace_size(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t d_model,
+                                int is_bwd) {
+  if (check_block_shape(B, L, Hq, Hkv, D, d_model) != OPR_OK) return 0;
+  opr_block_in in;
+  memset(&in, 0, sizeof(in));
+  in.B = B; in.L = L; in.Hq = Hq; in.Hkv = Hkv; in.D = D; in.d_model = d_model;
+  return carve_block_ws(nullptr, in, is_bwd ? 1 : 0, nullptr);
+}
+
+opr_status opr_block_fwd(const opr_block_in *in, void *y, void *qkv, void *o, float *lse, void *workspace,
+                         size_t ws_bytes, hipStream_t stream) {
+  const opr_status st = check_block_in(in);
+  if (st != OPR_OK) return st;
+  if (!y || !qkv || !o || !lse || !workspace) return OPR_E_INVALID;
+  if (!aligned16(y) || !aligned16(qkv) || !aligned16(o)) return OPR_E_INVALID;
+  if (ws_bytes < carve_block_ws(nullptr, *in, 0, nullptr)) return OPR_E_CAPACITY;
+  BlockWs w;
+  carve_block_ws(workspace, *in, 0, &w);
+  const int64_t T = (int64_t)in->B * in->L;
+  const int64_t NHD = (int64_t)(in->Hq + 2 * in->Hkv) * in->D, HqD = (int64_t)in->Hq * in->D;
+  bmark(in, 0, stream);
+  if (!gemm_bf16(false, true, T, NHD, in->d_model, in->x, in->w_qkv, qkv, false, w.gemm, kGemmWs, stream))
+    return OPR_E_HIP;
+  bmark(in, 1, stream);
+  if (launch_qk_norm_fwd(in->D, T, in->Hq, in->Hkv, in->norm_eps, qkv, in->g_q, in->g_k, w.qn, w.kn, w.v,
+                         stream) != hipSuccess)
+    return OPR_E_HIP;
+  bmark(in, 2, stream);
+  const opr_attn_in a = attn_in_of(*in, w.qn, w.kn, w.v);
+  const opr_status sa = opr_attn_fwd(&a, o, lse, w.attn, w.attn_bytes, stream);
+  if (sa != OPR_OK) return sa;
+  bmark(in, 3, stream);
+  if (!gemm_bf16(false, true, T, in->d_model, HqD, o, in->w_o, y, false, w.gemm, kGemmWs, stream))
+    return OPR_E_HIP;
+  bmark(in, 4, stream);
+  return hip_status();
+}
+
+opr_status opr_block_bwd(const opr_block_in *in, const void *qkv, const void *o, const float *lse,
+                         const void *dy, void *dx, float *dw_qkv, float *dw_o, float *dg_q, float *dg_k,
+                         void *workspace, size_t ws_bytes, hipStream_t stream) {
+  const opr_status st = check_block_in(in);
+  if (st != OPR_OK) return st;
+  if (!qkv || !o || !lse || !dy || !dx || !dw_qkv || !dw_o || !dg_q || !dg_k || !workspace) return OPR_E_INVALID;
+  if (!aligned16(qkv) || !aligned16(o) || !aligned16(dy) || !aligned16(dx) || !aligned16(dw_qkv) ||
+      !aligned16(dw_o))
+    return OPR_E_INVALID;
+  if (ws_bytes < carve_block_ws(nullptr, *in, 1, nullptr)) return OPR_E_CAPACITY;
+  BlockWs w;
+  carve_block_ws(workspace, *in, 1, &w);
+  const int64_t T = (int64_t)in->B * in->L;
+  const int64_t NHD = (int64_t)(in->Hq + 2 * in->Hkv) * in->D, HqD = (int64_t)in->Hq * in->D;
+  bmark(in, 0, stream);
+  // y = o w_o^T:  d(o) = dy w_o,  dw_o = dy^T o
+  if (!gemm_bf16(false, false, T, HqD, in->d_model, dy, in->w_o, w.dout, false, w.gemm, kGemmWs, stream) ||
+      !gemm_bf16(true, false, in->d_model, HqD, T, dy, o, dw_o, true, w.gemm, kGemmWs, stream))
+    return OPR_E_HIP;
+  bmark(in, 1, stream);
+  if (!in->reuse_fwd_workspace &&
+      launch_qk_norm_fwd(in->D, T, in->Hq, in->Hkv, in->norm_eps, qkv, in->g_q, in->g_k, w.qn, w.kn, w.v,
+                         stream) != hipSuccess)
+    return OPR_E_HIP;
+  bmark(in, 2, stream);
+  opr_attn_in a = attn_in_of(*in, w.qn, w.kn, w.v);
+  a.reuse_fwd_workspace = in->reuse_fwd_workspace ? 1 : 0;
+  const opr_status sa = opr_attn_bwd(&a, o, lse, w.dout, w.dqn, w.dkn, w.dv, w.attn, w.attn_bytes, stream);
+  if (sa != OPR_OK) return sa;
+  bmark(in, 3, stream);
+  if (launch_qk_norm_bwd(in->D, T, in->Hq, in->Hkv, in->norm_eps, qkv, in->g_q, in->g_k, w.dqn, w.dkn, w.dv,
+                         w.dqkv, w.part, dg_q, dg_k, stream) != hipSuccess)
+    return OPR_E_HIP;
+  bmark(in, 4, stream);
+  // qkv = x w_qkv^T:  dx = dqkv w_qkv,  dw_qkv = dqkv^T x
+  if (!gemm_bf16(false, false, T, in->d_model, NHD, w.dqkv, in->w_qkv, dx, false, w.gemm, kGemmWs, stream) ||
+      !gemm_bf16(true, false, NHD, in->d_model, T, w.dqkv, in->x, dw_qkv, true, w.gemm, kGemmWs, stream))
+    return OPR_E_HIP;
+  bmark(in, 5, stream);
   return hip_status();
 }
 

@@ -273,3 +273,29 @@ def make_tensors(B, L, Hq, Hkv, D, seed, with_dout=True):
         x = rng.standard_normal((B, L, H, D), dtype=np.float32)
         out[name] = round_to_bf16_bits(x)
     return out
+
+
+# ----------------------------------------------------------------------------
+# attention block: weights and activations
+# ----------------------------------------------------------------------------
+# hidden sizes of the Qwen-3 models with these head counts (32 q / 8 kv heads:
+# 4096; 64 q / 8 kv heads: 5120)
+BLOCK_D_MODEL = {32: 4096, 64: 5120}
+
+
+def make_block_weights(d_model: int, Hq: int, Hkv: int, D: int, seed: int):
+    """w_qkv [(Hq + 2 Hkv) D, d_model] ~ N(0, 1/d_model) and w_o [d_model, Hq D]
+    ~ N(0, 1/(Hq D)) as bfloat16 bit patterns (unit-variance projections of
+    unit-variance rows); g_q, g_k ~ U[0.5, 1.5] float32 [D]."""
+    rng = _rng(seed)
+    w_qkv = rng.standard_normal(((Hq + 2 * Hkv) * D, d_model), dtype=np.float32) / np.float32(np.sqrt(d_model))
+    w_o = rng.standard_normal((d_model, Hq * D), dtype=np.float32) / np.float32(np.sqrt(Hq * D))
+    g_q = rng.uniform(0.5, 1.5, size=D).astype(np.float32)
+    g_k = rng.uniform(0.5, 1.5, size=D).astype(np.float32)
+    return {"w_qkv": round_to_bf16_bits(w_qkv), "w_o": round_to_bf16_bits(w_o), "g_q": g_q, "g_k": g_k}
+
+
+def make_block_tensors(B: int, L: int, d_model: int, seed: int):
+    """x and dy ~ N(0, 1), [B, L, d_model], as bfloat16 bit patterns."""
+    rng = _rng(seed)
+    return {n: round_to_bf16_bits(rng.standard_normal((B, L, d_model), dtype=np.float32)) for n in ("x", "dy")}

@@ -23,7 +23,8 @@
  * Conventions for every entry point
  *  - Pointers are device pointers unless the comment says "host".  The caller
  *    allocates and owns every buffer, including the workspace; the library
- *    never allocates or frees memory and never synchronises the stream.
+ *    never allocates or frees memory and never synchronises the stream
+ *    (the one exception: the hipBLASLt handle of the block entry points).
  *  - All arguments are validated on the host before any HIP call.  On a
  *    validation failure the call returns an error status, writes nothing and
  *    enqueues nothing.
@@ -262,6 +263,89 @@ opr_status opr_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const void *
 
 /* Workspace bytes for opr_token_ce with a gradient; 0 if F or V is invalid. */
 size_t opr_token_ce_workspace_size(int32_t F, int32_t V);
+
+/* Inputs of the attention block (opr_block_fwd / opr_block_bwd). */
+typedef struct {
+  int32_t B, L, Hq, Hkv, D; /* as in opr_attn_in */
+  int32_t d_model;          /* hidden size, a multiple of 64 */
+  float softmax_scale;      /* 0 selects 1/sqrt(D) */
+  double rope_theta;        /* RoPE base; > 0 */
+  float norm_eps;           /* RMSNorm epsilon; > 0 */
+  const void *x;            /* bf16 [B][L][d_model], the block's input rows */
+  const void *w_qkv;        /* bf16 [(Hq + 2 Hkv) D][d_model]: the q heads', then the
+                               k heads', then the v heads' output rows (a linear
+                               layer's weight) */
+  const void *w_o;          /* bf16 [d_model][Hq D] */
+  const float *g_q, *g_k;   /* fp32 [D], RMSNorm weights shared by the q heads and
+                               by the k heads */
+  opr_layout layout;        /* as in opr_attn_in (order OPR_ORDER_ATTENTION) */
+  int32_t block_q, block_k; /* must both be OPR_ATTN_BLOCK */
+  /* Optional instrumentation, may be NULL: host array of caller-created
+   * events.  opr_block_fwd records [0] at its start, [1] after the qkv
+   * projection, [2] after the head norms, [3] after the attention and [4]
+   * after the output projection; opr_block_bwd records [0] at its start, [1]
+   * after the output projection's gradients, [2] after the head norms,
+   * [3] after the attention backward, [4] after the norms' backward and [5]
+   * after the qkv projection's gradients. */
+  hipEvent_t *timing_events;
+  /* opr_block_bwd only: nonzero when `workspace` is the one the matching
+   * opr_block_fwd call (same inputs, layout and stream, nothing written to
+   * the workspace in between) just used; the backward then reuses the
+   * normalised q, k, v and the attention's forward state left at the start
+   * of the workspace instead of recomputing them.  0 makes opr_block_bwd
+   * self-contained. */
+  int32_t reuse_fwd_workspace;
+} opr_block_in;
+
+/*
+ * opr_block_fwd - one attention block around the masked attention, with the
+ * per-head query/key normalisation of Qwen-3, the model family the pages
+ * train (wiki summary, "实验结果").  Every op but the attention acts on each
+ * token alone, so one pass over the packed rows still gives every token the
+ * result of its own N-pass sequence (section "理论保证", Theorem 2.1).
+ *
+ *   qkv = x w_qkv^T                                  (bf16 out, fp32 accumulation)
+ *   q_h = g_q * RMSNorm(qkv q head h), k_h = g_k * RMSNorm(qkv k head h)
+ *         (per token and head over D: x / sqrt(mean(x^2) + norm_eps)),
+ *   o   = opr_attn_fwd(q, k, v) with RoPE at the layout's position ids,
+ *   y   = o w_o^T                                    (o seen as [B][L][Hq D])
+ *
+ *  y    bf16 [B][L][d_model]; PAD rows get 0.
+ *  qkv  bf16 [B][L][(Hq + 2 Hkv) D], o bf16 [B][L][Hq][D] and lse fp32
+ *       [B][Hq][L]: written, and kept by the caller for opr_block_bwd.
+ *  workspace  >= opr_block_workspace_size(..., 0) bytes.
+ * x, w_qkv, w_o, y, qkv and o must be 16-byte aligned.  Errors: as
+ * opr_attn_fwd, plus OPR_E_INVALID (d_model, norm_eps, null or misaligned
+ * pointers) and OPR_E_HIP when a hipBLASLt call fails.  The GEMMs run in
+ * hipBLASLt; its handle is created on the device's first call and kept until
+ * the process ends (the one allocation the library leaves to a dependency).
+ */
+opr_status opr_block_fwd(const opr_block_in *in, void *y, void *qkv, void *o, float *lse, void *workspace,
+                         size_t ws_bytes, hipStream_t stream);
+
+/*
+ * opr_block_bwd - gradients of sum(y * dy) for opr_block_fwd.
+ *
+ *  qkv, o, lse  what opr_block_fwd wrote for the same inputs.
+ *  dy      bf16 [B][L][d_model].
+ *  dx      bf16 [B][L][d_model].
+ *  dw_qkv  fp32 [(Hq + 2 Hkv) D][d_model], dw_o fp32 [d_model][Hq D],
+ *  dg_q, dg_k  fp32 [D].  Every element is written, nothing accumulated.
+ *  workspace  >= opr_block_workspace_size(..., 1) bytes.
+ * The attention's q, k and v are recomputed from qkv unless the forward's
+ * workspace is reused (reuse_fwd_workspace; the forward-sized workspace is a
+ * prefix of the backward-sized one, so one backward-sized workspace serves
+ * both calls).  dx, dw_qkv and dw_o must be 16-byte aligned.  Errors as for
+ * opr_block_fwd.
+ */
+opr_status opr_block_bwd(const opr_block_in *in, const void *qkv, const void *o, const float *lse,
+                         const void *dy, void *dx, float *dw_qkv, float *dw_o, float *dg_q, float *dg_k,
+                         void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for opr_block_fwd (is_bwd = 0) or opr_block_bwd (is_bwd = 1);
+ * 0 if the sizes are invalid. */
+size_t opr_block_workspace_size(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t d_model,
+                                int is_bwd);
 
 /* One chunk of a K-pass plan (see opr_kpass_plan). */
 typedef struct {

@@ -633,3 +633,68 @@ def kpass_best_splits(turns, n_chunks: int, max_tokens: int, weight: float, elid
         elif cost == best:
             arg.append(starts)
     return best, arg
+
+
+# ----------------------------------------------------------------------------
+# attention block around the masked attention: q/k/v projection, per-head RMS
+# normalisation of q and k before RoPE (Qwen-3, the model family the pages
+# train: wiki summary, "实验结果"), the masked attention, output projection
+# ----------------------------------------------------------------------------
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """g * x / sqrt(mean(x^2) + eps) over the last axis."""
+    x = _f64(x)
+    return _f64(g) * x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def rms_norm_bwd(x: np.ndarray, g: np.ndarray, dy: np.ndarray, eps: float):
+    """(dx, dg) for y = rms_norm(x, g, eps) and upstream gradient dy.
+
+    With r = (mean(x^2) + eps)^(-1/2) and D the last axis' length,
+    dy_i/dx_j = g_i (r delta_ij - r^3 x_i x_j / D), so
+    dx = r g dy - x r^3 mean(g dy x), and dg = sum over the other axes of dy x r."""
+    x, g, dy = _f64(x), _f64(g), _f64(dy)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    dx = r * g * dy - x * r ** 3 * np.mean(g * dy * x, axis=-1, keepdims=True)
+    dg = (dy * x * r).reshape(-1, x.shape[-1]).sum(axis=0)
+    return dx, dg
+
+
+def _split_qkv(qkv, Hq, Hkv, D):
+    B, L, _ = qkv.shape
+    q = qkv[..., :Hq * D].reshape(B, L, Hq, D)
+    k = qkv[..., Hq * D:(Hq + Hkv) * D].reshape(B, L, Hkv, D)
+    v = qkv[..., (Hq + Hkv) * D:].reshape(B, L, Hkv, D)
+    return q, k, v
+
+
+def block_fwd(x, w_qkv, w_o, g_q, g_k, lay, Hq: int, Hkv: int, D: int, theta: float, eps: float,
+              attn=None):
+    """One block: qkv = x w_qkv^T; q, k normalised per (token, head); masked
+    attention at the layout's position ids (or ``attn(q, k, v)`` in its place);
+    y = o w_o^T.  Returns y [B, L, d] and the intermediates."""
+    x = _f64(x)
+    qkv = x @ _f64(w_qkv).T
+    q, k, v = _split_qkv(qkv, Hq, Hkv, D)
+    qn, kn = rms_norm(q, g_q, eps), rms_norm(k, g_k, eps)
+    o, lse = attn_fwd(qn, kn, v, lay, theta) if attn is None else attn(qn, kn, v)
+    B, L, _ = x.shape
+    y = o.reshape(B, L, Hq * D) @ _f64(w_o).T
+    return y, {"qkv": qkv, "q": q, "k": k, "v": v, "qn": qn, "kn": kn, "o": o, "lse": lse}
+
+
+def block_bwd(x, w_qkv, w_o, g_q, g_k, dy, lay, Hq: int, Hkv: int, D: int, theta: float, eps: float):
+    """Gradients of sum(y * dy) for block_fwd: (dx, dw_qkv, dw_o, dg_q, dg_k)."""
+    x, dy = _f64(x), _f64(dy)
+    B, L, d = x.shape
+    _, st = block_fwd(x, w_qkv, w_o, g_q, g_k, lay, Hq, Hkv, D, theta, eps)
+    o2 = st["o"].reshape(B * L, Hq * D)
+    dy2 = dy.reshape(B * L, d)
+    do = (dy2 @ _f64(w_o)).reshape(B, L, Hq, D)
+    dw_o = dy2.T @ o2
+    dqn, dkn, dv = attn_bwd(st["qn"], st["kn"], st["v"], do, lay, theta)
+    dq, dg_q = rms_norm_bwd(st["q"], g_q, dqn, eps)
+    dk, dg_k = rms_norm_bwd(st["k"], g_k, dkn, eps)
+    dqkv = np.concatenate([dq.reshape(B * L, -1), dk.reshape(B * L, -1), dv.reshape(B * L, -1)], axis=1)
+    dx = (dqkv @ _f64(w_qkv)).reshape(B, L, d)
+    dw_qkv = dqkv.T @ x.reshape(B * L, d)
+    return dx, dw_qkv, dw_o, dg_q, dg_k

@@ -30,7 +30,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(Bd):
     names = declared_entry_points()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     lib = ctypes.CDLL(Bd._LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -165,3 +165,51 @@ def test_token_ce_workspace_size(Bd):
     assert Bd.opr_token_ce_workspace_size(4096, 32) >= 4096 * 32 * 2
     assert Bd.opr_token_ce_workspace_size(4000, 32) == 0
     assert Bd.opr_token_ce_workspace_size(4096, 40) == 0
+
+
+def _block_in(Bd, **kw):
+    f = dict(B=1, L=256, Hq=4, Hkv=2, D=128, d_model=256, softmax_scale=0.0, rope_theta=1.0e6, norm_eps=1e-6,
+             x=FAKE, w_qkv=FAKE, w_o=FAKE, g_q=FAKE, g_k=FAKE, layout=_layout_struct(Bd), block_q=128,
+             block_k=128, timing_events=None, reuse_fwd_workspace=0)
+    f.update(kw)
+    return Bd.OprBlockIn(**f)
+
+
+def _bfwd(Bd, ws_bytes=1 << 40, y=FAKE, **kw):
+    a = _block_in(Bd, **kw)
+    return Bd.LIB.opr_block_fwd(ctypes.byref(a), y, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def _bbwd(Bd, ws_bytes=1 << 40, dx=FAKE, **kw):
+    a = _block_in(Bd, **kw)
+    return Bd.LIB.opr_block_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, dx, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                ws_bytes, None)
+
+
+def test_block_errors(Bd):
+    assert Bd.LIB.opr_block_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == Bd.OPR_E_INVALID
+    for f in (_bfwd, _bbwd):
+        assert f(Bd, d_model=100) == Bd.OPR_E_INVALID        # not a multiple of 64
+        assert f(Bd, d_model=0) == Bd.OPR_E_INVALID
+        assert f(Bd, norm_eps=0.0) == Bd.OPR_E_INVALID
+        assert f(Bd, norm_eps=float("nan")) == Bd.OPR_E_INVALID
+        assert f(Bd, D=96) == Bd.OPR_E_UNSUPPORTED
+        assert f(Bd, Hq=6, Hkv=4) == Bd.OPR_E_INVALID
+        for arg in ("x", "w_qkv", "w_o", "g_q", "g_k"):
+            assert f(Bd, **{arg: None}) == Bd.OPR_E_INVALID
+        assert f(Bd, x=FAKE + 2) == Bd.OPR_E_INVALID         # 16-byte alignment
+        assert f(Bd, layout=_layout_struct(Bd, "q_list")) == Bd.OPR_E_INVALID
+        assert f(Bd, layout=_layout_struct(Bd, order=0)) == Bd.OPR_E_INVALID
+        assert f(Bd, block_q=64) == Bd.OPR_E_UNSUPPORTED
+        assert f(Bd, ws_bytes=1024) == Bd.OPR_E_CAPACITY
+    assert _bfwd(Bd, y=None) == Bd.OPR_E_INVALID
+    assert _bfwd(Bd, y=FAKE + 8) == Bd.OPR_E_INVALID
+    assert _bbwd(Bd, dx=None) == Bd.OPR_E_INVALID
+
+
+def test_block_workspace_size(Bd):
+    f = Bd.opr_block_workspace_size(2, 16384, 32, 8, 128, 4096, False)
+    b = Bd.opr_block_workspace_size(2, 16384, 32, 8, 128, 4096, True)
+    assert Bd.opr_attn_workspace_size(2, 16384, 32, 8, 128, False) < f < b
+    assert Bd.opr_block_workspace_size(1, 100, 4, 2, 128, 100, False) == 0
+    assert Bd.opr_block_workspace_size(1, 100, 4, 2, 96, 128, True) == 0
