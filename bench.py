@@ -315,20 +315,23 @@ def block_step(torch, Bd, dev, rows, shape, steps, warmup):
 
 
 def block_depth(torch, Bd, dev, Ns, steps):
-    """One conversation of N turns through the block: one pass against N passes."""
+    """One conversation of N turns through the block: one pass (as packed and
+    without the last turn's dead context copy) against N passes."""
     Hq, Hkv, D = I.DEPTH_HEADS["Hq"], I.DEPTH_HEADS["Hkv"], I.DEPTH_HEADS["D"]
     dm = I.BLOCK_D_MODEL[Hq]
     out = []
     for N in Ns:
         conv = I.depth_conversation(N)
         rec = {"N": N, "d_model": dm}
-        for kind, rows in (("one_pass", [[conv]]), ("n_pass", [I.npass_conversations(conv)])):
+        for kind, rows in (("one_pass", [[conv]]), ("one_pass_elided", [[I.chunk_conversation(conv, 0, N, True)]]),
+                           ("n_pass", [I.npass_conversations(conv)])):
             L = I.row_used(rows[0])
             r = BlockRunner(torch, Bd, rows, L, Hq, Hkv, D, dm, dev)
             rec[kind] = {"tokens": L, "ms": round(r.time_steps(steps, 1), 4)}
             del r
             torch.cuda.empty_cache()
         rec["speedup"] = round(rec["n_pass"]["ms"] / rec["one_pass"]["ms"], 3)
+        rec["speedup_elided"] = round(rec["n_pass"]["ms"] / rec["one_pass_elided"]["ms"], 3)
         log(f"block depth N={N}: {rec}")
         out.append(rec)
     return out
