@@ -452,6 +452,50 @@ def attn_bwd(q, k, v, do, lay, theta: float, scale: float = None):
 # ----------------------------------------------------------------------------
 # N-pass brute force (Theorem 2.1)
 # ----------------------------------------------------------------------------
+def attn_rows(q, k, v, do, lay, b: int, rows, theta: float, scale: float = None):
+    """O, LSE and dQ of the listed query rows of row b alone, in fp64.
+
+    The definition of attn_fwd / attn_bwd restricted to some queries, for rows
+    too long for the whole oracle: each query's softmax runs over the keys of
+    its conversation that the mask allows, and
+    dq_p = R(pos_p)^T scale * sum_k dS_pk k'_k with dS_pk = P_pk (dP_pk - Delta_p),
+    dP_pk = dO_p . v_k and Delta_p = dO_p . O_p.  PAD rows get O = 0,
+    LSE = -inf and dq = 0.  Returns O [n, Hq, D], LSE [n, Hq], dQ [n, Hq, D].
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    rows = np.asarray(rows, dtype=np.int64)
+    Hq, D = q.shape[2], q.shape[3]
+    g = Hq // k.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    O = np.zeros((len(rows), Hq, D))
+    LSE = np.full((len(rows), Hq), -np.inf)
+    dQ = np.zeros((len(rows), Hq, D))
+    conv = lay["conv"][b, rows]
+    for c in np.unique(conv[conv >= 0]):
+        sel = np.nonzero(conv == c)[0]
+        a, e = conv_range(lay, b, int(c))
+        pos = lay["pos"][b, a:e]
+        M = conv_mask(lay, b, int(c), qidx=rows[sel] - a)
+        kr = rope(k[b, a:e], pos, theta)
+        qr = rope(q[b, rows[sel]], lay["pos"][b, rows[sel]], theta)
+        dqr = np.zeros((len(sel), Hq, D))
+        for h in range(Hq):
+            kv = h // g
+            S = np.where(M, scale * (qr[:, h] @ kr[:, kv].T), -np.inf)
+            m = S.max(axis=1, keepdims=True)
+            P = np.exp(S - m)
+            l = P.sum(axis=1, keepdims=True)
+            P = P / l
+            o = P @ v[b, a:e, kv]
+            O[sel, h] = o
+            LSE[sel, h] = (m + np.log(l))[:, 0]
+            dP = do[b, rows[sel], h] @ v[b, a:e, kv].T
+            delta = (do[b, rows[sel], h] * o).sum(axis=1, keepdims=True)
+            dqr[:, h] = scale * ((P * (dP - delta)) @ kr[:, kv])
+        dQ[sel] = rope_transpose(dqr, lay["pos"][b, rows[sel]], theta)
+    return O, LSE, dQ
+
+
 def _seg_index(lay, b, c):
     """{(turn, type): packed indices} for conversation c of row b."""
     a, e = conv_range(lay, b, c)

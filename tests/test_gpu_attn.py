@@ -236,3 +236,55 @@ def test_backward_reuse_is_identical(B):
     r = run_gpu(B, rows, L, t, reuse=True)
     for n in ("o", "lse", "dq", "dk", "dv"):
         np.testing.assert_array_equal(a[n], r[n], err_msg=n)
+
+
+def _rotate(x, pos, theta):
+    """Rotate-half RoPE of x [n, D] at positions pos [n] (fp64)."""
+    D = x.shape[-1]
+    ang = pos[:, None].astype(np.float64) * theta ** (-2.0 * np.arange(D // 2) / D)
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[:, : D // 2], x[:, D // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=1)
+
+
+def test_long_reasoning_chunked_stage_lists(B):
+    """One turn with 70,000 reasoning tokens: its last query tiles see ~549
+    key tiles, more stages than one LDS stage-list chunk holds (1024 in the
+    forward and dQ kernels, 512 in dK/dV), so the lists are built in several
+    chunks.  O, LSE and dQ are checked on sampled rows (the deepest t and
+    r_out rows, random rows, PAD rows) against the oracle row by row; dV and
+    dK by properties that hold at any size: every query's probabilities sum
+    to 1, so sum_k dV_k = sum over the group's heads and live queries of dO;
+    every query's dS sums to 0, so the rotated dK (R(pos_k) dK_k) sums to 0."""
+    conv = [(128, 70000, 64, 64)]
+    n = I.conv_len(conv)
+    L = n + 37
+    Hq, Hkv, D = 2, 1, 128
+    rows = [[conv]]
+    t = I.make_tensors(1, L, Hq, Hkv, D, seed=7070)
+    print(f"[attn] long reasoning: 1 x {L}", flush=True)
+    got = run_gpu(B, rows, L, t)
+    lay = O.layout(rows, L)
+    rng = np.random.default_rng(7071)
+    t_end = 128 + 70000
+    sel = np.concatenate([np.arange(t_end - 64, t_end), np.arange(n - 64, n), rng.integers(0, n, 32),
+                          np.arange(n, L)[:5]])
+    q, k, v, do = (bf16_f64(t[name]) for name in ("q", "k", "v", "do"))
+    o, lse, dq = O.attn_rows(q, k, v, do, lay, 0, sel, THETA)
+    live = lay["type"][0, sel] != O.PAD
+    assert (got["o"][0, sel[~live]] == 0).all() and (got["dq"][0, sel[~live]] == 0).all()
+    assert_close("O (sampled rows)", got["o"][0, sel[live]], o[live])
+    assert_close("LSE (sampled rows)", got["lse"][0][:, sel[live]].T, lse[live])
+    assert_close("dQ (sampled rows)", got["dq"][0, sel[live]], dq[live])
+    liv = lay["type"][0] != O.PAD
+    sum_dv = got["dv"][0, liv, 0].sum(axis=0)
+    sum_do = do[0, liv].sum(axis=(0, 1))
+    # one missing query tile (128 queries x 2 heads of N(0, 1) dO) would move
+    # the sum by about 16 per dimension
+    tol_v = 1e-3 * np.sqrt(liv.sum() * Hq)
+    print(f"  sum dV - sum dO: max {np.abs(sum_dv - sum_do).max():.3e} (tolerance {tol_v:.3e})", flush=True)
+    assert np.abs(sum_dv - sum_do).max() <= tol_v
+    dkr = _rotate(got["dk"][0, liv, 0], lay["pos"][0, liv], THETA)
+    norm = np.sqrt((dkr ** 2).sum())
+    print(f"  |sum R dK| / |R dK|: {np.abs(dkr.sum(axis=0)).max() / norm:.3e}", flush=True)
+    assert np.abs(dkr.sum(axis=0)).max() <= 5e-3 * norm

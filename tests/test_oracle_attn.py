@@ -139,6 +139,31 @@ def test_fwd_bwd_vs_sdpa(rows, heads, extra, seed):
     np.testing.assert_allclose(dv, rdv, atol=1e-11)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_attn_rows_vs_sdpa(seed):
+    """The oracle's single-row attention (O, LSE, dQ of listed queries, for
+    rows too long for the whole oracle) against the torch reference on every
+    row of small packed rows, PAD included."""
+    rng = np.random.default_rng(900 + seed)
+    rows = [[[(int(rng.integers(0, 7)), int(rng.integers(0, 9)), *([int(rng.integers(0, 6))] * 2))
+              for _ in range(int(rng.integers(1, 4)))] for _ in range(int(rng.integers(1, 3)))] for _ in range(2)]
+    L = max(I.row_used(r) for r in rows) + 3
+    Hq, Hkv, D = 4, 2, 16
+    lay = O.layout(rows, L)
+    q, k, v = (rng.standard_normal((2, L, h, D)) for h in (Hq, Hkv, Hkv))
+    do = rng.standard_normal((2, L, Hq, D))
+    ro, rlse, rdq, _, _ = _torch_reference(q, k, v, do, lay, THETA)
+    for b in range(2):
+        sel = rng.permutation(L)[: L // 2 + 1]
+        o, lse, dq = O.attn_rows(q, k, v, do, lay, b, sel, THETA)
+        np.testing.assert_allclose(o, ro[b, sel], atol=1e-12)
+        ref_lse = rlse[b][:, sel].T
+        finite = np.isfinite(ref_lse)
+        np.testing.assert_array_equal(np.isfinite(lse), finite)
+        np.testing.assert_allclose(lse[finite], ref_lse[finite], atol=1e-12)
+        np.testing.assert_allclose(dq, rdq[b, sel], atol=1e-11)
+
+
 def test_bwd_finite_differences():
     rows = [[[(3, 2, 2, 2), (2, 3, 1, 1)], [(2, 0, 1, 1)]]]
     L = I.row_used(rows[0]) + 2
