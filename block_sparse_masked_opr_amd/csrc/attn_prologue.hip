@@ -44,9 +44,11 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, i
 
 // Largest |x| of each (row, head) plane of x [B][L][H][D] bf16, times
 // `factor` (sqrt(2) bound of RoPE on a pair, rounded up), into pmax[b][h] as
-// float bits.  A workgroup covers kAbsTokens tokens of HPB heads: thread
-// (head hl, chunk j) reads 16-byte chunk j of head hl of every token, so each
-// 16-lane group reads one head's whole row and a wave reads contiguous runs.
+// float bits.  A workgroup covers kAbsTokens tokens of up to HPB heads:
+// thread (token row r, head hl, chunk j) reads 16-byte chunk j of head hl of
+// every tpr-th token from r, so each D/8-lane group reads one head's whole row
+// and a wave reads contiguous runs; with fewer heads than HPB the spare
+// threads take further token rows.
 constexpr int kAbsTokens = 64;
 
 // One launch covers k and v: blockIdx.y runs over the head blocks of job 0,
@@ -70,20 +72,31 @@ __global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, Ab
   const float factor = in0 ? j0.factor : j1.factor;
   const int hb = yb - (in0 ? 0 : j0.hb_end);
   const int b = blockIdx.z, tid = threadIdx.x;
-  const int hl = tid / CPH, j = tid % CPH;
+  // the block's heads [hb * HPB, hb * HPB + nh); threads beyond one token row
+  // of them take further tokens (tpr token rows per pass)
+  const int nh = min(HPB, H - hb * HPB);
+  const int row = nh * CPH, tpr = 256 / row;
+  const int r = tid / row, hl = (tid % row) / CPH, j = tid % CPH;
   const int h = hb * HPB + hl;
   const int t0 = blockIdx.x * kAbsTokens;
   uint32_t m = 0u;  // float bits of the largest |x| (non-negative: integer order)
-  if (h < H) {
+  if (r < tpr) {
     const uint16_t *src = x + (((int64_t)b * L + t0) * H + h) * D + j * 8;
     const int nt = min(kAbsTokens, L - t0);
 #pragma unroll 8
-    for (int t = 0; t < nt; ++t)
+    for (int t = r; t < nt; t += tpr)
       m = max(m, absmax8_bf16_bits(*reinterpret_cast<const uint4 *>(src + (int64_t)t * H * D)));
   }
 #pragma unroll
   for (int off = CPH / 2; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  if (j == 0 && h < H && m > 0u) atomicMax(pmax + (int64_t)b * H + h, __float_as_uint(__uint_as_float(m) * factor));
+  // one atomic per head and workgroup: the token rows meet in LDS first
+  __shared__ uint32_t hm[256 / CPH];
+  if (tid < HPB) hm[tid] = 0u;
+  __syncthreads();
+  if (j == 0 && r < tpr && m > 0u) atomicMax(&hm[hl], m);
+  __syncthreads();
+  if (tid < nh && hm[tid] > 0u)
+    atomicMax(pmax + (int64_t)b * H + hb * HPB + tid, __float_as_uint(__uint_as_float(hm[tid]) * factor));
 }
 
 // One workgroup per (64-slot block, group of kPackHeads heads, row): 4
