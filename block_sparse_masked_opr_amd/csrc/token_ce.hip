@@ -24,7 +24,8 @@
 //     8j .. 8j + 7 of a logit block are directly the B operand of a product
 //     whose 16 k values are logits 16 j + {0..3, 8..11} (lane group 0) and
 //     16 j + {4..7, 12..15} (lane group 1); A comes from W^T (transposed once
-//     into the workspace), two 8-byte reads per lane.  Each 64-feature group
+//     into the workspace, the logits of each 16-block permuted so that each
+//     lane group's eight are contiguous), one 16-byte read per lane.  Each 64-feature group
 //     goes through LDS into row-major order, so dout is written in full
 //     128-byte row pieces.
 // The kernel is bound by HBM: it reads o once and writes dout once.
@@ -46,12 +47,17 @@ __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 &a, const bf16x8 &b, co
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
 
-// wt[f][v] = w[v][f]
+// W^T with the logits of each 16-logit block in the order the gradient
+// product's lane groups take them: wt[f][16 b + p] = w[16 b + perm(p)][f] with
+// perm = (0..3, 8..11, 4..7, 12..15), so that lane group g finds its eight
+// logits 16 b + 4 g + {0..3, 8..11} in one 16-byte run.
 __global__ void transpose_head_kernel(const uint16_t *__restrict__ w, uint16_t *__restrict__ wt, int F, int V) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (int64_t)F * V) return;
   const int f = (int)(i % F), v = (int)(i / F);  // consecutive threads read consecutive f of one row
-  wt[(int64_t)f * V + v] = w[i];
+  const int q = v & 15;
+  const int p = (q & 3) | ((q & 8) >> 1) | ((q & 4) << 1);  // position of logit v in its block
+  wt[(int64_t)f * V + (v & ~15) + p] = w[i];
 }
 
 template <int NVB>  // V = 32 * NVB
@@ -165,21 +171,39 @@ __global__ __launch_bounds__(256) void token_ce_kernel(const uint16_t *__restric
   // own 32 x 64 tile) and written as full 128-byte row pieces
   __syncthreads();  // the partial-sum buffer is reused for the tiles
   uint16_t *tile = reinterpret_cast<uint16_t *>(&red[0][0][0][0]) + wave * (kRows * kGroup);
+  // W^T operands of a group: per half h, logit block vb and k half j, logits
+  // 32 vb + 16 j + 4 g + {0..3, 8..11} of W^T row fb + li, one 16-byte run in
+  // the permuted W^T.  The next group's are loaded while the current one is
+  // computed and written.
+  auto load_wt = [&](int G, uint4 (&a)[2][NVB][2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint16_t *wr = wt + (int64_t)(G * kGroup + 32 * h + li) * V + 8 * g;
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) a[h][vb][j] = *reinterpret_cast<const uint4 *>(wr + 32 * vb + 16 * j);
+    }
+  };
+  uint4 wa[2][NVB][2];
+  if (wave < ngroups) load_wt(wave, wa);
   for (int G = wave; G < ngroups; G += kWaves) {
+    uint4 cur[2][NVB][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) cur[h][vb][j] = wa[h][vb][j];
+    if (G + kWaves < ngroups) load_wt(G + kWaves, wa);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int fb = G * kGroup + 32 * h;
-      const uint16_t *wr = wt + (int64_t)(fb + li) * V + 4 * g;
       f32x16 c = zero_f32x16();
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          // logits 32 vb + 16 j + {0..3, 8..11} (+ 4 g): two 8-byte runs of W^T row fb + li
-          const uint2 lo = *reinterpret_cast<const uint2 *>(wr + 32 * vb + 16 * j);
-          const uint2 hi = *reinterpret_cast<const uint2 *>(wr + 32 * vb + 16 * j + 8);
-          c = mfma_bf16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), gb[vb][j], c);
-        }
+        for (int j = 0; j < 2; ++j) c = mfma_bf16(as_bf16x8(cur[h][vb][j]), gb[vb][j], c);
       // register r holds feature fb + 8 (r / 4) + 4 g + r % 4 of row li
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {

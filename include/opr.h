@@ -252,7 +252,7 @@ size_t opr_attn_workspace_size(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, in
  *  dout        bf16 [B][L][F], every element written, or NULL to skip the
  *              gradient; 16-byte aligned.
  *  workspace   device, >= opr_token_ce_workspace_size(F, V) bytes when dout
- *              is not NULL (it receives W transposed); may be NULL otherwise.
+ *              is not NULL (it receives a transposed copy of W); may be NULL otherwise.
  * Errors: OPR_E_INVALID (null or misaligned pointer, B/L, non-finite
  * grad_scale), OPR_E_UNSUPPORTED (F, V, B*L), OPR_E_CAPACITY (ws_bytes),
  * OPR_E_HIP.
