@@ -68,7 +68,7 @@ def test_plan_matches_bruteforce(Bd, seed):
     against the oracle's exhaustive search."""
     rng = np.random.default_rng(100 + seed)
     for case in range(8):
-        N = int(rng.integers(1, 7))
+        N = int(rng.integers(1, 10))
         conv = _random_conv(rng, N, 14 if case % 2 else 40)
         elide = bool(case % 3 != 2)
         weight = [0.0, 1.0, 2.5, 37.0][case % 4]
