@@ -13,7 +13,8 @@ pairs, recomputation not counted), conversation tokens/s, the roofline of the
 dominant kernel (timed with HIP events on its own stream), the fp64 CPU oracle
 timed on a bounded sample, and (unless --no-sweep) the one-pass vs N-pass
 speedup across conversation depth and the K-pass trade-off.  Beside the
-headline it also times the per-token loss step and (unless --no-block) the
+headline it also times the per-token loss step, the layout alone on 64 rows
+of 32768 tokens, and (unless --no-block) the
 same rows through a whole attention block (projections, q/k norms, attention;
 opr_block_fwd / opr_block_bwd), and the block's one-pass vs N-pass speedup.
 """
@@ -337,6 +338,45 @@ def block_depth(torch, Bd, dev, Ns, steps):
     return out
 
 
+def layout_step(torch, Bd, dev, steps):
+    """opr_build_layout alone on 64 rows x 32768 tokens (packed distributions):
+    bound by HBM; algorithmic bytes = everything the layout writes (per token
+    its ids, slots and runs of slots; per tile its classes and list entries).
+    The time holds the copies of the host turn lists as well."""
+    B, L = I.LAYOUT_BATCH
+    rows = I.layout_batch_rows(I.SEEDS["layout_batch"][0])
+    lay = Bd.opr_build_layout(rows, L, 128, 128, device=dev)
+    cpr, tpc, turns = I.flatten_rows(rows)
+    lws = torch.empty(Bd.opr_build_layout_workspace_size(B, L, len(tpc), len(turns)), dtype=torch.uint8, device=dev)
+    st = lay.c_struct()
+    args = (B, L, 128, 128, cpr.ctypes.data, tpc.ctypes.data, turns.ctypes.data, lws.data_ptr(), lws.numel(),
+            ctypes.byref(st), torch.cuda.current_stream(dev).cuda_stream)
+
+    def call():
+        status = Bd.LIB.opr_build_layout(*args)
+        if status != 0:
+            raise RuntimeError(f"opr_build_layout: {Bd.opr_status_string(status)}")
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        call()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    nbytes = sum(getattr(lay, f).numel() * getattr(lay, f).element_size() for f in Bd.Layout.FIELDS)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {"rows": B, "row_tokens": L, "packed_tokens": sum(I.row_used(r) for r in rows), "ms": round(ms, 4),
+           "bytes_written": nbytes,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+    log(f"layout step {out}")
+    return out
+
+
 def loss_step(torch, Bd, r, shape, steps, dev):
     """opr_token_ce on the forward's output: per-token loss of a V = 32 head on
     the t and r_out rows and its gradient (the loss step of training); bound
@@ -572,6 +612,7 @@ def main():
     log(f"loss step {result['loss_step']['ms']:.4f} ms, {result['loss_step']['roofline']['achieved']} GB/s")
     del r
     torch.cuda.empty_cache()
+    result["layout_step"] = layout_step(torch, Bd, dev, args.steps)
     if not args.no_block:
         result["block_step"] = block_step(torch, Bd, dev, rows, shape, args.steps, args.warmup)
     if not args.no_sweep:

@@ -13,7 +13,8 @@
 //                    the allowed keys of each 32-key sub-block with interval
 //                    arithmetic, then sums per 32x32 sub-block and per tile
 //                    (layout_classify_attention: the same over attention
-//                    order, from the query's two runs of slots)
+//                    order, from the query's two runs of slots, one
+//                    workgroup per q-tile row)
 //   layout_compact_q/k  one wave per tile row / column: ballot compaction of
 //                    the non-empty tiles into ascending lists
 //
@@ -265,47 +266,80 @@ __global__ __launch_bounds__(BQ) void layout_classify(int32_t B, int32_t L, int3
   }
 }
 
-// Tile classes over attention order: one workgroup of BQ threads per tile,
-// thread r is query slot m*BQ + r, whose allowed keys are its two runs of
-// slots; tiles after the diagonal are empty (no query sees a later slot).
+// Tile classes over attention order: one workgroup of BQ threads per q-tile
+// row (b, m).  The row's queries (slots m*BQ ..) put their two runs of slots
+// in LDS, and their union gives the span of key slots any of them sees: key
+// tiles outside it are empty and are written as such directly.  In the
+// others each thread counts whole 32x32 sub-blocks, summing over the
+// sub-block's 32 queries the part of their runs inside its 32 key slots.
+// kClsBatch tiles at a time meet in LDS, and their class words are written
+// together.
+constexpr int kClsBatch = 64;
+
 template <int BQ, int BK>
 __global__ __launch_bounds__(BQ) void layout_classify_attention(int32_t B, int32_t L, int32_t MT,
                                                                 int32_t NT, opr_layout out) {
-  constexpr int SQ = BQ / OPR_SUB_BLOCK, SK = BK / OPR_SUB_BLOCK;
-  __shared__ int32_t cnt[SQ * SK];
-  const int64_t tile = blockIdx.x;
-  const int32_t n = (int32_t)(tile % NT);
-  const int32_t m = (int32_t)((tile / NT) % MT);
-  const int32_t b = (int32_t)(tile / ((int64_t)NT * MT));
+  constexpr int SQ = BQ / OPR_SUB_BLOCK, SK = BK / OPR_SUB_BLOCK, NSB = SQ * SK;
+  __shared__ int4 runs[BQ];
+  __shared__ int32_t cnt[kClsBatch][NSB];
+  __shared__ int32_t span[2];
+  const int64_t row = blockIdx.x;  // b * MT + m
+  const int32_t m = (int32_t)(row % MT);
+  const int32_t b = (int32_t)(row / MT);
   const int tid = threadIdx.x;
-  if (tid < SQ * SK) cnt[tid] = 0;
-  __syncthreads();
   const int32_t q = m * BQ + tid;
-  const int32_t k_begin = n * BK;
-  if (k_begin <= m * BQ + BQ - 1 && q < L) {
-    const int4 iv = reinterpret_cast<const int4 *>(out.slot_qiv)[(int64_t)b * L + q];
-#pragma unroll
-    for (int j = 0; j < SK; ++j) {
-      const int32_t a = k_begin + j * OPR_SUB_BLOCK;
-      const int32_t e = min(a + OPR_SUB_BLOCK, L);
-      const int32_t c_ = overlap(a, e, iv.x, iv.y) + overlap(a, e, iv.z, iv.w);
-      if (c_) atomicAdd(&cnt[(tid / OPR_SUB_BLOCK) * SK + j], c_);
-    }
+  int4 iv = make_int4(0, 0, 0, 0);
+  if (q < L) iv = reinterpret_cast<const int4 *>(out.slot_qiv)[(int64_t)b * L + q];
+  runs[tid] = iv;
+  if (tid == 0) {
+    span[0] = INT32_MAX;
+    span[1] = INT32_MIN;
   }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t word = 0;
-    int32_t total = 0;
-    for (int i = 0; i < SQ * SK; ++i) {
-      const int32_t v = cnt[i];
-      total += v;
-      const uint32_t cls = v == 0 ? OPR_TILE_EMPTY
-                         : (v == OPR_SUB_BLOCK * OPR_SUB_BLOCK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
-      word |= cls << (2 * i);
+  if (iv.x < iv.y || iv.z < iv.w) {
+    atomicMin(&span[0], iv.x < iv.y ? iv.x : iv.z);
+    atomicMax(&span[1], iv.z < iv.w ? iv.w : iv.y);
+  }
+  __syncthreads();
+  uint8_t *tcls = out.tile_class + row * NT;
+  uint32_t *scls = out.sub_class + row * NT;
+  const int32_t n_lo = span[0] <= span[1] ? span[0] / BK : 0;
+  const int32_t n_hi = span[0] <= span[1] ? (span[1] - 1) / BK : -1;  // empty range if no key is seen
+  for (int32_t n = tid; n < NT; n += BQ) {
+    if (n < n_lo || n > n_hi) {
+      tcls[n] = OPR_TILE_EMPTY;
+      scls[n] = 0u;
     }
-    const uint8_t tcls = total == 0 ? OPR_TILE_EMPTY : (total == BQ * BK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
-    out.tile_class[tile] = tcls;
-    out.sub_class[tile] = word;
+  }
+  for (int32_t nb = n_lo; nb <= n_hi; nb += kClsBatch) {
+    const int nt = min(kClsBatch, n_hi + 1 - nb);
+    for (int x = tid; x < nt * NSB; x += BQ) {
+      const int t = x / NSB, i = x - t * NSB, sq = i / SK, j = i - sq * SK;
+      const int32_t a = (nb + t) * BK + j * OPR_SUB_BLOCK;
+      const int32_t e = min(a + OPR_SUB_BLOCK, L);
+      int32_t c = 0;
+#pragma unroll 8
+      for (int r = 0; r < OPR_SUB_BLOCK; ++r) {
+        const int4 u = runs[sq * OPR_SUB_BLOCK + r];
+        c += overlap(a, e, u.x, u.y) + overlap(a, e, u.z, u.w);
+      }
+      cnt[t][i] = c;
+    }
+    __syncthreads();
+    for (int t = tid; t < nt; t += BQ) {
+      uint32_t word = 0;
+      int32_t total = 0;
+      for (int i = 0; i < NSB; ++i) {
+        const int32_t v = cnt[t][i];
+        total += v;
+        const uint32_t cls = v == 0 ? OPR_TILE_EMPTY
+                           : (v == OPR_SUB_BLOCK * OPR_SUB_BLOCK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
+        word |= cls << (2 * i);
+      }
+      tcls[nb + t] = total == 0 ? OPR_TILE_EMPTY : (total == BQ * BK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
+      scls[nb + t] = word;
+    }
+    __syncthreads();
   }
 }
 
@@ -353,7 +387,7 @@ template <int BQ, int BK>
 void launch_classify(int64_t tiles, int32_t B, int32_t L, int32_t MT, int32_t NT,
                      const LayoutWs &ws, const opr_layout &out, hipStream_t s) {
   if (out.order == OPR_ORDER_ATTENTION)
-    layout_classify_attention<BQ, BK><<<dim3((unsigned)tiles), dim3(BQ), 0, s>>>(B, L, MT, NT, out);
+    layout_classify_attention<BQ, BK><<<dim3((unsigned)((int64_t)B * MT)), dim3(BQ), 0, s>>>(B, L, MT, NT, out);
   else
     layout_classify<BQ, BK><<<dim3((unsigned)tiles), dim3(BQ), 0, s>>>(B, L, MT, NT, ws, out);
 }

@@ -22,6 +22,7 @@ the MathChatSync-reasoning dataset, which is not available here:
 * ``packed_fwd_bwd`` - 2 rows x 16384, same distributions.
 * ``depth``   - one conversation of N turns (h, t, r) = (128, 1024, 256).
 * ``kpass``   - rows of 32768, N~U[4,12], h~U[32,256], t~U[256,2048], r~U[64,512].
+* ``layout_batch`` - 64 rows x 32768 with the packed distributions (layout only).
 
 Lengths use ``numpy.random.Generator(PCG64(seed))``; ``U[a, b]`` is inclusive.
 Tensors are float32 ``standard_normal`` drawn in the order Q, K, V, dO, each
@@ -67,7 +68,12 @@ SEEDS = {
     "packed_fwd_bwd": (201, 202),
     "depth": (None, 301),
     "kpass": (401, 402),
+    "layout_batch": (501, None),
 }
+
+# the layout alone on a large batch: 64 rows of 32768 tokens, packed
+# distributions (the attention workloads are too small to load the HBM)
+LAYOUT_BATCH = (64, 32768)
 
 
 def _rng(seed: int) -> np.random.Generator:
@@ -159,6 +165,12 @@ def _packed_sampler(rng):
 def packed_rows(shape: Shape, seed: int) -> List[Row]:
     """Rows for the packed workloads (N~U[2,6], h~U[16,128], t~U[64,512], r~U[32,256])."""
     return pack_greedy(_rng(seed), shape.B, shape.L, _packed_sampler)
+
+
+def layout_batch_rows(seed: int = 501) -> List[Row]:
+    """64 rows of 32768 tokens (N~U[2,6], h~U[16,128], t~U[64,512], r~U[32,256])."""
+    B, L = LAYOUT_BATCH
+    return pack_greedy(_rng(seed), B, L, _packed_sampler)
 
 
 def depth_conversation(N: int, h: int = 128, t: int = 1024, r: int = 256) -> Conversation:

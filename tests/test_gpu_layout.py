@@ -114,3 +114,23 @@ def test_depth(B, N):
 def test_kpass_rows(B):
     rows = I.kpass_rows(2)
     check_layout(B, rows, I.KPASS_ROW_LEN, 128, 128, "kpass K=2")
+
+
+def test_layout_batch_sampled_rows(B):
+    """64 rows x 32768 tokens (the layout's bandwidth workload): rows are built
+    independently, so rows 0, 31 and 63 are checked bit-exact against the
+    oracle's layout of those rows alone."""
+    Bn, L = I.LAYOUT_BATCH
+    rows = I.layout_batch_rows(I.SEEDS["layout_batch"][0])
+    print(f"[layout] batch {Bn} x {L}", flush=True)
+    lay = B.opr_build_layout(rows, L, 128, 128)
+    torch.cuda.synchronize()
+    got = lay.numpy()
+    for b in (0, 31, Bn - 1):
+        ref = O.layout([rows[b]], L)
+        for f in ("conv", "turn", "type", "pos"):
+            np.testing.assert_array_equal(got["tok_" + f][b], ref[f][0], err_msg=f"tok_{f} row {b}")
+        np.testing.assert_array_equal(got["tok_slot"][b], O.attention_order(ref, 0), err_msg=f"tok_slot row {b}")
+        s = O.schedule(ref, 0, 128, 128, order="attention")
+        for f in ("tile_class", "sub_class", "q_nnz", "q_list", "k_nnz", "k_list"):
+            np.testing.assert_array_equal(got[f][b], s[f], err_msg=f"{f} row {b}")
