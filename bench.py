@@ -605,6 +605,9 @@ def main():
         "tokens_per_s": round(conv_tokens / (ms * 1e-3), 1),
         "packed_tokens_per_s": round(packed_tokens / (ms * 1e-3), 1),
         "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
+        # secondary, labelled: the FlashAttention convention counts the
+        # backward as 2.5 forwards (14 * D * Hq * P for fwd + bwd)
+        "tflops_fa_convention": round(14.0 * shape.D * shape.Hq * P / (ms * 1e-3) / 1e12, 2),
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "roofline": roofline,
     }
