@@ -81,10 +81,18 @@ def copy_probe(steps=5):
     import torch
     src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
     dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
     for _ in range(steps):
         dst.copy_(src)
+    e.record()
     torch.cuda.synchronize()
-    log(f"copy probe: {steps} copies of {COPY_PROBE_BYTES} bytes")
+    ms = s.elapsed_time(e) / steps
+    # bytes read + bytes written: the practical HBM rate of a plain copy
+    log(f"copy probe: {steps} copies of {COPY_PROBE_BYTES} bytes, {ms:.3f} ms each, "
+        f"{2 * COPY_PROBE_BYTES / (ms * 1e-3) / 1e9:.0f} GB/s read + write")
 
 
 def summarize_traffic(run_dir, kernel):
