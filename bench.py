@@ -388,13 +388,14 @@ def layout_step(torch, Bd, dev, steps):
 def loss_step(torch, Bd, r, shape, steps, dev):
     """opr_token_ce on the forward's output: per-token loss of a V = 32 head on
     the t and r_out rows and its gradient (the loss step of training); bound
-    by HBM: it reads o once and writes dout once."""
+    by HBM: it reads o once and writes dout once (the kernel, then the dout
+    GEMM)."""
     B, L, F, V = shape.B, shape.L, shape.Hq * shape.D, 32
     g = torch.Generator(device=dev)
     g.manual_seed(7)
     w = (torch.randn((V, F), generator=g, device=dev) / math.sqrt(F)).to(torch.bfloat16)
     labels = torch.randint(0, V, (B, L), generator=g, device=dev, dtype=torch.int32)
-    ws = torch.empty(Bd.opr_token_ce_workspace_size(F, V), dtype=torch.uint8, device=dev)
+    ws = torch.empty(Bd.opr_token_ce_workspace_size(B, L, F, V), dtype=torch.uint8, device=dev)
     loss = torch.empty((B, L), dtype=torch.float32, device=dev)
     dout = torch.empty_like(r.o)
     for _ in range(3):
@@ -409,8 +410,8 @@ def loss_step(torch, Bd, r, shape, steps, dev):
     ms = s.elapsed_time(e) / steps
     scored = int(((r.lay.tok_type == 1) | (r.lay.tok_type == 3)).sum().item())
     # algorithmic bytes: o read and dout written (bf16), labels and types read, loss written,
-    # W read and its transpose written
-    nbytes = B * L * F * 2 * 2 + B * L * (4 + 1 + 4) + V * F * 2 * 2
+    # the logit gradient g (bf16 [rows][V]) written and read back, W read by both passes
+    nbytes = B * L * F * 2 * 2 + B * L * (4 + 1 + 4) + B * L * V * 2 * 2 + V * F * 2 * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": "token_ce", "ms": round(ms, 4), "rows": B * L, "scored_rows": scored, "F": F, "V": V,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -89,7 +89,7 @@ def _load() -> ctypes.CDLL:
     lib.opr_token_ce.restype = i32
     lib.opr_token_ce.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.opr_token_ce_workspace_size.restype = sz
-    lib.opr_token_ce_workspace_size.argtypes = [i32, i32]
+    lib.opr_token_ce_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.opr_block_fwd.restype = i32
     lib.opr_block_fwd.argtypes = [ctypes.POINTER(OprBlockIn), vp, vp, vp, vp, vp, sz, vp]
     lib.opr_block_bwd.restype = i32
@@ -283,8 +283,8 @@ def opr_attn_bwd(q, k, v, o, lse, dout, lay: Layout, theta: float = 1.0e6, scale
     return dq, dk, dv
 
 
-def opr_token_ce_workspace_size(F: int, V: int) -> int:
-    return int(LIB.opr_token_ce_workspace_size(F, V))
+def opr_token_ce_workspace_size(B: int, L: int, F: int, V: int) -> int:
+    return int(LIB.opr_token_ce_workspace_size(B, L, F, V))
 
 
 def opr_token_ce(o: torch.Tensor, w: torch.Tensor, labels: torch.Tensor, lay: Layout,
@@ -312,7 +312,7 @@ def opr_token_ce(o: torch.Tensor, w: torch.Tensor, labels: torch.Tensor, lay: La
         loss, dout = out
     ws_ptr, ws_n = None, 0
     if dout is not None:
-        need = opr_token_ce_workspace_size(F, V)
+        need = opr_token_ce_workspace_size(B, L, F, V)
         if workspace is None or workspace.numel() < need:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=o.device)
         ws_ptr, ws_n = workspace.data_ptr(), workspace.numel()

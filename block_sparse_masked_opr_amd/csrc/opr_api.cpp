@@ -24,9 +24,7 @@ hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, f
                                   const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq, float *dk,
                                    float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev);
-size_t token_ce_ws_bytes(int32_t F, int32_t V);
-bool gemm_bf16(bool trans_a, bool trans_b, int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
-               bool c_f32, void *ws, size_t ws_bytes, hipStream_t s);
+size_t token_ce_ws_bytes(int64_t n_rows, int32_t V);
 int block_norm_grid(int D, int64_t T, int NH);
 hipError_t launch_qk_norm_fwd(int D, int64_t T, int Hq, int Hkv, float eps, const void *qkv, const float *gq,
                               const float *gk, void *qn, void *kn, void *v, hipStream_t s);
@@ -444,10 +442,11 @@ opr_status opr_block_bwd(const opr_block_in *in, const void *qkv, const void *o,
   return hip_status();
 }
 
-size_t opr_token_ce_workspace_size(int32_t F, int32_t V) {
+size_t opr_token_ce_workspace_size(int32_t B, int32_t L, int32_t F, int32_t V) {
+  if (B < 1 || L < 1 || (int64_t)B * L >= (int64_t)1 << 31) return 0;
   if (F < 64 || F % 64 != 0 || F > (1 << 20)) return 0;
   if (V != 32 && V != 64 && V != 128) return 0;
-  return token_ce_ws_bytes(F, V);
+  return token_ce_ws_bytes((int64_t)B * L, V);
 }
 
 opr_status opr_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const void *o, const void *w,
@@ -460,10 +459,11 @@ opr_status opr_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const void *
   if (!o || !w || !labels || !tok_type || !loss) return OPR_E_INVALID;
   if (!aligned16(o) || !aligned16(w) || (dout && !aligned16(dout))) return OPR_E_INVALID;
   if (!isfinite(grad_scale)) return OPR_E_INVALID;
-  if (dout && (!workspace || ws_bytes < token_ce_ws_bytes(F, V))) {
+  if (dout && (!workspace || ws_bytes < token_ce_ws_bytes((int64_t)B * L, V))) {
     if (!workspace) return OPR_E_INVALID;
     return OPR_E_CAPACITY;
   }
+  if (dout && !aligned16(workspace)) return OPR_E_INVALID;
   if (launch_token_ce(B, L, F, V, o, w, labels, tok_type, grad_scale, loss, dout, workspace, stream) !=
       hipSuccess)
     return OPR_E_HIP;

@@ -27,6 +27,14 @@ struct Carver {
   }
 };
 
+// ---------------------------------------------------------------- GEMM
+// Row-major C[M][N] = op(A) op(B) with hipBLASLt, bf16 operands, fp32
+// accumulation, C bf16 or fp32 (c_f32); A is stored [M][K] (trans_a = false)
+// or [K][M], B [K][N] (trans_b = false) or [N][K].  ws: hipBLASLt scratch.
+// Returns false if a hipBLASLt call fails.  (gemm.cpp)
+bool gemm_bf16(bool trans_a, bool trans_b, int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
+               bool c_f32, void *ws, size_t ws_bytes, hipStream_t s);
+
 // ---------------------------------------------------------------- layout
 struct LayoutWs {
   int32_t *cpr;         // [B]   convs per row (copied from the host)

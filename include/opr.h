@@ -24,7 +24,8 @@
  *  - Pointers are device pointers unless the comment says "host".  The caller
  *    allocates and owns every buffer, including the workspace; the library
  *    never allocates or frees memory and never synchronises the stream
- *    (the one exception: the hipBLASLt handle of the block entry points).
+ *    (the one exception: the hipBLASLt handle of the entry points that run
+ *    GEMMs, opr_token_ce with a gradient and opr_block_*).
  *  - All arguments are validated on the host before any HIP call.  On a
  *    validation failure the call returns an error status, writes nothing and
  *    enqueues nothing.
@@ -236,7 +237,9 @@ size_t opr_attn_workspace_size(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, in
  *     loss[p]   = logsumexp(z_p) - z_p[labels[p]]
  *     dout[p]   = grad_scale * (softmax(z_p) - onehot(labels[p]))^T W
  * Every other row gets loss 0 and dout 0.  Logits are bf16 products with
- * fp32 accumulation; dout is rounded to bf16 once.
+ * fp32 accumulation; the logit gradient g = grad_scale * (softmax - onehot) is
+ * rounded to bf16 and dout = g W is a bf16 GEMM (hipBLASLt) with fp32
+ * accumulation, rounded to bf16 once.
  *
  *  B, L        rows and tokens per row of the layout; B*L < 2^31.
  *  F, V        features per token (F % 64 == 0, 64 <= F <= 2^20) and logits
@@ -251,18 +254,20 @@ size_t opr_attn_workspace_size(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, in
  *  loss        fp32 [B][L], every element written.
  *  dout        bf16 [B][L][F], every element written, or NULL to skip the
  *              gradient; 16-byte aligned.
- *  workspace   device, >= opr_token_ce_workspace_size(F, V) bytes when dout
- *              is not NULL (it receives a transposed copy of W); may be NULL otherwise.
+ *  workspace   device, 16-byte aligned, >= opr_token_ce_workspace_size(B, L,
+ *              F, V) bytes when dout is not NULL (it receives g and the GEMM's
+ *              scratch); may be NULL otherwise.
  * Errors: OPR_E_INVALID (null or misaligned pointer, B/L, non-finite
  * grad_scale), OPR_E_UNSUPPORTED (F, V, B*L), OPR_E_CAPACITY (ws_bytes),
- * OPR_E_HIP.
+ * OPR_E_HIP (a launch or the hipBLASLt call failed).
  */
 opr_status opr_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const void *o, const void *w,
                         const int32_t *labels, const uint8_t *tok_type, float grad_scale, float *loss,
                         void *dout, void *workspace, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes for opr_token_ce with a gradient; 0 if F or V is invalid. */
-size_t opr_token_ce_workspace_size(int32_t F, int32_t V);
+/* Workspace bytes for opr_token_ce with a gradient on B x L rows; 0 if the
+ * sizes are invalid. */
+size_t opr_token_ce_workspace_size(int32_t B, int32_t L, int32_t F, int32_t V);
 
 /* Inputs of the attention block (opr_block_fwd / opr_block_bwd). */
 typedef struct {

@@ -158,13 +158,16 @@ def test_token_ce_errors(Bd):
     assert _ce(Bd, gs=float("nan")) == Bd.OPR_E_INVALID
     assert _ce(Bd, ws=None) == Bd.OPR_E_INVALID         # the gradient needs the workspace
     assert _ce(Bd, ws_bytes=1024) == Bd.OPR_E_CAPACITY
+    assert _ce(Bd, ws=FAKE + 8) == Bd.OPR_E_INVALID      # the workspace is written with 16-byte stores
     assert _ce(Bd, B=1 << 16, L=1 << 15) == Bd.OPR_E_UNSUPPORTED
 
 
 def test_token_ce_workspace_size(Bd):
-    assert Bd.opr_token_ce_workspace_size(4096, 32) >= 4096 * 32 * 2
-    assert Bd.opr_token_ce_workspace_size(4000, 32) == 0
-    assert Bd.opr_token_ce_workspace_size(4096, 40) == 0
+    assert Bd.opr_token_ce_workspace_size(2, 16384, 4096, 32) >= 2 * 16384 * 32 * 2
+    assert Bd.opr_token_ce_workspace_size(2, 16384, 4096, 128) > Bd.opr_token_ce_workspace_size(2, 16384, 4096, 32)
+    assert Bd.opr_token_ce_workspace_size(2, 16384, 4000, 32) == 0
+    assert Bd.opr_token_ce_workspace_size(2, 16384, 4096, 40) == 0
+    assert Bd.opr_token_ce_workspace_size(0, 16384, 4096, 32) == 0
 
 
 def _block_in(Bd, **kw):
