@@ -350,14 +350,17 @@ def layout_step(torch, Bd, dev, steps):
     """opr_build_layout alone on 64 rows x 32768 tokens (packed distributions):
     bound by HBM; algorithmic bytes = everything the layout writes (per token
     its ids, slots and runs of slots; per tile its classes and list entries).
-    The time holds the copies of the host turn lists as well."""
+    The time holds the copies of the host turn lists (from pinned memory) as
+    well."""
     B, L = I.LAYOUT_BATCH
     rows = I.layout_batch_rows(I.SEEDS["layout_batch"][0])
     lay = Bd.opr_build_layout(rows, L, 128, 128, device=dev)
     cpr, tpc, turns = I.flatten_rows(rows)
     lws = torch.empty(Bd.opr_build_layout_workspace_size(B, L, len(tpc), len(turns)), dtype=torch.uint8, device=dev)
     st = lay.c_struct()
-    args = (B, L, 128, 128, cpr.ctypes.data, tpc.ctypes.data, turns.ctypes.data, lws.data_ptr(), lws.numel(),
+    # the host turn lists in pinned memory, so that their copies are asynchronous
+    host = [torch.from_numpy(np.ascontiguousarray(x)).pin_memory() for x in (cpr, tpc, turns)]
+    args = (B, L, 128, 128, host[0].data_ptr(), host[1].data_ptr(), host[2].data_ptr(), lws.data_ptr(), lws.numel(),
             ctypes.byref(st), torch.cuda.current_stream(dev).cuda_stream)
 
     def call():
