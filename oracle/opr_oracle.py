@@ -409,13 +409,16 @@ def attn_fwd(q, k, v, lay, theta: float, scale: float = None):
     return O, LSE
 
 
-def attn_bwd(q, k, v, do, lay, theta: float, scale: float = None):
+def attn_bwd(q, k, v, do, lay, theta: float, scale: float = None, o=None):
     """Gradients of sum(O * dO) w.r.t. the pre-RoPE q, k and v, float64.
 
-    dV = sum_group P^T dO; dP = dO V^T; dS = P (dP - rowsum(P dP));
+    dV = sum_group P^T dO; dP = dO V^T; dS = P (dP - Delta);
     dQ' = scale dS K'; dK' = scale sum_group dS^T Q'; dQ = R^T dQ', dK = R^T dK'.
+    Delta = rowsum(P dP), which is rowsum(dO * O); with ``o`` given (the forward
+    output as a backward receives it, e.g. stored in bf16), Delta = rowsum(dO * o).
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    o = None if o is None else _f64(o)
     B, L, Hq, D = q.shape
     Hkv = k.shape[2]
     g = Hq // Hkv
@@ -441,7 +444,9 @@ def attn_bwd(q, k, v, do, lay, theta: float, scale: float = None):
                 dO = do[b, a:e, h]
                 dv[b, a:e, kv] += P.T @ dO
                 dP = dO @ v[b, a:e, kv].T
-                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                delta = (P * dP).sum(axis=1, keepdims=True) if o is None else \
+                    (dO * o[b, a:e, h]).sum(axis=1, keepdims=True)
+                dS = P * (dP - delta)
                 dqr[:, h] = scale * (dS @ kr[:, kv])
                 dkr[:, kv] += scale * (dS.T @ qr[:, h])
             dq[b, a:e] = rope_transpose(dqr, pos, theta)

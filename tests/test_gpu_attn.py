@@ -3,8 +3,12 @@
 Bar: max |x - ref| <= 2e-2 and sum|x - ref| / sum|ref| <= 5e-3 for O, LSE,
 dQ, dK, dV over non-PAD rows; PAD rows must be exactly O = 0, LSE = -inf and
 zero gradients.  Both sides consume the same bf16 inputs (the oracle upcasts).
+The backward's Delta = rowsum(dout * o) is taken over o as the backward
+receives it, bf16: the reference backward gets the oracle's own O rounded to
+bf16 (with the exact O the dK of a 16-head group moves by up to 2.4e-2 from
+that rounding alone).
 Full comparisons run at sizes the oracle finishes in seconds (several tiles,
-ragged L, GQA 1/2/4/8, D 64 and 128, empty segments, empty rows); the packed
+ragged L, GQA 1/2/4/8/16, D 64 and 128, empty segments, empty rows); the packed
 workloads are checked on whole sampled conversations (the mask is block
 diagonal by conversation, so their rows and keys depend on nothing else) and
 on complete kv-head groups.
@@ -55,6 +59,12 @@ def run_gpu(Bd, rows, L, t, bwd=True, reuse=False):
     return out
 
 
+def as_stored(o):
+    """The oracle's forward output in the form the backward receives it (bf16,
+    the ABI's o): the backward's Delta = rowsum(dout * o) is taken over it."""
+    return bf16_f64(I.round_to_bf16_bits(np.asarray(o, dtype=np.float32)))
+
+
 def compare_full(label, rows, L, t, got, bwd=True):
     lay = O.layout(rows, L)
     q, k, v = (bf16_f64(t[n]) for n in ("q", "k", "v"))
@@ -67,7 +77,7 @@ def compare_full(label, rows, L, t, got, bwd=True):
     assert_close("O", got["o"][live], o[live])
     assert_close("LSE", got["lse"].transpose(0, 2, 1)[live], lse.transpose(0, 2, 1)[live])
     if bwd:
-        dq, dk, dv = O.attn_bwd(q, k, v, bf16_f64(t["do"]), lay, THETA)
+        dq, dk, dv = O.attn_bwd(q, k, v, bf16_f64(t["do"]), lay, THETA, o=as_stored(o))
         for n, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
             assert (got[n][pad] == 0).all(), n
             assert_close(n, got[n][live], ref[live])
@@ -86,6 +96,8 @@ SMALL = [
     ("mha d128 one tile", 3, 3, 0, 2, 2, 128),
     ("gqa8 d128", 4, 1, 200, 8, 1, 128),
     ("gqa4 d64 long turns", 5, 2, 1, 4, 1, 64),
+    ("gqa16 d128", 6, 1, 45, 16, 1, 128),
+    ("mqa32 d64 two groups", 7, 2, 3, 32, 2, 64),
 ]
 
 
@@ -144,7 +156,7 @@ def compare_convs(label, rows, L, t, got, shape, convs_per_row=2, groups=(0, Non
             assert_close("O", got["o"][b:b + 1, a:e][:, :, qh], o)
             assert_close("LSE", got["lse"][b:b + 1][:, qh, a:e], lse)
             if bwd:
-                dq, dk, dv = O.attn_bwd(q, k, v, bf16_f64(sl["do"][:, :, qh]), lay_c, THETA)
+                dq, dk, dv = O.attn_bwd(q, k, v, bf16_f64(sl["do"][:, :, qh]), lay_c, THETA, o=as_stored(o))
                 assert_close("dq", got["dq"][b:b + 1, a:e][:, :, qh], dq)
                 assert_close("dk", got["dk"][b:b + 1, a:e][:, :, kvh], dk)
                 assert_close("dv", got["dv"][b:b + 1, a:e][:, :, kvh], dv)
@@ -216,7 +228,7 @@ def test_scaled_inputs(B):
     lay = O.layout(rows, L)
     q, k, v, do = (bf16_f64(ts[n]) for n in ("q", "k", "v", "do"))
     o, lse = O.attn_fwd(q, k, v, lay, THETA)
-    dq, dk, dv = O.attn_bwd(q, k, v, do, lay, THETA)
+    dq, dk, dv = O.attn_bwd(q, k, v, do, lay, THETA, o=as_stored(o))
     live = lay["type"] != O.PAD
     print("[attn] scaled inputs", flush=True)
     # relative to the largest magnitude; O is bf16, whose rounding alone is up

@@ -164,6 +164,25 @@ def test_attn_rows_vs_sdpa(seed):
         np.testing.assert_allclose(dq, rdq[b, sel], atol=1e-11)
 
 
+def test_bwd_with_given_o():
+    """Delta from a given forward output: with the exact O it is the default
+    backward; with O rounded to bf16 only the terms through Delta move."""
+    rows = [[[(6, 9, 5, 5), (4, 7, 3, 3)]]]
+    L = I.row_used(rows[0]) + 2
+    lay = O.layout(rows, L)
+    rng = np.random.default_rng(31)
+    q, k, v = (rng.standard_normal((1, L, h, 16)) for h in (4, 2, 2))
+    do = rng.standard_normal((1, L, 4, 16))
+    o, _ = O.attn_fwd(q, k, v, lay, THETA)
+    ref = O.attn_bwd(q, k, v, do, lay, THETA)
+    for a, b in zip(O.attn_bwd(q, k, v, do, lay, THETA, o=o), ref):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    ob = I.bf16_bits_to_f32(I.round_to_bf16_bits(o.astype(np.float32))).astype(np.float64)
+    dq, dk, dv = O.attn_bwd(q, k, v, do, lay, THETA, o=ob)
+    np.testing.assert_array_equal(dv, ref[2])          # dV does not depend on Delta
+    assert 0 < np.abs(dk - ref[1]).max() < 1e-1
+
+
 def test_bwd_finite_differences():
     rows = [[[(3, 2, 2, 2), (2, 3, 1, 1)], [(2, 0, 1, 1)]]]
     L = I.row_used(rows[0]) + 2
