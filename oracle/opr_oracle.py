@@ -392,6 +392,8 @@ def attn_fwd(q, k, v, lay, theta: float, scale: float = None):
     for b in range(B):
         for c in range(n_convs(lay, b)):
             a, e = conv_range(lay, b, c)
+            if e == a:         # a conversation of empty segments: no queries, no keys
+                continue
             M = conv_mask(lay, b, c)
             pos = lay["pos"][b, a:e]
             qr = rope(q[b, a:e], pos, theta)
@@ -429,6 +431,8 @@ def attn_bwd(q, k, v, do, lay, theta: float, scale: float = None, o=None):
     for b in range(B):
         for c in range(n_convs(lay, b)):
             a, e = conv_range(lay, b, c)
+            if e == a:
+                continue
             M = conv_mask(lay, b, c)
             pos = lay["pos"][b, a:e]
             qr = rope(q[b, a:e], pos, theta)

@@ -128,6 +128,16 @@ def test_empty_row_and_pad(B):
     compare_full("empty row", rows, L, t, run_gpu(B, rows, L, t))
 
 
+def test_empty_conversations(B):
+    """Conversations with no turns, or with only empty segments, packed between
+    others (they hold no tokens)."""
+    a, b = [(40, 30, 20, 20), (10, 0, 5, 5)], [(7, 60, 33, 33)]
+    rows = [[a, [], b, [(0, 0, 0, 0)]], [[(0, 0, 0, 0), (0, 0, 0, 0)], b, [], a]]
+    L = max(I.row_used(r) for r in rows) + 9
+    t = I.make_tensors(2, L, 4, 2, 64, seed=78)
+    compare_full("empty conversations", rows, L, t, run_gpu(B, rows, L, t))
+
+
 def _group_subset(Hq, Hkv, groups):
     g = Hq // Hkv
     qh = [kv * g + j for kv in groups for j in range(g)]

@@ -223,6 +223,33 @@ def test_pad_rows_are_zero():
     assert (dq[0, 9:] == 0).all() and (dk[0, 9:] == 0).all() and (dv[0, 9:] == 0).all()
 
 
+def test_empty_conversations_change_nothing():
+    """A conversation with no turns, or with only empty segments, holds no
+    tokens: the row with it packed between others has exactly the outputs and
+    gradients of the row without it (every conversation starts at position 0
+    and sees only itself), and both agree with the torch reference."""
+    a, b = [(4, 3, 2, 2), (1, 5, 3, 3)], [(2, 6, 1, 1)]
+    with_empty = [[a, [], b, [(0, 0, 0, 0), (0, 0, 0, 0)], a]]
+    without = [[a, b, a]]
+    L = I.row_used(without[0]) + 3
+    lay_e, lay_n = O.layout(with_empty, L), O.layout(without, L)
+    np.testing.assert_array_equal(lay_e["pos"], lay_n["pos"])
+    np.testing.assert_array_equal(lay_e["type"], lay_n["type"])
+    rng = np.random.default_rng(8)
+    q, k, v = (rng.standard_normal((1, L, h, 16)) for h in (4, 2, 2))
+    do = rng.standard_normal((1, L, 4, 16))
+    oe, lsee = O.attn_fwd(q, k, v, lay_e, THETA)
+    on, lsen = O.attn_fwd(q, k, v, lay_n, THETA)
+    np.testing.assert_array_equal(oe, on)
+    np.testing.assert_array_equal(lsee, lsen)
+    for ge, gn in zip(O.attn_bwd(q, k, v, do, lay_e, THETA), O.attn_bwd(q, k, v, do, lay_n, THETA)):
+        np.testing.assert_array_equal(ge, gn)
+    ro, rlse, rdq, rdk, rdv = _torch_reference(q, k, v, do, lay_e, THETA)
+    np.testing.assert_allclose(oe, ro, atol=1e-12)
+    for g, r in zip(O.attn_bwd(q, k, v, do, lay_e, THETA), (rdq, rdk, rdv)):
+        np.testing.assert_allclose(g, r, atol=1e-11)
+
+
 def test_causal_special_case_vs_sdpa_is_causal():
     """One turn of only a human message: SDPA with is_causal=True."""
     L, D = 23, 16
