@@ -8,7 +8,7 @@
 //
 // Both kernels run in attention order (tiles of slots; results are written
 // at the slot's token).
-// attn_dkdv_kernel: one workgroup per (128-key tile n, kv head, row); wave w
+// attn_dkdv_kernel: one workgroup per (work item of 128-key tile n, kv head); wave w
 //   owns key slots n*128 + 32w .. +31, one per lane column, K' and V of its
 //   key in registers.  Its stages are (q-tile of k_list, head of the group,
 //   64-query half) with a non-empty sub-block; each streams the Q' and dO rows
@@ -20,7 +20,11 @@
 //   row), pipelined like the forward kernel over the K' / V tiles; S and dP^T
 //   are recomputed per non-empty sub-block and dQ^T += K'^T dS^T.
 // Work items start longest first, round-robin over the XCDs (q_order and
-// k_order of the prologue).  Partial sub-blocks are masked with 64-bit masks
+// k_items of the prologue).  A k-tile column whose stages exceed the cap of
+// the work order runs as several items, each over a contiguous part of its
+// stage range; parts after the first write partial dK/dV that
+// dkdv_split_reduce_kernel adds in a fixed order (deterministic).  Partial
+// sub-blocks are masked with 64-bit masks
 // built from the two runs of slots of each query or key.
 //
 // Units: k' and v carry one exponent per (row, kv head), constant inside a
@@ -67,9 +71,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   __shared__ int sh_count;
   __shared__ int64_t sh_next;
 
-  const int64_t R = blockIdx.x;  // rank: longest columns first, round-robin over the XCDs
-  if (R >= (int64_t)p.B * p.NT * p.Hkv) return;
-  const int32_t col = p.k_order[R / p.Hkv];
+  const int64_t R = blockIdx.x;  // rank: longest items first, round-robin over the XCDs
+  if (R / p.Hkv >= p.k_counts[0]) return;
+  const int4 item = p.k_items[R / p.Hkv];  // (column, part, parts, partial slot or -1)
+  const int32_t col = item.x;
   const int kvh = (int)(R % p.Hkv);
   const int b = col / p.NT;
   const int n = col - b * p.NT;
@@ -249,13 +254,15 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  int64_t fnext = 0;
+  // this item's part of the column's stage range
   const int64_t ftotal = (int64_t)nnz * p.group * 2;
-  while (fnext < ftotal) {
+  int64_t fnext = ftotal * item.y / item.z;
+  const int64_t fend = ftotal * (item.y + 1) / item.z;
+  while (fnext < fend) {
     __syncthreads();
     if (wave == 0) {
       int64_t f = fnext;
-      const int c = build_k_stages(lst, subs_b, p.NT, n, p.group, nnz, p.eqt + hbase * p.MTS,
+      const int c = build_k_stages(lst, subs_b, p.NT, n, p.group, fend, p.eqt + hbase * p.MTS,
                                    p.edot + hbase * p.MTS, p.MTS, &f, stages, lane);
       if (lane == 0) {
         sh_count = c;
@@ -282,8 +289,16 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   }
 
   if (key < p.L) {
-    const int tok = p.slot_tok[(int64_t)b * p.L + key];
-    const int64_t out = (((int64_t)b * p.L + tok) * p.Hkv + kvh) * D;
+    // part 0 writes at the key's token, parts 1.. into their partial slot
+    int64_t out;
+    if (item.w < 0) {
+      const int tok = p.slot_tok[(int64_t)b * p.L + key];
+      out = (((int64_t)b * p.L + tok) * p.Hkv + kvh) * D;
+    } else {
+      out = (((int64_t)item.w * p.Hkv + kvh) * OPR_ATTN_BLOCK + (key - n * OPR_ATTN_BLOCK)) * D;
+      dk = p.kpart;
+      dv = p.kpart + (int64_t)kSplitSlots * OPR_ATTN_BLOCK * D;
+    }
     if (!pwave) {
       // dK^T in units 2^(eqr + edor + ev - kDsShift), rotated back by RoPE
       const float2 *cs = p.rope + ((int64_t)b * p.Lp + key) * (D / 2);
@@ -321,6 +336,37 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   }
 }
 
+// dK and dV of the columns cut into parts: part 0 wrote them at the tokens;
+// add parts 1..s-1 from their partial slots, in order.  One workgroup per
+// (cut column, kv head); grid.x covers the most cut columns there can be.
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(AttnParams p, float *dk, float *dv) {
+  if ((int)blockIdx.x >= p.k_counts[1]) return;
+  const int4 e = p.k_split[blockIdx.x];  // (column, first partial slot, parts, 0)
+  const int kvh = blockIdx.y;
+  const int b = e.x / p.NT, n = e.x - b * p.NT;
+  constexpr int C4 = D / 4;  // float4 per key row
+  const float *pk = p.kpart, *pv = p.kpart + (int64_t)kSplitSlots * OPR_ATTN_BLOCK * D;
+  for (int i = threadIdx.x; i < OPR_ATTN_BLOCK * C4; i += 256) {
+    const int kl = i / C4, c4 = i - kl * C4;
+    const int key = n * OPR_ATTN_BLOCK + kl;
+    if (key >= p.L) continue;
+    const int tok = p.slot_tok[(int64_t)b * p.L + key];
+    const int64_t out = (((int64_t)b * p.L + tok) * p.Hkv + kvh) * D + 4 * c4;
+    float4 ak = *reinterpret_cast<const float4 *>(dk + out);
+    float4 av = *reinterpret_cast<const float4 *>(dv + out);
+    for (int j = 0; j < e.z - 1; ++j) {
+      const int64_t src = (((int64_t)(e.y + j) * p.Hkv + kvh) * OPR_ATTN_BLOCK + kl) * D + 4 * c4;
+      const float4 xk = *reinterpret_cast<const float4 *>(pk + src);
+      const float4 xv = *reinterpret_cast<const float4 *>(pv + src);
+      ak.x += xk.x; ak.y += xk.y; ak.z += xk.z; ak.w += xk.w;
+      av.x += xv.x; av.y += xv.y; av.z += xv.z; av.w += xv.w;
+    }
+    *reinterpret_cast<float4 *>(dk + out) = ak;
+    *reinterpret_cast<float4 *>(dv + out) = av;
+  }
+}
+
 }  // namespace
 
 void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParams *p);
@@ -332,10 +378,18 @@ hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq
                                    float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev) {
   AttnParams p;
   fill_params(in, scale, ws, &p);
-  const unsigned gk = (unsigned)((int64_t)in.B * in.Hkv * p.NT);
+  // every column once, plus the most extra parts the work order can make
+  const int32_t extra = kSplitSlots / in.Hkv + 1;
+  const unsigned gk = (unsigned)(((int64_t)in.B * p.NT + extra) * in.Hkv);
+  const dim3 gr((unsigned)extra, (unsigned)in.Hkv);
   if (ev) (void)hipEventRecord(ev[0], s);
-  if (in.D == 64) attn_dkdv_kernel<64><<<gk, 512, 0, s>>>(p, dk, dv);
-  else attn_dkdv_kernel<128><<<gk, 512, 0, s>>>(p, dk, dv);
+  if (in.D == 64) {
+    attn_dkdv_kernel<64><<<gk, 512, 0, s>>>(p, dk, dv);
+    dkdv_split_reduce_kernel<64><<<gr, 256, 0, s>>>(p, dk, dv);
+  } else {
+    attn_dkdv_kernel<128><<<gk, 512, 0, s>>>(p, dk, dv);
+    dkdv_split_reduce_kernel<128><<<gr, 256, 0, s>>>(p, dk, dv);
+  }
   if (ev) (void)hipEventRecord(ev[1], s);
   launch_attn_dq_kernel(p, in.D, dq, s);
   if (ev) (void)hipEventRecord(ev[2], s);

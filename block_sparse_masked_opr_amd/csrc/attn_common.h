@@ -318,11 +318,12 @@ __device__ __forceinline__ f16x8 tile_col8(const char *lds, const OperandOffsets
 // Work order.  Workgroups are dispatched round-robin over the 8 XCDs (block
 // b goes to XCD b mod 8, each XCD with its own L2), and a kernel lasts as
 // long as its slowest CU.  The work items are therefore handed out longest
-// first: q_order / k_order list the q-tile rows / k-tile columns (b*MT + m,
-// b*NT + n) by decreasing number of stages, and consecutive ranks go to
+// first: q_order lists the q-tile rows (b*MT + m) and k_items the dK/dV
+// items (a k-tile column b*NT + n, or one part of a long column's stage
+// range) by decreasing number of stages, and consecutive ranks go to
 // consecutive XCDs.
 //
-// dK/dV: rank R = block id; item (k_order[R / Hkv], kv head R % Hkv).
+// dK/dV: rank R = block id; item (k_items[R / Hkv], kv head R % Hkv).
 // Forward and dQ: super-rank R = (i / group) * 8 + x for block 8i + x, head
 // j = i % group of kv head R % Hkv of row k = q_order[R / Hkv]: the q heads
 // of one kv group sit on one XCD back to back and share its K/V tiles in L2.
@@ -363,7 +364,10 @@ struct AttnParams {
   // Everything is indexed by slot (attention order) except the outputs,
   // which are written at token slot_tok[s].
   const int32_t *q_order;      // [B*MT] q-tile rows, most stages first
-  const int32_t *k_order;      // [B*NT] k-tile columns, most stages first
+  const int4 *k_items;         // dK/dV items (column, part, parts, partial slot), most stages first
+  const int4 *k_split;         // columns cut into parts: (column, first partial slot, parts, 0)
+  const int32_t *k_counts;     // [0] items, [1] cut columns
+  float *kpart;                // partials of parts 1.. : [slot * Hkv + kv head][128][D], dK then dV
   const int32_t *slot_tok;     // [B][L] token at each slot
   const int4 *qiv;             // [B][L] key slots a query slot sees: [x, y) and [z, w)
   const int4 *kiv;             // [B][L] query slots that see a key slot: [x, y) and [z, w)

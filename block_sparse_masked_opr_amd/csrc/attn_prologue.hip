@@ -315,29 +315,84 @@ __global__ __launch_bounds__(256) void scale_delta_kernel(int32_t B, int32_t L, 
 
 // Longest-first work order (see q_work_item): the q-tile rows (b*MT + m) by
 // decreasing number of non-empty 64-key halves over their tile lists - the
-// stages of a forward or dQ workgroup - and the k-tile columns (b*NT + n) by
-// decreasing number of non-empty 64-query halves - the stages of a dK/dV
-// workgroup.  One workgroup: per-item costs, then a counting sort (costs
-// above kOrderBins - 1 share the last bin; ties in any order).
+// stages of a forward or dQ workgroup - and the dK/dV work items by
+// decreasing number of non-empty 64-query halves.  A k-tile column is one
+// item, or, when its halves exceed the cap, s = ceil(halves / cap) items
+// that each take 1/s of its stage range (a column seen by every later turn
+// of a long conversation would otherwise outlast all other workgroups).
+// The cap is max(kMinSplit, ceil(total halves * Hkv / kSplitSlots)): one
+// workgroup's share of the whole when one workgroup runs per CU on 256 CUs
+// (a smaller cap cut columns of balanced workloads for no gain in a
+// longest-first simulation of the schedule), and it keeps the extra items
+// below kSplitSlots / Hkv.  Part 0 of a cut
+// column writes dK/dV itself; parts 1..s-1 take partial slots, which
+// dkdv_split_reduce_kernel adds in order.  One workgroup: per-item costs,
+// then a counting sort (costs above kOrderBins - 1 share the last bin; ties
+// in any order).
 constexpr int kOrderThreads = 1024, kOrderBins = 4096;
+constexpr int32_t kMinSplit = 16;
+
+__device__ int64_t block_sum_i64(int64_t v, int64_t *red) {
+  const int tid = threadIdx.x;
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  int64_t t = 0;
+  for (int i = 0; i < kOrderThreads / 64; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive scan of bins[] in place (bins[i] becomes the first rank of bin i).
+__device__ void scan_bins(int32_t *bins, int32_t *wave_sum) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  constexpr int PER = kOrderBins / kOrderThreads;
+  int32_t v[PER], run = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    v[e] = bins[tid * PER + e];
+    run += v[e];
+  }
+  int32_t incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wave_sum[wv] = incl;
+  __syncthreads();
+  int32_t base = 0;
+  for (int i = 0; i < wv; ++i) base += wave_sum[i];
+  int32_t start = base + incl - run;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    bins[tid * PER + e] = start;
+    start += v[e];
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ int32_t parts_of(int32_t c, int32_t cap) { return c > cap ? (c + cap - 1) / cap : 1; }
 
 __global__ __launch_bounds__(kOrderThreads) void work_order_kernel(int32_t n_rows, int32_t n_cols, int32_t MT,
-                                                                   int32_t NT, const uint32_t *sub_class,
+                                                                   int32_t NT, int32_t Hkv, const uint32_t *sub_class,
                                                                    const int32_t *q_nnz, const int32_t *q_list,
                                                                    const int32_t *k_nnz, const int32_t *k_list,
-                                                                   int32_t *cost, int32_t *q_order,
-                                                                   int32_t *k_order) {
+                                                                   int32_t *cost, int32_t *q_order, int4 *k_raw,
+                                                                   int4 *k_items, int4 *k_split, int32_t *k_counts) {
   __shared__ int32_t bins[kOrderBins];
   __shared__ int32_t wave_sum[kOrderThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ int64_t red[kOrderThreads / 64];
+  __shared__ int32_t sh_items, sh_parts, sh_cut;
+  const int tid = threadIdx.x;
   for (int pass = 0; pass < 2; ++pass) {
     const int32_t n = pass == 0 ? n_rows : n_cols;
-    int32_t *order = pass == 0 ? q_order : k_order;
     int32_t *c = cost + (pass == 0 ? 0 : n_rows);
     for (int i = tid; i < kOrderBins; i += kOrderThreads) bins[i] = 0;
     __syncthreads();
     // 8 lanes per item, each summing every 8th entry of its tile list
     const int sub = tid & 7;
+    int64_t mine = 0;
     for (int32_t it = tid >> 3; it < n; it += kOrderThreads / 8) {
       int32_t k = 0;
       if (pass == 0) {  // row it: key halves are sub-block columns {0,1} and {2,3}
@@ -361,38 +416,65 @@ __global__ __launch_bounds__(kOrderThreads) void work_order_kernel(int32_t n_row
       k += __shfl_xor(k, 2);
       k += __shfl_xor(k, 4);
       if (sub == 0) {
-        k = min(k, kOrderBins - 1);
         c[it] = k;
-        atomicAdd(&bins[kOrderBins - 1 - k], 1);  // bin 0 holds the largest cost
+        mine += k;
+        if (pass == 0) atomicAdd(&bins[kOrderBins - 1 - min(k, kOrderBins - 1)], 1);  // bin 0: largest
+      }
+    }
+    if (pass == 0) {
+      __syncthreads();
+      scan_bins(bins, wave_sum);
+      for (int32_t it = tid; it < n; it += kOrderThreads)
+        q_order[atomicAdd(&bins[kOrderBins - 1 - min(c[it], kOrderBins - 1)], 1)] = it;
+      __syncthreads();
+      continue;
+    }
+    // columns: the cap, doubled until the extra parts fit (they do at once:
+    // each cut column adds fewer than c / cap parts)
+    const int64_t total = block_sum_i64(mine, red);
+    int64_t cap64 = (total * Hkv + kSplitSlots - 1) / kSplitSlots;
+    if (cap64 < kMinSplit) cap64 = kMinSplit;
+    for (;;) {
+      const int32_t cap = (int32_t)min(cap64, (int64_t)INT32_MAX);
+      int64_t extra = 0;
+      for (int32_t it = tid; it < n; it += kOrderThreads) extra += parts_of(c[it], cap) - 1;
+      extra = block_sum_i64(extra, red);
+      if (extra * Hkv < kSplitSlots || cap64 >= INT32_MAX) break;
+      cap64 *= 2;
+    }
+    const int32_t cap = (int32_t)min(cap64, (int64_t)INT32_MAX);
+    if (tid == 0) {
+      sh_items = 0;
+      sh_parts = 0;
+      sh_cut = 0;
+    }
+    __syncthreads();
+    for (int32_t it = tid; it < n; it += kOrderThreads) {
+      const int32_t s = parts_of(c[it], cap);
+      const int32_t first = atomicAdd(&sh_items, s);
+      int32_t slot = -1;
+      if (s > 1) {
+        slot = atomicAdd(&sh_parts, s - 1);
+        k_split[atomicAdd(&sh_cut, 1)] = make_int4(it, slot, s, 0);
+      }
+      const int32_t ic = (c[it] + s - 1) / s;
+      for (int32_t j = 0; j < s; ++j) {
+        k_raw[first + j] = make_int4(it, j, s, j == 0 ? -1 : slot + j - 1);
+        atomicAdd(&bins[kOrderBins - 1 - min(ic, kOrderBins - 1)], 1);
       }
     }
     __syncthreads();
-    // exclusive scan of the bins: 4 per thread, then over the threads
-    constexpr int PER = kOrderBins / kOrderThreads;
-    int32_t v[PER], run = 0;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      v[e] = bins[tid * PER + e];
-      run += v[e];
+    const int32_t n_items = sh_items;
+    scan_bins(bins, wave_sum);
+    for (int32_t i = tid; i < n_items; i += kOrderThreads) {
+      const int4 e = k_raw[i];
+      const int32_t ic = (c[e.x] + e.z - 1) / e.z;
+      k_items[atomicAdd(&bins[kOrderBins - 1 - min(ic, kOrderBins - 1)], 1)] = e;
     }
-    int32_t incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int32_t y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
+    if (tid == 0) {
+      k_counts[0] = n_items;
+      k_counts[1] = sh_cut;
     }
-    if (lane == 63) wave_sum[wv] = incl;
-    __syncthreads();
-    int32_t base = 0;
-    for (int i = 0; i < wv; ++i) base += wave_sum[i];
-    int32_t start = base + incl - run;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      bins[tid * PER + e] = start;
-      start += v[e];
-    }
-    __syncthreads();
-    for (int32_t it = tid; it < n; it += kOrderThreads) order[atomicAdd(&bins[kOrderBins - 1 - c[it]], 1)] = it;
     __syncthreads();
   }
 }
@@ -462,9 +544,10 @@ void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t
 
 void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int32_t MT = ws.Lp / OPR_ATTN_BLOCK, NT = MT;
-  work_order_kernel<<<1, kOrderThreads, 0, s>>>(in.B * MT, in.B * NT, MT, NT, in.layout.sub_class, in.layout.q_nnz,
-                                               in.layout.q_list, in.layout.k_nnz, in.layout.k_list, ws.order_cost,
-                                               ws.q_order, ws.k_order);
+  work_order_kernel<<<1, kOrderThreads, 0, s>>>(in.B * MT, in.B * NT, MT, NT, in.Hkv, in.layout.sub_class,
+                                               in.layout.q_nnz, in.layout.q_list, in.layout.k_nnz, in.layout.k_list,
+                                               ws.order_cost, ws.q_order, ws.k_raw, ws.k_items, ws.k_split,
+                                               ws.k_counts);
 }
 
 // delta and the fp16 dout copy with its tile exponents and their group minima.

@@ -45,21 +45,21 @@ __device__ inline int build_q_stages(const int32_t *lst, const uint32_t *subs, i
 
 // Key-side kernel (dK/dV) of k-tile n: wave w owns key sub-column w; the
 // stages run over the q-tiles k_list[...] x the G heads of the kv group x the
-// two 64-query halves, flat index f = (tile * G + head) * 2 + half.  The
+// two 64-query halves, flat index f = (tile * G + head) * 2 + half, from *f up
+// to fend (a work item's part of the column's range).  The
 // descriptor is (x, y, z, w): x and y as above, z the q' and w the dout
 // exponents (+ 64, one byte each) of the stage's four 16-query tiles
 // (eqt_g, edot_g: the group's [G][MTS] tile exponents).
 constexpr int kKStageCap = 512;  // dK/dV descriptors per list chunk (8 KB of LDS)
 
 __device__ inline int build_k_stages(const int32_t *lst, const uint32_t *subs_b, int NT, int n, int G,
-                                     int nnz, const int32_t *eqt_g, const int32_t *edot_g, int MTS,
+                                     int64_t fend, const int32_t *eqt_g, const int32_t *edot_g, int MTS,
                                      int64_t *f, uint4 *stages, int lane) {
   int count = 0;
-  const int64_t total = (int64_t)nnz * G * 2;
-  while (*f < total && count + 64 <= kKStageCap) {
+  while (*f < fend && count + 64 <= kKStageCap) {
     const int64_t ff = *f + lane;
     uint32_t cls = 0, x = 0, z = 0, zw = 0;
-    if (ff < total) {
+    if (ff < fend) {
       const int qh = (int)(ff & 1);
       const int64_t tj = ff >> 1;
       const int hj = (int)(tj % G);
@@ -84,7 +84,7 @@ __device__ inline int build_k_stages(const int32_t *lst, const uint32_t *subs_b,
     count += __popcll(bal);
     *f += 64;
   }
-  if (*f > total) *f = total;
+  if (*f > fend) *f = fend;
   return count;
 }
 

@@ -63,14 +63,18 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   w.eref = cv.take<int32_t>((size_t)2 * in.B * in.Hkv);
   const size_t tiles = (size_t)in.B * (Lp / OPR_ATTN_BLOCK);
   w.q_order = cv.take<int32_t>(tiles);
-  w.k_order = cv.take<int32_t>(tiles);
   w.order_cost = cv.take<int32_t>(2 * tiles);
+  w.k_items = cv.take<int4>(tiles + kSplitSlots);
+  w.k_raw = cv.take<int4>(tiles + kSplitSlots);
+  w.k_split = cv.take<int4>(kSplitSlots);
+  w.k_counts = cv.take<int32_t>(4);
   // everything above is the forward state; the backward part follows
   if (is_bwd) {
     w.dor = cv.take<uint16_t>(qn);
     w.edot = cv.take<int32_t>(etiles);
     w.dsc = cv.take<float>((size_t)in.B * in.Hq * Lp);
     w.lse2 = cv.take<float>((size_t)in.B * in.Hq * Lp);
+    w.kpart = cv.take<float>((size_t)kSplitSlots * OPR_ATTN_BLOCK * in.D * 2);
   }
   if (o) *o = w;
   return cv.off;
@@ -105,7 +109,10 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->eref = ws.eref;
   p->MTS = ws.Lp / kTile;
   p->q_order = ws.q_order;
-  p->k_order = ws.k_order;
+  p->k_items = ws.k_items;
+  p->k_split = ws.k_split;
+  p->k_counts = ws.k_counts;
+  p->kpart = ws.kpart;
   p->slot_tok = in.layout.slot_tok;
   p->qiv = reinterpret_cast<const int4 *>(in.layout.slot_qiv);
   p->kiv = reinterpret_cast<const int4 *>(in.layout.slot_kiv);

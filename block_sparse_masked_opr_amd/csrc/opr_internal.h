@@ -58,6 +58,11 @@ hipError_t launch_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t bl
                                hipStream_t stream);
 
 // ---------------------------------------------------------------- attention
+// Extra dK/dV work items from cutting long columns, summed over the kv heads:
+// the cap on a part's stages is at least total * Hkv / kSplitSlots, so the
+// parts beyond the first number fewer than kSplitSlots / Hkv.
+constexpr int kSplitSlots = 256;
+
 struct AttnWs {
   int32_t Lp;           // L rounded up to OPR_ATTN_BLOCK
   // everything below is in slot (attention) order
@@ -80,8 +85,15 @@ struct AttnWs {
   int32_t *edot;        //                                        (bwd)
   int32_t *eref;
   int32_t *q_order;     // [B*MT] q-tile rows, most stages first
-  int32_t *k_order;     // [B*NT] k-tile columns, most stages first
-  int32_t *order_cost;  // [B*MT + B*NT] their stage counts
+  int32_t *order_cost;  // [B*MT + B*NT] stage counts of the rows and columns
+  // dK/dV work items (column, part j, parts s, partial slot or -1), the
+  // longest first; a column longer than the cap is cut into s parts of its
+  // stage range (kSplitSlots bounds the extra parts, times Hkv)
+  int4 *k_items;        // [B*NT + kSplitSlots] sorted
+  int4 *k_raw;          // [B*NT + kSplitSlots] unsorted
+  int4 *k_split;        // [kSplitSlots] cut columns: (column, first slot, s, 0)
+  int32_t *k_counts;    // [4]: items, cut columns
+  float *kpart;         // [kSplitSlots][128][D] dK then dV partials of parts 1..s-1 (bwd)
   float *dsc;           // [B][Hq][Lp] rowsum(dout * o), scaled        (bwd)
   float *lse2;          // [B][Hq][Lp] log2-domain lse, +inf where no key (bwd)
 };

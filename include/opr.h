@@ -207,6 +207,8 @@ opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *worksp
  *  dout    bf16 [B][L][Hq][D].
  *  dq      fp32 [B][L][Hq][D];  dk, dv  fp32 [B][L][Hkv][D].  Every element
  *          is written (PAD rows get 0); nothing is accumulated into them.
+ *          The sums run in a fixed order: the same inputs give bit-identical
+ *          gradients on every call.
  *  workspace  >= opr_attn_workspace_size(B, L, Hq, Hkv, D, 1) bytes; the
  *             forward part of it is a prefix, so one backward-sized
  *             workspace serves both calls (see reuse_fwd_workspace).

@@ -260,6 +260,22 @@ def test_backward_reuse_is_identical(B):
         np.testing.assert_array_equal(a[n], r[n], err_msg=n)
 
 
+def test_cut_columns(B):
+    """One deep conversation over a single kv head: the history k-tiles, seen by
+    every later turn, have several times a workgroup's share of the stages, so
+    the backward runs each as several parts whose partial dK/dV are summed in a
+    fixed order.  Whole conversation against the oracle, and two backwards
+    bit-identical."""
+    conv = I.depth_conversation(3, h=128, t=640, r=192)
+    L = I.conv_len(conv)
+    t = I.make_tensors(1, L, 8, 1, 64, seed=4242)
+    a = run_gpu(B, [[conv]], L, t)
+    compare_full("cut columns", [[conv]], L, t, a)
+    r = run_gpu(B, [[conv]], L, t)
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_array_equal(a[n], r[n], err_msg=n)
+
+
 def _rotate(x, pos, theta):
     """Rotate-half RoPE of x [n, D] at positions pos [n] (fp64)."""
     D = x.shape[-1]
