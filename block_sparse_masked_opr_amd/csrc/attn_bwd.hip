@@ -373,7 +373,8 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
 
 void launch_attn_dq_kernel(const AttnParams &p, int D, float *dq, hipStream_t s);
 
-// ev (optional): events recorded before dK/dV, before dQ and after dQ.
+// ev (optional): events recorded before dK/dV, right after the dK/dV kernel
+// (so that its span is that kernel alone) and after dQ.
 hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq, float *dk,
                                    float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev) {
   AttnParams p;
@@ -383,14 +384,11 @@ hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq
   const unsigned gk = (unsigned)(((int64_t)in.B * p.NT + extra) * in.Hkv);
   const dim3 gr((unsigned)extra, (unsigned)in.Hkv);
   if (ev) (void)hipEventRecord(ev[0], s);
-  if (in.D == 64) {
-    attn_dkdv_kernel<64><<<gk, 512, 0, s>>>(p, dk, dv);
-    dkdv_split_reduce_kernel<64><<<gr, 256, 0, s>>>(p, dk, dv);
-  } else {
-    attn_dkdv_kernel<128><<<gk, 512, 0, s>>>(p, dk, dv);
-    dkdv_split_reduce_kernel<128><<<gr, 256, 0, s>>>(p, dk, dv);
-  }
+  if (in.D == 64) attn_dkdv_kernel<64><<<gk, 512, 0, s>>>(p, dk, dv);
+  else attn_dkdv_kernel<128><<<gk, 512, 0, s>>>(p, dk, dv);
   if (ev) (void)hipEventRecord(ev[1], s);
+  if (in.D == 64) dkdv_split_reduce_kernel<64><<<gr, 256, 0, s>>>(p, dk, dv);
+  else dkdv_split_reduce_kernel<128><<<gr, 256, 0, s>>>(p, dk, dv);
   launch_attn_dq_kernel(p, in.D, dq, s);
   if (ev) (void)hipEventRecord(ev[2], s);
   return hipGetLastError();

@@ -166,7 +166,8 @@ typedef struct {
    * the caller (hipEventCreate).  opr_attn_fwd records [0] before its
    * prologue, [1] before the attention kernel and [2] after it;
    * opr_attn_bwd records [0] before its prologue, [1] before the dK/dV
-   * kernel, [2] before the dQ kernel and [3] after it. */
+   * kernel, [2] after it and [3] after the dQ kernel ([2]..[3] also spans
+   * the small kernel that sums the parts of cut dK/dV columns). */
   hipEvent_t *timing_events;
   /* opr_attn_bwd only: nonzero when `workspace` is the one the matching
    * opr_attn_fwd call (same inputs, layout and stream, nothing written to the
