@@ -324,11 +324,10 @@ __global__ __launch_bounds__(256) void scale_delta_kernel(int32_t B, int32_t L, 
 // workgroup's share of the whole when one workgroup runs per CU on 256 CUs
 // (a smaller cap cut columns of balanced workloads for no gain in a
 // longest-first simulation of the schedule), and it keeps the extra items
-// below kSplitSlots / Hkv.  Part 0 of a cut
-// column writes dK/dV itself; parts 1..s-1 take partial slots, which
-// dkdv_split_reduce_kernel adds in order.  One workgroup: per-item costs,
-// then a counting sort (costs above kOrderBins - 1 share the last bin; ties
-// in any order).
+// below kSplitSlots / Hkv.  Part 0 of a cut column writes dK/dV itself;
+// parts 1..s-1 take partial slots, which dkdv_split_reduce_kernel adds in
+// order.  One workgroup: per-item costs, then a counting sort (costs above
+// kOrderBins - 1 share the last bin; ties in any order).
 constexpr int kOrderThreads = 1024, kOrderBins = 4096;
 constexpr int32_t kMinSplit = 16;
 
