@@ -446,6 +446,40 @@ def cpu_baseline(rows, L, shape, t_np):
                       f"fwd+bwd, {dt:.2f} s"}
 
 
+def depth_stages(Ns, steps=10):
+    """Per-stage times (HIP events recorded by the library) of the depth
+    workload, one pass against the N passes, one JSON line per (N, kind)."""
+    import torch
+    from block_sparse_masked_opr_amd import binding as Bd
+    dev = torch.device("cuda:0")
+    Hq, Hkv, D = I.DEPTH_HEADS["Hq"], I.DEPTH_HEADS["Hkv"], I.DEPTH_HEADS["D"]
+    names = ("fwd_prologue", "attn_fwd", "bwd_prologue", "attn_dkdv", "attn_dq")
+    for N in Ns:
+        conv = I.depth_conversation(N)
+        for kind, rows in (("one_pass", [[conv]]), ("n_pass", [I.npass_conversations(conv)])):
+            L = I.row_used(rows[0])
+            t = device_inputs(torch, 1, L, Hq, Hkv, D, I.SEEDS["depth"][1], dev)
+            r = Runner(torch, Bd, rows, L, Hq, Hkv, D, t, dev)
+            ev = HipEvents(torch)
+            evs = [(ev.array(3), ev.array(4)) for _ in range(steps)]
+            for _ in range(3):
+                r.step()
+            torch.cuda.synchronize()
+            for i in range(steps):
+                r.step(*evs[i])
+            torch.cuda.synchronize()
+            acc = dict.fromkeys(names, 0.0)
+            for f, b in evs:
+                for k, (e, a, z) in zip(names, ((f, 0, 1), (f, 1, 2), (b, 0, 1), (b, 1, 2), (b, 2, 3))):
+                    acc[k] += ev.ms(e[a], e[z])
+                ev.free(f)
+                ev.free(b)
+            print(json.dumps({"N": N, "kind": kind, "tokens": L, "pairs": useful_pairs(torch, r.lay),
+                              "stages_ms": {k: round(v / steps, 4) for k, v in acc.items()}}), flush=True)
+            del r, t
+            torch.cuda.empty_cache()
+
+
 def depth_sweep(torch, Bd, dev, Ns, steps):
     """One conversation of N turns: one pass (as packed, and without the last
     turn's context copy, which nothing sees) against the N passes."""
@@ -528,6 +562,8 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=3)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--depth-stages", metavar="N", type=int, nargs="+",
+                    help="only print per-stage times of the depth workload at these N (one pass and N passes)")
     ap.add_argument("--summarize-traffic", metavar="RUN_DIR",
                     help="write the HBM traffic summary of the dK/dV kernel from --pmc runs and exit")
     args = ap.parse_args()
@@ -542,6 +578,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.depth_stages:
+        depth_stages(args.depth_stages)
         return
 
     import torch
