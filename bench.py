@@ -470,7 +470,7 @@ def depth_stages(Ns, steps=10):
             torch.cuda.synchronize()
             acc = dict.fromkeys(names, 0.0)
             for f, b in evs:
-                for k, (e, a, z) in zip(names, ((f, 0, 1), (f, 1, 2), (b, 0, 1), (b, 1, 2), (b, 2, 3))):
+                for k, (e, a, z) in zip(names, ((f, 0, 1), (f, 1, 2), (b, 0, 1), (b, 2, 3), (b, 1, 2))):
                     acc[k] += ev.ms(e[a], e[z])
                 ev.free(f)
                 ev.free(b)
@@ -616,8 +616,8 @@ def main():
         stages["fwd_prologue"] += ev.ms(f[0], f[1])
         stages["attn_fwd"] += ev.ms(f[1], f[2])
         stages["bwd_prologue"] += ev.ms(b[0], b[1])
-        stages["attn_dkdv"] += ev.ms(b[1], b[2])
-        stages["attn_dq"] += ev.ms(b[2], b[3])
+        stages["attn_dq"] += ev.ms(b[1], b[2])
+        stages["attn_dkdv"] += ev.ms(b[2], b[3])
     stages = {k: v / args.steps for k, v in stages.items()}
     for f, b in evs:
         ev.free(f)

@@ -29,15 +29,22 @@
 //
 // Units: k' and v carry one exponent per (row, kv head), constant inside a
 // workgroup; q' and dout one per 16-slot tile and q head, so they change
-// inside a stage (eq, edo of the tile; eqr, edor their minima over the kv
-// group; the stage descriptor carries the four tiles' eq and edo).  The products are brought to group-wide units like this:
+// inside a stage (eq, edo of the tile; the stage descriptor carries the four
+// tiles' eq and edo).  Each key block w (the P-wave and the dS-wave of its 32
+// keys) accumulates in units fixed by eqr, edor: the smallest eq and edo of
+// the tiles of the stages that block runs, over this work item's stage range
+// (a pre-pass over the range, before the main loop).  So a key's units depend
+// only on the queries of its own stages, never on another conversation of the
+// row.  The dQ kernel stores per slot lse2 = lse log2 e - kPdvExp + edo and
+// delta' = delta 2^(edo + ev - kDsShift - kPdvExp) (delta in the units of
+// dP' 2^-(kDsShift + kPdvExp)).  With the tile's shift c = 2^-(eq - eqr):
 //   S: the score scale is 2^-(eq + ek) per tile;
-//   dV^T += dO'^T P'^T with P' = fp16(P * 2^(kPdvExp - (edo - edor))) (the
-//       stored lse2 carries the shift), so dV is in units 2^(kPdvExp + edor);
-//   dS' = P' (dP' dss - delta') with dP' = dO' V'^T in units 2^(edo + ev),
-//       dss = 2^-(kDsShift + kPdvExp + eq - eqr) per tile and delta' stored
-//       in the matching units, so dS' = dS 2^(eqr + edor + ev - kDsShift - eq)
-//       and dK^T += Q'^T dS'^T is in units 2^(eqr + edor + ev - kDsShift).
+//   dV^T += dO'^T P'^T with P' = fp16(P * 2^(kPdvExp - (edo - edor)))
+//       = exp2(S scale log2 e - lse2 + edor), so dV is in units 2^(kPdvExp + edor);
+//   dS' = P' (dP' 2^-(kDsShift + kPdvExp) - delta') c 2^bs with dP' = dO' V'^T
+//       in units 2^(edo + ev) and bs the dS-wave's shift of its keys' v' to
+//       the top of fp16's range, so dS' = dS 2^(eqr + edor + ev + bs - kDsShift - eq)
+//       and dK^T += Q'^T dS'^T is in units 2^(eqr + edor + ev + bs - kDsShift).
 #include "attn_common.h"
 #include "attn_sched.h"
 #include "opr_internal.h"
@@ -54,8 +61,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   constexpr int HALF_DB = NDB / 2;
   constexpr int TB = Tile<D>::BYTES, RB = Tile<D>::RB;
   constexpr int PSTRIDE = 4096;  // P of one key block: [qb][hh][lane] x 16 bytes
-  // per stage buffer: Q' tile, dO tile, lse2[64], scaled delta[64]
-  constexpr int BUF = 2 * TB + 512;
+  // per stage buffer: Q' tile, dO tile, lse2[64], scaled delta[64], score
+  // factors[64]
+  constexpr int BUF = 2 * TB + 768;
   // Separate LDS objects, so that the compiler sees that a copy or a store
   // into one leaves the others alone: a ring of three stage buffers (the
   // P-waves read stage i, the dS-waves stage i-1, stage i+1 streams in) and
@@ -67,9 +75,11 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   __shared__ __attribute__((aligned(1024))) char pbf0[4 * PSTRIDE];
   __shared__ __attribute__((aligned(1024))) char pbf1[4 * PSTRIDE];
   __shared__ __attribute__((aligned(1024))) char pbf2[4 * PSTRIDE];
-  __shared__ uint4 stages[kKStageCap];
+  __shared__ uint2 stages[kKStageCap];
   __shared__ int sh_count;
   __shared__ int64_t sh_next;
+  __shared__ int sh_emin[8];
+  __shared__ int4 sh_hull[4];
 
   const int64_t R = blockIdx.x;  // rank: longest items first, round-robin over the XCDs
   if (R / p.Hkv >= p.k_counts[0]) return;
@@ -85,18 +95,34 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   const int key = n * 128 + 32 * w + li;
   const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
   const int64_t hbase = (int64_t)b * p.Hq + (int64_t)kvh * p.group;  // first q head of the group
-  // q' and dout scales vary by stage (one per 64-slot tile, carried in the
-  // stage descriptor); eqr, edor are their minima over the group
-  const int eqr = p.eref[2 * kvplane], edor = p.eref[2 * kvplane + 1];
   const int ek = plane_exponent(p.mk[kvplane]);
   const int ev = plane_exponent(p.mv[kvplane]);
-
   // K' rows (P-waves) or V rows (dS-waves) of the lane's key, as B operands
   f16x8 frag[NS];
   {
     const uint16_t *src = (pwave ? p.kr : p.vr) + (kvplane * p.Lp + key) * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s) frag[s] = ld_f16x8(src + 16 * s + 8 * g);
+  }
+  // dS-waves: the shift bs that brings the largest |v'| of the block's 32
+  // keys to [2^14, 2^15).  v carries one scale per plane, so a block of small
+  // v (another conversation of the row holding the plane's largest values)
+  // would otherwise form its dP - delta bracket that much below fp16's normal
+  // range; dK is accumulated per key, so each block may use its own units.
+  int bs = 0;
+  if (!pwave) {
+    float mv = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mv = fmaxf(mv, fabsf((float)frag[s][e]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mv = fmaxf(mv, __shfl_xor(mv, off));
+    if (mv > 0.0f) {
+      int x;
+      frexpf(mv, &x);
+      bs = max(0, 15 - x);
+    }
   }
   // query slots that see this key: [iv.x, iv.y) and [iv.z, iv.w)
   const int4 iv = key < p.L ? p.kiv[(int64_t)b * p.L + key] : make_int4(0, 0, 0, 0);
@@ -115,29 +141,132 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   const int32_t *lst = p.k_list + tcol * p.MT;
   const uint32_t *subs_b = p.sub_class + (int64_t)b * p.MT * p.NT;
 
+  // this item's part of the column's stage range: flat stage index
+  // f = (tile * G + head) * 2 + half over k_list
+  const int64_t ftotal = (int64_t)nnz * p.group * 2;
+  const int64_t fbegin = ftotal * item.y / item.z;
+  const int64_t fend = ftotal * (item.y + 1) / item.z;
+
+  // Units of each key block: the smallest q' and dout row exponents over the
+  // queries of this item's stages that see the block's keys.  The query
+  // slots that see a key form at most two runs; over the 32 keys of a block
+  // inside one conversation the first runs join into one interval and the
+  // second runs into another (consecutive history keys are seen by the
+  // history from their slot on and by the t / r_out tail from some turn on;
+  // consecutive t / r_out keys by overlapping runs from their own slot), so
+  // the block's two hulls are exact there and a superset across a
+  // conversation boundary.  A 16-query tile inside a hull contributes its
+  // precomputed minimum, a tile cut by a hull's end its rows inside the
+  // hull.  A query outside both hulls meets only masked entries (P = 0): its
+  // shift against the block's units is clamped at 0, so its bracket stays
+  // finite and its products exactly 0.
+  int eqr, edor;
+  {
+    constexpr int kNone = 0x7FFFFFFF;
+    // hull of the lane's runs over the wave's 32 keys (both halves hold the same keys)
+    int h0 = iv.x < iv.y ? iv.x : kNone, h1 = iv.x < iv.y ? iv.y : -kNone;
+    int h2 = iv.z < iv.w ? iv.z : kNone, h3 = iv.z < iv.w ? iv.w : -kNone;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) {
+      h0 = min(h0, __shfl_xor(h0, off));
+      h1 = max(h1, __shfl_xor(h1, off));
+      h2 = min(h2, __shfl_xor(h2, off));
+      h3 = max(h3, __shfl_xor(h3, off));
+    }
+    if (pwave && lane == 0) sh_hull[w] = make_int4(h0, h1, h2, h3);
+    if (tid < 8) sh_emin[tid] = kExpMax;
+    __syncthreads();
+    int4 hull[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) hull[kb] = sh_hull[kb];
+    int mn[8];  // [key block][q', dout]
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mn[e] = kExpMax;
+    const int64_t gt = hbase * p.MTS, gr = hbase * p.Lp;  // the group's first head in the tile / row tables
+    for (int64_t ff = fbegin + tid; ff < fend; ff += 512) {
+      const int qh = (int)(ff & 1);
+      const int64_t tj = ff >> 1;
+      const int hj = (int)(tj % p.group);
+      const int q0 = lst[tj / p.group] * 128 + 64 * qh;
+      const int64_t tix = gt + (int64_t)hj * p.MTS + q0 / kTile;
+      const int4 e4 = *reinterpret_cast<const int4 *>(p.eqt + tix);
+      const int4 d4 = *reinterpret_cast<const int4 *>(p.edot + tix);
+      const int eqk[4] = {e4.x, e4.y, e4.z, e4.w}, edk[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int t0 = q0 + kTile * k, t1 = t0 + kTile;
+        uint32_t cut = 0u;  // blocks whose hull ends inside this tile
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int4 hl = hull[kb];
+          if ((hl.x <= t0 && t1 <= hl.y) || (hl.z <= t0 && t1 <= hl.w)) {
+            mn[2 * kb] = min(mn[2 * kb], eqk[k]);
+            mn[2 * kb + 1] = min(mn[2 * kb + 1], edk[k]);
+          } else if ((hl.x < t1 && t0 < hl.y) || (hl.z < t1 && t0 < hl.w)) {
+            cut |= 1u << kb;
+          }
+        }
+        if (cut) {
+          const int64_t rix = gr + (int64_t)hj * p.Lp + t0;
+          for (int r = 0; r < kTile; ++r) {
+            const int qs = t0 + r, eqv = p.eqq[rix + r], edv = p.edoq[rix + r];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              const int4 hl = hull[kb];
+              if (((cut >> kb) & 1u) && ((hl.x <= qs && qs < hl.y) || (hl.z <= qs && qs < hl.w))) {
+                mn[2 * kb] = min(mn[2 * kb], eqv);
+                mn[2 * kb + 1] = min(mn[2 * kb + 1], edv);
+              }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mn[e] = min(mn[e], __shfl_xor(mn[e], off));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) atomicMin(&sh_emin[e], mn[e]);
+    }
+    __syncthreads();
+    eqr = uniform(sh_emin[2 * w]);
+    edor = uniform(sh_emin[2 * w + 1]);
+  }
+  const float edor_f = (float)edor;
+  // a query's score factor fsq = scale log2(e) 2^-(eq + ek) times qsh is its
+  // shift 2^-(eq - eqr) against this block's units, times 2^bs (capped at
+  // qcap = 2^bs for a query the block is not seen by)
+  const float qsh = ldexpf(1.0f / p.scale_log2, eqr + ek + bs);
+  const float qcap = ldexpf(1.0f, bs);
+  const float kDss = ldexpf(1.0f, -kDsShift - kPdvExp);
+
   auto issue = [&](uint32_t x, char *nb) {
     const int q0 = (int)(x & 0xFFFFFFu), hj = (int)(x >> 24);
     const int64_t plane = hbase + hj;
     tc.issue(make_rsrc(p.qr + plane * p.Lp * D, plane_bytes), q0, nb, wave);
     tc.issue(make_rsrc(p.dor + plane * p.Lp * D, plane_bytes), q0, nb + TB, wave);
-    // lse2 (wave 0) and delta (wave 1) of the stage's 64 query slots
-    if (wave < 2)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc((wave == 0 ? p.lse2 : p.dsc) + plane * p.Lp, (uint32_t)p.Lp * 4),
-                                               (OPR_LDS void *)(nb + 2 * TB + 256 * wave), 4, 4 * lane, 4 * q0, 0, 0);
+    // lse2 (wave 0), delta (wave 1) and the score factors (wave 2) of the
+    // stage's 64 query slots
+    if (wave < 3)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          make_rsrc((wave == 0 ? p.lse2 : wave == 1 ? p.dsc : p.fsq) + plane * p.Lp, (uint32_t)p.Lp * 4),
+          (OPR_LDS void *)(nb + 2 * TB + 256 * wave), 4, 4 * lane, 4 * q0, 0, 0);
   };
 
   // P-wave element work of a stage: S^T = K' Q'^T (keys x queries) per
   // 32-query sub-block, P = exp2(S * scale * log2 e - lse2) masked by the
-  // key's runs (unless both sub-blocks are full), as fp16(P * 2^kPdvExp) (lse2 carries the -kPdvExp) into op and
-  // into LDS for the dS-wave.  The update that follows is dV^T += dO^T P^T.
-  auto p_elem = [&](uint4 desc, const char *buf, char *pout, f16x8 (&op)[2][2]) {
+  // key's runs (unless both sub-blocks are full), as
+  // fp16(P * 2^(kPdvExp - (edo - edor))) (lse2 carries -kPdvExp + edo) into op
+  // and into LDS for the dS-wave.  The update that follows is dV^T += dO^T P^T.
+  auto p_elem = [&](uint2 desc, const char *buf, char *pout, f16x8 (&op)[2][2]) {
     const int q0 = (int)(desc.x & 0xFFFFFFu);
-    // raw score -> log2 units, per 16-query tile 2 qb + hh (its q' exponent)
-    float fs[2][2];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) fs[k >> 1][k & 1] = ldexpf(p.scale_log2, -(stage_exponent(desc.z, k) + ek));
     const char *Qt = buf;
     const float *lse2s = reinterpret_cast<const float *>(buf + 2 * TB);
+    // raw score -> log2 units, per query (its q' row exponent)
+    const float *fss = reinterpret_cast<const float *>(buf + 2 * TB + 512);
     char *Pw = pout + w * PSTRIDE;
     // both products first, then both element blocks
     f32x16 s[2];
@@ -165,10 +294,13 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
         const int qbase = 32 * qb + 16 * hh + 8 * g;  // query rows of registers 8hh .. 8hh+7
         const float4 l0 = *reinterpret_cast<const float4 *>(lse2s + qbase);
         const float4 l1 = *reinterpret_cast<const float4 *>(lse2s + qbase + 4);
+        const float4 f0 = *reinterpret_cast<const float4 *>(fss + qbase);
+        const float4 f1 = *reinterpret_cast<const float4 *>(fss + qbase + 4);
         const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const float fv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          op[qb][hh][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * hh + e], fs[qb][hh], -lv[e]));
+          op[qb][hh][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * hh + e], fv[e], edor_f - lv[e]));
         }
         *reinterpret_cast<f16x8 *>(Pw + (2 * qb + hh) * 1024 + lane * 16) = op[qb][hh];
       }
@@ -179,13 +311,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   // dS = P * (dP - delta) into op, with P read back from the P-wave of the same
   // key block (masked entries have P = 0 and so dS = 0).  The update that
   // follows is dK^T += Q'^T dS^T.
-  auto ds_elem = [&](uint4 desc, const char *buf, const char *pin, f16x8 (&op)[2][2]) {
-    // dP' -> dS' units, per 16-query tile 2 qb + hh (its q' exponent)
-    float dss[2][2];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) dss[k >> 1][k & 1] = ldexpf(1.0f, -kDsShift - kPdvExp - (stage_exponent(desc.z, k) - eqr));
+  auto ds_elem = [&](uint2 desc, const char *buf, const char *pin, f16x8 (&op)[2][2]) {
     const char *dOt = buf + TB;
     const float *dscs = reinterpret_cast<const float *>(buf + 2 * TB + 256);
+    const float *fss = reinterpret_cast<const float *>(buf + 2 * TB + 512);
     const char *Pw = pin + w * PSTRIDE;
     f32x16 dp[2];
 #pragma unroll
@@ -205,13 +334,20 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
         const f16x8 pv = *reinterpret_cast<const f16x8 *>(Pw + (2 * qb + hh) * 1024 + lane * 16);
         const float4 d0 = *reinterpret_cast<const float4 *>(dscs + qbase);
         const float4 d1 = *reinterpret_cast<const float4 *>(dscs + qbase + 4);
+        const float4 f0 = *reinterpret_cast<const float4 *>(fss + qbase);
+        const float4 f1 = *reinterpret_cast<const float4 *>(fss + qbase + 4);
         const float dvv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        // the query's shift 2^(bs - (eq - eqr)) from its score factor (clamped
+        // at 2^bs for a query the block is not seen by)
+        const float sh[8] = {fminf(qcap, f0.x * qsh), fminf(qcap, f0.y * qsh), fminf(qcap, f0.z * qsh),
+                             fminf(qcap, f0.w * qsh), fminf(qcap, f1.x * qsh), fminf(qcap, f1.y * qsh),
+                             fminf(qcap, f1.z * qsh), fminf(qcap, f1.w * qsh)};
         // P * 2^kPdvExp times (dP * 2^-kDsShift - delta) * 2^-kPdvExp: the
         // second factor in fp32, then both multiplied as packed fp16 pairs
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const f16x2 t = {(_Float16)fmaf(dp[qb][8 * hh + e], dss[qb][hh], -dvv[e]),
-                           (_Float16)fmaf(dp[qb][8 * hh + e + 1], dss[qb][hh], -dvv[e + 1])};
+          const f16x2 t = {(_Float16)(fmaf(dp[qb][8 * hh + e], kDss, -dvv[e]) * sh[e]),
+                           (_Float16)(fmaf(dp[qb][8 * hh + e + 1], kDss, -dvv[e + 1]) * sh[e + 1])};
           const f16x2 pp = {pv[e], pv[e + 1]};
           const f16x2 d = t * pp;
           op[qb][hh][e] = d[0];
@@ -229,7 +365,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   // branch).
   auto wave_step = [&](int i, int ns, const char *ba, const char *bb, char *pa, const char *pr) {
     if (pwave ? i >= ns : i < 1) return;
-    const uint4 desc = uniform(stages[pwave ? i : i - 1]);
+    const uint2 desc = uniform(stages[pwave ? i : i - 1]);
     if (((desc.y >> (4 * w)) & 15u) == 0) return;
     f16x8 op[2][2];
     const char *T;
@@ -254,16 +390,12 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // this item's part of the column's stage range
-  const int64_t ftotal = (int64_t)nnz * p.group * 2;
-  int64_t fnext = ftotal * item.y / item.z;
-  const int64_t fend = ftotal * (item.y + 1) / item.z;
+  int64_t fnext = fbegin;
   while (fnext < fend) {
     __syncthreads();
     if (wave == 0) {
       int64_t f = fnext;
-      const int c = build_k_stages(lst, subs_b, p.NT, n, p.group, fend, p.eqt + hbase * p.MTS,
-                                   p.edot + hbase * p.MTS, p.MTS, &f, stages, lane);
+      const int c = build_k_stages(lst, subs_b, p.NT, n, p.group, fend, &f, stages, lane);
       if (lane == 0) {
         sh_count = c;
         sh_next = f;
@@ -300,9 +432,11 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
       dv = p.kpart + (int64_t)kSplitSlots * OPR_ATTN_BLOCK * D;
     }
     if (!pwave) {
-      // dK^T in units 2^(eqr + edor + ev - kDsShift), rotated back by RoPE
+      // dK^T in units 2^(eqr + edor + ev + bs - kDsShift), rotated back by
+      // RoPE; the unit exponent is applied to the value (as a factor it can
+      // leave fp32's range)
       const float2 *cs = p.rope + ((int64_t)b * p.Lp + key) * (D / 2);
-      const float kscale = ldexpf(p.scale, kDsShift - eqr - edor - ev);
+      const int uexp = kDsShift - eqr - edor - ev - bs;
 #pragma unroll
       for (int db = 0; db < HALF_DB; ++db) {
 #pragma unroll
@@ -312,7 +446,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
           for (int c = 0; c < 4; ++c) {
             const int r = 4 * a4 + c;
             const float2 rc = cs[acc_dim(db, r, g)];
-            const float g1 = kscale * acc[db][r], g2 = kscale * acc[db + HALF_DB][r];
+            const float g1 = ldexpf(p.scale * acc[db][r], uexp), g2 = ldexpf(p.scale * acc[db + HALF_DB][r], uexp);
             lo[c] = g1 * rc.x + g2 * rc.y;
             hi[c] = g2 * rc.x - g1 * rc.y;
           }
@@ -323,14 +457,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
       }
     } else {
       // dV^T in units 2^(kPdvExp + edor)
-      const float vscale = ldexpf(1.0f, -kPdvExp - edor);
+      const int uexp = -kPdvExp - edor;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4)
           *reinterpret_cast<float4 *>(dv + out + acc_dim(db, 4 * a4, g)) =
-              make_float4(vscale * acc[db][4 * a4], vscale * acc[db][4 * a4 + 1],
-                          vscale * acc[db][4 * a4 + 2], vscale * acc[db][4 * a4 + 3]);
+              make_float4(ldexpf(acc[db][4 * a4], uexp), ldexpf(acc[db][4 * a4 + 1], uexp),
+                          ldexpf(acc[db][4 * a4 + 2], uexp), ldexpf(acc[db][4 * a4 + 3], uexp));
       }
     }
   }
@@ -373,24 +507,31 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
 
 void launch_attn_dq_kernel(const AttnParams &p, int D, float *dq, hipStream_t s);
 
-// ev (optional): events recorded before dK/dV, right after the dK/dV kernel
-// (so that its span is that kernel alone) and after dQ.
-hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq, float *dk,
-                                   float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev) {
+// The backward: the dQ kernel first (it also writes the dout plane, its tile
+// exponents and the per-slot units that dK/dV reads), then dK/dV and the
+// reduce of the cut columns.  ev (optional): events recorded before dQ, after
+// it (before dK/dV) and right after the dK/dV kernel (so that its span is
+// that kernel alone).
+hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, const void *o, const float *lse,
+                                   const void *dout, float *dq, float *dk, float *dv, const AttnWs &ws,
+                                   hipStream_t s, hipEvent_t *ev) {
   AttnParams p;
   fill_params(in, scale, ws, &p);
+  p.o_in = static_cast<const uint16_t *>(o);
+  p.dout_in = static_cast<const uint16_t *>(dout);
+  p.lse_in = lse;
   // every column once, plus the most extra parts the work order can make
   const int32_t extra = kSplitSlots / in.Hkv + 1;
   const unsigned gk = (unsigned)(((int64_t)in.B * p.NT + extra) * in.Hkv);
   const dim3 gr((unsigned)extra, (unsigned)in.Hkv);
   if (ev) (void)hipEventRecord(ev[0], s);
+  launch_attn_dq_kernel(p, in.D, dq, s);
+  if (ev) (void)hipEventRecord(ev[1], s);
   if (in.D == 64) attn_dkdv_kernel<64><<<gk, 512, 0, s>>>(p, dk, dv);
   else attn_dkdv_kernel<128><<<gk, 512, 0, s>>>(p, dk, dv);
-  if (ev) (void)hipEventRecord(ev[1], s);
+  if (ev) (void)hipEventRecord(ev[2], s);
   if (in.D == 64) dkdv_split_reduce_kernel<64><<<gr, 256, 0, s>>>(p, dk, dv);
   else dkdv_split_reduce_kernel<128><<<gr, 256, 0, s>>>(p, dk, dv);
-  launch_attn_dq_kernel(p, in.D, dq, s);
-  if (ev) (void)hipEventRecord(ev[2], s);
   return hipGetLastError();
 }
 

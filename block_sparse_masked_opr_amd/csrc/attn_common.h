@@ -7,9 +7,9 @@
 // bf16's range, each staged operand (q and k after RoPE, v, dout) is stored
 // as fp16(x * 2^e) with a power-of-two exponent e chosen from the largest
 // magnitude it covers, so that this lands in [2^14, 2^15): for k and v one
-// per (row, kv head) plane (an absmax pre-pass), for q and dout one per
-// kTile-slot tile of each (row, q head) (found by the one wave that converts
-// the tile).
+// per (row, kv head) plane (an absmax pre-pass), for q and dout one per row
+// of each q head, i.e. per query (found by the threads that convert the
+// row), so that no two tokens - and no two conversations - share a scale.
 // The kernels fold the exponents back exactly: into the score scale (q, k)
 // and into the fixed units of their fp32 accumulators (v, dout), removed in
 // the epilogues.
@@ -43,9 +43,15 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const f16x8 &a, const f16x8 &b, c
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Exponent range of the plane scales; keeps every folded product of up to
-// three exponents inside fp32's normal range.
-constexpr int kExpMin = -32, kExpMax = 32;
+// Exponent range of the operand scales.  A factor folded from two exponents
+// (the score scale 2^-(eq + ek)) stays inside fp32's normal range; sums of
+// three (the epilogues' unit removal) are applied with ldexp to the
+// accumulated value, never formed as a factor on their own.  A tile or plane
+// whose largest magnitude lies in [2^(14 - kExpMax), 2^(15 - kExpMin)) keeps
+// the full 11-bit fp16 significand: [2^-46, 2^75) here; below it the values
+// keep an absolute precision of 2^-(kExpMax + 24), above it (and for the
+// |x| >= 2^(16 - kExpMin) that overflow fp16) the results are not finite.
+constexpr int kExpMin = -60, kExpMax = 60;
 // dS is stored shifted down by 2^kDsShift on top of the units of dP
 // (|v|, |dout| < 2^15 after scaling, so |dP| < 2^37 and |dS| < 2^15).
 constexpr int kDsShift = 22;
@@ -58,9 +64,8 @@ constexpr int kPdvExp = 15;
 // fp16(p * 2^kPExp) with p <= 2^kMaxSlack, i.e. at most 2^15.
 constexpr float kMaxSlack = 8.0f;
 constexpr int kPExp = 7;
-// Slots per exponent tile of q' and dout: half of a forward or dQ wave's 32
-// queries (lane i uses tile i / 16), a quarter of a dK/dV stage (accumulator
-// registers 8h .. 8h + 7 of 32-query block b hold tile 2b + h).
+// Slots per tile of the exponent minima of q' and dout (the dK/dV kernel's
+// unit search reads these before looking at single rows).
 constexpr int kTile = 16;
 
 // A-operand row order of a 32-row block: swap bits 2 and 3.
@@ -372,16 +377,24 @@ struct AttnParams {
   const int4 *qiv;             // [B][L] key slots a query slot sees: [x, y) and [z, w)
   const int4 *kiv;             // [B][L] query slots that see a key slot: [x, y) and [z, w)
   const float2 *rope;          // [B][Lp][D/2] (cos, sin)
-  // fp16 bits, one power-of-two scale per (row, head) plane: [B][H][Lp][D]
-  const uint16_t *qr, *kr, *vr, *dor;
+  // fp16 bits [B][H][Lp][D]: k' and v with one power-of-two scale per
+  // (row, kv head) plane, q' and dout with one per 16-slot tile of each
+  // (row, q head).  The dQ kernel writes dor; the dK/dV kernel reads it.
+  const uint16_t *qr, *kr, *vr;
+  uint16_t *dor;
   // plane maxima (float bits) [B][Hkv] of k', v
   const uint32_t *mk, *mv;
-  // tile exponents [B][Hq][MTS] of q' and dout; their minima over the kv
-  // group, eref [B][Hkv][2] = (q, dout)
-  const int32_t *eqt, *edot, *eref;
+  // row exponents [B][Hq][Lp] of q' and of dout (edoq, written by dQ), and
+  // their minima over each kTile-slot tile [B][Hq][MTS]
+  const int32_t *eqq, *eqt;
+  int32_t *edoq, *edot;
   int32_t MTS;                 // tiles per row: Lp / kTile
-  const float *dsc, *lse2;     // [B][Hq][Lp], see the backward units in attn_bwd.hip
-                               // (lse2 is +inf where no key)
+  // [B][Hq][Lp], written by the dQ kernel for dK/dV (units in attn_bwd.hip;
+  // lse2 is +inf where no key)
+  float *dsc, *lse2, *fsq;
+  // backward inputs in token order: o, dout bf16 [B][L][Hq][D], lse [B][Hq][L]
+  const uint16_t *o_in, *dout_in;
+  const float *lse_in;
 };
 
 }  // namespace opr

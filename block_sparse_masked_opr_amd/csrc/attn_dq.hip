@@ -1,19 +1,30 @@
-// dQ kernel of the one-pass masked attention backward (gfx950).
+// dQ kernel of the one-pass masked attention backward (gfx950).  It runs
+// first in the backward and also prepares what the dK/dV kernel reads.
 //
-// One workgroup per (128-query tile, q head, row), pipelined like the forward
-// kernel: a stage list of the non-empty 64-key halves in LDS, K' and V tiles
-// double buffered in LDS (buffer loads to LDS), one barrier per stage.  Per
-// non-empty 32x32 sub-block each wave recomputes S^T = K' Q'^T and
-// dP^T = V dO^T, masks partial sub-blocks with the query's key intervals,
-// forms dS = P * (dP - delta) (P from the forward LSE) and accumulates
-// dQ^T += K'^T dS^T, reading K'^T from the row-major K' tile with transposing
-// LDS reads.  The epilogue removes the operand units, applies the softmax
-// scale and rotates dQ back by the transposed RoPE rotation.
+// One workgroup per (128-query tile, q head, row).  Each lane owns one query
+// slot (and half of its head dims with its partner lane l ^ 32).  Prologue:
+// the lane reads dout and o of its slot's token (bf16, token order), forms
+// Delta = rowsum(dout * o) (fp32 over exact bf16 products), finds the
+// largest |dout| of the row (its half and the partner lane's), converts dout
+// to fp16 with that row's exponent into registers, and writes, for the dK/dV
+// kernel, the fp16 dout plane, the row exponent (and its minimum over each
+// 16-slot tile), and Delta, lse and the score factor in that kernel's
+// per-slot units.
+// Main loop, pipelined like the forward kernel: a stage list of the non-empty
+// 64-key halves in LDS, K' and V tiles double buffered in LDS (buffer loads
+// to LDS), one barrier per stage.  Per non-empty 32x32 sub-block each wave
+// recomputes S^T = K' Q'^T and dP^T = V dO^T, masks partial sub-blocks with
+// the query's key intervals, forms dS = P * (dP - Delta) (P from the forward
+// LSE) and accumulates dQ^T += K'^T dS^T, reading K'^T from the row-major K'
+// tile with transposing LDS reads.  The epilogue removes the operand units,
+// applies the softmax scale and rotates dQ back by the transposed RoPE
+// rotation.
 //
-// Units: q' and dout carry one exponent per 16-slot tile and q head (one per
-// lane's query), k' and v one per (row, kv head).  dP comes out in units
-// 2^(e_dout + e_v); delta is brought into those units times 2^-kDsShift, and
-// dS is formed as P * (dP * 2^-kDsShift - delta) before the fp16 conversion.
+// Units: q' and dout carry one exponent per row and q head (the lane's
+// query: eq, edo), k' and v one per (row, kv head) plane (ek, ev).
+// dP comes out in units 2^(edo + ev); Delta is brought into those units times
+// 2^-kDsShift, and dS is formed as P * (dP * 2^-kDsShift - Delta) before the
+// fp16 conversion.
 #include "attn_common.h"
 #include "attn_sched.h"
 #include "opr_internal.h"
@@ -44,25 +55,77 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int q = m * 128 + 32 * w + li;
   const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
-  // q' and dout scales of the lane's tile (query slot q), and their kv-group minima
-  const int64_t tix = ((int64_t)b * p.Hq + h) * p.MTS + q / kTile;
-  const int eq = p.eqt[tix], edo = p.edot[tix];
-  const int eqr = p.eref[2 * kvplane], edor = p.eref[2 * kvplane + 1];
+  const int64_t hq_row = ((int64_t)b * p.Hq + h) * p.Lp + q;
+  const int eq = p.eqq[hq_row];
   const int ek = plane_exponent(p.mk[kvplane]);
   const int ev = plane_exponent(p.mv[kvplane]);
   const float fs = ldexpf(p.scale_log2, -(eq + ek));
   const float dss = ldexpf(1.0f, -kDsShift);
-  const int64_t hq_row = ((int64_t)b * p.Hq + h) * p.Lp + q;
 
   f16x8 qb[NS], dob[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    qb[s] = ld_f16x8(p.qr + hq_row * D + 16 * s + 8 * g);
-    dob[s] = ld_f16x8(p.dor + hq_row * D + 16 * s + 8 * g);
+  for (int s = 0; s < NS; ++s) qb[s] = ld_f16x8(p.qr + hq_row * D + 16 * s + 8 * g);
+
+  // ---- prologue: Delta, the fp16 dout with its tile exponent, the dK/dV units
+  float lse2_q, dsc_q;
+  int edo_of_lane;
+  {
+    const int32_t tok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
+    uint4 dw[NS], ow[NS];  // bf16 dims 16 s + 8 g .. + 7 of dout and o
+#pragma unroll
+    for (int s = 0; s < NS; ++s) dw[s] = ow[s] = make_uint4(0u, 0u, 0u, 0u);
+    float lse = -INFINITY;
+    if (tok >= 0) {
+      const int64_t base = (((int64_t)b * p.L + tok) * p.Hq + h) * D + 8 * g;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        dw[s] = *reinterpret_cast<const uint4 *>(p.dout_in + base + 16 * s);
+        ow[s] = *reinterpret_cast<const uint4 *>(p.o_in + base + 16 * s);
+      }
+      lse = p.lse_in[((int64_t)b * p.Hq + h) * p.L + tok];
+    }
+    float delta = 0.0f;
+    uint32_t mx = 0u;  // float bits of the largest |dout| (integer order)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      delta = dot2_bf16(ow[s].x, dw[s].x, delta);
+      delta = dot2_bf16(ow[s].y, dw[s].y, delta);
+      delta = dot2_bf16(ow[s].z, dw[s].z, delta);
+      delta = dot2_bf16(ow[s].w, dw[s].w, delta);
+      mx = max(mx, absmax8_bf16_bits(dw[s]));
+    }
+    delta += __shfl_xor(delta, 32);
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));  // the row's other half
+    const int edo = mx > 0u ? plane_exponent(mx) : kExpMax;
+    edo_of_lane = edo;
+    uint16_t *drow = p.dor + hq_row * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint16_t *e16 = reinterpret_cast<const uint16_t *>(&dw[s]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dob[s][e] = (_Float16)ldexpf(bf16_to_f32(e16[e]), edo);
+      *reinterpret_cast<f16x8 *>(drow + 16 * s) = dob[s];
+    }
+    // the row exponent and its minimum over the kTile rows of the tile
+    // (lanes 16 t .. 16 t + 15 of a half)
+    int emin = edo;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) emin = min(emin, __shfl_xor(emin, off));
+    if (g == 0) p.edoq[hq_row] = edo;
+    if ((lane & 47) == 0) p.edot[((int64_t)b * p.Hq + h) * p.MTS + q / kTile] = emin;
+    // this kernel's units: P = exp2(S * scale * log2 e - lse2_q) (+inf: no
+    // key, P = 0), Delta in the units of dP times 2^-kDsShift
+    const bool live = lse != -INFINITY;
+    lse2_q = live ? lse * kLog2e : INFINITY;
+    dsc_q = ldexpf(delta, edo + ev - kDsShift);
+    // the dK/dV kernel's units (see attn_bwd.hip): the same quantities with
+    // the slot's dout tile exponent folded in and the 2^kPdvExp of its P
+    if (g == 0) {
+      p.lse2[hq_row] = live ? lse * kLog2e - (float)kPdvExp + (float)edo : INFINITY;
+      p.dsc[hq_row] = ldexpf(delta, edo + ev - kDsShift - kPdvExp);
+      p.fsq[hq_row] = fs;
+    }
   }
-  // the stored lse2 and delta are in the dK/dV kernel's units: undo them
-  const float lse2_q = p.lse2[hq_row] + (float)(kPdvExp - (edo - edor));
-  const float dsc_q = ldexpf(p.dsc[hq_row], kPdvExp + (eq - eqr));
   // key slots this query sees: [iv.x, iv.y) and [iv.z, iv.w)
   const int4 iv = q < p.L ? p.qiv[(int64_t)b * p.L + q] : make_int4(0, 0, 0, 0);
   OperandOffsets<D> of;
@@ -168,8 +231,9 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
     const int tok = p.slot_tok[(int64_t)b * p.L + q];
     float *out = dq + (((int64_t)b * p.L + tok) * p.Hq + h) * D;
     const float2 *cs = p.rope + ((int64_t)b * p.Lp + q) * (D / 2);
-    // dQ^T in units 2^(ek + ev + edo - kDsShift)
-    const float qscale = ldexpf(p.scale, kDsShift - ek - ev - edo);
+    // dQ^T in units 2^(ek + ev + edo - kDsShift); the unit exponent is
+    // applied to the value (it can exceed fp32's range as a factor)
+    const int uexp = kDsShift - ek - ev - edo_of_lane;
 #pragma unroll
     for (int db = 0; db < HALF_DB; ++db) {
 #pragma unroll
@@ -179,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * a + c;
           const float2 rc = cs[acc_dim(db, r, g)];
-          const float g1 = qscale * dqacc[db][r], g2 = qscale * dqacc[db + HALF_DB][r];
+          const float g1 = ldexpf(p.scale * dqacc[db][r], uexp), g2 = ldexpf(p.scale * dqacc[db + HALF_DB][r], uexp);
           lo[c] = g1 * rc.x + g2 * rc.y;
           hi[c] = g2 * rc.x - g1 * rc.y;
         }

@@ -51,8 +51,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
   const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int q = m * 128 + 32 * w + li;
   const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
-  // q' scale of the lane's tile (query slot q)
-  const int eq = p.eqt[((int64_t)b * p.Hq + h) * p.MTS + q / kTile];
+  // q' scale of the lane's row (query slot q)
+  const int eq = p.eqq[((int64_t)b * p.Hq + h) * p.Lp + q];
   const int ek = plane_exponent(p.mk[kvplane]);
   const int ev = plane_exponent(p.mv[kvplane]);
   const float fs = ldexpf(p.scale_log2, -(eq + ek));  // raw score -> log2 units

@@ -4,11 +4,12 @@
 //  - the RoPE table at the slots' strategic position ids (and the reset of
 //    the plane maxima),
 //  - the largest magnitude of every (row, kv head) plane of k and v,
-//  - head-major fp16 copies of q, k (after RoPE), v and dout in slot order:
-//    k and v with one power-of-two scale per plane, q and dout with one per
-//    64-slot tile of each (row, head), found while the tile is converted,
-//  - the backward preprocessing delta = rowsum(dout * o), fused with the dout
-//    copy, and its scaling into the units of the backward kernels.
+//  - head-major fp16 copies of q, k (after RoPE) and v in slot order: k and v
+//    with one power-of-two scale per plane, q with one per row (token and
+//    head), found while the row is converted,
+//  - the longest-first work order of the attention kernels.
+// (The backward's dout copy and delta = rowsum(dout * o) are formed by the
+// dQ kernel, attn_dq.hip.)
 //
 // RoPE (rotate-half): pair (j, j + D/2) of a head vector is rotated by
 // pos * theta^(-2j/D).  The angle and its cosine and sine are computed in
@@ -105,19 +106,20 @@ __global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, Ab
 // cosines and sines in registers and walk the heads.
 // x: [B][L][H][D] bf16 -> rows [B][H][Lp][D] in slot order, fp16(x' * 2^e),
 // x' = RoPE(x) or x.
-// TILE = false: e is the exponent of the head's plane maximum pmax[b][h].
-// TILE = true: e is the exponent of the largest |x'| of the wave's tile of the
-// head (kExpMax for an all-zero tile), reduced inside the wave; it is stored
-// in etile[b][h][tile] (group_min_kernel takes the minimum over each group).
+// ROWS = false: e is the exponent of the head's plane maximum pmax[b][h].
+// ROWS = true: e is the exponent of the row's own largest |x'| (kExpMax for
+// an all-zero row), reduced over the slot's 4 threads and stored in
+// erow[b][h][s]; the smallest over the wave's kTile rows goes to
+// etile[b][h][tile].
 // Slots s >= L are zero.
 constexpr int kPackHeads = 8;
 constexpr int kPackSlots = 64;
 
-template <int D, bool ROPE, bool TILE>
+template <int D, bool ROPE, bool ROWS>
 __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H, int32_t group,
                                                    const uint16_t *x, const int32_t *slot_tok,
                                                    const float2 *table, const uint32_t *pmax,
-                                                   uint16_t *rows, int32_t *etile) {
+                                                   uint16_t *rows, int32_t *erow, int32_t *etile) {
   constexpr int HALF = D / 2;
   constexpr int PER = HALF / 4;  // pairs per thread (4 threads per slot)
   static_assert(kPackSlots == 4 * kTile, "a wave covers one tile");
@@ -162,14 +164,18 @@ __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_
       }
     }
     int ex;
-    if (TILE) {
+    if (ROWS) {
       uint32_t m = 0u;  // float bits of the largest magnitude (integer order)
 #pragma unroll
       for (int e = 0; e < PER; ++e) m = max(m, max(__float_as_uint(fabsf(lo[e])), __float_as_uint(fabsf(hi[e]))));
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1));  // the slot's 4 threads
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2));
       ex = m > 0u ? plane_exponent(m) : kExpMax;
-      if (lane == 0) etile[((int64_t)b * H + h) * (Lp / kTile) + t0 / kTile + wave] = ex;
+      if (part == 0) erow[((int64_t)b * H + h) * Lp + t] = ex;
+      int mn = ex;
+#pragma unroll
+      for (int off = 4; off < 64; off <<= 1) mn = min(mn, __shfl_xor(mn, off));
+      if (lane == 0) etile[((int64_t)b * H + h) * (Lp / kTile) + t0 / kTile + wave] = mn;
     } else {
       ex = plane_exponent(pmax[(int64_t)b * H + h]);
     }
@@ -186,131 +192,6 @@ __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_
       *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
     }
   }
-}
-
-// Backward preprocessing, one workgroup per (64-slot block, group of
-// kPackHeads q heads, row) with the thread layout of pack_kernel (a wave per
-// tile): per head and slot s, with t = slot_tok[s] the token there,
-//   dsc[b][h][s] = sum_d dout * o of token t (float32 over bf16 inputs; the
-//                  units are applied by scale_delta_kernel),
-// and dout goes to its fp16 copy with the exponent of the tile's largest
-// |dout| (kExpMax for an all-zero tile), stored in etile[b][h][tile].
-template <int D>
-__global__ __launch_bounds__(256) void delta_pack_kernel(int32_t L, int32_t Lp, int32_t H, int32_t group,
-                                                         const uint16_t *o, const uint16_t *dout,
-                                                         const int32_t *slot_tok, uint16_t *rows, float *dsc,
-                                                         int32_t *etile) {
-  constexpr int HALF = D / 2;
-  constexpr int PER = HALF / 4;
-  const int hgroups = (H + kPackHeads - 1) / kPackHeads;
-  const int h0 = (int)(blockIdx.x % (unsigned)hgroups) * kPackHeads;
-  const int blk = (int)(blockIdx.x / (unsigned)hgroups);
-  const int t0 = blk * kPackSlots, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tt = tid >> 2, part = tid & 3;
-  const int t = t0 + tt;
-  const int j0 = part * PER;
-  const int32_t tok = t < L ? slot_tok[(int64_t)b * L + t] : -1;
-  const int h1 = min(H, h0 + kPackHeads);
-#pragma unroll 2
-  for (int h = h0; h < h1; ++h) {
-    uint4 dw[PER / 4], ow[PER / 4];  // bf16 words, low halves then high halves
-#pragma unroll
-    for (int c = 0; c < PER / 4; ++c) dw[c] = ow[c] = make_uint4(0, 0, 0, 0);
-    if (tok >= 0) {
-      const int64_t base = (((int64_t)b * L + tok) * H + h) * D;
-#pragma unroll
-      for (int c = 0; c < PER / 8; ++c) {
-        dw[c] = *reinterpret_cast<const uint4 *>(dout + base + j0 + 8 * c);
-        dw[PER / 8 + c] = *reinterpret_cast<const uint4 *>(dout + base + HALF + j0 + 8 * c);
-        ow[c] = *reinterpret_cast<const uint4 *>(o + base + j0 + 8 * c);
-        ow[PER / 8 + c] = *reinterpret_cast<const uint4 *>(o + base + HALF + j0 + 8 * c);
-      }
-    }
-    float acc = 0.0f;
-    uint32_t m = 0u;
-#pragma unroll
-    for (int c = 0; c < PER / 4; ++c) {
-      acc = dot2_bf16(ow[c].x, dw[c].x, acc);
-      acc = dot2_bf16(ow[c].y, dw[c].y, acc);
-      acc = dot2_bf16(ow[c].z, dw[c].z, acc);
-      acc = dot2_bf16(ow[c].w, dw[c].w, acc);
-      m = max(m, absmax8_bf16_bits(dw[c]));
-    }
-    acc += __shfl_xor(acc, 1);  // the 4 threads of a slot
-    acc += __shfl_xor(acc, 2);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    const int ex = m > 0u ? plane_exponent(m) : kExpMax;
-    if (lane == 0) etile[((int64_t)b * H + h) * (Lp / kTile) + t0 / kTile + wave] = ex;
-    if (part == 0) dsc[((int64_t)b * H + h) * Lp + t] = acc;
-    const uint16_t *dl = reinterpret_cast<const uint16_t *>(dw);
-    uint16_t lq[PER], hq[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      lq[e] = f32_to_f16_bits(ldexpf(bf16_to_f32(dl[e]), ex));
-      hq[e] = f32_to_f16_bits(ldexpf(bf16_to_f32(dl[PER + e]), ex));
-    }
-    uint16_t *dst = rows + (((int64_t)b * H + h) * Lp + t) * D;
-#pragma unroll
-    for (int c = 0; c < PER; c += 8) {
-      *reinterpret_cast<uint4 *>(dst + j0 + c) = *reinterpret_cast<const uint4 *>(&lq[c]);
-      *reinterpret_cast<uint4 *>(dst + HALF + j0 + c) = *reinterpret_cast<const uint4 *>(&hq[c]);
-    }
-  }
-}
-
-// emin[2 * (b * Hkv + kv)] = the smallest tile exponent of the kv group's
-// heads, etile [B][Hq][MTS]: one workgroup per (row, kv group).
-__global__ __launch_bounds__(256) void group_min_kernel(int32_t Hq, int32_t group, int32_t MTS,
-                                                        const int32_t *etile, int32_t *emin) {
-  __shared__ int32_t wmin[4];
-  const int64_t gk = blockIdx.x;  // b * Hkv + kv
-  const int64_t n = (int64_t)group * MTS;
-  const int32_t *src = etile + gk * n;  // the group's heads are consecutive
-  int32_t m = kExpMax;
-  for (int64_t i = threadIdx.x; i < n; i += 256) m = min(m, src[i]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = min(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) wmin[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) emin[2 * gk] = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
-}
-
-// Units of the backward, per slot s of q head h in kv group kv, with eq, edo
-// the tile exponents of q and dout at s and eqr, edor their group minima:
-//   lse2[b][h][s] = lse * log2(e) - kPdvExp + (edo - edor): the dK/dV kernel's
-//       fp16(P * 2^(kPdvExp - (edo - edor))) then cancels the dout tile scale in
-//       dV^T += dO'^T P^T; +inf where the row has no key or s >= L, so that
-//       recomputed probabilities are exactly 0;
-//   dsc[b][h][s] *= 2^(edo + ev - kDsShift - kPdvExp - (eq - eqr)): delta in
-//       the units of dP = dO' V'^T of that slot, shifted so that
-//       dS' = P' (dP dss - delta) comes out in units that Q' turns into the
-//       group-wide units of dK.
-// One thread per (b, h, s).
-__global__ __launch_bounds__(256) void scale_delta_kernel(int32_t B, int32_t L, int32_t Lp, int32_t Hq, int32_t group,
-                                                          const float *lse, const int32_t *slot_tok,
-                                                          const int32_t *eqt, const int32_t *edot,
-                                                          const int32_t *eref, const uint32_t *mv, float *dsc,
-                                                          float *lse2) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)B * Hq * Lp) return;
-  const int32_t sl = (int32_t)(gid % Lp);
-  const int64_t bh = gid / Lp;
-  const int h = (int)(bh % Hq);
-  const int64_t b = bh / Hq;
-  const int kv = h / group, Hkv = Hq / group;
-  const int64_t tix = bh * (Lp / kTile) + sl / kTile;
-  const int eq = eqt[tix], edo = edot[tix];
-  const int eqr = eref[2 * (b * Hkv + kv)], edor = eref[2 * (b * Hkv + kv) + 1];
-  const int ev = plane_exponent(mv[b * Hkv + kv]);
-  float l2 = INFINITY;
-  if (sl < L) {
-    const float l = lse[bh * L + slot_tok[b * L + sl]];
-    if (l != -INFINITY) l2 = l * kLog2e - (float)kPdvExp + (float)(edo - edor);
-  }
-  lse2[gid] = l2;
-  dsc[gid] = ldexpf(dsc[gid], edo + ev - kDsShift - kPdvExp - (eq - eqr));
 }
 
 // Longest-first work order (see q_work_item): the q-tile rows (b*MT + m) by
@@ -484,14 +365,14 @@ void launch_absmax_d(int32_t B, int32_t L, const AbsmaxJob *jobs, hipStream_t s)
   absmax_kernel<D><<<dim3((L + kAbsTokens - 1) / kAbsTokens, jobs[1].hb_end, B), 256, 0, s>>>(L, jobs[0], jobs[1]);
 }
 
-template <int D, bool ROPE, bool TILE>
+template <int D, bool ROPE, bool ROWS>
 void launch_pack_d(int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group, const void *x,
                    const int32_t *slot_tok, const float2 *table, const uint32_t *pmax, uint16_t *rows,
-                   int32_t *etile, hipStream_t s) {
+                   int32_t *erow, int32_t *etile, hipStream_t s) {
   const unsigned hgroups = (unsigned)((H + kPackHeads - 1) / kPackHeads);
   const dim3 grid(hgroups * (unsigned)(Lp / kPackSlots), 1, B);
-  pack_kernel<D, ROPE, TILE><<<grid, 256, 0, s>>>(L, Lp, H, group, static_cast<const uint16_t *>(x), slot_tok, table,
-                                                 pmax, rows, etile);
+  pack_kernel<D, ROPE, ROWS><<<grid, 256, 0, s>>>(L, Lp, H, group, static_cast<const uint16_t *>(x), slot_tok, table,
+                                                 pmax, rows, erow, etile);
 }
 
 }  // namespace
@@ -516,16 +397,15 @@ void launch_absmax_kv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   else launch_absmax_d<128>(in.B, in.L, jobs, s);
 }
 
-// q after RoPE, one scale per 64-slot tile of each (row, head).
+// q after RoPE, one scale per row of each (row, head).
 void launch_pack_q(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int32_t group = in.Hq / in.Hkv;
   if (in.D == 64)
     launch_pack_d<64, true, true>(in.B, in.L, ws.Lp, in.Hq, group, in.q, in.layout.slot_tok, ws.rope, nullptr,
-                                  ws.qr, ws.eqt, s);
+                                  ws.qr, ws.eqq, ws.eqt, s);
   else
     launch_pack_d<128, true, true>(in.B, in.L, ws.Lp, in.Hq, group, in.q, in.layout.slot_tok, ws.rope, nullptr,
-                                   ws.qr, ws.eqt, s);
-  group_min_kernel<<<(unsigned)(in.B * in.Hkv), 256, 0, s>>>(in.Hq, group, ws.Lp / kTile, ws.eqt, ws.eref);
+                                   ws.qr, ws.eqq, ws.eqt, s);
 }
 
 // k (RoPE) or v, one scale per plane.
@@ -533,11 +413,11 @@ void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t
                      const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
                      uint16_t *rows, hipStream_t s) {
   if (D == 64) {
-    if (rope) launch_pack_d<64, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, s);
-    else launch_pack_d<64, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, s);
+    if (rope) launch_pack_d<64, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
+    else launch_pack_d<64, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
   } else {
-    if (rope) launch_pack_d<128, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, s);
-    else launch_pack_d<128, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, s);
+    if (rope) launch_pack_d<128, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
+    else launch_pack_d<128, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
   }
 }
 
@@ -547,30 +427,6 @@ void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
                                                in.layout.q_nnz, in.layout.q_list, in.layout.k_nnz, in.layout.k_list,
                                                ws.order_cost, ws.q_order, ws.k_raw, ws.k_items, ws.k_split,
                                                ws.k_counts);
-}
-
-// delta and the fp16 dout copy with its tile exponents and their group minima.
-void launch_delta_pack(const opr_attn_in &in, const void *o, const void *dout, const AttnWs &ws,
-                       hipStream_t s) {
-  const int32_t group = in.Hq / in.Hkv;
-  const unsigned hgroups = (unsigned)((in.Hq + kPackHeads - 1) / kPackHeads);
-  const dim3 grid(hgroups * (unsigned)(ws.Lp / kPackSlots), 1, in.B);
-  const uint16_t *o16 = static_cast<const uint16_t *>(o);
-  const uint16_t *d16 = static_cast<const uint16_t *>(dout);
-  if (in.D == 64)
-    delta_pack_kernel<64><<<grid, 256, 0, s>>>(in.L, ws.Lp, in.Hq, group, o16, d16, in.layout.slot_tok, ws.dor,
-                                               ws.dsc, ws.edot);
-  else
-    delta_pack_kernel<128><<<grid, 256, 0, s>>>(in.L, ws.Lp, in.Hq, group, o16, d16, in.layout.slot_tok, ws.dor,
-                                                ws.dsc, ws.edot);
-  group_min_kernel<<<(unsigned)(in.B * in.Hkv), 256, 0, s>>>(in.Hq, group, ws.Lp / kTile, ws.edot, ws.eref + 1);
-}
-
-void launch_scale_delta(const opr_attn_in &in, const float *lse, const AttnWs &ws, hipStream_t s) {
-  const int64_t total = (int64_t)in.B * in.Hq * ws.Lp;
-  scale_delta_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(in.B, in.L, ws.Lp, in.Hq, in.Hq / in.Hkv, lse,
-                                                                     in.layout.slot_tok, ws.eqt, ws.edot, ws.eref,
-                                                                     ws.mv, ws.dsc, ws.lse2);
 }
 
 }  // namespace opr

@@ -46,19 +46,16 @@ __device__ inline int build_q_stages(const int32_t *lst, const uint32_t *subs, i
 // Key-side kernel (dK/dV) of k-tile n: wave w owns key sub-column w; the
 // stages run over the q-tiles k_list[...] x the G heads of the kv group x the
 // two 64-query halves, flat index f = (tile * G + head) * 2 + half, from *f up
-// to fend (a work item's part of the column's range).  The
-// descriptor is (x, y, z, w): x and y as above, z the q' and w the dout
-// exponents (+ 64, one byte each) of the stage's four 16-query tiles
-// (eqt_g, edot_g: the group's [G][MTS] tile exponents).
-constexpr int kKStageCap = 512;  // dK/dV descriptors per list chunk (8 KB of LDS)
+// to fend (a work item's part of the column's range).  The descriptor is
+// (x, y) as above.
+constexpr int kKStageCap = 1024;  // dK/dV descriptors per list chunk (8 KB of LDS)
 
 __device__ inline int build_k_stages(const int32_t *lst, const uint32_t *subs_b, int NT, int n, int G,
-                                     int64_t fend, const int32_t *eqt_g, const int32_t *edot_g, int MTS,
-                                     int64_t *f, uint4 *stages, int lane) {
+                                     int64_t fend, int64_t *f, uint2 *stages, int lane) {
   int count = 0;
   while (*f < fend && count + 64 <= kKStageCap) {
     const int64_t ff = *f + lane;
-    uint32_t cls = 0, x = 0, z = 0, zw = 0;
+    uint32_t cls = 0, x = 0;
     if (ff < fend) {
       const int qh = (int)(ff & 1);
       const int64_t tj = ff >> 1;
@@ -70,25 +67,14 @@ __device__ inline int build_k_stages(const int32_t *lst, const uint32_t *subs_b,
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) cls |= ((sub >> (2 * (4 * (2 * qh + qb) + w))) & 3u) << (4 * w + 2 * qb);
       x = (uint32_t)(m * 128 + 64 * qh) | ((uint32_t)hj << 24);
-      if (cls != 0) {
-        const int64_t tix = (int64_t)hj * MTS + (m * 128 + 64 * qh) / kTile;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          z |= (uint32_t)(eqt_g[tix + k] + 64) << (8 * k);
-          zw |= (uint32_t)(edot_g[tix + k] + 64) << (8 * k);
-        }
-      }
     }
     const uint64_t bal = __ballot(cls != 0);
-    if (cls != 0) stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint4(x, cls, z, zw);
+    if (cls != 0) stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint2(x, cls);
     count += __popcll(bal);
     *f += 64;
   }
   if (*f > fend) *f = fend;
   return count;
 }
-
-// Exponent byte k (0..3) of a dK/dV descriptor's z or w word.
-__device__ __forceinline__ int stage_exponent(uint32_t z, int k) { return (int)((z >> (8 * k)) & 0xFFu) - 64; }
 
 }  // namespace opr

@@ -17,13 +17,11 @@ void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t
                      const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
                      uint16_t *rows, hipStream_t s);
 void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
-void launch_delta_pack(const opr_attn_in &in, const void *o, const void *dout, const AttnWs &ws,
-                       hipStream_t s);
-void launch_scale_delta(const opr_attn_in &in, const float *lse, const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, float *lse,
                                   const AttnWs &ws, hipStream_t s);
-hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, float *dq, float *dk,
-                                   float *dv, const AttnWs &ws, hipStream_t s, hipEvent_t *ev);
+hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, const void *o, const float *lse,
+                                   const void *dout, float *dq, float *dk, float *dv, const AttnWs &ws,
+                                   hipStream_t s, hipEvent_t *ev);
 size_t token_ce_ws_bytes(int64_t n_rows, int32_t V);
 int block_norm_grid(int D, int64_t T, int NH);
 hipError_t launch_qk_norm_fwd(int D, int64_t T, int Hq, int Hkv, float eps, const void *qkv, const float *gq,
@@ -37,8 +35,11 @@ hipError_t launch_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const voi
 
 static bool valid_block(int32_t b) { return b == 32 || b == 64 || b == 128; }
 
-// The runs of slots are read and written as 16-byte vectors.
+// The runs of slots, the attention tensors and the per-token rows are read
+// and written as 16-byte vectors; workspaces are carved in 256-byte pieces
+// that the kernels read with 16-byte (int4, float4) accesses.
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned256(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   Carver cv(p);
@@ -59,8 +60,9 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
     w.mv = w.mk + (size_t)in.B * in.Hkv;
   }
   const size_t etiles = (size_t)in.B * in.Hq * (Lp / kTile);
+  const size_t erows = (size_t)in.B * in.Hq * Lp;
+  w.eqq = cv.take<int32_t>(erows);
   w.eqt = cv.take<int32_t>(etiles);
-  w.eref = cv.take<int32_t>((size_t)2 * in.B * in.Hkv);
   const size_t tiles = (size_t)in.B * (Lp / OPR_ATTN_BLOCK);
   w.q_order = cv.take<int32_t>(tiles);
   w.order_cost = cv.take<int32_t>(2 * tiles);
@@ -71,9 +73,11 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
   // everything above is the forward state; the backward part follows
   if (is_bwd) {
     w.dor = cv.take<uint16_t>(qn);
+    w.edoq = cv.take<int32_t>(erows);
     w.edot = cv.take<int32_t>(etiles);
-    w.dsc = cv.take<float>((size_t)in.B * in.Hq * Lp);
-    w.lse2 = cv.take<float>((size_t)in.B * in.Hq * Lp);
+    w.dsc = cv.take<float>(erows);
+    w.lse2 = cv.take<float>(erows);
+    w.fsq = cv.take<float>(erows);
     w.kpart = cv.take<float>((size_t)kSplitSlots * OPR_ATTN_BLOCK * in.D * 2);
   }
   if (o) *o = w;
@@ -104,9 +108,10 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->dor = ws.dor;
   p->mk = ws.mk;
   p->mv = ws.mv;
+  p->eqq = ws.eqq;
   p->eqt = ws.eqt;
+  p->edoq = ws.edoq;
   p->edot = ws.edot;
-  p->eref = ws.eref;
   p->MTS = ws.Lp / kTile;
   p->q_order = ws.q_order;
   p->k_items = ws.k_items;
@@ -118,6 +123,10 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->kiv = reinterpret_cast<const int4 *>(in.layout.slot_kiv);
   p->dsc = ws.dsc;
   p->lse2 = ws.lse2;
+  p->fsq = ws.fsq;
+  p->o_in = nullptr;
+  p->dout_in = nullptr;
+  p->lse_in = nullptr;
 }
 
 // Shape checks shared by the attention entry points and the size query.
@@ -140,6 +149,7 @@ static opr_status check_attn_in(const opr_attn_in *in) {
   const opr_status st = check_attn_shape(in->B, in->L, in->Hq, in->Hkv, in->D);
   if (st != OPR_OK) return st;
   if (!in->q || !in->k || !in->v) return OPR_E_INVALID;
+  if (!aligned16(in->q) || !aligned16(in->k) || !aligned16(in->v)) return OPR_E_INVALID;
   const opr_layout &l = in->layout;
   if (!l.tok_pos || !l.slot_tok || !l.slot_qiv || !l.slot_kiv || !l.tile_class || !l.sub_class ||
       !l.q_nnz || !l.q_list || !l.k_nnz || !l.k_list)
@@ -282,7 +292,7 @@ opr_status opr_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block
       !out->q_nnz || !out->q_list || !out->k_nnz || !out->k_list)
     return OPR_E_INVALID;
   if (out->order != OPR_ORDER_PACKED && out->order != OPR_ORDER_ATTENTION) return OPR_E_INVALID;
-  if (!aligned16(out->slot_qiv) || !aligned16(out->slot_kiv)) return OPR_E_INVALID;
+  if (!aligned16(out->slot_qiv) || !aligned16(out->slot_kiv) || !aligned256(workspace)) return OPR_E_INVALID;
   const int64_t MT = ((int64_t)L + block_q - 1) / block_q, NT = ((int64_t)L + block_k - 1) / block_k;
   if ((int64_t)B * MT * NT >= (int64_t)1 << 31) return OPR_E_UNSUPPORTED;
   // count conversations and turns, check every length and each row's capacity
@@ -339,6 +349,7 @@ opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *worksp
   const opr_status st = check_attn_in(in);
   if (st != OPR_OK) return st;
   if (!o || !lse || !workspace) return OPR_E_INVALID;
+  if (!aligned16(o) || !aligned256(workspace)) return OPR_E_INVALID;
   if (ws_bytes < carve_attn_ws(nullptr, *in, 0, nullptr)) return OPR_E_CAPACITY;
   AttnWs ws;
   carve_attn_ws(workspace, *in, 0, &ws);
@@ -356,14 +367,15 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   const opr_status st = check_attn_in(in);
   if (st != OPR_OK) return st;
   if (!o || !lse || !dout || !dq || !dk || !dv || !workspace) return OPR_E_INVALID;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned256(workspace))
+    return OPR_E_INVALID;
   if (ws_bytes < carve_attn_ws(nullptr, *in, 1, nullptr)) return OPR_E_CAPACITY;
   AttnWs ws;
   carve_attn_ws(workspace, *in, 1, &ws);
   mark(in, 0, stream);
   if (!in->reuse_fwd_workspace) forward_prologue(*in, ws, stream);
-  launch_delta_pack(*in, o, dout, ws, stream);
-  launch_scale_delta(*in, lse, ws, stream);
-  if (launch_attn_bwd_kernels(*in, effective_scale(in), dq, dk, dv, ws, stream,
+  if (launch_attn_bwd_kernels(*in, effective_scale(in), o, lse, dout, dq, dk, dv, ws, stream,
                               in->timing_events ? in->timing_events + 1 : nullptr) != hipSuccess)
     return OPR_E_HIP;
   return hip_status();
@@ -383,7 +395,7 @@ opr_status opr_block_fwd(const opr_block_in *in, void *y, void *qkv, void *o, fl
   const opr_status st = check_block_in(in);
   if (st != OPR_OK) return st;
   if (!y || !qkv || !o || !lse || !workspace) return OPR_E_INVALID;
-  if (!aligned16(y) || !aligned16(qkv) || !aligned16(o)) return OPR_E_INVALID;
+  if (!aligned16(y) || !aligned16(qkv) || !aligned16(o) || !aligned256(workspace)) return OPR_E_INVALID;
   if (ws_bytes < carve_block_ws(nullptr, *in, 0, nullptr)) return OPR_E_CAPACITY;
   BlockWs w;
   carve_block_ws(workspace, *in, 0, &w);
@@ -414,7 +426,7 @@ opr_status opr_block_bwd(const opr_block_in *in, const void *qkv, const void *o,
   if (st != OPR_OK) return st;
   if (!qkv || !o || !lse || !dy || !dx || !dw_qkv || !dw_o || !dg_q || !dg_k || !workspace) return OPR_E_INVALID;
   if (!aligned16(qkv) || !aligned16(o) || !aligned16(dy) || !aligned16(dx) || !aligned16(dw_qkv) ||
-      !aligned16(dw_o))
+      !aligned16(dw_o) || !aligned256(workspace))
     return OPR_E_INVALID;
   if (ws_bytes < carve_block_ws(nullptr, *in, 1, nullptr)) return OPR_E_CAPACITY;
   BlockWs w;

@@ -68,22 +68,20 @@ struct AttnWs {
   // everything below is in slot (attention) order
   float2 *rope;         // [B][Lp][D/2] (cos, sin) at each slot's position id
   // fp16 copies [B][H][Lp][D], zero past L: k and v with one power-of-two
-  // scale per (row, kv head) plane, q and dout with one per 16-slot tile of
-  // each (row, q head)
+  // scale per (row, kv head) plane, q and dout with one per row (slot and
+  // q head)
   uint16_t *qr;         // q after RoPE
   uint16_t *kr;         // k after RoPE
   uint16_t *vr;         // v
-  uint16_t *dor;        // dout                                   (bwd)
+  uint16_t *dor;        // dout, written by the dQ kernel             (bwd)
   // plane maxima (float bits): mk [B][Hkv], mv [B][Hkv], contiguous from pmax
   // (n_pmax words)
   uint32_t *pmax, *mk, *mv;
   int32_t n_pmax;
-  // tile exponents [B][Hq][Lp/16] of q (eqt) and dout (edot), one per 16-slot
-  // tile, and their minima over each kv group's heads and tiles,
-  // eref [B][Hkv][2] = (q, dout)
-  int32_t *eqt;
-  int32_t *edot;        //                                        (bwd)
-  int32_t *eref;
+  // row exponents [B][Hq][Lp] of q (eqq) and dout (edoq), and their minima
+  // over each 16-slot tile [B][Hq][Lp/16] (eqt, edot)
+  int32_t *eqq, *eqt;
+  int32_t *edoq, *edot; //                                        (bwd)
   int32_t *q_order;     // [B*MT] q-tile rows, most stages first
   int32_t *order_cost;  // [B*MT + B*NT] stage counts of the rows and columns
   // dK/dV work items (column, part j, parts s, partial slot or -1), the
@@ -94,8 +92,9 @@ struct AttnWs {
   int4 *k_split;        // [kSplitSlots] cut columns: (column, first slot, s, 0)
   int32_t *k_counts;    // [4]: items, cut columns
   float *kpart;         // [kSplitSlots][128][D] dK then dV partials of parts 1..s-1 (bwd)
-  float *dsc;           // [B][Hq][Lp] rowsum(dout * o), scaled        (bwd)
-  float *lse2;          // [B][Hq][Lp] log2-domain lse, +inf where no key (bwd)
+  float *dsc;           // [B][Hq][Lp] rowsum(dout * o) in dK/dV units (bwd)
+  float *lse2;          // [B][Hq][Lp] log2-domain lse in dK/dV units, +inf where no key (bwd)
+  float *fsq;           // [B][Hq][Lp] score factor of each query row in dK/dV (bwd)
 };
 
 size_t carve_attn_ws(void *ws, const opr_attn_in &in, int is_bwd, AttnWs *out);

@@ -165,9 +165,11 @@ typedef struct {
   /* Optional instrumentation, may be NULL: host array of events created by
    * the caller (hipEventCreate).  opr_attn_fwd records [0] before its
    * prologue, [1] before the attention kernel and [2] after it;
-   * opr_attn_bwd records [0] before its prologue, [1] before the dK/dV
-   * kernel, [2] after it and [3] after the dQ kernel ([2]..[3] also spans
-   * the small kernel that sums the parts of cut dK/dV columns). */
+   * opr_attn_bwd records [0] before its prologue (the forward state, only
+   * without reuse_fwd_workspace), [1] before the dQ kernel (which also
+   * forms delta = rowsum(dout * o) and the fp16 dout), [2] after it and [3]
+   * right after the dK/dV kernel (the small kernel that sums the parts of
+   * cut dK/dV columns runs after [3]). */
   hipEvent_t *timing_events;
   /* opr_attn_bwd only: nonzero when `workspace` is the one the matching
    * opr_attn_fwd call (same inputs, layout and stream, nothing written to the

@@ -100,14 +100,14 @@ def _attn_in(Bd, **kw):
     return Bd.OprAttnIn(**a)
 
 
-def _fwd(Bd, ws_bytes=1 << 40, **kw):
+def _fwd(Bd, ws_bytes=1 << 40, o=FAKE, ws=FAKE, **kw):
     a = _attn_in(Bd, **kw)
-    return Bd.LIB.opr_attn_fwd(ctypes.byref(a), FAKE, FAKE, FAKE, ws_bytes, None)
+    return Bd.LIB.opr_attn_fwd(ctypes.byref(a), o, FAKE, ws, ws_bytes, None)
 
 
-def _bwd(Bd, ws_bytes=1 << 40, dq=FAKE, **kw):
+def _bwd(Bd, ws_bytes=1 << 40, dq=FAKE, o=FAKE, dout=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, **kw):
     a = _attn_in(Bd, **kw)
-    return Bd.LIB.opr_attn_bwd(ctypes.byref(a), FAKE, FAKE, FAKE, dq, FAKE, FAKE, FAKE, ws_bytes, None)
+    return Bd.LIB.opr_attn_bwd(ctypes.byref(a), o, FAKE, dout, dq, dk, dv, ws, ws_bytes, None)
 
 
 def test_attn_errors(Bd):
@@ -128,6 +128,25 @@ def test_attn_errors(Bd):
         assert f(Bd, ws_bytes=1024) == Bd.OPR_E_CAPACITY
         assert f(Bd, B=0) == Bd.OPR_E_INVALID
     assert _bwd(Bd, dq=None) == Bd.OPR_E_INVALID
+
+
+def test_attn_alignment(Bd):
+    """The kernels read and write q, k, v, o, dout, dq, dk and dv with 16-byte
+    vector accesses and carve the workspace in 256-byte aligned pieces: a
+    pointer off those boundaries is rejected before any HIP call."""
+    for f in (_fwd, _bwd):
+        for name in ("q", "k", "v"):
+            for off in (2, 4, 8):
+                assert f(Bd, **{name: FAKE + off}) == Bd.OPR_E_INVALID, (f.__name__, name, off)
+        assert f(Bd, o=FAKE + 8) == Bd.OPR_E_INVALID
+        assert f(Bd, ws=FAKE + 16) == Bd.OPR_E_INVALID
+        assert f(Bd, ws=FAKE + 128) == Bd.OPR_E_INVALID
+    for name in ("dout", "dq", "dk", "dv"):
+        assert _bwd(Bd, **{name: FAKE + 4}) == Bd.OPR_E_INVALID, name
+    # aligned arguments pass validation and meet the workspace-size check
+    assert _fwd(Bd, ws_bytes=1024) == Bd.OPR_E_CAPACITY
+    assert _bwd(Bd, ws_bytes=1024) == Bd.OPR_E_CAPACITY
+    assert _build(Bd, ws=FAKE + 64) == Bd.OPR_E_INVALID
 
 
 def test_attn_workspace_size(Bd):
