@@ -78,8 +78,6 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   __shared__ uint2 stages[kKStageCap];
   __shared__ int sh_count;
   __shared__ int64_t sh_next;
-  __shared__ int sh_emin[8];
-  __shared__ int4 sh_hull[4];
 
   const int64_t R = blockIdx.x;  // rank: longest items first, round-robin over the XCDs
   if (R / p.Hkv >= p.k_counts[0]) return;
@@ -147,94 +145,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   const int64_t fbegin = ftotal * item.y / item.z;
   const int64_t fend = ftotal * (item.y + 1) / item.z;
 
-  // Units of each key block: the smallest q' and dout row exponents over the
-  // queries of this item's stages that see the block's keys.  The query
-  // slots that see a key form at most two runs; over the 32 keys of a block
-  // inside one conversation the first runs join into one interval and the
-  // second runs into another (consecutive history keys are seen by the
-  // history from their slot on and by the t / r_out tail from some turn on;
-  // consecutive t / r_out keys by overlapping runs from their own slot), so
-  // the block's two hulls are exact there and a superset across a
-  // conversation boundary.  A 16-query tile inside a hull contributes its
-  // precomputed minimum, a tile cut by a hull's end its rows inside the
-  // hull.  A query outside both hulls meets only masked entries (P = 0): its
-  // shift against the block's units is clamped at 0, so its bracket stays
-  // finite and its products exactly 0.
-  int eqr, edor;
-  {
-    constexpr int kNone = 0x7FFFFFFF;
-    // hull of the lane's runs over the wave's 32 keys (both halves hold the same keys)
-    int h0 = iv.x < iv.y ? iv.x : kNone, h1 = iv.x < iv.y ? iv.y : -kNone;
-    int h2 = iv.z < iv.w ? iv.z : kNone, h3 = iv.z < iv.w ? iv.w : -kNone;
-#pragma unroll
-    for (int off = 16; off > 0; off >>= 1) {
-      h0 = min(h0, __shfl_xor(h0, off));
-      h1 = max(h1, __shfl_xor(h1, off));
-      h2 = min(h2, __shfl_xor(h2, off));
-      h3 = max(h3, __shfl_xor(h3, off));
-    }
-    if (pwave && lane == 0) sh_hull[w] = make_int4(h0, h1, h2, h3);
-    if (tid < 8) sh_emin[tid] = kExpMax;
-    __syncthreads();
-    int4 hull[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) hull[kb] = sh_hull[kb];
-    int mn[8];  // [key block][q', dout]
-#pragma unroll
-    for (int e = 0; e < 8; ++e) mn[e] = kExpMax;
-    const int64_t gt = hbase * p.MTS, gr = hbase * p.Lp;  // the group's first head in the tile / row tables
-    for (int64_t ff = fbegin + tid; ff < fend; ff += 512) {
-      const int qh = (int)(ff & 1);
-      const int64_t tj = ff >> 1;
-      const int hj = (int)(tj % p.group);
-      const int q0 = lst[tj / p.group] * 128 + 64 * qh;
-      const int64_t tix = gt + (int64_t)hj * p.MTS + q0 / kTile;
-      const int4 e4 = *reinterpret_cast<const int4 *>(p.eqt + tix);
-      const int4 d4 = *reinterpret_cast<const int4 *>(p.edot + tix);
-      const int eqk[4] = {e4.x, e4.y, e4.z, e4.w}, edk[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int t0 = q0 + kTile * k, t1 = t0 + kTile;
-        uint32_t cut = 0u;  // blocks whose hull ends inside this tile
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int4 hl = hull[kb];
-          if ((hl.x <= t0 && t1 <= hl.y) || (hl.z <= t0 && t1 <= hl.w)) {
-            mn[2 * kb] = min(mn[2 * kb], eqk[k]);
-            mn[2 * kb + 1] = min(mn[2 * kb + 1], edk[k]);
-          } else if ((hl.x < t1 && t0 < hl.y) || (hl.z < t1 && t0 < hl.w)) {
-            cut |= 1u << kb;
-          }
-        }
-        if (cut) {
-          const int64_t rix = gr + (int64_t)hj * p.Lp + t0;
-          for (int r = 0; r < kTile; ++r) {
-            const int qs = t0 + r, eqv = p.eqq[rix + r], edv = p.edoq[rix + r];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-              const int4 hl = hull[kb];
-              if (((cut >> kb) & 1u) && ((hl.x <= qs && qs < hl.y) || (hl.z <= qs && qs < hl.w))) {
-                mn[2 * kb] = min(mn[2 * kb], eqv);
-                mn[2 * kb + 1] = min(mn[2 * kb + 1], edv);
-              }
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mn[e] = min(mn[e], __shfl_xor(mn[e], off));
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) atomicMin(&sh_emin[e], mn[e]);
-    }
-    __syncthreads();
-    eqr = uniform(sh_emin[2 * w]);
-    edor = uniform(sh_emin[2 * w + 1]);
-  }
+  // this key block's units, from dkdv_units_kernel
+  const int eqr = uniform(p.kunits[R * 8 + 2 * w]), edor = uniform(p.kunits[R * 8 + 2 * w + 1]);
   const float edor_f = (float)edor;
   // a query's score factor fsq = scale log2(e) 2^-(eq + ek) times qsh is its
   // shift 2^-(eq - eqr) against this block's units, times 2^bs (capped at
@@ -470,6 +382,112 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   }
 }
 
+// Units of the dK/dV work items: for rank R (item R / Hkv, kv head R % Hkv)
+// and each of its 4 key blocks, the smallest q' and dout row exponents over
+// the queries of the item's stages that see the block's keys, into
+// kunits[R][block][q', dout].  The query slots that see a key form at most
+// two runs; over the 32 keys of a block inside one conversation the first
+// runs join into one interval and the second runs into another (consecutive
+// history keys are seen by the history from their slot on and by the t /
+// r_out tail from some turn on; consecutive t / r_out keys by overlapping
+// runs from their own slot), so the block's two hulls are exact there and a
+// superset across a conversation boundary.  A 16-query tile inside a hull
+// contributes its precomputed minimum, a tile cut by a hull's end its rows
+// inside the hull.  One workgroup of 4 waves per rank: wave w forms block w's
+// hulls, then all threads share the stages.  (Its own launch of many small
+// workgroups: inside the dK/dV kernel, with one workgroup per CU, these
+// dependent loads would stall the matrix cores.)
+__global__ __launch_bounds__(256) void dkdv_units_kernel(AttnParams p) {
+  const int64_t R = blockIdx.x;
+  if (R / p.Hkv >= p.k_counts[0]) return;
+  const int4 item = p.k_items[R / p.Hkv];
+  const int32_t col = item.x;
+  const int kvh = (int)(R % p.Hkv);
+  const int b = col / p.NT, n = col - b * p.NT;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  __shared__ int4 sh_hull[4];
+  __shared__ int sh_emin[8];
+  {
+    constexpr int kNone = 0x7FFFFFFF;
+    const int key = n * 128 + 32 * w + (lane & 31);
+    const int4 iv = key < p.L ? p.kiv[(int64_t)b * p.L + key] : make_int4(0, 0, 0, 0);
+    int h0 = iv.x < iv.y ? iv.x : kNone, h1 = iv.x < iv.y ? iv.y : -kNone;
+    int h2 = iv.z < iv.w ? iv.z : kNone, h3 = iv.z < iv.w ? iv.w : -kNone;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) {
+      h0 = min(h0, __shfl_xor(h0, off));
+      h1 = max(h1, __shfl_xor(h1, off));
+      h2 = min(h2, __shfl_xor(h2, off));
+      h3 = max(h3, __shfl_xor(h3, off));
+    }
+    if (lane == 0) sh_hull[w] = make_int4(h0, h1, h2, h3);
+    if (tid < 8) sh_emin[tid] = kExpMax;
+  }
+  __syncthreads();
+  int4 hull[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) hull[kb] = sh_hull[kb];
+  int mn[8];  // [key block][q', dout]
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mn[e] = kExpMax;
+  const int64_t tcol = (int64_t)b * p.NT + n;
+  const int32_t *lst = p.k_list + tcol * p.MT;
+  const int64_t ftotal = (int64_t)p.k_nnz[tcol] * p.group * 2;
+  const int64_t fbegin = ftotal * item.y / item.z, fend = ftotal * (item.y + 1) / item.z;
+  const int64_t hbase = (int64_t)b * p.Hq + (int64_t)kvh * p.group;
+  const int64_t gt = hbase * p.MTS, gr = hbase * p.Lp;  // the group's first head in the tile / row tables
+  for (int64_t ff = fbegin + tid; ff < fend; ff += 256) {
+    const int qh = (int)(ff & 1);
+    const int64_t tj = ff >> 1;
+    const int hj = (int)(tj % p.group);
+    const int q0 = lst[tj / p.group] * 128 + 64 * qh;
+    const int64_t tix = gt + (int64_t)hj * p.MTS + q0 / kTile;
+    const int4 e4 = *reinterpret_cast<const int4 *>(p.eqt + tix);
+    const int4 d4 = *reinterpret_cast<const int4 *>(p.edot + tix);
+    const int eqk[4] = {e4.x, e4.y, e4.z, e4.w}, edk[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t0 = q0 + kTile * k, t1 = t0 + kTile;
+      uint32_t cut = 0u;  // blocks whose hull ends inside this tile
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int4 hl = hull[kb];
+        if ((hl.x <= t0 && t1 <= hl.y) || (hl.z <= t0 && t1 <= hl.w)) {
+          mn[2 * kb] = min(mn[2 * kb], eqk[k]);
+          mn[2 * kb + 1] = min(mn[2 * kb + 1], edk[k]);
+        } else if ((hl.x < t1 && t0 < hl.y) || (hl.z < t1 && t0 < hl.w)) {
+          cut |= 1u << kb;
+        }
+      }
+      if (cut) {
+        const int64_t rix = gr + (int64_t)hj * p.Lp + t0;
+        for (int r = 0; r < kTile; ++r) {
+          const int qs = t0 + r, eqv = p.eqq[rix + r], edv = p.edoq[rix + r];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const int4 hl = hull[kb];
+            if (((cut >> kb) & 1u) && ((hl.x <= qs && qs < hl.y) || (hl.z <= qs && qs < hl.w))) {
+              mn[2 * kb] = min(mn[2 * kb], eqv);
+              mn[2 * kb + 1] = min(mn[2 * kb + 1], edv);
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mn[e] = min(mn[e], __shfl_xor(mn[e], off));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) atomicMin(&sh_emin[e], mn[e]);
+  }
+  __syncthreads();
+  if (tid < 8) p.kunits[R * 8 + tid] = sh_emin[tid];
+}
+
 // dK and dV of the columns cut into parts: part 0 wrote them at the tokens;
 // add parts 1..s-1 from their partial slots, in order.  One workgroup per
 // (cut column, kv head); grid.x covers the most cut columns there can be.
@@ -510,8 +528,8 @@ void launch_attn_dq_kernel(const AttnParams &p, int D, float *dq, hipStream_t s)
 // The backward: the dQ kernel first (it also writes the dout plane, its tile
 // exponents and the per-slot units that dK/dV reads), then dK/dV and the
 // reduce of the cut columns.  ev (optional): events recorded before dQ, after
-// it (before dK/dV) and right after the dK/dV kernel (so that its span is
-// that kernel alone).
+// it and the small kernel that picks the dK/dV units, and right after the
+// dK/dV kernel (so that its span is that kernel alone).
 hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, const void *o, const float *lse,
                                    const void *dout, float *dq, float *dk, float *dv, const AttnWs &ws,
                                    hipStream_t s, hipEvent_t *ev) {
@@ -526,6 +544,7 @@ hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, const voi
   const dim3 gr((unsigned)extra, (unsigned)in.Hkv);
   if (ev) (void)hipEventRecord(ev[0], s);
   launch_attn_dq_kernel(p, in.D, dq, s);
+  dkdv_units_kernel<<<gk, 256, 0, s>>>(p);
   if (ev) (void)hipEventRecord(ev[1], s);
   if (in.D == 64) attn_dkdv_kernel<64><<<gk, 512, 0, s>>>(p, dk, dv);
   else attn_dkdv_kernel<128><<<gk, 512, 0, s>>>(p, dk, dv);

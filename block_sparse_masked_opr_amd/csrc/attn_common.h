@@ -373,6 +373,7 @@ struct AttnParams {
   const int4 *k_split;         // columns cut into parts: (column, first partial slot, parts, 0)
   const int32_t *k_counts;     // [0] items, [1] cut columns
   float *kpart;                // partials of parts 1.. : [slot * Hkv + kv head][128][D], dK then dV
+  int32_t *kunits;             // [rank][4 key blocks][q', dout]: the dK/dV units of each work item
   const int32_t *slot_tok;     // [B][L] token at each slot
   const int4 *qiv;             // [B][L] key slots a query slot sees: [x, y) and [z, w)
   const int4 *kiv;             // [B][L] query slots that see a key slot: [x, y) and [z, w)

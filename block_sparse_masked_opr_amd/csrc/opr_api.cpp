@@ -78,6 +78,7 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
     w.dsc = cv.take<float>(erows);
     w.lse2 = cv.take<float>(erows);
     w.fsq = cv.take<float>(erows);
+    w.kunits = cv.take<int32_t>(((size_t)in.B * (Lp / OPR_ATTN_BLOCK) + kSplitSlots / in.Hkv + 1) * in.Hkv * 8);
     w.kpart = cv.take<float>((size_t)kSplitSlots * OPR_ATTN_BLOCK * in.D * 2);
   }
   if (o) *o = w;
@@ -124,6 +125,7 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->dsc = ws.dsc;
   p->lse2 = ws.lse2;
   p->fsq = ws.fsq;
+  p->kunits = ws.kunits;
   p->o_in = nullptr;
   p->dout_in = nullptr;
   p->lse_in = nullptr;

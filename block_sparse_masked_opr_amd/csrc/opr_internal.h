@@ -95,6 +95,7 @@ struct AttnWs {
   float *dsc;           // [B][Hq][Lp] rowsum(dout * o) in dK/dV units (bwd)
   float *lse2;          // [B][Hq][Lp] log2-domain lse in dK/dV units, +inf where no key (bwd)
   float *fsq;           // [B][Hq][Lp] score factor of each query row in dK/dV (bwd)
+  int32_t *kunits;      // [(B*NT + kSplitSlots/Hkv + 1) * Hkv][8] units of the dK/dV items (bwd)
 };
 
 size_t carve_attn_ws(void *ws, const opr_attn_in &in, int is_bwd, AttnWs *out);

@@ -167,8 +167,9 @@ typedef struct {
    * prologue, [1] before the attention kernel and [2] after it;
    * opr_attn_bwd records [0] before its prologue (the forward state, only
    * without reuse_fwd_workspace), [1] before the dQ kernel (which also
-   * forms delta = rowsum(dout * o) and the fp16 dout), [2] after it and [3]
-   * right after the dK/dV kernel (the small kernel that sums the parts of
+   * forms delta = rowsum(dout * o) and the fp16 dout), [2] after it and
+   * the small kernel that picks the dK/dV kernel's units, and [3] right
+   * after the dK/dV kernel (the small kernel that sums the parts of
    * cut dK/dV columns runs after [3]). */
   hipEvent_t *timing_events;
   /* opr_attn_bwd only: nonzero when `workspace` is the one the matching
