@@ -76,6 +76,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   __shared__ __attribute__((aligned(1024))) char pbf1[4 * PSTRIDE];
   __shared__ __attribute__((aligned(1024))) char pbf2[4 * PSTRIDE];
   __shared__ uint2 stages[kKStageCap];
+  // per wave: two factors of each of the stage's 64 queries (see p_elem, ds_elem)
+  __shared__ __attribute__((aligned(16))) float qfac[8][2][64];
   __shared__ int sh_count;
   __shared__ int64_t sh_next;
 
@@ -176,9 +178,12 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   auto p_elem = [&](uint2 desc, const char *buf, char *pout, f16x8 (&op)[2][2]) {
     const int q0 = (int)(desc.x & 0xFFFFFFu);
     const char *Qt = buf;
-    const float *lse2s = reinterpret_cast<const float *>(buf + 2 * TB);
     // raw score -> log2 units, per query (its q' row exponent)
     const float *fss = reinterpret_cast<const float *>(buf + 2 * TB + 512);
+    // lane i forms edor - lse2 of the stage's query i once, for all lanes
+    float *bq = qfac[wave][0];
+    bq[lane] = edor_f - reinterpret_cast<const float *>(buf + 2 * TB)[lane];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     char *Pw = pout + w * PSTRIDE;
     // both products first, then both element blocks
     f32x16 s[2];
@@ -204,15 +209,16 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int qbase = 32 * qb + 16 * hh + 8 * g;  // query rows of registers 8hh .. 8hh+7
-        const float4 l0 = *reinterpret_cast<const float4 *>(lse2s + qbase);
-        const float4 l1 = *reinterpret_cast<const float4 *>(lse2s + qbase + 4);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float4 l0 = *reinterpret_cast<const float4 *>(bq + qbase);
+        const float4 l1 = *reinterpret_cast<const float4 *>(bq + qbase + 4);
         const float4 f0 = *reinterpret_cast<const float4 *>(fss + qbase);
         const float4 f1 = *reinterpret_cast<const float4 *>(fss + qbase + 4);
-        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const float bv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
         const float fv[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          op[qb][hh][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * hh + e], fv[e], edor_f - lv[e]));
+          op[qb][hh][e] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * hh + e], fv[e], bv[e]));
         }
         *reinterpret_cast<f16x8 *>(Pw + (2 * qb + hh) * 1024 + lane * 16) = op[qb][hh];
       }
@@ -225,8 +231,16 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   // follows is dK^T += Q'^T dS^T.
   auto ds_elem = [&](uint2 desc, const char *buf, const char *pin, f16x8 (&op)[2][2]) {
     const char *dOt = buf + TB;
-    const float *dscs = reinterpret_cast<const float *>(buf + 2 * TB + 256);
-    const float *fss = reinterpret_cast<const float *>(buf + 2 * TB + 512);
+    // lane i forms, for the stage's query i, its shift 2^(bs - (eq - eqr))
+    // from its score factor (clamped at 2^bs for a query the block is not
+    // seen by) folded into the dP factor and into delta
+    float *dsq = qfac[wave][0], *dvq = qfac[wave][1];
+    {
+      const float sh = fminf(qcap, reinterpret_cast<const float *>(buf + 2 * TB + 512)[lane] * qsh);
+      dsq[lane] = kDss * sh;
+      dvq[lane] = reinterpret_cast<const float *>(buf + 2 * TB + 256)[lane] * sh;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     const char *Pw = pin + w * PSTRIDE;
     f32x16 dp[2];
 #pragma unroll
@@ -244,22 +258,20 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
       for (int hh = 0; hh < 2; ++hh) {
         const int qbase = 32 * qb + 16 * hh + 8 * g;
         const f16x8 pv = *reinterpret_cast<const f16x8 *>(Pw + (2 * qb + hh) * 1024 + lane * 16);
-        const float4 d0 = *reinterpret_cast<const float4 *>(dscs + qbase);
-        const float4 d1 = *reinterpret_cast<const float4 *>(dscs + qbase + 4);
-        const float4 f0 = *reinterpret_cast<const float4 *>(fss + qbase);
-        const float4 f1 = *reinterpret_cast<const float4 *>(fss + qbase + 4);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float4 s0 = *reinterpret_cast<const float4 *>(dsq + qbase);
+        const float4 s1 = *reinterpret_cast<const float4 *>(dsq + qbase + 4);
+        const float4 d0 = *reinterpret_cast<const float4 *>(dvq + qbase);
+        const float4 d1 = *reinterpret_cast<const float4 *>(dvq + qbase + 4);
+        const float dss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         const float dvv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-        // the query's shift 2^(bs - (eq - eqr)) from its score factor (clamped
-        // at 2^bs for a query the block is not seen by)
-        const float sh[8] = {fminf(qcap, f0.x * qsh), fminf(qcap, f0.y * qsh), fminf(qcap, f0.z * qsh),
-                             fminf(qcap, f0.w * qsh), fminf(qcap, f1.x * qsh), fminf(qcap, f1.y * qsh),
-                             fminf(qcap, f1.z * qsh), fminf(qcap, f1.w * qsh)};
-        // P * 2^kPdvExp times (dP * 2^-kDsShift - delta) * 2^-kPdvExp: the
-        // second factor in fp32, then both multiplied as packed fp16 pairs
+        // P * 2^kPdvExp times (dP * 2^-kDsShift - delta) * 2^-kPdvExp (with the
+        // query's shift): the second factor in fp32, then both multiplied as
+        // packed fp16 pairs
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const f16x2 t = {(_Float16)(fmaf(dp[qb][8 * hh + e], kDss, -dvv[e]) * sh[e]),
-                           (_Float16)(fmaf(dp[qb][8 * hh + e + 1], kDss, -dvv[e + 1]) * sh[e + 1])};
+          const f16x2 t = {(_Float16)fmaf(dp[qb][8 * hh + e], dss[e], -dvv[e]),
+                           (_Float16)fmaf(dp[qb][8 * hh + e + 1], dss[e + 1], -dvv[e + 1])};
           const f16x2 pp = {pv[e], pv[e + 1]};
           const f16x2 d = t * pp;
           op[qb][hh][e] = d[0];
