@@ -78,6 +78,8 @@ def _load() -> ctypes.CDLL:
     lib.opr_build_layout.restype = i32
     lib.opr_build_layout.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, sz,
                                      ctypes.POINTER(OprLayout), vp]
+    lib.opr_build_layout_noalloc.restype = i32
+    lib.opr_build_layout_noalloc.argtypes = [i32, i32, i32, i32, vp, vp, vp, ctypes.POINTER(OprLayout), vp]
     lib.opr_build_layout_workspace_size.restype = sz
     lib.opr_build_layout_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.opr_attn_fwd.restype = i32
@@ -107,7 +109,7 @@ def _load() -> ctypes.CDLL:
 
 LIB = _load()
 
-EXPORTED = ("opr_build_layout", "opr_build_layout_workspace_size", "opr_attn_fwd",
+EXPORTED = ("opr_build_layout", "opr_build_layout_noalloc", "opr_build_layout_workspace_size", "opr_attn_fwd",
             "opr_attn_bwd", "opr_attn_workspace_size", "opr_token_ce", "opr_token_ce_workspace_size",
             "opr_block_fwd", "opr_block_bwd", "opr_block_workspace_size", "opr_kpass_plan",
             "opr_status_string")
@@ -217,6 +219,33 @@ def opr_build_layout(rows: Sequence, L: int, block_q: int = OPR_ATTN_BLOCK,
                               turns.ctypes.data, workspace.data_ptr(), workspace.numel(),
                               ctypes.byref(cs), _stream(device))
     _check(st, "opr_build_layout")
+    return lay
+
+
+OPR_LAYOUT_SCRATCH_BYTES = 32 << 20
+
+
+def opr_build_layout_noalloc(rows: Sequence, L: int, block_q: int = OPR_ATTN_BLOCK,
+                             block_k: int = OPR_ATTN_BLOCK, device="cuda", out: Optional[Layout] = None,
+                             order: int = OPR_ORDER_ATTENTION) -> Layout:
+    """opr_build_layout without a workspace: the library's fixed device
+    scratch (OPR_LAYOUT_SCRATCH_BYTES per GPU) is used instead.  Calls that
+    overlap on one GPU race on that scratch."""
+    device = torch.device(device)
+    B = len(rows)
+    cpr, tpc, turns = inputs.flatten_rows(rows)
+    C, T = len(tpc), len(turns)
+    if out is not None and (out.B, out.L, out.block_q, out.block_k, out.order) == (B, L, block_q, block_k, order):
+        lay = out
+    else:
+        lay = Layout(B, L, block_q, block_k, device, order)
+    cpr = np.ascontiguousarray(cpr, dtype=np.int32)
+    tpc = np.ascontiguousarray(tpc if C else np.zeros(1, np.int32), dtype=np.int32)
+    turns = np.ascontiguousarray(turns if T else np.zeros((1, 4), np.int32), dtype=np.int32)
+    cs = lay.c_struct()
+    st = LIB.opr_build_layout_noalloc(B, L, block_q, block_k, cpr.ctypes.data, tpc.ctypes.data,
+                                      turns.ctypes.data, ctypes.byref(cs), _stream(device))
+    _check(st, "opr_build_layout_noalloc")
     return lay
 
 

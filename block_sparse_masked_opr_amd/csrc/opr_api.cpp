@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "attn_common.h"
 #include "opr_internal.h"
 
@@ -269,32 +271,21 @@ static void bmark(const opr_block_in *in, int i, hipStream_t s) {
   if (in->timing_events) hipEventRecord(in->timing_events[i], s);
 }
 
-}  // namespace opr
-
-using namespace opr;
-
-extern "C" {
-
-size_t opr_build_layout_workspace_size(int32_t B, int32_t L, int32_t n_convs, int32_t n_turns) {
-  if (B < 1 || L < 1 || n_convs < 0 || n_turns < 0) return 0;
-  if ((int64_t)B * L >= (int64_t)1 << 31) return 0;
-  return carve_layout_ws(nullptr, B, L, n_convs, n_turns, nullptr);
-}
-
-opr_status opr_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
-                            const int32_t *convs_per_row, const int32_t *turns_per_conv,
-                            const opr_turn *turns, void *workspace, size_t ws_bytes,
-                            const opr_layout *out, hipStream_t stream) {
+// Arguments of the layout builders, validated on the host before any HIP
+// call; on success *C and *T are the conversation and turn counts.
+static opr_status check_layout_args(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
+                                    const int32_t *convs_per_row, const int32_t *turns_per_conv,
+                                    const opr_turn *turns, const opr_layout *out, int64_t *C_out, int64_t *T_out) {
   if (B < 1 || L < 1) return OPR_E_INVALID;
   if ((int64_t)B * L >= (int64_t)1 << 31) return OPR_E_UNSUPPORTED;
   if (!valid_block(block_q) || !valid_block(block_k)) return OPR_E_UNSUPPORTED;
-  if (!convs_per_row || !workspace || !out) return OPR_E_INVALID;
+  if (!convs_per_row || !out) return OPR_E_INVALID;
   if (!out->tok_conv || !out->tok_turn || !out->tok_pos || !out->tok_type || !out->tok_slot ||
       !out->slot_tok || !out->slot_qiv || !out->slot_kiv || !out->tile_class || !out->sub_class ||
       !out->q_nnz || !out->q_list || !out->k_nnz || !out->k_list)
     return OPR_E_INVALID;
   if (out->order != OPR_ORDER_PACKED && out->order != OPR_ORDER_ATTENTION) return OPR_E_INVALID;
-  if (!aligned16(out->slot_qiv) || !aligned16(out->slot_kiv) || !aligned256(workspace)) return OPR_E_INVALID;
+  if (!aligned16(out->slot_qiv) || !aligned16(out->slot_kiv)) return OPR_E_INVALID;
   const int64_t MT = ((int64_t)L + block_q - 1) / block_q, NT = ((int64_t)L + block_k - 1) / block_k;
   if ((int64_t)B * MT * NT >= (int64_t)1 << 31) return OPR_E_UNSUPPORTED;
   // count conversations and turns, check every length and each row's capacity
@@ -322,9 +313,17 @@ opr_status opr_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block
       if (T >= (int64_t)1 << 30) return OPR_E_INVALID;
     }
   }
-  const size_t need = carve_layout_ws(nullptr, B, L, (int32_t)C, (int32_t)T, nullptr);
-  if (ws_bytes < need) return OPR_E_CAPACITY;
+  *C_out = C;
+  *T_out = T;
+  return OPR_OK;
+}
 
+// Copies the host segment arrays into the workspace and launches the layout
+// kernels (arguments already validated).
+static opr_status run_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
+                                   const int32_t *convs_per_row, const int32_t *turns_per_conv,
+                                   const opr_turn *turns, int64_t C, int64_t T, void *workspace,
+                                   const opr_layout *out, hipStream_t stream) {
   LayoutWs ws;
   carve_layout_ws(workspace, B, L, (int32_t)C, (int32_t)T, &ws);
   if (hipMemcpyAsync(ws.cpr, convs_per_row, sizeof(int32_t) * B, hipMemcpyHostToDevice, stream) != hipSuccess)
@@ -336,6 +335,76 @@ opr_status opr_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block
   if (launch_build_layout(B, L, block_q, block_k, (int32_t)C, (int32_t)T, ws, *out, stream) != hipSuccess)
     return OPR_E_HIP;
   return hip_status();
+}
+
+// The scratch of opr_build_layout_noalloc: a file-scope device array, one
+// copy on every GPU the library runs on (held until the process ends).  In
+// host code `scratch` names a host-side stand-in, not the device memory: the
+// first call on a device looks up that device's copy with
+// hipGetSymbolAddress (the device current) and keeps the address; every later
+// use goes through that address.  All calls on one device share it.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[OPR_LAYOUT_SCRATCH_BYTES];
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];
+
+static opr_status layout_scratch(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return OPR_E_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return OPR_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return OPR_E_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return OPR_OK;
+}
+
+}  // namespace opr
+
+using namespace opr;
+
+extern "C" {
+
+size_t opr_build_layout_workspace_size(int32_t B, int32_t L, int32_t n_convs, int32_t n_turns) {
+  if (B < 1 || L < 1 || n_convs < 0 || n_turns < 0) return 0;
+  if ((int64_t)B * L >= (int64_t)1 << 31) return 0;
+  return carve_layout_ws(nullptr, B, L, n_convs, n_turns, nullptr);
+}
+
+opr_status opr_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
+                            const int32_t *convs_per_row, const int32_t *turns_per_conv,
+                            const opr_turn *turns, void *workspace, size_t ws_bytes,
+                            const opr_layout *out, hipStream_t stream) {
+  int64_t C = 0, T = 0;
+  const opr_status st = check_layout_args(B, L, block_q, block_k, convs_per_row, turns_per_conv, turns, out, &C, &T);
+  if (st != OPR_OK) return st;
+  if (!workspace) return OPR_E_INVALID;
+  if (!aligned256(workspace)) return OPR_E_INVALID;
+  if (ws_bytes < carve_layout_ws(nullptr, B, L, (int32_t)C, (int32_t)T, nullptr)) return OPR_E_CAPACITY;
+  return run_build_layout(B, L, block_q, block_k, convs_per_row, turns_per_conv, turns, C, T, workspace, out, stream);
+}
+
+opr_status opr_build_layout_noalloc(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
+                                    const int32_t *convs_per_row, const int32_t *turns_per_conv,
+                                    const opr_turn *turns, const opr_layout *out, hipStream_t stream) {
+  int64_t C = 0, T = 0;
+  const opr_status st = check_layout_args(B, L, block_q, block_k, convs_per_row, turns_per_conv, turns, out, &C, &T);
+  if (st != OPR_OK) return st;
+  if (carve_layout_ws(nullptr, B, L, (int32_t)C, (int32_t)T, nullptr) > OPR_LAYOUT_SCRATCH_BYTES)
+    return OPR_E_CAPACITY;
+  void *ws = nullptr;
+  const opr_status ss = layout_scratch(&ws);
+  if (ss != OPR_OK) return ss;
+  return run_build_layout(B, L, block_q, block_k, convs_per_row, turns_per_conv, turns, C, T, ws, out, stream);
 }
 
 size_t opr_attn_workspace_size(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int is_bwd) {

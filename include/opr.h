@@ -150,6 +150,33 @@ opr_status opr_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block
  * turns in total (the sums of convs_per_row and turns_per_conv). */
 size_t opr_build_layout_workspace_size(int32_t B, int32_t L, int32_t n_convs, int32_t n_turns);
 
+/* Size of the fixed device scratch of opr_build_layout_noalloc: 32 MiB on
+ * every GPU the library runs on. */
+#define OPR_LAYOUT_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * opr_build_layout_noalloc - opr_build_layout for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace and allocates
+ * nothing (no hipMalloc, hipFree or allocating library call): its scratch is
+ * a fixed OPR_LAYOUT_SCRATCH_BYTES array in the library's device code, one
+ * copy per GPU, held until the process ends.
+ *
+ * Arguments, results and errors are those of opr_build_layout without
+ * workspace and ws_bytes, plus OPR_E_CAPACITY when
+ * opr_build_layout_workspace_size(B, L, n_convs, n_turns) exceeds
+ * OPR_LAYOUT_SCRATCH_BYTES (about 8 M packed tokens in total; checked
+ * before any HIP call, nothing is enqueued).  The first call on a device
+ * looks up that device's scratch with the device current; `stream` must
+ * belong to the current device.  All calls on one GPU share its scratch:
+ * calls that overlap on one GPU (other streams, other host threads) race
+ * and must be serialised by the caller.  Every scratch word a call reads is
+ * written earlier by the same call, so nothing needs clearing between calls.
+ */
+opr_status opr_build_layout_noalloc(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
+                                    const int32_t *convs_per_row, const int32_t *turns_per_conv,
+                                    const opr_turn *turns, const opr_layout *out, hipStream_t stream);
+
 /* Inputs shared by the forward and backward calls. */
 typedef struct {
   int32_t B, L, Hq, Hkv, D; /* D in {64, 128}; Hq % Hkv == 0; q head h reads kv

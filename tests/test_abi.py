@@ -30,7 +30,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(Bd):
     names = declared_entry_points()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     lib = ctypes.CDLL(Bd._LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -84,6 +84,31 @@ def test_build_layout_errors(Bd):
     odd.slot_kiv = FAKE + 8
     assert _build(Bd, out=odd) == Bd.OPR_E_INVALID
     assert _build(Bd, B=1 << 16, L=1 << 15, cpr=(0,) * (1 << 16)) == Bd.OPR_E_UNSUPPORTED
+
+
+def _build_noalloc(Bd, B=1, L=64, bq=128, bk=128, cpr=(1,), tpc=(1,), turns=((8, 12, 6, 6),), out=None):
+    cpr_a = (ctypes.c_int32 * max(1, len(cpr)))(*cpr)
+    tpc_a = (ctypes.c_int32 * max(1, len(tpc)))(*tpc)
+    turns_a = (Bd.OprTurn * max(1, len(turns)))(*[Bd.OprTurn(*t) for t in turns])
+    out = _layout_struct(Bd) if out is None else out
+    return Bd.LIB.opr_build_layout_noalloc(B, L, bq, bk, ctypes.addressof(cpr_a), ctypes.addressof(tpc_a),
+                                           ctypes.addressof(turns_a), ctypes.byref(out), None)
+
+
+def test_build_layout_noalloc_errors(Bd):
+    """The no-allocation variant validates like opr_build_layout and rejects a
+    request whose scratch would exceed OPR_LAYOUT_SCRATCH_BYTES, before any
+    HIP call."""
+    assert _build_noalloc(Bd, B=0) == Bd.OPR_E_INVALID
+    assert _build_noalloc(Bd, bq=48) == Bd.OPR_E_UNSUPPORTED
+    assert _build_noalloc(Bd, turns=((8, -1, 6, 6),)) == Bd.OPR_E_INVALID
+    assert _build_noalloc(Bd, L=31) == Bd.OPR_E_CAPACITY
+    assert _build_noalloc(Bd, out=_layout_struct(Bd, "k_list")) == Bd.OPR_E_INVALID
+    # 64 rows x 2^17 tokens: 32 MiB of per-token turn indices alone
+    big = 1 << 17
+    assert Bd.opr_build_layout_workspace_size(64, big, 1, 1) > Bd.OPR_LAYOUT_SCRATCH_BYTES
+    assert _build_noalloc(Bd, B=64, L=big, cpr=(1,) + (0,) * 63) == Bd.OPR_E_CAPACITY
+    assert Bd.opr_build_layout_workspace_size(8, 32768, 1, 1) <= Bd.OPR_LAYOUT_SCRATCH_BYTES
 
 
 def test_layout_workspace_size(Bd):
