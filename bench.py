@@ -35,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from block_sparse_masked_opr_amd import inputs as I  # noqa: E402  (no torch, no GPU)
+from block_sparse_masked_opr_amd import sequences as S  # noqa: E402
 
 PEAK_FP16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
@@ -332,8 +333,8 @@ def block_depth(torch, Bd, dev, Ns, steps):
     for N in Ns:
         conv = I.depth_conversation(N)
         rec = {"N": N, "d_model": dm}
-        for kind, rows in (("one_pass", [[conv]]), ("one_pass_elided", [[I.chunk_conversation(conv, 0, N, True)]]),
-                           ("n_pass", [I.npass_conversations(conv)])):
+        for kind, rows in (("one_pass", [[conv]]), ("one_pass_elided", [[S.chunk_conversation(conv, 0, N, True)]]),
+                           ("n_pass", [S.npass_conversations(conv)])):
             L = I.row_used(rows[0])
             r = BlockRunner(torch, Bd, rows, L, Hq, Hkv, D, dm, dev)
             rec[kind] = {"tokens": L, "ms": round(r.time_steps(steps, 1), 4)}
@@ -456,7 +457,7 @@ def depth_stages(Ns, steps=10):
     names = ("fwd_prologue", "attn_fwd", "bwd_prologue", "attn_dkdv", "attn_dq")
     for N in Ns:
         conv = I.depth_conversation(N)
-        for kind, rows in (("one_pass", [[conv]]), ("n_pass", [I.npass_conversations(conv)])):
+        for kind, rows in (("one_pass", [[conv]]), ("n_pass", [S.npass_conversations(conv)])):
             L = I.row_used(rows[0])
             t = device_inputs(torch, 1, L, Hq, Hkv, D, I.SEEDS["depth"][1], dev)
             r = Runner(torch, Bd, rows, L, Hq, Hkv, D, t, dev)
@@ -488,8 +489,8 @@ def depth_sweep(torch, Bd, dev, Ns, steps):
     for N in Ns:
         conv = I.depth_conversation(N)
         rec = {"N": N}
-        for kind, rows in (("one_pass", [[conv]]), ("one_pass_elided", [[I.chunk_conversation(conv, 0, N, True)]]),
-                           ("n_pass", [I.npass_conversations(conv)])):
+        for kind, rows in (("one_pass", [[conv]]), ("one_pass_elided", [[S.chunk_conversation(conv, 0, N, True)]]),
+                           ("n_pass", [S.npass_conversations(conv)])):
             L = I.row_used(rows[0])
             t = device_inputs(torch, 1, L, Hq, Hkv, D, I.SEEDS["depth"][1], dev)
             r = Runner(torch, Bd, rows, L, Hq, Hkv, D, t, dev)
@@ -528,9 +529,9 @@ def kpass_sweep(torch, Bd, dev, steps):
 
     out = []
     for K in (1, 2, 4, "N"):
-        out.append(run({"K": K, "policy": "equal", "elide_last_rin": False}, I.kpass_rows(K)))
+        out.append(run({"K": K, "policy": "equal", "elide_last_rin": False}, S.kpass_rows(K)))
     for K in (1, 2, 4):
-        out.append(run({"K": K, "policy": "equal", "elide_last_rin": True}, I.kpass_rows(K, elide_last_rin=True)))
+        out.append(run({"K": K, "policy": "equal", "elide_last_rin": True}, S.kpass_rows(K, elide_last_rin=True)))
     eq = [x for x in out if x["policy"] == "equal"]
     A = np.array([[x["pairs"], x["packed_tokens"]] for x in eq], dtype=np.float64)
     coef, *_ = np.linalg.lstsq(A, np.array([x["ms"] for x in eq]), rcond=None)
@@ -541,7 +542,7 @@ def kpass_sweep(torch, Bd, dev, steps):
         chunks = []
         for c in convs:
             plan, _ = Bd.opr_kpass_plan(c, max_tokens=cap, tokens_weight=weight, elide_last_rin=True)
-            chunks += [I.chunk_conversation(c, p["first_turn"], p["first_turn"] + p["n_turns"], True) for p in plan]
+            chunks += [S.chunk_conversation(c, p["first_turn"], p["first_turn"] + p["n_turns"], True) for p in plan]
         rec = {"K": None, "policy": "planned", "elide_last_rin": True, "cap": cap, "tokens_weight": round(weight, 2),
                "chunks": len(chunks)}
         out.append(run(rec, I.pack_first_fit_decreasing(chunks, L)))

@@ -1,8 +1,10 @@
 """Seeded synthetic inputs: conversation shapes, packed rows and tensors.
 
 This module is shared by the HIP path's tests/bench and by the oracle's tests.
-It holds no attention, mask or position arithmetic: it only draws segment
-lengths, groups conversations into rows, and draws random tensors.  Every
+It holds no attention, mask or position arithmetic and none of the method's
+sequence rules (the N-pass and K-pass turn lists are in ``sequences.py``): it
+only draws segment lengths, groups conversations into rows, and draws random
+tensors.  Every
 consumer (the oracle, the C ABI) derives tokens, positions and masks from the
 turn lists itself.
 
@@ -21,7 +23,9 @@ the MathChatSync-reasoning dataset, which is not available here:
 * ``packed_fwd`` - 1 row x 8192, N~U[2,6], h~U[16,128], t~U[64,512], r~U[32,256].
 * ``packed_fwd_bwd`` - 2 rows x 16384, same distributions.
 * ``depth``   - one conversation of N turns (h, t, r) = (128, 1024, 256).
-* ``kpass``   - rows of 32768, N~U[4,12], h~U[32,256], t~U[256,2048], r~U[64,512].
+* ``kpass``   - conversations with N~U[4,12], h~U[32,256], t~U[256,2048],
+  r~U[64,512] that fill 4 rows of 32768 tokens at K = 1 (the K-pass chunk
+  sequences built from them are in ``sequences.py``).
 * ``layout_batch`` - 64 rows x 32768 with the packed distributions (layout only).
 
 Lengths use ``numpy.random.Generator(PCG64(seed))``; ``U[a, b]`` is inclusive.
@@ -177,50 +181,6 @@ def depth_conversation(N: int, h: int = 128, t: int = 1024, r: int = 256) -> Con
     return [(h, t, r, r) for _ in range(N)]
 
 
-def npass_conversations(conv: Conversation) -> List[Conversation]:
-    """The N separate sequences of the N-pass formulation, as turn lists.
-
-    Pass i holds the human messages and responses of the earlier turns and the
-    whole of turn i: [h_1, r_1, ..., h_{i-1}, r_{i-1}, h_i, t_i, r_i].  Earlier
-    turns are written (h, 0, r, 0) (response as context, no reasoning) and turn i
-    as (h, t, 0, r) (reasoning and the response generated after it).
-    """
-    out = []
-    for i in range(len(conv)):
-        hist = [(h, 0, r_in, 0) for (h, _t, r_in, _r) in conv[:i]]
-        h, t, _r_in, r_out = conv[i]
-        out.append(hist + [(h, t, 0, r_out)])
-    return out
-
-
-def chunk_conversation(conv: Conversation, a: int, b: int, elide_last_rin: bool = False) -> Conversation:
-    """The sequence of a K-pass chunk that trains turns [a, b) of a conversation.
-
-    The turns before a are history written (h, 0, r_in, 0); turns a .. b-1 keep
-    every segment.  With elide_last_rin, turn b-1 loses its context copy r_in
-    (written (h, t, 0, r_out)), which no token of the sequence sees.
-    """
-    if not 0 <= a < b <= len(conv):
-        raise ValueError(f"chunk [{a}, {b}) of a {len(conv)}-turn conversation")
-    hist = [(h, 0, r_in, 0) for (h, _t, r_in, _r) in conv[:a]]
-    own = [tuple(x) for x in conv[a:b]]
-    if elide_last_rin:
-        h, t, _r_in, r_out = own[-1]
-        own[-1] = (h, t, 0, r_out)
-    return hist + own
-
-
-def kpass_conversations(conv: Conversation, K: int, elide_last_rin: bool = False) -> List[Conversation]:
-    """Split a conversation into K contiguous chunks of near-equal turn count.
-
-    Chunk k holds turns [floor(kN/K), floor((k+1)N/K)) (see chunk_conversation).
-    K is capped at N.
-    """
-    N = len(conv)
-    K = max(1, min(K, N))
-    return [chunk_conversation(conv, (k * N) // K, ((k + 1) * N) // K, elide_last_rin) for k in range(K)]
-
-
 def _kpass_sampler(rng):
     return sample_conversation(rng, (4, 12), (32, 256), (256, 2048), (64, 512))
 
@@ -239,15 +199,6 @@ def kpass_base_conversations(seed: int = 401, rows: int = 4, L: int = KPASS_ROW_
 
     packed = pack_greedy(rng, rows, L, sampler)
     return [c for row in packed for c in row]
-
-
-def kpass_rows(K, seed: int = 401, L: int = KPASS_ROW_LEN, elide_last_rin: bool = False) -> List[Row]:
-    """Rows of L tokens for K in {1, 2, 4, ...} or K == 'N' (N-pass)."""
-    convs = kpass_base_conversations(seed, L=L)
-    chunks = []
-    for c in convs:
-        chunks.extend(npass_conversations(c) if K == "N" else kpass_conversations(c, int(K), elide_last_rin))
-    return pack_first_fit_decreasing(chunks, L)
 
 
 # ----------------------------------------------------------------------------

@@ -505,6 +505,63 @@ def attn_rows(q, k, v, do, lay, b: int, rows, theta: float, scale: float = None)
     return O, LSE, dQ
 
 
+def attn_cols(q, k, v, do, lay, b: int, cols, theta: float, scale: float = None, row_chunk: int = 512):
+    """dK and dV of the listed key tokens of row b alone, in fp64.
+
+    The definition of attn_bwd restricted to some keys, for rows too long for
+    the whole oracle.  A key j of conversation c is seen by the queries p of c
+    with M[p, j]; for each q head h of its kv group
+        P_pj  = exp(scale q'_p . k'_j - LSE_p)     (LSE_p over p's whole row)
+        dS_pj = P_pj (dO_p . v_j - Delta_p),        Delta_p = dO_p . O_p,
+    and dv_j = sum_h sum_p P_pj dO_p, dk_j = R(pos_j)^T scale sum_h sum_p dS_pj q'_p.
+    Every query row that sees a listed key is computed whole (its softmax
+    needs all of its keys), row_chunk rows at a time.  PAD keys get zeros.
+    Returns dK [n, Hkv, D], dV [n, Hkv, D] in the order of ``cols``.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    cols = np.asarray(cols, dtype=np.int64)
+    Hq, D = q.shape[2], q.shape[3]
+    Hkv = k.shape[2]
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    dK = np.zeros((len(cols), Hkv, D))
+    dV = np.zeros((len(cols), Hkv, D))
+    conv = lay["conv"][b, cols]
+    for c in np.unique(conv[conv >= 0]):
+        sel = np.nonzero(conv == c)[0]
+        a, e = conv_range(lay, b, int(c))
+        n = e - a
+        jl = cols[sel] - a                                   # conversation-local key indices
+        pos = lay["pos"][b, a:e]
+        kr = rope(k[b, a:e], pos, theta)
+        qr = rope(q[b, a:e], pos, theta)
+        # the queries that see at least one listed key
+        seen = np.zeros(n, dtype=bool)
+        for r0 in range(0, n, row_chunk):
+            seen[r0:r0 + row_chunk] = conv_mask(lay, b, int(c), qidx=np.arange(r0, min(n, r0 + row_chunk)))[:, jl].any(axis=1)
+        rows_all = np.nonzero(seen)[0]
+        dkr = np.zeros((len(sel), Hkv, D))
+        for r0 in range(0, len(rows_all), row_chunk):
+            rows = rows_all[r0:r0 + row_chunk]
+            M = conv_mask(lay, b, int(c), qidx=rows)         # [nr, n]
+            for h in range(Hq):
+                kv = h // g
+                S = np.where(M, scale * (qr[rows, h] @ kr[:, kv].T), -np.inf)
+                m = S.max(axis=1, keepdims=True)
+                P = np.exp(S - m)
+                P = P / P.sum(axis=1, keepdims=True)
+                O = P @ v[b, a:e, kv]
+                dO = do[b, a + rows, h]
+                delta = (dO * O).sum(axis=1, keepdims=True)
+                Pj = P[:, jl]                                # [nr, nsel]
+                dPj = dO @ v[b, cols[sel], kv].T
+                dSj = Pj * (dPj - delta)
+                dV[sel, kv] += Pj.T @ dO
+                dkr[:, kv] += scale * (dSj.T @ qr[rows, h])
+        dK[sel] = rope_transpose(dkr, pos[jl], theta)
+    return dK, dV
+
+
 def _seg_index(lay, b, c):
     """{(turn, type): packed indices} for conversation c of row b."""
     a, e = conv_range(lay, b, c)

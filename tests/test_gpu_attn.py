@@ -26,6 +26,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 from block_sparse_masked_opr_amd import inputs as I  # noqa: E402
+from block_sparse_masked_opr_amd import sequences as S  # noqa: E402
 from oracle import opr_oracle as O  # noqa: E402
 from tests.helpers import MAX_ABS, MEAN_REL, assert_close, bf16_f64, errors, from_device_bf16, to_device_bf16  # noqa: E402
 
@@ -265,7 +266,7 @@ def test_npass_rows_match_onepass(B):
     t = I.make_tensors(1, L1, 4, 2, 128, seed=5150)
     lay1 = O.layout([[conv]], L1)
     passes = O.npass_index(lay1, 0, 0)
-    np_rows = [[I.npass_conversations(conv)[i] for i in range(len(conv))]]
+    np_rows = [[S.npass_conversations(conv)[i] for i in range(len(conv))]]
     Ln = sum(len(p["idx"]) for p in passes)
     idx = np.concatenate([p["idx"] for p in passes])
     tn = {n: np.ascontiguousarray(t[n][:, idx]) for n in t}

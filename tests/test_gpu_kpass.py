@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 from block_sparse_masked_opr_amd import inputs as I  # noqa: E402
+from block_sparse_masked_opr_amd import sequences as S  # noqa: E402
 from oracle import opr_oracle as O  # noqa: E402
 from tests.helpers import assert_close  # noqa: E402
 from tests.test_gpu_attn import compare_full, run_gpu  # noqa: E402
@@ -41,7 +42,7 @@ def test_planned_chunk_rows(B):
         print(f"[kpass] {len(c)} turns, cap {cap}: chunks {[(p['first_turn'], p['n_turns']) for p in plan]}",
               flush=True)
         for p in plan:
-            chunks.append(I.chunk_conversation(c, p["first_turn"], p["first_turn"] + p["n_turns"], True))
+            chunks.append(S.chunk_conversation(c, p["first_turn"], p["first_turn"] + p["n_turns"], True))
     L = max(I.conv_len(x) for x in chunks) + 70
     rows = I.pack_first_fit_decreasing(chunks, L)
     t = I.make_tensors(len(rows), L, 4, 2, 128, seed=4343)
@@ -70,7 +71,7 @@ def test_chunks_reproduce_onepass(B):
     acc = {n: np.zeros_like(g1[n]) for n in ("dq", "dk", "dv")}
     for p in plan:
         a, b = p["first_turn"], p["first_turn"] + p["n_turns"]
-        seq = I.chunk_conversation(conv, a, b, True)
+        seq = S.chunk_conversation(conv, a, b, True)
         n = I.conv_len(seq)
         assert n == p["tokens"]
         layc = O.layout([[seq]], n)

@@ -14,6 +14,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 from block_sparse_masked_opr_amd import inputs as I  # noqa: E402
+from block_sparse_masked_opr_amd import sequences as S  # noqa: E402
 from oracle import opr_oracle as O  # noqa: E402
 
 
@@ -106,13 +107,13 @@ def test_depth(B, N):
     # schedule, which the device computes from them
     check_layout(B, [[conv]], I.conv_len(conv), 128, 128, f"depth 1-pass N={N}", intervals=N <= 8)
     if N <= 8:
-        np_convs = I.npass_conversations(conv)
+        np_convs = S.npass_conversations(conv)
         L = sum(I.conv_len(c) for c in np_convs)
         check_layout(B, [np_convs], L, 128, 128, f"depth N-pass N={N}")
 
 
 def test_kpass_rows(B):
-    rows = I.kpass_rows(2)
+    rows = S.kpass_rows(2)
     check_layout(B, rows, I.KPASS_ROW_LEN, 128, 128, "kpass K=2")
 
 

@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 from block_sparse_masked_opr_amd import inputs as I  # noqa: E402
+from block_sparse_masked_opr_amd import sequences as S  # noqa: E402
 from oracle import opr_oracle as O  # noqa: E402
 from tests.helpers import assert_close, bf16_f64, from_device_bf16, to_device_bf16  # noqa: E402
 
@@ -198,7 +199,7 @@ def test_theorem_loss_and_gradients_on_gpu(B):
     w_bits = I.round_to_bf16_bits((rng.standard_normal((V, Hq * D)) / np.sqrt(Hq * D) * 4).astype(np.float32))
     passes = O.npass_index(lay1, 0, 0)
     idx = np.concatenate([p["idx"] for p in passes])
-    np_rows = [[I.npass_conversations(conv)[i] for i in range(len(conv))]]
+    np_rows = [[S.npass_conversations(conv)[i] for i in range(len(conv))]]
     tn = {n: np.ascontiguousarray(t[n][:, idx]) for n in t}
     print("[loss] theorem: one pass", flush=True)
     g1 = _gpu_chain(B, [[conv]], L1, t, w_bits, labels1)

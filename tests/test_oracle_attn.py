@@ -164,6 +164,50 @@ def test_attn_rows_vs_sdpa(seed):
         np.testing.assert_allclose(dq, rdq[b, sel], atol=1e-11)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_attn_cols_vs_sdpa_and_full_backward(seed):
+    """The oracle's single-key gradients (dK, dV of listed keys, for rows too
+    long for the whole oracle) against the torch reference (SDPA + autograd)
+    and against the full-matrix backward, on listed keys of small packed rows
+    (PAD keys, empty segments and several query chunks included)."""
+    rng = np.random.default_rng(950 + seed)
+    rows = [[[(int(rng.integers(0, 7)), int(rng.integers(0, 9)), *([int(rng.integers(0, 6))] * 2))
+              for _ in range(int(rng.integers(1, 4)))] for _ in range(int(rng.integers(1, 3)))] for _ in range(2)]
+    L = max(I.row_used(r) for r in rows) + 3
+    Hq, Hkv, D = 4, 2, 16
+    lay = O.layout(rows, L)
+    q, k, v = (rng.standard_normal((2, L, h, D)) for h in (Hq, Hkv, Hkv))
+    do = rng.standard_normal((2, L, Hq, D))
+    _, _, _, rdk, rdv = _torch_reference(q, k, v, do, lay, THETA)
+    _, fdk, fdv = O.attn_bwd(q, k, v, do, lay, THETA)
+    for b in range(2):
+        sel = rng.permutation(L)[: L // 2 + 1]
+        dk, dv = O.attn_cols(q, k, v, do, lay, b, sel, THETA, row_chunk=int(rng.integers(1, 9)))
+        np.testing.assert_allclose(dk, rdk[b, sel], atol=1e-11)
+        np.testing.assert_allclose(dv, rdv[b, sel], atol=1e-11)
+        np.testing.assert_allclose(dk, fdk[b, sel], atol=1e-12)
+        np.testing.assert_allclose(dv, fdv[b, sel], atol=1e-12)
+
+
+def test_attn_cols_invariants():
+    """Properties that hold at any size: every query's probabilities sum to 1,
+    so the dV of all keys sums to the sum of dO over the group's heads and the
+    live queries; every query's dS sums to 0, so the rotated dK sums to 0."""
+    rows = [[[(12, 20, 9, 9), (7, 15, 6, 6), (10, 4, 8, 8)]]]
+    L = I.row_used(rows[0]) + 4
+    Hq, Hkv, D = 4, 1, 16
+    lay = O.layout(rows, L)
+    rng = np.random.default_rng(77)
+    q, k, v = (rng.standard_normal((1, L, h, D)) for h in (Hq, Hkv, Hkv))
+    do = rng.standard_normal((1, L, Hq, D))
+    dk, dv = O.attn_cols(q, k, v, do, lay, 0, np.arange(L), THETA, row_chunk=16)
+    live = lay["type"][0] != O.PAD
+    np.testing.assert_allclose(dv[live, 0].sum(axis=0), do[0, live].sum(axis=(0, 1)), atol=1e-10)
+    dkr = O.rope(dk[live], lay["pos"][0, live], THETA)           # R(pos) dK: back in the rotated frame
+    np.testing.assert_allclose(dkr.sum(axis=0), 0.0, atol=1e-10)
+    assert (dk[~live] == 0).all() and (dv[~live] == 0).all()
+
+
 def test_bwd_with_given_o():
     """Delta from a given forward output: with the exact O it is the default
     backward; with O rounded to bf16 only the terms through Delta move."""
@@ -354,7 +398,7 @@ def test_theorem_tiny_loss_and_gradients():
 def test_kpass_with_k_equal_n_reproduces_npass_rows():
     """K = N chunks: the t and r_out rows of chunk i equal pass i of the N-pass."""
     conv = [(3, 4, 2, 2), (2, 5, 3, 3), (4, 2, 2, 2)]
-    chunks = I.kpass_conversations(conv, len(conv))
+    chunks = [O.kpass_chunk(conv, i, i + 1, False) for i in range(len(conv))]
     full = O.layout([[conv]], I.conv_len(conv))
     rng = np.random.default_rng(3)
     D = 16

@@ -262,17 +262,6 @@ def test_npass_sequence_positions(conv):
         np.testing.assert_array_equal(lay["pos"][0][p["idx"]], np.arange(len(p["idx"])))
 
 
-def test_npass_turn_lists_are_causal():
-    """The N-pass turn lists (history (h,0,r,0), last turn (h,t,0,r)) are
-    ordinary causal sequences under the rules."""
-    conv = [(3, 4, 2, 2), (2, 5, 3, 3), (4, 1, 2, 2)]
-    for p in I.npass_conversations(conv):
-        n = I.conv_len(p)
-        lay = O.layout([[p]], n)
-        M = O.dense_mask(lay, 0)
-        np.testing.assert_array_equal(M, np.tril(np.ones((n, n), dtype=bool)))
-
-
 def test_useful_pairs_closed_form():
     """P = sum over non-PAD tokens of (pos + 1) (each query sees positions 0..pos)."""
     rows = I.packed_rows(I.Shape("s", 1, 2048, 1, 1, 64), 7)
