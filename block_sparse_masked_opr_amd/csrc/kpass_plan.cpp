@@ -18,7 +18,9 @@
 // start of turn l is the same in every chunk sequence that contains it:
 // S_l = sum over m < l of (h_m + r_in_m).  Chunk costs therefore come from
 // prefix sums, and a dynamic program over turn boundaries finds the optimum in
-// O(K * N^2) (exactly K chunks) or O(N^2) (any number).
+// O(K * N^2) time and O(K * N) memory (exactly K chunks), or in O(N^2) time
+// and O(N) memory (any number: one layer over (cost, chunks), compared in that
+// order, so that ties go to fewer chunks).
 //
 // The context copy r_in of a chunk's last turn is seen by no query of its
 // sequence (only later turns see a turn's r_in, and it carries no loss), so
@@ -27,6 +29,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <new>
 #include <vector>
 
 #include "opr.h"
@@ -81,6 +84,94 @@ inline Chunk chunk_of(const Prefix &P, int a, int b, bool elide) {
   return c;
 }
 
+// Size limits: N <= kMaxTurns turns for any number of chunks (O(N^2)); for
+// exactly K chunks K * N^2 <= kMaxWork (time) as well.
+constexpr int32_t kMaxTurns = 1 << 16;
+constexpr int64_t kMaxWork = (int64_t)1 << 33;
+
+opr_status plan(const opr_turn *turns, int32_t n_turns, int32_t n_chunks, int32_t max_tokens, double tokens_weight,
+                int32_t elide_last_rin, opr_chunk *chunks, int32_t *n_out, double *cost) {
+  const int N = n_turns;
+  const bool elide = elide_last_rin != 0;
+  const Prefix P = prefixes(turns, N);
+  const int64_t cap = max_tokens > 0 ? max_tokens : std::numeric_limits<int64_t>::max();
+  const double inf = std::numeric_limits<double>::infinity();
+  auto chunk_cost = [&](const Chunk &c) { return (double)c.pairs + tokens_weight * (double)c.tokens; };
+
+  std::vector<int> ends;  // chunk boundaries 0 = ends[0] < ... < ends[K] = N
+  double total = inf;
+  if (n_chunks == 0) {
+    // best[j]: least (cost, chunks) of turns [0, j), compared in that order
+    std::vector<double> bc(N + 1, inf);
+    std::vector<int32_t> bn(N + 1, std::numeric_limits<int32_t>::max()), from(N + 1, -1);
+    bc[0] = 0.0;
+    bn[0] = 0;
+    for (int j = 1; j <= N; ++j) {
+      for (int i = 0; i < j; ++i) {
+        if (bc[i] == inf) continue;
+        const Chunk c = chunk_of(P, i, j, elide);
+        if (c.tokens > cap) continue;
+        const double v = bc[i] + chunk_cost(c);
+        const int32_t nv = bn[i] + 1;
+        if (v < bc[j] || (v == bc[j] && nv < bn[j])) {
+          bc[j] = v;
+          bn[j] = nv;
+          from[j] = i;
+        }
+      }
+    }
+    if (bc[N] == inf) return OPR_E_CAPACITY;
+    total = bc[N];
+    for (int j = N; j > 0; j = from[j]) ends.push_back(j);
+    ends.push_back(0);
+    std::vector<int>(ends.rbegin(), ends.rend()).swap(ends);
+  } else {
+    // best[k][j]: least cost of turns [0, j) in exactly k chunks
+    const int K = n_chunks;
+    std::vector<double> best((size_t)(K + 1) * (N + 1), inf);
+    std::vector<int32_t> from((size_t)(K + 1) * (N + 1), -1);
+    auto at = [&](int k, int j) { return (size_t)k * (N + 1) + j; };
+    best[at(0, 0)] = 0.0;
+    for (int k = 1; k <= K; ++k) {
+      for (int j = k; j <= N; ++j) {
+        double bj = inf;
+        int arg = -1;
+        for (int i = k - 1; i < j; ++i) {
+          const double bi = best[at(k - 1, i)];
+          if (bi == inf) continue;
+          const Chunk c = chunk_of(P, i, j, elide);
+          if (c.tokens > cap) continue;
+          const double v = bi + chunk_cost(c);
+          if (v < bj) {
+            bj = v;
+            arg = i;
+          }
+        }
+        best[at(k, j)] = bj;
+        from[at(k, j)] = arg;
+      }
+    }
+    if (best[at(K, N)] == inf) return OPR_E_CAPACITY;
+    total = best[at(K, N)];
+    ends.assign(K + 1, 0);
+    ends[K] = N;
+    for (int k = K; k >= 1; --k) ends[k - 1] = from[at(k, ends[k])];
+  }
+
+  const int K = (int)ends.size() - 1;
+  for (int k = 0; k < K; ++k) {
+    const Chunk c = chunk_of(P, ends[k], ends[k + 1], elide);
+    chunks[k].first_turn = ends[k];
+    chunks[k].n_turns = ends[k + 1] - ends[k];
+    chunks[k].tokens = (int32_t)c.tokens;
+    chunks[k].rin_elided = elide ? 1 : 0;
+    chunks[k].pairs = c.pairs;
+  }
+  *n_out = K;
+  if (cost) *cost = total;
+  return OPR_OK;
+}
+
 }  // namespace
 
 extern "C" opr_status opr_kpass_plan(const opr_turn *turns, int32_t n_turns, int32_t n_chunks,
@@ -97,62 +188,11 @@ extern "C" opr_status opr_kpass_plan(const opr_turn *turns, int32_t n_turns, int
   }
   // every chunk holds at most each turn's segments once
   if (total > std::numeric_limits<int32_t>::max()) return OPR_E_INVALID;
-
-  const int N = n_turns;
-  const bool elide = elide_last_rin != 0;
-  const Prefix P = prefixes(turns, N);
-  const int64_t cap = max_tokens > 0 ? max_tokens : std::numeric_limits<int64_t>::max();
-  const double inf = std::numeric_limits<double>::infinity();
-  auto chunk_cost = [&](const Chunk &c) { return (double)c.pairs + tokens_weight * (double)c.tokens; };
-
-  // best[k][j]: least cost of turns [0, j) in exactly k chunks (k = 0 .. Kmax);
-  // with n_chunks == 0 the answer is the least over k, fewer chunks on ties.
-  const int Kmax = n_chunks > 0 ? n_chunks : N;
-  std::vector<double> best((size_t)(Kmax + 1) * (N + 1), inf);
-  std::vector<int32_t> from((size_t)(Kmax + 1) * (N + 1), -1);
-  auto at = [&](int k, int j) { return (size_t)k * (N + 1) + j; };
-  best[at(0, 0)] = 0.0;
-  for (int k = 1; k <= Kmax; ++k) {
-    for (int j = k; j <= N; ++j) {
-      double bj = inf;
-      int arg = -1;
-      for (int i = k - 1; i < j; ++i) {
-        const double bi = best[at(k - 1, i)];
-        if (bi == inf) continue;
-        const Chunk c = chunk_of(P, i, j, elide);
-        if (c.tokens > cap) continue;
-        const double v = bi + chunk_cost(c);
-        if (v < bj) {
-          bj = v;
-          arg = i;
-        }
-      }
-      best[at(k, j)] = bj;
-      from[at(k, j)] = arg;
-    }
+  if (n_turns > kMaxTurns) return OPR_E_UNSUPPORTED;
+  if (n_chunks > 0 && (int64_t)n_chunks * n_turns * n_turns > kMaxWork) return OPR_E_UNSUPPORTED;
+  try {
+    return plan(turns, n_turns, n_chunks, max_tokens, tokens_weight, elide_last_rin, chunks, n_out, cost);
+  } catch (const std::bad_alloc &) {
+    return OPR_E_UNSUPPORTED;  // the tables do not fit in host memory; nothing was written
   }
-  int K = -1;
-  if (n_chunks > 0) {
-    if (best[at(n_chunks, N)] != inf) K = n_chunks;
-  } else {
-    for (int k = 1; k <= N; ++k)
-      if (best[at(k, N)] < (K < 0 ? inf : best[at(K, N)])) K = k;
-  }
-  if (K < 0) return OPR_E_CAPACITY;
-
-  // walk the boundaries back from turn N
-  std::vector<int> ends(K + 1);
-  ends[K] = N;
-  for (int k = K; k >= 1; --k) ends[k - 1] = from[at(k, ends[k])];
-  for (int k = 0; k < K; ++k) {
-    const Chunk c = chunk_of(P, ends[k], ends[k + 1], elide);
-    chunks[k].first_turn = ends[k];
-    chunks[k].n_turns = ends[k + 1] - ends[k];
-    chunks[k].tokens = (int32_t)c.tokens;
-    chunks[k].rin_elided = elide ? 1 : 0;
-    chunks[k].pairs = c.pairs;
-  }
-  *n_out = K;
-  if (cost) *cost = best[at(K, N)];
-  return OPR_OK;
 }

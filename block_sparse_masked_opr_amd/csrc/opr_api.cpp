@@ -561,7 +561,10 @@ opr_status opr_token_ce(int32_t B, int32_t L, int32_t F, int32_t V, const void *
 }
 
 const char *opr_status_string(opr_status s) {
-  switch (s) {
+  // a C caller may pass any int: read the bytes, never an out-of-range enum value
+  int32_t v;
+  memcpy(&v, &s, sizeof(v));
+  switch (v) {
     case OPR_OK: return "OPR_OK";
     case OPR_E_INVALID: return "OPR_E_INVALID: invalid argument";
     case OPR_E_CAPACITY: return "OPR_E_CAPACITY: row longer than L or workspace too small";

@@ -423,9 +423,14 @@ typedef struct {
  *                 entries [0, *n_out) are written in turn order.
  *  n_out          host, the number of chunks.
  *  cost           host, may be NULL: the minimised objective.
+ * Time and memory: O(n_turns^2) time and O(n_turns) memory for any number
+ * of chunks, O(n_chunks * n_turns^2) time and O(n_chunks * n_turns) memory
+ * for exactly n_chunks.
  * Errors: OPR_E_INVALID (null pointer, counts, lengths, weight),
  * OPR_E_CAPACITY (no split meets max_tokens: some turn's sequence alone is
- * longer, or n_chunks chunks cannot all fit).  On error nothing is written.
+ * longer, or n_chunks chunks cannot all fit), OPR_E_UNSUPPORTED (n_turns >
+ * 65536, n_chunks * n_turns^2 > 2^33, or the tables do not fit in host
+ * memory).  On error nothing is written.
  */
 opr_status opr_kpass_plan(const opr_turn *turns, int32_t n_turns, int32_t n_chunks, int32_t max_tokens,
                           double tokens_weight, int32_t elide_last_rin, opr_chunk *chunks, int32_t *n_out,

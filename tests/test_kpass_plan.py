@@ -114,6 +114,32 @@ def test_plan_errors(Bd):
     assert [c["tokens"] for c in ch] == [15, 16]
 
 
+def test_plan_long_conversation_and_limits(Bd):
+    """Any number of chunks runs in O(N^2) time and O(N) memory: a 3000-turn
+    conversation plans quickly, every chunk within the cap and the chunks
+    covering the turns in order.  Requests past the documented limits are
+    refused (OPR_E_UNSUPPORTED), never an exception or an allocation failure
+    escaping the C ABI."""
+    import time
+    rng = np.random.default_rng(5)
+    # short messages and responses, long reasoning: the history stays small
+    conv = [(int(rng.integers(0, 4)), int(rng.integers(0, 60)), *([int(rng.integers(0, 4))] * 2)) for _ in range(3000)]
+    cap = I.conv_len(conv) // 3
+    t0 = time.time()
+    ch, cost = Bd.opr_kpass_plan(conv, max_tokens=cap, elide_last_rin=True)
+    assert time.time() - t0 < 20.0
+    assert len(ch) > 1 and ch[0]["first_turn"] == 0 and sum(c["n_turns"] for c in ch) == 3000
+    assert all(c["tokens"] <= cap for c in ch)
+    assert all(ch[i]["first_turn"] + ch[i]["n_turns"] == ch[i + 1]["first_turn"] for i in range(len(ch) - 1))
+    assert cost == sum(c["pairs"] for c in ch)          # tokens_weight 0: the cost is the pairs
+    with pytest.raises(Bd.OprError) as e:
+        Bd.opr_kpass_plan(conv, n_chunks=2000)           # 2000 * 3000^2 > 2^33
+    assert e.value.status == Bd.OPR_E_UNSUPPORTED
+    with pytest.raises(Bd.OprError) as e:
+        Bd.opr_kpass_plan([(1, 1, 1, 1)] * 65537)
+    assert e.value.status == Bd.OPR_E_UNSUPPORTED
+
+
 def _own_index(lay_c, lay_1):
     """For each token of a chunk sequence, the one-pass token with the same
     (turn, type, offset in its segment)."""

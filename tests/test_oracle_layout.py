@@ -134,6 +134,19 @@ def test_schedule_brute_force(rows, extra, bq, bk):
         _check_schedule(O.dense_mask(lay, b), O.schedule(lay, b, bq, bk), L, bq, bk)
 
 
+@settings(max_examples=60, deadline=None)
+@given(rows=st.lists(row_st, min_size=1, max_size=2), extra=st.integers(0, 9),
+       bq=st.sampled_from([1, 2, 4, 8]), bk=st.sampled_from([1, 2, 4, 8]))
+def test_schedule_brute_force_small_tiles(rows, extra, bq, bk):
+    """The class rule at tile sizes where tiles one pair short of full (a 2 x 2
+    tile on a causal diagonal holds 3 of 4 pairs) and one pair from empty are
+    common: FULL only with every pair allowed, EMPTY only with none."""
+    L = _L_for(rows, extra)
+    lay = O.layout(rows, L)
+    for b in range(len(rows)):
+        _check_schedule(O.dense_mask(lay, b), O.schedule(lay, b, bq, bk), L, bq, bk)
+
+
 # ---------------------------------------------------------------------------
 # attention order (a reordering of this library; the mask itself is unchanged)
 # ---------------------------------------------------------------------------
