@@ -150,6 +150,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return *reinterpret_cast<uint16_t *>(&h);
 }
 
+// RoPE (rotate-half) of one rotation pair (x1, x2) = (x_j, x_{j+D/2}) by the
+// angle's (cos, sin): (x1 cos - x2 sin, x2 cos + x1 sin), with explicit fused
+// multiply-adds, so that every kernel that rotates q or k rounds the same way.
+__device__ __forceinline__ void rope_pair(float x1, float x2, float2 cs, float &lo, float &hi) {
+  lo = fmaf(x1, cs.x, -(x2 * cs.y));
+  hi = fmaf(x2, cs.x, x1 * cs.y);
+}
+
 // Exponent e with max_abs * 2^e in [2^14, 2^15) (0 for an all-zero plane),
 // clamped to [kExpMin, kExpMax].  max_abs is stored as the bits of a
 // non-negative float (so that atomicMax on the bits orders them).
@@ -381,20 +389,22 @@ struct AttnParams {
   // fp16 bits [B][H][Lp][D]: k' and v with one power-of-two scale per
   // (row, kv head) plane, q' and dout with one per 16-slot tile of each
   // (row, q head).  The dQ kernel writes dor; the dK/dV kernel reads it.
-  const uint16_t *qr, *kr, *vr;
+  uint16_t *qr;                // written by the forward kernel (or the q pack)
+  const uint16_t *kr, *vr;
   uint16_t *dor;
   // plane maxima (float bits) [B][Hkv] of k', v
   const uint32_t *mk, *mv;
   // row exponents [B][Hq][Lp] of q' and of dout (edoq, written by dQ), and
   // their minima over each kTile-slot tile [B][Hq][MTS]
-  const int32_t *eqq, *eqt;
+  int32_t *eqq, *eqt;
   int32_t *edoq, *edot;
   int32_t MTS;                 // tiles per row: Lp / kTile
   // [B][Hq][Lp], written by the dQ kernel for dK/dV (units in attn_bwd.hip;
   // lse2 is +inf where no key)
   float *dsc, *lse2, *fsq;
-  // backward inputs in token order: o, dout bf16 [B][L][Hq][D], lse [B][Hq][L]
-  const uint16_t *o_in, *dout_in;
+  // inputs in token order: q (forward), o, dout bf16 [B][L][Hq][D], lse
+  // [B][Hq][L] (backward)
+  const uint16_t *q_in, *o_in, *dout_in;
   const float *lse_in;
 };
 

@@ -1,7 +1,9 @@
 // Forward kernel of the one-pass masked attention (gfx950).
 //
 // The kernel runs in attention order: q-tile m is query slots m*128 .. +127
-// and K/V rows are slots; results go to the slot's token.  One workgroup of
+// and K/V rows are slots; results go to the slot's token.  Each lane first
+// converts its own query row (RoPE, fp16 with the row's exponent) and writes
+// it to the q' plane that the backward reads.  One workgroup of
 // 4 waves per (128-slot query tile m, q head h, row b); wave w owns query
 // slots m*128 + 32w .. +31, one per lane column.  Work items start longest
 // first, spread over the XCDs, with the q heads of one kv group side by side
@@ -51,18 +53,67 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
   const int tid = threadIdx.x, w = uniform(tid >> 6), lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int q = m * 128 + 32 * w + li;
   const int64_t kvplane = (int64_t)b * p.Hkv + kvh;
-  // q' scale of the lane's row (query slot q)
-  const int eq = p.eqq[((int64_t)b * p.Hq + h) * p.Lp + q];
   const int ek = plane_exponent(p.mk[kvplane]);
   const int ev = plane_exponent(p.mv[kvplane]);
-  const float fs = ldexpf(p.scale_log2, -(eq + ek));  // raw score -> log2 units
 
+  // Prologue: q of the lane's token (its half of the head dims, the partner
+  // lane l ^ 32 holds the other half), rotated by RoPE at the slot's position
+  // id, as fp16 with the row's own exponent eq; written to the q' plane with
+  // eq (and eq's minimum over each 16-slot tile) for the backward.  Lane g
+  // holds dims 16 s + 8 g + e, so each rotation pair (d, d + D/2) is the
+  // lane's own (k-steps s and s + NS/2).
   f16x8 qb[NS];
+  int eq;
   {
-    const uint16_t *qrow = p.qr + (((int64_t)b * p.Hq + h) * p.Lp + q) * D;
+    const int64_t hq_row = ((int64_t)b * p.Hq + h) * p.Lp + q;
+    const int32_t tok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
+    float x[NS][8];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qb[s] = ld_f16x8(qrow + 16 * s + 8 * g);
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[s][e] = 0.0f;
+    if (tok >= 0) {
+      const uint16_t *src = p.q_in + (((int64_t)b * p.L + tok) * p.Hq + h) * D + 8 * g;
+      uint4 wv[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) wv[s] = *reinterpret_cast<const uint4 *>(src + 16 * s);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint16_t *e16 = reinterpret_cast<const uint16_t *>(&wv[s]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[s][e] = bf16_to_f32(e16[e]);
+      }
+      const float2 *cs = p.rope + ((int64_t)b * p.Lp + q) * (D / 2) + 8 * g;
+#pragma unroll
+      for (int s = 0; s < NS / 2; ++s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x1 = x[s][e], x2 = x[s + NS / 2][e];
+          rope_pair(x1, x2, cs[16 * s + e], x[s][e], x[s + NS / 2][e]);
+        }
+      }
+    }
+    uint32_t mx = 0u;  // float bits of the row's largest |q'| (integer order)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = max(mx, __float_as_uint(fabsf(x[s][e])));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+    eq = mx > 0u ? plane_exponent(mx) : kExpMax;
+    uint16_t *dst = p.qr + hq_row * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[s][e] = (_Float16)ldexpf(x[s][e], eq);
+      *reinterpret_cast<f16x8 *>(dst + 16 * s) = qb[s];
+    }
+    int emin = eq;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) emin = min(emin, __shfl_xor(emin, off));
+    if (g == 0) p.eqq[hq_row] = eq;
+    if ((lane & 47) == 0) p.eqt[((int64_t)b * p.Hq + h) * p.MTS + q / kTile] = emin;
   }
+  const float fs = ldexpf(p.scale_log2, -(eq + ek));  // raw score -> log2 units
   // key slots this query sees: [iv.x, iv.y) and [iv.z, iv.w)
   const int4 iv = q < p.L ? p.qiv[(int64_t)b * p.L + q] : make_int4(0, 0, 0, 0);
   OperandOffsets<D> of;
@@ -208,6 +259,7 @@ hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, f
                                   const AttnWs &ws, hipStream_t s) {
   AttnParams p;
   fill_params(in, scale, ws, &p);
+  p.q_in = static_cast<const uint16_t *>(in.q);
   const unsigned grid = (unsigned)q_grid((int64_t)in.B * p.MT, in.Hkv, p.group);
   uint16_t *o16 = static_cast<uint16_t *>(o);
   if (in.D == 64) attn_fwd_kernel<64><<<grid, 256, 0, s>>>(p, o16, lse);

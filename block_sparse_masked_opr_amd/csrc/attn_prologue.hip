@@ -158,8 +158,7 @@ __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_
         hi[e] = bf16_to_f32(hb[e]);
         if (ROPE) {
           const float x1 = lo[e], x2 = hi[e];
-          lo[e] = x1 * cs[e].x - x2 * cs[e].y;
-          hi[e] = x2 * cs[e].x + x1 * cs[e].y;
+          rope_pair(x1, x2, cs[e], lo[e], hi[e]);
         }
       }
     }

@@ -128,6 +128,7 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->lse2 = ws.lse2;
   p->fsq = ws.fsq;
   p->kunits = ws.kunits;
+  p->q_in = nullptr;
   p->o_in = nullptr;
   p->dout_in = nullptr;
   p->lse_in = nullptr;
@@ -174,13 +175,14 @@ static void mark(const opr_attn_in *in, int i, hipStream_t s) {
   if (in->timing_events) hipEventRecord(in->timing_events[i], s);
 }
 
-// RoPE table, plane maxima of k and v, fp16 copies of q (per-tile scales),
-// k and v in slot order and the work order: the forward state at the start of
-// the workspace.
-static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_t stream) {
+// RoPE table, plane maxima of k and v, fp16 copies of k and v in slot order
+// and the work order: the forward state at the start of the workspace.  The
+// forward kernel converts q itself (and leaves q' there); a backward that does
+// not reuse the forward's workspace packs q here (pack_q).
+static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_t stream, bool pack_q) {
   launch_rope_table(in, ws, stream);
   launch_absmax_kv(in, ws, stream);
-  launch_pack_q(in, ws, stream);
+  if (pack_q) launch_pack_q(in, ws, stream);
   const int32_t *st = in.layout.slot_tok;
   launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hkv, 1, in.k, st, ws.rope, ws.mk, ws.kr, stream);
   launch_pack_any(in.D, false, in.B, in.L, ws.Lp, in.Hkv, 1, in.v, st, ws.rope, ws.mv, ws.vr, stream);
@@ -425,7 +427,7 @@ opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *worksp
   AttnWs ws;
   carve_attn_ws(workspace, *in, 0, &ws);
   mark(in, 0, stream);
-  forward_prologue(*in, ws, stream);
+  forward_prologue(*in, ws, stream, false);
   mark(in, 1, stream);
   if (launch_attn_fwd_kernel(*in, effective_scale(in), o, lse, ws, stream) != hipSuccess) return OPR_E_HIP;
   mark(in, 2, stream);
@@ -445,7 +447,7 @@ opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse, 
   AttnWs ws;
   carve_attn_ws(workspace, *in, 1, &ws);
   mark(in, 0, stream);
-  if (!in->reuse_fwd_workspace) forward_prologue(*in, ws, stream);
+  if (!in->reuse_fwd_workspace) forward_prologue(*in, ws, stream, true);
   if (launch_attn_bwd_kernels(*in, effective_scale(in), o, lse, dout, dq, dk, dv, ws, stream,
                               in->timing_events ? in->timing_events + 1 : nullptr) != hipSuccess)
     return OPR_E_HIP;

@@ -118,6 +118,10 @@ typedef struct {
 /*
  * opr_build_layout - token layout, position ids and tile schedule.
  *
+ * The sequence construction of the one pass: each response stored twice
+ * (wiki summary, section "Token 复制"), the strategic position ids (section
+ * "位置 ID 策略"), the block-sparse mask of the four visibility rules
+ * (section "分块稀疏注意力掩码"), generated on the device (section "实现细节").
  * Packs each row's conversations back to back (segments of a turn in the
  * order h, t, r_in, r_out; the rest of the row is PAD), assigns the strategic
  * position ids above and the attention-order slots, writes the mask of every
@@ -211,21 +215,36 @@ typedef struct {
 /*
  * opr_attn_fwd - masked attention forward.
  *
- * RoPE (rotate-half pairs (j, j + D/2), angle pos * theta^(-2j/D)) is applied
- * to q and k at the layout's position ids; then for every query token and q
- * head, softmax(scale * q k^T) over exactly the keys the mask allows, times v.
- * The kernels run in attention order: q, k, v are gathered into slot order,
- * empty tiles are skipped, and partial 32x32 sub-blocks test the mask per
- * element from the two runs of slots of the layout; results are written back
- * at the tokens' own rows.
+ * The attention of the one pass: every token attends, with ordinary softmax
+ * attention, to exactly the keys the four visibility rules allow (wiki
+ * summary, section "分块稀疏注意力掩码"), with RoPE at the strategic position
+ * ids (section "位置 ID 策略"), so that each token gets the result of its own
+ * N-pass sequence (section "理论保证", Theorem 2.1).  RoPE (rotate-half pairs
+ * (j, j + D/2), angle pos * theta^(-2j/D); the pages name no variant, this is
+ * Qwen-3's, their model family) is applied to q and k at the layout's
+ * position ids; then for every query token and q head, softmax(scale q k^T)
+ * over the allowed keys, times v.  The kernels run in attention order: q, k,
+ * v are gathered into slot order, empty tiles are skipped, and partial 32x32
+ * sub-blocks test the mask per element from the two runs of slots of the
+ * layout; results are written back at the tokens' own rows.
  *
- *  o    bf16 [B][L][Hq][D]   attention output; PAD rows get 0.
+ *  in->q, k, v  16-byte aligned.
+ *  o    bf16 [B][L][Hq][D]   attention output; PAD rows get 0; 16-byte aligned.
  *  lse  fp32 [B][Hq][L]      natural-log sum of exp of the scaled scores of
  *                            the allowed keys; -inf for PAD rows.
- *  workspace  >= opr_attn_workspace_size(B, L, Hq, Hkv, D, 0) bytes.
- * Errors: OPR_E_INVALID (including a layout of another order),
- * OPR_E_UNSUPPORTED (D, block sizes), OPR_E_CAPACITY
- * (ws_bytes), OPR_E_HIP.
+ *  workspace  >= opr_attn_workspace_size(B, L, Hq, Hkv, D, 0) bytes, 256-byte
+ *             aligned.
+ * Input range: the matrix products run on fp16 operands with power-of-two
+ * scales (one per query row and q head for q after RoPE, one per (row, kv
+ * head) plane for k after RoPE and v).  Results are accurate for finite
+ * inputs whose largest magnitude per row (q, dout) or per plane (k, v) lies
+ * in [2^-46, 2^75); rows or planes of smaller values keep an absolute
+ * precision of about 2^-84, and magnitudes of 2^76 and more overflow fp16
+ * and give non-finite results.  (The data is not inspected on the host; no
+ * status reports it.)
+ * Errors: OPR_E_INVALID (null or misaligned pointer, a layout of another
+ * order), OPR_E_UNSUPPORTED (D, block sizes), OPR_E_CAPACITY (ws_bytes),
+ * OPR_E_HIP.
  */
 opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *workspace,
                         size_t ws_bytes, hipStream_t stream);
@@ -234,15 +253,24 @@ opr_status opr_attn_fwd(const opr_attn_in *in, void *o, float *lse, void *worksp
  * opr_attn_bwd - gradients of sum(o * dout) with respect to q, k and v
  * (before RoPE: the RoPE rotation is transposed back onto dq and dk).
  *
- *  o, lse  the outputs of opr_attn_fwd for the same inputs.
- *  dout    bf16 [B][L][Hq][D].
- *  dq      fp32 [B][L][Hq][D];  dk, dv  fp32 [B][L][Hkv][D].  Every element
- *          is written (PAD rows get 0); nothing is accumulated into them.
- *          The sums run in a fixed order: the same inputs give bit-identical
- *          gradients on every call.
- *  workspace  >= opr_attn_workspace_size(B, L, Hq, Hkv, D, 1) bytes; the
- *             forward part of it is a prefix, so one backward-sized
- *             workspace serves both calls (see reuse_fwd_workspace).
+ * The gradients of the one pass equal those of the N separate passes summed
+ * onto the shared tokens (wiki summary, section "理论保证": the loss is the
+ * same per token, so is its gradient).  With P the masked softmax,
+ * dV = sum over the kv group's heads of P^T dout, dS = P (dout v^T - delta)
+ * with delta = rowsum(dout * o) over the o given here, dQ = scale dS k',
+ * dK = scale sum over the group of dS^T q'.
+ *
+ *  o, lse  the outputs of opr_attn_fwd for the same inputs; o 16-byte aligned.
+ *  dout    bf16 [B][L][Hq][D]; 16-byte aligned.  The input range of
+ *          opr_attn_fwd applies to it per row.
+ *  dq      fp32 [B][L][Hq][D];  dk, dv  fp32 [B][L][Hkv][D]; 16-byte aligned.
+ *          Every element is written (PAD rows get 0); nothing is accumulated
+ *          into them.  The sums run in a fixed order: the same inputs give
+ *          bit-identical gradients on every call.
+ *  workspace  >= opr_attn_workspace_size(B, L, Hq, Hkv, D, 1) bytes, 256-byte
+ *             aligned; the forward part of it is a prefix, so one
+ *             backward-sized workspace serves both calls (see
+ *             reuse_fwd_workspace).
  * Errors as for opr_attn_fwd.
  */
 opr_status opr_attn_bwd(const opr_attn_in *in, const void *o, const float *lse,
