@@ -66,24 +66,26 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
 #pragma unroll
   for (int s = 0; s < NS; ++s) qb[s] = ld_f16x8(p.qr + hq_row * D + 16 * s + 8 * g);
 
-  // ---- prologue: Delta, the fp16 dout with its tile exponent, the dK/dV units
+  // ---- prologue: Delta, the fp16 dout with its row exponent, the dK/dV
+  // units.  The loads are issued here; the conversion (convert_dout) runs once
+  // the stage list is built and the first K/V tiles stream in.
+  const int32_t tok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
+  uint4 dw[NS], ow[NS];  // bf16 dims 16 s + 8 g .. + 7 of dout and o
+#pragma unroll
+  for (int s = 0; s < NS; ++s) dw[s] = ow[s] = make_uint4(0u, 0u, 0u, 0u);
+  float lse = -INFINITY;
+  if (tok >= 0) {
+    const int64_t base = (((int64_t)b * p.L + tok) * p.Hq + h) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      dw[s] = *reinterpret_cast<const uint4 *>(p.dout_in + base + 16 * s);
+      ow[s] = *reinterpret_cast<const uint4 *>(p.o_in + base + 16 * s);
+    }
+    lse = p.lse_in[((int64_t)b * p.Hq + h) * p.L + tok];
+  }
   float lse2_q, dsc_q;
   int edo_of_lane;
-  {
-    const int32_t tok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
-    uint4 dw[NS], ow[NS];  // bf16 dims 16 s + 8 g .. + 7 of dout and o
-#pragma unroll
-    for (int s = 0; s < NS; ++s) dw[s] = ow[s] = make_uint4(0u, 0u, 0u, 0u);
-    float lse = -INFINITY;
-    if (tok >= 0) {
-      const int64_t base = (((int64_t)b * p.L + tok) * p.Hq + h) * D + 8 * g;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        dw[s] = *reinterpret_cast<const uint4 *>(p.dout_in + base + 16 * s);
-        ow[s] = *reinterpret_cast<const uint4 *>(p.o_in + base + 16 * s);
-      }
-      lse = p.lse_in[((int64_t)b * p.Hq + h) * p.L + tok];
-    }
+  auto convert_dout = [&]() {
     float delta = 0.0f;
     uint32_t mx = 0u;  // float bits of the largest |dout| (integer order)
 #pragma unroll
@@ -119,13 +121,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
     lse2_q = live ? lse * kLog2e : INFINITY;
     dsc_q = ldexpf(delta, edo + ev - kDsShift);
     // the dK/dV kernel's units (see attn_bwd.hip): the same quantities with
-    // the slot's dout tile exponent folded in and the 2^kPdvExp of its P
+    // the slot's dout row exponent folded in and the 2^kPdvExp of its P
     if (g == 0) {
       p.lse2[hq_row] = live ? lse * kLog2e - (float)kPdvExp + (float)edo : INFINITY;
       p.dsc[hq_row] = ldexpf(delta, edo + ev - kDsShift - kPdvExp);
       p.fsq[hq_row] = fs;
     }
-  }
+  };
   // key slots this query sees: [iv.x, iv.y) and [iv.z, iv.w)
   const int4 iv = q < p.L ? p.qiv[(int64_t)b * p.L + q] : make_int4(0, 0, 0, 0);
   OperandOffsets<D> of;
@@ -150,8 +152,9 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
     tc.issue(rv, k0, nb + TB, w);
   };
 
-  int tnext = 0;
-  while (tnext < nnz) {
+  // the stage list is built in chunks of up to kStageCap stages
+  int tnext = 0, ns = 0;
+  auto build = [&]() {
     __syncthreads();
     if (w == 0) {
       int t = tnext;
@@ -162,10 +165,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
       }
     }
     __syncthreads();
-    const int ns = uniform(sh_count);
+    ns = uniform(sh_count);
     tnext = uniform(sh_next);
-    if (ns == 0) continue;
-    issue(uniform((int)stages[0].x), buf0);
+    if (ns > 0) issue(uniform((int)stages[0].x), buf0);
+  };
+  build();
+  convert_dout();  // while the first K/V tiles stream in
+  for (;;) {
     auto stage = [&](int i, const char *buf, char *nxt) {
       wait_all_and_barrier();
       if (i + 1 < ns) issue(uniform((int)stages[i + 1].x), nxt);
@@ -225,6 +231,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
       stage(i, buf0, buf1);
       if (i + 1 < ns) stage(i + 1, buf1, buf0);
     }
+    if (tnext >= nnz) break;
+    build();
   }
 
   if (q < p.L) {

@@ -61,36 +61,45 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
   // id, as fp16 with the row's own exponent eq; written to the q' plane with
   // eq (and eq's minimum over each 16-slot tile) for the backward.  Lane g
   // holds dims 16 s + 8 g + e, so each rotation pair (d, d + D/2) is the
-  // lane's own (k-steps s and s + NS/2).
+  // lane's own (k-steps s and s + NS/2).  The loads are issued here; the
+  // conversion (convert_q) runs once the stage list is built and the first
+  // K/V tiles stream in, so that their latencies overlap.
+  const int64_t hq_row = ((int64_t)b * p.Hq + h) * p.Lp + q;
+  const int32_t tok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
+  uint4 wv[NS];
+  float2 csv[NS / 2][8];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) wv[s] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int s = 0; s < NS / 2; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) csv[s][e] = make_float2(1.0f, 0.0f);
+  if (tok >= 0) {
+    const uint16_t *src = p.q_in + (((int64_t)b * p.L + tok) * p.Hq + h) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) wv[s] = *reinterpret_cast<const uint4 *>(src + 16 * s);
+    const float2 *cs = p.rope + ((int64_t)b * p.Lp + q) * (D / 2) + 8 * g;
+#pragma unroll
+    for (int s = 0; s < NS / 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) csv[s][e] = cs[16 * s + e];
+  }
   f16x8 qb[NS];
-  int eq;
-  {
-    const int64_t hq_row = ((int64_t)b * p.Hq + h) * p.Lp + q;
-    const int32_t tok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
+  float fs;  // raw score -> log2 units: scale log2(e) 2^-(eq + ek)
+  auto convert_q = [&]() {
     float x[NS][8];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NS; ++s) {
+      const uint16_t *e16 = reinterpret_cast<const uint16_t *>(&wv[s]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[s][e] = 0.0f;
-    if (tok >= 0) {
-      const uint16_t *src = p.q_in + (((int64_t)b * p.L + tok) * p.Hq + h) * D + 8 * g;
-      uint4 wv[NS];
+      for (int e = 0; e < 8; ++e) x[s][e] = bf16_to_f32(e16[e]);
+    }
 #pragma unroll
-      for (int s = 0; s < NS; ++s) wv[s] = *reinterpret_cast<const uint4 *>(src + 16 * s);
+    for (int s = 0; s < NS / 2; ++s) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const uint16_t *e16 = reinterpret_cast<const uint16_t *>(&wv[s]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[s][e] = bf16_to_f32(e16[e]);
-      }
-      const float2 *cs = p.rope + ((int64_t)b * p.Lp + q) * (D / 2) + 8 * g;
-#pragma unroll
-      for (int s = 0; s < NS / 2; ++s) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x1 = x[s][e], x2 = x[s + NS / 2][e];
-          rope_pair(x1, x2, cs[16 * s + e], x[s][e], x[s + NS / 2][e]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float x1 = x[s][e], x2 = x[s + NS / 2][e];
+        rope_pair(x1, x2, csv[s][e], x[s][e], x[s + NS / 2][e]);
       }
     }
     uint32_t mx = 0u;  // float bits of the row's largest |q'| (integer order)
@@ -99,7 +108,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = max(mx, __float_as_uint(fabsf(x[s][e])));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
-    eq = mx > 0u ? plane_exponent(mx) : kExpMax;
+    const int eq = mx > 0u ? plane_exponent(mx) : kExpMax;
     uint16_t *dst = p.qr + hq_row * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -112,8 +121,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
     for (int off = 8; off > 0; off >>= 1) emin = min(emin, __shfl_xor(emin, off));
     if (g == 0) p.eqq[hq_row] = eq;
     if ((lane & 47) == 0) p.eqt[((int64_t)b * p.Hq + h) * p.MTS + q / kTile] = emin;
-  }
-  const float fs = ldexpf(p.scale_log2, -(eq + ek));  // raw score -> log2 units
+    fs = ldexpf(p.scale_log2, -(eq + ek));
+  };
   // key slots this query sees: [iv.x, iv.y) and [iv.z, iv.w)
   const int4 iv = q < p.L ? p.qiv[(int64_t)b * p.L + q] : make_int4(0, 0, 0, 0);
   OperandOffsets<D> of;
@@ -139,8 +148,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
     tc.issue(rv, k0, nb + TB, w);
   };
 
-  int tnext = 0;
-  while (tnext < nnz) {
+  // the stage list is built in chunks of up to kStageCap stages
+  int tnext = 0, ns = 0;
+  auto build = [&]() {
     __syncthreads();  // the previous chunk's stages and buffers are no longer read
     if (w == 0) {
       int t = tnext;
@@ -151,10 +161,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
       }
     }
     __syncthreads();
-    const int ns = uniform(sh_count);
+    ns = uniform(sh_count);
     tnext = uniform(sh_next);
-    if (ns == 0) continue;
-    issue(uniform((int)stages[0].x), buf0);
+    if (ns > 0) issue(uniform((int)stages[0].x), buf0);
+  };
+  build();
+  convert_q();  // while the first K/V tiles stream in
+  for (;;) {
     // stage i reads `buf` while stage i+1 streams into `nxt`
     auto stage = [&](int i, const char *buf, char *nxt) {
       wait_all_and_barrier();
@@ -227,6 +240,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnParams p, uint16_t
       stage(i, buf0, buf1);
       if (i + 1 < ns) stage(i + 1, buf1, buf0);
     }
+    if (tnext >= nnz) break;
+    build();
   }
 
   const float lsum = lrow + __shfl_xor(lrow, 32);
