@@ -565,6 +565,8 @@ def main():
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--depth-stages", metavar="N", type=int, nargs="+",
                     help="only print per-stage times of the depth workload at these N (one pass and N passes)")
+    ap.add_argument("--layout-only", action="store_true",
+                    help="only time opr_build_layout on 64 rows x 32768 tokens and print its JSON")
     ap.add_argument("--summarize-traffic", metavar="RUN_DIR",
                     help="write the HBM traffic summary of the dK/dV kernel from --pmc runs and exit")
     args = ap.parse_args()
@@ -588,6 +590,9 @@ def main():
     from block_sparse_masked_opr_amd import binding as Bd
 
     dev = torch.device("cuda:0")
+    if args.layout_only:
+        print(json.dumps(layout_step(torch, Bd, dev, args.steps)), flush=True)
+        return
     shape = I.PACKED_FWD_BWD
     seed_len, seed_t = I.SEEDS["packed_fwd_bwd"]
     rows = I.packed_rows(shape, seed_len)

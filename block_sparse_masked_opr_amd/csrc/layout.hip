@@ -13,10 +13,11 @@
 //                    the allowed keys of each 32-key sub-block with interval
 //                    arithmetic, then sums per 32x32 sub-block and per tile
 //                    (layout_classify_attention: the same over attention
-//                    order, from the query's two runs of slots, one
-//                    workgroup per q-tile row)
-//   layout_compact_q/k  one wave per tile row / column: ballot compaction of
-//                    the non-empty tiles into ascending lists
+//                    order, from the queries' two runs of slots, one
+//                    workgroup per q-tile row, a lane per 32x32 sub-block)
+//   layout_compact   one wave per tile row and per tile column (one launch):
+//                    ballot compaction of the non-empty tiles into ascending
+//                    lists
 //
 // Visibility of a query q in turn i of a conversation, as key intervals of
 // the packed row (segments of a turn are stored h, t, r_in, r_out):
@@ -35,26 +36,40 @@ namespace {
 constexpr int kPrepThreads = 1024;
 
 // Exclusive prefix sum of n values (produced by get(i)) into out[0..n], using
-// the whole workgroup; out[n] is the total.
+// the whole workgroup; out[n] is the total.  Per chunk of kPrepThreads
+// values: an inclusive scan inside each wave (shuffles), the wave totals
+// scanned by wave 0 through LDS (sh: kPrepThreads / 64 + 1 words), two
+// barriers per chunk.
 template <class Get>
 __device__ void block_exclusive_scan(int n, Get get, int32_t *out, int32_t *sh) {
-  const int tid = threadIdx.x;
+  constexpr int kWaves = kPrepThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int32_t carry = 0;
   for (int base = 0; base < n; base += kPrepThreads) {
     const int i = base + tid;
     const int32_t v = (i < n) ? get(i) : 0;
-    sh[tid] = v;
-    __syncthreads();
-    for (int d = 1; d < kPrepThreads; d <<= 1) {
-      const int32_t add = (tid >= d) ? sh[tid - d] : 0;
-      __syncthreads();
-      sh[tid] += add;
-      __syncthreads();
+    int32_t incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
     }
-    if (i < n) out[i] = carry + sh[tid] - v;
-    const int32_t total = sh[kPrepThreads - 1];
+    if (lane == 63) sh[wv] = incl;
     __syncthreads();
-    carry += total;
+    if (wv == 0) {
+      int32_t t = lane < kWaves ? sh[lane] : 0;
+#pragma unroll
+      for (int d = 1; d < kWaves; d <<= 1) {
+        const int32_t y = __shfl_up(t, d);
+        if (lane >= d) t += y;
+      }
+      if (lane < kWaves) sh[lane] = t;  // inclusive totals of waves 0 .. lane
+    }
+    __syncthreads();
+    const int32_t before = (wv > 0 ? sh[wv - 1] : 0) + incl - v;
+    if (i < n) out[i] = carry + before;
+    carry += sh[kWaves - 1];
+    __syncthreads();  // sh is rewritten by the next chunk
   }
   if (tid == 0) out[n] = carry;
   __syncthreads();
@@ -266,128 +281,124 @@ __global__ __launch_bounds__(BQ) void layout_classify(int32_t B, int32_t L, int3
   }
 }
 
-// Tile classes over attention order: one workgroup of BQ threads per q-tile
-// row (b, m).  The row's queries (slots m*BQ ..) put their two runs of slots
-// in LDS, and their union gives the span of key slots any of them sees: key
-// tiles outside it are empty and are written as such directly.  In the
-// others each thread counts whole 32x32 sub-blocks, summing over the
-// sub-block's 32 queries the part of their runs inside its 32 key slots.
-// kClsBatch tiles at a time meet in LDS, and their class words are written
-// together.
-constexpr int kClsBatch = 64;
+// Tile classes over attention order: one workgroup of kClsThreads threads
+// per q-tile row (b, m).  The row's queries (slots m*BQ ..) put their two
+// runs of slots in LDS, and their union gives the span of key slots any of
+// them sees: key tiles outside it are empty and are written as such directly.
+// Inside it, a group of SQ*SK consecutive lanes takes one tile, a lane one
+// 32x32 sub-block: it sums over the sub-block's 32 queries the part of their
+// runs inside its 32 key slots.  The group forms the tile's class word and
+// total with shuffles (no LDS table, no barrier per tile), and its first lane
+// writes them.  Two waves per row: with more, fewer rows share a compute unit
+// and the row's serial steps (loads, span, passes) are no better hidden.
+constexpr int kClsThreads = 128;
 
 template <int BQ, int BK>
-__global__ __launch_bounds__(BQ) void layout_classify_attention(int32_t B, int32_t L, int32_t MT,
-                                                                int32_t NT, opr_layout out) {
-  constexpr int SQ = BQ / OPR_SUB_BLOCK, SK = BK / OPR_SUB_BLOCK, NSB = SQ * SK;
+__global__ __launch_bounds__(kClsThreads) void layout_classify_attention(int32_t B, int32_t L, int32_t MT,
+                                                                         int32_t NT, opr_layout out) {
+  constexpr int SQ = BQ / OPR_SUB_BLOCK, SK = BK / OPR_SUB_BLOCK, NSB = SQ * SK, TPW = 64 / NSB;
+  static_assert(NSB <= 64 && 64 % NSB == 0, "a tile's sub-blocks fit in one wave");
+  static_assert(BQ <= kClsThreads, "one thread per query slot of the tile row");
   __shared__ int4 runs[BQ];
-  __shared__ int32_t cnt[kClsBatch][NSB];
   __shared__ int32_t span[2];
   const int64_t row = blockIdx.x;  // b * MT + m
   const int32_t m = (int32_t)(row % MT);
   const int32_t b = (int32_t)(row / MT);
-  const int tid = threadIdx.x;
-  const int32_t q = m * BQ + tid;
-  int4 iv = make_int4(0, 0, 0, 0);
-  if (q < L) iv = reinterpret_cast<const int4 *>(out.slot_qiv)[(int64_t)b * L + q];
-  runs[tid] = iv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (tid == 0) {
     span[0] = INT32_MAX;
     span[1] = INT32_MIN;
   }
   __syncthreads();
-  if (iv.x < iv.y || iv.z < iv.w) {
-    atomicMin(&span[0], iv.x < iv.y ? iv.x : iv.z);
-    atomicMax(&span[1], iv.z < iv.w ? iv.w : iv.y);
+  {
+    const int32_t q = m * BQ + tid;
+    int4 iv = make_int4(0, 0, 0, 0);
+    if (tid < BQ && q < L) iv = reinterpret_cast<const int4 *>(out.slot_qiv)[(int64_t)b * L + q];
+    if (tid < BQ) runs[tid] = iv;
+    const bool any = iv.x < iv.y || iv.z < iv.w;
+    int32_t lo = any ? (iv.x < iv.y ? iv.x : iv.z) : INT32_MAX;
+    int32_t hi = any ? (iv.z < iv.w ? iv.w : iv.y) : INT32_MIN;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, __shfl_xor(lo, off));
+      hi = max(hi, __shfl_xor(hi, off));
+    }
+    if (lane == 0 && lo <= hi) {  // one atomic pair per wave
+      atomicMin(&span[0], lo);
+      atomicMax(&span[1], hi);
+    }
   }
   __syncthreads();
   uint8_t *tcls = out.tile_class + row * NT;
   uint32_t *scls = out.sub_class + row * NT;
   const int32_t n_lo = span[0] <= span[1] ? span[0] / BK : 0;
   const int32_t n_hi = span[0] <= span[1] ? (span[1] - 1) / BK : -1;  // empty range if no key is seen
-  for (int32_t n = tid; n < NT; n += BQ) {
+  for (int32_t n = tid; n < NT; n += kClsThreads) {
     if (n < n_lo || n > n_hi) {
       tcls[n] = OPR_TILE_EMPTY;
       scls[n] = 0u;
     }
   }
-  for (int32_t nb = n_lo; nb <= n_hi; nb += kClsBatch) {
-    const int nt = min(kClsBatch, n_hi + 1 - nb);
-    for (int x = tid; x < nt * NSB; x += BQ) {
-      const int t = x / NSB, i = x - t * NSB, sq = i / SK, j = i - sq * SK;
-      const int32_t a = (nb + t) * BK + j * OPR_SUB_BLOCK;
+  const int grp = lane / NSB, i = lane % NSB, sq = i / SK, j = i % SK;
+  constexpr int kPass = (kClsThreads / 64) * TPW;  // tiles per pass of the workgroup
+  for (int32_t nb = n_lo; nb <= n_hi; nb += kPass) {
+    const int32_t n = nb + wv * TPW + grp;
+    int32_t c = 0;
+    if (n <= n_hi) {
+      const int32_t a = n * BK + j * OPR_SUB_BLOCK;
       const int32_t e = min(a + OPR_SUB_BLOCK, L);
-      int32_t c = 0;
 #pragma unroll 8
       for (int r = 0; r < OPR_SUB_BLOCK; ++r) {
         const int4 u = runs[sq * OPR_SUB_BLOCK + r];
         c += overlap(a, e, u.x, u.y) + overlap(a, e, u.z, u.w);
       }
-      cnt[t][i] = c;
     }
-    __syncthreads();
-    for (int t = tid; t < nt; t += BQ) {
-      uint32_t word = 0;
-      int32_t total = 0;
-      for (int i = 0; i < NSB; ++i) {
-        const int32_t v = cnt[t][i];
-        total += v;
-        const uint32_t cls = v == 0 ? OPR_TILE_EMPTY
-                           : (v == OPR_SUB_BLOCK * OPR_SUB_BLOCK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
-        word |= cls << (2 * i);
-      }
-      tcls[nb + t] = total == 0 ? OPR_TILE_EMPTY : (total == BQ * BK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
-      scls[nb + t] = word;
+    uint32_t word = (c == 0 ? OPR_TILE_EMPTY : (c == OPR_SUB_BLOCK * OPR_SUB_BLOCK ? OPR_TILE_FULL : OPR_TILE_PARTIAL))
+                    << (2 * i);
+    int32_t total = c;
+#pragma unroll
+    for (int off = NSB / 2; off > 0; off >>= 1) {
+      word |= (uint32_t)__shfl_xor((int)word, off);
+      total += __shfl_xor(total, off);
     }
-    __syncthreads();
+    if (i == 0 && n <= n_hi) {
+      tcls[n] = total == 0 ? OPR_TILE_EMPTY : (total == BQ * BK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
+      scls[n] = word;
+    }
   }
 }
 
-// One wave per (b, m): k-tile indices of the non-empty tiles of q-tile row m.
-__global__ __launch_bounds__(64) void layout_compact_q(int32_t MT, int32_t NT, opr_layout out) {
-  const int64_t row = blockIdx.x;  // b * MT + m
-  const uint8_t *cls = out.tile_class + row * NT;
-  int32_t *lst = out.q_list + row * NT;
+// The lists of non-empty tiles, one wave per list: blocks [0, B*MT) take
+// q-tile row b*MT + m (its k-tile indices), the next B*NT k-tile column
+// b*NT + n (its q-tile indices).  Ballot compaction, ascending.
+__global__ __launch_bounds__(64) void layout_compact(int32_t B, int32_t MT, int32_t NT, opr_layout out) {
+  const int64_t id = blockIdx.x;
   const int lane = threadIdx.x;
+  const bool is_row = id < (int64_t)B * MT;
+  const int64_t idx = is_row ? id : id - (int64_t)B * MT;  // row b*MT + m, or column b*NT + n
+  const int64_t b = is_row ? idx / MT : idx / NT;
+  const int32_t len = is_row ? NT : MT;
+  const uint8_t *cls = is_row ? out.tile_class + idx * NT : out.tile_class + b * MT * NT + (idx - b * NT);
+  const int64_t stride = is_row ? 1 : NT;
+  int32_t *lst = is_row ? out.q_list + idx * NT : out.k_list + idx * MT;
   int32_t count = 0;
-  for (int32_t base = 0; base < NT; base += 64) {
-    const int32_t n = base + lane;
-    const bool nz = n < NT && cls[n] != OPR_TILE_EMPTY;
+  for (int32_t base = 0; base < len; base += 64) {
+    const int32_t x = base + lane;
+    const bool nz = x < len && cls[(int64_t)x * stride] != OPR_TILE_EMPTY;
     const uint64_t bal = __ballot(nz);
     const int32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (nz) lst[count + before] = n;
+    if (nz) lst[count + before] = x;
     count += __popcll(bal);
   }
-  for (int32_t n = count + lane; n < NT; n += 64) lst[n] = -1;
-  if (lane == 0) out.q_nnz[row] = count;
-}
-
-// One wave per (b, n): q-tile indices of the non-empty tiles of k-tile column n.
-__global__ __launch_bounds__(64) void layout_compact_k(int32_t MT, int32_t NT, opr_layout out) {
-  const int64_t col = blockIdx.x;  // b * NT + n
-  const int64_t b = col / NT;
-  const int32_t n = (int32_t)(col - b * NT);
-  const uint8_t *cls = out.tile_class + b * MT * NT + n;
-  int32_t *lst = out.k_list + col * MT;
-  const int lane = threadIdx.x;
-  int32_t count = 0;
-  for (int32_t base = 0; base < MT; base += 64) {
-    const int32_t m = base + lane;
-    const bool nz = m < MT && cls[(int64_t)m * NT] != OPR_TILE_EMPTY;
-    const uint64_t bal = __ballot(nz);
-    const int32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (nz) lst[count + before] = m;
-    count += __popcll(bal);
-  }
-  for (int32_t m = count + lane; m < MT; m += 64) lst[m] = -1;
-  if (lane == 0) out.k_nnz[col] = count;
+  for (int32_t x = count + lane; x < len; x += 64) lst[x] = -1;
+  if (lane == 0) (is_row ? out.q_nnz : out.k_nnz)[idx] = count;
 }
 
 template <int BQ, int BK>
 void launch_classify(int64_t tiles, int32_t B, int32_t L, int32_t MT, int32_t NT,
                      const LayoutWs &ws, const opr_layout &out, hipStream_t s) {
   if (out.order == OPR_ORDER_ATTENTION)
-    layout_classify_attention<BQ, BK><<<dim3((unsigned)((int64_t)B * MT)), dim3(BQ), 0, s>>>(B, L, MT, NT, out);
+    layout_classify_attention<BQ, BK><<<dim3((unsigned)((int64_t)B * MT)), dim3(kClsThreads), 0, s>>>(B, L, MT, NT, out);
   else
     layout_classify<BQ, BK><<<dim3((unsigned)tiles), dim3(BQ), 0, s>>>(B, L, MT, NT, ws, out);
 }
@@ -425,8 +436,7 @@ hipError_t launch_build_layout(int32_t B, int32_t L, int32_t bq, int32_t bk, int
   OPR_CLASSIFY_CASE(64, 32) OPR_CLASSIFY_CASE(64, 64) OPR_CLASSIFY_CASE(64, 128)
   OPR_CLASSIFY_CASE(128, 32) OPR_CLASSIFY_CASE(128, 64) OPR_CLASSIFY_CASE(128, 128)
 #undef OPR_CLASSIFY_CASE
-  layout_compact_q<<<(unsigned)((int64_t)B * MT), 64, 0, s>>>(MT, NT, out);
-  layout_compact_k<<<(unsigned)((int64_t)B * NT), 64, 0, s>>>(MT, NT, out);
+  layout_compact<<<(unsigned)((int64_t)B * (MT + NT)), 64, 0, s>>>(B, MT, NT, out);
   return hipGetLastError();
 }
 
