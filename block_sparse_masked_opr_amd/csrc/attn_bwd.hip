@@ -27,24 +27,27 @@
 // sub-blocks are masked with 64-bit masks
 // built from the two runs of slots of each query or key.
 //
-// Units: k' and v carry one exponent per (row, kv head), constant inside a
-// workgroup; q' and dout one per 16-slot tile and q head, so they change
-// inside a stage (eq, edo of the tile; the stage descriptor carries the four
-// tiles' eq and edo).  Each key block w (the P-wave and the dS-wave of its 32
-// keys) accumulates in units fixed by eqr, edor: the smallest eq and edo of
-// the tiles of the stages that block runs, over this work item's stage range
-// (a pre-pass over the range, before the main loop).  So a key's units depend
-// only on the queries of its own stages, never on another conversation of the
-// row.  The dQ kernel stores per slot lse2 = lse log2 e - kPdvExp + edo and
-// delta' = delta 2^(edo + ev - kDsShift - kPdvExp) (delta in the units of
-// dP' 2^-(kDsShift + kPdvExp)).  With the tile's shift c = 2^-(eq - eqr):
-//   S: the score scale is 2^-(eq + ek) per tile;
+// Units: k' and v carry one exponent per (row, kv head) plane (ek, ev),
+// constant inside a workgroup; q' and dout one per query row and q head (eq,
+// edo), so they change from query to query inside a stage.  Each key block w
+// (the P-wave and the dS-wave of its 32 keys) accumulates in units fixed by
+// eqr, edor: the smallest eq and edo over the queries of this work item's
+// stages that see the block's keys (dkdv_units_kernel, before this kernel),
+// so a key's units depend only on queries that see it, never on another
+// conversation of the row.  The dQ kernel stores per slot
+// lse2 = lse log2 e - kPdvExp + edo, delta' = delta 2^(edo + ev - kDsShift -
+// kPdvExp) (delta in the units of dP' 2^-(kDsShift + kPdvExp)) and the score
+// factor fsq = scale log2 e 2^-(eq + ek).  With the query's shift
+// c = 2^-(eq - eqr):
+//   S: raw scores times fsq are in log2 units;
 //   dV^T += dO'^T P'^T with P' = fp16(P * 2^(kPdvExp - (edo - edor)))
-//       = exp2(S scale log2 e - lse2 + edor), so dV is in units 2^(kPdvExp + edor);
+//       = exp2(S fsq - lse2 + edor), so dV is in units 2^(kPdvExp + edor);
 //   dS' = P' (dP' 2^-(kDsShift + kPdvExp) - delta') c 2^bs with dP' = dO' V'^T
 //       in units 2^(edo + ev) and bs the dS-wave's shift of its keys' v' to
 //       the top of fp16's range, so dS' = dS 2^(eqr + edor + ev + bs - kDsShift - eq)
 //       and dK^T += Q'^T dS'^T is in units 2^(eqr + edor + ev + bs - kDsShift).
+//   c is capped at 1: a query with eq below eqr does not see the block, its
+//   P' is 0, and the cap keeps its factor finite.
 #include "attn_common.h"
 #include "attn_sched.h"
 #include "opr_internal.h"
