@@ -1,13 +1,16 @@
 // Prologue kernels of the attention path.  Everything here is indexed by
 // slot (attention order): slot s < L holds token slot_tok[s] of the layout,
-// slots L .. Lp-1 are empty and padded with zeros.
-//  - the RoPE table at the slots' strategic position ids (and the reset of
-//    the plane maxima),
-//  - the largest magnitude of every (row, kv head) plane of k and v,
-//  - head-major fp16 copies of q, k (after RoPE) and v in slot order: k and v
-//    with one power-of-two scale per plane, q with one per row (token and
-//    head), found while the row is converted,
-//  - the longest-first work order of the attention kernels.
+// slots L .. Lp-1 are empty and padded with zeros.  Three launches:
+//  - rope_order_kernel: the longest-first work order of the attention kernels
+//    (one workgroup) beside the RoPE table at the slots' strategic position
+//    ids (and the reset of the plane maxima); both need the layout alone,
+//  - absmax_kernel: the largest magnitude of every (row, kv head) plane of k
+//    and v,
+//  - pack_kv_kernel: head-major fp16 copies of k (after RoPE) and v in slot
+//    order with one power-of-two scale per plane.
+// pack_kernel makes the same copy of q, one scale per row (token and head),
+// for a backward that does not reuse the forward's state (the forward kernel
+// converts q itself).
 // (The backward's dout copy and delta = rowsum(dout * o) are formed by the
 // dQ kernel, attn_dq.hip.)
 //
@@ -22,25 +25,30 @@ namespace opr {
 namespace {
 
 // table[b][s][j] = (cos, sin) of pos(b, slot_tok[s]) * theta^(-2j/D); PAD
-// and s >= L use position 0.  The first n_zero threads also clear zero_words
+// and s >= L use position 0.  Element gid < n_zero also clears zero_words[gid]
 // (the plane maxima start at 0).
-__global__ __launch_bounds__(256) void rope_table_kernel(int32_t B, int32_t L, int32_t Lp, int32_t half,
-                                                         double log2_theta, const int32_t *tok_pos,
-                                                         const int32_t *slot_tok, float2 *table,
-                                                         uint32_t *zero_words, int32_t n_zero) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid < n_zero) zero_words[gid] = 0u;
-  const int64_t total = (int64_t)B * Lp * half;
+struct RopeArgs {
+  int32_t B, L, Lp, half;
+  double log2_theta;
+  const int32_t *tok_pos, *slot_tok;
+  float2 *table;
+  uint32_t *zero_words;
+  int32_t n_zero;
+};
+
+__device__ __forceinline__ void rope_entry(const RopeArgs &a, int64_t gid) {
+  if (gid < a.n_zero) a.zero_words[gid] = 0u;
+  const int64_t total = (int64_t)a.B * a.Lp * a.half;
   if (gid >= total) return;
-  const int32_t j = (int32_t)(gid % half);
-  const int64_t bt = gid / half;
-  const int32_t t = (int32_t)(bt % Lp);
-  const int32_t b = (int32_t)(bt / Lp);
-  const int32_t pos = t < L ? tok_pos[(int64_t)b * L + slot_tok[(int64_t)b * L + t]] : 0;
-  const double inv_freq = exp2(-(2.0 * j / (2.0 * half)) * log2_theta);
-  double s, c;
-  sincos((double)pos * inv_freq, &s, &c);
-  table[gid] = make_float2((float)c, (float)s);
+  const int32_t j = (int32_t)(gid % a.half);
+  const int64_t bt = gid / a.half;
+  const int32_t t = (int32_t)(bt % a.Lp);
+  const int32_t b = (int32_t)(bt / a.Lp);
+  const int32_t pos = t < a.L ? a.tok_pos[(int64_t)b * a.L + a.slot_tok[(int64_t)b * a.L + t]] : 0;
+  const double inv_freq = exp2(-(2.0 * j / (2.0 * a.half)) * a.log2_theta);
+  double sn, cs;
+  sincos((double)pos * inv_freq, &sn, &cs);
+  a.table[gid] = make_float2((float)cs, (float)sn);
 }
 
 // Largest |x| of each (row, head) plane of x [B][L][H][D] bf16, times
@@ -116,17 +124,16 @@ constexpr int kPackHeads = 8;
 constexpr int kPackSlots = 64;
 
 template <int D, bool ROPE, bool ROWS>
-__global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H, int32_t group,
-                                                   const uint16_t *x, const int32_t *slot_tok,
-                                                   const float2 *table, const uint32_t *pmax,
-                                                   uint16_t *rows, int32_t *erow, int32_t *etile) {
+__device__ __forceinline__ void pack_rows(unsigned bx, int b, int32_t L, int32_t Lp, int32_t H, const uint16_t *x,
+                                          const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
+                                          uint16_t *rows, int32_t *erow, int32_t *etile) {
   constexpr int HALF = D / 2;
   constexpr int PER = HALF / 4;  // pairs per thread (4 threads per slot)
   static_assert(kPackSlots == 4 * kTile, "a wave covers one tile");
   const int hgroups = (H + kPackHeads - 1) / kPackHeads;
-  const int h0 = (int)(blockIdx.x % (unsigned)hgroups) * kPackHeads;
-  const int blk = (int)(blockIdx.x / (unsigned)hgroups);
-  const int t0 = blk * kPackSlots, b = blockIdx.z;
+  const int h0 = (int)(bx % (unsigned)hgroups) * kPackHeads;
+  const int blk = (int)(bx / (unsigned)hgroups);
+  const int t0 = blk * kPackSlots;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tt = tid >> 2, part = tid & 3;
   const int t = t0 + tt;
@@ -193,6 +200,27 @@ __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_
   }
 }
 
+template <int D, bool ROPE, bool ROWS>
+__global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H, const uint16_t *x,
+                                                   const int32_t *slot_tok, const float2 *table,
+                                                   const uint32_t *pmax, uint16_t *rows, int32_t *erow,
+                                                   int32_t *etile) {
+  pack_rows<D, ROPE, ROWS>(blockIdx.x, blockIdx.z, L, Lp, H, x, slot_tok, table, pmax, rows, erow, etile);
+}
+
+// k (after RoPE; blockIdx.y = 0) and v (blockIdx.y = 1) in one launch, one
+// scale per plane.
+template <int D>
+__global__ __launch_bounds__(256) void pack_kv_kernel(int32_t L, int32_t Lp, int32_t H, const uint16_t *k,
+                                                      const uint16_t *v, const int32_t *slot_tok,
+                                                      const float2 *table, const uint32_t *mk, const uint32_t *mv,
+                                                      uint16_t *kr, uint16_t *vr) {
+  if (blockIdx.y == 0)
+    pack_rows<D, true, false>(blockIdx.x, blockIdx.z, L, Lp, H, k, slot_tok, table, mk, kr, nullptr, nullptr);
+  else
+    pack_rows<D, false, false>(blockIdx.x, blockIdx.z, L, Lp, H, v, slot_tok, table, mv, vr, nullptr, nullptr);
+}
+
 // Longest-first work order (see q_work_item): the q-tile rows (b*MT + m) by
 // decreasing number of non-empty 64-key halves over their tile lists - the
 // stages of a forward or dQ workgroup - and the dK/dV work items by
@@ -253,12 +281,21 @@ __device__ void scan_bins(int32_t *bins, int32_t *wave_sum) {
 
 __device__ __forceinline__ int32_t parts_of(int32_t c, int32_t cap) { return c > cap ? (c + cap - 1) / cap : 1; }
 
-__global__ __launch_bounds__(kOrderThreads) void work_order_kernel(int32_t n_rows, int32_t n_cols, int32_t MT,
-                                                                   int32_t NT, int32_t Hkv, const uint32_t *sub_class,
-                                                                   const int32_t *q_nnz, const int32_t *q_list,
-                                                                   const int32_t *k_nnz, const int32_t *k_list,
-                                                                   int32_t *cost, int32_t *q_order, int4 *k_raw,
-                                                                   int4 *k_items, int4 *k_split, int32_t *k_counts) {
+struct OrderArgs {
+  int32_t n_rows, n_cols, MT, NT, Hkv;
+  const uint32_t *sub_class;
+  const int32_t *q_nnz, *q_list, *k_nnz, *k_list;
+  int32_t *cost, *q_order;
+  int4 *k_raw, *k_items, *k_split;
+  int32_t *k_counts;
+};
+
+__device__ void work_order(const OrderArgs &a) {
+  const int32_t n_rows = a.n_rows, n_cols = a.n_cols, MT = a.MT, NT = a.NT, Hkv = a.Hkv;
+  const uint32_t *sub_class = a.sub_class;
+  const int32_t *q_nnz = a.q_nnz, *q_list = a.q_list, *k_nnz = a.k_nnz, *k_list = a.k_list;
+  int32_t *cost = a.cost, *q_order = a.q_order, *k_counts = a.k_counts;
+  int4 *k_raw = a.k_raw, *k_items = a.k_items, *k_split = a.k_split;
   __shared__ int32_t bins[kOrderBins];
   __shared__ int32_t wave_sum[kOrderThreads / 64];
   __shared__ int64_t red[kOrderThreads / 64];
@@ -359,31 +396,56 @@ __global__ __launch_bounds__(kOrderThreads) void work_order_kernel(int32_t n_row
 }
 
 
+// The work order (workgroup 0) and the RoPE table (the other workgroups):
+// both depend on the layout alone, so one launch runs them side by side, the
+// single-workgroup order first so that it starts at once.
+__global__ __launch_bounds__(kOrderThreads) void rope_order_kernel(RopeArgs ra, OrderArgs oa) {
+  if (blockIdx.x == 0) {
+    work_order(oa);
+    return;
+  }
+  rope_entry(ra, (int64_t)(blockIdx.x - 1) * kOrderThreads + threadIdx.x);
+}
+
 template <int D>
 void launch_absmax_d(int32_t B, int32_t L, const AbsmaxJob *jobs, hipStream_t s) {
   absmax_kernel<D><<<dim3((L + kAbsTokens - 1) / kAbsTokens, jobs[1].hb_end, B), 256, 0, s>>>(L, jobs[0], jobs[1]);
 }
 
 template <int D, bool ROPE, bool ROWS>
-void launch_pack_d(int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group, const void *x,
-                   const int32_t *slot_tok, const float2 *table, const uint32_t *pmax, uint16_t *rows,
-                   int32_t *erow, int32_t *etile, hipStream_t s) {
+void launch_pack_d(int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x, const int32_t *slot_tok,
+                   const float2 *table, const uint32_t *pmax, uint16_t *rows, int32_t *erow, int32_t *etile,
+                   hipStream_t s) {
   const unsigned hgroups = (unsigned)((H + kPackHeads - 1) / kPackHeads);
   const dim3 grid(hgroups * (unsigned)(Lp / kPackSlots), 1, B);
-  pack_kernel<D, ROPE, ROWS><<<grid, 256, 0, s>>>(L, Lp, H, group, static_cast<const uint16_t *>(x), slot_tok, table,
-                                                 pmax, rows, erow, etile);
+  pack_kernel<D, ROPE, ROWS><<<grid, 256, 0, s>>>(L, Lp, H, static_cast<const uint16_t *>(x), slot_tok, table, pmax,
+                                                 rows, erow, etile);
+}
+
+template <int D>
+void launch_pack_kv_d(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+  const unsigned hgroups = (unsigned)((in.Hkv + kPackHeads - 1) / kPackHeads);
+  const dim3 grid(hgroups * (unsigned)(ws.Lp / kPackSlots), 2, in.B);
+  pack_kv_kernel<D><<<grid, 256, 0, s>>>(in.L, ws.Lp, in.Hkv, static_cast<const uint16_t *>(in.k),
+                                        static_cast<const uint16_t *>(in.v), in.layout.slot_tok, ws.rope, ws.mk,
+                                        ws.mv, ws.kr, ws.vr);
 }
 
 }  // namespace
 
-// RoPE table + clearing of the plane maxima (they start at zero).
-void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+// The work order, the RoPE table and the clearing of the plane maxima (they
+// start at zero), in one launch.
+void launch_rope_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int32_t half = in.D / 2;
   const int64_t total = (int64_t)in.B * ws.Lp * half;
   const int64_t n = total > ws.n_pmax ? total : (int64_t)ws.n_pmax;
-  rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(in.B, in.L, ws.Lp, half, log2(in.rope_theta),
-                                                                in.layout.tok_pos, in.layout.slot_tok, ws.rope,
-                                                                ws.pmax, ws.n_pmax);
+  const RopeArgs ra = {in.B, in.L, ws.Lp, half, log2(in.rope_theta), in.layout.tok_pos, in.layout.slot_tok,
+                       ws.rope, ws.pmax, ws.n_pmax};
+  const int32_t MT = ws.Lp / OPR_ATTN_BLOCK, NT = MT;
+  const OrderArgs oa = {in.B * MT, in.B * NT, MT, NT, in.Hkv, in.layout.sub_class, in.layout.q_nnz,
+                        in.layout.q_list, in.layout.k_nnz, in.layout.k_list, ws.order_cost, ws.q_order,
+                        ws.k_raw, ws.k_items, ws.k_split, ws.k_counts};
+  rope_order_kernel<<<(unsigned)(1 + (n + kOrderThreads - 1) / kOrderThreads), kOrderThreads, 0, s>>>(ra, oa);
 }
 
 // Plane maxima of k (times sqrt(2), the RoPE bound) and of v.
@@ -398,34 +460,18 @@ void launch_absmax_kv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
 
 // q after RoPE, one scale per row of each (row, head).
 void launch_pack_q(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
-  const int32_t group = in.Hq / in.Hkv;
   if (in.D == 64)
-    launch_pack_d<64, true, true>(in.B, in.L, ws.Lp, in.Hq, group, in.q, in.layout.slot_tok, ws.rope, nullptr,
-                                  ws.qr, ws.eqq, ws.eqt, s);
+    launch_pack_d<64, true, true>(in.B, in.L, ws.Lp, in.Hq, in.q, in.layout.slot_tok, ws.rope, nullptr, ws.qr,
+                                  ws.eqq, ws.eqt, s);
   else
-    launch_pack_d<128, true, true>(in.B, in.L, ws.Lp, in.Hq, group, in.q, in.layout.slot_tok, ws.rope, nullptr,
-                                   ws.qr, ws.eqq, ws.eqt, s);
+    launch_pack_d<128, true, true>(in.B, in.L, ws.Lp, in.Hq, in.q, in.layout.slot_tok, ws.rope, nullptr, ws.qr,
+                                   ws.eqq, ws.eqt, s);
 }
 
-// k (RoPE) or v, one scale per plane.
-void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,
-                     const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
-                     uint16_t *rows, hipStream_t s) {
-  if (D == 64) {
-    if (rope) launch_pack_d<64, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
-    else launch_pack_d<64, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
-  } else {
-    if (rope) launch_pack_d<128, true, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
-    else launch_pack_d<128, false, false>(B, L, Lp, H, group, x, slot_tok, table, pmax, rows, nullptr, nullptr, s);
-  }
-}
-
-void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
-  const int32_t MT = ws.Lp / OPR_ATTN_BLOCK, NT = MT;
-  work_order_kernel<<<1, kOrderThreads, 0, s>>>(in.B * MT, in.B * NT, MT, NT, in.Hkv, in.layout.sub_class,
-                                               in.layout.q_nnz, in.layout.q_list, in.layout.k_nnz, in.layout.k_list,
-                                               ws.order_cost, ws.q_order, ws.k_raw, ws.k_items, ws.k_split,
-                                               ws.k_counts);
+// k (after RoPE) and v, one scale per plane.
+void launch_pack_kv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+  if (in.D == 64) launch_pack_kv_d<64>(in, ws, s);
+  else launch_pack_kv_d<128>(in, ws, s);
 }
 
 }  // namespace opr

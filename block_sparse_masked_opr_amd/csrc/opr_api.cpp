@@ -12,13 +12,10 @@
 namespace opr {
 
 // launchers defined in the .hip files
-void launch_rope_table(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
+void launch_rope_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_absmax_kv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_pack_q(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
-void launch_pack_any(int D, bool rope, int32_t B, int32_t L, int32_t Lp, int32_t H, int32_t group,
-                     const void *x, const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
-                     uint16_t *rows, hipStream_t s);
-void launch_work_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
+void launch_pack_kv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, float *lse,
                                   const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_bwd_kernels(const opr_attn_in &in, float scale, const void *o, const float *lse,
@@ -180,13 +177,10 @@ static void mark(const opr_attn_in *in, int i, hipStream_t s) {
 // forward kernel converts q itself (and leaves q' there); a backward that does
 // not reuse the forward's workspace packs q here (pack_q).
 static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_t stream, bool pack_q) {
-  launch_rope_table(in, ws, stream);
+  launch_rope_order(in, ws, stream);
   launch_absmax_kv(in, ws, stream);
   if (pack_q) launch_pack_q(in, ws, stream);
-  const int32_t *st = in.layout.slot_tok;
-  launch_pack_any(in.D, true, in.B, in.L, ws.Lp, in.Hkv, 1, in.k, st, ws.rope, ws.mk, ws.kr, stream);
-  launch_pack_any(in.D, false, in.B, in.L, ws.Lp, in.Hkv, 1, in.v, st, ws.rope, ws.mv, ws.vr, stream);
-  launch_work_order(in, ws, stream);
+  launch_pack_kv(in, ws, stream);
 }
 
 static opr_status hip_status() {
