@@ -15,14 +15,10 @@ static void reached(const char *what) {
   std::abort();
 }
 
-void launch_rope_table(const opr_attn_in &, const AttnWs &, hipStream_t) { reached("launch_rope_table"); }
+void launch_rope_order(const opr_attn_in &, const AttnWs &, hipStream_t) { reached("launch_rope_order"); }
 void launch_absmax_kv(const opr_attn_in &, const AttnWs &, hipStream_t) { reached("launch_absmax_kv"); }
 void launch_pack_q(const opr_attn_in &, const AttnWs &, hipStream_t) { reached("launch_pack_q"); }
-void launch_pack_any(int, bool, int32_t, int32_t, int32_t, int32_t, int32_t, const void *, const int32_t *,
-                     const float2 *, const uint32_t *, uint16_t *, hipStream_t) {
-  reached("launch_pack_any");
-}
-void launch_work_order(const opr_attn_in &, const AttnWs &, hipStream_t) { reached("launch_work_order"); }
+void launch_pack_kv(const opr_attn_in &, const AttnWs &, hipStream_t) { reached("launch_pack_kv"); }
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &, float, void *, float *, const AttnWs &, hipStream_t) {
   reached("launch_attn_fwd_kernel");
   return hipSuccess;
