@@ -189,8 +189,10 @@ class Runner:
         B = len(rows)
         self.t = t
         self.lay = Bd.opr_build_layout(rows, L, 128, 128, device=dev)
-        cpr, tpc, turns = I.flatten_rows(rows)
-        self.lws = torch.empty(Bd.opr_build_layout_workspace_size(B, L, len(tpc), len(turns)), dtype=torch.uint8, device=dev)
+        # the host lists in pinned memory: the layout reads them in place
+        self.lists = Bd.pinned_lists(rows)
+        self.lws = torch.empty(Bd.opr_build_layout_workspace_size(B, L, self.lists[3], self.lists[4]),
+                               dtype=torch.uint8, device=dev)
         # one workspace: the backward reuses the forward state at its start
         self.ws = torch.empty(Bd.opr_attn_workspace_size(B, L, Hq, Hkv, D, True), dtype=torch.uint8, device=dev)
         self.o = torch.empty_like(t["q"])
@@ -201,7 +203,8 @@ class Runner:
 
     def step(self, ev_f=None, ev_b=None):
         Bd, t = self.Bd, self.t
-        Bd.opr_build_layout(self.rows, self.L, 128, 128, device=self.o.device, workspace=self.lws, out=self.lay)
+        Bd.opr_build_layout(self.rows, self.L, 128, 128, device=self.o.device, workspace=self.lws, out=self.lay,
+                            lists=self.lists)
         Bd.opr_attn_fwd(t["q"], t["k"], t["v"], self.lay, self.theta, workspace=self.ws,
                         out=(self.o, self.lse), events=ev_f)
         Bd.opr_attn_bwd(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], self.lay, self.theta,
@@ -246,9 +249,9 @@ class BlockRunner:
                                    torch.rand(D, generator=g, device=dev) + 0.5, Hq, Hkv, D)
         self.x, self.dy = rn((B, L, dm), 1.0), rn((B, L, dm), 1.0)
         self.lay = Bd.opr_build_layout(rows, L, 128, 128, device=dev)
-        cpr, tpc, turns = I.flatten_rows(rows)
-        self.lws = torch.empty(Bd.opr_build_layout_workspace_size(B, L, len(tpc), len(turns)), dtype=torch.uint8,
-                               device=dev)
+        self.lists = Bd.pinned_lists(rows)
+        self.lws = torch.empty(Bd.opr_build_layout_workspace_size(B, L, self.lists[3], self.lists[4]),
+                               dtype=torch.uint8, device=dev)
         self.ws = torch.empty(Bd.opr_block_workspace_size(B, L, Hq, Hkv, D, dm, True), dtype=torch.uint8, device=dev)
         e = dict(device=dev)
         self.fwd_out = (torch.empty((B, L, dm), dtype=torch.bfloat16, **e),
@@ -261,7 +264,8 @@ class BlockRunner:
 
     def step(self, ev_f=None, ev_b=None):
         Bd = self.Bd
-        Bd.opr_build_layout(self.rows, self.L, 128, 128, device=self.x.device, workspace=self.lws, out=self.lay)
+        Bd.opr_build_layout(self.rows, self.L, 128, 128, device=self.x.device, workspace=self.lws, out=self.lay,
+                            lists=self.lists)
         y, qkv, o, lse = Bd.opr_block_fwd(self.x, self.wts, self.lay, self.theta, workspace=self.ws,
                                           out=self.fwd_out, events=ev_f)
         Bd.opr_block_bwd(self.x, self.wts, self.lay, qkv, o, lse, self.dy, self.theta, workspace=self.ws,

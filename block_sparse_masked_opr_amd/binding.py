@@ -190,18 +190,33 @@ class Layout:
         return out
 
 
+def pinned_lists(rows: Sequence):
+    """The host lists of opr_build_layout (convs per row, turns per
+    conversation, turns) in page-locked memory, which the layout's first kernel
+    reads in place (no copy on the stream).  Build once, pass as ``lists``."""
+    cpr, tpc, turns = inputs.flatten_rows(rows)
+    return tuple(torch.from_numpy(np.ascontiguousarray(x if len(x) else np.zeros(1, np.int32),
+                                                       dtype=np.int32)).pin_memory()
+                 for x in (cpr, tpc, turns)) + (len(tpc), len(turns))
+
+
 def opr_build_layout(rows: Sequence, L: int, block_q: int = OPR_ATTN_BLOCK,
                      block_k: int = OPR_ATTN_BLOCK, device="cuda",
                      workspace: Optional[torch.Tensor] = None, out: Optional[Layout] = None,
-                     order: int = OPR_ORDER_ATTENTION) -> Layout:
+                     order: int = OPR_ORDER_ATTENTION, lists=None) -> Layout:
     """rows: list of rows, each a list of conversations of (h, t, r_in, r_out)
     turns.  ``out``: a Layout of the same (B, L, block_q, block_k, order) to
     refill.  ``order``: OPR_ORDER_ATTENTION (what the attention calls need) or
-    OPR_ORDER_PACKED (the tile schedule over the packed rows)."""
+    OPR_ORDER_PACKED (the tile schedule over the packed rows).  ``lists``: the
+    rows' host lists from pinned_lists(rows), else they are flattened into
+    pageable arrays here (copied with hipMemcpyAsync)."""
     device = torch.device(device)
     B = len(rows)
-    cpr, tpc, turns = inputs.flatten_rows(rows)
-    C, T = len(tpc), len(turns)
+    if lists is not None:
+        C, T = lists[3], lists[4]
+    else:
+        cpr, tpc, turns = inputs.flatten_rows(rows)
+        C, T = len(tpc), len(turns)
     if out is not None and (out.B, out.L, out.block_q, out.block_k, out.order) == (B, L, block_q, block_k, order):
         lay = out
     else:
@@ -211,13 +226,16 @@ def opr_build_layout(rows: Sequence, L: int, block_q: int = OPR_ATTN_BLOCK,
         raise OprError(OPR_E_INVALID, "opr_build_layout_workspace_size")
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    cpr = np.ascontiguousarray(cpr, dtype=np.int32)
-    tpc = np.ascontiguousarray(tpc if C else np.zeros(1, np.int32), dtype=np.int32)
-    turns = np.ascontiguousarray(turns if T else np.zeros((1, 4), np.int32), dtype=np.int32)
+    if lists is not None:
+        p_cpr, p_tpc, p_turns = (x.data_ptr() for x in lists[:3])
+    else:
+        cpr = np.ascontiguousarray(cpr, dtype=np.int32)
+        tpc = np.ascontiguousarray(tpc if C else np.zeros(1, np.int32), dtype=np.int32)
+        turns = np.ascontiguousarray(turns if T else np.zeros((1, 4), np.int32), dtype=np.int32)
+        p_cpr, p_tpc, p_turns = cpr.ctypes.data, tpc.ctypes.data, turns.ctypes.data
     cs = lay.c_struct()
-    st = LIB.opr_build_layout(B, L, block_q, block_k, cpr.ctypes.data, tpc.ctypes.data,
-                              turns.ctypes.data, workspace.data_ptr(), workspace.numel(),
-                              ctypes.byref(cs), _stream(device))
+    st = LIB.opr_build_layout(B, L, block_q, block_k, p_cpr, p_tpc, p_turns, workspace.data_ptr(),
+                              workspace.numel(), ctypes.byref(cs), _stream(device))
     _check(st, "opr_build_layout")
     return lay
 

@@ -88,6 +88,14 @@ __device__ inline int last_le(const int32_t *a, int lo, int hi, int32_t x) {
 __global__ __launch_bounds__(kPrepThreads) void layout_prep(int32_t B, int32_t C, int32_t T,
                                                             LayoutWs ws) {
   __shared__ int32_t sh[kPrepThreads];
+  if (ws.src_cpr) {
+    // the host arrays, read in place (4-byte words: any opr_turn alignment)
+    int32_t *tw = reinterpret_cast<int32_t *>(ws.turns);
+    for (int i = threadIdx.x; i < B; i += kPrepThreads) ws.cpr[i] = ws.src_cpr[i];
+    for (int i = threadIdx.x; i < C; i += kPrepThreads) ws.tpc[i] = ws.src_tpc[i];
+    for (int i = threadIdx.x; i < 4 * T; i += kPrepThreads) tw[i] = ws.src_turns[i];
+    __syncthreads();  // the block's own copies are visible to all its threads
+  }
   const int32_t *cpr = ws.cpr;
   const int32_t *tpc = ws.tpc;
   const int4 *turns = ws.turns;
@@ -419,6 +427,7 @@ size_t carve_layout_ws(void *p, int32_t B, int32_t L, int32_t C, int32_t T, Layo
   w.turn_conv = cv.take<int32_t>(T > 0 ? T : 1);
   w.row_turn0 = cv.take<int32_t>(B + 1);
   w.gturn = cv.take<int32_t>((size_t)B * L);
+  w.src_cpr = w.src_tpc = w.src_turns = nullptr;
   if (o) *o = w;
   return cv.off;
 }

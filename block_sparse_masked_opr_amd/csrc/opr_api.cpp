@@ -316,18 +316,49 @@ static opr_status check_layout_args(int32_t B, int32_t L, int32_t block_q, int32
 
 // Copies the host segment arrays into the workspace and launches the layout
 // kernels (arguments already validated).
+// The device address of a host array that the GPU can read in place
+// (page-locked and mapped into the device's address space), else null.  For
+// pageable memory the query fails; that is not an error of the call, so the
+// error it leaves is cleared.
+static const void *mapped_host(const void *p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (a.type != hipMemoryTypeHost || !a.devicePointer) return nullptr;
+  // the device address of p itself, also when p lies inside the allocation
+  // and the query reports the allocation's own addresses
+  const char *d = static_cast<const char *>(a.devicePointer);
+  if (a.hostPointer && a.hostPointer != p) d += static_cast<const char *>(p) - static_cast<const char *>(a.hostPointer);
+  return d;
+}
+
 static opr_status run_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
                                    const int32_t *convs_per_row, const int32_t *turns_per_conv,
                                    const opr_turn *turns, int64_t C, int64_t T, void *workspace,
                                    const opr_layout *out, hipStream_t stream) {
   LayoutWs ws;
   carve_layout_ws(workspace, B, L, (int32_t)C, (int32_t)T, &ws);
-  if (hipMemcpyAsync(ws.cpr, convs_per_row, sizeof(int32_t) * B, hipMemcpyHostToDevice, stream) != hipSuccess)
-    return OPR_E_HIP;
-  if (C > 0 && hipMemcpyAsync(ws.tpc, turns_per_conv, sizeof(int32_t) * C, hipMemcpyHostToDevice, stream) != hipSuccess)
-    return OPR_E_HIP;
-  if (T > 0 && hipMemcpyAsync(ws.turns, turns, sizeof(opr_turn) * T, hipMemcpyHostToDevice, stream) != hipSuccess)
-    return OPR_E_HIP;
+  // Page-locked, mapped host arrays are read in place by the first kernel:
+  // no copy on the stream, so no wait between a copy engine and the compute
+  // queue.  Any other host memory goes through hipMemcpyAsync.
+  const void *dc = mapped_host(convs_per_row);
+  const void *dt = C > 0 ? mapped_host(turns_per_conv) : dc;
+  const void *du = T > 0 ? mapped_host(turns) : dc;
+  if (dc && dt && du) {
+    ws.src_cpr = static_cast<const int32_t *>(dc);
+    ws.src_tpc = static_cast<const int32_t *>(dt);
+    ws.src_turns = static_cast<const int32_t *>(du);
+  } else {
+    if (hipMemcpyAsync(ws.cpr, convs_per_row, sizeof(int32_t) * B, hipMemcpyHostToDevice, stream) != hipSuccess)
+      return OPR_E_HIP;
+    if (C > 0 &&
+        hipMemcpyAsync(ws.tpc, turns_per_conv, sizeof(int32_t) * C, hipMemcpyHostToDevice, stream) != hipSuccess)
+      return OPR_E_HIP;
+    if (T > 0 && hipMemcpyAsync(ws.turns, turns, sizeof(opr_turn) * T, hipMemcpyHostToDevice, stream) != hipSuccess)
+      return OPR_E_HIP;
+  }
   if (launch_build_layout(B, L, block_q, block_k, (int32_t)C, (int32_t)T, ws, *out, stream) != hipSuccess)
     return OPR_E_HIP;
   return hip_status();

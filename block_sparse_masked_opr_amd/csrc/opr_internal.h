@@ -40,6 +40,10 @@ struct LayoutWs {
   int32_t *cpr;         // [B]   convs per row (copied from the host)
   int32_t *tpc;         // [C]   turns per conversation (copied)
   int4 *turns;          // [T]   (h, t, r_in, r_out) (copied)
+  // The caller's host arrays at device addresses when they are page-locked
+  // and mapped (layout_prep copies them into cpr, tpc, turns itself), else
+  // null (they were copied with hipMemcpyAsync).
+  const int32_t *src_cpr, *src_tpc, *src_turns;
   int32_t *row_conv0;   // [B+1] first conversation of each row
   int32_t *conv_turn0;  // [C+1] first turn of each conversation
   int32_t *tok_g;       // [T+1] tokens before each turn, counted over all rows

@@ -142,8 +142,13 @@ typedef struct {
  * Errors: OPR_E_INVALID (null pointer, misaligned slot_qiv / slot_kiv,
  * negative count or length, bad B/L, unknown order),
  * OPR_E_UNSUPPORTED (block size), OPR_E_CAPACITY (a row longer than L, or
- * ws_bytes too small), OPR_E_HIP.  The host arrays are copied to the
- * workspace with hipMemcpyAsync before the call returns control.
+ * ws_bytes too small), OPR_E_HIP.
+ * Host arrays: when all three are in page-locked host memory mapped for the
+ * device (hipHostMalloc, or torch's pinned memory), the first kernel reads
+ * them in place and no copy is enqueued; otherwise they are copied to the
+ * workspace with hipMemcpyAsync (pageable memory is staged before the call
+ * returns).  Either way, keep them unchanged until the stream has run the
+ * call.
  */
 opr_status opr_build_layout(int32_t B, int32_t L, int32_t block_q, int32_t block_k,
                             const int32_t *convs_per_row, const int32_t *turns_per_conv,

@@ -135,3 +135,40 @@ def test_layout_batch_sampled_rows(B):
         s = O.schedule(ref, 0, 128, 128, order="attention")
         for f in ("tile_class", "sub_class", "q_nnz", "q_list", "k_nnz", "k_list"):
             np.testing.assert_array_equal(got[f][b], s[f], err_msg=f"{f} row {b}")
+
+
+def test_pinned_host_lists_match_pageable(B):
+    """Page-locked host lists are read in place by the first kernel (no copy
+    on the stream); pageable ones are copied with hipMemcpyAsync.  Both give
+    bit-identical layouts: random rows with empty segments and conversations,
+    and 3 rows of the 64 x 32768 batch, with the turn list at a 4-byte offset
+    inside its pinned allocation (not 16-byte aligned, not the allocation's
+    start)."""
+    import ctypes
+    dev = torch.device("cuda")
+    batch = I.layout_batch_rows(I.SEEDS["layout_batch"][0])
+    rnd = _random_rows(77, 3, 4, 5, 60)
+    cases = [("random", rnd, max(I.row_used(r) for r in rnd) + 5), ("batch rows 0-2", batch[:3], I.LAYOUT_BATCH[1])]
+    for label, rows, L in cases:
+        print(f"[layout] pinned host lists: {label}", flush=True)
+        ref = B.opr_build_layout(rows, L).numpy()
+        cpr, tpc, turns = I.flatten_rows(rows)
+        cpr = np.ascontiguousarray(cpr, dtype=np.int32)
+        tpc = np.ascontiguousarray(tpc, dtype=np.int32)
+        tw = np.ascontiguousarray(turns, dtype=np.int32).reshape(-1)
+        h_cpr = torch.from_numpy(cpr).pin_memory()
+        h_tpc = torch.from_numpy(tpc).pin_memory()
+        h_turns = torch.zeros(tw.size + 1, dtype=torch.int32).pin_memory()
+        h_turns[1:] = torch.from_numpy(tw)
+        lay = B.Layout(len(rows), L, 128, 128, dev, B.OPR_ORDER_ATTENTION)
+        ws = torch.empty(B.opr_build_layout_workspace_size(len(rows), L, len(tpc), len(tw) // 4), dtype=torch.uint8,
+                         device=dev)
+        st = lay.c_struct()
+        status = B.LIB.opr_build_layout(len(rows), L, 128, 128, h_cpr.data_ptr(), h_tpc.data_ptr(),
+                                        h_turns.data_ptr() + 4, ws.data_ptr(), ws.numel(), ctypes.byref(st),
+                                        torch.cuda.current_stream(dev).cuda_stream)
+        assert status == 0, B.opr_status_string(status)
+        torch.cuda.synchronize()
+        got = lay.numpy()
+        for f in ref:
+            np.testing.assert_array_equal(got[f], ref[f], err_msg=f"{f} {label}")
