@@ -426,8 +426,11 @@ def loss_step(torch, Bd, r, shape, steps, dev):
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
 
 
-def cpu_baseline(rows, L, shape, t_np):
-    """The fp64 oracle on a bounded sample: one conversation, one kv group."""
+def cpu_baseline(rows, L, shape, t_np, budget_s=10.0):
+    """The fp64 oracle on a bounded sample of the workload: the conversations
+    of row 0 in order, each with every q and kv head, fwd + bwd, until about
+    budget_s seconds of oracle time have been spent (at least one
+    conversation)."""
     from oracle import opr_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -435,20 +438,24 @@ def cpu_baseline(rows, L, shape, t_np):
     except Exception:
         threads = os.cpu_count()
     lay = O.layout(rows, L)
-    a, e = O.conv_range(lay, 0, 0)
-    g = shape.Hq // shape.Hkv
-    sub = {n: I.bf16_bits_to_f32(t_np[n][0:1, a:e]).astype(np.float64) for n in t_np}
-    q, k, v, do = sub["q"][:, :, :g], sub["k"][:, :, :1], sub["v"][:, :, :1], sub["do"][:, :, :g]
-    lay_c = O.layout([[rows[0][0]]], e - a)
-    P = O.useful_pairs(lay_c)
-    t0 = time.perf_counter()
-    O.attn_fwd(q, k, v, lay_c, shape.theta)
-    O.attn_bwd(q, k, v, do, lay_c, shape.theta)
-    dt = time.perf_counter() - t0
-    flops = 12.0 * shape.D * g * P
+    flops, dt, done, toks = 0.0, 0.0, 0, 0
+    for c in range(O.n_convs(lay, 0)):
+        a, e = O.conv_range(lay, 0, c)
+        if e <= a:
+            continue
+        sub = {n: I.bf16_bits_to_f32(t_np[n][0:1, a:e]).astype(np.float64) for n in t_np}
+        lay_c = O.layout([[rows[0][c]]], e - a)
+        t0 = time.perf_counter()
+        O.attn_fwd(sub["q"], sub["k"], sub["v"], lay_c, shape.theta)
+        O.attn_bwd(sub["q"], sub["k"], sub["v"], sub["do"], lay_c, shape.theta)
+        dt += time.perf_counter() - t0
+        flops += 12.0 * shape.D * shape.Hq * O.useful_pairs(lay_c)
+        done, toks = done + 1, toks + (e - a)
+        if dt >= budget_s:
+            break
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"row 0 conversation 0 ({e - a} tokens, {P} pairs), q heads 0-{g - 1} over kv head 0, "
-                      f"fwd+bwd, {dt:.2f} s"}
+            "sample": f"row 0, its first {done} conversations ({toks} tokens), all {shape.Hq} q / {shape.Hkv} kv "
+                      f"heads, fwd+bwd, {dt:.1f} s"}
 
 
 def depth_stages(Ns, steps=10):

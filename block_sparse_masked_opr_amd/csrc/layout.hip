@@ -85,15 +85,32 @@ __device__ inline int last_le(const int32_t *a, int lo, int hi, int32_t x) {
   return lo;
 }
 
+// n words from host memory mapped for the device into the workspace.  Each
+// thread has kStageIn loads in flight before it stores: a read crosses the
+// host link, so one round trip per word would dominate.
+constexpr int kStageIn = 8;
+__device__ void stage_in(const int32_t *src, int32_t *dst, int n) {
+  for (int base = 0; base < n; base += kPrepThreads * kStageIn) {
+    int32_t v[kStageIn];
+#pragma unroll
+    for (int u = 0; u < kStageIn; ++u)  // unconditional loads (index clamped): no branch between them
+      v[u] = src[min(base + u * kPrepThreads + (int)threadIdx.x, n - 1)];
+#pragma unroll
+    for (int u = 0; u < kStageIn; ++u) {
+      const int i = base + u * kPrepThreads + (int)threadIdx.x;
+      if (i < n) dst[i] = v[u];
+    }
+  }
+}
+
 __global__ __launch_bounds__(kPrepThreads) void layout_prep(int32_t B, int32_t C, int32_t T,
                                                             LayoutWs ws) {
   __shared__ int32_t sh[kPrepThreads];
   if (ws.src_cpr) {
     // the host arrays, read in place (4-byte words: any opr_turn alignment)
-    int32_t *tw = reinterpret_cast<int32_t *>(ws.turns);
-    for (int i = threadIdx.x; i < B; i += kPrepThreads) ws.cpr[i] = ws.src_cpr[i];
-    for (int i = threadIdx.x; i < C; i += kPrepThreads) ws.tpc[i] = ws.src_tpc[i];
-    for (int i = threadIdx.x; i < 4 * T; i += kPrepThreads) tw[i] = ws.src_turns[i];
+    stage_in(ws.src_cpr, ws.cpr, B);
+    stage_in(ws.src_tpc, ws.tpc, C);
+    stage_in(ws.src_turns, reinterpret_cast<int32_t *>(ws.turns), 4 * T);
     __syncthreads();  // the block's own copies are visible to all its threads
   }
   const int32_t *cpr = ws.cpr;
