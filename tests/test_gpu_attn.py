@@ -300,6 +300,31 @@ def test_scaled_inputs(B):
     assert_close("LSE", got["lse"].transpose(0, 2, 1)[live], lse.transpose(0, 2, 1)[live])
 
 
+def test_input_range_edges(B):
+    """Inputs near the ends of the stated range (largest magnitude per row or
+    plane in [2^-46, 2^75)): q x 2^-40 and k x 2^40 (scores unchanged, operand
+    exponents near +52 and -28), v x 2^70 (exponent near -58) and dout x 2^-44
+    (near +56).  Every output is held relative to its largest magnitude, as in
+    test_scaled_inputs."""
+    rows = [[[(50, 120, 40, 40), (30, 60, 70, 70)], [(100, 0, 30, 30)]]]
+    L = I.row_used(rows[0]) + 11
+    t = I.make_tensors(1, L, 4, 1, 128, seed=98)
+    f = {"q": 2.0 ** -40, "k": 2.0 ** 40, "v": 2.0 ** 70, "do": 2.0 ** -44}
+    ts = {n: I.round_to_bf16_bits(I.bf16_bits_to_f32(t[n]) * np.float32(f[n])) for n in t}
+    got = run_gpu(B, rows, L, ts)
+    lay = O.layout(rows, L)
+    q, k, v, do = (bf16_f64(ts[n]) for n in ("q", "k", "v", "do"))
+    o, lse = O.attn_fwd(q, k, v, lay, THETA)
+    dq, dk, dv = O.attn_bwd(q, k, v, do, lay, THETA)
+    live = lay["type"] != O.PAD
+    print("[attn] input range edges", flush=True)
+    for n, x, ref in (("O", got["o"], o), ("dq", got["dq"], dq), ("dk", got["dk"], dk), ("dv", got["dv"], dv)):
+        assert np.isfinite(x).all(), n
+        top = float(np.abs(ref[live]).max())
+        assert_close(n, x[live] / top, ref[live] / top, max_abs=5e-3)
+    assert_close("LSE", got["lse"].transpose(0, 2, 1)[live], lse.transpose(0, 2, 1)[live])
+
+
 def _scaled(t, f):
     """bf16 inputs times per-element factors f[name] (broadcast), rounded to bf16 once."""
     out = dict(t)
