@@ -316,17 +316,18 @@ static opr_status check_layout_args(int32_t B, int32_t L, int32_t block_q, int32
 
 // Copies the host segment arrays into the workspace and launches the layout
 // kernels (arguments already validated).
-// The device address of a host array that the GPU can read in place
-// (page-locked and mapped into the device's address space), else null.  For
-// pageable memory the query fails; that is not an error of the call, so the
-// error it leaves is cleared.
+// The device address of a host array that the current GPU can read in place
+// (page-locked and mapped into its address space), else null.  For pageable
+// memory the query fails; that is not an error of the call, so the error it
+// leaves is cleared.  Memory reported for another device takes the copy.
 static const void *mapped_host(const void *p) {
   hipPointerAttribute_t a;
-  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+  int dev = -1;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess || hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return nullptr;
   }
-  if (a.type != hipMemoryTypeHost || !a.devicePointer) return nullptr;
+  if (a.type != hipMemoryTypeHost || !a.devicePointer || a.device != dev) return nullptr;
   // the device address of p itself, also when p lies inside the allocation
   // and the query reports the allocation's own addresses
   const char *d = static_cast<const char *>(a.devicePointer);
