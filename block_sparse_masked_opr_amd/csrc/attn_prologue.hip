@@ -1,13 +1,13 @@
 // Prologue kernels of the attention path.  Everything here is indexed by
 // slot (attention order): slot s < L holds token slot_tok[s] of the layout,
-// slots L .. Lp-1 are empty and padded with zeros.  Three launches:
+// slots L .. Lp-1 are empty and padded with zeros.  Two launches:
 //  - rope_order_kernel: the longest-first work order of the attention kernels
-//    (one workgroup) beside the RoPE table at the slots' strategic position
-//    ids (and the reset of the plane maxima); both need the layout alone,
-//  - absmax_kernel: the largest magnitude of every (row, kv head) plane of k
-//    and v,
-//  - pack_kv_kernel: head-major fp16 copies of k (after RoPE) and v in slot
-//    order with one power-of-two scale per plane.
+//    (one workgroup), the partial maxima of every (row, kv head) plane of k
+//    and v over 256-token blocks, and the RoPE table at the slots' strategic
+//    position ids; all three need only the inputs and the layout,
+//  - pack_kv_kernel: each workgroup reduces its planes' partial maxima, then
+//    writes head-major fp16 copies of k (after RoPE) and v in slot order with
+//    one power-of-two scale per plane.
 // pack_kernel makes the same copy of q, one scale per row (token and head),
 // for a backward that does not reuse the forward's state (the forward kernel
 // converts q itself).
@@ -51,61 +51,60 @@ __device__ __forceinline__ void rope_entry(const RopeArgs &a, int64_t gid) {
   a.table[gid] = make_float2((float)cs, (float)sn);
 }
 
-// Largest |x| of each (row, head) plane of x [B][L][H][D] bf16, times
-// `factor` (sqrt(2) bound of RoPE on a pair, rounded up), into pmax[b][h] as
-// float bits.  A workgroup covers kAbsTokens tokens of up to HPB heads:
-// thread (token row r, head hl, chunk j) reads 16-byte chunk j of head hl of
-// every tpr-th token from r, so each D/8-lane group reads one head's whole row
-// and a wave reads contiguous runs; with fewer heads than HPB the spare
-// threads take further token rows.
-constexpr int kAbsTokens = 64;
-
-// One launch covers k and v: blockIdx.y runs over the head blocks of job 0,
-// then job 1.
-struct AbsmaxJob {
-  const uint16_t *x;  // [B][L][H][D] bf16
-  uint32_t *pmax;     // [B][H]
-  int32_t H;
-  int32_t hb_end;     // one past this job's last head block (cumulative)
-  float factor;
+// Largest |x| of each (row, head) plane of k and v [B][L][H][D] bf16 (k
+// times sqrt(2), RoPE's bound on a pair, rounded up), as partial maxima over
+// kAbsSlots-token blocks: part[job][b][h][x] (float bits; job 0 = k, 1 = v).
+// No atomics into shared words, so nothing has to be cleared first and the
+// workgroups run in the same launch as the work order and the RoPE table.  A
+// workgroup of NT threads covers one token block of up to HPB heads: thread
+// (token row r, head hl, chunk j) reads 16-byte chunk j of head hl of every
+// tpr-th token from r, so each D/8-lane group reads one head's whole row and a
+// wave reads contiguous runs; with fewer heads than HPB the spare threads take
+// further token rows.
+struct AbsArgs {
+  const uint16_t *k, *v;    // [B][L][H][D] bf16
+  uint32_t *part;           // [2][B][H][nx]
+  int32_t B, L, H, nx, hb;  // nx token blocks, hb head blocks per (job, row)
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, AbsmaxJob j1) {
-  constexpr int CPH = D / 8, HPB = 256 / CPH;
-  const int yb = blockIdx.y;
-  const bool in0 = yb < j0.hb_end;
-  const uint16_t *x = in0 ? j0.x : j1.x;
-  uint32_t *pmax = in0 ? j0.pmax : j1.pmax;
-  const int32_t H = in0 ? j0.H : j1.H;
-  const float factor = in0 ? j0.factor : j1.factor;
-  const int hb = yb - (in0 ? 0 : j0.hb_end);
-  const int b = blockIdx.z, tid = threadIdx.x;
+template <int D, int NT>
+__device__ void plane_max_part(const AbsArgs &a, int64_t blk) {
+  constexpr int CPH = D / 8, HPB = NT / CPH;
+  const int xb = (int)(blk % a.nx);
+  int64_t rest = blk / a.nx;
+  const int hb = (int)(rest % a.hb);
+  rest /= a.hb;
+  const int b = (int)(rest % a.B);
+  const int job = (int)(rest / a.B);
+  const uint16_t *x = job == 0 ? a.k : a.v;
+  const float factor = job == 0 ? 1.4142136f : 1.0f;
+  const int H = a.H, L = a.L, tid = threadIdx.x;
   // the block's heads [hb * HPB, hb * HPB + nh); threads beyond one token row
   // of them take further tokens (tpr token rows per pass)
   const int nh = min(HPB, H - hb * HPB);
-  const int row = nh * CPH, tpr = 256 / row;
+  const int row = nh * CPH, tpr = NT / row;
   const int r = tid / row, hl = (tid % row) / CPH, j = tid % CPH;
   const int h = hb * HPB + hl;
-  const int t0 = blockIdx.x * kAbsTokens;
+  const int t0 = xb * kAbsSlots;
   uint32_t m = 0u;  // float bits of the largest |x| (non-negative: integer order)
   if (r < tpr) {
     const uint16_t *src = x + (((int64_t)b * L + t0) * H + h) * D + j * 8;
-    const int nt = min(kAbsTokens, L - t0);
+    const int nt = min(kAbsSlots, L - t0);
 #pragma unroll 8
     for (int t = r; t < nt; t += tpr)
       m = max(m, absmax8_bf16_bits(*reinterpret_cast<const uint4 *>(src + (int64_t)t * H * D)));
   }
 #pragma unroll
   for (int off = CPH / 2; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  // one atomic per head and workgroup: the token rows meet in LDS first
-  __shared__ uint32_t hm[256 / CPH];
+  // the token rows meet in LDS
+  __shared__ uint32_t hm[HPB];
   if (tid < HPB) hm[tid] = 0u;
   __syncthreads();
   if (j == 0 && r < tpr && m > 0u) atomicMax(&hm[hl], m);
   __syncthreads();
-  if (tid < nh && hm[tid] > 0u)
-    atomicMax(pmax + (int64_t)b * H + hb * HPB + tid, __float_as_uint(__uint_as_float(hm[tid]) * factor));
+  if (tid < nh)
+    a.part[(((int64_t)job * a.B + b) * H + hb * HPB + tid) * a.nx + xb] =
+        __float_as_uint(__uint_as_float(hm[tid]) * factor);
 }
 
 // One workgroup per (64-slot block, group of kPackHeads heads, row): 4
@@ -114,7 +113,8 @@ __global__ __launch_bounds__(256) void absmax_kernel(int32_t L, AbsmaxJob j0, Ab
 // cosines and sines in registers and walk the heads.
 // x: [B][L][H][D] bf16 -> rows [B][H][Lp][D] in slot order, fp16(x' * 2^e),
 // x' = RoPE(x) or x.
-// ROWS = false: e is the exponent of the head's plane maximum pmax[b][h].
+// ROWS = false: e is the exponent of the head's plane maximum hmax[h - h0]
+// (the caller reduces it for the block's heads).
 // ROWS = true: e is the exponent of the row's own largest |x'| (kExpMax for
 // an all-zero row), reduced over the slot's 4 threads and stored in
 // erow[b][h][s]; the smallest over the wave's kTile rows goes to
@@ -125,7 +125,7 @@ constexpr int kPackSlots = 64;
 
 template <int D, bool ROPE, bool ROWS>
 __device__ __forceinline__ void pack_rows(unsigned bx, int b, int32_t L, int32_t Lp, int32_t H, const uint16_t *x,
-                                          const int32_t *slot_tok, const float2 *table, const uint32_t *pmax,
+                                          const int32_t *slot_tok, const float2 *table, const uint32_t *hmax,
                                           uint16_t *rows, int32_t *erow, int32_t *etile) {
   constexpr int HALF = D / 2;
   constexpr int PER = HALF / 4;  // pairs per thread (4 threads per slot)
@@ -183,7 +183,7 @@ __device__ __forceinline__ void pack_rows(unsigned bx, int b, int32_t L, int32_t
       for (int off = 4; off < 64; off <<= 1) mn = min(mn, __shfl_xor(mn, off));
       if (lane == 0) etile[((int64_t)b * H + h) * (Lp / kTile) + t0 / kTile + wave] = mn;
     } else {
-      ex = plane_exponent(pmax[(int64_t)b * H + h]);
+      ex = plane_exponent(hmax[h - h0]);
     }
     uint16_t lq[PER], hq[PER];
 #pragma unroll
@@ -202,23 +202,35 @@ __device__ __forceinline__ void pack_rows(unsigned bx, int b, int32_t L, int32_t
 
 template <int D, bool ROPE, bool ROWS>
 __global__ __launch_bounds__(256) void pack_kernel(int32_t L, int32_t Lp, int32_t H, const uint16_t *x,
-                                                   const int32_t *slot_tok, const float2 *table,
-                                                   const uint32_t *pmax, uint16_t *rows, int32_t *erow,
-                                                   int32_t *etile) {
-  pack_rows<D, ROPE, ROWS>(blockIdx.x, blockIdx.z, L, Lp, H, x, slot_tok, table, pmax, rows, erow, etile);
+                                                   const int32_t *slot_tok, const float2 *table, uint16_t *rows,
+                                                   int32_t *erow, int32_t *etile) {
+  pack_rows<D, ROPE, ROWS>(blockIdx.x, blockIdx.z, L, Lp, H, x, slot_tok, table, nullptr, rows, erow, etile);
 }
 
 // k (after RoPE; blockIdx.y = 0) and v (blockIdx.y = 1) in one launch, one
-// scale per plane.
+// scale per plane.  Each workgroup first reduces its heads' partial maxima;
+// the first slot block of each (row, head group) also writes the plane maxima
+// that the attention kernels read (mk, mv).
 template <int D>
 __global__ __launch_bounds__(256) void pack_kv_kernel(int32_t L, int32_t Lp, int32_t H, const uint16_t *k,
                                                       const uint16_t *v, const int32_t *slot_tok,
-                                                      const float2 *table, const uint32_t *mk, const uint32_t *mv,
-                                                      uint16_t *kr, uint16_t *vr) {
-  if (blockIdx.y == 0)
-    pack_rows<D, true, false>(blockIdx.x, blockIdx.z, L, Lp, H, k, slot_tok, table, mk, kr, nullptr, nullptr);
+                                                      const float2 *table, const uint32_t *part, int32_t nx,
+                                                      uint32_t *mk, uint32_t *mv, uint16_t *kr, uint16_t *vr) {
+  const int job = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int hgroups = (H + kPackHeads - 1) / kPackHeads;
+  const int h0 = (int)(blockIdx.x % (unsigned)hgroups) * kPackHeads;
+  const int nh = min(kPackHeads, H - h0);
+  __shared__ uint32_t hmax[kPackHeads];
+  if (tid < kPackHeads) hmax[tid] = 0u;
+  __syncthreads();
+  const uint32_t *pp = part + (((int64_t)job * gridDim.z + b) * H + h0) * nx;
+  for (int i = tid; i < nh * nx; i += 256) atomicMax(&hmax[i / nx], pp[i]);
+  __syncthreads();
+  if (blockIdx.x < (unsigned)hgroups && tid < nh) (job == 0 ? mk : mv)[(int64_t)b * H + h0 + tid] = hmax[tid];
+  if (job == 0)
+    pack_rows<D, true, false>(blockIdx.x, b, L, Lp, H, k, slot_tok, table, hmax, kr, nullptr, nullptr);
   else
-    pack_rows<D, false, false>(blockIdx.x, blockIdx.z, L, Lp, H, v, slot_tok, table, mv, vr, nullptr, nullptr);
+    pack_rows<D, false, false>(blockIdx.x, b, L, Lp, H, v, slot_tok, table, hmax, vr, nullptr, nullptr);
 }
 
 // Longest-first work order (see q_work_item): the q-tile rows (b*MT + m) by
@@ -396,30 +408,31 @@ __device__ void work_order(const OrderArgs &a) {
 }
 
 
-// The work order (workgroup 0) and the RoPE table (the other workgroups):
-// both depend on the layout alone, so one launch runs them side by side, the
-// single-workgroup order first so that it starts at once.
-__global__ __launch_bounds__(kOrderThreads) void rope_order_kernel(RopeArgs ra, OrderArgs oa) {
+// The work order (workgroup 0), the k/v partial maxima (the next n_abs
+// workgroups) and the RoPE table (the rest): all three depend on the inputs
+// alone, so one launch runs them side by side, the single-workgroup order
+// first so that it starts at once.
+template <int D>
+__global__ __launch_bounds__(kOrderThreads) void rope_order_kernel(RopeArgs ra, OrderArgs oa, AbsArgs aa,
+                                                                   int32_t n_abs) {
   if (blockIdx.x == 0) {
     work_order(oa);
     return;
   }
-  rope_entry(ra, (int64_t)(blockIdx.x - 1) * kOrderThreads + threadIdx.x);
-}
-
-template <int D>
-void launch_absmax_d(int32_t B, int32_t L, const AbsmaxJob *jobs, hipStream_t s) {
-  absmax_kernel<D><<<dim3((L + kAbsTokens - 1) / kAbsTokens, jobs[1].hb_end, B), 256, 0, s>>>(L, jobs[0], jobs[1]);
+  if ((int32_t)blockIdx.x <= n_abs) {
+    plane_max_part<D, kOrderThreads>(aa, (int64_t)blockIdx.x - 1);
+    return;
+  }
+  rope_entry(ra, (int64_t)(blockIdx.x - 1 - n_abs) * kOrderThreads + threadIdx.x);
 }
 
 template <int D, bool ROPE, bool ROWS>
 void launch_pack_d(int32_t B, int32_t L, int32_t Lp, int32_t H, const void *x, const int32_t *slot_tok,
-                   const float2 *table, const uint32_t *pmax, uint16_t *rows, int32_t *erow, int32_t *etile,
-                   hipStream_t s) {
+                   const float2 *table, uint16_t *rows, int32_t *erow, int32_t *etile, hipStream_t s) {
   const unsigned hgroups = (unsigned)((H + kPackHeads - 1) / kPackHeads);
   const dim3 grid(hgroups * (unsigned)(Lp / kPackSlots), 1, B);
-  pack_kernel<D, ROPE, ROWS><<<grid, 256, 0, s>>>(L, Lp, H, static_cast<const uint16_t *>(x), slot_tok, table, pmax,
-                                                 rows, erow, etile);
+  pack_kernel<D, ROPE, ROWS><<<grid, 256, 0, s>>>(L, Lp, H, static_cast<const uint16_t *>(x), slot_tok, table, rows,
+                                                 erow, etile);
 }
 
 template <int D>
@@ -427,45 +440,45 @@ void launch_pack_kv_d(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const unsigned hgroups = (unsigned)((in.Hkv + kPackHeads - 1) / kPackHeads);
   const dim3 grid(hgroups * (unsigned)(ws.Lp / kPackSlots), 2, in.B);
   pack_kv_kernel<D><<<grid, 256, 0, s>>>(in.L, ws.Lp, in.Hkv, static_cast<const uint16_t *>(in.k),
-                                        static_cast<const uint16_t *>(in.v), in.layout.slot_tok, ws.rope, ws.mk,
-                                        ws.mv, ws.kr, ws.vr);
+                                        static_cast<const uint16_t *>(in.v), in.layout.slot_tok, ws.rope,
+                                        ws.pmax_part, ws.n_part, ws.mk, ws.mv, ws.kr, ws.vr);
 }
 
-}  // namespace
-
-// The work order, the RoPE table and the clearing of the plane maxima (they
-// start at zero), in one launch.
-void launch_rope_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+template <int D>
+void launch_rope_order_d(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   const int32_t half = in.D / 2;
-  const int64_t total = (int64_t)in.B * ws.Lp * half;
-  const int64_t n = total > ws.n_pmax ? total : (int64_t)ws.n_pmax;
+  const int64_t n = (int64_t)in.B * ws.Lp * half;
   const RopeArgs ra = {in.B, in.L, ws.Lp, half, log2(in.rope_theta), in.layout.tok_pos, in.layout.slot_tok,
-                       ws.rope, ws.pmax, ws.n_pmax};
+                       ws.rope, nullptr, 0};
   const int32_t MT = ws.Lp / OPR_ATTN_BLOCK, NT = MT;
   const OrderArgs oa = {in.B * MT, in.B * NT, MT, NT, in.Hkv, in.layout.sub_class, in.layout.q_nnz,
                         in.layout.q_list, in.layout.k_nnz, in.layout.k_list, ws.order_cost, ws.q_order,
                         ws.k_raw, ws.k_items, ws.k_split, ws.k_counts};
-  rope_order_kernel<<<(unsigned)(1 + (n + kOrderThreads - 1) / kOrderThreads), kOrderThreads, 0, s>>>(ra, oa);
+  constexpr int HPB = kOrderThreads / (D / 8);
+  const int32_t hb = (in.Hkv + HPB - 1) / HPB;
+  const AbsArgs aa = {static_cast<const uint16_t *>(in.k), static_cast<const uint16_t *>(in.v), ws.pmax_part,
+                      in.B, in.L, in.Hkv, ws.n_part, hb};
+  const int32_t n_abs = 2 * in.B * hb * ws.n_part;
+  const unsigned grid = (unsigned)(1 + n_abs + (n + kOrderThreads - 1) / kOrderThreads);
+  rope_order_kernel<D><<<grid, kOrderThreads, 0, s>>>(ra, oa, aa, n_abs);
 }
 
-// Plane maxima of k (times sqrt(2), the RoPE bound) and of v.
-void launch_absmax_kv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
-  const int HPB = 256 / (in.D / 8);
-  const int32_t hb = (in.Hkv + HPB - 1) / HPB;
-  AbsmaxJob jobs[2] = {{static_cast<const uint16_t *>(in.k), ws.mk, in.Hkv, hb, 1.4142136f},
-                       {static_cast<const uint16_t *>(in.v), ws.mv, in.Hkv, 2 * hb, 1.0f}};
-  if (in.D == 64) launch_absmax_d<64>(in.B, in.L, jobs, s);
-  else launch_absmax_d<128>(in.B, in.L, jobs, s);
+}  // namespace
+
+// The work order, the k/v partial maxima and the RoPE table, in one launch.
+void launch_rope_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
+  if (in.D == 64) launch_rope_order_d<64>(in, ws, s);
+  else launch_rope_order_d<128>(in, ws, s);
 }
 
 // q after RoPE, one scale per row of each (row, head).
 void launch_pack_q(const opr_attn_in &in, const AttnWs &ws, hipStream_t s) {
   if (in.D == 64)
-    launch_pack_d<64, true, true>(in.B, in.L, ws.Lp, in.Hq, in.q, in.layout.slot_tok, ws.rope, nullptr, ws.qr,
-                                  ws.eqq, ws.eqt, s);
+    launch_pack_d<64, true, true>(in.B, in.L, ws.Lp, in.Hq, in.q, in.layout.slot_tok, ws.rope, ws.qr, ws.eqq,
+                                  ws.eqt, s);
   else
-    launch_pack_d<128, true, true>(in.B, in.L, ws.Lp, in.Hq, in.q, in.layout.slot_tok, ws.rope, nullptr, ws.qr,
-                                   ws.eqq, ws.eqt, s);
+    launch_pack_d<128, true, true>(in.B, in.L, ws.Lp, in.Hq, in.q, in.layout.slot_tok, ws.rope, ws.qr, ws.eqq,
+                                   ws.eqt, s);
 }
 
 // k (after RoPE) and v, one scale per plane.

@@ -13,7 +13,6 @@ namespace opr {
 
 // launchers defined in the .hip files
 void launch_rope_order(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
-void launch_absmax_kv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_pack_q(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 void launch_pack_kv(const opr_attn_in &in, const AttnWs &ws, hipStream_t s);
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &in, float scale, void *o, float *lse,
@@ -58,6 +57,8 @@ size_t carve_attn_ws(void *p, const opr_attn_in &in, int is_bwd, AttnWs *o) {
     w.mk = w.pmax;
     w.mv = w.mk + (size_t)in.B * in.Hkv;
   }
+  w.n_part = (in.L + kAbsSlots - 1) / kAbsSlots;
+  w.pmax_part = cv.take<uint32_t>((size_t)2 * in.B * in.Hkv * w.n_part);
   const size_t etiles = (size_t)in.B * in.Hq * (Lp / kTile);
   const size_t erows = (size_t)in.B * in.Hq * Lp;
   w.eqq = cv.take<int32_t>(erows);
@@ -178,7 +179,6 @@ static void mark(const opr_attn_in *in, int i, hipStream_t s) {
 // not reuse the forward's workspace packs q here (pack_q).
 static void forward_prologue(const opr_attn_in &in, const AttnWs &ws, hipStream_t stream, bool pack_q) {
   launch_rope_order(in, ws, stream);
-  launch_absmax_kv(in, ws, stream);
   if (pack_q) launch_pack_q(in, ws, stream);
   launch_pack_kv(in, ws, stream);
 }

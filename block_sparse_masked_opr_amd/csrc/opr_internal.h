@@ -36,6 +36,9 @@ bool gemm_bf16(bool trans_a, bool trans_b, int64_t M, int64_t N, int64_t K, cons
                bool c_f32, void *ws, size_t ws_bytes, hipStream_t s);
 
 // ---------------------------------------------------------------- layout
+// Tokens per workgroup of the k/v plane maxima (partial maxima per block).
+constexpr int kAbsSlots = 256;
+
 struct LayoutWs {
   int32_t *cpr;         // [B]   convs per row (copied from the host)
   int32_t *tpc;         // [C]   turns per conversation (copied)
@@ -79,9 +82,12 @@ struct AttnWs {
   uint16_t *vr;         // v
   uint16_t *dor;        // dout, written by the dQ kernel             (bwd)
   // plane maxima (float bits): mk [B][Hkv], mv [B][Hkv], contiguous from pmax
-  // (n_pmax words)
+  // (n_pmax words); their partial maxima over kAbsSlots-token blocks,
+  // [2 (k, v)][B][Hkv][n_part] (the k/v packs reduce them)
   uint32_t *pmax, *mk, *mv;
   int32_t n_pmax;
+  uint32_t *pmax_part;
+  int32_t n_part;
   // row exponents [B][Hq][Lp] of q (eqq) and dout (edoq), and their minima
   // over each 16-slot tile [B][Hq][Lp/16] (eqt, edot)
   int32_t *eqq, *eqt;

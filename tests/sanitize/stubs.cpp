@@ -16,7 +16,6 @@ static void reached(const char *what) {
 }
 
 void launch_rope_order(const opr_attn_in &, const AttnWs &, hipStream_t) { reached("launch_rope_order"); }
-void launch_absmax_kv(const opr_attn_in &, const AttnWs &, hipStream_t) { reached("launch_absmax_kv"); }
 void launch_pack_q(const opr_attn_in &, const AttnWs &, hipStream_t) { reached("launch_pack_q"); }
 void launch_pack_kv(const opr_attn_in &, const AttnWs &, hipStream_t) { reached("launch_pack_kv"); }
 hipError_t launch_attn_fwd_kernel(const opr_attn_in &, float, void *, float *, const AttnWs &, hipStream_t) {
