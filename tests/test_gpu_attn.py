@@ -41,9 +41,11 @@ def B():
     return binding
 
 
-def run_gpu(Bd, rows, L, t, bwd=True, reuse=False):
+def run_gpu(Bd, rows, L, t, bwd=True, reuse=False, theta=None, scale=0.0):
     """Layout, forward and (optionally) backward on the GPU.  reuse: the
-    backward gets the forward's workspace and reuses its state."""
+    backward gets the forward's workspace and reuses its state.  theta, scale:
+    the RoPE base (THETA if None) and the softmax scale (0: 1/sqrt(D))."""
+    theta = THETA if theta is None else theta
     dev = torch.device("cuda:0")
     lay = Bd.opr_build_layout(rows, L, 128, 128, device=dev)
     q, k, v = (to_device_bf16(t[n], dev) for n in ("q", "k", "v"))
@@ -51,11 +53,11 @@ def run_gpu(Bd, rows, L, t, bwd=True, reuse=False):
     if reuse:
         ws = torch.empty(Bd.opr_attn_workspace_size(len(rows), L, q.shape[2], k.shape[2], q.shape[3], True),
                          dtype=torch.uint8, device=dev)
-    o, lse = Bd.opr_attn_fwd(q, k, v, lay, THETA, workspace=ws)
+    o, lse = Bd.opr_attn_fwd(q, k, v, lay, theta, scale, workspace=ws)
     res = {"o": o, "lse": lse}
     if bwd:
         do = to_device_bf16(t["do"], dev)
-        res["dq"], res["dk"], res["dv"] = Bd.opr_attn_bwd(q, k, v, o, lse, do, lay, THETA, workspace=ws,
+        res["dq"], res["dk"], res["dv"] = Bd.opr_attn_bwd(q, k, v, o, lse, do, lay, theta, scale, workspace=ws,
                                                           reuse_fwd_workspace=reuse)
     torch.cuda.synchronize()
     out = {"o": bf16_f64(from_device_bf16(res["o"])), "lse": res["lse"].cpu().numpy().astype(np.float64)}
@@ -322,6 +324,29 @@ def test_input_range_edges(B):
         assert np.isfinite(x).all(), n
         top = float(np.abs(ref[live]).max())
         assert_close(n, x[live] / top, ref[live] / top, max_abs=5e-3)
+    assert_close("LSE", got["lse"].transpose(0, 2, 1)[live], lse.transpose(0, 2, 1)[live])
+
+
+@pytest.mark.parametrize("scale,theta", [(0.25, 1.0e4), (0.05, 5.0e5)])
+def test_softmax_scale_and_rope_theta(B, scale, theta):
+    """A softmax scale other than 1/sqrt(D) (0.25: scores about 2.8 times
+    wider, so the running maximum is raised more often) and other RoPE bases:
+    forward and backward against the oracle at the same scale and base, exact
+    gradient (4 q heads per kv head).  dQ grows with the scale, so outputs are
+    held as everywhere values exceed unit size: mean-rel <= 5e-3 and max-abs
+    <= 2e-2 times max(1, the largest |ref|)."""
+    rows = [[[(40, 150, 60, 60), (30, 100, 40, 40)], [(70, 0, 20, 20)]], [[(20, 60, 30, 30)]]]
+    L = max(I.row_used(r) for r in rows) + 9
+    t = I.make_tensors(len(rows), L, 8, 2, 128, seed=97)
+    got = run_gpu(B, rows, L, t, theta=theta, scale=scale)
+    lay = O.layout(rows, L)
+    q, k, v, do = (bf16_f64(t[n]) for n in ("q", "k", "v", "do"))
+    o, lse = O.attn_fwd(q, k, v, lay, theta, scale=scale)
+    dq, dk, dv = O.attn_bwd(q, k, v, do, lay, theta, scale=scale)
+    live = lay["type"] != O.PAD
+    print(f"[attn] softmax scale {scale}, rope theta {theta:g}", flush=True)
+    for n, x, ref in (("O", got["o"], o), ("dq", got["dq"], dq), ("dk", got["dk"], dk), ("dv", got["dv"], dv)):
+        _assert_slices(n, x, ref, [("all", live)])
     assert_close("LSE", got["lse"].transpose(0, 2, 1)[live], lse.transpose(0, 2, 1)[live])
 
 
