@@ -232,14 +232,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Asynchronous copies of 64-row tiles from a plane [rows][D] fp16 (buffer
-// resource over the plane) into swizzled LDS tiles.  Each of the NW waves
-// issues NI of the D/8 one-kilobyte instructions; the per-lane byte offsets
-// inside the 64-row block are fixed, the first row goes in the scalar offset.
-template <int D, int NW = 4>
+// Asynchronous copies of ROWS-row tiles (64 or 32) from a plane [rows][D]
+// fp16 (buffer resource over the plane) into swizzled LDS tiles.  Each of the
+// NW waves issues NI of the tile's one-kilobyte instructions; the per-lane
+// byte offsets inside the block are fixed, the first row goes in the scalar
+// offset.
+template <int D, int NW = 4, int ROWS = 64>
 struct TileCopy {
-  static constexpr int NI = Tile<D>::NC / NW;
-  static_assert(NI >= 1 && NI * NW == Tile<D>::NC, "waves must split the tile's instructions evenly");
+  static constexpr int NI = ROWS * Tile<D>::RB / 1024 / NW;
+  static_assert(NI >= 1 && NI * NW * 1024 == ROWS * Tile<D>::RB, "waves must split the tile's instructions evenly");
   int voff[NI];
   __device__ __forceinline__ void init(int w, int lane) {
     constexpr int NC = Tile<D>::NC, RPI = 1024 / Tile<D>::RB;
@@ -274,6 +275,20 @@ __device__ __forceinline__ void sched_lds_reads_ahead() {
     __builtin_amdgcn_sched_group_barrier(kDsRead, READS, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
+}
+
+// Wait until at most N of this wave's vector memory operations (the newest:
+// asynchronous LDS fills of later stages) are outstanding and all its LDS
+// operations are done, then for the whole workgroup.  The barrier carries no
+// fence (a fenced barrier would also wait for the fills still streaming into
+// other buffers); the empty asm keeps the compiler from moving memory
+// operations across it.
+template <int N>
+__device__ __forceinline__ void wait_older_copies_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));  // vmcnt(N) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Wait for this thread's outstanding memory operations (including the

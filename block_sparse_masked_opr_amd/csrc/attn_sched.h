@@ -43,6 +43,34 @@ __device__ inline int build_q_stages(const int32_t *lst, const uint32_t *subs, i
   return count;
 }
 
+// Forward: the stages are the 32-key quarters j of the tiles q_list[t ...]
+// in which any wave's 32 x 32 sub-block (w, j) is non-empty, up to CAP per
+// chunk.  Descriptor: x = first key slot, y bits 2w = class of wave w's
+// sub-block.  Returns the count; advances *t.
+template <int CAP>
+__device__ inline int build_q_quarters(const int32_t *lst, const uint32_t *subs, int nnz, int *t,
+                                       uint2 *stages, int lane) {
+  int count = 0;
+  while (*t < nnz && count + 64 <= CAP) {
+    const int tile = *t + (lane >> 2), j = lane & 3;
+    uint32_t cls = 0;
+    int k0 = 0;
+    if (tile < nnz) {
+      const int n = lst[tile];
+      const uint32_t sub = subs[n];
+      k0 = n * 128 + 32 * j;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) cls |= ((sub >> (2 * (4 * w + j))) & 3u) << (2 * w);
+    }
+    const uint64_t bal = __ballot(cls != 0);
+    if (cls != 0) stages[count + __popcll(bal & ((1ull << lane) - 1ull))] = make_uint2((uint32_t)k0, cls);
+    count += __popcll(bal);
+    *t += 16;
+  }
+  if (*t > nnz) *t = nnz;
+  return count;
+}
+
 // Key-side kernel (dK/dV) of k-tile n: wave w owns key sub-column w; the
 // stages run over the q-tiles k_list[...] x the G heads of the kv group x the
 // two 64-query halves, flat index f = (tile * G + head) * 2 + half, from *f up
