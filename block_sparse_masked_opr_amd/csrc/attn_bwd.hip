@@ -290,9 +290,8 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   // no query of the stage skips it.  Both roles share the accumulator update
   // (one copy of the code, so the accumulators stay in place across the role
   // branch).
-  auto wave_step = [&](int i, int ns, const char *ba, const char *bb, char *pa, const char *pr) {
+  auto wave_step = [&](int i, int ns, uint2 desc, const char *ba, const char *bb, char *pa, const char *pr) {
     if (pwave ? i >= ns : i < 1) return;
-    const uint2 desc = uniform(stages[pwave ? i : i - 1]);
     if (((desc.y >> (4 * w)) & 15u) == 0) return;
     f16x8 op[2][2];
     const char *T;
@@ -336,9 +335,16 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     // step i: stage i + 1 streams into buf[(i + 1) % 3] while the waves run
     // their stages (wave_step)
     auto step = [&](int i, const char *ba, const char *bb, char *bl, char *pa, const char *pr) {
+      // the stage list is fixed for the chunk: the wave's descriptor and the
+      // next stage's are read before the barrier, together (entries outside
+      // the list are read but not used)
+      const uint2 d0 = stages[pwave ? min(i, kKStageCap - 1) : max(i - 1, 0)];
+      const uint32_t x1 = stages[min(i + 1, kKStageCap - 1)].x;
+      const uint2 desc = uniform(d0);
+      const uint32_t k1 = uniform(x1);
       wait_all_and_barrier();
-      if (i + 1 < ns) issue(uniform((int)stages[i + 1].x), bl);
-      wave_step(i, ns, ba, bb, pa, pr);
+      if (i + 1 < ns) issue(k1, bl);
+      wave_step(i, ns, desc, ba, bb, pa, pr);
     };
     for (int i = 0; i <= ns; i += 3) {
       step(i, buf0, buf2, buf1, pbf0, pbf2);

@@ -102,6 +102,15 @@ __device__ __forceinline__ int64_t uniform(int64_t x) {
   return (int64_t)(((uint64_t)uniform((uint32_t)(u >> 32)) << 32) | uniform((uint32_t)u));
 }
 
+// max(x[l], x[l ^ 32]) in every lane l: the two halves of the wave swapped
+// with one v_permlane32_swap (VALU, no LDS round trip).  The builtin returns
+// the lower halves of both operands in one register and the upper halves in
+// the other, so each lane sees both values of its pair.
+__device__ __forceinline__ float pair_max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ int kperm(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }

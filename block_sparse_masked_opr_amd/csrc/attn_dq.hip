@@ -11,10 +11,11 @@
 // 16-slot tile), and Delta, lse and the score factor in that kernel's
 // per-slot units.
 // Main loop, pipelined like the forward kernel: a stage list of the non-empty
-// 64-key halves in LDS, K' and V tiles double buffered in LDS (buffer loads
-// to LDS), one barrier per stage.  Per non-empty 32x32 sub-block each wave
-// recomputes S^T = K' Q'^T and dP^T = V dO^T, masks partial sub-blocks with
-// the query's key intervals, forms dS = P * (dP - Delta) (P from the forward
+// 32-key quarters in LDS, K' and V tiles in a ring of three LDS buffers
+// (buffer loads to LDS, two stages in flight, each wave waiting only for its
+// own copies of the current stage), one barrier per stage.  Per non-empty
+// 32x32 sub-block each wave recomputes S^T = K' Q'^T and dP^T = V dO^T, masks
+// partial sub-blocks with the query's key intervals, forms dS = P * (dP - Delta) (P from the forward
 // LSE) and accumulates dQ^T += K'^T dS^T, reading K'^T from the row-major K'
 // tile with transposing LDS reads.  The epilogue removes the operand units,
 // applies the softmax scale and rotates dQ back by the transposed RoPE
@@ -33,18 +34,22 @@ namespace opr {
 namespace {
 
 constexpr int kReadsAhead = 4;  // S / dP products whose K' / V operand reads are in flight
+constexpr int kDqStageCap = 256;  // 32-key stages per list chunk (2 KB of LDS)
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq) {
   constexpr int NS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int HALF_DB = NDB / 2;
-  constexpr int TB = Tile<D>::BYTES, RB = Tile<D>::RB;
+  constexpr int RB = Tile<D>::RB;
+  constexpr int TB = 32 * RB;  // one 32-row tile
   constexpr int BUF = 2 * TB;  // K' tile, V tile
-  // two separate LDS objects so the copy into one provably leaves the other alone
+  // a ring of three separate LDS objects, so that the compiler sees that the
+  // copies into two of them leave the third alone
   __shared__ __attribute__((aligned(1024))) char buf0[BUF];
   __shared__ __attribute__((aligned(1024))) char buf1[BUF];
-  __shared__ uint2 stages[kStageCap];
+  __shared__ __attribute__((aligned(1024))) char buf2[BUF];
+  __shared__ uint2 stages[kDqStageCap];
   __shared__ int sh_count, sh_next;
 
   const QItem it = q_work_item(p.q_order, p.MT, p.Hkv, p.group, (int64_t)p.B * p.MT);
@@ -132,8 +137,9 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   const int4 iv = q < p.L ? p.qiv[(int64_t)b * p.L + q] : make_int4(0, 0, 0, 0);
   OperandOffsets<D> of;
   of.init(lane);
-  TileCopy<D> tc;
+  TileCopy<D, 4, 32> tc;
   tc.init(w, lane);
+  constexpr int kCopies = 2 * TileCopy<D, 4, 32>::NI;  // copy instructions per wave and stage (K' and V)
   const uint32_t plane_bytes = (uint32_t)p.Lp * D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.kr + kvplane * p.Lp * D, plane_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.vr + kvplane * p.Lp * D, plane_bytes);
@@ -152,13 +158,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
     tc.issue(rv, k0, nb + TB, w);
   };
 
-  // the stage list is built in chunks of up to kStageCap stages
+  // the stage list (32-key quarters) is built in chunks of up to kDqStageCap stages
   int tnext = 0, ns = 0;
   auto build = [&]() {
-    __syncthreads();
+    __syncthreads();  // the previous chunk's stages and buffers are no longer read
     if (w == 0) {
       int t = tnext;
-      const int c = build_q_stages(lst, subs, nnz, &t, stages, lane);
+      const int c = build_q_quarters<kDqStageCap>(lst, subs, nnz, &t, stages, lane);
       if (lane == 0) {
         sh_count = c;
         sh_next = t;
@@ -168,68 +174,64 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
     ns = uniform(sh_count);
     tnext = uniform(sh_next);
     if (ns > 0) issue(uniform((int)stages[0].x), buf0);
+    if (ns > 1) issue(uniform((int)stages[1].x), buf1);
   };
   build();
   convert_dout();  // while the first K/V tiles stream in
   for (;;) {
-    auto stage = [&](int i, const char *buf, char *nxt) {
-      wait_all_and_barrier();
-      if (i + 1 < ns) issue(uniform((int)stages[i + 1].x), nxt);
-      const uint2 desc = uniform(stages[i]);
-      const uint32_t c0 = (desc.y >> (4 * w)) & 3u, c1 = (desc.y >> (4 * w + 2)) & 3u;
-      if ((c0 | c1) == 0) return;
+    // stage i reads `buf` (buf[i % 3]) while stages i+1 and i+2 stream in; at
+    // its start it waits for its own tiles only (the copies of stage i+1, if
+    // any, are the newest kCopies of the wave), then refills the buffer that
+    // stage i-1 used with stage i+2.  The stage list is fixed for the chunk,
+    // so both descriptors are read before the barrier, together (an entry
+    // past the list is read but not used).
+    auto stage = [&](int i, const char *buf, char *nxt2) {
+      const uint2 d0 = stages[i];
+      const uint32_t x2 = stages[min(i + 2, kDqStageCap - 1)].x;
+      const uint2 desc = uniform(d0);
+      const int k2 = uniform((int)x2);
+      if (i + 1 < ns) wait_older_copies_and_barrier<kCopies>();
+      else wait_older_copies_and_barrier<0>();
+      if (i + 2 < ns) issue(k2, nxt2);
+      const uint32_t c = (desc.y >> (2 * w)) & 3u;
+      if (c == 0) return;
       const int k0 = (int)desc.x;
       const char *Kt = buf, *Vt = buf + TB;
 
-      // Both 32-key sub-blocks always (straight-line code): the mask is exact,
-      // so an empty one gives p = 0 and dS = 0.
-      f32x16 s[2], dpt[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = zero_f32x16();
-        dpt[kb] = zero_f32x16();
-      }
+      // S^T and dP^T of the stage's 32 keys (straight-line code: the mask is
+      // exact, so masked scores give p = 0 and dS = 0)
+      f32x16 sc = zero_f32x16(), dpt = zero_f32x16();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = mfma32x32x16(lds_f16x8(Kt + kb * 32 * RB + of.row8[st]), qb[st], s[kb]);
-          dpt[kb] = mfma32x32x16(lds_f16x8(Vt + kb * 32 * RB + of.row8[st]), dob[st], dpt[kb]);
-        }
+        sc = mfma32x32x16(lds_f16x8(Kt + of.row8[st]), qb[st], sc);
+        dpt = mfma32x32x16(lds_f16x8(Vt + of.row8[st]), dob[st], dpt);
       }
-      sched_lds_reads_ahead<4 * NS, kReadsAhead, 1>();
+      sched_lds_reads_ahead<2 * NS, kReadsAhead, 1>();
       __builtin_amdgcn_sched_barrier(0);
-      if (c0 != 2 || c1 != 2) {
+      if (c != 2) {
+        // lane group g holds keys 16h + 8g + 0..7 of the 32
         const uint64_t mk = (range_bits(iv.x, iv.y, k0) | range_bits(iv.z, iv.w, k0)) >> (8 * g);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) s[kb][rr] = mask_select(mk, 32 * kb + 16 * (rr >> 3) + (rr & 7), s[kb][rr]);
-        }
+        for (int rr = 0; rr < 16; ++rr) sc[rr] = mask_select(mk, 16 * (rr >> 3) + (rr & 7), sc[rr]);
       }
-      f16x8 dsb[2][2];
+      f16x8 dsb[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][rr], fs, -lse2_q));
-          dsb[kb][rr >> 3][rr & 7] = (_Float16)(pv * fmaf(dpt[kb][rr], dss, -dsc_q));
-        }
+      for (int rr = 0; rr < 16; ++rr) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sc[rr], fs, -lse2_q));
+        dsb[rr >> 3][rr & 7] = (_Float16)(pv * fmaf(dpt[rr], dss, -dsc_q));
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            dqacc[db] = mfma32x32x16(tile_col8<D>(Kt, of, 32 * kb + 16 * hh, db), dsb[kb][hh], dqacc[db]);
-        }
+        for (int db = 0; db < NDB; ++db)
+          dqacc[db] = mfma32x32x16(tile_col8<D>(Kt, of, 16 * hh, db), dsb[hh], dqacc[db]);
       }
     };
-    for (int i = 0; i < ns; i += 2) {
-      stage(i, buf0, buf1);
+    for (int i = 0; i < ns; i += 3) {
+      stage(i, buf0, buf2);
       if (i + 1 < ns) stage(i + 1, buf1, buf0);
+      if (i + 2 < ns) stage(i + 2, buf2, buf1);
     }
     if (tnext >= nnz) break;
     build();

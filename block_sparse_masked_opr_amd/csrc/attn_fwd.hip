@@ -189,12 +189,17 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnParams p, uint16_t
     // stage i reads `buf` (buf[i % 3]) while stages i+1 and i+2 stream in; at
     // its start it waits for its own tiles only (the copies of stage i+1, if
     // any, are the newest kCopies of the wave), then refills the buffer that
-    // stage i-1 used with stage i+2
+    // stage i-1 used with stage i+2.  The stage list is fixed for the chunk,
+    // so both descriptors are read before the barrier, together.
     auto stage = [&](int i, const char *buf, char *nxt2) {
+      // (an entry past the list is read but not used)
+      const uint2 d0 = stages[i];
+      const uint32_t x2 = stages[min(i + 2, kFwdStageCap - 1)].x;
+      const uint2 desc = uniform(d0);
+      const int k2 = uniform((int)x2);
       if (i + 1 < ns) wait_older_copies_and_barrier<kCopies>();
       else wait_older_copies_and_barrier<0>();
-      if (i + 2 < ns) issue(uniform((int)stages[i + 2].x), nxt2);
-      const uint2 desc = uniform(stages[i]);
+      if (i + 2 < ns) issue(k2, nxt2);
       const uint32_t c = (desc.y >> (2 * w)) & 3u;
       if (c == 0) return;
       const int k0 = (int)desc.x;
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnParams p, uint16_t
       float mx = sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * fs;
+      mx = pair_max_xor32(mx) * fs;
       if (__ballot(mx > mrow + kMaxSlack) != 0) {  // raise the running maximum (wave-uniform)
         const float mnew = fmaxf(mrow, mx);
         const float alpha = (mnew == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(mrow - mnew);
