@@ -566,8 +566,9 @@ def kpass_sweep(torch, Bd, dev, steps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first: the clock settles over the first few tens of steps")
     ap.add_argument("--no-sweep", action="store_true", help="skip the depth and K-pass sweeps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-block", action="store_true", help="skip the attention-block measurements")
