@@ -211,15 +211,22 @@ class Runner:
                         workspace=self.ws, out=(self.dq, self.dk, self.dv), events=ev_b,
                         reuse_fwd_workspace=True)
 
-    def time_steps(self, steps, warmup):
+    def fwd_step(self):
+        Bd, t = self.Bd, self.t
+        Bd.opr_build_layout(self.rows, self.L, 128, 128, device=self.o.device, workspace=self.lws, out=self.lay,
+                            lists=self.lists)
+        Bd.opr_attn_fwd(t["q"], t["k"], t["v"], self.lay, self.theta, workspace=self.ws, out=(self.o, self.lse))
+
+    def time_steps(self, steps, warmup, fwd_only=False):
         torch = self.torch
+        run = self.fwd_step if fwd_only else self.step
         for _ in range(warmup):
-            self.step()
+            run()
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         for _ in range(steps):
-            self.step()
+            run()
         e.record()
         torch.cuda.synchronize()
         return s.elapsed_time(e) / steps
@@ -348,6 +355,27 @@ def block_depth(torch, Bd, dev, Ns, steps):
         rec["speedup_elided"] = round(rec["n_pass"]["ms"] / rec["one_pass_elided"]["ms"], 3)
         log(f"block depth N={N}: {rec}")
         out.append(rec)
+    return out
+
+
+def packed_fwd_step(torch, Bd, dev, steps, warmup):
+    """The packed forward workload (one row of 8192 tokens, 32 q / 8 kv heads,
+    D = 128): layout + forward per step, useful FLOPs 4 * D * Hq * P."""
+    shape = I.PACKED_FWD
+    seed_len, seed_t = I.SEEDS["packed_fwd"]
+    rows = I.packed_rows(shape, seed_len)
+    t = device_inputs(torch, shape.B, shape.L, shape.Hq, shape.Hkv, shape.D, seed_t, dev)
+    r = Runner(torch, Bd, rows, shape.L, shape.Hq, shape.Hkv, shape.D, t, dev, shape.theta)
+    P = useful_pairs(torch, r.lay)
+    ms = r.time_steps(steps, warmup, fwd_only=True)
+    tflops = 4.0 * shape.D * shape.Hq * P / (ms * 1e-3) / 1e12
+    conv_tokens = sum(I.conv_logical_tokens(c) for row in rows for c in row)
+    out = {"workload": "packed_fwd: 1 row x 8192 tokens, 32 q / 8 kv heads, D=128, layout + fwd per step",
+           "useful_pairs": P, "ms": round(ms, 4), "useful_tflops": round(tflops, 2),
+           "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
+           "tokens_per_s": round(conv_tokens / (ms * 1e-3), 1)}
+    del r
+    torch.cuda.empty_cache()
     return out
 
 
@@ -685,6 +713,8 @@ def main():
     del r
     torch.cuda.empty_cache()
     result["layout_step"] = layout_step(torch, Bd, dev, args.steps)
+    result["packed_fwd"] = packed_fwd_step(torch, Bd, dev, args.steps, args.warmup)
+    log(f"packed forward {result['packed_fwd']['ms']:.4f} ms, {result['packed_fwd']['useful_tflops']} TFLOP/s")
     if not args.no_block:
         result["block_step"] = block_step(torch, Bd, dev, rows, shape, args.steps, args.warmup)
     if not args.no_sweep:
