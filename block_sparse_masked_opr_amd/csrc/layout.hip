@@ -310,26 +310,56 @@ __global__ __launch_bounds__(BQ) void layout_classify(int32_t B, int32_t L, int3
 // per q-tile row (b, m).  The row's queries (slots m*BQ ..) put their two
 // runs of slots in LDS, and their union gives the span of key slots any of
 // them sees: key tiles outside it are empty and are written as such directly.
-// Inside it, a group of SQ*SK consecutive lanes takes one tile, a lane one
-// 32x32 sub-block: it sums over the sub-block's 32 queries the part of their
-// runs inside its 32 key slots.  The group forms the tile's class word and
-// total with shuffles (no LDS table, no barrier per tile), and its first lane
-// writes them.  Two waves per row: with more, fewer rows share a compute unit
-// and the row's serial steps (loads, span, passes) are no better hidden.
+// Inside it only a 32x32 sub-block's class is needed, not its count: a query
+// row's runs touch an interval of 32-key blocks and cover a (possibly empty)
+// inner interval of them, so the lane of query row r forms two 64-bit masks
+// over a window of 64 key blocks (blocks its runs touch, blocks they cover),
+// and 32 lanes - the 32 query rows of a sub-row - OR the first and AND the
+// second with shuffles: a block is empty if no row touches it, full if every
+// row covers it (a row past L covers nothing), partial otherwise.  Adjacent
+// runs are merged first, so that a block across their boundary counts as
+// covered.  The masks go to LDS per (sub-row, window), and one thread per tile
+// then assembles its 2-bit sub-block classes and the tile's class.  The span
+// is taken in chunks of kClsWin windows.
 constexpr int kClsThreads = 128;
+constexpr int kClsWin = 32;  // 64-block windows per chunk (2048 key blocks)
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Bits of the block indices [a, b) inside the 64-block window at base.
+__device__ __forceinline__ uint64_t window_bits(int32_t a, int32_t b, int32_t base) {
+  const int32_t lo = max(0, min(64, a - base)), hi = max(0, min(64, b - base));
+  const uint64_t below_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+  const uint64_t below_lo = lo >= 64 ? ~0ull : ((1ull << lo) - 1ull);
+  return below_hi & ~below_lo;
+}
+
+// Blocks of 32 keys in the window at base that the slot run [x, y) touches
+// and covers.
+__device__ __forceinline__ void run_blocks(int32_t x, int32_t y, int32_t base, uint64_t &touch, uint64_t &cover) {
+  if (x >= y) return;
+  touch |= window_bits(x >> 5, ((y - 1) >> 5) + 1, base);
+  cover |= window_bits((x + 31) >> 5, y >> 5, base);
+}
 
 template <int BQ, int BK>
 __global__ __launch_bounds__(kClsThreads) void layout_classify_attention(int32_t B, int32_t L, int32_t MT,
                                                                          int32_t NT, opr_layout out) {
-  constexpr int SQ = BQ / OPR_SUB_BLOCK, SK = BK / OPR_SUB_BLOCK, NSB = SQ * SK, TPW = 64 / NSB;
-  static_assert(NSB <= 64 && 64 % NSB == 0, "a tile's sub-blocks fit in one wave");
+  constexpr int SQ = BQ / OPR_SUB_BLOCK, SK = BK / OPR_SUB_BLOCK;
+  static_assert(OPR_SUB_BLOCK == 32, "32-key blocks: one bit per block in a 64-block window");
   static_assert(BQ <= kClsThreads, "one thread per query slot of the tile row");
+  constexpr int kTilesPerChunk = kClsWin * 64 / SK;
   __shared__ int4 runs[BQ];
   __shared__ int32_t span[2];
+  __shared__ uint64_t touch_w[SQ][kClsWin], cover_w[SQ][kClsWin];
   const int64_t row = blockIdx.x;  // b * MT + m
   const int32_t m = (int32_t)(row % MT);
   const int32_t b = (int32_t)(row / MT);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   if (tid == 0) {
     span[0] = INT32_MAX;
     span[1] = INT32_MIN;
@@ -339,6 +369,10 @@ __global__ __launch_bounds__(kClsThreads) void layout_classify_attention(int32_t
     const int32_t q = m * BQ + tid;
     int4 iv = make_int4(0, 0, 0, 0);
     if (tid < BQ && q < L) iv = reinterpret_cast<const int4 *>(out.slot_qiv)[(int64_t)b * L + q];
+    // merge two runs that touch or overlap, so that a block across their
+    // boundary is covered
+    if (iv.x < iv.y && iv.z < iv.w && max(iv.x, iv.z) <= min(iv.y, iv.w))
+      iv = make_int4(min(iv.x, iv.z), max(iv.y, iv.w), 0, 0);
     if (tid < BQ) runs[tid] = iv;
     const bool any = iv.x < iv.y || iv.z < iv.w;
     int32_t lo = any ? (iv.x < iv.y ? iv.x : iv.z) : INT32_MAX;
@@ -364,32 +398,48 @@ __global__ __launch_bounds__(kClsThreads) void layout_classify_attention(int32_t
       scls[n] = 0u;
     }
   }
-  const int grp = lane / NSB, i = lane % NSB, sq = i / SK, j = i % SK;
-  constexpr int kPass = (kClsThreads / 64) * TPW;  // tiles per pass of the workgroup
-  for (int32_t nb = n_lo; nb <= n_hi; nb += kPass) {
-    const int32_t n = nb + wv * TPW + grp;
-    int32_t c = 0;
-    if (n <= n_hi) {
-      const int32_t a = n * BK + j * OPR_SUB_BLOCK;
-      const int32_t e = min(a + OPR_SUB_BLOCK, L);
-#pragma unroll 8
-      for (int r = 0; r < OPR_SUB_BLOCK; ++r) {
-        const int4 u = runs[sq * OPR_SUB_BLOCK + r];
-        c += overlap(a, e, u.x, u.y) + overlap(a, e, u.z, u.w);
+  const int grp = tid >> 5, r = tid & 31;  // 32-lane groups: one (sub-row, window) each
+  for (int32_t c0 = n_lo; c0 <= n_hi; c0 += kTilesPerChunk) {
+    const int32_t c1 = min(n_hi, c0 + kTilesPerChunk - 1);
+    const int32_t kb0 = c0 * SK;  // first key block of the chunk
+    const int32_t nwin = ((c1 - c0 + 1) * SK + 63) / 64;
+    for (int it = grp; it < SQ * nwin; it += kClsThreads / 32) {
+      const int sq = it / nwin, win = it - sq * nwin;
+      const int4 u = runs[sq * OPR_SUB_BLOCK + r];
+      const int32_t base = kb0 + 64 * win;
+      uint64_t touch = 0, cover = 0;
+      run_blocks(u.x, u.y, base, touch, cover);
+      run_blocks(u.z, u.w, base, touch, cover);
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) {
+        touch |= shfl_xor_u64(touch, off);
+        cover &= shfl_xor_u64(cover, off);
+      }
+      if (r == 0) {
+        touch_w[sq][win] = touch;
+        cover_w[sq][win] = cover;
       }
     }
-    uint32_t word = (c == 0 ? OPR_TILE_EMPTY : (c == OPR_SUB_BLOCK * OPR_SUB_BLOCK ? OPR_TILE_FULL : OPR_TILE_PARTIAL))
-                    << (2 * i);
-    int32_t total = c;
+    __syncthreads();
+    for (int32_t n = c0 + tid; n <= c1; n += kClsThreads) {
+      uint32_t word = 0;
+      int touched = 0, covered = 0;
 #pragma unroll
-    for (int off = NSB / 2; off > 0; off >>= 1) {
-      word |= (uint32_t)__shfl_xor((int)word, off);
-      total += __shfl_xor(total, off);
-    }
-    if (i == 0 && n <= n_hi) {
-      tcls[n] = total == 0 ? OPR_TILE_EMPTY : (total == BQ * BK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
+      for (int i = 0; i < SQ; ++i) {
+#pragma unroll
+        for (int j = 0; j < SK; ++j) {
+          const int32_t k = n * SK + j - kb0;
+          const uint32_t t = (uint32_t)(touch_w[i][k >> 6] >> (k & 63)) & 1u;
+          const uint32_t f = (uint32_t)(cover_w[i][k >> 6] >> (k & 63)) & 1u;
+          word |= (t ? (f ? OPR_TILE_FULL : OPR_TILE_PARTIAL) : OPR_TILE_EMPTY) << (2 * (i * SK + j));
+          touched += (int)t;
+          covered += (int)f;
+        }
+      }
+      tcls[n] = touched == 0 ? OPR_TILE_EMPTY : (covered == SQ * SK ? OPR_TILE_FULL : OPR_TILE_PARTIAL);
       scls[n] = word;
     }
+    __syncthreads();  // the masks are rewritten by the next chunk
   }
 }
 
