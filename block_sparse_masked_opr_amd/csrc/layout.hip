@@ -75,6 +75,61 @@ __device__ void block_exclusive_scan(int n, Get get, int32_t *out, int32_t *sh) 
   __syncthreads();
 }
 
+// Two exclusive prefix sums in one pass (get(i) gives both values), as
+// block_exclusive_scan; sh holds 2 * (kPrepThreads / 64) words.
+template <class Get>
+__device__ void block_exclusive_scan2(int n, Get get, int32_t *out0, int32_t *out1, int32_t *sh) {
+  constexpr int kWaves = kPrepThreads / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t carry0 = 0, carry1 = 0;
+  for (int base = 0; base < n; base += kPrepThreads) {
+    const int i = base + tid;
+    const int2 v = (i < n) ? get(i) : make_int2(0, 0);
+    int32_t inc0 = v.x, inc1 = v.y;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t y0 = __shfl_up(inc0, d), y1 = __shfl_up(inc1, d);
+      if (lane >= d) {
+        inc0 += y0;
+        inc1 += y1;
+      }
+    }
+    if (lane == 63) {
+      sh[wv] = inc0;
+      sh[kWaves + wv] = inc1;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      int32_t t0 = lane < kWaves ? sh[lane] : 0, t1 = lane < kWaves ? sh[kWaves + lane] : 0;
+#pragma unroll
+      for (int d = 1; d < kWaves; d <<= 1) {
+        const int32_t y0 = __shfl_up(t0, d), y1 = __shfl_up(t1, d);
+        if (lane >= d) {
+          t0 += y0;
+          t1 += y1;
+        }
+      }
+      if (lane < kWaves) {
+        sh[lane] = t0;
+        sh[kWaves + lane] = t1;
+      }
+    }
+    __syncthreads();
+    if (i < n) {
+      out0[i] = carry0 + (wv > 0 ? sh[wv - 1] : 0) + inc0 - v.x;
+      out1[i] = carry1 + (wv > 0 ? sh[kWaves + wv - 1] : 0) + inc1 - v.y;
+    }
+    carry0 += sh[kWaves - 1];
+    carry1 += sh[2 * kWaves - 1];
+    __syncthreads();  // sh is rewritten by the next chunk
+  }
+  if (tid == 0) {
+    out0[n] = carry0;
+    out1[n] = carry1;
+  }
+  __syncthreads();
+}
+
 // Index of the last entry of the non-decreasing a[lo..hi) that is <= x
 // (a[lo] <= x is guaranteed by the callers).
 __device__ inline int last_le(const int32_t *a, int lo, int hi, int32_t x) {
@@ -118,16 +173,17 @@ __global__ __launch_bounds__(kPrepThreads) void layout_prep(int32_t B, int32_t C
   const int4 *turns = ws.turns;
   block_exclusive_scan(B, [&](int i) { return cpr[i]; }, ws.row_conv0, sh);
   block_exclusive_scan(C, [&](int i) { return tpc[i]; }, ws.conv_turn0, sh);
-  // tokens of a turn: h + t + r_in + r_out
-  block_exclusive_scan(T, [&](int i) { int4 u = turns[i]; return u.x + u.y + u.z + u.w; },
-                       ws.tok_g, sh);
-  // the next human message starts after h_i and r_in_i: the position advance
-  // per turn is h + r_in, which is also the number of history tokens
-  block_exclusive_scan(T, [&](int i) { int4 u = turns[i]; return u.x + u.z; }, ws.pos_g, sh);
+  // tokens of a turn: h + t + r_in + r_out; the next human message starts
+  // after h_i and r_in_i: the position advance per turn is h + r_in, which is
+  // also the number of history tokens
+  block_exclusive_scan2(T, [&](int i) { const int4 u = turns[i]; return make_int2(u.x + u.y + u.z + u.w, u.x + u.z); },
+                        ws.tok_g, ws.pos_g, sh);
+  // the row of each conversation and the conversation of each turn, scattered
+  // from the prefix sums (the scans end with a barrier)
+  for (int b = threadIdx.x; b < B; b += kPrepThreads)
+    for (int c = ws.row_conv0[b], ce = ws.row_conv0[b + 1]; c < ce; ++c) ws.conv_row[c] = b;
   for (int c = threadIdx.x; c < C; c += kPrepThreads)
-    ws.conv_row[c] = last_le(ws.row_conv0, 0, B + 1, c);
-  for (int t = threadIdx.x; t < T; t += kPrepThreads)
-    ws.turn_conv[t] = last_le(ws.conv_turn0, 0, C + 1, t);
+    for (int t = ws.conv_turn0[c], te = ws.conv_turn0[c + 1]; t < te; ++t) ws.turn_conv[t] = c;
   for (int b = threadIdx.x; b <= B; b += kPrepThreads) ws.row_turn0[b] = ws.conv_turn0[ws.row_conv0[b]];
 }
 
