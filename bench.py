@@ -47,7 +47,11 @@ KERNEL_SOURCES = {
     "attn_fwd": ("attn_fwd.hip", "attn_common.h", "attn_sched.h"),
     "attn_dkdv": ("attn_bwd.hip", "attn_common.h", "attn_sched.h"),
     "attn_dq": ("attn_dq.hip", "attn_common.h", "attn_sched.h"),
+    "layout": ("layout.hip", "opr_internal.h"),
 }
+# the workload each traffic summary is taken on, and its file under profiles/
+TRAFFIC_WORKLOAD = {"attn_dkdv": "packed_fwd_bwd", "layout": "layout_batch"}
+TRAFFIC_FILE = {"attn_dkdv": "attn_dkdv_packed_fwd_bwd_traffic.json", "layout": "layout_batch_traffic.json"}
 COPY_PROBE_BYTES = 1 << 30    # bytes read (and written) per copy-probe dispatch
 
 
@@ -61,7 +65,7 @@ def source_hash(kernel):
 
 
 def traffic_file(kernel):
-    return os.path.join(PROFILES, f"{kernel}_packed_fwd_bwd_traffic.json")
+    return os.path.join(PROFILES, TRAFFIC_FILE[kernel])
 
 
 def load_traffic(kernel):
@@ -97,31 +101,37 @@ def copy_probe(steps=5):
 
 
 def summarize_traffic(run_dir, kernel):
-    """Write profiles/<kernel>_packed_fwd_bwd_traffic.json from four rocprofv3
+    """Write profiles/<kernel>_<workload>_traffic.json from four rocprofv3
     --pmc runs under run_dir: fetch/ and write/ of the benchmark (FETCH_SIZE,
     WRITE_SIZE) and copy_fetch/ and copy_write/ of --copy-probe.  Counters are
-    KiB per dispatch; each is scaled by (probe bytes) / (probe counter)."""
+    KiB per dispatch; each is scaled by (probe bytes) / (probe counter).  For
+    "layout" a launch is one opr_build_layout call: the per-dispatch averages
+    of its kernels are summed."""
+    import collections
     import csv
     import glob
 
     def per_dispatch(sub, counter, match):
-        vals = []
+        vals = collections.defaultdict(list)
         for f in glob.glob(os.path.join(run_dir, sub, "**", "*counter_collection.csv"), recursive=True):
             for row in csv.DictReader(open(f)):
                 if row["Counter_Name"] == counter and match(row["Kernel_Name"]):
-                    vals.append(float(row["Counter_Value"]))
+                    vals[row["Kernel_Name"]].append(float(row["Counter_Value"]))
         if not vals:
             raise SystemExit(f"no {counter} rows in {sub}")
-        return sum(vals) / len(vals)
+        return sum(sum(v) / len(v) for v in vals.values())
 
-    is_kernel = lambda name: (kernel + "_kernel") in name                       # noqa: E731
+    if kernel == "layout":
+        is_kernel = lambda name: "::layout_" in name                              # noqa: E731
+    else:
+        is_kernel = lambda name: (kernel + "_kernel") in name                     # noqa: E731
     # the probe's copy kernel only (not the fill that initialises its source)
     is_copy = lambda name: "copy" in name.lower() and "fill" not in name.lower()  # noqa: E731
     fetch = per_dispatch("fetch", "FETCH_SIZE", is_kernel)
     write = per_dispatch("write", "WRITE_SIZE", is_kernel)
     cf = COPY_PROBE_BYTES / per_dispatch("copy_fetch", "FETCH_SIZE", is_copy)
     cw = COPY_PROBE_BYTES / per_dispatch("copy_write", "WRITE_SIZE", is_copy)
-    d = {"kernel": kernel, "workload": "packed_fwd_bwd", "source_sha": source_hash(kernel),
+    d = {"kernel": kernel, "workload": TRAFFIC_WORKLOAD[kernel], "source_sha": source_hash(kernel),
          "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
          "copy_probe_bytes": COPY_PROBE_BYTES, "fetch_bytes_per_kib": cf, "write_bytes_per_kib": cw,
          "bytes_per_launch": round(fetch * cf + write * cw)}
@@ -416,7 +426,7 @@ def layout_step(torch, Bd, dev, steps):
     out = {"rows": B, "row_tokens": L, "packed_tokens": sum(I.row_used(r) for r in rows), "ms": round(ms, 4),
            "bytes_written": nbytes,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("layout")}}
     log(f"layout step {out}")
     return out
 
@@ -608,10 +618,13 @@ def main():
     ap.add_argument("--layout-only", action="store_true",
                     help="only time opr_build_layout on 64 rows x 32768 tokens and print its JSON")
     ap.add_argument("--summarize-traffic", metavar="RUN_DIR",
-                    help="write the HBM traffic summary of the dK/dV kernel from --pmc runs and exit")
+                    help="write the HBM traffic summary of a kernel (--traffic-kernel) from --pmc runs and exit")
+    ap.add_argument("--traffic-kernel", default="attn_dkdv", choices=sorted(TRAFFIC_WORKLOAD),
+                    help="the kernel that --summarize-traffic summarises (layout: one opr_build_layout call "
+                         "of --layout-only)")
     args = ap.parse_args()
     if args.summarize_traffic:
-        summarize_traffic(args.summarize_traffic, "attn_dkdv")
+        summarize_traffic(args.summarize_traffic, args.traffic_kernel)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

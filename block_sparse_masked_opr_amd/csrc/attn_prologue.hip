@@ -36,7 +36,21 @@ struct RopeArgs {
   int32_t n_zero;
 };
 
-__device__ __forceinline__ void rope_entry(const RopeArgs &a, int64_t gid) {
+// 2 pi in two parts (the double nearest to it and the remainder) and 1 / (2 pi)
+constexpr double k2PiHi = 6.283185307179586232, k2PiLo = 2.4492935982947064e-16;
+constexpr double kInv2Pi = 0.15915494309189533577;
+
+// One workgroup's entries (gid0 + threadIdx.x); the inverse frequencies of the
+// D/2 <= 64 rotation pairs are formed once per workgroup.  The angle
+// x = pos * inv_freq is reduced by the nearest multiple of 2 pi (two-part
+// constant, each step one rounding) before sin and cos, so the library
+// routines see |r| <= pi; the reduction adds about 1e-16 rad to x's own
+// rounding.
+__device__ __forceinline__ void rope_entries(const RopeArgs &a, int64_t gid0) {
+  __shared__ double inv_freq[64];
+  if ((int)threadIdx.x < a.half) inv_freq[threadIdx.x] = exp2(-(2.0 * threadIdx.x / (2.0 * a.half)) * a.log2_theta);
+  __syncthreads();
+  const int64_t gid = gid0 + threadIdx.x;
   if (gid < a.n_zero) a.zero_words[gid] = 0u;
   const int64_t total = (int64_t)a.B * a.Lp * a.half;
   if (gid >= total) return;
@@ -45,9 +59,11 @@ __device__ __forceinline__ void rope_entry(const RopeArgs &a, int64_t gid) {
   const int32_t t = (int32_t)(bt % a.Lp);
   const int32_t b = (int32_t)(bt / a.Lp);
   const int32_t pos = t < a.L ? a.tok_pos[(int64_t)b * a.L + a.slot_tok[(int64_t)b * a.L + t]] : 0;
-  const double inv_freq = exp2(-(2.0 * j / (2.0 * a.half)) * a.log2_theta);
+  const double x = (double)pos * inv_freq[j];
+  const double nq = rint(x * kInv2Pi);
+  const double r = fma(-nq, k2PiLo, fma(-nq, k2PiHi, x));
   double sn, cs;
-  sincos((double)pos * inv_freq, &sn, &cs);
+  sincos(r, &sn, &cs);
   a.table[gid] = make_float2((float)cs, (float)sn);
 }
 
@@ -423,7 +439,7 @@ __global__ __launch_bounds__(kOrderThreads) void rope_order_kernel(RopeArgs ra, 
     plane_max_part<D, kOrderThreads>(aa, (int64_t)blockIdx.x - 1);
     return;
   }
-  rope_entry(ra, (int64_t)(blockIdx.x - 1 - n_abs) * kOrderThreads + threadIdx.x);
+  rope_entries(ra, (int64_t)(blockIdx.x - 1 - n_abs) * kOrderThreads);
 }
 
 template <int D, bool ROPE, bool ROWS>

@@ -65,3 +65,27 @@ def test_traffic_of_other_sources_is_not_reported(traffic_env):
     assert bench.load_traffic("attn_dkdv") is None
     os.remove(path)
     assert bench.load_traffic("attn_dkdv") is None
+
+
+def test_layout_traffic_sums_its_kernels(tmp_path, monkeypatch):
+    # one opr_build_layout call is four dispatches: the summary adds the
+    # per-dispatch average of each kernel
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(tmp_path / "profiles")
+    run = tmp_path / "run"
+    ks = ["opr::(anonymous namespace)::layout_prep(int, int, int, opr::LayoutWs)",
+          "opr::(anonymous namespace)::layout_fill(int, int, opr::LayoutWs, opr_layout)",
+          "void opr::(anonymous namespace)::layout_classify_attention<128, 128>(int, int, int, int, opr_layout)",
+          "opr::(anonymous namespace)::layout_compact(int, int, int, opr_layout)"]
+    _counter_csv(run / "fetch", [(k, "FETCH_SIZE", v) for k in ks for v in (10.0, 30.0)]
+                 + [("void opr::attn_fwd_kernel<128>()", "FETCH_SIZE", 9e9)])
+    _counter_csv(run / "write", [(k, "WRITE_SIZE", 100.0 * (i + 1)) for i, k in enumerate(ks)])
+    _counter_csv(run / "copy_fetch", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288.0)])
+    _counter_csv(run / "copy_write", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576.0)])
+    bench.summarize_traffic(str(run), "layout")
+    d = json.load(open(bench.traffic_file("layout")))
+    assert bench.traffic_file("layout").endswith("layout_batch_traffic.json")
+    assert d["workload"] == "layout_batch"
+    assert d["fetch_kib_per_dispatch"] == 4 * 20.0 and d["write_kib_per_dispatch"] == 1000.0
+    assert d["bytes_per_launch"] == 80 * 2048 + 1000 * 1024
+    assert bench.load_traffic("layout") == d["bytes_per_launch"]
