@@ -12,12 +12,14 @@
 //   layout_classify  one workgroup per tile, one thread per query row: counts
 //                    the allowed keys of each 32-key sub-block with interval
 //                    arithmetic, then sums per 32x32 sub-block and per tile
-//                    (layout_classify_attention: the same over attention
-//                    order, from the queries' two runs of slots, one
-//                    workgroup per q-tile row, a lane per 32x32 sub-block)
-//   layout_compact   one wave per tile row and per tile column (one launch):
-//                    ballot compaction of the non-empty tiles into ascending
-//                    lists
+//                    (layout_classify_attention: the same classes over
+//                    attention order, one workgroup per q-tile row, from
+//                    per-query-row masks of the 32-key blocks its two runs
+//                    of slots touch and cover, reduced with OR and AND)
+//   layout_compact   one wave per tile row; per 16 tile columns one
+//                    workgroup that reads the classes row-wise and compacts
+//                    the columns from LDS (one launch): ballot compaction of
+//                    the non-empty tiles into ascending lists
 //
 // Visibility of a query q in turn i of a conversation, as key intervals of
 // the packed row (segments of a turn are stored h, t, r_in, r_out):
@@ -140,20 +142,29 @@ __device__ inline int last_le(const int32_t *a, int lo, int hi, int32_t x) {
   return lo;
 }
 
-// n words from host memory mapped for the device into the workspace.  Each
-// thread has kStageIn loads in flight before it stores: a read crosses the
-// host link, so one round trip per word would dominate.
-constexpr int kStageIn = 8;
-__device__ void stage_in(const int32_t *src, int32_t *dst, int n) {
+// The three host lists (n0, n1, n2 words), read in place from host memory
+// mapped for the device, into the workspace.  A read crosses the host link, so
+// the words of all three lists are read as one flat range: each thread has
+// kStageIn loads in flight before it stores, and one round trip covers
+// kPrepThreads * kStageIn words (every list of a 64-row batch of 32768-token
+// rows fits one).
+constexpr int kStageIn = 16;
+__device__ void stage_in3(const int32_t *s0, int32_t *d0, int n0, const int32_t *s1, int32_t *d1, int n1,
+                          const int32_t *s2, int32_t *d2, int n2) {
+  const int n = n0 + n1 + n2;
   for (int base = 0; base < n; base += kPrepThreads * kStageIn) {
     int32_t v[kStageIn];
 #pragma unroll
-    for (int u = 0; u < kStageIn; ++u)  // unconditional loads (index clamped): no branch between them
-      v[u] = src[min(base + u * kPrepThreads + (int)threadIdx.x, n - 1)];
+    for (int u = 0; u < kStageIn; ++u) {  // unconditional loads (index clamped): no branch between them
+      const int i = min(base + u * kPrepThreads + (int)threadIdx.x, n - 1);
+      v[u] = i < n0 ? s0[i] : i < n0 + n1 ? s1[i - n0] : s2[i - n0 - n1];
+    }
 #pragma unroll
     for (int u = 0; u < kStageIn; ++u) {
       const int i = base + u * kPrepThreads + (int)threadIdx.x;
-      if (i < n) dst[i] = v[u];
+      if (i < n0) d0[i] = v[u];
+      else if (i < n0 + n1) d1[i - n0] = v[u];
+      else if (i < n) d2[i - n0 - n1] = v[u];
     }
   }
 }
@@ -163,9 +174,7 @@ __global__ __launch_bounds__(kPrepThreads) void layout_prep(int32_t B, int32_t C
   __shared__ int32_t sh[kPrepThreads];
   if (ws.src_cpr) {
     // the host arrays, read in place (4-byte words: any opr_turn alignment)
-    stage_in(ws.src_cpr, ws.cpr, B);
-    stage_in(ws.src_tpc, ws.tpc, C);
-    stage_in(ws.src_turns, reinterpret_cast<int32_t *>(ws.turns), 4 * T);
+    stage_in3(ws.src_cpr, ws.cpr, B, ws.src_tpc, ws.tpc, C, ws.src_turns, reinterpret_cast<int32_t *>(ws.turns), 4 * T);
     __syncthreads();  // the block's own copies are visible to all its threads
   }
   const int32_t *cpr = ws.cpr;
@@ -499,30 +508,90 @@ __global__ __launch_bounds__(kClsThreads) void layout_classify_attention(int32_t
   }
 }
 
-// The lists of non-empty tiles, one wave per list: blocks [0, B*MT) take
-// q-tile row b*MT + m (its k-tile indices), the next B*NT k-tile column
-// b*NT + n (its q-tile indices).  Ballot compaction, ascending.
-__global__ __launch_bounds__(64) void layout_compact(int32_t B, int32_t MT, int32_t NT, opr_layout out) {
-  const int64_t id = blockIdx.x;
-  const int lane = threadIdx.x;
-  const bool is_row = id < (int64_t)B * MT;
-  const int64_t idx = is_row ? id : id - (int64_t)B * MT;  // row b*MT + m, or column b*NT + n
-  const int64_t b = is_row ? idx / MT : idx / NT;
-  const int32_t len = is_row ? NT : MT;
-  const uint8_t *cls = is_row ? out.tile_class + idx * NT : out.tile_class + b * MT * NT + (idx - b * NT);
-  const int64_t stride = is_row ? 1 : NT;
-  int32_t *lst = is_row ? out.q_list + idx * NT : out.k_list + idx * MT;
-  int32_t count = 0;
-  for (int32_t base = 0; base < len; base += 64) {
-    const int32_t x = base + lane;
-    const bool nz = x < len && cls[(int64_t)x * stride] != OPR_TILE_EMPTY;
-    const uint64_t bal = __ballot(nz);
-    const int32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (nz) lst[count + before] = x;
-    count += __popcll(bal);
+// The lists of non-empty tiles, ballot compaction, ascending; workgroups of
+// kCmpThreads.  Workgroups [0, row_groups) take q-tile rows, one wave per row
+// b*MT + m (its k-tile indices; the row's classes are contiguous).  The rest
+// take kCmpCols k-tile columns of one row b each (their q-tile indices): a
+// column's classes lie NT bytes apart, so the block's kCmpCols contiguous
+// bytes of kCmpRows q-tile rows at a time are read row-wise (one load per
+// row and thread where NT allows aligned loads), stored column-major in LDS,
+// and each wave compacts its kCmpCols / 4 columns there.
+constexpr int kCmpThreads = 256, kCmpCols = 16, kCmpRows = 256;
+
+__device__ __forceinline__ void compact_ballot(bool nz, int32_t x, int32_t *lst, int32_t &count, int lane) {
+  const uint64_t bal = __ballot(nz);
+  const int32_t before = __popcll(bal & ((1ull << lane) - 1ull));
+  if (nz) lst[count + before] = x;
+  count += __popcll(bal);
+}
+
+__global__ __launch_bounds__(kCmpThreads) void layout_compact(int32_t B, int32_t MT, int32_t NT, int32_t row_groups,
+                                                              opr_layout out) {
+  __shared__ uint8_t tcol[kCmpCols][kCmpRows + 4];  // [column][row], padded
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if ((int32_t)blockIdx.x < row_groups) {
+    const int64_t idx = (int64_t)blockIdx.x * (kCmpThreads / 64) + wv;  // row b*MT + m
+    if (idx >= (int64_t)B * MT) return;
+    const uint8_t *cls = out.tile_class + idx * NT;
+    int32_t *lst = out.q_list + idx * NT;
+    int32_t count = 0;
+    for (int32_t base = 0; base < NT; base += 64) {
+      const int32_t x = base + lane;
+      compact_ballot(x < NT && cls[x] != OPR_TILE_EMPTY, x, lst, count, lane);
+    }
+    for (int32_t x = count + lane; x < NT; x += 64) lst[x] = -1;
+    if (lane == 0) out.q_nnz[idx] = count;
+    return;
   }
-  for (int32_t x = count + lane; x < len; x += 64) lst[x] = -1;
-  if (lane == 0) (is_row ? out.q_nnz : out.k_nnz)[idx] = count;
+  const int32_t cgroups = (NT + kCmpCols - 1) / kCmpCols;
+  const int32_t g = (int32_t)blockIdx.x - row_groups;
+  const int32_t b = g / cgroups, n0 = (g % cgroups) * kCmpCols;
+  const uint8_t *cls = out.tile_class + (int64_t)b * MT * NT;
+  // whole aligned 16-byte row pieces: every row of the block starts on a
+  // 16-byte boundary and holds all kCmpCols columns
+  const bool vec = (NT % kCmpCols) == 0 && (reinterpret_cast<uintptr_t>(out.tile_class) & 15u) == 0;
+  constexpr int kWaveCols = kCmpCols / (kCmpThreads / 64);
+  int32_t count[kWaveCols];
+#pragma unroll
+  for (int c = 0; c < kWaveCols; ++c) count[c] = 0;
+  for (int32_t m0 = 0; m0 < MT; m0 += kCmpRows) {
+    const int32_t rows = min(kCmpRows, MT - m0);
+    __syncthreads();  // the previous chunk's columns have been read
+    if (vec) {
+      // thread r: the block's 16 bytes of row m0 + r
+      if (tid < rows) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(cls + (int64_t)(m0 + tid) * NT + n0);
+        const uint32_t ws4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < kCmpCols; ++e) tcol[e][tid] = (uint8_t)(ws4[e >> 2] >> (8 * (e & 3)));
+      }
+    } else {
+      // thread: byte tid % kCmpCols of rows tid / kCmpCols + k * (kCmpThreads / kCmpCols)
+      for (int32_t r = tid / kCmpCols; r < rows; r += kCmpThreads / kCmpCols) {
+        const int32_t n = n0 + tid % kCmpCols;
+        tcol[tid % kCmpCols][r] = n < NT ? cls[(int64_t)(m0 + r) * NT + n] : (uint8_t)OPR_TILE_EMPTY;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kWaveCols; ++c) {
+      const int32_t n = n0 + wv * kWaveCols + c;
+      if (n >= NT) break;
+      int32_t *lst = out.k_list + ((int64_t)b * NT + n) * MT;
+      for (int32_t base = 0; base < rows; base += 64) {
+        const int32_t x = base + lane;
+        compact_ballot(x < rows && tcol[wv * kWaveCols + c][x] != OPR_TILE_EMPTY, m0 + x, lst, count[c], lane);
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kWaveCols; ++c) {
+    const int32_t n = n0 + wv * kWaveCols + c;
+    if (n >= NT) break;
+    int32_t *lst = out.k_list + ((int64_t)b * NT + n) * MT;
+    for (int32_t x = count[c] + lane; x < MT; x += 64) lst[x] = -1;
+    if (lane == 0) out.k_nnz[(int64_t)b * NT + n] = count[c];
+  }
 }
 
 template <int BQ, int BK>
@@ -568,7 +637,9 @@ hipError_t launch_build_layout(int32_t B, int32_t L, int32_t bq, int32_t bk, int
   OPR_CLASSIFY_CASE(64, 32) OPR_CLASSIFY_CASE(64, 64) OPR_CLASSIFY_CASE(64, 128)
   OPR_CLASSIFY_CASE(128, 32) OPR_CLASSIFY_CASE(128, 64) OPR_CLASSIFY_CASE(128, 128)
 #undef OPR_CLASSIFY_CASE
-  layout_compact<<<(unsigned)((int64_t)B * (MT + NT)), 64, 0, s>>>(B, MT, NT, out);
+  const int64_t row_groups = ((int64_t)B * MT + kCmpThreads / 64 - 1) / (kCmpThreads / 64);
+  const int64_t col_groups = (int64_t)B * ((NT + kCmpCols - 1) / kCmpCols);
+  layout_compact<<<(unsigned)(row_groups + col_groups), kCmpThreads, 0, s>>>(B, MT, NT, (int32_t)row_groups, out);
   return hipGetLastError();
 }
 
