@@ -543,8 +543,14 @@ __global__ __launch_bounds__(kCmpThreads) void layout_compact(int32_t B, int32_t
     if (lane == 0) out.q_nnz[idx] = count;
     return;
   }
+  // Workgroups go to the 8 XCDs round-robin by index, and the column groups
+  // of one row b share the cache lines of its classes: the groups are numbered
+  // so that consecutive ones (the same b) land on one XCD.  The column part of
+  // the grid is padded to a multiple of 8 workgroups, Q per XCD.
   const int32_t cgroups = (NT + kCmpCols - 1) / kCmpCols;
-  const int32_t g = (int32_t)blockIdx.x - row_groups;
+  const int32_t Q = (B * cgroups + 7) / 8;
+  const int32_t g = (int32_t)(blockIdx.x % 8) * Q + ((int32_t)blockIdx.x - row_groups) / 8;
+  if (g >= B * cgroups) return;
   const int32_t b = g / cgroups, n0 = (g % cgroups) * kCmpCols;
   const uint8_t *cls = out.tile_class + (int64_t)b * MT * NT;
   // whole aligned 16-byte row pieces: every row of the block starts on a
@@ -638,7 +644,7 @@ hipError_t launch_build_layout(int32_t B, int32_t L, int32_t bq, int32_t bk, int
   OPR_CLASSIFY_CASE(128, 32) OPR_CLASSIFY_CASE(128, 64) OPR_CLASSIFY_CASE(128, 128)
 #undef OPR_CLASSIFY_CASE
   const int64_t row_groups = ((int64_t)B * MT + kCmpThreads / 64 - 1) / (kCmpThreads / 64);
-  const int64_t col_groups = (int64_t)B * ((NT + kCmpCols - 1) / kCmpCols);
+  const int64_t col_groups = 8 * (((int64_t)B * ((NT + kCmpCols - 1) / kCmpCols) + 7) / 8);
   layout_compact<<<(unsigned)(row_groups + col_groups), kCmpThreads, 0, s>>>(B, MT, NT, (int32_t)row_groups, out);
   return hipGetLastError();
 }
