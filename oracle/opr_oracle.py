@@ -571,7 +571,7 @@ def _seg_index(lay, b, c):
     return out
 
 
-def npass_index(lay, b: int, c: int) -> List[Dict[str, np.ndarray]]:
+def npass_index(lay, b: int, c: int, n_turns: int = None) -> List[Dict[str, np.ndarray]]:
     """For each turn i, the packed rows that make up pass i of the N-pass.
 
     Pass i is the ordinary sequence [h_1, r_1, ..., h_{i-1}, r_{i-1}, h_i, t_i, r_i]
@@ -579,10 +579,14 @@ def npass_index(lay, b: int, c: int) -> List[Dict[str, np.ndarray]]:
     copy r_in_j stands for r_j of an earlier turn, the generation copy r_out_i
     for r_i of turn i.  Returns per pass: 'idx' (packed rows in sequence order)
     and 'role' (the packed type each sequence position stands for).
+
+    Turns that hold no tokens leave no trace in the layout, so trailing ones
+    are invisible to it; ``n_turns`` (the conversation's turn count) gives
+    them their passes, which then hold the history alone.
     """
     seg = _seg_index(lay, b, c)
     empty = np.zeros(0, dtype=np.int64)
-    N = max(i for (i, _y) in seg) + 1
+    N = max(i for (i, _y) in seg) + 1 if n_turns is None else n_turns
     passes = []
     for i in range(N):
         parts, roles = [], []

@@ -3,7 +3,7 @@ sequences.py, which the GPU tests and the benchmark run through the kernels)
 against the oracle's own derivation of the same sequences from the pages
 (oracle.npass_index, oracle.kpass_chunk) and against the rules themselves."""
 import numpy as np
-from hypothesis import given, settings, strategies as st
+from hypothesis import example, given, settings, strategies as st
 
 from block_sparse_masked_opr_amd import inputs as I
 from block_sparse_masked_opr_amd import sequences as S
@@ -14,13 +14,14 @@ turn = st.tuples(st.integers(0, 6), st.integers(0, 6), st.integers(0, 6))
 
 @settings(max_examples=40, deadline=None)
 @given(conv=st.lists(turn, min_size=1, max_size=5))
+@example(conv=[(0, 0, 1), (0, 0, 0)])  # a trailing empty turn: its pass is the history alone
 def test_npass_sequences_match_oracle_passes(conv):
     """Pass i as the product writes it has, token by token, the roles of the
     oracle's pass i gathered from the one-pass row (history h / r_in, then
     h_i, t_i, r_out_i), positions 0..n-1 and a plain causal mask."""
     conv = [(h, t, r, r) for (h, t, r) in conv]
     full = O.layout([[conv]], max(1, I.conv_len(conv)))
-    passes = O.npass_index(full, 0, 0) if I.conv_len(conv) else []
+    passes = O.npass_index(full, 0, 0, len(conv)) if I.conv_len(conv) else []
     seqs = S.npass_conversations(conv)
     assert len(seqs) == len(conv)
     for i, seq in enumerate(seqs):
