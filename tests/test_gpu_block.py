@@ -6,7 +6,9 @@ Tolerances: the GPU block stores bf16 at each stage the interface fixes
 (qkv, the normalised q and k, o, y; d(o), dqkv, dx), each a relative rounding
 of at most 2^-9, on top of the attention kernels' own error; the oracle rounds
 nothing.  Outputs are held to max |x - ref| <= 3e-2 max |ref| and
-sum |x - ref| / sum |ref| <= 1e-2.
+sum |x - ref| / sum |ref| <= 1e-2.  The attention inside the block is also
+checked alone, from the GPU's own qkv, at the attention kernels' bar
+(max-abs 2e-2, mean-rel 5e-3).
 """
 from __future__ import annotations
 
@@ -90,6 +92,22 @@ def test_block_small(B, case):
     close("dw_o", got["dw_o"], dw_o)
     close("dg_q", got["dg_q"], dg_q)
     close("dg_k", got["dg_k"], dg_k)
+    check_attention_inside(got, lay, wf, Hq, Hkv, D, live)
+
+
+def check_attention_inside(got, lay, wf, Hq, Hkv, D, live):
+    """The block's attention alone, at the attention bar (max-abs 2e-2,
+    mean-rel 5e-3): the oracle normalises the GPU's own bf16 qkv, rounds the
+    normalised q and k to bf16 as the block stores them, and attends; so the
+    stored-bf16 steps before the attention leave the comparison, and what is
+    left is the attention kernels' error (plus at most one bf16 step of the
+    norm's rounding on a few elements)."""
+    q, k, v = O._split_qkv(got["qkv"], Hq, Hkv, D)
+    rb = lambda a: bf16_f64(I.round_to_bf16_bits(np.asarray(a, dtype=np.float32)))  # noqa: E731
+    qn, kn = rb(O.rms_norm(q, wf["g_q"], EPS)), rb(O.rms_norm(k, wf["g_k"], EPS))
+    o, lse = O.attn_fwd(qn, kn, v, lay, THETA)
+    assert_close("o (attention alone)", got["o"][live], o[live])
+    assert_close("lse (attention alone)", got["lse"].transpose(0, 2, 1)[live], lse.transpose(0, 2, 1)[live])
 
 
 def test_block_packed_full_size(B):
@@ -112,6 +130,8 @@ def test_block_packed_full_size(B):
     args = (wf["w_qkv"], wf["w_o"], wf["g_q"], wf["g_k"])
     y, st = O.block_fwd(x, *args, lay, s.Hq, s.Hkv, s.D, s.theta, EPS)
     close("o (conversation 0)", got["o"][:1, :n], st["o"])
+    sub = {"qkv": got["qkv"][:1, :n], "o": got["o"][:1, :n], "lse": got["lse"][:1, :, :n]}
+    check_attention_inside(sub, lay, wf, s.Hq, s.Hkv, s.D, np.ones((1, n), dtype=bool))
     close("y (conversation 0)", got["y"][:1, :n], y)
     dx = O.block_bwd(x, *args, dy, lay, s.Hq, s.Hkv, s.D, s.theta, EPS)[0]
     close("dx (conversation 0)", got["dx"][:1, :n], dx)
