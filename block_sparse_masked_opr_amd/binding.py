@@ -3,7 +3,9 @@
 Argument marshalling only: torch provides device memory and the current HIP
 stream; every step of the computation runs in libopr's kernels.  Importing
 this module loads libopr.so and raises if it has not been built; there is no
-fallback path.
+fallback path.  With OPR_LIB=debug in the environment it loads the checked
+build, libopr_debug.so, instead (same kernels with invariant tests;
+opr_debug_errors reads their error bits).
 """
 from __future__ import annotations
 
@@ -16,7 +18,8 @@ import torch
 
 from . import inputs
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libopr.so")
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                         "libopr_debug.so" if os.environ.get("OPR_LIB") == "debug" else "libopr.so")
 
 OPR_OK, OPR_E_INVALID, OPR_E_CAPACITY, OPR_E_UNSUPPORTED, OPR_E_HIP = 0, -1, -2, -3, -4
 OPR_ATTN_BLOCK = 128
@@ -104,6 +107,8 @@ def _load() -> ctypes.CDLL:
                                    ctypes.POINTER(ctypes.c_double)]
     lib.opr_status_string.restype = ctypes.c_char_p
     lib.opr_status_string.argtypes = [i32]
+    lib.opr_debug_errors.restype = i32
+    lib.opr_debug_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     return lib
 
 
@@ -112,11 +117,22 @@ LIB = _load()
 EXPORTED = ("opr_build_layout", "opr_build_layout_noalloc", "opr_build_layout_workspace_size", "opr_attn_fwd",
             "opr_attn_bwd", "opr_attn_workspace_size", "opr_token_ce", "opr_token_ce_workspace_size",
             "opr_block_fwd", "opr_block_bwd", "opr_block_workspace_size", "opr_kpass_plan",
-            "opr_status_string")
+            "opr_status_string", "opr_debug_errors")
 
 
 def opr_status_string(status: int) -> str:
     return LIB.opr_status_string(int(status)).decode()
+
+
+def opr_debug_errors() -> Optional[int]:
+    """The current device's invariant-test bits of a checked build (then
+    cleared); None for a release build, which tests nothing."""
+    bits = ctypes.c_uint32(0)
+    st = LIB.opr_debug_errors(ctypes.byref(bits))
+    if st == OPR_E_UNSUPPORTED:
+        return None
+    _check(st, "opr_debug_errors")
+    return int(bits.value)
 
 
 def _check(status: int, what: str) -> None:

@@ -87,6 +87,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
   const int64_t R = blockIdx.x;  // rank: longest items first, round-robin over the XCDs
   if (R / p.Hkv >= p.k_counts[0]) return;
   const int4 item = p.k_items[R / p.Hkv];  // (column, part, parts, partial slot or -1)
+  if (!OPR_DCHECK(p.dbg, (unsigned)item.x < (unsigned)(p.B * p.NT) && (unsigned)item.y < (unsigned)item.z &&
+                             item.w < kSplitSlots, kDbgItem))
+    return;
   const int32_t col = item.x;
   const int kvh = (int)(R % p.Hkv);
   const int b = col / p.NT;
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     __syncthreads();
     if (wave == 0) {
       int64_t f = fnext;
-      const int c = build_k_stages(lst, subs_b, p.NT, n, p.group, fend, &f, stages, lane);
+      const int c = build_k_stages(lst, subs_b, p.NT, p.MT, n, p.group, fend, &f, stages, lane, p.dbg);
       if (lane == 0) {
         sh_count = c;
         sh_next = f;
@@ -358,6 +361,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_kernel(AttnParams p, float *
     int64_t out;
     if (item.w < 0) {
       const int tok = p.slot_tok[(int64_t)b * p.L + key];
+      if (!OPR_DCHECK(p.dbg, (unsigned)tok < (unsigned)p.L, kDbgToken)) return;
       out = (((int64_t)b * p.L + tok) * p.Hkv + kvh) * D;
     } else {
       out = (((int64_t)item.w * p.Hkv + kvh) * OPR_ATTN_BLOCK + (key - n * OPR_ATTN_BLOCK)) * D;
@@ -461,7 +465,9 @@ __global__ __launch_bounds__(256) void dkdv_units_kernel(AttnParams p) {
     const int qh = (int)(ff & 1);
     const int64_t tj = ff >> 1;
     const int hj = (int)(tj % p.group);
-    const int q0 = lst[tj / p.group] * 128 + 64 * qh;
+    const int m = lst[tj / p.group];
+    if (!OPR_DCHECK(p.dbg, (unsigned)m < (unsigned)p.MT, kDbgKList)) continue;
+    const int q0 = m * 128 + 64 * qh;
     const int64_t tix = gt + (int64_t)hj * p.MTS + q0 / kTile;
     const int4 e4 = *reinterpret_cast<const int4 *>(p.eqt + tix);
     const int4 d4 = *reinterpret_cast<const int4 *>(p.edot + tix);
@@ -525,6 +531,7 @@ __global__ __launch_bounds__(256) void dkdv_split_reduce_kernel(AttnParams p, fl
     const int key = n * OPR_ATTN_BLOCK + kl;
     if (key >= p.L) continue;
     const int tok = p.slot_tok[(int64_t)b * p.L + key];
+    if (!OPR_DCHECK(p.dbg, (unsigned)tok < (unsigned)p.L, kDbgToken)) continue;
     const int64_t out = (((int64_t)b * p.L + tok) * p.Hkv + kvh) * D + 4 * c4;
     float4 ak = *reinterpret_cast<const float4 *>(dk + out);
     float4 av = *reinterpret_cast<const float4 *>(dv + out);

@@ -391,6 +391,20 @@ inline int64_t q_grid(int64_t n_rows, int Hkv, int group) {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Checked builds (-DOPR_DEBUG): the attention kernels test the invariants
+// their indexing relies on (tile-list entries inside the tile grid, the
+// token of a live slot inside its row, dK/dV work items inside their
+// tables); a violated one sets its bit in a device word (dbg) and the access
+// it guards is skipped, so the kernel still ends normally.  Bits:
+// 1 q-tile list entry, 2 k-tile list entry, 4 token of a slot, 8 dK/dV item.
+// Release builds compile no test (OPR_DCHECK is true).
+#ifdef OPR_DEBUG
+#define OPR_DCHECK(dbg, cond, bit) ((cond) ? true : (atomicOr((dbg), (bit)), false))
+#else
+#define OPR_DCHECK(dbg, cond, bit) true
+#endif
+constexpr uint32_t kDbgQList = 1u, kDbgKList = 2u, kDbgToken = 4u, kDbgItem = 8u;
+
 // Parameters shared by the attention kernels.
 struct AttnParams {
   int32_t B, L, Lp, Hq, Hkv, group, MT, NT;
@@ -430,6 +444,7 @@ struct AttnParams {
   // [B][Hq][L] (backward)
   const uint16_t *q_in, *o_in, *dout_in;
   const float *lse_in;
+  uint32_t *dbg;               // checked builds: the device's error word (else null)
 };
 
 }  // namespace opr

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
   // ---- prologue: Delta, the fp16 dout with its row exponent, the dK/dV
   // units.  The loads are issued here; the conversion (convert_dout) runs once
   // the stage list is built and the first K/V tiles stream in.
-  const int32_t tok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
+  int32_t tok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
+  if (tok >= 0 && !OPR_DCHECK(p.dbg, tok < p.L, kDbgToken)) tok = -1;
   uint4 dw[NS], ow[NS];  // bf16 dims 16 s + 8 g .. + 7 of dout and o
 #pragma unroll
   for (int s = 0; s < NS; ++s) dw[s] = ow[s] = make_uint4(0u, 0u, 0u, 0u);
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
     __syncthreads();  // the previous chunk's stages and buffers are no longer read
     if (w == 0) {
       int t = tnext;
-      const int c = build_q_quarters<kDqStageCap>(lst, subs, nnz, &t, stages, lane);
+      const int c = build_q_quarters<kDqStageCap>(lst, subs, nnz, p.NT, &t, stages, lane, p.dbg);
       if (lane == 0) {
         sh_count = c;
         sh_next = t;
@@ -237,9 +238,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(AttnParams p, float *dq
     build();
   }
 
-  if (q < p.L) {
-    const int tok = p.slot_tok[(int64_t)b * p.L + q];
-    float *out = dq + (((int64_t)b * p.L + tok) * p.Hq + h) * D;
+  // the slot's token, read again here rather than held through the loop
+  const int etok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
+  if (etok >= 0 && OPR_DCHECK(p.dbg, etok < p.L, kDbgToken)) {
+    float *out = dq + (((int64_t)b * p.L + etok) * p.Hq + h) * D;
     const float2 *cs = p.rope + ((int64_t)b * p.Lp + q) * (D / 2);
     // dQ^T in units 2^(ek + ev + edo - kDsShift); the unit exponent is
     // applied to the value (it can exceed fp32's range as a factor)

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnParams p, uint16_t
   // conversion (convert_q) runs once the stage list is built and the first
   // K/V tiles stream in, so that their latencies overlap.
   const int64_t hq_row = ((int64_t)b * p.Hq + h) * p.Lp + q;
-  const int32_t tok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
+  int32_t tok = q < p.L ? p.slot_tok[(int64_t)b * p.L + q] : -1;
+  if (tok >= 0 && !OPR_DCHECK(p.dbg, tok < p.L, kDbgToken)) tok = -1;
   uint4 wv[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) wv[s] = make_uint4(0u, 0u, 0u, 0u);
@@ -160,13 +161,13 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnParams p, uint16_t
     tc.issue(rv, k0, nb + TB, w);
   };
 
-  // the stage list (32-key quarters) is built in chunks of up to kStageCap stages
+  // the stage list (32-key quarters) is built in chunks of up to kFwdStageCap stages
   int tnext = 0, ns = 0;
   auto build = [&]() {
     __syncthreads();  // the previous chunk's stages and buffers are no longer read
     if (w == 0) {
       int t = tnext;
-      const int c = build_q_quarters<kFwdStageCap>(lst, subs, nnz, &t, stages, lane);
+      const int c = build_q_quarters<kFwdStageCap>(lst, subs, nnz, p.NT, &t, stages, lane, p.dbg);
       if (lane == 0) {
         sh_count = c;
         sh_next = t;
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_kernel(AttnParams p, uint16_t
   }
 
   const float lsum = lrow + __shfl_xor(lrow, 32);
-  if (q < p.L) {
+  if (tok >= 0) {  // every slot below L holds a token
     // O = acc / sum, acc in units 2^ev (v) times 2^kPExp (shared with sum)
     const float inv = lsum > 0.0f ? ldexpf(1.0f / lsum, -ev) : 0.0f;
     uint16_t *orow = o + (((int64_t)b * p.L + tok) * p.Hq + h) * D;

@@ -316,6 +316,7 @@ struct OrderArgs {
   int32_t *cost, *q_order;
   int4 *k_raw, *k_items, *k_split;
   int32_t *k_counts;
+  uint32_t *dbg;  // checked builds: the error word (attn_common.h)
 };
 
 __device__ void work_order(const OrderArgs &a) {
@@ -344,7 +345,8 @@ __device__ void work_order(const OrderArgs &a) {
         const int32_t *lst = q_list + (int64_t)it * NT;
         const uint32_t *subs = sub_class + (int64_t)it * NT;
         for (int32_t t = sub; t < cnt; t += 8) {
-          const uint32_t w = subs[lst[t]];
+          const int32_t n = lst[t];
+          const uint32_t w = OPR_DCHECK(a.dbg, (unsigned)n < (unsigned)NT, kDbgQList) ? subs[n] : 0u;
           k += ((w & 0x0F0F0F0Fu) != 0) + ((w & 0xF0F0F0F0u) != 0);
         }
       } else {          // column it: query halves are sub-block rows {0,1} and {2,3}
@@ -352,7 +354,9 @@ __device__ void work_order(const OrderArgs &a) {
         const int32_t cnt = k_nnz[it];
         const int32_t *lst = k_list + (int64_t)it * MT;
         for (int32_t t = sub; t < cnt; t += 8) {
-          const uint32_t w = sub_class[((int64_t)b * MT + lst[t]) * NT + col];
+          const int32_t m = lst[t];
+          const uint32_t w =
+              OPR_DCHECK(a.dbg, (unsigned)m < (unsigned)MT, kDbgKList) ? sub_class[((int64_t)b * MT + m) * NT + col] : 0u;
           k += ((w & 0x0000FFFFu) != 0) + ((w & 0xFFFF0000u) != 0);
         }
       }
@@ -469,7 +473,7 @@ void launch_rope_order_d(const opr_attn_in &in, const AttnWs &ws, hipStream_t s)
   const int32_t MT = ws.Lp / OPR_ATTN_BLOCK, NT = MT;
   const OrderArgs oa = {in.B * MT, in.B * NT, MT, NT, in.Hkv, in.layout.sub_class, in.layout.q_nnz,
                         in.layout.q_list, in.layout.k_nnz, in.layout.k_list, ws.order_cost, ws.q_order,
-                        ws.k_raw, ws.k_items, ws.k_split, ws.k_counts};
+                        ws.k_raw, ws.k_items, ws.k_split, ws.k_counts, debug_word()};
   constexpr int HPB = kOrderThreads / (D / 8);
   const int32_t hb = (in.Hkv + HPB - 1) / HPB;
   const AbsArgs aa = {static_cast<const uint16_t *>(in.k), static_cast<const uint16_t *>(in.v), ws.pmax_part,

@@ -130,6 +130,7 @@ void fill_params(const opr_attn_in &in, float scale, const AttnWs &ws, AttnParam
   p->o_in = nullptr;
   p->dout_in = nullptr;
   p->lse_in = nullptr;
+  p->dbg = debug_word();
 }
 
 // Shape checks shared by the attention entry points and the size query.
@@ -396,11 +397,59 @@ static opr_status layout_scratch(void **ptr) {
   return OPR_OK;
 }
 
+#ifdef OPR_DEBUG
+// The error word of the checked kernels, one per device (found and kept like
+// the layout scratch above).
+static __device__ __align__(256) uint32_t dbg_word[64];
+static void *g_dbg_ptr[kMaxDevices];
+#endif
+
+uint32_t *debug_word() {
+#ifdef OPR_DEBUG
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_dbg_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(dbg_word)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_dbg_ptr[dev] = p;
+  }
+  return static_cast<uint32_t *>(g_dbg_ptr[dev]);
+#else
+  return nullptr;
+#endif
+}
+
 }  // namespace opr
 
 using namespace opr;
 
 extern "C" {
+
+opr_status opr_debug_errors(uint32_t *bits) {
+  if (!bits) return OPR_E_INVALID;
+  *bits = 0;
+#ifdef OPR_DEBUG
+  uint32_t *w = debug_word();
+  if (!w) return OPR_E_HIP;
+  uint32_t v = 0;
+  if (hipDeviceSynchronize() != hipSuccess || hipMemcpy(&v, w, sizeof v, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(w, 0, sizeof v) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    return OPR_E_HIP;
+  }
+  *bits = v;
+  return OPR_OK;
+#else
+  return OPR_E_UNSUPPORTED;
+#endif
+}
 
 size_t opr_build_layout_workspace_size(int32_t B, int32_t L, int32_t n_convs, int32_t n_turns) {
   if (B < 1 || L < 1 || n_convs < 0 || n_turns < 0) return 0;

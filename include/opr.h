@@ -472,6 +472,24 @@ opr_status opr_kpass_plan(const opr_turn *turns, int32_t n_turns, int32_t n_chun
 /* Static, human-readable name of a status code. */
 const char *opr_status_string(opr_status status);
 
+/* ---------------------------------------------------------------------------
+ * opr_debug_errors: the invariant tests of a checked build.
+ *
+ * A library built with -DOPR_DEBUG (libopr_debug.so; block_sparse_masked_opr_amd
+ * build(debug=True)) runs the same kernels with tests of the invariants
+ * their indexing relies on; a violated test sets a bit in a per-device word
+ * and skips the access it guards, so no kernel leaves its buffers.  Bits:
+ * 1 a q-tile list entry outside the tile grid, 2 a k-tile list entry outside
+ * it, 4 the token of a live slot outside its row, 8 a dK/dV work item outside
+ * its tables.  Any bit set means the layout given to the attention calls did
+ * not come from opr_build_layout for the same B and L, or a library bug.
+ *  bits   host; receives the current device's word, which is then cleared.
+ * Synchronises the current device (checked builds only).
+ * Errors: OPR_E_INVALID (bits NULL), OPR_E_UNSUPPORTED (a release build:
+ * *bits = 0, nothing is tested), OPR_E_HIP.
+ */
+opr_status opr_debug_errors(uint32_t *bits);
+
 #ifdef __cplusplus
 }
 #endif

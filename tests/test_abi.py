@@ -30,11 +30,28 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol(Bd):
     names = declared_entry_points()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     lib = ctypes.CDLL(Bd._LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(Bd.EXPORTED) == names
+
+
+def test_checked_build_exports_and_debug_errors(Bd):
+    """The checked library exports the same entry points; opr_debug_errors
+    rejects a null pointer in both builds and reports a release build as
+    unsupported with no bits (no HIP call on either path)."""
+    bits = ctypes.c_uint32(7)
+    assert Bd.LIB.opr_debug_errors(None) == Bd.OPR_E_INVALID
+    assert Bd.LIB.opr_debug_errors(ctypes.byref(bits)) == Bd.OPR_E_UNSUPPORTED and bits.value == 0
+    dbg = os.path.join(ROOT, "block_sparse_masked_opr_amd", "libopr_debug.so")
+    if not os.path.exists(dbg):
+        pytest.skip("libopr_debug.so not built")
+    lib = ctypes.CDLL(dbg)
+    for n in declared_entry_points():
+        assert hasattr(lib, n), n
+    lib.opr_debug_errors.argtypes = [ctypes.c_void_p]
+    assert lib.opr_debug_errors(None) == Bd.OPR_E_INVALID
 
 
 def test_status_strings(Bd):
