@@ -405,6 +405,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 #endif
 constexpr uint32_t kDbgQList = 1u, kDbgKList = 2u, kDbgToken = 4u, kDbgItem = 8u;
 
+// Host: the current device's error word of a checked build (opr_api.cpp;
+// opr_debug_errors reads it); null in release builds or if its address cannot
+// be found.
+uint32_t *debug_word();
+
 // Parameters shared by the attention kernels.
 struct AttnParams {
   int32_t B, L, Lp, Hq, Hkv, group, MT, NT;

@@ -110,11 +110,6 @@ struct AttnWs {
 
 size_t carve_attn_ws(void *ws, const opr_attn_in &in, int is_bwd, AttnWs *out);
 
-// Checked builds (OPR_DEBUG): the current device's error word of the kernels'
-// invariant tests (opr_debug_errors reads it); null in release builds or if
-// its address cannot be found.
-uint32_t *debug_word();
-
 hipError_t launch_attn_fwd(const opr_attn_in &in, float scale, void *o, float *lse,
                            const AttnWs &ws, hipStream_t stream);
 
